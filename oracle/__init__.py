@@ -1,0 +1,123 @@
+"""Python access to the plain C oracle of the Engram forward pass.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by ``__graft_entry__.smoke()``
+and by the CPU-baseline leg of ``bench.py``.  The product library never uses it.
+
+``build()`` compiles ``engram_oracle.c`` with gcc into ``liboracle.so`` next to
+it.  The wrappers take numpy arrays and return numpy arrays; floating-point
+results are float64.  See ``engram_oracle.c`` for the definitions and the
+passages of "Conditional Memory via Scalable Lookup" they follow.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "engram_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+F32 = 0
+BF16 = 1
+
+_lib = None
+
+
+def build() -> str:
+    """Compile the oracle (gcc, -O2, one thread) and return the library path."""
+    tmp = _LIB + ".tmp"
+    subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall", "-Wextra",
+                           "-o", tmp, _SRC, "-lm"])
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32, i64 = ctypes.c_int32, ctypes.c_int64
+        L.oracle_compress.argtypes = [P, i64, P, i32, P]
+        L.oracle_compress.restype = i64
+        L.oracle_hash.argtypes = [P, i32, i64, i64, i64, P, i32, i32, i32, P, P, i32, P]
+        L.oracle_hash.restype = None
+        L.oracle_gather.argtypes = [P, i64, i32, P, i32, P]
+        L.oracle_gather.restype = None
+        L.oracle_gate.argtypes = [P, i64, i32, i32, P, P, P, P, P, ctypes.c_double, i32, P, P]
+        L.oracle_gate.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def compress(raw: np.ndarray, cmap: np.ndarray):
+    """Canonical ids (int32, same shape as raw; -1 where out of range) and the bad-id count."""
+    raw = np.ascontiguousarray(raw, dtype=np.int32)
+    cmap = np.ascontiguousarray(cmap, dtype=np.int32)
+    out = np.empty_like(raw)
+    bad = lib().oracle_compress(_p(raw), raw.size, _p(cmap), cmap.size, _p(out))
+    return out, int(bad)
+
+
+def hash_ids(ids: np.ndarray, orders: Sequence[int], heads: int, mult: np.ndarray,
+             rows: np.ndarray, pad_id: int, t_begin: int = 0, t_count: int | None = None):
+    """Hash indices [batch * t_count, len(orders) * heads] (int32) of positions
+    t_begin .. t_begin + t_count - 1 of every row of ids [batch, ld]."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    batch, ld = ids.shape
+    if t_count is None:
+        t_count = ld - t_begin
+    orders_a = np.ascontiguousarray(orders, dtype=np.int32)
+    mult = np.ascontiguousarray(mult, dtype=np.uint64)
+    rows = np.ascontiguousarray(rows, dtype=np.uint32)
+    n_tables = len(orders) * heads
+    assert mult.shape == (len(orders), heads, max(orders)) and rows.shape == (n_tables,)
+    idx = np.empty((batch * t_count, n_tables), dtype=np.int32)
+    lib().oracle_hash(_p(ids), batch, ld, t_begin, t_count, _p(orders_a), len(orders), heads,
+                      max(orders), _p(mult), _p(rows), pad_id, _p(idx))
+    return idx
+
+
+def gather(idx: np.ndarray, tables: Sequence[np.ndarray]):
+    """Concatenated rows [n_tok, n_tables * w] (dtype of the tables); bitwise copies."""
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    n_tok, n_tables = idx.shape
+    assert len(tables) == n_tables
+    tables = [np.ascontiguousarray(t) for t in tables]
+    row_bytes = tables[0].shape[1] * tables[0].itemsize
+    ptrs = (ctypes.c_void_p * n_tables)(*[t.ctypes.data for t in tables])
+    out = np.empty((n_tok, n_tables * tables[0].shape[1]), dtype=tables[0].dtype)
+    lib().oracle_gather(_p(idx), n_tok, n_tables, ptrs, row_bytes, _p(out))
+    return out
+
+
+def gate(mem: np.ndarray, h: np.ndarray, wk: np.ndarray, wv: np.ndarray, gq: np.ndarray,
+         gk: np.ndarray, eps: float, dtype: int):
+    """One gating branch: (out [n_tok, d_model] float64, alpha [n_tok] float64).
+
+    Arrays hold float32 values (dtype F32) or raw bfloat16 bits as uint16 (dtype BF16).
+    """
+    mem, h, wk, wv, gq, gk = (np.ascontiguousarray(a) for a in (mem, h, wk, wv, gq, gk))
+    n_tok, d_mem = mem.shape
+    d_model = h.shape[1]
+    assert h.shape[0] == n_tok and wk.shape == (d_model, d_mem) and wv.shape == (d_model, d_mem)
+    assert gq.shape == (d_model,) and gk.shape == (d_mem,)
+    want = np.float32 if dtype == F32 else np.uint16
+    for a in (mem, h, wk, wv, gq, gk):
+        assert a.dtype == want, a.dtype
+    out = np.empty((n_tok, d_model), dtype=np.float64)
+    alpha = np.empty(n_tok, dtype=np.float64)
+    lib().oracle_gate(_p(mem), n_tok, d_mem, d_model, _p(h), _p(wk), _p(wv), _p(gq), _p(gk),
+                      float(eps), dtype, _p(out), _p(alpha))
+    return out, alpha

@@ -1,0 +1,177 @@
+/*
+ * engram_oracle.c -- plain, single-threaded CPU oracle of the Engram forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or call
+ * this file: it exists so that tests, the smoke check and the benchmark's CPU
+ * baseline can compare the HIP library against an obviously correct definition.
+ * It shares no code, header, table or constant with the HIP library.
+ *
+ * Source of the method: "Conditional Memory via Scalable Lookup: A New Axis of
+ * Sparsity for Large Language Models" (DeepSeek-AI & Peking University), as
+ * translated on the pages studied, and the review page "Engram: LLM에 '기억의
+ * 서랍'을 달아주다" (koala.ai.kr), whose pseudocode gives the gate's order of
+ * operations.  Each function names the passage it follows.
+ *
+ * Readings of points the pages leave open (see the design notes):
+ *   - hash: z = (XOR_j  x'_{t-j} * c[n][k][j]  mod 2^64) mod M[n][k], one odd
+ *     64-bit multiplier per (order, head, position in the gram); positions
+ *     before the start of a sequence read the id `pad_id`;
+ *   - gate: key = W_K * RMSNorm(e) (normalised before the projection), the
+ *     scale is 1/sqrt(d_model), RMSNorm(x) = x / sqrt(mean(x^2) + eps) * gamma;
+ *   - the short causal convolution is not part of this path.
+ *
+ * Arithmetic: integers in uint64 with C's own '%' (no reduction tricks);
+ * floating point decoded exactly to double, accumulated in double, sigmoid as
+ * 1 / (1 + exp(-x)) in double.  Results are returned in double; callers round.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#define ORACLE_F32 0
+#define ORACLE_BF16 1
+
+/* Exact decode of one element of a float32 or bfloat16 array to double. */
+static double load_elem(const void* base, int64_t i, int dtype) {
+  if (dtype == ORACLE_F32) {
+    return (double)((const float*)base)[i];
+  }
+  uint16_t b = ((const uint16_t*)base)[i];
+  uint32_t u = (uint32_t)b << 16; /* bfloat16 is the top half of a float32 */
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/*
+ * Tokenizer compression (section 2.2, "tokenizer compression"): each raw id is
+ * replaced by its canonical id through the precomputed surjection P.
+ *   out[i] = map[raw[i]]   for 0 <= raw[i] < vocab,  else -1.
+ * Returns the number of out-of-range raw ids.
+ */
+int64_t oracle_compress(const int32_t* raw, int64_t n, const int32_t* map, int32_t vocab,
+                        int32_t* out) {
+  int64_t bad = 0;
+  for (int64_t i = 0; i < n; ++i) {
+    int32_t x = raw[i];
+    if (x >= 0 && x < vocab) {
+      out[i] = map[x];
+    } else {
+      out[i] = -1;
+      ++bad;
+    }
+  }
+  return bad;
+}
+
+/*
+ * Multi-head hashing of suffix n-grams (section 2.2, Eq. (1)).
+ * For every sequence b < batch, position t in [t_begin, t_begin + t_count),
+ * order index o (n = orders[o]) and head k < heads:
+ *   g_{t,n}   = (x'_{t-n+1}, ..., x'_t)              (suffix n-gram)
+ *   h         = XOR over j = 0..n-1 of ( x'_{t-j} * mult[o][k][j]  mod 2^64 )
+ *   z_{t,n,k} = h mod rows[o*heads + k]
+ * x'_{t-j} for t-j < 0 is pad_id.  ids is [batch][ld] row-major; mult is
+ * [n_orders][heads][max_order]; idx is [batch*t_count][n_orders*heads] with the
+ * column o*heads + k (order-major, head-minor, the concatenation order of Eq. (2)).
+ */
+void oracle_hash(const int32_t* ids, int32_t batch, int64_t ld, int64_t t_begin, int64_t t_count,
+                 const int32_t* orders, int32_t n_orders, int32_t heads, int32_t max_order,
+                 const uint64_t* mult, const uint32_t* rows, int32_t pad_id, int32_t* idx) {
+  const int32_t n_tables = n_orders * heads;
+  for (int32_t b = 0; b < batch; ++b) {
+    for (int64_t dt = 0; dt < t_count; ++dt) {
+      const int64_t t = t_begin + dt;
+      int32_t* row_out = idx + ((int64_t)b * t_count + dt) * n_tables;
+      for (int32_t o = 0; o < n_orders; ++o) {
+        const int32_t n = orders[o];
+        for (int32_t k = 0; k < heads; ++k) {
+          uint64_t h = 0;
+          for (int32_t j = 0; j < n; ++j) {
+            const int64_t pos = t - j;
+            const int32_t x = pos >= 0 ? ids[(int64_t)b * ld + pos] : pad_id;
+            const uint64_t c = mult[((int64_t)o * heads + k) * max_order + j];
+            h ^= (uint64_t)(uint32_t)x * c; /* unsigned wrap = mod 2^64 */
+          }
+          const uint64_t m = rows[o * heads + k];
+          row_out[o * heads + k] = (int32_t)(h % m);
+        }
+      }
+    }
+  }
+}
+
+/*
+ * Table lookup and concatenation (section 2.2, Eq. (1)-(2)):
+ *   e_t = concat over tables b (order-major, head-minor) of E_b[z_{t,b}].
+ * tables[b] points at a row-major [rows][row_bytes] array; the copy is bitwise.
+ */
+void oracle_gather(const int32_t* idx, int64_t n_tok, int32_t n_tables, const void* const* tables,
+                   int32_t row_bytes, void* out) {
+  for (int64_t t = 0; t < n_tok; ++t) {
+    for (int32_t b = 0; b < n_tables; ++b) {
+      const int64_t r = idx[t * n_tables + b];
+      const char* src = (const char*)tables[b] + r * (int64_t)row_bytes;
+      char* dst = (char*)out + (t * n_tables + b) * (int64_t)row_bytes;
+      memcpy(dst, src, (size_t)row_bytes);
+    }
+  }
+}
+
+/*
+ * Context-aware gating of one branch (section 2.3, Eq. (3)-(4), the gated value
+ * and the residual update; section 2.4, Eq. (6) for a branch m; the review
+ * page's context_aware_gating pseudocode for where the key's RMSNorm sits):
+ *   q     = RMSNorm_{gq}(h_t)
+ *   k     = W_K * RMSNorm_{gk}(e_t)
+ *   v     = W_V * e_t
+ *   alpha = sigmoid( q . k / sqrt(d_model) )
+ *   out   = h_t + alpha * v
+ * mem: [n_tok][d_mem]; h, out: [n_tok][d_model]; W_K, W_V: [d_model][d_mem]
+ * row-major (output x input); gq: [d_model]; gk: [d_mem]; all of `dtype`.
+ * out and alpha are double.  Returns 0.
+ */
+int oracle_gate(const void* mem, int64_t n_tok, int32_t d_mem, int32_t d_model, const void* h,
+                const void* wk, const void* wv, const void* gq, const void* gk, double eps,
+                int32_t dtype, double* out, double* alpha) {
+  for (int64_t t = 0; t < n_tok; ++t) {
+    /* RMSNorm of the memory vector and of the hidden state */
+    double ss_e = 0.0;
+    for (int32_t j = 0; j < d_mem; ++j) {
+      const double e = load_elem(mem, t * d_mem + j, dtype);
+      ss_e += e * e;
+    }
+    const double rms_e = sqrt(ss_e / d_mem + eps);
+    double ss_h = 0.0;
+    for (int32_t i = 0; i < d_model; ++i) {
+      const double x = load_elem(h, t * d_model + i, dtype);
+      ss_h += x * x;
+    }
+    const double rms_h = sqrt(ss_h / d_model + eps);
+
+    /* logit = sum_i q_i * k_i */
+    double logit = 0.0;
+    for (int32_t i = 0; i < d_model; ++i) {
+      double k = 0.0;
+      for (int32_t j = 0; j < d_mem; ++j) {
+        const double en = load_elem(mem, t * d_mem + j, dtype) / rms_e * load_elem(gk, j, dtype);
+        k += load_elem(wk, (int64_t)i * d_mem + j, dtype) * en;
+      }
+      const double q = load_elem(h, t * d_model + i, dtype) / rms_h * load_elem(gq, i, dtype);
+      logit += q * k;
+    }
+    logit /= sqrt((double)d_model);
+    const double a = 1.0 / (1.0 + exp(-logit));
+    alpha[t] = a;
+
+    /* value projection and residual update */
+    for (int32_t i = 0; i < d_model; ++i) {
+      double v = 0.0;
+      for (int32_t j = 0; j < d_mem; ++j) {
+        v += load_elem(wv, (int64_t)i * d_mem + j, dtype) * load_elem(mem, t * d_mem + j, dtype);
+      }
+      out[t * d_model + i] = load_elem(h, t * d_model + i, dtype) + a * v;
+    }
+  }
+  return 0;
+}
