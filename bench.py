@@ -1,0 +1,212 @@
+#!/usr/bin/env python3
+"""Throughput of the Engram forward pass (compress -> hash -> gather -> gate) on one MI355X.
+
+One step = one pass of the whole path over one batch of seeded synthetic input
+already resident in HBM: the "small" workload (4 x 4096 Zipf(1.1) tokens, 16
+bf16 tables of 1,000,003 x 80, memory dim 1280, d_model 2560, one branch).
+Prints ONE JSON line with tokens/s, the per-call breakdown, the roofline of the
+dominant kernel (the gate) and the CPU oracle's tokens/s on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--config small|multi|large|tiny]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Engram tokens/s (hash+gather+gate); gather HBM GB/s & MFMA util vs peak"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3       # fp32 vector / matrix
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__)
+    p.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", default="small")
+    p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time of the CPU baseline")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+def workload_desc(cfg):
+    return {
+        "workload": cfg.name,
+        "tokens": cfg.tokens, "batch": cfg.batch, "seq_len": cfg.seq,
+        "tables": f"{cfg.n_tables} x {cfg.rows} x {cfg.w} {cfg.dtype}",
+        "orders": list(cfg.orders), "heads": cfg.heads, "d_mem": cfg.d_mem, "d_model": cfg.d_model,
+        "branches": cfg.n_branch, "zipf_s": cfg.zipf_s, "parallelism": "single GPU",
+    }
+
+
+def algorithmic(cfg):
+    """Algorithmic work of one step, per call (bytes moved to/from HBM, flops)."""
+    T, nt, dm, d, M = cfg.tokens, cfg.n_tables, cfg.d_mem, cfg.d_model, cfg.n_branch
+    es = 4 if cfg.dtype == "f32" else 2
+    return {
+        "compress": {"bytes": 8 * T},
+        "hash": {"bytes": 4 * T + 4 * nt * T},
+        "gather": {"bytes": 4 * nt * T + 2 * dm * es * T},
+        # weights once, memory vector once, hidden read + output written per branch
+        "gate": {"flops": 4 * dm * d * M * T,
+                 "bytes": dm * es * T + M * (2 * d * dm * es + 2 * d * es * T)},
+    }
+
+
+def cpu_baseline(cfg, target_s):
+    """The oracle (single thread) on the first tokens of sequence 0: compress, hash,
+    gather and gate.  Table rows are regenerated outside the timed region."""
+    import numpy as np
+    import torch
+    import oracle
+    import synth
+
+    def host_view(t):
+        t = t.contiguous()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+    raw = synth.raw_ids(cfg)
+    cmap = synth.comp_map(cfg)
+    mult, rows = synth.multipliers(cfg), synth.table_rows_u32(cfg)
+    wts = [synth.weights(cfg, m) for m in range(cfg.n_branch)]
+    gns = [synth.gains(cfg, m) for m in range(cfg.n_branch)]
+    wts = [(host_view(a), host_view(b)) for a, b in wts]
+    gns = [(host_view(a), host_view(b)) for a, b in gns]
+    dt = oracle.F32 if cfg.dtype == "f32" else oracle.BF16
+
+    def run(n):
+        seq = raw[:1, :n]
+        t0 = time.perf_counter()
+        ids, _ = oracle.compress(seq, cmap)
+        idx = oracle.hash_ids(ids, cfg.orders, cfg.heads, mult, rows, cfg.vocab_c)
+        t_int = time.perf_counter() - t0
+        subs, remap = [], np.empty_like(idx)
+        for b in range(cfg.n_tables):   # input generation: not timed
+            uniq, inv = np.unique(idx[:, b], return_inverse=True)
+            subs.append(host_view(synth.table_rows(cfg, b, torch.from_numpy(uniq.astype(np.int64)))))
+            remap[:, b] = inv
+        h = [host_view(synth.hidden_rows(cfg, m, torch.arange(n))) for m in range(cfg.n_branch)]
+        t1 = time.perf_counter()
+        e = oracle.gather(remap, subs)
+        for m in range(cfg.n_branch):
+            oracle.gate(e, h[m], wts[m][0], wts[m][1], gns[m][0], gns[m][1], cfg.eps, dt)
+        return t_int + time.perf_counter() - t1
+
+    probe = 8
+    t = run(probe)
+    n = int(max(probe, min(cfg.seq, probe * target_s / max(t, 1e-9))))
+    t = run(n)
+    return {"value": n / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} tokens of sequence 0 of the {cfg.name} workload: compress, hash, "
+                      f"gather and all {cfg.n_branch} gate branch(es), one thread, {t:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": f"--gpus {args.gpus}: this benchmark runs on exactly one GPU; "
+                                   "the Engram path here is single-GPU (no multi-GPU runs)"}))
+        sys.exit(2)
+
+    import torch
+    import synth
+    import hashed_gram_embedding_hash_amd as eg
+    from hashed_gram_embedding_hash_amd.pipeline import EngramLayer
+
+    cfg = synth.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    print(f"[bench] building inputs for {cfg.name}", file=sys.stderr, flush=True)
+    inp = synth.device_inputs(cfg, dev)
+    layer = EngramLayer(inp["map"], cfg.orders, cfg.heads, inp["mult"], inp["tables"], inp["wk"], inp["wv"],
+                        inp["gq"], inp["gk"], cfg.eps, pad_id=cfg.vocab_c)
+    outs = [torch.empty_like(h) for h in inp["h"]]
+    bufs = layer.buffers(cfg.batch, cfg.seq)
+    raw, h = inp["raw"], inp["h"]
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        eg.engram_compress(raw, layer.cmap, out=bufs["ids"])
+        if ev is not None:
+            ev[1].record()
+        eg.engram_hash(bufs["ids"], layer.orders, layer.heads, layer.mult, layer.rows, layer.pad_id,
+                       out=bufs["idx"])
+        if ev is not None:
+            ev[2].record()
+        eg.engram_gather(bufs["idx"], layer.tables, out=bufs["mem"])
+        if ev is not None:
+            ev[3].record()
+        eg.engram_gate_forward(bufs["mem"], h, layer.wk, layer.wv, layer.gq, layer.gk, cfg.eps, out=outs)
+        if ev is not None:
+            ev[4].record()
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = evs[0][0].elapsed_time(evs[-1][4])
+    ms_step = total_ms / args.steps
+    names = ["compress", "hash", "gather", "gate"]
+    per = {n: sum(evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(args.steps)) / args.steps
+           for k, n in enumerate(names)}
+
+    work = algorithmic(cfg)
+    kernels = {}
+    for n in names:
+        s = per[n] * 1e-3
+        d = {"ms": round(per[n], 5)}
+        if "bytes" in work[n]:
+            d["GB/s"] = round(work[n]["bytes"] / s / 1e9, 1)
+            d["hbm_frac"] = round(work[n]["bytes"] / s / 1e9 / PEAK_HBM_GBS, 4)
+        if "flops" in work[n]:
+            d["TFLOP/s"] = round(work[n]["flops"] / s / 1e12, 2)
+        kernels[n] = d
+    gate_s = per["gate"] * 1e-3
+    if cfg.dtype == "bf16":
+        peak, dtype = PEAK_BF16_TFLOPS, "bf16"
+    else:
+        peak, dtype = PEAK_FP32_TFLOPS, "f32"
+    achieved = work["gate"]["flops"] / gate_s / 1e12
+    roofline = {"kernel": "engram_gate_forward (scale_cols + gate_mfma<K> + gate_mfma<V>)",
+                "bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None,
+                "flops_per_launch": work["gate"]["flops"], "avg_ms": round(per["gate"], 5)}
+
+    result = {
+        "metric": METRIC,
+        "value": round(cfg.tokens / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": dtype, "data": "synthetic (seeded Zipf ids, counter-generated tables/weights/hidden)",
+        "config": workload_desc(cfg),
+        "wall_s_timed": round(t_wall, 4),
+        "kernels": kernels,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,255 @@
+"""Engram forward pass on AMD Instinct MI355X: Python binding of libengram.so.
+
+The work happens in the HIP kernels behind the C ABI declared in
+``include/engram.h``; this module only marshals arguments (torch tensors give
+device memory and stream handles) and turns non-OK statuses into exceptions.
+The functions carry the C names:
+
+* ``engram_compress``  -- tokenizer compression lookup ("Conditional Memory via
+  Scalable Lookup", section 2.2);
+* ``engram_hash``      -- multi-head multiply-XOR hashing of suffix n-grams
+  (section 2.2, Eq. 1);
+* ``engram_gather``    -- table lookup and concatenation (Eq. 1-2);
+* ``engram_gate_forward`` -- context-aware gating and residual update
+  (section 2.3, Eq. 3-4; section 2.4, Eq. 6 for several branches);
+* ``engram_prefetch_host`` -- the same gather from pinned host-memory tables
+  over PCIe (section 2.5, Figure 2(b); section 6.4).
+
+There is no fallback: if the library is missing or fails to load, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libengram.so")
+
+F32 = 0
+BF16 = 1
+MAX_TABLES = 32
+MAX_ORDER = 4
+MAX_BRANCHES = 8
+
+_STATUS = {0: "ENGRAM_OK", 1: "ENGRAM_ERR_INVALID_ARG", 2: "ENGRAM_ERR_UNSUPPORTED", 3: "ENGRAM_ERR_HIP"}
+
+# names exported by include/engram.h
+EXPORTS = (
+    "engram_last_error", "engram_version", "engram_compress", "engram_hash", "engram_gather",
+    "engram_gate_forward", "engram_prefetch_host", "engram_host_alloc", "engram_host_free",
+)
+
+
+class EngramError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libengram.so (built by ``build.build()``); raises if it is absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m hashed_gram_embedding_hash_amd.build`")
+        # torch first, so the library binds to the HIP runtime torch already loaded
+        import torch  # noqa: F401
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, i64, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64
+        st = ctypes.c_int
+        L.engram_last_error.restype = ctypes.c_char_p
+        L.engram_last_error.argtypes = []
+        L.engram_version.restype = ctypes.c_char_p
+        L.engram_version.argtypes = []
+        L.engram_compress.argtypes = [P, i64, P, i32, P, P, P]
+        L.engram_hash.argtypes = [P, i32, i64, i64, i64, P, i32, i32, P, P, i32, P, P]
+        L.engram_gather.argtypes = [P, i64, i32, P, P, i32, i32, P, P, P]
+        L.engram_gate_forward.argtypes = [P, i64, i32, i32, i32, P, P, P, P, P, ctypes.c_float, i32,
+                                          P, P, P]
+        L.engram_prefetch_host.argtypes = [P, i64, i32, P, P, i32, i32, P, P, P]
+        L.engram_host_alloc.argtypes = [ctypes.c_size_t, ctypes.POINTER(ctypes.c_void_p)]
+        L.engram_host_free.argtypes = [P]
+        for f in ("engram_compress", "engram_hash", "engram_gather", "engram_gate_forward",
+                  "engram_prefetch_host", "engram_host_alloc", "engram_host_free"):
+            getattr(L, f).restype = st
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise EngramError(status, lib().engram_last_error().decode())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t, name: str, dtype=None):
+    import torch
+    if not torch.is_tensor(t) or not t.is_cuda:
+        raise TypeError(f"{name}: expected a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _opt(t, name, dtype=None):
+    return ctypes.c_void_p(0) if t is None else _dev(t, name, dtype)
+
+
+def _edtype(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr_array(ptrs: Sequence[int]):
+    return (ctypes.c_void_p * len(ptrs))(*ptrs)
+
+
+def version() -> str:
+    return lib().engram_version().decode()
+
+
+# ---------------------------------------------------------------------------
+def engram_compress(raw, cmap, out=None, err_count=None, stream=None):
+    """out[i] = cmap[raw[i]] (or -1 for an out-of-range id, counted in err_count)."""
+    import torch
+    if out is None:
+        out = torch.empty_like(raw)
+    _check(lib().engram_compress(_dev(raw, "raw", torch.int32), raw.numel(), _dev(cmap, "map", torch.int32),
+                                 cmap.numel(), _dev(out, "out", torch.int32),
+                                 _opt(err_count, "err_count", torch.int32), _stream(stream)))
+    return out
+
+
+def engram_hash(ids, orders: Sequence[int], heads: int, mult, rows, pad_id: int, t_begin: int = 0,
+                t_count: Optional[int] = None, out=None, stream=None):
+    """Hash indices [batch * t_count, len(orders) * heads] (int32) of ids [batch, ld].
+
+    ``mult``: uint64 array-like [n_orders][heads][max(orders)] (host); ``rows``:
+    per-table sizes (host)."""
+    import numpy as np
+    import torch
+    batch, ld = ids.shape
+    if t_count is None:
+        t_count = ld - t_begin
+    orders_a = np.ascontiguousarray(orders, dtype=np.int32)
+    mult_a = np.ascontiguousarray(mult, dtype=np.uint64)
+    rows_a = np.ascontiguousarray(rows, dtype=np.uint32)
+    n_tables = len(orders) * heads
+    if mult_a.shape != (len(orders), heads, max(orders)) or rows_a.shape != (n_tables,):
+        raise ValueError("mult must be [n_orders][heads][max_order] and rows [n_tables]")
+    if out is None:
+        out = torch.empty((batch * t_count, n_tables), dtype=torch.int32, device=ids.device)
+    _check(lib().engram_hash(_dev(ids, "ids", torch.int32), batch, ld, t_begin, t_count,
+                             orders_a.ctypes.data, len(orders), heads, mult_a.ctypes.data,
+                             rows_a.ctypes.data, pad_id, _dev(out, "idx", torch.int32), _stream(stream)))
+    return out
+
+
+def engram_gather(idx, tables: Sequence, out=None, err_count=None, stream=None):
+    """Concatenated rows [n_tok, n_tables * w]; tables: GPU tensors [rows_b, w] of one dtype."""
+    import numpy as np
+    import torch
+    n_tok, n_tables = idx.shape
+    w = tables[0].shape[1]
+    dt = tables[0].dtype
+    for t in tables:
+        if t.shape[1] != w or t.dtype != dt:
+            raise ValueError("all tables need the same width and dtype")
+        _dev(t, "table")
+    ptrs = _ptr_array([t.data_ptr() for t in tables])
+    rows = np.array([t.shape[0] for t in tables], dtype=np.int64)
+    if out is None:
+        out = torch.empty((n_tok, n_tables * w), dtype=dt, device=idx.device)
+    _check(lib().engram_gather(_dev(idx, "idx", torch.int32), n_tok, n_tables, ptrs, rows.ctypes.data, w,
+                               _edtype(tables[0]), _dev(out, "out", dt), _opt(err_count, "err_count", torch.int32),
+                               _stream(stream)))
+    return out
+
+
+def engram_gate_forward(mem, h: Sequence, wk: Sequence, wv: Sequence, gq: Sequence, gk: Sequence,
+                        eps: float = 1e-6, out: Optional[Sequence] = None, gate_out=None, stream=None):
+    """out[m] = h[m] + sigmoid(RMSNorm(h[m]) . W_K[m] RMSNorm(mem) / sqrt(d)) * W_V[m] mem.
+
+    Lists hold one tensor per branch; ``out`` defaults to new tensors (pass ``h``
+    for in-place).  ``gate_out``: optional float32 [n_branch, n_tok] for alpha."""
+    import torch
+    n_tok, d_mem = mem.shape
+    nb = len(h)
+    d_model = h[0].shape[1]
+    dt = mem.dtype
+    _dev(mem, "mem", dt)
+    if out is None:
+        out = [torch.empty_like(x) for x in h]
+    if not (len(wk) == len(wv) == len(gq) == len(gk) == len(out) == nb):
+        raise ValueError("one h/wk/wv/gq/gk/out per branch")
+    for name, seq in (("h", h), ("wk", wk), ("wv", wv), ("gq", gq), ("gk", gk), ("out", out)):
+        for x in seq:
+            _dev(x, name, dt)
+    for x in list(h) + list(out):
+        if tuple(x.shape) != (n_tok, d_model):
+            raise ValueError("h/out must be [n_tok, d_model]")
+    for x in list(wk) + list(wv):
+        if tuple(x.shape) != (d_model, d_mem):
+            raise ValueError("weights must be [d_model, d_mem]")
+    arr = lambda seq: _ptr_array([x.data_ptr() for x in seq])
+    _check(lib().engram_gate_forward(mem.data_ptr(), n_tok, d_mem, d_model, nb, arr(h), arr(wk), arr(wv),
+                                     arr(gq), arr(gk), float(eps), _edtype(mem), arr(out),
+                                     _opt(gate_out, "gate_out", torch.float32), _stream(stream)))
+    return out
+
+
+def engram_prefetch_host(idx, host_tables: Sequence, rows: Sequence[int], w: int, dtype, staging=None,
+                         err_count=None, stream=None):
+    """Gather from pinned host tables into the device buffer ``staging`` [n_tok, n_tables * w].
+
+    ``host_tables``: pinned CPU tensors, or integer addresses from ``host_alloc``."""
+    import numpy as np
+    import torch
+    n_tok, n_tables = idx.shape
+    ptrs = []
+    for t in host_tables:
+        if torch.is_tensor(t):
+            if t.is_cuda or not t.is_pinned():
+                raise ValueError("host tables must be pinned host memory")
+            ptrs.append(t.data_ptr())
+        else:
+            ptrs.append(int(t))
+    rows_a = np.ascontiguousarray(rows, dtype=np.int64)
+    if staging is None:
+        staging = torch.empty((n_tok, n_tables * w), dtype=dtype, device=idx.device)
+    _check(lib().engram_prefetch_host(_dev(idx, "idx", torch.int32), n_tok, n_tables, _ptr_array(ptrs),
+                                      rows_a.ctypes.data, w, BF16 if dtype == torch.bfloat16 else F32,
+                                      _dev(staging, "staging", dtype), _opt(err_count, "err_count", torch.int32),
+                                      _stream(stream)))
+    return staging
+
+
+def host_alloc(nbytes: int) -> int:
+    """Pinned, device-mapped host allocation (hipHostMalloc); returns the address."""
+    p = ctypes.c_void_p()
+    _check(lib().engram_host_alloc(nbytes, ctypes.byref(p)))
+    return p.value
+
+
+def host_free(addr: int):
+    _check(lib().engram_host_free(ctypes.c_void_p(addr)))

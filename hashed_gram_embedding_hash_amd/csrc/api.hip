@@ -1,0 +1,304 @@
+// api.hip -- the C ABI of include/engram.h: argument validation, error
+// reporting and kernel launches.  Every check happens on the host before
+// anything is enqueued, so a non-OK status never leaves partial work behind.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+
+#include "engram_internal.h"
+
+namespace engram {
+
+static thread_local char g_err[512];
+
+engram_status fail(engram_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+engram_status hip_fail(hipError_t e, const char* what) {
+  return fail(ENGRAM_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+engram_status check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, what);
+  return ENGRAM_OK;
+}
+
+}  // namespace engram
+
+using namespace engram;
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+size_t dtype_size(engram_dtype dt) { return dt == ENGRAM_F32 ? 4 : 2; }
+
+bool valid_dtype(engram_dtype dt) { return dt == ENGRAM_F32 || dt == ENGRAM_BF16; }
+
+// Shared validation of engram_gather / engram_prefetch_host.
+engram_status check_gather(const char* fn, const int32_t* idx, int64_t n_tok, int32_t n_tables,
+                           const void* const* tables, const int64_t* rows, int32_t w,
+                           engram_dtype dtype, void* out) {
+  if (n_tok < 0) return fail(ENGRAM_ERR_INVALID_ARG, "%s: n_tok < 0", fn);
+  if (n_tables <= 0 || n_tables > ENGRAM_MAX_TABLES)
+    return fail(ENGRAM_ERR_INVALID_ARG, "%s: n_tables %d not in [1, %d]", fn, n_tables,
+                ENGRAM_MAX_TABLES);
+  if (!valid_dtype(dtype)) return fail(ENGRAM_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+  if (w <= 0) return fail(ENGRAM_ERR_INVALID_ARG, "%s: w must be positive", fn);
+  if (tables == nullptr || rows == nullptr)
+    return fail(ENGRAM_ERR_INVALID_ARG, "%s: null tables or rows array", fn);
+  const int64_t row_bytes = (int64_t)w * (int64_t)dtype_size(dtype);
+  if (row_bytes % 16 != 0)
+    return fail(ENGRAM_ERR_UNSUPPORTED, "%s: row bytes %lld not a multiple of 16", fn,
+                (long long)row_bytes);
+  if ((row_bytes / 16) * n_tables > 1024)
+    return fail(ENGRAM_ERR_UNSUPPORTED, "%s: concatenated row of %lld bytes exceeds 16 KiB", fn,
+                (long long)(row_bytes * n_tables));
+  for (int b = 0; b < n_tables; ++b) {
+    if (rows[b] <= 0) return fail(ENGRAM_ERR_INVALID_ARG, "%s: rows[%d] must be positive", fn, b);
+    if (tables[b] == nullptr || !aligned(tables[b], 16))
+      return fail(ENGRAM_ERR_INVALID_ARG, "%s: table %d null or not 16-byte aligned", fn, b);
+  }
+  if (n_tok > 0 && (idx == nullptr || out == nullptr || !aligned(out, 16) || !aligned(idx, 4)))
+    return fail(ENGRAM_ERR_INVALID_ARG, "%s: null or misaligned idx/out", fn);
+  return ENGRAM_OK;
+}
+
+// Device address of a pinned host allocation, or nullptr if `p` is not one.
+const void* mapped_host_pointer(const void* p) {
+  hipPointerAttribute_t attr;
+  memset(&attr, 0, sizeof attr);
+  if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+    (void)hipGetLastError();  // clear the sticky lookup error
+    return nullptr;
+  }
+  if (attr.type != hipMemoryTypeHost || attr.devicePointer == nullptr) return nullptr;
+  // devicePointer/hostPointer describe the allocation containing p
+  const char* hb = (const char*)attr.hostPointer;
+  const char* db = (const char*)attr.devicePointer;
+  if (hb == nullptr) return db;
+  return db + ((const char*)p - hb);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* engram_last_error(void) { return g_err; }
+
+const char* engram_version(void) { return "engram-mi355x 0.1.0 (gfx950)"; }
+
+engram_status engram_compress(const int32_t* raw, int64_t n, const int32_t* map, int32_t vocab,
+                              int32_t* out, int32_t* err_count, hipStream_t stream) {
+  if (n < 0) return fail(ENGRAM_ERR_INVALID_ARG, "engram_compress: n < 0");
+  if (vocab <= 0) return fail(ENGRAM_ERR_INVALID_ARG, "engram_compress: vocab must be positive");
+  if (map == nullptr) return fail(ENGRAM_ERR_INVALID_ARG, "engram_compress: null map");
+  if (n == 0) return ENGRAM_OK;
+  if (raw == nullptr || out == nullptr)
+    return fail(ENGRAM_ERR_INVALID_ARG, "engram_compress: null raw/out");
+  launch_compress(raw, n, map, vocab, out, err_count, stream);
+  return check_launch("engram_compress");
+}
+
+engram_status engram_hash(const int32_t* ids, int32_t batch, int64_t ld, int64_t t_begin,
+                          int64_t t_count, const int32_t* orders, int32_t n_orders, int32_t heads,
+                          const uint64_t* mult, const uint32_t* rows, int32_t pad_id, int32_t* idx,
+                          hipStream_t stream) {
+  const char* fn = "engram_hash";
+  if (batch < 0 || ld < 0 || t_begin < 0 || t_count < 0)
+    return fail(ENGRAM_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (t_begin + t_count > ld)
+    return fail(ENGRAM_ERR_INVALID_ARG, "%s: window [%lld, %lld) exceeds row length %lld", fn,
+                (long long)t_begin, (long long)(t_begin + t_count), (long long)ld);
+  if (orders == nullptr || mult == nullptr || rows == nullptr)
+    return fail(ENGRAM_ERR_INVALID_ARG, "%s: null orders/mult/rows", fn);
+  if (n_orders <= 0 || heads <= 0 || (int64_t)n_orders * heads > ENGRAM_MAX_TABLES)
+    return fail(ENGRAM_ERR_INVALID_ARG, "%s: n_orders*heads must be in [1, %d]", fn,
+                ENGRAM_MAX_TABLES);
+  int max_order = 0;
+  for (int o = 0; o < n_orders; ++o) {
+    if (orders[o] < 1 || orders[o] > ENGRAM_MAX_ORDER)
+      return fail(ENGRAM_ERR_INVALID_ARG, "%s: orders[%d] = %d not in [1, %d]", fn, o, orders[o],
+                  ENGRAM_MAX_ORDER);
+    if (orders[o] > max_order) max_order = orders[o];
+  }
+  HashArgs a;
+  memset(&a, 0, sizeof a);
+  const int nt = n_orders * heads;
+  for (int o = 0; o < n_orders; ++o) {
+    for (int k = 0; k < heads; ++k) {
+      const int tb = o * heads + k;
+      const uint32_t M = rows[tb];
+      if (M == 0 || M >= (1u << 31))
+        return fail(ENGRAM_ERR_INVALID_ARG, "%s: rows[%d] = %u not in [1, 2^31)", fn, tb, M);
+      a.rows[tb] = M;
+      a.barrett[tb] = ~0ull / M;
+      a.order[tb] = orders[o];
+      for (int j = 0; j < orders[o]; ++j) a.mult[tb][j] = mult[((int64_t)o * heads + k) * max_order + j];
+    }
+  }
+  if (batch == 0 || t_count == 0) return ENGRAM_OK;
+  if (ids == nullptr || idx == nullptr) return fail(ENGRAM_ERR_INVALID_ARG, "%s: null ids/idx", fn);
+  const uint64_t blocks = (uint64_t)((t_count + 63) / 64) * (uint64_t)batch;
+  if (blocks >= (1ull << 31))
+    return fail(ENGRAM_ERR_UNSUPPORTED, "%s: %llu workgroups exceed one launch", fn,
+                (unsigned long long)blocks);
+  a.ids = ids;
+  a.idx = idx;
+  a.ld = ld;
+  a.t_begin = t_begin;
+  a.t_count = t_count;
+  a.n_tables = nt;
+  a.max_order = max_order;
+  a.pad_id = pad_id;
+  a.batch = batch;
+  launch_hash(a, stream);
+  return check_launch(fn);
+}
+
+engram_status engram_gather(const int32_t* idx, int64_t n_tok, int32_t n_tables,
+                            const void* const* tables, const int64_t* rows, int32_t w,
+                            engram_dtype dtype, void* out, int32_t* err_count, hipStream_t stream) {
+  const engram_status st = check_gather("engram_gather", idx, n_tok, n_tables, tables, rows, w, dtype, out);
+  if (st != ENGRAM_OK) return st;
+  if (n_tok == 0) return ENGRAM_OK;
+  GatherArgs a;
+  memset(&a, 0, sizeof a);
+  for (int b = 0; b < n_tables; ++b) {
+    a.table[b] = (const char*)tables[b];
+    a.rows[b] = rows[b];
+  }
+  a.idx = idx;
+  a.out = (char*)out;
+  a.err_count = err_count;
+  a.n_tok = n_tok;
+  a.n_tables = n_tables;
+  a.chunks_per_row = (int32_t)(w * dtype_size(dtype) / 16);
+  launch_gather(a, false, stream);
+  return check_launch("engram_gather");
+}
+
+engram_status engram_prefetch_host(const int32_t* idx, int64_t n_tok, int32_t n_tables,
+                                   const void* const* host_tables, const int64_t* rows, int32_t w,
+                                   engram_dtype dtype, void* staging, int32_t* err_count,
+                                   hipStream_t stream) {
+  const char* fn = "engram_prefetch_host";
+  const engram_status st = check_gather(fn, idx, n_tok, n_tables, host_tables, rows, w, dtype, staging);
+  if (st != ENGRAM_OK) return st;
+  GatherArgs a;
+  memset(&a, 0, sizeof a);
+  for (int b = 0; b < n_tables; ++b) {
+    const void* d = mapped_host_pointer(host_tables[b]);
+    if (d == nullptr)
+      return fail(ENGRAM_ERR_INVALID_ARG, "%s: table %d is not pinned, device-mapped host memory", fn, b);
+    a.table[b] = (const char*)d;
+    a.rows[b] = rows[b];
+  }
+  if (n_tok == 0) return ENGRAM_OK;
+  a.idx = idx;
+  a.out = (char*)staging;
+  a.err_count = err_count;
+  a.n_tok = n_tok;
+  a.n_tables = n_tables;
+  a.chunks_per_row = (int32_t)(w * dtype_size(dtype) / 16);
+  launch_gather(a, true, stream);
+  return check_launch(fn);
+}
+
+engram_status engram_gate_forward(const void* mem, int64_t n_tok, int32_t d_mem, int32_t d_model,
+                                  int32_t n_branch, const void* const* h, const void* const* wk,
+                                  const void* const* wv, const void* const* gq,
+                                  const void* const* gk, float eps, engram_dtype dtype,
+                                  void* const* out, float* gate_out, hipStream_t stream) {
+  const char* fn = "engram_gate_forward";
+  if (n_tok < 0 || d_mem <= 0 || d_model <= 0)
+    return fail(ENGRAM_ERR_INVALID_ARG, "%s: bad sizes n_tok=%lld d_mem=%d d_model=%d", fn,
+                (long long)n_tok, d_mem, d_model);
+  if (n_branch <= 0 || n_branch > ENGRAM_MAX_BRANCHES)
+    return fail(ENGRAM_ERR_INVALID_ARG, "%s: n_branch %d not in [1, %d]", fn, n_branch,
+                ENGRAM_MAX_BRANCHES);
+  if (!valid_dtype(dtype)) return fail(ENGRAM_ERR_INVALID_ARG, "%s: unknown dtype", fn);
+  if (!(eps >= 0.f)) return fail(ENGRAM_ERR_INVALID_ARG, "%s: eps must be >= 0", fn);
+  if (h == nullptr || wk == nullptr || wv == nullptr || gq == nullptr || gk == nullptr || out == nullptr)
+    return fail(ENGRAM_ERR_INVALID_ARG, "%s: null pointer array", fn);
+  if (dtype == ENGRAM_BF16 && (d_mem % 64 != 0 || d_model % 32 != 0))
+    return fail(ENGRAM_ERR_UNSUPPORTED, "%s: bf16 needs d_mem %% 64 == 0 and d_model %% 32 == 0 (got %d, %d)",
+                fn, d_mem, d_model);
+  if (n_tok > 0x7fffffffLL) return fail(ENGRAM_ERR_UNSUPPORTED, "%s: n_tok >= 2^31", fn);
+  const size_t al = dtype == ENGRAM_BF16 ? 16 : 4;
+  if (n_tok > 0 && (mem == nullptr || !aligned(mem, al)))
+    return fail(ENGRAM_ERR_INVALID_ARG, "%s: null or misaligned mem", fn);
+  if (gate_out != nullptr && !aligned(gate_out, 4))
+    return fail(ENGRAM_ERR_INVALID_ARG, "%s: misaligned gate_out", fn);
+  GateArgs a;
+  memset(&a, 0, sizeof a);
+  for (int m = 0; m < n_branch; ++m) {
+    if (wk[m] == nullptr || wv[m] == nullptr || gq[m] == nullptr || gk[m] == nullptr ||
+        !aligned(wk[m], al) || !aligned(wv[m], al) || !aligned(gq[m], al) || !aligned(gk[m], al))
+      return fail(ENGRAM_ERR_INVALID_ARG, "%s: branch %d: null or misaligned weights/gains", fn, m);
+    if (n_tok > 0 && (h[m] == nullptr || out[m] == nullptr || !aligned(h[m], al) || !aligned(out[m], al)))
+      return fail(ENGRAM_ERR_INVALID_ARG, "%s: branch %d: null or misaligned h/out", fn, m);
+    a.h[m] = h[m];
+    a.wk[m] = wk[m];
+    a.wv[m] = wv[m];
+    a.gq[m] = gq[m];
+    a.gk[m] = gk[m];
+    a.out[m] = out[m];
+  }
+  if (n_tok == 0) return ENGRAM_OK;
+  a.mem = mem;
+  a.gate_out = gate_out;
+  a.n_tok = n_tok;
+  a.d_mem = d_mem;
+  a.d_model = d_model;
+  a.n_branch = n_branch;
+  a.eps = eps;
+  a.inv_sqrt_d = 1.0f / sqrtf((float)d_model);
+
+  if (dtype == ENGRAM_F32) {
+    if ((size_t)d_mem * 4 > 64 * 1024)
+      return fail(ENGRAM_ERR_UNSUPPORTED, "%s: fp32 path needs d_mem <= 16384", fn);
+    launch_gate_f32(a, stream);
+    return check_launch(fn);
+  }
+
+  const size_t bytes = gate_bf16_scratch_bytes(a);
+  void* scratch = nullptr;
+  hipError_t e = hipMallocAsync(&scratch, bytes, stream);
+  if (e != hipSuccess) return hip_fail(e, "engram_gate_forward: hipMallocAsync(scratch)");
+  a.part_dot = (float*)scratch;
+  launch_gate_bf16(a, stream);
+  const engram_status st = check_launch(fn);
+  e = hipFreeAsync(scratch, stream);
+  if (st != ENGRAM_OK) return st;
+  if (e != hipSuccess) return hip_fail(e, "engram_gate_forward: hipFreeAsync(scratch)");
+  return ENGRAM_OK;
+}
+
+engram_status engram_host_alloc(size_t bytes, void** ptr) {
+  if (ptr == nullptr) return fail(ENGRAM_ERR_INVALID_ARG, "engram_host_alloc: null ptr");
+  *ptr = nullptr;
+  if (bytes == 0) return fail(ENGRAM_ERR_INVALID_ARG, "engram_host_alloc: zero bytes");
+  const hipError_t e = hipHostMalloc(ptr, bytes, hipHostMallocMapped | hipHostMallocPortable);
+  if (e != hipSuccess) {
+    *ptr = nullptr;
+    return hip_fail(e, "engram_host_alloc: hipHostMalloc");
+  }
+  return ENGRAM_OK;
+}
+
+engram_status engram_host_free(void* ptr) {
+  if (ptr == nullptr) return ENGRAM_OK;
+  const hipError_t e = hipHostFree(ptr);
+  if (e != hipSuccess) return hip_fail(e, "engram_host_free: hipHostFree");
+  return ENGRAM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// engram_internal.h -- shared declarations of the HIP library (kernels + C ABI).
+// gfx950 only.  Nothing here is visible through include/engram.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/engram.h"
+
+namespace engram {
+
+// ---------------------------------------------------------------- errors
+engram_status fail(engram_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+engram_status hip_fail(hipError_t e, const char* what);
+// Status of the last launch on this thread (hipGetLastError), mapped to engram_status.
+engram_status check_launch(const char* what);
+
+// ---------------------------------------------------------------- compress
+void launch_compress(const int32_t* raw, int64_t n, const int32_t* map, int32_t vocab, int32_t* out,
+                     int32_t* err_count, hipStream_t s);
+
+// ---------------------------------------------------------------- hash
+struct HashArgs {
+  uint64_t mult[ENGRAM_MAX_TABLES][ENGRAM_MAX_ORDER];  // per table, per position in the gram
+  uint64_t barrett[ENGRAM_MAX_TABLES];                  // floor((2^64 - 1) / rows)
+  uint32_t rows[ENGRAM_MAX_TABLES];
+  int32_t order[ENGRAM_MAX_TABLES];                     // n of the table's order
+  const int32_t* ids;
+  int32_t* idx;
+  int64_t ld, t_begin, t_count;
+  int32_t n_tables, max_order, pad_id, batch;
+};
+void launch_hash(const HashArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- gather / prefetch
+struct GatherArgs {
+  const char* table[ENGRAM_MAX_TABLES];  // device-accessible base of each table
+  int64_t rows[ENGRAM_MAX_TABLES];
+  const int32_t* idx;
+  char* out;
+  int32_t* err_count;
+  int64_t n_tok;
+  int32_t n_tables;
+  int32_t chunks_per_row;  // row bytes / 16
+};
+// `host_source`: the tables are pinned host memory read over PCIe (launch tuned for that).
+void launch_gather(const GatherArgs& a, bool host_source, hipStream_t s);
+
+// ---------------------------------------------------------------- gate
+struct GateArgs {
+  const void* mem;
+  const void* h[ENGRAM_MAX_BRANCHES];
+  const void* wk[ENGRAM_MAX_BRANCHES];
+  const void* wv[ENGRAM_MAX_BRANCHES];
+  const void* gq[ENGRAM_MAX_BRANCHES];
+  const void* gk[ENGRAM_MAX_BRANCHES];
+  void* out[ENGRAM_MAX_BRANCHES];
+  float* gate_out;   // [n_branch][n_tok] or null
+  float* part_dot;   // scratch: [n_branch][n_ftiles][n_tok]
+  float* part_hh;    // scratch: [n_branch][n_ftiles][n_tok]
+  float* ee;         // scratch: [n_branch][n_ftiles][n_tok] partial sums of e^2
+  int64_t n_tok;
+  int32_t d_mem, d_model, n_branch, n_ftiles;
+  float eps, inv_sqrt_d;
+};
+// bf16 path: returns the scratch bytes it needs for these shapes (and sets a.n_ftiles).
+// launch_gate_bf16 expects a.part_dot to point at a scratch block of that size.
+size_t gate_bf16_scratch_bytes(GateArgs& a);
+void launch_gate_bf16(const GateArgs& a, hipStream_t s);
+void launch_gate_f32(const GateArgs& a, hipStream_t s);
+
+}  // namespace engram

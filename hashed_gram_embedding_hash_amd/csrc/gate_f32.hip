@@ -1,0 +1,103 @@
+// gate_f32.hip -- context-aware gating with every operation in fp32.
+//
+// Same definition as the bf16 path ("Conditional Memory via Scalable Lookup",
+// section 2.3, Eq. (3)-(4), gated value, residual; section 2.4 Eq. (6) per
+// branch), for fp32 tables, weights and hidden states.  fp32 inputs have no
+// matrix-core path worth taking at the sizes this dtype is used for (tiny,
+// launch-bound configurations), so one workgroup handles one (token, branch):
+//   1. block reductions give sum(e^2) and sum(h^2);
+//   2. RMSNorm(e) * gk is staged in LDS;
+//   3. each wavefront takes output features in turn, its lanes read one row of
+//      W_K (coalesced) against the staged vector and reduce across the wave;
+//      q_i * k_i accumulates into the logit;
+//   4. alpha = sigmoid(logit / sqrt(d_model)), then the same row-per-wavefront
+//      loop over W_V writes out_i = h_i + alpha * v_i.
+// All reductions run in a fixed order, so results are bit-reproducible.
+#include "engram_internal.h"
+
+namespace engram {
+namespace {
+
+constexpr int NTHR = 256;
+constexpr int NWAVE = NTHR / 64;
+
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Sum over the workgroup; every thread gets the result.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float s = 0.f;
+  for (int w = 0; w < NWAVE; ++w) s += red[w];
+  __syncthreads();
+  return s;
+}
+
+__global__ __launch_bounds__(NTHR) void gate_f32_kernel(const GateArgs a) {
+  extern __shared__ float s_en[];  // [d_mem]
+  __shared__ float red[NWAVE];
+  __shared__ float s_dot[NWAVE];
+
+  const int64_t t = blockIdx.x;
+  const int m = blockIdx.y;
+  const int d_mem = a.d_mem, d_model = a.d_model;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float* e = (const float*)a.mem + t * d_mem;
+  const float* h = (const float*)a.h[m] + t * d_model;
+  const float* wk = (const float*)a.wk[m];
+  const float* wv = (const float*)a.wv[m];
+  const float* gq = (const float*)a.gq[m];
+  const float* gk = (const float*)a.gk[m];
+  float* out = (float*)a.out[m] + t * d_model;
+
+  float ss = 0.f;
+  for (int j = threadIdx.x; j < d_mem; j += NTHR) ss += e[j] * e[j];
+  const float rms_e = sqrtf(block_sum(ss, red) / (float)d_mem + a.eps);
+  float sh = 0.f;
+  for (int i = threadIdx.x; i < d_model; i += NTHR) sh += h[i] * h[i];
+  const float rms_h = sqrtf(block_sum(sh, red) / (float)d_model + a.eps);
+
+  for (int j = threadIdx.x; j < d_mem; j += NTHR) s_en[j] = e[j] / rms_e * gk[j];
+  __syncthreads();
+
+  float dot = 0.f;  // meaningful in lane 0 of each wave
+  for (int i = wave; i < d_model; i += NWAVE) {
+    const float* row = wk + (int64_t)i * d_mem;
+    float k = 0.f;
+    for (int j = lane; j < d_mem; j += 64) k += row[j] * s_en[j];
+    k = wave_sum(k);
+    dot += (h[i] / rms_h * gq[i]) * k;
+  }
+  if (lane == 0) s_dot[wave] = dot;
+  __syncthreads();
+  float logit = 0.f;
+  for (int w = 0; w < NWAVE; ++w) logit += s_dot[w];
+  logit /= sqrtf((float)d_model);
+  const float alpha = 1.f / (1.f + expf(-logit));
+  if (threadIdx.x == 0 && a.gate_out != nullptr) a.gate_out[(int64_t)m * a.n_tok + t] = alpha;
+
+  // every thread of the wave holds h[i]; stores happen after the last read of h
+  // in this loop iteration, so out may alias h
+  for (int i = wave; i < d_model; i += NWAVE) {
+    const float* row = wv + (int64_t)i * d_mem;
+    float v = 0.f;
+    for (int j = lane; j < d_mem; j += 64) v += row[j] * e[j];
+    v = wave_sum(v);
+    const float hi = h[i];
+    if (lane == 0) out[i] = hi + alpha * v;
+  }
+}
+
+}  // namespace
+
+void launch_gate_f32(const GateArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)a.n_tok, (unsigned)a.n_branch);
+  hipLaunchKernelGGL(gate_f32_kernel, grid, dim3(NTHR), (size_t)a.d_mem * sizeof(float), s, a);
+}
+
+}  // namespace engram

@@ -1,0 +1,67 @@
+// hash.hip -- multi-head multiply-XOR hashing of suffix n-grams.
+// "Conditional Memory via Scalable Lookup", section 2.2, Eq. (1): for each
+// position t, n-gram order n and head k, the suffix n-gram of canonical ids is
+// mapped by its own hash function into a prime-sized table.  The hash is the
+// lightweight multiply-XOR form:
+//   h = XOR_j ( x'_{t-j} * c[n][k][j] mod 2^64 ),   z = h mod M[n][k].
+//
+// Layout of the work: one thread per (position, table) pair, table index
+// fastest, so a wavefront writes consecutive int32 entries of the token-major
+// index matrix [tokens][tables].  A workgroup owns POS consecutive positions of
+// one sequence and first stages their ids plus the (max_order - 1) ids before
+// them in LDS; every thread then reads its n ids from LDS.
+//
+// The 64-bit reduction modulo a prime M < 2^31 uses a Barrett quotient with the
+// host-computed constant m = floor((2^64 - 1) / M):  q = mulhi(h, m) is either
+// floor(h / M) or one less, so r = h - q * M needs at most one subtraction.
+#include "engram_internal.h"
+
+namespace engram {
+namespace {
+
+constexpr int POS = 64;  // positions per workgroup
+
+__device__ __forceinline__ uint32_t mod_barrett(uint64_t h, uint32_t M, uint64_t m) {
+  const uint64_t q = __umul64hi(h, m);
+  const uint64_t r = h - q * (uint64_t)M;
+  return (uint32_t)(r >= M ? r - M : r);
+}
+
+__global__ __launch_bounds__(256) void hash_kernel(const HashArgs a) {
+  __shared__ int32_t s_ids[POS + ENGRAM_MAX_ORDER - 1];
+  const uint32_t nblk = (uint32_t)((a.t_count + POS - 1) / POS);  // workgroups per sequence
+  const int32_t b = (int32_t)(blockIdx.x / nblk);
+  const int64_t p0 = (int64_t)(blockIdx.x - (uint32_t)b * nblk) * POS;  // window-relative start
+  const int64_t t0 = a.t_begin + p0;                       // absolute first position
+  const int halo = a.max_order - 1;
+  const int64_t npos = (a.t_count - p0) < POS ? (a.t_count - p0) : POS;
+  const int32_t* row = a.ids + (int64_t)b * a.ld;
+
+  for (int i = threadIdx.x; i < npos + halo; i += blockDim.x) {
+    const int64_t t = t0 - halo + i;
+    s_ids[i] = t >= 0 ? row[t] : a.pad_id;
+  }
+  __syncthreads();
+
+  const int nt = a.n_tables;
+  int32_t* out = a.idx + ((int64_t)b * a.t_count + p0) * nt;
+  const int pairs = (int)npos * nt;
+  for (int q = threadIdx.x; q < pairs; q += blockDim.x) {
+    const int pos = q / nt;
+    const int tb = q - pos * nt;
+    const int n = a.order[tb];
+    const int32_t* g = s_ids + pos + halo;  // g[-j] is x'_{t-j}
+    uint64_t h = 0;
+    for (int j = 0; j < n; ++j) h ^= (uint64_t)(uint32_t)g[-j] * a.mult[tb][j];
+    out[q] = (int32_t)mod_barrett(h, a.rows[tb], a.barrett[tb]);
+  }
+}
+
+}  // namespace
+
+void launch_hash(const HashArgs& a, hipStream_t s) {
+  const uint64_t nblk = (uint64_t)((a.t_count + POS - 1) / POS);
+  hipLaunchKernelGGL(hash_kernel, dim3((unsigned)(nblk * (uint64_t)a.batch)), dim3(256), 0, s, a);
+}
+
+}  // namespace engram

@@ -1,0 +1,64 @@
+"""One Engram layer forward pass as a sequence of C-ABI calls.
+
+"Conditional Memory via Scalable Lookup", Figure 1 and sections 2.2-2.4:
+compress the raw ids, hash every suffix n-gram into its tables, gather and
+concatenate the rows, then gate the memory against each branch's hidden
+state and add it to the residual.  This class only owns the parameters and
+the intermediate device buffers and issues the four calls on one stream; the
+arithmetic is in the HIP kernels.
+"""
+from __future__ import annotations
+
+from typing import List, Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import (engram_compress, engram_gate_forward, engram_gather, engram_hash)
+
+
+class EngramLayer:
+    def __init__(self, cmap: torch.Tensor, orders: Sequence[int], heads: int, mult: np.ndarray,
+                 tables: Sequence[torch.Tensor], wk: Sequence[torch.Tensor], wv: Sequence[torch.Tensor],
+                 gq: Sequence[torch.Tensor], gk: Sequence[torch.Tensor], eps: float = 1e-6,
+                 pad_id: Optional[int] = None):
+        self.cmap = cmap
+        self.orders = tuple(orders)
+        self.heads = heads
+        self.mult = np.ascontiguousarray(mult, dtype=np.uint64)
+        self.tables = list(tables)
+        self.rows = np.array([t.shape[0] for t in tables], dtype=np.uint32)
+        self.wk, self.wv, self.gq, self.gk = list(wk), list(wv), list(gq), list(gk)
+        self.eps = eps
+        # default padding id: one past the largest canonical id
+        self.pad_id = int(cmap.max().item()) + 1 if pad_id is None else pad_id
+        self._bufs = {}
+
+    @property
+    def n_tables(self) -> int:
+        return len(self.orders) * self.heads
+
+    def buffers(self, batch: int, seq: int):
+        key = (batch, seq)
+        if key not in self._bufs:
+            dev = self.cmap.device
+            n = batch * seq
+            w = self.tables[0].shape[1]
+            self._bufs[key] = dict(
+                ids=torch.empty((batch, seq), dtype=torch.int32, device=dev),
+                idx=torch.empty((n, self.n_tables), dtype=torch.int32, device=dev),
+                mem=torch.empty((n, self.n_tables * w), dtype=self.tables[0].dtype, device=dev),
+            )
+        return self._bufs[key]
+
+    def __call__(self, raw: torch.Tensor, h: Sequence[torch.Tensor], out: Optional[Sequence[torch.Tensor]] = None,
+                 gate_out: Optional[torch.Tensor] = None, stream=None) -> List[torch.Tensor]:
+        """raw: int32 [batch, seq]; h: per-branch [batch*seq, d_model]; returns per-branch outputs."""
+        batch, seq = raw.shape
+        b = self.buffers(batch, seq)
+        engram_compress(raw, self.cmap, out=b["ids"], stream=stream)
+        engram_hash(b["ids"], self.orders, self.heads, self.mult, self.rows, self.pad_id, out=b["idx"],
+                    stream=stream)
+        engram_gather(b["idx"], self.tables, out=b["mem"], stream=stream)
+        return engram_gate_forward(b["mem"], h, self.wk, self.wv, self.gq, self.gk, self.eps, out=out,
+                                   gate_out=gate_out, stream=stream)

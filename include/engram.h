@@ -1,0 +1,173 @@
+/*
+ * engram.h -- C ABI of the Engram forward pass on AMD Instinct MI355X (gfx950).
+ *
+ * The module computed here is defined in "Conditional Memory via Scalable
+ * Lookup: A New Axis of Sparsity for Large Language Models" (DeepSeek-AI and
+ * Peking University):
+ *   section 2.2  tokenizer compression, suffix n-grams, multi-head hashing into
+ *                prime-sized tables (Eq. 1), concatenated memory vector (Eq. 2);
+ *   section 2.3  context-aware gating (Eq. 3-4), gated value and residual add;
+ *   section 2.4  several branches sharing one lookup (Eq. 6);
+ *   section 2.5 / Figure 2(b) and section 6.4  host-memory offload with
+ *                prefetch of the rows whose addresses are known in advance.
+ * The order of operations in the gate (key = W_K * RMSNorm(memory)) follows the
+ * context_aware_gating pseudocode of the review page "Engram: LLM에 '기억의
+ * 서랍'을 달아주다" (koala.ai.kr).
+ *
+ * Conventions for every entry point
+ *   - Pointers named "device" must be device memory (hipMalloc or any
+ *     allocator over it, e.g. torch CUDA tensors); "host" pointers are ordinary
+ *     host memory read during the call.  Arrays of pointers (tables, branch
+ *     buffers) are host arrays of device pointers.
+ *   - All work is enqueued asynchronously on `stream` (0 = the null stream);
+ *     the call returns after enqueueing.  Outputs are valid once the stream
+ *     reaches that point.
+ *   - Ownership: the library never frees or keeps caller buffers.  The gate
+ *     allocates its own small stream-ordered scratch (hipMallocAsync /
+ *     hipFreeAsync on `stream`).
+ *   - Errors: arguments are validated on the host before anything is enqueued;
+ *     a non-OK status means nothing was enqueued (ENGRAM_ERR_INVALID_ARG,
+ *     ENGRAM_ERR_UNSUPPORTED) or a HIP call failed (ENGRAM_ERR_HIP).
+ *     engram_last_error() returns a message for the calling thread's last
+ *     non-OK status.  Data errors found on the device (an out-of-range id or
+ *     row index) never abort: the element is written as documented and an
+ *     optional device counter is incremented.
+ *   - Calls are thread-safe; calls on different streams may run concurrently.
+ */
+#ifndef ENGRAM_H
+#define ENGRAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum engram_status {
+  ENGRAM_OK = 0,
+  ENGRAM_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size or range     */
+  ENGRAM_ERR_UNSUPPORTED = 2, /* valid request outside the implemented shapes    */
+  ENGRAM_ERR_HIP = 3          /* a HIP runtime call or a kernel launch failed    */
+} engram_status;
+
+typedef enum engram_dtype {
+  ENGRAM_F32 = 0, /* IEEE binary32 */
+  ENGRAM_BF16 = 1 /* bfloat16 (top 16 bits of binary32), round-to-nearest-even on output */
+} engram_dtype;
+
+/* Limits of this implementation. */
+#define ENGRAM_MAX_TABLES 32   /* n_orders * heads                       */
+#define ENGRAM_MAX_ORDER 4     /* largest n-gram order                   */
+#define ENGRAM_MAX_BRANCHES 8  /* gating branches per call               */
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char* engram_last_error(void);
+
+/* Library version string. */
+const char* engram_version(void);
+
+/*
+ * Tokenizer compression -- section 2.2 ("tokenizer compression"): each raw id
+ * is mapped through the precomputed surjection P to its canonical id.
+ *   out[i] = map[raw[i]]  if 0 <= raw[i] < vocab,  else -1 (and *err_count += 1).
+ * raw, out: device int32[n] (may alias).  map: device int32[vocab].
+ * err_count: device int32 counter or NULL; it is incremented, never cleared.
+ * n == 0 is a no-op.  Errors: INVALID_ARG for n < 0, vocab <= 0 or null pointers.
+ */
+engram_status engram_compress(const int32_t* raw, int64_t n, const int32_t* map, int32_t vocab,
+                              int32_t* out, int32_t* err_count, hipStream_t stream);
+
+/*
+ * Multi-head hashing of suffix n-grams -- section 2.2, Eq. (1).
+ * ids: device int32 [batch][ld] canonical ids, row-major.  For every row b,
+ * position t in [t_begin, t_begin + t_count), order index o (n = orders[o]) and
+ * head k < heads:
+ *   h = XOR_{j=0}^{n-1} ( (uint64) x'_{t-j} * mult[o][k][j]  mod 2^64 )
+ *   idx[b*t_count + (t - t_begin)][o*heads + k] = h mod rows[o*heads + k]
+ * where x'_{t-j} is pad_id when t-j < 0 (n-grams never cross rows).  The id is
+ * taken as its 32-bit unsigned pattern.
+ * orders: host int32[n_orders], each 1..ENGRAM_MAX_ORDER.
+ * mult:   host uint64[n_orders][heads][max(orders)] multipliers (entries j >= n unused).
+ * rows:   host uint32[n_orders*heads] table sizes, each in [1, 2^31).
+ * idx:    device int32 [batch*t_count][n_orders*heads] (order-major, head-minor
+ *         columns: the concatenation order of Eq. (2)).
+ * Requires 0 <= t_begin, t_begin + t_count <= ld, n_orders*heads <= ENGRAM_MAX_TABLES.
+ * batch == 0 or t_count == 0 is a no-op.
+ */
+engram_status engram_hash(const int32_t* ids, int32_t batch, int64_t ld, int64_t t_begin,
+                          int64_t t_count, const int32_t* orders, int32_t n_orders, int32_t heads,
+                          const uint64_t* mult, const uint32_t* rows, int32_t pad_id,
+                          int32_t* idx, hipStream_t stream);
+
+/*
+ * Table lookup and concatenation -- section 2.2, Eq. (1)-(2):
+ *   out[t][b*w : (b+1)*w] = tables[b][idx[t][b]][0 : w]     (bitwise copy)
+ * idx:    device int32 [n_tok][n_tables].
+ * tables: host array of n_tables device pointers; table b is row-major
+ *         [rows[b]][w] of `dtype`, 16-byte aligned.
+ * rows:   host int64[n_tables] row counts.  An index outside [0, rows[b]) yields
+ *         a zero block and increments *err_count (device int32, or NULL).
+ * out:    device [n_tok][n_tables*w] of `dtype`, 16-byte aligned.
+ * Requires w * sizeof(dtype) to be a multiple of 16 (UNSUPPORTED otherwise).
+ */
+engram_status engram_gather(const int32_t* idx, int64_t n_tok, int32_t n_tables,
+                            const void* const* tables, const int64_t* rows, int32_t w,
+                            engram_dtype dtype, void* out, int32_t* err_count, hipStream_t stream);
+
+/*
+ * Context-aware gating -- section 2.3, Eq. (3)-(4), the gated value and the
+ * residual update; section 2.4, Eq. (6) for branches m < n_branch sharing `mem`
+ * (every branch has its own W_K, W_V and gains; the paper's shared W_V is the
+ * case of equal pointers):
+ *   q     = RMSNorm_{gq[m]}(h[m]_t),  RMSNorm_g(x) = x / sqrt(mean(x^2) + eps) * g
+ *   k     = Wk[m] * RMSNorm_{gk[m]}(mem_t)
+ *   v     = Wv[m] * mem_t
+ *   alpha = sigmoid( q . k / sqrt(d_model) )
+ *   out[m]_t = h[m]_t + alpha * v
+ * mem:   device [n_tok][d_mem].   h[m], out[m]: device [n_tok][d_model]; out[m]
+ *        may equal h[m] (in place).  Wk[m], Wv[m]: device [d_model][d_mem]
+ *        row-major (output x input).  gq[m]: device [d_model]; gk[m]: [d_mem].
+ *        All of `dtype`, 16-byte aligned.
+ * gate_out: device float32 [n_branch][n_tok] receiving alpha, or NULL.
+ * Arithmetic: bf16 products with fp32 accumulation on the matrix cores
+ * (RMSNorm(mem)*gk rounded to bf16 before the W_K product), fp32 elsewhere;
+ * ENGRAM_F32 computes everything in fp32.
+ * Shapes: ENGRAM_BF16 needs d_mem % 64 == 0 and d_model % 32 == 0; ENGRAM_F32
+ * accepts any positive sizes.  n_tok == 0 is a no-op.
+ */
+engram_status engram_gate_forward(const void* mem, int64_t n_tok, int32_t d_mem, int32_t d_model,
+                                  int32_t n_branch, const void* const* h, const void* const* wk,
+                                  const void* const* wv, const void* const* gq,
+                                  const void* const* gk, float eps, engram_dtype dtype,
+                                  void* const* out, float* gate_out, hipStream_t stream);
+
+/*
+ * Prefetch from host-resident tables -- section 2.5 and Figure 2(b), section
+ * 6.4: hash addresses are known before the layer runs, so the rows can be
+ * fetched from host DRAM over PCIe into device memory ahead of use.
+ * Same result as engram_gather, bit for bit, but host_tables[b] are pinned,
+ * device-mapped host allocations (hipHostMalloc, e.g. engram_host_alloc or a
+ * pinned torch tensor); the GPU reads the rows over PCIe and writes them to the
+ * device buffer `staging` [n_tok][n_tables*w].  Intended for a side stream, with
+ * events ordering the consumer after it.
+ * Errors: INVALID_ARG if a table pointer is not a device-accessible pinned host
+ * allocation; otherwise as engram_gather.
+ */
+engram_status engram_prefetch_host(const int32_t* idx, int64_t n_tok, int32_t n_tables,
+                                   const void* const* host_tables, const int64_t* rows, int32_t w,
+                                   engram_dtype dtype, void* staging, int32_t* err_count,
+                                   hipStream_t stream);
+
+/* Pinned, device-mapped host allocation for offloaded tables (hipHostMalloc,
+ * hipHostMallocMapped | hipHostMallocPortable). *ptr is NULL on failure. */
+engram_status engram_host_alloc(size_t bytes, void** ptr);
+engram_status engram_host_free(void* ptr);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ENGRAM_H */

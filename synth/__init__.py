@@ -370,3 +370,39 @@ def offload_rows(cfg: Config, mem_available_bytes: Optional[int]) -> int:
         return cfg.rows
     f = 0.6 * mem_available_bytes / full
     return next_prime(int(cfg.rows * f))
+
+
+def device_inputs(cfg: Config, device, tables: bool = True, table_rows_override: Optional[int] = None):
+    """All inputs of one configuration, generated directly on ``device``.
+
+    Returns a dict: raw ids [batch, seq(+decode)] int32, map int32[vocab],
+    mult (numpy uint64), rows (numpy uint32, per table), tables (list of
+    [rows, w] tensors, omitted when tables=False), h / wk / wv / gq / gk (lists
+    per branch).  Hidden states cover the batch * seq prefill tokens.
+    """
+    import torch
+    dt = torch_dtype(cfg)
+    nrows = table_rows_override or cfg.rows
+    out = {
+        "raw": torch.from_numpy(raw_ids(cfg)).to(device),
+        "map": torch.from_numpy(comp_map(cfg)).to(device),
+        "mult": multipliers(cfg),
+        "rows": np.full(cfg.n_tables, nrows, dtype=np.uint32),
+    }
+    if tables:
+        tabs = []
+        for b in range(cfg.n_tables):
+            t = torch.empty((nrows, cfg.w), dtype=dt, device=device)
+            tabs.append(fill_table(cfg, b, t))
+        out["tables"] = tabs
+    out["h"], out["wk"], out["wv"], out["gq"], out["gk"] = [], [], [], [], []
+    for m in range(cfg.n_branch):
+        h = torch.empty((cfg.tokens, cfg.d_model), dtype=dt, device=device)
+        out["h"].append(fill_hidden(cfg, m, h))
+        wk, wv = weights(cfg, m, device)
+        gq, gk = gains(cfg, m, device)
+        out["wk"].append(wk)
+        out["wv"].append(wv)
+        out["gq"].append(gq)
+        out["gk"].append(gk)
+    return out

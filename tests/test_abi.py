@@ -1,0 +1,128 @@
+"""The C ABI library: it loads, exports every entry point of include/engram.h,
+and rejects bad arguments on the host (no GPU work is started by these calls)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import hashed_gram_embedding_hash_amd as eg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "engram.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(engram_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for n in ("engram_compress", "engram_hash", "engram_gather", "engram_gate_forward", "engram_prefetch_host"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = eg.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert set(declared_functions()) == set(eg.EXPORTS)
+    assert "gfx950" in eg.version()
+
+
+def test_library_is_gfx950_code_object():
+    data = open(eg.LIB_PATH, "rb").read()
+    assert b"gfx950" in data
+
+
+def _st(name):
+    return {"ok": 0, "arg": 1, "unsup": 2, "hip": 3}[name]
+
+
+def test_compress_argument_errors():
+    L = eg.lib()
+    assert L.engram_compress(None, -1, None, 10, None, None, None) == _st("arg")
+    assert b"n < 0" in L.engram_last_error()
+    assert L.engram_compress(None, 5, None, 10, None, None, None) == _st("arg")
+    assert L.engram_compress(None, 0, ctypes.c_void_p(16), 0, None, None, None) == _st("arg")
+    # n == 0 is a no-op and touches no device memory
+    assert L.engram_compress(None, 0, ctypes.c_void_p(16), 10, None, None, None) == _st("ok")
+
+
+def test_hash_argument_errors():
+    L = eg.lib()
+    orders = np.array([2, 3], np.int32)
+    mult = np.ones((2, 2, 3), np.uint64)
+    rows = np.array([7, 7, 7, 7], np.uint32)
+    call = lambda **kw: L.engram_hash(
+        kw.get("ids", ctypes.c_void_p(256)), kw.get("batch", 1), kw.get("ld", 10), kw.get("t_begin", 0),
+        kw.get("t_count", 10), kw.get("orders", orders.ctypes.data), kw.get("n_orders", 2), kw.get("heads", 2),
+        kw.get("mult", mult.ctypes.data), kw.get("rows", rows.ctypes.data), 0, kw.get("idx", ctypes.c_void_p(256)),
+        None)
+    assert call(t_begin=5, t_count=6) == _st("arg")
+    assert b"exceeds" in L.engram_last_error()
+    assert call(batch=-1) == _st("arg")
+    bad_orders = np.array([2, 5], np.int32)
+    assert call(orders=bad_orders.ctypes.data) == _st("arg")
+    bad_rows = np.array([7, 0, 7, 7], np.uint32)
+    assert call(rows=bad_rows.ctypes.data) == _st("arg")
+    big_rows = np.array([7, 1 << 31, 7, 7], np.uint32)
+    assert call(rows=big_rows.ctypes.data) == _st("arg")
+    assert call(heads=17) == _st("arg")          # 2 * 17 tables > 32
+    assert call(ids=None) == _st("arg")
+    assert call(t_count=0) == _st("ok")          # empty window: no-op
+
+
+def test_gather_argument_errors():
+    L = eg.lib()
+    tabs = (ctypes.c_void_p * 2)(256, 512)
+    rows = np.array([10, 10], np.int64)
+    g = lambda **kw: L.engram_gather(ctypes.c_void_p(256), kw.get("n", 4), kw.get("nt", 2), kw.get("tabs", tabs),
+                                     kw.get("rows", rows.ctypes.data), kw.get("w", 8), kw.get("dt", eg.BF16),
+                                     kw.get("out", ctypes.c_void_p(1024)), None, None)
+    assert g(w=4) == _st("unsup")                 # 8-byte rows
+    assert g(dt=7) == _st("arg")
+    assert g(nt=0) == _st("arg")
+    assert g(nt=33) == _st("arg")
+    assert g(tabs=(ctypes.c_void_p * 2)(256, 513)) == _st("arg")   # misaligned table
+    assert g(out=ctypes.c_void_p(1032)) == _st("arg")               # misaligned output
+    assert g(rows=np.array([10, 0], np.int64).ctypes.data) == _st("arg")
+    assert g(n=-1) == _st("arg")
+    assert g(w=5120) == _st("unsup")              # 2 x 10240-byte rows exceed 16 KiB per token
+    assert g(n=0) == _st("ok")
+
+
+def test_gate_argument_errors():
+    L = eg.lib()
+    one = (ctypes.c_void_p * 1)(4096)
+    gf = lambda **kw: L.engram_gate_forward(
+        ctypes.c_void_p(4096), kw.get("n", 8), kw.get("dm", 1280), kw.get("dmod", 2560), kw.get("nb", 1),
+        one, one, one, one, one, ctypes.c_float(kw.get("eps", 1e-6)), kw.get("dt", eg.BF16), one, None, None)
+    assert gf(dm=1000) == _st("unsup")
+    assert gf(dmod=2500) == _st("unsup")
+    assert b"d_mem % 64" in L.engram_last_error()
+    assert gf(nb=0) == _st("arg")
+    assert gf(nb=9) == _st("arg")
+    assert gf(eps=-1.0) == _st("arg")
+    assert gf(n=-2) == _st("arg")
+    assert gf(dt=5) == _st("arg")
+    assert gf(n=0) == _st("ok")
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(eg, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(eg, "_lib", None)
+    with pytest.raises(ImportError):
+        eg.lib()
+
+
+def test_product_path_does_not_use_the_oracle():
+    pkg = os.path.join(ROOT, "hashed_gram_embedding_hash_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f

@@ -1,0 +1,105 @@
+"""Full-size workloads through the same layer object and launch configuration
+the benchmark times, checked against the oracle.
+
+Every compressed id and hash index is compared (the oracle hashes all tokens);
+memory vectors and gated outputs are compared on a sample of tokens that
+includes positions 0, 1, 2 and seq-1 of every sequence (the padded n-grams and
+the last position).
+"""
+import numpy as np
+import pytest
+import torch
+
+import hashed_gram_embedding_hash_amd as eg
+from hashed_gram_embedding_hash_amd.pipeline import EngramLayer
+import synth
+from gpu_helpers import host_view, oracle_gate_tokens, oracle_ids_idx, oracle_memory, rel_err, sample_tokens
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def build_layer(cfg, inp):
+    return EngramLayer(inp["map"], cfg.orders, cfg.heads, inp["mult"], inp["tables"], inp["wk"], inp["wv"],
+                       inp["gq"], inp["gk"], cfg.eps, pad_id=cfg.vocab_c)
+
+
+@pytest.mark.parametrize("name,n_sample", [("small", 160), ("multi", 40), ("large", 40)])
+def test_full_config_sampled(name, n_sample):
+    cfg = synth.CONFIGS[name]
+    say(f"full config {name}: {cfg.tokens} tokens, {cfg.n_tables} x {cfg.rows} rows, "
+        f"d_model {cfg.d_model}, {cfg.n_branch} branches")
+    inp = synth.device_inputs(cfg, DEV)
+    layer = build_layer(cfg, inp)
+    alpha = torch.empty((cfg.n_branch, cfg.tokens), dtype=torch.float32, device=DEV)
+    out = layer(inp["raw"], inp["h"], gate_out=alpha)
+    torch.cuda.synchronize()
+    bufs = layer.buffers(cfg.batch, cfg.seq)
+    say("  gpu pass done")
+
+    raw = synth.raw_ids(cfg)
+    ids_o, idx_o = oracle_ids_idx(cfg, raw)
+    assert np.array_equal(bufs["ids"].cpu().numpy(), ids_o)
+    assert np.array_equal(bufs["idx"].cpu().numpy(), idx_o)
+    say("  ids and indices bit-exact")
+
+    tok = sample_tokens(cfg, n_sample)
+    e_o = oracle_memory(cfg, idx_o[tok])
+    assert np.array_equal(host_view(bufs["mem"][torch.from_numpy(tok).to(DEV)]), e_o)
+    say(f"  memory vectors of {len(tok)} sampled tokens bit-exact")
+    for m in range(cfg.n_branch):
+        out_o, alpha_o = oracle_gate_tokens(cfg, m, e_o, tok)
+        got = out[m][torch.from_numpy(tok).to(DEV)].float().cpu().numpy()
+        err = rel_err(got, out_o)
+        aerr = np.abs(alpha[m].cpu().numpy()[tok] - alpha_o).max()
+        say(f"  branch {m}: out rel err {err:.2e}, alpha abs err {aerr:.2e}")
+        assert err <= 1e-2 and aerr <= 2e-3
+    # alpha is a probability everywhere, and outputs are finite
+    assert torch.all((alpha > 0) & (alpha < 1))
+    for o in out:
+        assert torch.isfinite(o.float()).all()
+
+
+def test_decode_prefetch_pipeline():
+    """Offload-style decode: 256 sequences with 4096-token histories; for a few steps
+    hash the new position, prefetch rows from pinned host tables, gate 64 sampled tokens."""
+    cfg = synth.CONFIGS["offload"].replace(rows=1_000_003)
+    say(f"decode prefetch: {cfg.batch} sequences, host tables {cfg.n_tables} x {cfg.rows}")
+    raw = synth.raw_ids(cfg)                       # [256, 4096 + steps]
+    host = []
+    for b in range(cfg.n_tables):
+        t = torch.empty((cfg.rows, cfg.w), dtype=torch.bfloat16, pin_memory=True)
+        t.copy_(synth.table_rows(cfg, b, torch.arange(cfg.rows, device=DEV)))
+        host.append(t)
+    rows = [cfg.rows] * cfg.n_tables
+    cmap = torch.from_numpy(synth.comp_map(cfg)).to(DEV)
+    ids_d = eg.engram_compress(torch.from_numpy(raw).to(DEV), cmap)
+    wk, wv = synth.weights(cfg, 0, DEV)
+    gq, gk = synth.gains(cfg, 0, DEV)
+    side = torch.cuda.Stream()
+    for step in (0, 1, 7):
+        t = cfg.seq + step
+        with torch.cuda.stream(side):
+            idx = eg.engram_hash(ids_d, cfg.orders, cfg.heads, synth.multipliers(cfg), synth.table_rows_u32(cfg),
+                                 cfg.vocab_c, t_begin=t, t_count=1)
+            staged = eg.engram_prefetch_host(idx, host, rows, cfg.w, torch.bfloat16)
+        torch.cuda.current_stream().wait_stream(side)
+        _, idx_o = oracle_ids_idx(cfg, raw, t_begin=t, t_count=1)
+        assert np.array_equal(idx.cpu().numpy(), idx_o)
+        e_o = oracle_memory(cfg, idx_o)
+        assert np.array_equal(host_view(staged), e_o)
+        sel = np.arange(0, cfg.batch, 4)          # 64 of the 256 sequences
+        tokens = sel * (cfg.seq + cfg.decode_steps) + t
+        h = synth.hidden_rows(cfg, 0, torch.from_numpy(tokens)).to(DEV)
+        alpha = torch.empty((1, len(sel)), dtype=torch.float32, device=DEV)
+        out = eg.engram_gate_forward(staged[torch.from_numpy(sel).to(DEV)].contiguous(), [h], [wk], [wv], [gq],
+                                     [gk], cfg.eps, gate_out=alpha)[0]
+        out_o, alpha_o = oracle_gate_tokens(cfg, 0, e_o[sel], tokens)
+        err = rel_err(out.float().cpu().numpy(), out_o)
+        aerr = np.abs(alpha.cpu().numpy()[0] - alpha_o).max()
+        say(f"  step {step}: indices and staged rows bit-exact; out rel err {err:.2e}, alpha err {aerr:.2e}")
+        assert err <= 1e-2 and aerr <= 2e-3

@@ -1,0 +1,270 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on seeded inputs.
+
+Bar: bit-exact for compressed ids, hash indices and gathered/staged memory
+vectors; max relative error (gpu_helpers.rel_err: |g - r| / max(|r|, rms(r)))
+<= 1e-5 for fp32 outputs and <= 1e-2 for bf16 outputs.  Because tables of
+std 0.02 make alpha * v small next to h, the bf16 cases also check alpha
+(absolute error <= 2e-3: the key's bf16 operands carry a relative rounding of
+2^-9 when the gains differ from 1) and, in the stress cases whose tables have
+std >= 0.5, the update out - h itself (rel_err <= 5e-2: bf16 rounding of out,
+2^-9 |out|, over |alpha v| of about 0.5).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import hashed_gram_embedding_hash_amd as eg
+import oracle
+import synth
+from gpu_helpers import (host_view, oracle_gate_tokens, oracle_ids_idx, oracle_memory, rel_err,
+                         sample_tokens)
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+ALPHA_TOL_BF16 = 2e-3
+UPDATE_TOL_STRESS = 5e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# compress
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["tiny", "small"])
+def test_compress_bit_exact(name):
+    cfg = synth.CONFIGS[name]
+    say("compress", name)
+    raw = synth.raw_ids(cfg)
+    cmap = synth.comp_map(cfg)
+    got = eg.engram_compress(torch.from_numpy(raw).to(DEV), torch.from_numpy(cmap).to(DEV)).cpu().numpy()
+    want, _ = oracle.compress(raw, cmap)
+    assert np.array_equal(got, want)
+
+
+def test_compress_out_of_range_counted_and_empty():
+    say("compress bad ids")
+    cmap = np.array([4, 3, 2, 1, 0], np.int32)
+    raw = np.array([0, 5, -1, 4, 1 << 30, 2] * 50, np.int32)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    got = eg.engram_compress(torch.from_numpy(raw).to(DEV), torch.from_numpy(cmap).to(DEV), err_count=err)
+    want, bad = oracle.compress(raw, cmap)
+    assert np.array_equal(got.cpu().numpy(), want) and int(err.item()) == bad == 150
+    empty = torch.empty(0, dtype=torch.int32, device=DEV)
+    assert eg.engram_compress(empty, torch.from_numpy(cmap).to(DEV)).numel() == 0
+
+
+# ---------------------------------------------------------------------------
+# hash
+# ---------------------------------------------------------------------------
+def test_hash_all_bigrams_and_trigram_sample_tiny():
+    """Brute force over the tiny vocabulary: every bigram (770^2) and 200k trigrams."""
+    cfg = synth.CONFIGS["tiny"]
+    say("hash brute force")
+    V = cfg.vocab_c
+    a, b = np.meshgrid(np.arange(V, dtype=np.int32), np.arange(V, dtype=np.int32), indexing="ij")
+    rng = np.random.default_rng(0)
+    ids = np.stack([rng.integers(0, V, a.size).astype(np.int32), a.ravel(), b.ravel()], axis=1)
+    ids = np.ascontiguousarray(ids)
+    mult, rows = synth.multipliers(cfg), synth.table_rows_u32(cfg)
+    got = eg.engram_hash(torch.from_numpy(ids).to(DEV), cfg.orders, cfg.heads, mult, rows, V,
+                         t_begin=2, t_count=1).cpu().numpy()
+    want = oracle.hash_ids(ids, cfg.orders, cfg.heads, mult, rows, V, t_begin=2, t_count=1)
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("name", ["tiny", "small", "multi"])
+def test_hash_config_bit_exact(name):
+    cfg = synth.CONFIGS[name]
+    say("hash", name)
+    raw = synth.raw_ids(cfg)
+    ids_o, idx_o = oracle_ids_idx(cfg, raw)
+    ids_d = eg.engram_compress(torch.from_numpy(raw).to(DEV), torch.from_numpy(synth.comp_map(cfg)).to(DEV))
+    idx_d = eg.engram_hash(ids_d, cfg.orders, cfg.heads, synth.multipliers(cfg), synth.table_rows_u32(cfg),
+                           cfg.vocab_c)
+    assert np.array_equal(idx_d.cpu().numpy(), idx_o)
+    assert idx_o.min() >= 0 and idx_o.max() < cfg.rows
+
+
+def test_hash_windows_orders_and_large_primes():
+    """Ragged windows, orders 1..4, per-table primes up to 2^31 - 1, decode-style t_count = 1."""
+    say("hash windows")
+    rng = np.random.default_rng(1)
+    ids = rng.integers(0, 2_000_000_000, (5, 777)).astype(np.int32)
+    orders, heads = (1, 2, 3, 4), 3
+    mult = synth.hash_multipliers(123, orders, heads)
+    rows = np.array([synth.next_prime(int(x)) for x in rng.integers(2, 2**31 - 100, 12)], np.uint32)
+    rows[0], rows[1], rows[2] = 2_147_483_647, 1, 2
+    ids_d = torch.from_numpy(ids).to(DEV)
+    for t_begin, t_count in ((0, 777), (0, 1), (1, 100), (700, 77), (776, 1), (300, 0)):
+        got = eg.engram_hash(ids_d, orders, heads, mult, rows, 999, t_begin=t_begin, t_count=t_count)
+        want = oracle.hash_ids(ids, orders, heads, mult, rows, 999, t_begin=t_begin, t_count=t_count)
+        assert np.array_equal(got.cpu().numpy(), want), (t_begin, t_count)
+
+
+# ---------------------------------------------------------------------------
+# gather
+# ---------------------------------------------------------------------------
+def test_gather_tiny_fp32_and_ragged():
+    cfg = synth.CONFIGS["tiny"]
+    say("gather tiny")
+    tables = [synth.table_rows(cfg, b, torch.arange(cfg.rows)) for b in range(cfg.n_tables)]
+    tabs_d = [t.to(DEV) for t in tables]
+    rng = np.random.default_rng(2)
+    for n in (1, 5, 64, 333):
+        idx = rng.integers(0, cfg.rows, (n, cfg.n_tables)).astype(np.int32)
+        got = eg.engram_gather(torch.from_numpy(idx).to(DEV), tabs_d).cpu().numpy()
+        assert np.array_equal(got, oracle.gather(idx, [t.numpy() for t in tables])), n
+
+
+def test_gather_bf16_out_of_range_rows_zeroed():
+    say("gather bad rows")
+    rows, w, nt = 1000, 80, 16
+    tables = [torch.randn(rows, w).to(torch.bfloat16) for _ in range(nt)]
+    idx = np.random.default_rng(3).integers(0, rows, (257, nt)).astype(np.int32)
+    idx[5, 3] = rows
+    idx[100, 15] = -1
+    idx[256, 0] = 1 << 30
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    got = eg.engram_gather(torch.from_numpy(idx).to(DEV), [t.to(DEV) for t in tables], err_count=err)
+    got = host_view(got)
+    assert int(err.item()) == 3
+    ok = idx.copy()
+    for (t, b) in ((5, 3), (100, 15), (256, 0)):
+        ok[t, b] = 0
+    want = oracle.gather(ok, [host_view(t) for t in tables])
+    for (t, b) in ((5, 3), (100, 15), (256, 0)):
+        want[t, b * w:(b + 1) * w] = 0
+    assert np.array_equal(got, want)
+
+
+# ---------------------------------------------------------------------------
+# gate
+# ---------------------------------------------------------------------------
+def test_gate_fp32_tiny_full_pipeline():
+    cfg = synth.CONFIGS["tiny"]
+    say("pipeline tiny fp32")
+    inp = synth.device_inputs(cfg, DEV)
+    raw = synth.raw_ids(cfg)
+    ids_o, idx_o = oracle_ids_idx(cfg, raw)
+    ids_d = eg.engram_compress(inp["raw"], inp["map"])
+    idx_d = eg.engram_hash(ids_d, cfg.orders, cfg.heads, inp["mult"], inp["rows"], cfg.vocab_c)
+    e_d = eg.engram_gather(idx_d, inp["tables"])
+    alpha = torch.empty((1, cfg.tokens), dtype=torch.float32, device=DEV)
+    out = eg.engram_gate_forward(e_d, inp["h"], inp["wk"], inp["wv"], inp["gq"], inp["gk"], cfg.eps,
+                                 gate_out=alpha)[0]
+    e_o = oracle_memory(cfg, idx_o)
+    assert np.array_equal(host_view(e_d), e_o)
+    out_o, alpha_o = oracle_gate_tokens(cfg, 0, e_o, np.arange(cfg.tokens))
+    assert rel_err(out.cpu().numpy(), out_o) <= 1e-5
+    assert np.abs(alpha.cpu().numpy()[0] - alpha_o).max() <= 1e-5
+
+
+def _gate_case(cfg, n_tok, seed, table_std=None, gamma_jitter=None, n_branch=None, inplace=False):
+    """Random-token gate check of the bf16 path against the oracle on n_tok tokens."""
+    cfg = cfg.replace(**{k: v for k, v in dict(table_std=table_std, gamma_jitter=gamma_jitter,
+                                                     n_branch=n_branch).items() if v is not None})
+    rng = np.random.default_rng(seed)
+    idx = rng.integers(0, cfg.rows, (n_tok, cfg.n_tables)).astype(np.int32)
+    e_o = oracle_memory(cfg, idx)
+    tokens = rng.choice(1 << 20, n_tok, replace=False).astype(np.int64)
+    e_d = torch.from_numpy(e_o.view(np.int16)).to(DEV).view(torch.bfloat16)
+    hs = [synth.hidden_rows(cfg, m, torch.from_numpy(tokens)).to(DEV) for m in range(cfg.n_branch)]
+    ws = [synth.weights(cfg, m, DEV) for m in range(cfg.n_branch)]
+    gs = [synth.gains(cfg, m, DEV) for m in range(cfg.n_branch)]
+    alpha = torch.empty((cfg.n_branch, n_tok), dtype=torch.float32, device=DEV)
+    h_in = [h.clone() for h in hs]
+    out = eg.engram_gate_forward(e_d, h_in, [w[0] for w in ws], [w[1] for w in ws], [g[0] for g in gs],
+                                 [g[1] for g in gs], cfg.eps, out=h_in if inplace else None, gate_out=alpha)
+    torch.cuda.synchronize()
+    for m in range(cfg.n_branch):
+        out_o, alpha_o = oracle_gate_tokens(cfg, m, e_o, tokens)
+        err = rel_err(out[m].float().cpu().numpy(), out_o)
+        aerr = np.abs(alpha[m].cpu().numpy() - alpha_o).max()
+        upd_err = rel_err((out[m].float() - hs[m].float()).cpu().numpy(), out_o - host_bf16_to_f64(hs[m]))
+        say(f"  branch {m}: out rel err {err:.2e}, alpha abs err {aerr:.2e}, update rel err {upd_err:.2e}")
+        assert err <= 1e-2 and aerr <= ALPHA_TOL_BF16
+        if cfg.table_std >= 0.5:
+            assert upd_err <= UPDATE_TOL_STRESS
+    return out, alpha
+
+
+def host_bf16_to_f64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def test_gate_bf16_small_shape_ragged():
+    """d_model 2560, d_mem 1280; 300 tokens = one full and one ragged 256-token tile."""
+    say("gate bf16 small 300")
+    _gate_case(synth.CONFIGS["small"], 300, seed=10)
+
+
+def test_gate_bf16_stress_unit_tables_and_gains():
+    """Tables ~N(0,1) and gains != 1, so alpha * v is comparable to h."""
+    say("gate bf16 stress")
+    _gate_case(synth.CONFIGS["small"], 97, seed=11, table_std=1.0, gamma_jitter=0.3)
+
+
+def test_gate_bf16_multi_branch_in_place():
+    say("gate bf16 multi-branch in place")
+    _gate_case(synth.CONFIGS["multi"], 130, seed=12, table_std=0.5, inplace=True)
+
+
+def test_gate_bf16_zero_value_and_closed_gate_are_identity():
+    """W_V = 0, or a gate driven to 0, leaves h bit-exact."""
+    cfg = synth.CONFIGS["small"]
+    say("gate bf16 identities")
+    n = 64
+    e = (torch.randn(n, cfg.d_mem) * 0.5).to(torch.bfloat16).to(DEV)
+    h = torch.randn(n, cfg.d_model).to(torch.bfloat16).to(DEV)
+    wk, wv = (w.to(DEV) for w in synth.weights(cfg, 0))
+    gq, gk = (g.to(DEV) for g in synth.gains(cfg, 0))
+    out = eg.engram_gate_forward(e, [h], [wk], [torch.zeros_like(wv)], [gq], [gk], cfg.eps)[0]
+    assert torch.equal(out.view(torch.int16), h.view(torch.int16))
+    # h = -k direction with a huge query gain: logit -> -inf, alpha == 0 exactly
+    en = e.float() / torch.sqrt((e.float() ** 2).mean(1, keepdim=True) + cfg.eps)
+    k = en @ wk.float().T
+    h2 = (-k).to(torch.bfloat16).contiguous()
+    big = torch.full_like(gq, 1e4)
+    alpha = torch.empty((1, n), dtype=torch.float32, device=DEV)
+    out2 = eg.engram_gate_forward(e, [h2], [wk], [wv], [big], [gk], cfg.eps, gate_out=alpha)[0]
+    assert torch.all(alpha == 0)
+    assert torch.equal(out2.view(torch.int16), h2.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# prefetch from pinned host tables
+# ---------------------------------------------------------------------------
+def test_prefetch_host_equals_gather():
+    cfg = synth.CONFIGS["small"]
+    say("prefetch host")
+    rows = 50_021
+    tables = [synth.table_rows(cfg, b, torch.arange(rows)) for b in range(cfg.n_tables)]
+    pinned = [t.pin_memory() for t in tables]
+    dev_t = [t.to(DEV) for t in tables]
+    idx = torch.from_numpy(np.random.default_rng(4).integers(0, rows, (256, 16)).astype(np.int32)).to(DEV)
+    a = eg.engram_gather(idx, dev_t)
+    b = eg.engram_prefetch_host(idx, pinned, [rows] * 16, cfg.w, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    # engram_host_alloc'd tables
+    addrs = []
+    try:
+        for t in tables:
+            p = eg.host_alloc(t.numel() * 2)
+            addrs.append(p)
+            torch.from_numpy(host_view(t)).numpy()  # keep a CPU copy alive
+            import ctypes
+            ctypes.memmove(p, t.view(torch.int16).numpy().ctypes.data, t.numel() * 2)
+        c = eg.engram_prefetch_host(idx, addrs, [rows] * 16, cfg.w, torch.bfloat16)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+    finally:
+        for p in addrs:
+            eg.host_free(p)
+    # pageable memory is refused with a clear error
+    with pytest.raises(eg.EngramError):
+        eg.engram_prefetch_host(idx, [t.data_ptr() for t in tables], [rows] * 16, cfg.w, torch.bfloat16)
