@@ -8,31 +8,45 @@
 //   alpha = sigmoid(q . k / sqrt(d_model)),   out_t = h_t + alpha v
 //
 // The two projections are dense contractions [tokens x d_mem] x [d_mem x d_model]
-// and run as bf16 MFMA GEMMs (v_mfma_f32_32x32x16_bf16).  The catch is that
-// alpha needs the whole d_model-long dot product q . k before any element of
-// the value can be scaled, so the work is split in two launches over the same
-// tiling:
-//   phase K: acc = W_K' e^T per (feature tile, token tile), W_K' = W_K * diag(gk)
-//            (prepared once per call by scale_cols_kernel);  the epilogue
-//            reduces  sum_f h[t,f] gq[f] acc[f,t]  and  sum_f h[t,f]^2  over the
-//            tile's features into per-(feature tile, token) partials; the main
-//            loop also squares one slice of the memory row (k-steps with
-//            kt % n_ftiles == ftile) so that the sums of e^2 come for free;
+// and run as bf16 MFMA GEMMs (v_mfma_f32_32x32x16_bf16).  alpha needs the whole
+// d_model-long dot product q . k before any element of the value can be scaled,
+// so the work is two launches over the same tiling:
+//   phase K: acc = W_K' e^T per (feature tile, token tile), W_K' = W_K diag(gk)
+//            (prepared once per call by scale_cols_kernel); the epilogue reduces
+//            sum_f h[t,f] gq[f] acc[f,t] and sum_f h[t,f]^2 over the tile's
+//            features into per-(feature tile, token) partials; the main loop
+//            also sums e^2 over one slice of the memory row (k-steps with
+//            kt % n_ftiles == ftile), so every tile does 1/n_ftiles of it;
 //   phase V: a prologue turns the partials into alpha for the tile's tokens
-//            (fixed-order sums, so results are bit-reproducible); the main loop
-//            is acc = W_V e^T and the epilogue writes out = h + alpha acc.
-// Since  q . k = (sum_f h_f gq_f k~_f) / (rms(h) rms(e))  with k~ = W_K' e, the
+//            (fixed-order sums, bit-reproducible); the main loop is
+//            acc = W_V e^T and the epilogue writes out = h + alpha acc.
+// Since q . k = (sum_f h_f gq_f k~_f) / (rms(h) rms(e)) with k~ = W_K' e, the
 // RMSNorm scales are applied to the reduced scalar, never to a tensor.
 //
-// Tiling: 256 features x 256 tokens per workgroup, BK = 64, four wavefronts in
-// a 2 x 2 arrangement, each owning 128 x 128 outputs = 4 x 4 MFMA 32x32 tiles
-// (256 fp32 accumulators per lane).  Features are the MFMA rows, so a lane's
-// 16 accumulators of one tile belong to ONE token and 4 groups of 4
-// consecutive features: the epilogue's h loads and out stores are 8-byte
-// vectors, and the per-token reductions are plain adds inside a lane.
-// Operands are staged global -> registers -> LDS (double-buffered, one barrier
-// per k-step, next k-step's global loads in flight during the MFMAs); LDS rows
-// are 128 B with the 16-B chunk index XOR-swizzled by the row.
+// Tiling.  256 features x 256 tokens per workgroup, four wavefronts in 2 x 2,
+// each owning 128 x 128 outputs = 4 x 4 MFMA 32x32 tiles (256 fp32
+// accumulators per lane).  Features are the MFMA rows, so all 16 accumulators
+// of a lane in one tile belong to ONE token; the weight rows are loaded in a
+// permuted order (bits 2 and 3 of the row index swapped inside each 32-row
+// tile) so that a lane's accumulator groups 0-1 and 2-3 each cover 8
+// consecutive features: every epilogue access is a 16-byte vector.
+//
+// Main loop.  BK = 64 per k-step, double-buffered LDS (2 x 64 KB).  The next
+// k-step's operands are loaded global -> registers (16-B native vectors, so the
+// staging array stays in registers) while the current k-step's 64 MFMAs run,
+// then written to the other LDS buffer; one LDS-only barrier per k-step (a
+// plain __syncthreads() would also wait for the in-flight global loads).
+// LDS rows are 128 B; the 16-B chunk index is XOR-swizzled with
+// (r & 7) ^ ((r >> 3) & 1), which keeps the fragment reads (32 consecutive
+// rows, one chunk) free of bank conflicts for 128- and 256-byte LDS clocks.
+//
+// Epilogue.  The LDS buffers are reused for the h tile (256 tokens x 256
+// features, 128 KB), loaded with coalesced 16-byte loads; 16-byte chunks
+// are swizzled by (token & 31) so that 32 lanes reading 32 tokens hit distinct
+// banks.  Phase V writes out into the same LDS tile and then streams it to
+// HBM with coalesced 16-byte stores.
+#include <type_traits>
+
 #include "engram_internal.h"
 
 namespace engram {
@@ -40,17 +54,23 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16-B chunk (native vector: stays in registers)
 
 constexpr int BF = 256;   // features per workgroup
 constexpr int BT = 256;   // tokens per workgroup
-constexpr int BK = 64;    // contraction depth per k-step
+constexpr int BK = 64;    // contraction depth per stage
+constexpr int NSTAGE = 2;  // LDS double buffer
 constexpr int NTHR = 256;
 constexpr int WF = 128, WT = 128;           // per-wavefront tile
 constexpr int MF = WF / 32, MT = WT / 32;   // MFMA tiles per wavefront
-constexpr int A_CHUNKS = BF * BK / 8 / NTHR;  // 16-B chunks of the weight tile per thread
-constexpr int B_CHUNKS = BT * BK / 8 / NTHR;  // 16-B chunks of the memory tile per thread
-constexpr int LDS_A = BF * BK;              // bf16 elements
-constexpr int LDS_B = BT * BK;
+constexpr int ROW_CH = BK / 8;              // 16-B chunks per LDS row (8)
+constexpr int STAGE_A = BF * BK;            // bf16 elements of the weight tile in a stage
+constexpr int STAGE = (BF + BT) * BK;       // bf16 elements per stage
+constexpr int CH_A = BF * ROW_CH / NTHR;   // 16-B chunks of the weight tile per thread per stage
+constexpr int CH_B = BT * ROW_CH / NTHR;   // 16-B chunks of the memory tile per thread per stage
+constexpr int H_CH = BF / 8;               // 16-B chunks per h row in the epilogue tile (32)
+constexpr int H_LOADS = BT * H_CH / NTHR;  // 32 chunks per thread
+constexpr int SMEM_ELEMS = (NSTAGE * STAGE > BT * BF) ? NSTAGE * STAGE : BT * BF;
 
 enum { PHASE_K = 0, PHASE_V = 1 };
 
@@ -63,12 +83,31 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// 16-B chunk position of logical chunk `c` in LDS row `row`
-__device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 7); }
+// Physical 16-B chunk of logical chunk c in a 128-B stage row r.  Fragment reads
+// hit 32 consecutive rows at one logical chunk; (r & 7) ^ ((r >> 3) & 1) keeps
+// them conflict-free whether the LDS serves 128 or 256 bytes per clock.
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r & 7) ^ ((r >> 3) & 1)); }
+// LDS element offset of 16-B chunk q (row q / ROW_CH) of a stage operand tile
+__device__ __forceinline__ int st_off(int q) {
+  const int r = q / ROW_CH;
+  return r * BK + swz(r, q % ROW_CH) * 8;
+}
+// feature offset (inside a 32-row MFMA tile) held by MFMA row rho: bits 2 and 3 swapped
+__device__ __forceinline__ int tile_row_feature(int rho) {
+  return (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1);
+}
 
-__device__ __forceinline__ float sum_sq8(const uint4& v) {
-  float s = 0.f;
+// Workgroup barrier that orders LDS accesses only: unlike __syncthreads() it does
+// not wait for this wave's in-flight global loads (the next stages' prefetch).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ float sumsq8(const uint4& v) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  float s = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float a = bf16_lo(w[i]), b = bf16_hi(w[i]);
@@ -81,18 +120,29 @@ __device__ __forceinline__ float sum_sq8(const uint4& v) {
 template <int PHASE>
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gate_mfma_kernel(const GateArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][LDS_A + LDS_B];
-  __shared__ float s_red[2][2][BT];  // [wave row][dot, hh][token]
+  __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM_ELEMS];  // stage ring, then h tile
+  __shared__ float s_red[2][2][BT];  // [feature-wave][dot, hh][token]
   __shared__ float s_alpha[BT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wf = wave >> 1, wt = wave & 1;
-  const int ftile = blockIdx.x;
-  const int m = blockIdx.z;
+
+  // ---- XCD-aware tile order: hardware block b runs on XCD b % 8; give each XCD a
+  // contiguous run of logical tiles (feature tile fastest, so an XCD's concurrent
+  // blocks share memory-vector tiles in its L2)
+  const int n_ttiles = (int)((a.n_tok + BT - 1) / BT);
+  const uint32_t nblocks = gridDim.x;
+  uint32_t logical = blockIdx.x;
+  if ((nblocks & 7) == 0) logical = (blockIdx.x & 7) * (nblocks >> 3) + (blockIdx.x >> 3);
+  const int ftile = (int)(logical % (uint32_t)a.n_ftiles);
+  const uint32_t rest = logical / (uint32_t)a.n_ftiles;
+  const int ttile = (int)(rest % (uint32_t)n_ttiles);
+  const int m = (int)(rest / (uint32_t)n_ttiles);
+
   const int f0 = ftile * BF;
-  const int64_t t0 = (int64_t)blockIdx.y * BT;
+  const int64_t t0 = (int64_t)ttile * BT;
   const int64_t n_tok = a.n_tok;
   const int d_mem = a.d_mem, d_model = a.d_model;
 
@@ -103,70 +153,65 @@ void gate_mfma_kernel(const GateArgs a) {
 
   // ---- phase V prologue: alpha for this tile's tokens
   if (PHASE == PHASE_V) {
-    if (tid < BT) {
-      const int64_t t = t0 + tid;
-      float alpha = 0.f;
-      if (t < n_tok) {
-        float dot = 0.f, hh = 0.f, ee = 0.f;
-        const int64_t base = (int64_t)m * a.n_ftiles * n_tok + t;
-        for (int j = 0; j < a.n_ftiles; ++j) {
-          dot += a.part_dot[base + (int64_t)j * n_tok];
-          hh += a.part_hh[base + (int64_t)j * n_tok];
-          ee += a.ee[base + (int64_t)j * n_tok];
-        }
-        const float rms_h = sqrtf(hh / (float)d_model + a.eps);
-        const float rms_e = sqrtf(ee / (float)d_mem + a.eps);
-        const float logit = dot / (rms_h * rms_e) * a.inv_sqrt_d;
-        alpha = 1.f / (1.f + expf(-logit));
-        if (ftile == 0 && a.gate_out != nullptr) a.gate_out[(int64_t)m * n_tok + t] = alpha;
+    const int64_t t = t0 + tid;
+    float alpha = 0.f;
+    if (t < n_tok) {
+      float dot = 0.f, hh = 0.f, ee = 0.f;
+      const int64_t base = (int64_t)m * a.n_ftiles * n_tok + t;
+      for (int j = 0; j < a.n_ftiles; ++j) {
+        dot += a.part_dot[base + (int64_t)j * n_tok];
+        hh += a.part_hh[base + (int64_t)j * n_tok];
+        ee += a.ee[base + (int64_t)j * n_tok];
       }
-      s_alpha[tid] = alpha;
+      const float rms_h = sqrtf(hh / (float)d_model + a.eps);
+      const float rms_e = sqrtf(ee / (float)d_mem + a.eps);
+      const float logit = dot / (rms_h * rms_e) * a.inv_sqrt_d;
+      alpha = 1.f / (1.f + expf(-logit));
+      if (ftile == 0 && a.gate_out != nullptr) a.gate_out[(int64_t)m * n_tok + t] = alpha;
     }
+    s_alpha[tid] = alpha;
   }
 
-  // ---- global -> register staging addresses (row-clamped: padded rows read valid memory)
-  const int lrow = tid >> 3;  // + 32 * i
-  const int lcc = tid & 7;
-  const uint16_t* a_src[A_CHUNKS];
-  const uint16_t* b_src[B_CHUNKS];
+  // ---- global -> register -> LDS staging.  Thread tid moves 16-B chunks
+  // q = tid + NTHR * i of each operand tile: row q / ROW_CH, logical chunk q % ROW_CH.
+  // All offsets are 32-bit from wave-uniform bases, so the loads take the
+  // scalar-base + vector-offset form and only one VGPR per chunk stays live.
+  const uint16_t* Et0 = E + t0 * d_mem;   // memory rows of this token tile
+  uint32_t a_off[CH_A], b_off[CH_B];
 #pragma unroll
-  for (int i = 0; i < A_CHUNKS; ++i) {
-    int f = f0 + lrow + 32 * i;
-    f = f < d_model ? f : d_model - 1;
-    a_src[i] = W + (int64_t)f * d_mem + lcc * 8;
+  for (int i = 0; i < CH_A; ++i) {
+    const int q = tid + NTHR * i;
+    const int r = q / ROW_CH, c = q % ROW_CH;
+    int f = f0 + (r & ~31) + tile_row_feature(r & 31);
+    f = f < d_model ? f : d_model - 1;   // rows past d_model: any valid row, result unused
+    a_off[i] = (uint32_t)f * (uint32_t)d_mem + c * 8;
   }
 #pragma unroll
-  for (int i = 0; i < B_CHUNKS; ++i) {
-    int64_t t = t0 + lrow + 32 * i;
-    t = t < n_tok ? t : n_tok - 1;
-    b_src[i] = E + t * d_mem + lcc * 8;
+  for (int i = 0; i < CH_B; ++i) {
+    const int q = tid + NTHR * i;
+    const int r = q / ROW_CH, c = q % ROW_CH;
+    const int rr = t0 + r < n_tok ? r : (int)(n_tok - 1 - t0);  // padded tokens: a valid row
+    b_off[i] = (uint32_t)rr * (uint32_t)d_mem + c * 8;
   }
 
-  uint4 ra[A_CHUNKS], rb[B_CHUNKS];
-  float ee_acc[B_CHUNKS];
-#pragma unroll
-  for (int i = 0; i < B_CHUNKS; ++i) ee_acc[i] = 0.f;
 
-  auto load_global = [&](int kt) {
-#pragma unroll
-    for (int i = 0; i < A_CHUNKS; ++i) ra[i] = *reinterpret_cast<const uint4*>(a_src[i] + kt * BK);
-#pragma unroll
-    for (int i = 0; i < B_CHUNKS; ++i) rb[i] = *reinterpret_cast<const uint4*>(b_src[i] + kt * BK);
-  };
-  auto store_lds = [&](int buf) {
-    uint16_t* la = lds[buf];
-    uint16_t* lb = lds[buf] + LDS_A;
-#pragma unroll
-    for (int i = 0; i < A_CHUNKS; ++i) {
-      const int row = lrow + 32 * i;
-      *reinterpret_cast<uint4*>(la + row * BK + swz(row, lcc) * 8) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < B_CHUNKS; ++i) {
-      const int row = lrow + 32 * i;
-      *reinterpret_cast<uint4*>(lb + row * BK + swz(row, lcc) * 8) = rb[i];
-    }
-  };
+  u32x4 ra[CH_A], rb[CH_B];  // the next stage, in flight while the current one is consumed
+#define ENGRAM_LOAD_STAGE(kt)                                                              \
+  do {                                                                                     \
+    const int k0_ = (kt) * BK;                                                             \
+    _Pragma("unroll") for (int i = 0; i < CH_A; ++i)                                       \
+        ra[i] = *reinterpret_cast<const u32x4*>(W + a_off[i] + k0_);                       \
+    _Pragma("unroll") for (int i = 0; i < CH_B; ++i)                                       \
+        rb[i] = *reinterpret_cast<const u32x4*>(Et0 + b_off[i] + k0_);                     \
+  } while (0)
+#define ENGRAM_STORE_STAGE(kt)                                                             \
+  do {                                                                                     \
+    uint16_t* st_ = smem + ((kt) & 1) * STAGE;                                             \
+    _Pragma("unroll") for (int i = 0; i < CH_A; ++i)                                       \
+        *reinterpret_cast<u32x4*>(st_ + st_off(tid + NTHR * i)) = ra[i];                   \
+    _Pragma("unroll") for (int i = 0; i < CH_B; ++i)                                       \
+        *reinterpret_cast<u32x4*>(st_ + STAGE_A + st_off(tid + NTHR * i)) = rb[i];         \
+  } while (0)
 
   floatx16 acc[MF][MT];
 #pragma unroll
@@ -177,37 +222,38 @@ void gate_mfma_kernel(const GateArgs a) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int nk = d_mem / BK;
-  load_global(0);
-  if (PHASE == PHASE_K && (0 % a.n_ftiles) == ftile) {
-#pragma unroll
-    for (int i = 0; i < B_CHUNKS; ++i) ee_acc[i] += sum_sq8(rb[i]);
-  }
-  store_lds(0);
-  __syncthreads();
+  ENGRAM_LOAD_STAGE(0);
+  ENGRAM_STORE_STAGE(0);
+  lds_barrier();
 
   const int arow0 = wf * WF + (lane & 31);
   const int brow0 = wt * WT + (lane & 31);
   const int khalf = lane >> 5;
+  float ee_acc = 0.f;  // phase K: sum of e^2 of token row `tid` over this tile's k slice
 
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) load_global(kt + 1);
-    const uint16_t* la = lds[cur];
-    const uint16_t* lb = lds[cur] + LDS_A;
+    // next stage's global loads fly during this stage's MFMAs
+    if (kt + 1 < nk) ENGRAM_LOAD_STAGE(kt + 1);
+    const uint16_t* la = smem + (kt & 1) * STAGE;
+    const uint16_t* lb = la + STAGE_A;
+    if (PHASE == PHASE_K && (kt % a.n_ftiles) == ftile) {
+#pragma unroll
+      for (int c = 0; c < ROW_CH; ++c)
+        ee_acc += sumsq8(*reinterpret_cast<const uint4*>(lb + tid * BK + c * 8));
+    }
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s) {
       const int c = s * 2 + khalf;
       bf16x8 af[MF], bfr[MT];
 #pragma unroll
       for (int i = 0; i < MF; ++i) {
-        const int row = arow0 + i * 32;
-        af[i] = *reinterpret_cast<const bf16x8*>(la + row * BK + swz(row, c) * 8);
+        const int r = arow0 + i * 32;
+        af[i] = *reinterpret_cast<const bf16x8*>(la + r * BK + swz(r, c) * 8);
       }
 #pragma unroll
       for (int j = 0; j < MT; ++j) {
-        const int row = brow0 + j * 32;
-        bfr[j] = *reinterpret_cast<const bf16x8*>(lb + row * BK + swz(row, c) * 8);
+        const int r = brow0 + j * 32;
+        bfr[j] = *reinterpret_cast<const bf16x8*>(lb + r * BK + swz(r, c) * 8);
       }
 #pragma unroll
       for (int i = 0; i < MF; ++i)
@@ -215,99 +261,131 @@ void gate_mfma_kernel(const GateArgs a) {
         for (int j = 0; j < MT; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
     }
-    if (more) {
-      if (PHASE == PHASE_K && ((kt + 1) % a.n_ftiles) == ftile) {
-#pragma unroll
-        for (int i = 0; i < B_CHUNKS; ++i) ee_acc[i] += sum_sq8(rb[i]);
-      }
-      store_lds(cur ^ 1);
-    }
-    __syncthreads();
+    // the other buffer was last read in k-step kt-1, which every wave finished
+    // before the previous barrier
+    if (kt + 1 < nk) ENGRAM_STORE_STAGE(kt + 1);
+    lds_barrier();
+  }
+#undef ENGRAM_LOAD_STAGE
+#undef ENGRAM_STORE_STAGE
+
+  // Everything below re-derives its indices from an opaque copy of the thread id, so
+  // the compiler cannot compute epilogue addresses before the loop and keep them
+  // live (in registers the main loop needs) across it.
+  int etid = tid;
+  asm volatile("" : "+v"(etid));
+  const int elane = etid & 63, ewave = etid >> 6;
+  const int ewf = ewave >> 1, ewt = ewave & 1;
+
+  if (PHASE == PHASE_K) {
+    const int64_t t = t0 + etid;
+    if (t < n_tok) a.ee[((int64_t)m * a.n_ftiles + ftile) * n_tok + t] = ee_acc;
   }
 
-  // ---- epilogues.  Lane owns token column (lane & 31) of every MFMA tile and
-  // features 8*g + 4*(lane >> 5) + {0..3} of it (g = 0..3).
-  const int fl = (lane >> 5) * 4;
-  if (PHASE == PHASE_K) {
-    // sums of e^2 over this block's slice of the memory row
-    float* ee_out = a.ee + ((int64_t)m * a.n_ftiles + ftile) * n_tok;
+  // ---- h tile [BT tokens][BF features] into LDS (16-B chunks swizzled by token);
+  // the last loop barrier already retired every read of the stage ring
 #pragma unroll
-    for (int i = 0; i < B_CHUNKS; ++i) {
-      float v = ee_acc[i];
-      v += __shfl_xor(v, 1, 64);
-      v += __shfl_xor(v, 2, 64);
-      v += __shfl_xor(v, 4, 64);
-      const int64_t t = t0 + lrow + 32 * i;
-      if (lcc == 0 && t < n_tok) ee_out[t] = v;
+  for (int half = 0; half < 2; ++half) {
+    uint4 hv[H_LOADS / 2];
+#pragma unroll
+    for (int i = 0; i < H_LOADS / 2; ++i) {
+      const int p = (half * (H_LOADS / 2) + i) * NTHR + etid;
+      const int tl = p / H_CH;
+      const int c = (p % H_CH) ^ (tl & 31);
+      int64_t t = t0 + tl;
+      t = t < n_tok ? t : n_tok - 1;
+      int f = f0 + c * 8;
+      f = f < d_model ? f : 0;
+      hv[i] = *reinterpret_cast<const uint4*>(H + t * d_model + f);
     }
+#pragma unroll
+    for (int i = 0; i < H_LOADS / 2; ++i) {
+      const int p = (half * (H_LOADS / 2) + i) * NTHR + etid;
+      *reinterpret_cast<uint4*>(smem + p * 8) = hv[i];
+    }
+  }
+  __syncthreads();
+
+  // Lane (token column tl) holds, for MFMA tile (i, j) and pair gp, features
+  // fl = ewf*WF + i*32 + gp*16 + (elane>>5)*8 + 0..7 in acc[i][j][8*gp + 0..7].
+  const int hsel = (elane >> 5) * 8;
+  if (PHASE == PHASE_K) {
     const uint16_t* GQ = (const uint16_t*)a.gq[m];
 #pragma unroll
     for (int j = 0; j < MT; ++j) {
-      const int tl = wt * WT + j * 32 + (lane & 31);
-      const int64_t t = t0 + tl;
+      const int tl = ewt * WT + j * 32 + (elane & 31);
       float dot = 0.f, hh = 0.f;
-      if (t < n_tok) {
-        const uint16_t* hrow = H + t * d_model;
 #pragma unroll
-        for (int i = 0; i < MF; ++i) {
+      for (int i = 0; i < MF; ++i) {
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int f = f0 + wf * WF + i * 32 + g * 8 + fl;
-            if (f < d_model) {
-              const uint2 hv = *reinterpret_cast<const uint2*>(hrow + f);
-              const uint2 gv = *reinterpret_cast<const uint2*>(GQ + f);
-              const float h0 = bf16_lo(hv.x), h1 = bf16_hi(hv.x), h2 = bf16_lo(hv.y), h3 = bf16_hi(hv.y);
-              dot += h0 * bf16_lo(gv.x) * acc[i][j][g * 4 + 0];
-              dot += h1 * bf16_hi(gv.x) * acc[i][j][g * 4 + 1];
-              dot += h2 * bf16_lo(gv.y) * acc[i][j][g * 4 + 2];
-              dot += h3 * bf16_hi(gv.y) * acc[i][j][g * 4 + 3];
-              hh += h0 * h0 + h1 * h1 + h2 * h2 + h3 * h3;
+        for (int gp = 0; gp < 2; ++gp) {
+          const int fl = ewf * WF + i * 32 + gp * 16 + hsel;
+          if (f0 + fl < d_model) {
+            const int c = (fl >> 3) ^ (tl & 31);
+            const uint4 hv = *reinterpret_cast<const uint4*>(smem + tl * BF + c * 8);
+            const uint4 gv = *reinterpret_cast<const uint4*>(GQ + f0 + fl);
+            const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
+            const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float h0 = bf16_lo(hw[q]), h1 = bf16_hi(hw[q]);
+              dot += h0 * bf16_lo(gw[q]) * acc[i][j][gp * 8 + 2 * q];
+              dot += h1 * bf16_hi(gw[q]) * acc[i][j][gp * 8 + 2 * q + 1];
+              hh += h0 * h0 + h1 * h1;
             }
           }
         }
       }
       dot += __shfl_xor(dot, 32, 64);
       hh += __shfl_xor(hh, 32, 64);
-      if (lane < 32) {
-        s_red[wf][0][tl] = dot;
-        s_red[wf][1][tl] = hh;
+      if (elane < 32) {
+        s_red[ewf][0][tl] = dot;
+        s_red[ewf][1][tl] = hh;
       }
     }
     __syncthreads();
-    if (tid < BT) {
-      const int64_t t = t0 + tid;
-      if (t < n_tok) {
-        const int64_t o = ((int64_t)m * a.n_ftiles + ftile) * n_tok + t;
-        a.part_dot[o] = s_red[0][0][tid] + s_red[1][0][tid];
-        a.part_hh[o] = s_red[0][1][tid] + s_red[1][1][tid];
-      }
+    const int64_t t = t0 + etid;
+    if (t < n_tok) {
+      const int64_t o = ((int64_t)m * a.n_ftiles + ftile) * n_tok + t;
+      a.part_dot[o] = s_red[0][0][etid] + s_red[1][0][etid];
+      a.part_hh[o] = s_red[0][1][etid] + s_red[1][1][etid];
     }
   } else {
-    uint16_t* O = (uint16_t*)a.out[m];
 #pragma unroll
     for (int j = 0; j < MT; ++j) {
-      const int tl = wt * WT + j * 32 + (lane & 31);
-      const int64_t t = t0 + tl;
-      if (t >= n_tok) continue;
+      const int tl = ewt * WT + j * 32 + (elane & 31);
       const float alpha = s_alpha[tl];
-      const uint16_t* hrow = H + t * d_model;
-      uint16_t* orow = O + t * d_model;
 #pragma unroll
       for (int i = 0; i < MF; ++i) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int f = f0 + wf * WF + i * 32 + g * 8 + fl;
-          if (f < d_model) {
-            const uint2 hv = *reinterpret_cast<const uint2*>(hrow + f);
-            uint2 o;
-            o.x = pack_bf16(bf16_lo(hv.x) + alpha * acc[i][j][g * 4 + 0],
-                            bf16_hi(hv.x) + alpha * acc[i][j][g * 4 + 1]);
-            o.y = pack_bf16(bf16_lo(hv.y) + alpha * acc[i][j][g * 4 + 2],
-                            bf16_hi(hv.y) + alpha * acc[i][j][g * 4 + 3]);
-            *reinterpret_cast<uint2*>(orow + f) = o;
-          }
+        for (int gp = 0; gp < 2; ++gp) {
+          const int fl = ewf * WF + i * 32 + gp * 16 + hsel;
+          const int c = (fl >> 3) ^ (tl & 31);
+          uint4* cell = reinterpret_cast<uint4*>(smem + tl * BF + c * 8);
+          const uint4 hv = *cell;
+          const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
+          uint32_t ow[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            ow[q] = pack_bf16(bf16_lo(hw[q]) + alpha * acc[i][j][gp * 8 + 2 * q],
+                              bf16_hi(hw[q]) + alpha * acc[i][j][gp * 8 + 2 * q + 1]);
+          *cell = make_uint4(ow[0], ow[1], ow[2], ow[3]);
         }
       }
+    }
+    __syncthreads();
+    uint16_t* O = (uint16_t*)a.out[m];
+#pragma unroll 4
+    for (int i = 0; i < BT * H_CH / NTHR; ++i) {
+      const int p = i * NTHR + etid;
+      const int tl = p / H_CH;
+      const int phys = p % H_CH;
+      const int c = phys ^ (tl & 31);
+      const int64_t t = t0 + tl;
+      const int f = f0 + c * 8;
+      if (t < n_tok && f < d_model)
+        *reinterpret_cast<uint4*>(O + t * d_model + f) =
+            *reinterpret_cast<const uint4*>(smem + tl * BF + phys * 8);
     }
   }
 }
@@ -331,16 +409,15 @@ __global__ __launch_bounds__(256) void scale_cols_kernel(const uint16_t* __restr
 }
 
 struct ScratchLayout {
-  size_t wk_bytes, part_elems, total;
+  size_t wk_bytes, part_bytes, total;
 };
 
 ScratchLayout layout_for(const GateArgs& a) {
   ScratchLayout L;
-  L.wk_bytes = (size_t)a.n_branch * a.d_model * a.d_mem * 2;
-  L.wk_bytes = (L.wk_bytes + 255) & ~(size_t)255;
-  L.part_elems = (size_t)a.n_branch * a.n_ftiles * (size_t)a.n_tok;
-  const size_t part_bytes = ((L.part_elems * 4) + 255) & ~(size_t)255;
-  L.total = L.wk_bytes + 3 * part_bytes;
+  L.wk_bytes = ((size_t)a.n_branch * a.d_model * a.d_mem * 2 + 255) & ~(size_t)255;
+  const size_t part_elems = (size_t)a.n_branch * a.n_ftiles * (size_t)a.n_tok;
+  L.part_bytes = (part_elems * 4 + 255) & ~(size_t)255;
+  L.total = L.wk_bytes + 3 * L.part_bytes;
   return L;
 }
 
@@ -357,7 +434,6 @@ void launch_gate_bf16(const GateArgs& a_in, hipStream_t s) {
   GateArgs a = a_in;
   const ScratchLayout L = layout_for(a);
   char* base = (char*)a_in.part_dot;
-  const size_t part_bytes = ((L.part_elems * 4) + 255) & ~(size_t)255;
   for (int m = 0; m < a.n_branch; ++m) {
     uint16_t* dst = (uint16_t*)(base + (size_t)m * a.d_model * a.d_mem * 2);
     const int64_t n8 = (int64_t)a.d_model * a.d_mem / 8;
@@ -366,12 +442,13 @@ void launch_gate_bf16(const GateArgs& a_in, hipStream_t s) {
     a.wk[m] = dst;
   }
   a.part_dot = (float*)(base + L.wk_bytes);
-  a.part_hh = (float*)(base + L.wk_bytes + part_bytes);
-  a.ee = (float*)(base + L.wk_bytes + 2 * part_bytes);
+  a.part_hh = (float*)(base + L.wk_bytes + L.part_bytes);
+  a.ee = (float*)(base + L.wk_bytes + 2 * L.part_bytes);
 
-  const dim3 grid((unsigned)a.n_ftiles, (unsigned)((a.n_tok + BT - 1) / BT), (unsigned)a.n_branch);
-  hipLaunchKernelGGL(gate_mfma_kernel<PHASE_K>, grid, dim3(NTHR), 0, s, a);
-  hipLaunchKernelGGL(gate_mfma_kernel<PHASE_V>, grid, dim3(NTHR), 0, s, a);
+  const int64_t n_ttiles = (a.n_tok + BT - 1) / BT;
+  const unsigned blocks = (unsigned)(n_ttiles * a.n_ftiles * a.n_branch);
+  hipLaunchKernelGGL(gate_mfma_kernel<PHASE_K>, dim3(blocks), dim3(NTHR), 0, s, a);
+  hipLaunchKernelGGL(gate_mfma_kernel<PHASE_V>, dim3(blocks), dim3(NTHR), 0, s, a);
 }
 
 }  // namespace engram
