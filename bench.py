@@ -8,10 +8,15 @@ Prints ONE JSON line with tokens/s, the per-call breakdown, the roofline of the
 dominant kernel (the gate) and the CPU oracle's tokens/s on a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--config small|multi|large|tiny]
+    python bench.py --calibrate-copy MIB     # plain device copy, for HBM counter scaling
+
+Between timed steps (outside the timed events) a scratch buffer larger than the
+last-level cache is rewritten, so every step starts with cold L2 and MALL.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -24,6 +29,8 @@ METRIC = "Engram tokens/s (hash+gather+gate); gather HBM GB/s & MFMA util vs pea
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3       # fp32 vector / matrix
+GATE_SOURCE = os.path.join(ROOT, "hashed_gram_embedding_hash_amd", "csrc", "gate_bf16.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_persistent_kernel_small_hbm_traffic.txt")
 
 
 def parse():
@@ -34,6 +41,9 @@ def parse():
     p.add_argument("--config", default="small")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time of the CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--flush-mb", type=int, default=512, help="cache-flush buffer rewritten between steps (0: off)")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                   help="only run a plain device-to-device copy of MIB MiB three times and exit")
     return p.parse_args()
 
 
@@ -59,6 +69,45 @@ def algorithmic(cfg):
         "gate": {"flops": 4 * dm * d * M * T,
                  "bytes": dm * es * T + M * (2 * d * dm * es + 2 * d * es * T)},
     }
+
+
+def gate_source_sha():
+    with open(GATE_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(cfg):
+    """HBM bytes per launch of the gate's persistent kernel, from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE scaled by a plain copy of known size).  None when
+    the summary is missing, covers another workload, or the kernel source has changed
+    since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith(" "):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("workload") != cfg.name or kv.get("source_sha256") != gate_source_sha():
+        return None
+    try:
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy(mib):
+    import torch
+    n = mib * (1 << 20) // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy": "torch bf16 device copy", "bytes_read": 2 * n, "bytes_written": 2 * n,
+                      "kib_read": 2 * n / 1024, "kib_written": 2 * n / 1024}), flush=True)
 
 
 def cpu_baseline(cfg, target_s):
@@ -116,6 +165,10 @@ def main():
                                    "the Engram path here is single-GPU (no multi-GPU runs)"}))
         sys.exit(2)
 
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
+
     import torch
     import synth
     import hashed_gram_embedding_hash_amd as eg
@@ -148,6 +201,8 @@ def main():
         if ev is not None:
             ev[4].record()
 
+    flush = (torch.empty(args.flush_mb << 18, dtype=torch.float32, device=dev) if args.flush_mb > 0 else None)
+
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
@@ -158,11 +213,13 @@ def main():
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(float(i))       # evicts L2 and MALL; outside the step's events
         step(evs[i])
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    total_ms = evs[0][0].elapsed_time(evs[-1][4])
-    ms_step = total_ms / args.steps
+    # per-step time: first to last event of each step (the flush between steps excluded)
+    ms_step = sum(evs[i][0].elapsed_time(evs[i][4]) for i in range(args.steps)) / args.steps
     names = ["compress", "hash", "gather", "gate"]
     per = {n: sum(evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(args.steps)) / args.steps
            for k, n in enumerate(names)}
@@ -184,9 +241,12 @@ def main():
     else:
         peak, dtype = PEAK_FP32_TFLOPS, "f32"
     achieved = work["gate"]["flops"] / gate_s / 1e12
-    roofline = {"kernel": "engram_gate_forward (scale_cols + gate_mfma<K> + gate_mfma<V>)",
+    traffic = measured_traffic(cfg) if cfg.dtype == "bf16" else None
+    roofline = {"kernel": "engram_gate_forward: gate_prep_kernel + gate_persistent_kernel "
+                          "(events bracket both; the prep kernel is ~1% of the call)",
                 "bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": None,
+                "frac": round(achieved / peak, 4), "traffic": traffic,
+                "traffic_algorithmic": work["gate"]["bytes"],
                 "flops_per_launch": work["gate"]["flops"], "avg_ms": round(per["gate"], 5)}
 
     result = {
@@ -199,6 +259,7 @@ def main():
         "dtype": dtype, "data": "synthetic (seeded Zipf ids, counter-generated tables/weights/hidden)",
         "config": workload_desc(cfg),
         "wall_s_timed": round(t_wall, 4),
+        "cache_flush_mb_between_steps": args.flush_mb,
         "kernels": kernels,
         "roofline": roofline,
     }

@@ -59,8 +59,9 @@ struct GateArgs {
   float* part_dot;   // scratch: [n_branch][n_ftiles][n_tok]
   float* part_hh;    // scratch: [n_branch][n_ftiles][n_tok]
   float* ee;         // scratch: [n_branch][n_ftiles][n_tok] partial sums of e^2
+  int32_t* counters; // scratch: per-queue tile heads, then per-(branch, token tile) done counts
   int64_t n_tok;
-  int32_t d_mem, d_model, n_branch, n_ftiles;
+  int32_t d_mem, d_model, n_branch, n_ftiles, n_ttiles;
   float eps, inv_sqrt_d;
 };
 // bf16 path: returns the scratch bytes it needs for these shapes (and sets a.n_ftiles).
