@@ -42,18 +42,21 @@
 // lane's accumulator groups 0-1 and 2-3 each cover 8 consecutive features:
 // every epilogue access is a 16-byte vector.
 //
-// Main loop.  BK = 64 per k-step, double-buffered LDS (2 x 64 KB).  The next
-// k-step's operands are loaded global -> registers (16-B native vectors, so the
-// staging array stays in registers) while the current k-step's 64 MFMAs run,
-// then written to the other LDS buffer; one LDS-only barrier per k-step (a
-// plain __syncthreads() would also wait for the in-flight global loads).  The
-// loop body is branch-free; the fragment registers are double-buffered so the
-// LDS reads of sub-step s+1 are in flight during sub-step s's MFMAs.  LDS rows are 128 B; the 16-B chunk index is XOR-swizzled with
-// (r & 7) ^ ((r >> 3) & 1), which keeps the fragment reads (32 consecutive
-// rows, one chunk) free of bank conflicts.
+// Main loop.  BK = 32 per k-step over a ring of four 32-KB LDS slots (weight rows
+// and memory rows of one k-step each).  Operands move global -> LDS with direct
+// loads (no registers), issued three k-steps ahead: three stages are in flight
+// while the fourth is read, enough to cover the latency of L2 misses that a
+// single register-staged stage could not.  The loads are issued from inline asm
+// and waited for with explicit vmcnt counts, because the compiler would otherwise
+// make every LDS read wait for all of them.  One LDS-only barrier per k-step both
+// publishes the next stage and frees the slot just read.  The fragment registers
+// are double-buffered so that a sub-step's MFMAs cover the next sub-step's LDS
+// reads.  Slot rows are 64 B; the 16-B chunk index is XOR-swizzled by slot_key so
+// the fragment reads (32 consecutive rows, one chunk) are free of bank conflicts.
 //
-// Epilogue.  The LDS buffers are reused for the h tile (256 tokens x 256
-// features, 128 KB), loaded with coalesced 16-byte loads; 16-byte chunks
+// Epilogue.  The slot ring is reused for the h tile (256 tokens x 256 features,
+// 128 KB): once no stage is left to load, each freed slot receives one quarter of
+// it, behind the last k-steps' MFMAs; 16-byte chunks
 // are swizzled by (token & 31) so that 32 lanes reading 32 tokens hit distinct
 // banks.  A V tile writes out into the same LDS tile and then streams it to
 // HBM with coalesced 16-byte stores.
@@ -68,18 +71,19 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16-B chunk (nati
 
 constexpr int BF = 256;   // features per tile
 constexpr int BT = 256;   // tokens per tile
-constexpr int BK = 64;    // contraction depth per k-step
+constexpr int BK = 32;    // contraction depth per k-step
 constexpr int NTHR = 256;
 constexpr int WF = 128, WT = 128;           // per-wavefront tile
 constexpr int MF = WF / 32, MT = WT / 32;   // MFMA tiles per wavefront
-constexpr int ROW_CH = BK / 8;              // 16-B chunks per LDS row (8)
-constexpr int STAGE_A = BF * BK;            // bf16 elements of the weight tile in a stage
-constexpr int STAGE = (BF + BT) * BK;       // bf16 elements per stage
-constexpr int CH_A = BF * ROW_CH / NTHR;    // 16-B chunks of the weight tile per thread per stage
-constexpr int CH_B = BT * ROW_CH / NTHR;    // 16-B chunks of the memory tile per thread per stage
+constexpr int NSLOT = 4;                    // LDS ring slots: 3 stages in flight + 1 being read
+constexpr int SLOT_A_BYTES = BF * BK * 2;   // weight rows of a slot (64 B each)
+constexpr int SLOT_BYTES = (BF + BT) * BK * 2;
+constexpr int G_INSTR = SLOT_BYTES / 1024 / (NTHR / 64);  // 16-B-per-lane loads per wave per slot (8)
 constexpr int H_CH = BF / 8;                // 16-B chunks per h row in the epilogue tile (32)
 constexpr int H_LOADS = BT * H_CH / NTHR;   // 32 chunks per thread
-constexpr int SMEM_ELEMS = (2 * STAGE > BT * BF) ? 2 * STAGE : BT * BF;
+constexpr int SMEM_ELEMS = (NSLOT * SLOT_BYTES / 2 > BT * BF) ? NSLOT * SLOT_BYTES / 2 : BT * BF;
+static_assert(NSLOT * SLOT_BYTES == BT * BF * 2, "the h tile fills the slot ring exactly");
+static_assert(NSLOT == 4 && G_INSTR == 8, "wait counts below assume 4 slots of 8 loads per wave");
 constexpr int NQ = 8;                       // work queues (one per XCD)
 constexpr int SPIN_LIMIT = 1 << 24;         // ~0.5 s of s_sleep before a V tile gives up waiting
 
@@ -94,13 +98,34 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// Physical 16-B chunk of logical chunk c in a 128-B stage row r.
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r & 7) ^ ((r >> 3) & 1)); }
-// LDS element offset of 16-B chunk q (row q / ROW_CH) of a stage operand tile
-__device__ __forceinline__ int st_off(int q) {
-  const int r = q / ROW_CH;
-  return r * BK + swz(r, q % ROW_CH) * 8;
+// A slot row is 64 B (4 chunks of 16 B); logical chunk c of row r sits at physical
+// chunk c ^ slot_key(r).  Eight consecutive rows at one logical chunk, and four
+// consecutive rows at two neighbouring logical chunks, then cover distinct 16-B
+// bank groups, so the fragment reads are conflict-free.
+__device__ __forceinline__ int slot_key(int r) { return ((r >> 2) & 1) | (r & 2); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// One 16-byte-per-lane direct global->LDS load: lane l's 16 bytes from `src` land at
+// LDS byte address lds + 16 l (lds must be wave-uniform).  Issued from inline asm so
+// that the compiler does not serialise later LDS reads behind it; completion is
+// tracked by hand with wait_vm_lgkm0.  The compiler writes M0 (the LDS address
+// operand); one wait state separates that write from the load that reads it.
+__device__ __forceinline__ void dma16(const uint16_t* src, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
 }
+
+// s_waitcnt vmcnt(N) lgkmcnt(0): at most N of this wave's vector-memory operations
+// still in flight, and all its LDS operations done.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
 // feature offset (inside a 32-row MFMA tile) held by MFMA row rho: bits 2 and 3 swapped
 __device__ __forceinline__ int tile_row_feature(int rho) {
   return (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1);
@@ -139,30 +164,6 @@ __device__ __forceinline__ float ld_coherent(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Half `half` (tokens 128 half .. 128 half + 127) of the epilogue's h tile
-// [BT tokens][BF features] straight into LDS with direct global->LDS loads: LDS
-// 16-B chunk P = tl * 32 + phys holds logical chunk phys ^ (tl & 31) of token tl
-// (the swizzle keeps the epilogue's 32-tokens-per-read accesses conflict-free).
-// Every wave instruction fills 64 consecutive chunks (two token rows).
-__device__ __forceinline__ void load_h_half(uint16_t* smem, const uint16_t* Ht0, int64_t t0,
-                                            int64_t n_tok, int f0, int d_model, int half,
-                                            int wave, int lane) {
-  typedef __attribute__((address_space(3))) void lds_void;
-  const int tr_lim = (int)(n_tok - 1 - t0);
-#pragma unroll
-  for (int i = 0; i < H_LOADS / 2; ++i) {
-    const int base = half * (BT / 2) * H_CH + (wave * (H_LOADS / 2) + i) * 64;  // wave-uniform
-    const int p = base + lane;
-    const int tl = p / H_CH;
-    const int c = (p % H_CH) ^ (tl & 31);
-    const int tr = tl < tr_lim ? tl : tr_lim;   // tokens past n_tok: a valid row, unused
-    int f = f0 + c * 8;
-    f = f < d_model ? f : 0;
-    __builtin_amdgcn_global_load_lds(Ht0 + (uint32_t)tr * (uint32_t)d_model + f,
-                                     (lds_void*)(smem + base * 8), 16, 0, 0);
-  }
-}
-
 struct Tile {
   int phase, m, ttile, ftile;
 };
@@ -190,7 +191,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, u
   const int PHASE = tile.phase;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wf = wave >> 1, wt = wave & 1;
   const int m = tile.m, ftile = tile.ftile;
   const int f0 = ftile * BF;
@@ -232,69 +233,89 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, u
     s_alpha[tid] = alpha;
   }
 
-  // ---- global -> register -> LDS staging.  Thread tid moves 16-B chunks
-  // q = tid + NTHR * i of each operand tile: row q / ROW_CH, logical chunk q % ROW_CH.
-  // Offsets are 32-bit from wave-uniform bases.
-  const uint16_t* Et0 = E + t0 * d_mem;  // memory rows of this token tile
-  // Chunk i of this thread sits in row (tid / ROW_CH) + 32 i, logical chunk tid % ROW_CH.
-  // The weight row permutation only touches the low 5 bits of the row, so row i of the
-  // weight tile is feature f0 + 32 i + tile_row_feature(tid / ROW_CH); rows past d_model
-  // (and tokens past n_tok) are clamped to a valid row whose result is unused.
-  const int srow = tid / ROW_CH;                     // 0..31
-  const int scol = (tid % ROW_CH) * 8;
-  const int a_f = f0 + tile_row_feature(srow);
-  const int b_lim = (int)(n_tok - 1 - t0);           // last valid row of the token tile
-#define ENGRAM_A_OFF(i) ((uint32_t)min(a_f + 32 * (i), d_model - 1) * (uint32_t)d_mem + scol)
-#define ENGRAM_B_OFF(i) ((uint32_t)min(srow + 32 * (i), b_lim) * (uint32_t)d_mem + scol)
+  // ---- operand staging: a ring of NSLOT LDS slots, filled by direct global->LDS
+  // loads issued DIST k-steps ahead.  Every wave issues exactly G_INSTR load
+  // instructions per ring step ("group"): groups 0..NSLOT-1 in the prologue, group
+  // kt + NSLOT right after the barrier that ends k-step kt, into the slot k-step kt
+  // has just finished reading.  Group g is stage g while g < nk, else the h-tile
+  // quarter that lands in slot g % NSLOT (the epilogue's h tile fills the whole ring).
+  // So before the barrier that ends k-step kt, stage kt+1 has landed once at most
+  // 2 G_INSTR of this wave's loads are still in flight (groups kt+2, kt+3).
+  //
+  // Waves 0-1 load weight rows 0-127 / 128-255, waves 2-3 memory rows; instruction i
+  // of a wave fills rows (8 (wave & 1) + i) * 16 .. + 15 of its operand: lane l reads
+  // row + l / 4, physical chunk l % 4 (logical chunk (l % 4) ^ key(row)).
+  const int nk = d_mem / BK;
+  const uint16_t* Et0 = E + t0 * d_mem;   // memory rows of this token tile
+  const uint16_t* Ht0 = H + t0 * d_model;
+  const int b_lim = (int)(n_tok - 1 - t0);  // last valid row of the token tile
+  const bool wave_loads_a = (wave >> 1) == 0;
+  const uint16_t* src_base = wave_loads_a ? W : Et0;
+  // Row of instruction i: 16 i + (first row of instruction 0); both operands' rows
+  // advance by 16 per instruction (the weight row permutation only touches bits 2-3),
+  // and rows past the last valid one are clamped to it (their results are unused):
+  // offset_i = min(src_off0 + i * src_step, src_lim).
+  uint32_t src_off0, src_step, src_lim;
+  {
+    const int lrow = lane >> 2;
+    const int lchunk = (lane & 3) ^ slot_key(lrow);  // slot_key only sees bits 1-2 of the row
+    const int r0 = (wave & 1) * G_INSTR * 16 + lrow;
+    const int row0 = wave_loads_a ? f0 + tile_row_feature(r0) : r0;
+    const int last = wave_loads_a ? d_model - 1 : b_lim;
+    src_off0 = (uint32_t)row0 * (uint32_t)d_mem + (uint32_t)(lchunk * 8);
+    src_step = 16u * (uint32_t)d_mem;
+    src_lim = (uint32_t)last * (uint32_t)d_mem + (uint32_t)(lchunk * 8);
+  }
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr)smem;
+  const uint32_t wave_dst = lds0 + (uint32_t)((wave >> 1) * SLOT_A_BYTES + (wave & 1) * G_INSTR * 1024);
 
-  // The next stage's global loads, in flight in registers across a k-step's MFMAs.
-  // Native 16-byte vectors with static indices keep them out of scratch.
-  u32x4 ra[CH_A], rb[CH_B];
-#define ENGRAM_LOAD_STAGE(kt)                                                              \
+  // stage g (< nk) into slot g % NSLOT
+#define ENGRAM_ISSUE_STAGE(g)                                                              \
   do {                                                                                     \
-    const int k0_ = (kt) * BK;                                                             \
-    _Pragma("unroll") for (int i = 0; i < CH_A; ++i)                                       \
-        ra[i] = *reinterpret_cast<const u32x4*>(W + ENGRAM_A_OFF(i) + k0_);                \
-    _Pragma("unroll") for (int i = 0; i < CH_B; ++i)                                       \
-        rb[i] = *reinterpret_cast<const u32x4*>(Et0 + ENGRAM_B_OFF(i) + k0_);              \
+    const uint16_t* src_ = src_base + (g) * BK;                                            \
+    const uint32_t dst_ = wave_dst + (uint32_t)(((g) % NSLOT) * SLOT_BYTES);               \
+    _Pragma("unroll") for (int i = 0; i < G_INSTR; ++i)                                    \
+        dma16(src_ + min(src_off0 + (uint32_t)i * src_step, src_lim), dst_ + i * 1024);    \
   } while (0)
-#define ENGRAM_STORE_STAGE(buf)                                                            \
-  do {                                                                                     \
-    uint16_t* st_ = smem + (buf) * STAGE;                                                  \
-    _Pragma("unroll") for (int i = 0; i < CH_A; ++i)                                       \
-        *reinterpret_cast<u32x4*>(st_ + st_off(tid + NTHR * i)) = ra[i];                   \
-    _Pragma("unroll") for (int i = 0; i < CH_B; ++i)                                       \
-        *reinterpret_cast<u32x4*>(st_ + STAGE_A + st_off(tid + NTHR * i)) = rb[i];         \
-  } while (0)
-  // sums of e^2 of the rows this thread stages (rows tid / ROW_CH + 32 i), over the
-  // k-steps of this tile's slice
-  float ee_rows[CH_B];
+  // h-tile quarter q (tokens 64 q .. 64 q + 63) into slot q, two token rows per
+  // instruction; LDS chunk tl * 32 + phys holds logical chunk phys ^ (tl & 31) of
+  // token tl.  Addresses come from an opaque copy of the lane id so that they are
+  // not computed ahead and kept live through the main loop.
+  auto issue_hq = [&](int q) {
+    int hl = lane;
+    asm volatile("" : "+v"(hl));
+    const uint32_t slot_lds = lds0 + (uint32_t)(q * SLOT_BYTES);
 #pragma unroll
-  for (int i = 0; i < CH_B; ++i) ee_rows[i] = 0.f;
-#define ENGRAM_EE(kt_stage)                                                                \
-  do {                                                                                     \
-    if (PHASE == PHASE_K) {                                                                \
-      const float mk_ = (((kt_stage) % a.n_ftiles) == ftile) ? 1.f : 0.f;                  \
-      _Pragma("unroll") for (int i = 0; i < CH_B; ++i) ee_rows[i] += mk_ * sumsq8(rb[i]);  \
-    }                                                                                      \
-  } while (0)
+    for (int i = 0; i < G_INSTR; ++i) {
+      const int blk = wave * G_INSTR + i;
+      const int tl = q * 64 + blk * 2 + (hl >> 5);
+      const int c = (hl & 31) ^ (tl & 31);
+      const int tr = tl < b_lim ? tl : b_lim;
+      int f = f0 + c * 8;
+      f = f < d_model ? f : 0;
+      dma16(Ht0 + (uint32_t)tr * (uint32_t)d_model + f, slot_lds + (uint32_t)(blk * 1024));
+    }
+  };
 
-  // MFMA operand fragments, double-buffered across the 4 sub-steps of a k-step
+  // MFMA operand fragments, double-buffered across the sub-steps.  Fragment row r of
+  // a slot operand is 64 B; sub-step s of lane l reads logical chunk 2 s + l / 32.
+  const int khalf = lane >> 5;
   const int arow0 = wf * WF + (lane & 31);
   const int brow0 = wt * WT + (lane & 31);
-  const int khalf = lane >> 5;
+  uint32_t fr_a[2], fr_b[2];  // byte offsets inside a slot, per sub-step
+#pragma unroll
+  for (int ss = 0; ss < 2; ++ss) {
+    fr_a[ss] = (uint32_t)(arow0 * (BK * 2) + (((ss * 2 + khalf) ^ slot_key(arow0)) * 16));
+    fr_b[ss] = (uint32_t)(SLOT_A_BYTES + brow0 * (BK * 2) + (((ss * 2 + khalf) ^ slot_key(brow0)) * 16));
+  }
   bf16x8 fa[2][MF], fb[2][MT];
-#define ENGRAM_LOAD_FRAGS(buf, la_, lb_, s_)                                               \
+#define ENGRAM_LOAD_FRAGS(buf, slot_base_, ss_)                                            \
   do {                                                                                     \
-    const int c_ = (s_) * 2 + khalf;                                                       \
-    _Pragma("unroll") for (int i = 0; i < MF; ++i) {                                       \
-      const int r_ = arow0 + i * 32;                                                       \
-      fa[buf][i] = *reinterpret_cast<const bf16x8*>((la_) + r_ * BK + swz(r_, c_) * 8);    \
-    }                                                                                      \
-    _Pragma("unroll") for (int j = 0; j < MT; ++j) {                                       \
-      const int r_ = brow0 + j * 32;                                                       \
-      fb[buf][j] = *reinterpret_cast<const bf16x8*>((lb_) + r_ * BK + swz(r_, c_) * 8);    \
-    }                                                                                      \
+    const char* sb_ = (const char*)smem + (slot_base_);                                    \
+    _Pragma("unroll") for (int i = 0; i < MF; ++i)                                         \
+        fa[buf][i] = *reinterpret_cast<const bf16x8*>(sb_ + fr_a[ss_] + i * 32 * BK * 2);  \
+    _Pragma("unroll") for (int j = 0; j < MT; ++j)                                         \
+        fb[buf][j] = *reinterpret_cast<const bf16x8*>(sb_ + fr_b[ss_] + j * 32 * BK * 2);  \
   } while (0)
 #define ENGRAM_MFMAS(buf)                                                                  \
   do {                                                                                     \
@@ -302,6 +323,18 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, u
         _Pragma("unroll") for (int j = 0; j < MT; ++j)                                     \
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j],    \
                                                                  acc[i][j], 0, 0, 0);      \
+  } while (0)
+  // Sum of e^2 over the k-steps kt with kt % n_ftiles == ftile, from the memory
+  // fragments: waves with wf == 0 see every token row of the tile (lanes l and l+32
+  // hold the two halves of a sub-step's 16 columns).
+  float ee_acc[MT];
+#pragma unroll
+  for (int j = 0; j < MT; ++j) ee_acc[j] = 0.f;
+  const bool ee_wave = PHASE == PHASE_K && wf == 0;
+#define ENGRAM_EE(buf)                                                                     \
+  do {                                                                                     \
+    _Pragma("unroll") for (int j = 0; j < MT; ++j)                                         \
+        ee_acc[j] += sumsq8(__builtin_bit_cast(u32x4, fb[buf][j]));                        \
   } while (0)
 
   floatx16 acc[MF][MT];
@@ -312,66 +345,60 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, u
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nk = d_mem / BK;
-  ENGRAM_LOAD_STAGE(0);
-  ENGRAM_EE(0);
-  ENGRAM_STORE_STAGE(0);
+  for (int g = 0; g < NSLOT; ++g) {
+    if (g < nk) ENGRAM_ISSUE_STAGE(g);
+    else issue_hq(g);
+  }
+  wait_vm_lgkm0<3 * G_INSTR>();
   lds_barrier();
-  ENGRAM_LOAD_FRAGS(0, smem, smem + STAGE_A, 0);
+  // k-step 0: both sub-steps' fragments, sub-step 0's MFMAs
+  ENGRAM_LOAD_FRAGS(0, 0, 0);
+  ENGRAM_LOAD_FRAGS(1, 0, 1);
+  ENGRAM_MFMAS(0);
+  bool ee_prev = ee_wave && (0 % a.n_ftiles) == ftile;
+  if (ee_prev) ENGRAM_EE(0);
+  wait_vm_lgkm0<2 * G_INSTR>();
+  lds_barrier();
+  if (NSLOT < nk) ENGRAM_ISSUE_STAGE(NSLOT);
+  else issue_hq(0);
 
-  // k-steps with a successor: MFMAs on LDS buffer kt & 1 while stage kt+1 loads into
-  // registers; then stage kt+1 goes to the other buffer, last read in k-step kt-1
-  // (finished before the previous barrier).  Scheduling barriers pin the order that
-  // hides latency: global loads first, each sub-step's fragment reads a full sub-step
-  // (16 MFMAs) ahead of their use, LDS writes last.
-  for (int kt = 0; kt + 1 < nk; ++kt) {
-    const uint16_t* la = smem + (kt & 1) * STAGE;
-    const uint16_t* lb = la + STAGE_A;
-    ENGRAM_LOAD_STAGE(kt + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    ENGRAM_LOAD_FRAGS(1, la, lb, 1);
-    ENGRAM_MFMAS(0);
-    __builtin_amdgcn_sched_barrier(0);
-    ENGRAM_LOAD_FRAGS(0, la, lb, 2);
-    ENGRAM_MFMAS(1);
-    __builtin_amdgcn_sched_barrier(0);
-    ENGRAM_LOAD_FRAGS(1, la, lb, 3);
-    ENGRAM_MFMAS(0);
-    __builtin_amdgcn_sched_barrier(0);
-    ENGRAM_MFMAS(1);
-    __builtin_amdgcn_sched_barrier(0);
-    ENGRAM_EE(kt + 1);
-    ENGRAM_STORE_STAGE((kt + 1) & 1);
-    lds_barrier();
-    const uint16_t* na = smem + ((kt + 1) & 1) * STAGE;
-    ENGRAM_LOAD_FRAGS(0, na, na + STAGE_A, 0);
+  // k-step kt: sub-step 1 of k-step kt-1 (fragments already in registers) covers the
+  // latency of this step's first fragment reads; then sub-step 0 of kt.  The barrier
+  // at the end publishes stage kt+1 and frees slot kt % NSLOT for group kt + NSLOT:
+  // a stage while one is left, else the h-tile quarter of that slot.
+#define ENGRAM_KSTEP(kt)                                                                   \
+  do {                                                                                     \
+    const uint32_t slot_ = (uint32_t)(((kt) % NSLOT) * SLOT_BYTES);                        \
+    ENGRAM_LOAD_FRAGS(0, slot_, 0);                                                        \
+    __builtin_amdgcn_sched_barrier(0);                                                     \
+    ENGRAM_MFMAS(1);                                                                       \
+    __builtin_amdgcn_sched_barrier(0);                                                     \
+    if (ee_prev) ENGRAM_EE(1);                                                             \
+    ENGRAM_LOAD_FRAGS(1, slot_, 1);                                                        \
+    __builtin_amdgcn_sched_barrier(0);                                                     \
+    ENGRAM_MFMAS(0);                                                                       \
+    __builtin_amdgcn_sched_barrier(0);                                                     \
+    ee_prev = ee_wave && ((kt) % a.n_ftiles) == ftile;                                     \
+    if (ee_prev) ENGRAM_EE(0);                                                             \
+    wait_vm_lgkm0<2 * G_INSTR>();                                                          \
+    lds_barrier();                                                                         \
+  } while (0)
+  int kt = 1;
+  for (; kt + NSLOT < nk; ++kt) {
+    ENGRAM_KSTEP(kt);
+    ENGRAM_ISSUE_STAGE(kt + NSLOT);
   }
-  // Last k-step.  The other stage buffer is free (last read in k-step nk-2): once this
-  // step's fragment reads are issued, the half of the epilogue's h tile that lives
-  // there starts loading straight into LDS, behind the remaining 32 MFMAs.
-  const uint16_t* Ht0 = H + t0 * d_model;
-  {
-    const uint16_t* la = smem + ((nk - 1) & 1) * STAGE;
-    const uint16_t* lb = la + STAGE_A;
-    ENGRAM_LOAD_FRAGS(1, la, lb, 1);
-    ENGRAM_MFMAS(0);
-    __builtin_amdgcn_sched_barrier(0);
-    ENGRAM_LOAD_FRAGS(0, la, lb, 2);
-    ENGRAM_MFMAS(1);
-    __builtin_amdgcn_sched_barrier(0);
-    ENGRAM_LOAD_FRAGS(1, la, lb, 3);
-    load_h_half(smem, Ht0, t0, n_tok, f0, d_model, nk & 1, wave, lane);
-    ENGRAM_MFMAS(0);
-    __builtin_amdgcn_sched_barrier(0);
-    ENGRAM_MFMAS(1);
+  for (; kt < nk; ++kt) {
+    ENGRAM_KSTEP(kt);
+    issue_hq(kt % NSLOT);
   }
-#undef ENGRAM_LOAD_STAGE
-#undef ENGRAM_STORE_STAGE
+#undef ENGRAM_KSTEP
+#undef ENGRAM_ISSUE_STAGE
+  ENGRAM_MFMAS(1);
+  if (ee_prev) ENGRAM_EE(1);
 #undef ENGRAM_EE
 #undef ENGRAM_LOAD_FRAGS
 #undef ENGRAM_MFMAS
-#undef ENGRAM_A_OFF
-#undef ENGRAM_B_OFF
 
   // Everything below re-derives its indices from an opaque copy of the thread id, so
   // the compiler cannot compute epilogue addresses before the loop and keep them
@@ -381,25 +408,21 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, u
   const int elane = etid & 63, ewave = etid >> 6;
   const int ewf = ewave >> 1, ewt = ewave & 1;
 
-  if (PHASE == PHASE_K) {
-    // rows tid / ROW_CH + 32 i: the ROW_CH lanes of a row hold its partial sums
+  if (ee_wave) {
+    // lanes l and l + 32 of a wf == 0 wave hold the two halves of token row
+    // ewt * WT + j * 32 + l % 32
     float* ee_out = a.ee + ((int64_t)m * a.n_ftiles + ftile) * n_tok + t0;
 #pragma unroll
-    for (int i = 0; i < CH_B; ++i) {
-      float v = ee_rows[i];
-      v += __shfl_xor(v, 1, 64);
-      v += __shfl_xor(v, 2, 64);
-      v += __shfl_xor(v, 4, 64);
-      const int r = etid / ROW_CH + 32 * i;
-      if ((etid % ROW_CH) == 0 && t0 + r < n_tok) st_coherent(ee_out + r, v);
+    for (int j = 0; j < MT; ++j) {
+      const float v = ee_acc[j] + __shfl_xor(ee_acc[j], 32, 64);
+      const int r = ewt * WT + j * 32 + (elane & 31);
+      if (elane < 32 && t0 + r < n_tok) st_coherent(ee_out + r, v);
     }
   }
 
-  // ---- the other half of the h tile, into the buffer the last k-step read
-  __syncthreads();
-  load_h_half(smem, Ht0, t0, n_tok, f0, d_model, (nk - 1) & 1, ewave, elane);
-  __builtin_amdgcn_s_waitcnt(0);  // this wave's direct-to-LDS loads have landed
-  __syncthreads();
+  // ---- the h tile: its four quarters were loaded into the ring as it drained
+  wait_vm_lgkm0<0>();
+  lds_barrier();
 
   // Lane (token column tl) holds, for MFMA tile (i, j) and pair gp, features
   // fl = wf*WF + i*32 + gp*16 + (lane>>5)*8 + 0..7 in acc[i][j][8*gp + 0..7].
