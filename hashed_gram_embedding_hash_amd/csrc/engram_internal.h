@@ -59,6 +59,7 @@ struct GateArgs {
   float* part_dot;   // scratch: [n_branch][n_ftiles][n_tok]
   float* part_hh;    // scratch: [n_branch][n_ftiles][n_tok]
   float* ee;         // scratch: [n_branch][n_ftiles][n_tok] partial sums of e^2
+  float* alpha;      // scratch: [n_branch][n_tok] gates, published by the last K tile of a token tile
   int32_t* counters; // scratch: per-queue tile heads, then per-(branch, token tile) done counts
   int64_t n_tok;
   int32_t d_mem, d_model, n_branch, n_ftiles, n_ttiles;

@@ -11,23 +11,26 @@
 // and run as bf16 MFMA GEMMs (v_mfma_f32_32x32x16_bf16).  alpha needs the whole
 // d_model-long dot product q . k before any element of the value can be scaled,
 // so every output tile is computed twice over the same tiling:
-//   K tile: acc = W_K' e^T for (feature tile, token tile), W_K' = W_K diag(gk)
-//           (prepared once per call by gate_prep_kernel); the epilogue reduces
-//           sum_f h[t,f] gq[f] acc[f,t] and sum_f h[t,f]^2 over the tile's
-//           features into per-(feature tile, token) partials; the main loop
-//           also sums e^2 over one slice of the memory row (k-steps with
-//           kt % n_ftiles == ftile), so every tile does 1/n_ftiles of it;
-//   V tile: waits until all K tiles of its (branch, token tile) are done,
-//           turns the partials into alpha (fixed-order sums: bit-reproducible),
-//           computes acc = W_V e^T and writes out = h + alpha acc.
-// Since q . k = (sum_f h_f gq_f k~_f) / (rms(h) rms(e)) with k~ = W_K' e, the
-// RMSNorm scales are applied to the reduced scalar, never to a tensor.
+//   K tile: acc = W_K' e^T for (feature tile, token tile), with
+//           W_K'[f][c] = gq[f] W_K[f][c] gk[c] (both RMSNorm gains folded in,
+//           prepared once per call by gate_prep_kernel); the epilogue reduces
+//           sum_f h[t,f] acc[f,t] and sum_f h[t,f]^2 over the tile's features into
+//           per-(feature tile, token) partials; the main loop also sums e^2 over
+//           one slice of the memory row (k-steps with kt % n_ftiles == ftile), so
+//           every tile does 1/n_ftiles of it.  The last K tile of a (branch, token
+//           tile) to finish turns the partials into alpha (fixed-order sums:
+//           bit-reproducible) and publishes it;
+//   V tile: waits until alpha of its (branch, token tile) is published, computes
+//           acc = W_V e^T and writes out = h + alpha acc.
+// Since q . k = (sum_f h_f gq_f k~_f) / (rms(h) rms(e)) with k~ = W_K diag(gk) e,
+// the RMSNorm scales are applied to the reduced scalar, never to a tensor.
 //
 // Scheduling.  One persistent launch of one workgroup per CU.  Workgroup b
 // serves work queue b % 8 (the XCD it is dispatched to), which holds the token
 // tiles T with T % 8 == b % 8: first all their K tiles, then all their V tiles,
 // feature tile fastest.  A workgroup claims the next tile of its queue with an
-// atomic increment; a V tile spins until the done-counter of its K tiles is
+// atomic increment (the next one already when the current tile's epilogue
+// starts, so the claim's latency is hidden); a V tile spins until the done-counter of its K tiles is
 // full.  Those K tiles sit earlier in the same queue, so they were claimed
 // before by running workgroups that never wait: the spin always ends.  The
 // single queue per XCD removes the partial last round of a two-launch design
@@ -71,21 +74,20 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16-B chunk (nati
 
 constexpr int BF = 256;   // features per tile
 constexpr int BT = 256;   // tokens per tile
-constexpr int BK = 32;    // contraction depth per k-step
+constexpr int BK = 64;    // contraction depth per k-step
 constexpr int NTHR = 256;
 constexpr int WF = 128, WT = 128;           // per-wavefront tile
 constexpr int MF = WF / 32, MT = WT / 32;   // MFMA tiles per wavefront
-constexpr int NSLOT = 4;                    // LDS ring slots: 3 stages in flight + 1 being read
-constexpr int SLOT_A_BYTES = BF * BK * 2;   // weight rows of a slot (64 B each)
-constexpr int SLOT_BYTES = (BF + BT) * BK * 2;
+constexpr int NSLOT = 5;                    // LDS ring slots
+constexpr int SLOT_BYTES = 256 * BK * 2;    // one operand of one k-step: 256 rows x 128 B
 constexpr int G_INSTR = SLOT_BYTES / 1024 / (NTHR / 64);  // 16-B-per-lane loads per wave per slot (8)
 constexpr int H_CH = BF / 8;                // 16-B chunks per h row in the epilogue tile (32)
 constexpr int H_LOADS = BT * H_CH / NTHR;   // 32 chunks per thread
-constexpr int SMEM_ELEMS = (NSLOT * SLOT_BYTES / 2 > BT * BF) ? NSLOT * SLOT_BYTES / 2 : BT * BF;
-static_assert(NSLOT * SLOT_BYTES == BT * BF * 2, "the h tile fills the slot ring exactly");
-static_assert(NSLOT == 4 && G_INSTR == 8, "wait counts below assume 4 slots of 8 loads per wave");
+constexpr int SMEM_BYTES = NSLOT * SLOT_BYTES;  // 160 KB: the whole LDS of a CU
+static_assert(4 * SLOT_BYTES == BT * BF * 2, "the h tile is four slots");
+static_assert(G_INSTR == 8 && BF == 256 && BT == 256, "load and wait counts below assume these");
 constexpr int NQ = 8;                       // work queues (one per XCD)
-constexpr int SPIN_LIMIT = 1 << 24;         // ~0.5 s of s_sleep before a V tile gives up waiting
+constexpr int SPIN_LIMIT = 1 << 18;         // polls (each one L2 round trip plus s_sleep 1: 0.1-0.5 s) before a V tile gives up
 
 enum { PHASE_K = 0, PHASE_V = 1 };
 
@@ -98,11 +100,10 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// A slot row is 64 B (4 chunks of 16 B); logical chunk c of row r sits at physical
-// chunk c ^ slot_key(r).  Eight consecutive rows at one logical chunk, and four
-// consecutive rows at two neighbouring logical chunks, then cover distinct 16-B
-// bank groups, so the fragment reads are conflict-free.
-__device__ __forceinline__ int slot_key(int r) { return ((r >> 2) & 1) | (r & 2); }
+// A slot row is 128 B (8 chunks of 16 B); logical chunk c of row r sits at
+// physical chunk c ^ row_key(r).  The fragment reads (32 consecutive rows at one
+// logical chunk) then touch every bank group once per 8 rows: conflict-free.
+__device__ __forceinline__ int row_key(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
@@ -186,8 +187,8 @@ __device__ __forceinline__ bool decode_tile(const GateArgs& a, int x, int q, Til
 
 // One K or V tile.  A single main loop serves both phases (one copy of the
 // loop keeps register allocation simple); only the epilogues differ.
-__device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, uint16_t* smem,
-                                          float (*s_red)[2][BT], float* s_alpha) {
+__device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, char* smem, int x,
+                                          int& next_claim) {
   const int PHASE = tile.phase;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -205,86 +206,65 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, u
   const uint16_t* E = (const uint16_t*)a.mem;
   const uint16_t* H = (const uint16_t*)a.h[m];
 
+  float alpha = 0.f;  // V tiles: the gate of token t0 + tid (to LDS once the ring drains)
   if (PHASE == PHASE_V) {
-    // ---- wait for the K tiles of this (branch, token tile), then alpha per token
+    // ---- wait until the last K tile of this (branch, token tile) has published its
+    // gates (done count n_ftiles + 1), then fetch this thread's token's gate; the load
+    // completes behind the main loop
     if (tid == 0) {
       int spin = 0;
-      while (__hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.n_ftiles &&
+      while (__hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.n_ftiles + 1 &&
              ++spin < SPIN_LIMIT)
         __builtin_amdgcn_s_sleep(1);
     }
-    __syncthreads();  // the partial loads below are issued only after the count is seen
-    const int64_t t = t0 + tid;
-    float alpha = 0.f;
-    if (t < n_tok) {
-      float dot = 0.f, hh = 0.f, ee = 0.f;
-      const int64_t base = (int64_t)m * a.n_ftiles * n_tok + t;
-      for (int j = 0; j < a.n_ftiles; ++j) {
-        dot += ld_coherent(a.part_dot + base + (int64_t)j * n_tok);
-        hh += ld_coherent(a.part_hh + base + (int64_t)j * n_tok);
-        ee += ld_coherent(a.ee + base + (int64_t)j * n_tok);
-      }
-      const float rms_h = sqrtf(hh / (float)d_model + a.eps);
-      const float rms_e = sqrtf(ee / (float)d_mem + a.eps);
-      const float logit = dot / (rms_h * rms_e) * a.inv_sqrt_d;
-      alpha = 1.f / (1.f + expf(-logit));
-      if (ftile == 0 && a.gate_out != nullptr) a.gate_out[(int64_t)m * n_tok + t] = alpha;
-    }
-    s_alpha[tid] = alpha;
+    lds_barrier();  // the gate loads below are issued only after the count is seen
+    if (t0 + tid < n_tok) alpha = ld_coherent(a.alpha + (int64_t)m * n_tok + t0 + tid);
   }
 
-  // ---- operand staging: a ring of NSLOT LDS slots, filled by direct global->LDS
-  // loads issued DIST k-steps ahead.  Every wave issues exactly G_INSTR load
-  // instructions per ring step ("group"): groups 0..NSLOT-1 in the prologue, group
-  // kt + NSLOT right after the barrier that ends k-step kt, into the slot k-step kt
-  // has just finished reading.  Group g is stage g while g < nk, else the h-tile
-  // quarter that lands in slot g % NSLOT (the epilogue's h tile fills the whole ring).
-  // So before the barrier that ends k-step kt, stage kt+1 has landed once at most
-  // 2 G_INSTR of this wave's loads are still in flight (groups kt+2, kt+3).
+  // ---- operand stream.  Chunk c of the tile's stream lands in LDS slot c % NSLOT:
+  // chunks 2 kt and 2 kt + 1 are the weight rows and the memory rows of k-step kt
+  // (256 rows x 128 B each), chunks 2 nk .. 2 nk + 3 the four quarters of the
+  // epilogue's h tile.  Chunks 0-4 are issued up front.  The barrier that ends
+  // k-step kt - 1 frees its two slots, and during k-step kt chunks 2 kt + 3 and
+  // 2 kt + 4 are issued into them, spread through the MFMA stream (one load after
+  // every four MFMAs) so that a full load queue delays a few MFMAs instead of
+  // stalling all of them at once.  Every chunk is G_INSTR direct global->LDS loads
+  // per wave, so at the end of k-step kt, when chunks 2 kt + 2 and 2 kt + 3 must
+  // have landed, at most the G_INSTR loads of chunk 2 kt + 4 may be in flight.
   //
-  // Waves 0-1 load weight rows 0-127 / 128-255, waves 2-3 memory rows; instruction i
-  // of a wave fills rows (8 (wave & 1) + i) * 16 .. + 15 of its operand: lane l reads
-  // row + l / 4, physical chunk l % 4 (logical chunk (l % 4) ^ key(row)).
+  // Instruction i of wave w fills rows 64 w + 8 i .. + 7 of a chunk: lane l reads
+  // row 64 w + 8 i + l / 8 at physical chunk l % 8 (logical (l % 8) ^ row_key).
   const int nk = d_mem / BK;
   const uint16_t* Et0 = E + t0 * d_mem;   // memory rows of this token tile
   const uint16_t* Ht0 = H + t0 * d_model;
   const int b_lim = (int)(n_tok - 1 - t0);  // last valid row of the token tile
-  const bool wave_loads_a = (wave >> 1) == 0;
-  const uint16_t* src_base = wave_loads_a ? W : Et0;
-  // Row of instruction i: 16 i + (first row of instruction 0); both operands' rows
-  // advance by 16 per instruction (the weight row permutation only touches bits 2-3),
-  // and rows past the last valid one are clamped to it (their results are unused):
-  // offset_i = min(src_off0 + i * src_step, src_lim).
-  uint32_t src_off0, src_step, src_lim;
-  {
-    const int lrow = lane >> 2;
-    const int lchunk = (lane & 3) ^ slot_key(lrow);  // slot_key only sees bits 1-2 of the row
-    const int r0 = (wave & 1) * G_INSTR * 16 + lrow;
-    const int row0 = wave_loads_a ? f0 + tile_row_feature(r0) : r0;
-    const int last = wave_loads_a ? d_model - 1 : b_lim;
-    src_off0 = (uint32_t)row0 * (uint32_t)d_mem + (uint32_t)(lchunk * 8);
-    src_step = 16u * (uint32_t)d_mem;
-    src_lim = (uint32_t)last * (uint32_t)d_mem + (uint32_t)(lchunk * 8);
+  uint32_t off_a[G_INSTR], off_b[G_INSTR];
+#pragma unroll
+  for (int i = 0; i < G_INSTR; ++i) {
+    const int r = wave * 64 + i * 8 + (lane >> 3);
+    const int cl = (lane & 7) ^ row_key(r);
+    // weight rows are permuted (tile_row_feature); rows past the end are clamped to
+    // the last valid one (their results are unused)
+    off_a[i] = (uint32_t)min(f0 + tile_row_feature(r), d_model - 1) * (uint32_t)d_mem + cl * 8;
+    off_b[i] = (uint32_t)min(r, b_lim) * (uint32_t)d_mem + cl * 8;
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr)smem;
-  const uint32_t wave_dst = lds0 + (uint32_t)((wave >> 1) * SLOT_A_BYTES + (wave & 1) * G_INSTR * 1024);
-
-  // stage g (< nk) into slot g % NSLOT
-#define ENGRAM_ISSUE_STAGE(g)                                                              \
+  const uint32_t wave_dst = lds0 + (uint32_t)(wave * G_INSTR * 1024);
+#define ENGRAM_ISSUE(base_, off_, kt_, slot_)                                              \
   do {                                                                                     \
-    const uint16_t* src_ = src_base + (g) * BK;                                            \
-    const uint32_t dst_ = wave_dst + (uint32_t)(((g) % NSLOT) * SLOT_BYTES);               \
+    const uint16_t* src_ = (base_) + (kt_) * BK;                                           \
+    const uint32_t dst_ = wave_dst + (uint32_t)((slot_) * SLOT_BYTES);                     \
     _Pragma("unroll") for (int i = 0; i < G_INSTR; ++i)                                    \
-        dma16(src_ + min(src_off0 + (uint32_t)i * src_step, src_lim), dst_ + i * 1024);    \
+        dma16(src_ + off_[i], dst_ + i * 1024);                                            \
   } while (0)
-  // h-tile quarter q (tokens 64 q .. 64 q + 63) into slot q, two token rows per
-  // instruction; LDS chunk tl * 32 + phys holds logical chunk phys ^ (tl & 31) of
-  // token tl.  Addresses come from an opaque copy of the lane id so that they are
-  // not computed ahead and kept live through the main loop.
-  auto issue_hq = [&](int q) {
+  // h-tile quarter q (tokens 64 q .. 64 q + 63) into slot `slot`, two token rows per
+  // instruction; byte (tl % 64) * 512 + 16 phys of the quarter holds logical chunk
+  // phys ^ (tl & 31) of token tl.  Addresses come from an opaque copy of the lane id
+  // so that they are not computed ahead and kept live through the main loop.
+  auto issue_hq = [&](int q, int slot) {
     int hl = lane;
     asm volatile("" : "+v"(hl));
-    const uint32_t slot_lds = lds0 + (uint32_t)(q * SLOT_BYTES);
+    const uint32_t dst = lds0 + (uint32_t)(slot * SLOT_BYTES);
 #pragma unroll
     for (int i = 0; i < G_INSTR; ++i) {
       const int blk = wave * G_INSTR + i;
@@ -293,29 +273,40 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, u
       const int tr = tl < b_lim ? tl : b_lim;
       int f = f0 + c * 8;
       f = f < d_model ? f : 0;
-      dma16(Ht0 + (uint32_t)tr * (uint32_t)d_model + f, slot_lds + (uint32_t)(blk * 1024));
+      dma16(Ht0 + (uint32_t)tr * (uint32_t)d_model + f, dst + (uint32_t)(blk * 1024));
+    }
+  };
+  // any chunk (the prologue and the last k-steps)
+  auto issue_chunk = [&](int c) {
+    const int slot = c % NSLOT;
+    if (c < 2 * nk) {
+      if (c & 1) ENGRAM_ISSUE(Et0, off_b, c >> 1, slot);
+      else ENGRAM_ISSUE(W, off_a, c >> 1, slot);
+    } else {
+      issue_hq(c - 2 * nk, slot);
     }
   };
 
-  // MFMA operand fragments, double-buffered across the sub-steps.  Fragment row r of
-  // a slot operand is 64 B; sub-step s of lane l reads logical chunk 2 s + l / 32.
+  // MFMA operand fragments, double-buffered across the 4 sub-steps of a k-step;
+  // sub-step s of lane l reads logical chunk 2 s + l / 32 of rows (l % 32) + 32 i.
   const int khalf = lane >> 5;
   const int arow0 = wf * WF + (lane & 31);
   const int brow0 = wt * WT + (lane & 31);
-  uint32_t fr_a[2], fr_b[2];  // byte offsets inside a slot, per sub-step
+  uint32_t fr_a[4], fr_b[4];
 #pragma unroll
-  for (int ss = 0; ss < 2; ++ss) {
-    fr_a[ss] = (uint32_t)(arow0 * (BK * 2) + (((ss * 2 + khalf) ^ slot_key(arow0)) * 16));
-    fr_b[ss] = (uint32_t)(SLOT_A_BYTES + brow0 * (BK * 2) + (((ss * 2 + khalf) ^ slot_key(brow0)) * 16));
+  for (int ss = 0; ss < 4; ++ss) {
+    fr_a[ss] = (uint32_t)(arow0 * (BK * 2) + (((ss * 2 + khalf) ^ row_key(arow0)) * 16));
+    fr_b[ss] = (uint32_t)(brow0 * (BK * 2) + (((ss * 2 + khalf) ^ row_key(brow0)) * 16));
   }
   bf16x8 fa[2][MF], fb[2][MT];
-#define ENGRAM_LOAD_FRAGS(buf, slot_base_, ss_)                                            \
+#define ENGRAM_LOAD_FRAGS(buf, sa_, sb_, ss_)                                              \
   do {                                                                                     \
-    const char* sb_ = (const char*)smem + (slot_base_);                                    \
+    const char* pa_ = smem + (sa_) + fr_a[ss_];                                            \
+    const char* pb_ = smem + (sb_) + fr_b[ss_];                                            \
     _Pragma("unroll") for (int i = 0; i < MF; ++i)                                         \
-        fa[buf][i] = *reinterpret_cast<const bf16x8*>(sb_ + fr_a[ss_] + i * 32 * BK * 2);  \
+        fa[buf][i] = *reinterpret_cast<const bf16x8*>(pa_ + i * 32 * BK * 2);              \
     _Pragma("unroll") for (int j = 0; j < MT; ++j)                                         \
-        fb[buf][j] = *reinterpret_cast<const bf16x8*>(sb_ + fr_b[ss_] + j * 32 * BK * 2);  \
+        fb[buf][j] = *reinterpret_cast<const bf16x8*>(pb_ + j * 32 * BK * 2);              \
   } while (0)
 #define ENGRAM_MFMAS(buf)                                                                  \
   do {                                                                                     \
@@ -323,6 +314,21 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, u
         _Pragma("unroll") for (int j = 0; j < MT; ++j)                                     \
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j],    \
                                                                  acc[i][j], 0, 0, 0);      \
+  } while (0)
+  // the same 16 MFMAs with load instructions q0 .. q0 + 3 of a chunk (source base_ +
+  // k-step kt_, destination slot slot_) issued after each row of four
+#define ENGRAM_MFMAS_LOADS(buf, base_, off_, kt_, slot_, q0)                               \
+  do {                                                                                     \
+    const uint16_t* src_ = (base_) + (kt_) * BK;                                           \
+    const uint32_t dst_ = wave_dst + (uint32_t)((slot_) * SLOT_BYTES);                     \
+    _Pragma("unroll") for (int i = 0; i < MF; ++i) {                                       \
+      _Pragma("unroll") for (int j = 0; j < MT; ++j)                                       \
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j],      \
+                                                               acc[i][j], 0, 0, 0);        \
+      __builtin_amdgcn_sched_barrier(0);                                                   \
+      dma16(src_ + off_[(q0) + i], dst_ + ((q0) + i) * 1024);                              \
+      __builtin_amdgcn_sched_barrier(0);                                                   \
+    }                                                                                      \
   } while (0)
   // Sum of e^2 over the k-steps kt with kt % n_ftiles == ftile, from the memory
   // fragments: waves with wf == 0 see every token row of the tile (lanes l and l+32
@@ -345,57 +351,78 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, u
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  for (int g = 0; g < NSLOT; ++g) {
-    if (g < nk) ENGRAM_ISSUE_STAGE(g);
-    else issue_hq(g);
-  }
+  for (int c = 0; c < NSLOT; ++c) issue_chunk(c);
   wait_vm_lgkm0<3 * G_INSTR>();
   lds_barrier();
-  // k-step 0: both sub-steps' fragments, sub-step 0's MFMAs
-  ENGRAM_LOAD_FRAGS(0, 0, 0);
-  ENGRAM_LOAD_FRAGS(1, 0, 1);
+  // k-step 0, sub-steps 0-2 (sub-step 3's MFMAs open k-step 1); no slot is free yet
+  bool ee_now = ee_wave && ftile == 0;
+  ENGRAM_LOAD_FRAGS(0, 0, SLOT_BYTES, 0);
+  ENGRAM_LOAD_FRAGS(1, 0, SLOT_BYTES, 1);
   ENGRAM_MFMAS(0);
-  bool ee_prev = ee_wave && (0 % a.n_ftiles) == ftile;
-  if (ee_prev) ENGRAM_EE(0);
-  wait_vm_lgkm0<2 * G_INSTR>();
+  if (ee_now) ENGRAM_EE(0);
+  ENGRAM_LOAD_FRAGS(0, 0, SLOT_BYTES, 2);
+  ENGRAM_MFMAS(1);
+  if (ee_now) ENGRAM_EE(1);
+  ENGRAM_LOAD_FRAGS(1, 0, SLOT_BYTES, 3);
+  ENGRAM_MFMAS(0);
+  if (ee_now) ENGRAM_EE(0);
+  wait_vm_lgkm0<G_INSTR>();
   lds_barrier();
-  if (NSLOT < nk) ENGRAM_ISSUE_STAGE(NSLOT);
-  else issue_hq(0);
 
-  // k-step kt: sub-step 1 of k-step kt-1 (fragments already in registers) covers the
-  // latency of this step's first fragment reads; then sub-step 0 of kt.  The barrier
-  // at the end publishes stage kt+1 and frees slot kt % NSLOT for group kt + NSLOT:
-  // a stage while one is left, else the h-tile quarter of that slot.
-#define ENGRAM_KSTEP(kt)                                                                   \
+  // k-step kt: sub-step 3 of k-step kt-1 (fragments already in registers) covers
+  // the latency of this step's first fragment reads; each later sub-step's MFMAs
+  // cover the next one's reads.  MFMAS_0 .. MFMAS_3 run the four MFMA groups and
+  // issue this step's share of the operand stream; the barrier at the end publishes
+  // k-step kt+1 and frees k-step kt's slots.
+#define ENGRAM_KSTEP(kt, MFMAS_0, MFMAS_1, MFMAS_2, MFMAS_3)                               \
   do {                                                                                     \
-    const uint32_t slot_ = (uint32_t)(((kt) % NSLOT) * SLOT_BYTES);                        \
-    ENGRAM_LOAD_FRAGS(0, slot_, 0);                                                        \
+    const int sa_ = ((2 * (kt)) % NSLOT) * SLOT_BYTES;                                     \
+    const int sb_ = ((2 * (kt) + 1) % NSLOT) * SLOT_BYTES;                                 \
+    ENGRAM_LOAD_FRAGS(0, sa_, sb_, 0);                                                     \
     __builtin_amdgcn_sched_barrier(0);                                                     \
-    ENGRAM_MFMAS(1);                                                                       \
+    MFMAS_0;                                                                               \
     __builtin_amdgcn_sched_barrier(0);                                                     \
-    if (ee_prev) ENGRAM_EE(1);                                                             \
-    ENGRAM_LOAD_FRAGS(1, slot_, 1);                                                        \
+    if (ee_now) ENGRAM_EE(1);                                                              \
+    ee_now = ee_wave && ((kt) % a.n_ftiles) == ftile;                                      \
+    ENGRAM_LOAD_FRAGS(1, sa_, sb_, 1);                                                     \
     __builtin_amdgcn_sched_barrier(0);                                                     \
-    ENGRAM_MFMAS(0);                                                                       \
+    MFMAS_1;                                                                               \
     __builtin_amdgcn_sched_barrier(0);                                                     \
-    ee_prev = ee_wave && ((kt) % a.n_ftiles) == ftile;                                     \
-    if (ee_prev) ENGRAM_EE(0);                                                             \
-    wait_vm_lgkm0<2 * G_INSTR>();                                                          \
+    if (ee_now) ENGRAM_EE(0);                                                              \
+    ENGRAM_LOAD_FRAGS(0, sa_, sb_, 2);                                                     \
+    __builtin_amdgcn_sched_barrier(0);                                                     \
+    MFMAS_2;                                                                               \
+    __builtin_amdgcn_sched_barrier(0);                                                     \
+    if (ee_now) ENGRAM_EE(1);                                                              \
+    ENGRAM_LOAD_FRAGS(1, sa_, sb_, 3);                                                     \
+    __builtin_amdgcn_sched_barrier(0);                                                     \
+    MFMAS_3;                                                                               \
+    __builtin_amdgcn_sched_barrier(0);                                                     \
+    if (ee_now) ENGRAM_EE(0);                                                              \
+    wait_vm_lgkm0<G_INSTR>();                                                              \
     lds_barrier();                                                                         \
   } while (0)
   int kt = 1;
-  for (; kt + NSLOT < nk; ++kt) {
-    ENGRAM_KSTEP(kt);
-    ENGRAM_ISSUE_STAGE(kt + NSLOT);
+  // chunks 2 kt + 3 (memory rows of k-step kt + 1) and 2 kt + 4 (weight rows of
+  // k-step kt + 2) into the slots k-step kt - 1 freed
+  for (; kt + 2 < nk; ++kt) {
+    const int s3 = (2 * kt + 3) % NSLOT, s4 = (2 * kt + 4) % NSLOT;
+    ENGRAM_KSTEP(kt, ENGRAM_MFMAS_LOADS(1, Et0, off_b, kt + 1, s3, 0),
+                 ENGRAM_MFMAS_LOADS(0, Et0, off_b, kt + 1, s3, 4),
+                 ENGRAM_MFMAS_LOADS(1, W, off_a, kt + 2, s4, 0),
+                 ENGRAM_MFMAS_LOADS(0, W, off_a, kt + 2, s4, 4));
   }
+  // the last k-steps: the stream ends with the h-tile quarters
   for (; kt < nk; ++kt) {
-    ENGRAM_KSTEP(kt);
-    issue_hq(kt % NSLOT);
+    issue_chunk(2 * kt + 3);
+    issue_chunk(2 * kt + 4);
+    ENGRAM_KSTEP(kt, ENGRAM_MFMAS(1), ENGRAM_MFMAS(0), ENGRAM_MFMAS(1), ENGRAM_MFMAS(0));
   }
-#undef ENGRAM_KSTEP
-#undef ENGRAM_ISSUE_STAGE
+  issue_chunk(2 * nk + 3);
   ENGRAM_MFMAS(1);
-  if (ee_prev) ENGRAM_EE(1);
+  if (ee_now) ENGRAM_EE(1);
+#undef ENGRAM_KSTEP
+#undef ENGRAM_ISSUE
 #undef ENGRAM_EE
 #undef ENGRAM_LOAD_FRAGS
 #undef ENGRAM_MFMAS
@@ -420,15 +447,30 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, u
     }
   }
 
-  // ---- the h tile: its four quarters were loaded into the ring as it drained
+  // ---- the h tile: quarter q is chunk 2 nk + q, in slot (2 nk + q) % NSLOT; the
+  // fifth slot, (2 nk + 4) % NSLOT, holds the epilogue's cross-wave scratch
   wait_vm_lgkm0<0>();
   lds_barrier();
+  // claim this workgroup's next tile now; the atomic's latency hides behind the epilogue
+  if (tid == 0) next_claim = atomicAdd(a.counters + x, 1);
+  int qslot[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) qslot[q] = ((2 * nk + q) % NSLOT) * SLOT_BYTES;
+  char* scratch = smem + ((2 * nk + 4) % NSLOT) * SLOT_BYTES;
+  float (*s_red)[2][BT] = reinterpret_cast<float (*)[2][BT]>(scratch);  // [feature-wave][dot, hh][token]
+  float* s_alpha = reinterpret_cast<float*>(scratch + 4 * BT * sizeof(float));
+  // LDS byte offset of logical 16-B chunk c of token tl in the h tile
+#define ENGRAM_HOFF(tl, c) (qslot[(tl) >> 6] + ((tl) & 63) * (BF * 2) + (((c) ^ ((tl) & 31)) * 16))
+  int* s_flag = reinterpret_cast<int*>(scratch + 5 * BT * sizeof(float));
+  if (PHASE == PHASE_V) {
+    s_alpha[etid] = alpha;
+    lds_barrier();
+  }
 
   // Lane (token column tl) holds, for MFMA tile (i, j) and pair gp, features
   // fl = wf*WF + i*32 + gp*16 + (lane>>5)*8 + 0..7 in acc[i][j][8*gp + 0..7].
   const int hsel = (elane >> 5) * 8;
   if (PHASE == PHASE_K) {
-    const uint16_t* GQ = (const uint16_t*)a.gq[m];
 #pragma unroll
     for (int j = 0; j < MT; ++j) {
       const int tl = ewt * WT + j * 32 + (elane & 31);
@@ -439,14 +481,12 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, u
         for (int gp = 0; gp < 2; ++gp) {
           const int fl = ewf * WF + i * 32 + gp * 16 + hsel;
           if (f0 + fl < d_model) {
-            const int c = (fl >> 3) ^ (tl & 31);
-            const u32x4 hv = *reinterpret_cast<const u32x4*>(smem + tl * BF + c * 8);
-            const u32x4 gv = *reinterpret_cast<const u32x4*>(GQ + f0 + fl);
+            const u32x4 hv = *reinterpret_cast<const u32x4*>(smem + ENGRAM_HOFF(tl, fl >> 3));
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const float h0 = bf16_lo(hv[q]), h1 = bf16_hi(hv[q]);
-              dot += h0 * bf16_lo(gv[q]) * acc[i][j][gp * 8 + 2 * q];
-              dot += h1 * bf16_hi(gv[q]) * acc[i][j][gp * 8 + 2 * q + 1];
+              dot += h0 * acc[i][j][gp * 8 + 2 * q];
+              dot += h1 * acc[i][j][gp * 8 + 2 * q + 1];
               hh += h0 * h0 + h1 * h1;
             }
           }
@@ -469,7 +509,44 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, u
     // publish: __syncthreads() waits until every wave's partial stores have completed,
     // then the count goes up
     __syncthreads();
-    if (etid == 0) __hip_atomic_fetch_add(done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (etid == 0) *s_flag = __hip_atomic_fetch_add(done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    lds_barrier();
+    if (*s_flag == a.n_ftiles - 1) {
+      // The last K tile of this (branch, token tile): every other one stored its
+      // partials before its increment, so all are in L2.  Turn them into gates
+      // (fixed-order sums: bit-reproducible), publish, and count once more.
+      const int64_t t = t0 + etid;
+      if (t < n_tok) {
+        const int nf = a.n_ftiles;
+        const int64_t base = (int64_t)m * nf * n_tok + t;
+        float dot = 0.f, hh = 0.f, ee = 0.f;
+        for (int j0 = 0; j0 < nf; j0 += 8) {  // eight of each in flight at once
+          float vd[8], vh[8], ve[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const bool ok = j0 + u < nf;
+            const int64_t o = base + (int64_t)(ok ? j0 + u : 0) * n_tok;
+            vd[u] = ok ? ld_coherent(a.part_dot + o) : 0.f;
+            vh[u] = ok ? ld_coherent(a.part_hh + o) : 0.f;
+            ve[u] = ok ? ld_coherent(a.ee + o) : 0.f;
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            dot += vd[u];
+            hh += vh[u];
+            ee += ve[u];
+          }
+        }
+        const float rms_h = sqrtf(hh / (float)d_model + a.eps);
+        const float rms_e = sqrtf(ee / (float)d_mem + a.eps);
+        const float logit = dot / (rms_h * rms_e) * a.inv_sqrt_d;
+        const float g = 1.f / (1.f + expf(-logit));
+        st_coherent(a.alpha + (int64_t)m * n_tok + t, g);
+        if (a.gate_out != nullptr) a.gate_out[(int64_t)m * n_tok + t] = g;
+      }
+      __syncthreads();  // the gate stores have completed
+      if (etid == 0) __hip_atomic_fetch_add(done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   } else {
 #pragma unroll
     for (int j = 0; j < MT; ++j) {
@@ -480,8 +557,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, u
 #pragma unroll
         for (int gp = 0; gp < 2; ++gp) {
           const int fl = ewf * WF + i * 32 + gp * 16 + hsel;
-          const int c = (fl >> 3) ^ (tl & 31);
-          u32x4* cell = reinterpret_cast<u32x4*>(smem + tl * BF + c * 8);
+          u32x4* cell = reinterpret_cast<u32x4*>(smem + ENGRAM_HOFF(tl, fl >> 3));
           const u32x4 hv = *cell;
           u32x4 ov;
 #pragma unroll
@@ -492,9 +568,9 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, u
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
     uint16_t* Ot0 = (uint16_t*)a.out[m] + t0 * d_model;
-#pragma unroll 8
+#pragma unroll
     for (int i = 0; i < H_LOADS; ++i) {
       const int p = i * NTHR + etid;
       const int tl = p / H_CH;
@@ -503,32 +579,37 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, u
       const int f = f0 + c * 8;
       if (t0 + tl < n_tok && f < d_model)
         *reinterpret_cast<u32x4*>(Ot0 + (uint32_t)tl * (uint32_t)d_model + f) =
-            *reinterpret_cast<const u32x4*>(smem + p * 8);
+            *reinterpret_cast<const u32x4*>(smem + qslot[tl >> 6] + (tl & 63) * (BF * 2) + phys * 16);
     }
   }
+#undef ENGRAM_HOFF
 }
 
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gate_persistent_kernel(const GateArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM_ELEMS];  // stages, then h tile
-  __shared__ float s_red[2][2][BT];  // [feature-wave][dot, hh][token]
-  __shared__ float s_alpha[BT];
-  __shared__ int s_tile;
+  // the operand ring, then the h tile and the epilogue scratch; between tiles its
+  // first word broadcasts the claimed tile number
+  __shared__ __attribute__((aligned(16))) char smem[SMEM_BYTES];
+  int* s_tile = reinterpret_cast<int*>(smem);
   const int x = blockIdx.x % NQ;
+  int claim = 0;  // thread 0: the tile claimed for after the current one
+  if (threadIdx.x == 0) claim = atomicAdd(a.counters + x, 1);
   for (;;) {
-    if (threadIdx.x == 0) s_tile = atomicAdd(a.counters + x, 1);
-    __syncthreads();
+    if (threadIdx.x == 0) *s_tile = claim;
+    lds_barrier();
     Tile t;
-    const bool have = decode_tile(a, x, s_tile, t);
-    __syncthreads();  // every thread has read s_tile before it is claimed again
+    const bool have = decode_tile(a, x, *s_tile, t);
+    lds_barrier();  // every thread has read the tile number before the ring is refilled
     if (!have) break;
-    gate_tile(a, t, smem, s_red, s_alpha);
-    __syncthreads();  // LDS free for the next tile
+    gate_tile(a, t, smem, x, claim);
+    // LDS free for the next tile; a V tile's output stores keep draining meanwhile
+    lds_barrier();
   }
 }
 
-// One launch before the gate: W'[m][i][j] = bf16(W_K[m][i][j] * gk[m][j]) for every
-// branch, and the tile queues / done counters cleared.
+// One launch before the gate: W'[m][f][c] = bf16(gq[m][f] * W_K[m][f][c] * gk[m][c])
+// for every branch (both RMSNorm gains folded into the key weights, one rounding),
+// and the tile queues / done counters cleared.
 __global__ __launch_bounds__(256) void gate_prep_kernel(const GateArgs a, uint16_t* wk_scaled,
                                                         int64_t n8_per_branch, int n_counters) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -536,18 +617,20 @@ __global__ __launch_bounds__(256) void gate_prep_kernel(const GateArgs a, uint16
   if (i >= n8_per_branch * a.n_branch) return;
   const int m = (int)(i / n8_per_branch);
   const int64_t k = i - m * n8_per_branch;
-  const int j = (int)((k * 8) % a.d_mem);
+  const int f = (int)((k * 8) / a.d_mem);
+  const int j = (int)((k * 8) - (int64_t)f * a.d_mem);
   const u32x4 wv = reinterpret_cast<const u32x4*>(a.wk[m])[k];
   const u32x4 gv = *reinterpret_cast<const u32x4*>((const uint16_t*)a.gk[m] + j);
+  const float gq = __uint_as_float((uint32_t)((const uint16_t*)a.gq[m])[f] << 16);
   u32x4 o;
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    o[q] = pack_bf16(bf16_lo(wv[q]) * bf16_lo(gv[q]), bf16_hi(wv[q]) * bf16_hi(gv[q]));
+    o[q] = pack_bf16(gq * bf16_lo(wv[q]) * bf16_lo(gv[q]), gq * bf16_hi(wv[q]) * bf16_hi(gv[q]));
   reinterpret_cast<u32x4*>(wk_scaled)[i] = o;
 }
 
 struct ScratchLayout {
-  size_t wk_bytes, part_bytes, counter_bytes, total;
+  size_t wk_bytes, part_bytes, alpha_bytes, counter_bytes, total;
   int n_counters;
 };
 
@@ -556,9 +639,10 @@ ScratchLayout layout_for(const GateArgs& a) {
   L.wk_bytes = ((size_t)a.n_branch * a.d_model * a.d_mem * 2 + 255) & ~(size_t)255;
   const size_t part_elems = (size_t)a.n_branch * a.n_ftiles * (size_t)a.n_tok;
   L.part_bytes = (part_elems * 4 + 255) & ~(size_t)255;
+  L.alpha_bytes = ((size_t)a.n_branch * (size_t)a.n_tok * 4 + 255) & ~(size_t)255;
   L.n_counters = NQ + a.n_branch * a.n_ttiles;
   L.counter_bytes = ((size_t)L.n_counters * 4 + 255) & ~(size_t)255;
-  L.total = L.wk_bytes + 3 * L.part_bytes + L.counter_bytes;
+  L.total = L.wk_bytes + 3 * L.part_bytes + L.alpha_bytes + L.counter_bytes;
   return L;
 }
 
@@ -592,7 +676,8 @@ void launch_gate_bf16(const GateArgs& a_in, hipStream_t s) {
   a.part_dot = (float*)(base + L.wk_bytes);
   a.part_hh = (float*)(base + L.wk_bytes + L.part_bytes);
   a.ee = (float*)(base + L.wk_bytes + 2 * L.part_bytes);
-  a.counters = (int32_t*)(base + L.wk_bytes + 3 * L.part_bytes);
+  a.alpha = (float*)(base + L.wk_bytes + 3 * L.part_bytes);
+  a.counters = (int32_t*)(base + L.wk_bytes + 3 * L.part_bytes + L.alpha_bytes);
 
   const int64_t n8 = (int64_t)a.d_model * a.d_mem / 8;
   const int64_t work = n8 * a.n_branch > L.n_counters ? n8 * a.n_branch : L.n_counters;
