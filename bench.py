@@ -9,6 +9,7 @@ dominant kernel (the gate) and the CPU oracle's tokens/s on a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--config small|multi|large|tiny]
     python bench.py --calibrate-copy MIB     # plain device copy, for HBM counter scaling
+    python bench.py --config offload         # decode steps: host-resident vs HBM-resident tables
 
 Between timed steps (outside the timed events) a scratch buffer larger than the
 last-level cache is rewritten, so every step starts with cold L2 and MALL.
@@ -42,6 +43,12 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time of the CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--flush-mb", type=int, default=512, help="cache-flush buffer rewritten between steps (0: off)")
+    p.add_argument("--offload-rows", type=int, default=0,
+                   help="offload config: rows per table (default: 100B parameters, scaled to 60%% of free host RAM)")
+    p.add_argument("--offload-reps", type=int, default=3)
+    p.add_argument("--offload-host-gb", type=float, default=48.0,
+                   help="offload config: cap on pinned host table bytes (the GPU's system-memory aperture is "
+                        "shared with the runtime; on the measured host, pinning beyond ~64 GB fails)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB three times and exit")
     return p.parse_args()
@@ -110,6 +117,187 @@ def calibrate_copy(mib):
                       "kib_read": 2 * n / 1024, "kib_written": 2 * n / 1024}), flush=True)
 
 
+def mem_available_bytes():
+    with open("/proc/meminfo") as f:
+        for line in f:
+            if line.startswith("MemAvailable:"):
+                return int(line.split()[1]) * 1024
+    return None
+
+
+def run_offload(args):
+    """Decode steps of the host-offload workload (256 sequences, one new token each):
+    the rows of step s+1 are hashed and fetched on a side stream while step s gates.
+    The same two-stream pipeline runs once with the tables in pinned host memory
+    (engram_prefetch_host over PCIe) and once with the same tables in HBM
+    (engram_gather); the overhead is the ratio of the steady-state step times."""
+    import ctypes
+    import numpy as np
+    import torch
+    import synth
+    import hashed_gram_embedding_hash_amd as eg
+
+    cfg = synth.CONFIGS["offload"]
+    dev = torch.device("cuda:0")
+    say = lambda *a: print("[bench]", *a, file=sys.stderr, flush=True)
+    avail = mem_available_bytes()
+    rows = args.offload_rows or synth.offload_rows(cfg, avail)
+    row_bytes = cfg.w * 2
+    cap_rows = int(args.offload_host_gb * 1e9 / (cfg.n_tables * row_bytes))
+    if not args.offload_rows and rows > cap_rows:
+        rows = synth.next_prime(cap_rows)
+    free_hbm, _ = torch.cuda.mem_get_info()
+    if cfg.n_tables * rows * row_bytes > 0.8 * free_hbm:  # the HBM-resident copy must fit as well
+        rows = synth.next_prime(int(0.8 * free_hbm / (cfg.n_tables * row_bytes)))
+    say(f"offload: target {cfg.n_tables} tables x {rows} rows = {cfg.n_tables * rows * row_bytes / 1e9:.1f} GB "
+        f"(host MemAvailable {avail / 1e9 if avail else float('nan'):.0f} GB)")
+
+    dtabs, haddr = [], []
+    try:
+        for b in range(cfg.n_tables):
+            t = torch.empty((rows, cfg.w), dtype=torch.bfloat16, device=dev)
+            dtabs.append(synth.fill_table(cfg, b, t))
+        torch.cuda.synchronize()
+        say("device tables filled")
+        for b in range(cfg.n_tables):
+            haddr.append(eg.host_alloc(rows * row_bytes))
+        for b in range(cfg.n_tables):
+            arr = np.ctypeslib.as_array((ctypes.c_int16 * (rows * cfg.w)).from_address(haddr[b]))
+            torch.from_numpy(arr).view(torch.bfloat16).view(rows, cfg.w).copy_(dtabs[b])
+        torch.cuda.synchronize()
+        table_bytes = cfg.n_tables * rows * row_bytes
+        say(f"host tables filled: {cfg.n_tables} x {rows} rows = {table_bytes / 1e9:.1f} GB")
+
+        S, B, T0 = cfg.decode_steps, cfg.batch, cfg.seq
+        raw = torch.from_numpy(synth.raw_ids(cfg)).to(dev)            # [B, T0 + S]
+        ids = eg.engram_compress(raw, torch.from_numpy(synth.comp_map(cfg)).to(dev))
+        mult, rows_u32 = synth.multipliers(cfg), np.full(cfg.n_tables, rows, dtype=np.uint32)
+        wk, wv = synth.weights(cfg, 0, dev)
+        gq, gk = synth.gains(cfg, 0, dev)
+        tok = (torch.arange(B, dtype=torch.int64) * (T0 + S)).view(1, B) + (T0 + torch.arange(S)).view(S, 1)
+        h = synth.hidden_rows(cfg, 0, tok.reshape(-1), dev).view(S, B, cfg.d_model)
+        out = torch.empty((B, cfg.d_model), dtype=torch.bfloat16, device=dev)
+        idx = [torch.empty((B, cfg.n_tables), dtype=torch.int32, device=dev) for _ in range(2)]
+        stg = [torch.empty((B, cfg.n_tables * cfg.w), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+        main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+        hrows = [rows] * cfg.n_tables
+
+        # Per-step calls go straight to the C ABI with arguments prepared once, so the
+        # host issues a step in a few microseconds and the GPU sets the pace.
+        L = eg.lib()
+        P = ctypes.c_void_p
+        ms, ss = P(main.cuda_stream), P(side.cuda_stream)
+        orders_a = np.ascontiguousarray(cfg.orders, dtype=np.int32)
+        mult_a = np.ascontiguousarray(mult, dtype=np.uint64)
+        rows64 = np.full(cfg.n_tables, rows, dtype=np.int64)
+        dptrs = (P * cfg.n_tables)(*[t.data_ptr() for t in dtabs])
+        hptrs = (P * cfg.n_tables)(*haddr)
+        arr = lambda xs: (P * len(xs))(*[x.data_ptr() for x in xs])
+        wk_a, wv_a, gq_a, gk_a, out_a = arr([wk]), arr([wv]), arr([gq]), arr([gk]), arr([out])
+        h_a = [arr([h[s]]) for s in range(S)]
+        chk = lambda st: st == 0 or eg._check(st)
+
+        def fetch(mode, s, buf, stream):
+            st = ss if stream is side else ms
+            chk(L.engram_hash(ids.data_ptr(), B, ids.shape[1], T0 + s, 1, orders_a.ctypes.data, len(cfg.orders),
+                              cfg.heads, mult_a.ctypes.data, rows_u32.ctypes.data, cfg.vocab_c, idx[buf].data_ptr(), st))
+            fn = L.engram_prefetch_host if mode == "host" else L.engram_gather
+            chk(fn(idx[buf].data_ptr(), B, cfg.n_tables, hptrs if mode == "host" else dptrs, rows64.ctypes.data,
+                   cfg.w, eg.BF16, stg[buf].data_ptr(), None, st))
+
+        def gate(s, buf):
+            chk(L.engram_gate_forward(stg[buf].data_ptr(), B, cfg.d_mem, cfg.d_model, 1, h_a[s], wk_a, wv_a, gq_a,
+                                      gk_a, cfg.eps, eg.BF16, out_a, None, ms))
+
+        def pipeline(mode):
+            ready = [torch.cuda.Event() for _ in range(2)]
+            free = [torch.cuda.Event() for _ in range(2)]
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            side.wait_stream(main)
+            with torch.cuda.stream(side):
+                fetch(mode, 0, 0, side)
+                ready[0].record(side)
+            t0.record(main)
+            host0 = time.perf_counter()
+            for s in range(S):
+                cur, nxt = s % 2, (s + 1) % 2
+                if s + 1 < S:
+                    with torch.cuda.stream(side):
+                        side.wait_event(free[nxt])      # the gate of step s-1 has read that buffer
+                        fetch(mode, s + 1, nxt, side)
+                        ready[nxt].record(side)
+                main.wait_event(ready[cur])
+                gate(s, cur)
+                free[cur].record(main)
+            t1.record(main)
+            host_us.append((time.perf_counter() - host0) * 1e6 / S)
+            torch.cuda.synchronize()
+            return t0.elapsed_time(t1) * 1e3 / S     # us per step
+
+        def serial(fn, n=S):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for s in range(n):
+                fn(s)
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) * 1e3 / n
+
+        host_us = []
+        for mode in ("hbm", "host"):
+            pipeline(mode)                             # warm-up
+        steps = {"hbm": [], "host": []}
+        for _ in range(args.offload_reps):
+            for mode in ("hbm", "host"):
+                steps[mode].append(pipeline(mode))
+        med = {k: float(np.median(v)) for k, v in steps.items()}
+        comp = {
+            "hash_us": serial(lambda s: chk(L.engram_hash(ids.data_ptr(), B, ids.shape[1], T0 + s, 1,
+                                                          orders_a.ctypes.data, len(cfg.orders), cfg.heads,
+                                                          mult_a.ctypes.data, rows_u32.ctypes.data, cfg.vocab_c,
+                                                          idx[0].data_ptr(), ms))),
+            "gather_hbm_us": serial(lambda s: chk(L.engram_gather(idx[0].data_ptr(), B, cfg.n_tables, dptrs,
+                                                                  rows64.ctypes.data, cfg.w, eg.BF16,
+                                                                  stg[0].data_ptr(), None, ms))),
+            "prefetch_host_us": serial(lambda s: chk(L.engram_prefetch_host(idx[0].data_ptr(), B, cfg.n_tables, hptrs,
+                                                                         rows64.ctypes.data, cfg.w, eg.BF16,
+                                                                         stg[0].data_ptr(), None, ms))),
+            "gate_us": serial(lambda s: gate(s, 0)),
+        }
+        pcie_bytes = B * cfg.n_tables * row_bytes
+        comp["prefetch_host_GBps"] = pcie_bytes / (comp["prefetch_host_us"] * 1e-6) / 1e9
+        # reference: pinned host-to-device copy of one contiguous 256 MiB block
+        nb = min(256 << 20, rows * row_bytes)
+        dst = torch.empty(nb, dtype=torch.uint8, device=dev)
+        src = torch.from_numpy(np.ctypeslib.as_array((ctypes.c_uint8 * nb).from_address(haddr[0])))
+        comp["h2d_memcpy_GBps"] = nb / (serial(lambda s: dst.copy_(src, non_blocking=True), 5) * 1e-6) / 1e9
+        res = {
+            "metric": "host-offload overhead of an Engram decode step (tables in pinned host DRAM vs HBM)",
+            "value": round(100.0 * (med["host"] / med["hbm"] - 1.0), 2), "unit": "%", "higher_is_better": False,
+            "n_gpus": 1, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "offload", "sequences": B, "history": T0, "decode_steps": S,
+                       "tables": f"{cfg.n_tables} x {rows} x {cfg.w} bf16", "table_GB": round(table_bytes / 1e9, 2),
+                       "host_mem_available_GB": round(avail / 1e9, 1) if avail else None,
+                       "full_size_rows": cfg.rows,
+                       "sizing": f"100B parameters scaled to min(60% of free host RAM, {args.offload_host_gb:g} GB "
+                                 "of pinned host memory, 80% of free HBM)",
+                       "d_mem": cfg.d_mem, "d_model": cfg.d_model, "branches": 1,
+                       "pipeline": "side stream: hash + fetch of step s+1; main stream: gate of step s"},
+            "step_us": {k: round(v, 2) for k, v in med.items()},
+            "step_us_all": {k: [round(x, 2) for x in v] for k, v in steps.items()},
+            "host_enqueue_us_per_step": round(float(np.median(host_us)), 2),
+            "decode_tokens_per_s": {k: round(B / (v * 1e-6), 1) for k, v in med.items()},
+            "components_serial": {k: round(v, 2) for k, v in comp.items()},
+            "pcie_bytes_per_step": pcie_bytes,
+        }
+        print(json.dumps(res), flush=True)
+    finally:
+        dtabs.clear()
+        torch.cuda.synchronize()
+        for a in haddr:
+            eg.host_free(a)
+
+
 def cpu_baseline(cfg, target_s):
     """The oracle (single thread) on the first tokens of sequence 0: compress, hash,
     gather and gate.  Table rows are regenerated outside the timed region."""
@@ -167,6 +355,10 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+
+    if args.config == "offload":
+        run_offload(args)
         return
 
     import torch

@@ -5,6 +5,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 
 #include "engram_internal.h"
 
@@ -86,6 +87,24 @@ const void* mapped_host_pointer(const void* p) {
   if (hb == nullptr) return db;
   return db + ((const char*)p - hb);
 }
+
+// The bf16 gate's scratch (folded key weights, partial sums, gates, work-queue
+// counters): one grow-only buffer per device, reused by every call.  A call on the
+// stream that used it last needs nothing more (stream order); a call on another
+// stream first waits for an event recorded after the previous use.  Growing frees the
+// old buffer in stream order behind that wait.  The lock is held from acquiring the
+// buffer until the launches and the event record are enqueued, so concurrent host
+// threads take turns.  Buffers live until the process ends.
+struct GateScratch {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+  hipStream_t last = nullptr;
+  hipEvent_t done = nullptr;
+  bool used = false;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+GateScratch g_scratch[kMaxDevices];
 
 }  // namespace
 
@@ -270,15 +289,46 @@ engram_status engram_gate_forward(const void* mem, int64_t n_tok, int32_t d_mem,
   }
 
   const size_t bytes = gate_bf16_scratch_bytes(a);
-  void* scratch = nullptr;
-  hipError_t e = hipMallocAsync(&scratch, bytes, stream);
-  if (e != hipSuccess) return hip_fail(e, "engram_gate_forward: hipMallocAsync(scratch)");
-  a.part_dot = (float*)scratch;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "engram_gate_forward: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(ENGRAM_ERR_UNSUPPORTED, "%s: device %d", fn, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  GateScratch& g = g_scratch[dev];
+  if (g.done == nullptr) {
+    e = hipEventCreateWithFlags(&g.done, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      g.done = nullptr;
+      return hip_fail(e, "engram_gate_forward: hipEventCreateWithFlags");
+    }
+  }
+  if (g.used && g.last != stream) {
+    e = hipStreamWaitEvent(stream, g.done, 0);
+    if (e != hipSuccess) return hip_fail(e, "engram_gate_forward: hipStreamWaitEvent");
+  }
+  if (g.bytes < bytes) {
+    if (g.ptr != nullptr) {
+      e = hipFreeAsync(g.ptr, stream);
+      g.ptr = nullptr;
+      g.bytes = 0;
+      if (e != hipSuccess) return hip_fail(e, "engram_gate_forward: hipFreeAsync(scratch)");
+    }
+    const size_t grow = bytes + bytes / 4;  // slack for slightly larger later calls
+    e = hipMallocAsync(&g.ptr, grow, stream);
+    if (e != hipSuccess) {
+      g.ptr = nullptr;
+      return hip_fail(e, "engram_gate_forward: hipMallocAsync(scratch)");
+    }
+    g.bytes = grow;
+  }
+  a.part_dot = (float*)g.ptr;
   launch_gate_bf16(a, stream);
   const engram_status st = check_launch(fn);
-  e = hipFreeAsync(scratch, stream);
+  e = hipEventRecord(g.done, stream);
+  g.last = stream;
+  g.used = true;
   if (st != ENGRAM_OK) return st;
-  if (e != hipSuccess) return hip_fail(e, "engram_gate_forward: hipFreeAsync(scratch)");
+  if (e != hipSuccess) return hip_fail(e, "engram_gate_forward: hipEventRecord");
   return ENGRAM_OK;
 }
 

@@ -23,8 +23,10 @@
  *     the call returns after enqueueing.  Outputs are valid once the stream
  *     reaches that point.
  *   - Ownership: the library never frees or keeps caller buffers.  The gate
- *     allocates its own small stream-ordered scratch (hipMallocAsync /
- *     hipFreeAsync on `stream`).
+ *     keeps one grow-only scratch buffer per device (a few MB to a few hundred
+ *     MB, by shape), allocated stream-ordered on first use and held until the
+ *     process ends; a call on a different stream than the previous gate call
+ *     first waits for that call's work on the scratch.
  *   - Errors: arguments are validated on the host before anything is enqueued;
  *     a non-OK status means nothing was enqueued (ENGRAM_ERR_INVALID_ARG,
  *     ENGRAM_ERR_UNSUPPORTED) or a HIP call failed (ENGRAM_ERR_HIP).

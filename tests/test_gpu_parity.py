@@ -213,6 +213,39 @@ def test_gate_bf16_multi_branch_in_place():
     _gate_case(synth.CONFIGS["multi"], 130, seed=12, table_std=0.5, inplace=True)
 
 
+def test_gate_bf16_scratch_shared_across_streams_and_sizes():
+    """The gate keeps one scratch buffer per device.  Calls alternating between two
+    streams, with a larger shape in between (the buffer grows), must give exactly the
+    results of the same calls made one at a time (the gate's sums have a fixed order)."""
+    cfg = synth.CONFIGS["small"]
+    say("gate bf16 scratch reuse across streams")
+    g = torch.Generator().manual_seed(5)
+    wk, wv = synth.weights(cfg, 0, DEV)
+    gq, gk = synth.gains(cfg, 0, DEV)
+    cases = []
+    for n in (300, 2100, 300, 777):
+        e = (torch.randn(n, cfg.d_mem, generator=g) * 0.05).to(torch.bfloat16).to(DEV)
+        h = torch.randn(n, cfg.d_model, generator=g).to(torch.bfloat16).to(DEV)
+        cases.append((e, h))
+    ref = []
+    for e, h in cases:
+        ref.append(eg.engram_gate_forward(e, [h], [wk], [wv], [gq], [gk], cfg.eps)[0])
+        torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.empty_like(h) for _, h in cases]
+    for rep in range(2):
+        for i, (e, h) in enumerate(cases):
+            s = streams[(i + rep) % 2]
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                eg.engram_gate_forward(e, [h], [wk], [wv], [gq], [gk], cfg.eps, out=[outs[i]], stream=s)
+        torch.cuda.synchronize()
+        for i in range(len(cases)):
+            assert torch.equal(outs[i].view(torch.int16), ref[i].view(torch.int16)), (rep, i)
+            outs[i].zero_()
+        torch.cuda.synchronize()
+
+
 def test_gate_bf16_zero_value_and_closed_gate_are_identity():
     """W_V = 0, or a gate driven to 0, leaves h bit-exact."""
     cfg = synth.CONFIGS["small"]
