@@ -30,6 +30,11 @@ FLAGS = [
     "-Wno-unused-function",
     # keep the compiler from forming packed-fp32 (v_pk_*_f32) instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # atomics stay single atomics: the gate claims its next tile early and reads the
+    # result late, which the wave-aggregating rewrite (it consumes the result at once)
+    # would turn into a full memory round trip; the library's other atomics are
+    # already one per wave or rare
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -427,6 +427,10 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
 #undef ENGRAM_LOAD_FRAGS
 #undef ENGRAM_MFMAS
 
+  // Nothing of the epilogue may be scheduled into the last k-steps (measured: 8 %
+  // slower when the compiler is free to interleave them).
+  __builtin_amdgcn_sched_barrier(0);
+
   // Everything below re-derives its indices from an opaque copy of the thread id, so
   // the compiler cannot compute epilogue addresses before the loop and keep them
   // live (in registers the main loop needs) across it.
@@ -453,14 +457,15 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
   lds_barrier();
   // claim this workgroup's next tile now; the atomic's latency hides behind the epilogue
   if (tid == 0) next_claim = atomicAdd(a.counters + x, 1);
-  int qslot[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) qslot[q] = ((2 * nk + q) % NSLOT) * SLOT_BYTES;
+  // byte offset of h-tile quarter q (a runtime q must not index a local array: that
+  // would live in scratch memory and cost a memory round trip per access)
+  const int q0slot = (2 * nk) % NSLOT;
+#define ENGRAM_QSLOT(q) ((q0slot + (q) >= NSLOT ? q0slot + (q) - NSLOT : q0slot + (q)) * SLOT_BYTES)
   char* scratch = smem + ((2 * nk + 4) % NSLOT) * SLOT_BYTES;
   float (*s_red)[2][BT] = reinterpret_cast<float (*)[2][BT]>(scratch);  // [feature-wave][dot, hh][token]
   float* s_alpha = reinterpret_cast<float*>(scratch + 4 * BT * sizeof(float));
   // LDS byte offset of logical 16-B chunk c of token tl in the h tile
-#define ENGRAM_HOFF(tl, c) (qslot[(tl) >> 6] + ((tl) & 63) * (BF * 2) + (((c) ^ ((tl) & 31)) * 16))
+#define ENGRAM_HOFF(tl, c) (ENGRAM_QSLOT((tl) >> 6) + ((tl) & 63) * (BF * 2) + (((c) ^ ((tl) & 31)) * 16))
   int* s_flag = reinterpret_cast<int*>(scratch + 5 * BT * sizeof(float));
   if (PHASE == PHASE_V) {
     s_alpha[etid] = alpha;
@@ -474,24 +479,34 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
 #pragma unroll
     for (int j = 0; j < MT; ++j) {
       const int tl = ewt * WT + j * 32 + (elane & 31);
-      float dot = 0.f, hh = 0.f;
+      // all eight cells first (no LDS writes in between, so the reads issue back to
+      // back); features past d_model (a ragged last feature tile) count as zero
+      u32x4 hv[MF][2];
+#pragma unroll
+      for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp) {
+          const int fl = ewf * WF + i * 32 + gp * 16 + hsel;
+          hv[i][gp] = *reinterpret_cast<const u32x4*>(smem + ENGRAM_HOFF(tl, fl >> 3));
+          if (f0 + fl >= d_model) hv[i][gp] = (u32x4){0u, 0u, 0u, 0u};
+        }
+      float dot = 0.f, hh = 0.f, dot2 = 0.f, hh2 = 0.f;  // two chains each
 #pragma unroll
       for (int i = 0; i < MF; ++i) {
 #pragma unroll
         for (int gp = 0; gp < 2; ++gp) {
-          const int fl = ewf * WF + i * 32 + gp * 16 + hsel;
-          if (f0 + fl < d_model) {
-            const u32x4 hv = *reinterpret_cast<const u32x4*>(smem + ENGRAM_HOFF(tl, fl >> 3));
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float h0 = bf16_lo(hv[q]), h1 = bf16_hi(hv[q]);
-              dot += h0 * acc[i][j][gp * 8 + 2 * q];
-              dot += h1 * acc[i][j][gp * 8 + 2 * q + 1];
-              hh += h0 * h0 + h1 * h1;
-            }
+          for (int q = 0; q < 4; ++q) {
+            const float h0 = bf16_lo(hv[i][gp][q]), h1 = bf16_hi(hv[i][gp][q]);
+            dot += h0 * acc[i][j][gp * 8 + 2 * q];
+            dot2 += h1 * acc[i][j][gp * 8 + 2 * q + 1];
+            hh += h0 * h0;
+            hh2 += h1 * h1;
           }
         }
       }
+      dot += dot2;
+      hh += hh2;
       dot += __shfl_xor(dot, 32, 64);
       hh += __shfl_xor(hh, 32, 64);
       if (elane < 32) {
@@ -552,37 +567,55 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
     for (int j = 0; j < MT; ++j) {
       const int tl = ewt * WT + j * 32 + (elane & 31);
       const float alpha = s_alpha[tl];
+      // all eight cells of this token column are read before any is written, so the
+      // reads are issued back to back (a write could alias a later read otherwise)
+      u32x4 hv[MF][2];
+#pragma unroll
+      for (int i = 0; i < MF; ++i)
+#pragma unroll
+        for (int gp = 0; gp < 2; ++gp)
+          hv[i][gp] = *reinterpret_cast<const u32x4*>(
+              smem + ENGRAM_HOFF(tl, (ewf * WF + i * 32 + gp * 16 + hsel) >> 3));
 #pragma unroll
       for (int i = 0; i < MF; ++i) {
 #pragma unroll
         for (int gp = 0; gp < 2; ++gp) {
-          const int fl = ewf * WF + i * 32 + gp * 16 + hsel;
-          u32x4* cell = reinterpret_cast<u32x4*>(smem + ENGRAM_HOFF(tl, fl >> 3));
-          const u32x4 hv = *cell;
           u32x4 ov;
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            ov[q] = pack_bf16(bf16_lo(hv[q]) + alpha * acc[i][j][gp * 8 + 2 * q],
-                              bf16_hi(hv[q]) + alpha * acc[i][j][gp * 8 + 2 * q + 1]);
-          *cell = ov;
+            ov[q] = pack_bf16(bf16_lo(hv[i][gp][q]) + alpha * acc[i][j][gp * 8 + 2 * q],
+                              bf16_hi(hv[i][gp][q]) + alpha * acc[i][j][gp * 8 + 2 * q + 1]);
+          *reinterpret_cast<u32x4*>(smem + ENGRAM_HOFF(tl, (ewf * WF + i * 32 + gp * 16 + hsel) >> 3)) = ov;
         }
       }
     }
     lds_barrier();
+    // Stream the tile out: 16-B chunk p = 256 i + tid is token tl = p / 32, physical
+    // chunk p % 32; eight LDS reads are issued ahead of their eight stores.
     uint16_t* Ot0 = (uint16_t*)a.out[m] + t0 * d_model;
+    const bool full = t0 + BT <= n_tok && f0 + BF <= d_model;
 #pragma unroll
-    for (int i = 0; i < H_LOADS; ++i) {
-      const int p = i * NTHR + etid;
-      const int tl = p / H_CH;
-      const int phys = p % H_CH;
-      const int c = phys ^ (tl & 31);
-      const int f = f0 + c * 8;
-      if (t0 + tl < n_tok && f < d_model)
-        *reinterpret_cast<u32x4*>(Ot0 + (uint32_t)tl * (uint32_t)d_model + f) =
-            *reinterpret_cast<const u32x4*>(smem + qslot[tl >> 6] + (tl & 63) * (BF * 2) + phys * 16);
+    for (int i0 = 0; i0 < H_LOADS; i0 += 8) {
+      u32x4 ov[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int p = (i0 + u) * NTHR + etid;
+        const int tl = p / H_CH;
+        ov[u] = *reinterpret_cast<const u32x4*>(smem + ENGRAM_QSLOT(tl >> 6) + (tl & 63) * (BF * 2) +
+                                                (p % H_CH) * 16);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int p = (i0 + u) * NTHR + etid;
+        const int tl = p / H_CH;
+        const int f = f0 + ((p % H_CH) ^ (tl & 31)) * 8;
+        if (full || (t0 + tl < n_tok && f < d_model))
+          *reinterpret_cast<u32x4*>(Ot0 + (uint32_t)tl * (uint32_t)d_model + f) = ov[u];
+      }
     }
   }
 #undef ENGRAM_HOFF
+#undef ENGRAM_QSLOT
 }
 
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -602,8 +635,10 @@ void gate_persistent_kernel(const GateArgs a) {
     lds_barrier();  // every thread has read the tile number before the ring is refilled
     if (!have) break;
     gate_tile(a, t, smem, x, claim);
-    // LDS free for the next tile; a V tile's output stores keep draining meanwhile
-    lds_barrier();
+    // LDS free for the next tile.  A full barrier: letting a V tile's 128 KB of output
+    // stores drain behind the next tile's operand loads measured 8 % slower than
+    // finishing them first.
+    __syncthreads();
   }
 }
 
