@@ -299,14 +299,18 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
     fr_b[ss] = (uint32_t)(brow0 * (BK * 2) + (((ss * 2 + khalf) ^ row_key(brow0)) * 16));
   }
   bf16x8 fa[2][MF], fb[2][MT];
+  // Reads are issued in the order the MFMAs consume them (row i = 0 of the weight
+  // fragments with all memory fragments, then the other weight rows), so the first
+  // MFMAs wait for two reads, not five.
 #define ENGRAM_LOAD_FRAGS(buf, sa_, sb_, ss_)                                              \
   do {                                                                                     \
     const char* pa_ = smem + (sa_) + fr_a[ss_];                                            \
     const char* pb_ = smem + (sb_) + fr_b[ss_];                                            \
-    _Pragma("unroll") for (int i = 0; i < MF; ++i)                                         \
-        fa[buf][i] = *reinterpret_cast<const bf16x8*>(pa_ + i * 32 * BK * 2);              \
+    fa[buf][0] = *reinterpret_cast<const bf16x8*>(pa_);                                    \
     _Pragma("unroll") for (int j = 0; j < MT; ++j)                                         \
         fb[buf][j] = *reinterpret_cast<const bf16x8*>(pb_ + j * 32 * BK * 2);              \
+    _Pragma("unroll") for (int i = 1; i < MF; ++i)                                         \
+        fa[buf][i] = *reinterpret_cast<const bf16x8*>(pa_ + i * 32 * BK * 2);              \
   } while (0)
 #define ENGRAM_MFMAS(buf)                                                                  \
   do {                                                                                     \
@@ -315,19 +319,39 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j],    \
                                                                  acc[i][j], 0, 0, 0);      \
   } while (0)
-  // the same 16 MFMAs with load instructions q0 .. q0 + 3 of a chunk (source base_ +
-  // k-step kt_, destination slot slot_) issued after each row of four
-#define ENGRAM_MFMAS_LOADS(buf, base_, off_, kt_, slot_, q0)                               \
+  // One fragment read (n = 0..7, in the order the MFMAs consume them) of sub-step ss_.
+#define ENGRAM_READ1(buf, sa_, sb_, ss_, n)                                                \
+  do {                                                                                     \
+    if ((n) == 0)                                                                          \
+      fa[buf][0] = *reinterpret_cast<const bf16x8*>(smem + (sa_) + fr_a[ss_]);             \
+    else if ((n) <= MT)                                                                    \
+      fb[buf][(n) - 1] = *reinterpret_cast<const bf16x8*>(smem + (sb_) + fr_b[ss_] +       \
+                                                          ((n) - 1) * 32 * BK * 2);        \
+    else                                                                                   \
+      fa[buf][(n) - MT] = *reinterpret_cast<const bf16x8*>(smem + (sa_) + fr_a[ss_] +      \
+                                                           ((n) - MT) * 32 * BK * 2);      \
+  } while (0)
+  // The 16 MFMAs of fragment buffer bm, with the next sub-step's eight fragment reads
+  // (sub-step rs into buffer br) spread one after every second MFMA, and, when
+  // dma_, load instructions q0 .. q0 + 3 of an operand chunk one after every fourth.
+  // Spreading the reads (rather than issuing all eight at once) measured 12 % faster:
+  // bursts of fragment reads and direct-to-LDS writes contend for the LDS.
+#define ENGRAM_GROUP(bm, br, rs, sa_, sb_, dma_, base_, off_, kt_, slot_, q0)              \
   do {                                                                                     \
     const uint16_t* src_ = (base_) + (kt_) * BK;                                           \
     const uint32_t dst_ = wave_dst + (uint32_t)((slot_) * SLOT_BYTES);                     \
-    _Pragma("unroll") for (int i = 0; i < MF; ++i) {                                       \
-      _Pragma("unroll") for (int j = 0; j < MT; ++j)                                       \
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j],      \
-                                                               acc[i][j], 0, 0, 0);        \
+    _Pragma("unroll") for (int k_ = 0; k_ < MF * MT; ++k_) {                               \
+      acc[k_ / MT][k_ % MT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                     \
+          fa[bm][k_ / MT], fb[bm][k_ % MT], acc[k_ / MT][k_ % MT], 0, 0, 0);               \
       __builtin_amdgcn_sched_barrier(0);                                                   \
-      dma16(src_ + off_[(q0) + i], dst_ + ((q0) + i) * 1024);                              \
-      __builtin_amdgcn_sched_barrier(0);                                                   \
+      if ((k_ % 2) == 0) {                                                                 \
+        ENGRAM_READ1(br, sa_, sb_, rs, k_ / 2);                                            \
+        __builtin_amdgcn_sched_barrier(0);                                                 \
+      }                                                                                    \
+      if ((dma_) && (k_ % MT) == MT - 1) {                                                 \
+        dma16(src_ + off_[(q0) + k_ / MT], dst_ + ((q0) + k_ / MT) * 1024);                \
+        __builtin_amdgcn_sched_barrier(0);                                                 \
+      }                                                                                    \
     }                                                                                      \
   } while (0)
   // Sum of e^2 over the k-steps kt with kt % n_ftiles == ftile, from the memory
@@ -369,59 +393,72 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
   wait_vm_lgkm0<G_INSTR>();
   lds_barrier();
 
-  // k-step kt: sub-step 3 of k-step kt-1 (fragments already in registers) covers
-  // the latency of this step's first fragment reads; each later sub-step's MFMAs
-  // cover the next one's reads.  MFMAS_0 .. MFMAS_3 run the four MFMA groups and
-  // issue this step's share of the operand stream; the barrier at the end publishes
-  // k-step kt+1 and frees k-step kt's slots.
-#define ENGRAM_KSTEP(kt, MFMAS_0, MFMAS_1, MFMAS_2, MFMAS_3)                               \
+  // k-step kt: the MFMAs of sub-step 3 of k-step kt-1 (fragments in registers) cover
+  // this step's first fragment reads, each later sub-step's MFMAs cover the next one's
+  // reads.  A load of the operand stream follows every fourth MFMA when dma_; the
+  // barrier at the end publishes k-step kt+1 and frees k-step kt's slots.
+#define ENGRAM_KSTEP(kt, dma_, b0_, o0_, k0_, s0_, b1_, o1_, k1_, s1_)                     \
   do {                                                                                     \
     const int sa_ = ((2 * (kt)) % NSLOT) * SLOT_BYTES;                                     \
     const int sb_ = ((2 * (kt) + 1) % NSLOT) * SLOT_BYTES;                                 \
-    ENGRAM_LOAD_FRAGS(0, sa_, sb_, 0);                                                     \
     __builtin_amdgcn_sched_barrier(0);                                                     \
-    MFMAS_0;                                                                               \
-    __builtin_amdgcn_sched_barrier(0);                                                     \
+    ENGRAM_GROUP(1, 0, 0, sa_, sb_, dma_, b0_, o0_, k0_, s0_, 0);                          \
     if (ee_now) ENGRAM_EE(1);                                                              \
     ee_now = ee_wave && ((kt) % a.n_ftiles) == ftile;                                      \
-    ENGRAM_LOAD_FRAGS(1, sa_, sb_, 1);                                                     \
-    __builtin_amdgcn_sched_barrier(0);                                                     \
-    MFMAS_1;                                                                               \
-    __builtin_amdgcn_sched_barrier(0);                                                     \
+    ENGRAM_GROUP(0, 1, 1, sa_, sb_, dma_, b0_, o0_, k0_, s0_, 4);                          \
     if (ee_now) ENGRAM_EE(0);                                                              \
-    ENGRAM_LOAD_FRAGS(0, sa_, sb_, 2);                                                     \
-    __builtin_amdgcn_sched_barrier(0);                                                     \
-    MFMAS_2;                                                                               \
-    __builtin_amdgcn_sched_barrier(0);                                                     \
+    ENGRAM_GROUP(1, 0, 2, sa_, sb_, dma_, b1_, o1_, k1_, s1_, 0);                          \
     if (ee_now) ENGRAM_EE(1);                                                              \
-    ENGRAM_LOAD_FRAGS(1, sa_, sb_, 3);                                                     \
-    __builtin_amdgcn_sched_barrier(0);                                                     \
-    MFMAS_3;                                                                               \
-    __builtin_amdgcn_sched_barrier(0);                                                     \
+    ENGRAM_GROUP(0, 1, 3, sa_, sb_, dma_, b1_, o1_, k1_, s1_, 4);                          \
     if (ee_now) ENGRAM_EE(0);                                                              \
+    __builtin_amdgcn_sched_barrier(0);                                                     \
     wait_vm_lgkm0<G_INSTR>();                                                              \
     lds_barrier();                                                                         \
   } while (0)
   int kt = 1;
   // chunks 2 kt + 3 (memory rows of k-step kt + 1) and 2 kt + 4 (weight rows of
   // k-step kt + 2) into the slots k-step kt - 1 freed
-  for (; kt + 2 < nk; ++kt) {
-    const int s3 = (2 * kt + 3) % NSLOT, s4 = (2 * kt + 4) % NSLOT;
-    ENGRAM_KSTEP(kt, ENGRAM_MFMAS_LOADS(1, Et0, off_b, kt + 1, s3, 0),
-                 ENGRAM_MFMAS_LOADS(0, Et0, off_b, kt + 1, s3, 4),
-                 ENGRAM_MFMAS_LOADS(1, W, off_a, kt + 2, s4, 0),
-                 ENGRAM_MFMAS_LOADS(0, W, off_a, kt + 2, s4, 4));
-  }
-  // the last k-steps: the stream ends with the h-tile quarters
+  for (; kt + 2 < nk; ++kt)
+    ENGRAM_KSTEP(kt, true, Et0, off_b, kt + 1, (2 * kt + 3) % NSLOT, W, off_a, kt + 2,
+                 (2 * kt + 4) % NSLOT);
+  // The last k-steps: the stream ends with the h-tile quarters, issued as a burst;
+  // each sub-step's fragments are read in one burst too (measured faster here than
+  // spreading them, behind the burst of h-tile loads).
   for (; kt < nk; ++kt) {
     issue_chunk(2 * kt + 3);
     issue_chunk(2 * kt + 4);
-    ENGRAM_KSTEP(kt, ENGRAM_MFMAS(1), ENGRAM_MFMAS(0), ENGRAM_MFMAS(1), ENGRAM_MFMAS(0));
+    const int sa = ((2 * kt) % NSLOT) * SLOT_BYTES;
+    const int sb = ((2 * kt + 1) % NSLOT) * SLOT_BYTES;
+    ENGRAM_LOAD_FRAGS(0, sa, sb, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    ENGRAM_MFMAS(1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (ee_now) ENGRAM_EE(1);
+    ee_now = ee_wave && (kt % a.n_ftiles) == ftile;
+    ENGRAM_LOAD_FRAGS(1, sa, sb, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    ENGRAM_MFMAS(0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (ee_now) ENGRAM_EE(0);
+    ENGRAM_LOAD_FRAGS(0, sa, sb, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    ENGRAM_MFMAS(1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (ee_now) ENGRAM_EE(1);
+    ENGRAM_LOAD_FRAGS(1, sa, sb, 3);
+    __builtin_amdgcn_sched_barrier(0);
+    ENGRAM_MFMAS(0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (ee_now) ENGRAM_EE(0);
+    wait_vm_lgkm0<G_INSTR>();
+    lds_barrier();
   }
   issue_chunk(2 * nk + 3);
   ENGRAM_MFMAS(1);
   if (ee_now) ENGRAM_EE(1);
 #undef ENGRAM_KSTEP
+#undef ENGRAM_GROUP
+#undef ENGRAM_READ1
 #undef ENGRAM_ISSUE
 #undef ENGRAM_EE
 #undef ENGRAM_LOAD_FRAGS
