@@ -37,8 +37,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_persistent_kernel_small_hbm_
 def parse():
     p = argparse.ArgumentParser(description=__doc__)
     p.add_argument("--gpus", type=int, default=int(os.environ.get("WORLD_SIZE", "1")))
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--steps", type=int, default=30)
+    # the GPU's clocks settle over the first ~10-20 steps of this workload
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", default="small")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time of the CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
