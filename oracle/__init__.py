@@ -50,8 +50,10 @@ def lib():
         L.oracle_hash.restype = None
         L.oracle_gather.argtypes = [P, i64, i32, P, i32, P]
         L.oracle_gather.restype = None
-        L.oracle_gate.argtypes = [P, i64, i32, i32, P, P, P, P, P, ctypes.c_double, i32, P, P]
+        L.oracle_gate.argtypes = [P, i64, i32, i32, P, P, P, P, P, ctypes.c_double, i32, P, P, P]
         L.oracle_gate.restype = ctypes.c_int
+        L.oracle_conv.argtypes = [P, i32, i64, i32, P, P, i32, i32, ctypes.c_double, i32, P, P]
+        L.oracle_conv.restype = None
         _lib = L
     return _lib
 
@@ -103,8 +105,9 @@ def gather(idx: np.ndarray, tables: Sequence[np.ndarray]):
 
 
 def gate(mem: np.ndarray, h: np.ndarray, wk: np.ndarray, wv: np.ndarray, gq: np.ndarray,
-         gk: np.ndarray, eps: float, dtype: int):
-    """One gating branch: (out [n_tok, d_model] float64, alpha [n_tok] float64).
+         gk: np.ndarray, eps: float, dtype: int, with_value: bool = False):
+    """One gating branch: (out [n_tok, d_model] float64, alpha [n_tok] float64), and the
+    gated value alpha * v [n_tok, d_model] float64 as a third element when with_value.
 
     Arrays hold float32 values (dtype F32) or raw bfloat16 bits as uint16 (dtype BF16).
     """
@@ -118,6 +121,28 @@ def gate(mem: np.ndarray, h: np.ndarray, wk: np.ndarray, wv: np.ndarray, gq: np.
         assert a.dtype == want, a.dtype
     out = np.empty((n_tok, d_model), dtype=np.float64)
     alpha = np.empty(n_tok, dtype=np.float64)
+    value = np.empty((n_tok, d_model), dtype=np.float64) if with_value else None
     lib().oracle_gate(_p(mem), n_tok, d_mem, d_model, _p(h), _p(wk), _p(wv), _p(gq), _p(gk),
-                      float(eps), dtype, _p(out), _p(alpha))
-    return out, alpha
+                      float(eps), dtype, _p(out), _p(alpha), _p(value) if with_value else None)
+    return (out, alpha, value) if with_value else (out, alpha)
+
+
+def conv(value: np.ndarray, batch: int, seq: int, w: np.ndarray, gamma: np.ndarray, dil: int,
+         eps: float, dtype: int, base: np.ndarray):
+    """Eq. (5) convolution: base + SiLU(Conv1D(RMSNorm(value))) as float64 [batch*seq, d_model].
+
+    value, base: float64 [batch*seq, d_model] (tokens b*seq + t); w: [d_model, taps] and
+    gamma: [d_model] as float32 (F32) or bfloat16 bits (BF16)."""
+    value = np.ascontiguousarray(value, dtype=np.float64)
+    base = np.ascontiguousarray(base, dtype=np.float64)
+    w, gamma = np.ascontiguousarray(w), np.ascontiguousarray(gamma)
+    n_tok, d_model = value.shape
+    taps = w.shape[1]
+    assert n_tok == batch * seq and base.shape == value.shape and w.shape == (d_model, taps)
+    assert gamma.shape == (d_model,)
+    want = np.float32 if dtype == F32 else np.uint16
+    assert w.dtype == want and gamma.dtype == want
+    out = np.empty_like(value)
+    lib().oracle_conv(_p(value), batch, seq, d_model, _p(w), _p(gamma), taps, dil, float(eps), dtype,
+                      _p(base), _p(out))
+    return out

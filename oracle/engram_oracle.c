@@ -129,11 +129,12 @@ void oracle_gather(const int32_t* idx, int64_t n_tok, int32_t n_tables, const vo
  *   out   = h_t + alpha * v
  * mem: [n_tok][d_mem]; h, out: [n_tok][d_model]; W_K, W_V: [d_model][d_mem]
  * row-major (output x input); gq: [d_model]; gk: [d_mem]; all of `dtype`.
- * out and alpha are double.  Returns 0.
+ * out and alpha are double; `value` (double [n_tok][d_model], or NULL) receives the
+ * gated value alpha * v that the convolution of Eq. (5) consumes.  Returns 0.
  */
 int oracle_gate(const void* mem, int64_t n_tok, int32_t d_mem, int32_t d_model, const void* h,
                 const void* wk, const void* wv, const void* gq, const void* gk, double eps,
-                int32_t dtype, double* out, double* alpha) {
+                int32_t dtype, double* out, double* alpha, double* value) {
   for (int64_t t = 0; t < n_tok; ++t) {
     /* RMSNorm of the memory vector and of the hidden state */
     double ss_e = 0.0;
@@ -171,7 +172,46 @@ int oracle_gate(const void* mem, int64_t n_tok, int32_t d_mem, int32_t d_model, 
         v += load_elem(wv, (int64_t)i * d_mem + j, dtype) * load_elem(mem, t * d_mem + j, dtype);
       }
       out[t * d_model + i] = load_elem(h, t * d_model + i, dtype) + a * v;
+      if (value != NULL) value[t * d_model + i] = a * v;
     }
   }
   return 0;
+}
+
+/*
+ * Short depthwise causal convolution over the gated values (section 2.3, Eq. (5)).
+ * With V~ the sequence of gated values of one sequence (token t, channel c):
+ *   n_t     = RMSNorm_{gamma}(V~_t)            = V~_t / sqrt(mean_c(V~_t^2) + eps) * gamma
+ *   z_{t,c} = sum_{j=0}^{taps-1} w[c][j] * n_{t - j*dil, c}    (zero before the sequence start)
+ *   Y_t     = SiLU(z_t) + V~_t,    SiLU(x) = x / (1 + exp(-x))
+ * and the layer output is h_t + Y_t.  `base` holds h_t + V~_t (what the gate writes), so
+ *   out = base + SiLU(z).
+ * Tap j reads the token j*dil positions back (the kernel covers lags 0, dil, ..,
+ * (taps-1)*dil).  value, base, out: double [batch*seq][d_model] (token b*seq + t);
+ * w: [d_model][taps] and gamma: [d_model] of `dtype`.
+ */
+void oracle_conv(const double* value, int32_t batch, int64_t seq, int32_t d_model, const void* w,
+                 const void* gamma, int32_t taps, int32_t dil, double eps, int32_t dtype,
+                 const double* base, double* out) {
+  const int64_t n_tok = (int64_t)batch * seq;
+  for (int64_t t = 0; t < n_tok; ++t) {
+    for (int32_t c = 0; c < d_model; ++c) out[t * d_model + c] = base[t * d_model + c];
+  }
+  for (int32_t b = 0; b < batch; ++b) {
+    for (int64_t t = 0; t < seq; ++t) {
+      for (int32_t c = 0; c < d_model; ++c) {
+        double z = 0.0;
+        for (int32_t j = 0; j < taps; ++j) {
+          const int64_t ts = t - (int64_t)j * dil;
+          if (ts < 0) continue;
+          const double* row = value + ((int64_t)b * seq + ts) * d_model;
+          double ss = 0.0;
+          for (int32_t k = 0; k < d_model; ++k) ss += row[k] * row[k];
+          const double n = row[c] / sqrt(ss / d_model + eps) * load_elem(gamma, c, dtype);
+          z += load_elem(w, (int64_t)c * taps + j, dtype) * n;
+        }
+        out[((int64_t)b * seq + t) * d_model + c] += z / (1.0 + exp(-z));
+      }
+    }
+  }
 }

@@ -365,3 +365,87 @@ def test_tiny_pipeline_end_to_end():
     assert np.all((alpha > 0) & (alpha < 1)) and np.isfinite(out).all()
     # tables ~ N(0, 0.02): the update is small next to the residual
     assert np.abs(out - h).max() < 0.2
+
+
+# ---------------------------------------------------------------------------
+# Short depthwise causal convolution (section 2.3, Eq. (5))
+
+def _silu_lib(x):
+    from scipy.special import expit  # the logistic function, as a library routine
+    return np.asarray(x, dtype=np.float64) * expit(x)
+
+
+def test_conv_zero_weights_leave_the_base():
+    """SiLU(0) = 0: with all kernel weights zero the output is the base, bit for bit."""
+    rng = np.random.default_rng(31)
+    b, s, d = 2, 11, 6
+    v = rng.standard_normal((b * s, d))
+    base = rng.standard_normal((b * s, d))
+    w = np.zeros((d, 4), dtype=np.float32)
+    g = rng.standard_normal(d).astype(np.float32)
+    out = oracle.conv(v, b, s, w, g, 3, 1e-6, oracle.F32, base)
+    assert np.array_equal(out, base)
+
+
+def test_conv_delta_reaches_exactly_the_dilated_taps():
+    """One non-zero token (a constant row, whose RMSNorm is gamma) in sequence 0: tap j
+    of the kernel shows up j * dil positions later and nowhere else; sequence 1 and
+    earlier positions stay zero.  Values are SiLU of the tap weights, SiLU computed
+    from scipy's logistic function."""
+    b, s, d, dil, t0 = 2, 16, 5, 3, 2
+    v = np.zeros((b * s, d))
+    v[t0, :] = 0.37
+    taps = np.array([1.0, -1.0, 2.0, 0.5], dtype=np.float32)
+    w = np.tile(taps, (d, 1))
+    g = np.ones(d, dtype=np.float32)
+    out = oracle.conv(v, b, s, w, g, dil, 1e-12, oracle.F32, np.zeros_like(v))
+    expect = np.zeros_like(v)
+    for j in range(4):
+        expect[t0 + j * dil, :] = _silu_lib(np.float64(taps[j]))
+    assert np.allclose(out, expect, rtol=1e-10, atol=1e-12)
+    assert np.count_nonzero(out[s:]) == 0 and np.count_nonzero(out[:t0]) == 0
+
+
+def test_conv_is_causal_per_sequence_with_dilated_reach():
+    """Changing the gated value of one token changes the outputs of exactly the
+    tokens t, t + dil, t + 2 dil, t + 3 dil of the same sequence."""
+    rng = np.random.default_rng(32)
+    b, s, d, dil = 3, 20, 7, 3
+    v = rng.standard_normal((b * s, d))
+    w = rng.standard_normal((d, 4)).astype(np.float32)
+    g = (1 + 0.1 * rng.standard_normal(d)).astype(np.float32)
+    base = np.zeros_like(v)
+    o1 = oracle.conv(v, b, s, w, g, dil, 1e-6, oracle.F32, base)
+    v2 = v.copy()
+    tb, tt = 1, 5
+    v2[tb * s + tt] += 1.0
+    o2 = oracle.conv(v2, b, s, w, g, dil, 1e-6, oracle.F32, base)
+    changed = np.nonzero(np.any(o1 != o2, axis=1))[0]
+    assert list(changed) == [tb * s + tt + j * dil for j in range(4)]
+
+
+def test_conv_rmsnorm_makes_it_scale_invariant():
+    rng = np.random.default_rng(33)
+    b, s, d = 1, 13, 8
+    v = rng.standard_normal((b * s, d))
+    w = rng.standard_normal((d, 4)).astype(np.float32)
+    g = rng.standard_normal(d).astype(np.float32)
+    base = rng.standard_normal((b * s, d))
+    o1 = oracle.conv(v, b, s, w, g, 3, 0.0, oracle.F32, base)
+    o2 = oracle.conv(v * 7.5, b, s, w, g, 3, 0.0, oracle.F32, base)
+    assert np.allclose(o1, o2, rtol=1e-12, atol=1e-12)
+
+
+def test_gate_value_output_is_the_gated_value():
+    """The gate's optional value output is alpha * v = out - h."""
+    rng = np.random.default_rng(34)
+    n, dm, d = 5, 16, 12
+    e = rng.standard_normal((n, dm)).astype(np.float32)
+    h = rng.standard_normal((n, d)).astype(np.float32)
+    wk = rng.standard_normal((d, dm)).astype(np.float32)
+    wv = rng.standard_normal((d, dm)).astype(np.float32)
+    ones_q, ones_k = np.ones(d, dtype=np.float32), np.ones(dm, dtype=np.float32)
+    out, alpha, value = oracle.gate(e, h, wk, wv, ones_q, ones_k, 1e-6, oracle.F32, with_value=True)
+    assert np.allclose(value, out - h.astype(np.float64), rtol=1e-12, atol=1e-12)
+    v = e.astype(np.float64) @ wv.astype(np.float64).T
+    assert np.allclose(value, alpha[:, None] * v, rtol=1e-12, atol=1e-12)
