@@ -43,6 +43,8 @@ def parse():
     p.add_argument("--config", default="small")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time of the CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-conv", action="store_true",
+                   help="skip the separate measurement of the short convolution (Eq. 5)")
     p.add_argument("--flush-mb", type=int, default=512, help="cache-flush buffer rewritten between steps (0: off)")
     p.add_argument("--offload-rows", type=int, default=0,
                    help="offload config: rows per table (default: 100B parameters, scaled to 60%% of free host RAM)")
@@ -208,7 +210,7 @@ def run_offload(args):
 
         def gate(s, buf):
             chk(L.engram_gate_forward(stg[buf].data_ptr(), B, cfg.d_mem, cfg.d_model, 1, h_a[s], wk_a, wv_a, gq_a,
-                                      gk_a, cfg.eps, eg.BF16, out_a, None, ms))
+                                      gk_a, cfg.eps, eg.BF16, out_a, None, None, ms))
 
         def pipeline(mode):
             ready = [torch.cuda.Event() for _ in range(2)]
@@ -297,6 +299,55 @@ def run_offload(args):
         torch.cuda.synchronize()
         for a in haddr:
             eg.host_free(a)
+
+
+def measure_conv(args, cfg, bufs, h, layer, outs, flush):
+    """The short convolution of Eq. (5), measured beside the step (it is not part of the
+    hash+gather+gate metric): the gate writing the gated values as well, then
+    engram_conv_forward on every branch, each bracketed by events, with the cache flush
+    between them."""
+    import torch
+    import synth
+    import hashed_gram_embedding_hash_amd as eg
+    dev = outs[0].device
+    dil = synth.conv_dilation(cfg)
+    vals = [torch.empty_like(x) for x in outs]
+    params = [synth.conv_params(cfg, m, device=dev) for m in range(cfg.n_branch)]
+
+    def gate(with_values):
+        eg.engram_gate_forward(bufs["mem"], h, layer.wk, layer.wv, layer.gq, layer.gk, cfg.eps, out=outs,
+                               value_out=vals if with_values else None)
+
+    def conv():
+        for m in range(cfg.n_branch):
+            eg.engram_conv_forward(vals[m], cfg.batch, cfg.seq, params[m][0], params[m][1], dil, outs[m], cfg.eps)
+
+    for _ in range(3):
+        gate(True)
+        conv()
+    torch.cuda.synchronize()
+    reps = max(5, args.steps)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(reps)]
+    for i in range(reps):
+        for k, fn in enumerate((lambda: gate(False), lambda: gate(True), conv)):
+            if flush is not None:
+                flush.fill_(float(i + k))
+            ev[i][2 * k].record()
+            fn()
+            ev[i][2 * k + 1].record()
+    torch.cuda.synchronize()
+    ms = [sum(ev[i][2 * k].elapsed_time(ev[i][2 * k + 1]) for i in range(reps)) / reps for k in range(3)]
+    es = 2 if cfg.dtype == "bf16" else 4
+    unit = cfg.tokens * cfg.d_model * es * cfg.n_branch     # one [tokens, d_model] array per branch
+    conv_bytes = 3 * unit          # read the gated values once, read and write out
+    return {"kernel": "engram_conv_forward: conv_rms_kernel + conv_apply_kernel",
+            "taps": synth.CONV_TAPS, "dilation": dil, "branches": cfg.n_branch, "reps": reps,
+            "ms": round(ms[2], 5), "bytes_algorithmic": conv_bytes,
+            "GB/s": round(conv_bytes / (ms[2] * 1e-3) / 1e9, 1),
+            "hbm_frac": round(conv_bytes / (ms[2] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "gate_ms": round(ms[0], 5), "gate_with_values_ms": round(ms[1], 5),
+            "values_write_GB/s": round(unit / max(1e-9, (ms[1] - ms[0]) * 1e-3) / 1e9, 1),
+            "gate_with_values_plus_conv_ms": round(ms[1] + ms[2], 5)}
 
 
 def cpu_baseline(cfg, target_s):
@@ -456,6 +507,9 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
     }
+    if not args.no_conv:
+        print("[bench] short convolution", file=sys.stderr, flush=True)
+        result["conv"] = measure_conv(args, cfg, bufs, h, layer, outs, flush)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)

@@ -12,6 +12,8 @@ The functions carry the C names:
 * ``engram_gather``    -- table lookup and concatenation (Eq. 1-2);
 * ``engram_gate_forward`` -- context-aware gating and residual update
   (section 2.3, Eq. 3-4; section 2.4, Eq. 6 for several branches);
+* ``engram_conv_forward`` -- the short depthwise causal convolution over the
+  gated values (section 2.3, Eq. 5);
 * ``engram_prefetch_host`` -- the same gather from pinned host-memory tables
   over PCIe (section 2.5, Figure 2(b); section 6.4).
 
@@ -32,13 +34,16 @@ BF16 = 1
 MAX_TABLES = 32
 MAX_ORDER = 4
 MAX_BRANCHES = 8
+CONV_MAX_TAPS = 8
+CONV_MAX_DILATION = 16
 
 _STATUS = {0: "ENGRAM_OK", 1: "ENGRAM_ERR_INVALID_ARG", 2: "ENGRAM_ERR_UNSUPPORTED", 3: "ENGRAM_ERR_HIP"}
 
 # names exported by include/engram.h
 EXPORTS = (
     "engram_last_error", "engram_version", "engram_compress", "engram_hash", "engram_gather",
-    "engram_gate_forward", "engram_prefetch_host", "engram_host_alloc", "engram_host_free",
+    "engram_gate_forward", "engram_conv_forward", "engram_prefetch_host", "engram_host_alloc",
+    "engram_host_free",
 )
 
 
@@ -71,12 +76,13 @@ def lib() -> ctypes.CDLL:
         L.engram_hash.argtypes = [P, i32, i64, i64, i64, P, i32, i32, P, P, i32, P, P]
         L.engram_gather.argtypes = [P, i64, i32, P, P, i32, i32, P, P, P]
         L.engram_gate_forward.argtypes = [P, i64, i32, i32, i32, P, P, P, P, P, ctypes.c_float, i32,
-                                          P, P, P]
+                                          P, P, P, P]
+        L.engram_conv_forward.argtypes = [P, i32, i64, i32, P, P, i32, i32, ctypes.c_float, i32, P, P]
         L.engram_prefetch_host.argtypes = [P, i64, i32, P, P, i32, i32, P, P, P]
         L.engram_host_alloc.argtypes = [ctypes.c_size_t, ctypes.POINTER(ctypes.c_void_p)]
         L.engram_host_free.argtypes = [P]
         for f in ("engram_compress", "engram_hash", "engram_gather", "engram_gate_forward",
-                  "engram_prefetch_host", "engram_host_alloc", "engram_host_free"):
+                  "engram_conv_forward", "engram_prefetch_host", "engram_host_alloc", "engram_host_free"):
             getattr(L, f).restype = st
         _lib = L
     return _lib
@@ -187,11 +193,14 @@ def engram_gather(idx, tables: Sequence, out=None, err_count=None, stream=None):
 
 
 def engram_gate_forward(mem, h: Sequence, wk: Sequence, wv: Sequence, gq: Sequence, gk: Sequence,
-                        eps: float = 1e-6, out: Optional[Sequence] = None, gate_out=None, stream=None):
+                        eps: float = 1e-6, out: Optional[Sequence] = None, gate_out=None,
+                        value_out: Optional[Sequence] = None, stream=None):
     """out[m] = h[m] + sigmoid(RMSNorm(h[m]) . W_K[m] RMSNorm(mem) / sqrt(d)) * W_V[m] mem.
 
     Lists hold one tensor per branch; ``out`` defaults to new tensors (pass ``h``
-    for in-place).  ``gate_out``: optional float32 [n_branch, n_tok] for alpha."""
+    for in-place).  ``gate_out``: optional float32 [n_branch, n_tok] for alpha.
+    ``value_out``: optional list (entries may be None) of [n_tok, d_model] tensors
+    receiving the gated values alpha * v."""
     import torch
     n_tok, d_mem = mem.shape
     nb = len(h)
@@ -202,19 +211,44 @@ def engram_gate_forward(mem, h: Sequence, wk: Sequence, wv: Sequence, gq: Sequen
         out = [torch.empty_like(x) for x in h]
     if not (len(wk) == len(wv) == len(gq) == len(gk) == len(out) == nb):
         raise ValueError("one h/wk/wv/gq/gk/out per branch")
+    if value_out is not None and len(value_out) != nb:
+        raise ValueError("one value_out entry per branch")
     for name, seq in (("h", h), ("wk", wk), ("wv", wv), ("gq", gq), ("gk", gk), ("out", out)):
         for x in seq:
             _dev(x, name, dt)
-    for x in list(h) + list(out):
+    vals = [x for x in (value_out or []) if x is not None]
+    for x in vals:
+        _dev(x, "value_out", dt)
+    for x in list(h) + list(out) + vals:
         if tuple(x.shape) != (n_tok, d_model):
-            raise ValueError("h/out must be [n_tok, d_model]")
+            raise ValueError("h/out/value_out must be [n_tok, d_model]")
     for x in list(wk) + list(wv):
         if tuple(x.shape) != (d_model, d_mem):
             raise ValueError("weights must be [d_model, d_mem]")
     arr = lambda seq: _ptr_array([x.data_ptr() for x in seq])
+    varr = None if value_out is None else _ptr_array([0 if x is None else x.data_ptr() for x in value_out])
     _check(lib().engram_gate_forward(mem.data_ptr(), n_tok, d_mem, d_model, nb, arr(h), arr(wk), arr(wv),
                                      arr(gq), arr(gk), float(eps), _edtype(mem), arr(out),
-                                     _opt(gate_out, "gate_out", torch.float32), _stream(stream)))
+                                     _opt(gate_out, "gate_out", torch.float32), varr, _stream(stream)))
+    return out
+
+
+def engram_conv_forward(value, batch: int, seq: int, w, gamma, dilation: int, out, eps: float = 1e-6,
+                        stream=None):
+    """out += SiLU(Conv1D(RMSNorm_gamma(value))) per sequence, in place, and returns ``out``.
+
+    value, out: [batch * seq, d_model] (token t of sequence b is row b * seq + t);
+    w: [d_model, taps] depthwise kernel, tap j looking j * dilation tokens back;
+    gamma: [d_model]."""
+    n_tok, d_model = value.shape
+    dt = value.dtype
+    if n_tok != batch * seq or tuple(out.shape) != (n_tok, d_model):
+        raise ValueError("value and out must be [batch * seq, d_model]")
+    if w.dim() != 2 or w.shape[0] != d_model or tuple(gamma.shape) != (d_model,):
+        raise ValueError("w must be [d_model, taps] and gamma [d_model]")
+    _check(lib().engram_conv_forward(_dev(value, "value", dt), batch, seq, d_model, _dev(w, "w", dt),
+                                     _dev(gamma, "gamma", dt), w.shape[1], dilation, float(eps), _edtype(value),
+                                     _dev(out, "out", dt), _stream(stream)))
     return out
 
 

@@ -88,14 +88,15 @@ const void* mapped_host_pointer(const void* p) {
   return db + ((const char*)p - hb);
 }
 
-// The bf16 gate's scratch (folded key weights, partial sums, gates, work-queue
-// counters): one grow-only buffer per device, reused by every call.  A call on the
-// stream that used it last needs nothing more (stream order); a call on another
-// stream first waits for an event recorded after the previous use.  Growing frees the
-// old buffer in stream order behind that wait.  The lock is held from acquiring the
-// buffer until the launches and the event record are enqueued, so concurrent host
-// threads take turns.  Buffers live until the process ends.
-struct GateScratch {
+// The library scratch (the bf16 gate's folded key weights, partial sums, gates and
+// work-queue counters; the convolution's per-token inverse RMS): one grow-only buffer
+// per device, reused by every call.  A call on the stream that used it last needs
+// nothing more (stream order); a call on another stream first waits for an event
+// recorded after the previous use.  Growing frees the old buffer in stream order behind
+// that wait.  The lock is held from acquiring the buffer until the launches and the
+// event record are enqueued, so concurrent host threads take turns.  Buffers live until
+// the process ends.
+struct Scratch {
   void* ptr = nullptr;
   size_t bytes = 0;
   hipStream_t last = nullptr;
@@ -104,7 +105,55 @@ struct GateScratch {
 };
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
-GateScratch g_scratch[kMaxDevices];
+Scratch g_scratch[kMaxDevices];
+
+// Runs launch(ptr) with ptr pointing at >= `bytes` of the current device's scratch.
+template <class Launch>
+engram_status with_scratch(const char* fn, size_t bytes, hipStream_t stream, Launch&& launch) {
+  auto hip_fail = [fn](hipError_t e, const char* what) {
+    return fail(ENGRAM_ERR_HIP, "%s: %s: %s (%d)", fn, what, hipGetErrorString(e), (int)e);
+  };
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(ENGRAM_ERR_UNSUPPORTED, "%s: device %d", fn, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  Scratch& g = g_scratch[dev];
+  if (g.done == nullptr) {
+    e = hipEventCreateWithFlags(&g.done, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      g.done = nullptr;
+      return hip_fail(e, "hipEventCreateWithFlags(scratch)");
+    }
+  }
+  if (g.used && g.last != stream) {
+    e = hipStreamWaitEvent(stream, g.done, 0);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent(scratch)");
+  }
+  if (g.bytes < bytes) {
+    if (g.ptr != nullptr) {
+      e = hipFreeAsync(g.ptr, stream);
+      g.ptr = nullptr;
+      g.bytes = 0;
+      if (e != hipSuccess) return hip_fail(e, "hipFreeAsync(scratch)");
+    }
+    const size_t grow = bytes + bytes / 4;  // slack for slightly larger later calls
+    e = hipMallocAsync(&g.ptr, grow, stream);
+    if (e != hipSuccess) {
+      g.ptr = nullptr;
+      return hip_fail(e, "hipMallocAsync(scratch)");
+    }
+    g.bytes = grow;
+  }
+  launch(g.ptr);
+  const engram_status st = check_launch(fn);
+  e = hipEventRecord(g.done, stream);
+  g.last = stream;
+  g.used = true;
+  if (st != ENGRAM_OK) return st;
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord(scratch)");
+  return ENGRAM_OK;
+}
 
 }  // namespace
 
@@ -235,7 +284,8 @@ engram_status engram_gate_forward(const void* mem, int64_t n_tok, int32_t d_mem,
                                   int32_t n_branch, const void* const* h, const void* const* wk,
                                   const void* const* wv, const void* const* gq,
                                   const void* const* gk, float eps, engram_dtype dtype,
-                                  void* const* out, float* gate_out, hipStream_t stream) {
+                                  void* const* out, float* gate_out, void* const* value_out,
+                                  hipStream_t stream) {
   const char* fn = "engram_gate_forward";
   if (n_tok < 0 || d_mem <= 0 || d_model <= 0)
     return fail(ENGRAM_ERR_INVALID_ARG, "%s: bad sizes n_tok=%lld d_mem=%d d_model=%d", fn,
@@ -270,6 +320,9 @@ engram_status engram_gate_forward(const void* mem, int64_t n_tok, int32_t d_mem,
     a.gq[m] = gq[m];
     a.gk[m] = gk[m];
     a.out[m] = out[m];
+    a.vout[m] = value_out != nullptr ? value_out[m] : nullptr;
+    if (n_tok > 0 && a.vout[m] != nullptr && !aligned(a.vout[m], al))
+      return fail(ENGRAM_ERR_INVALID_ARG, "%s: branch %d: misaligned value_out", fn, m);
   }
   if (n_tok == 0) return ENGRAM_OK;
   a.mem = mem;
@@ -289,47 +342,59 @@ engram_status engram_gate_forward(const void* mem, int64_t n_tok, int32_t d_mem,
   }
 
   const size_t bytes = gate_bf16_scratch_bytes(a);
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e, "engram_gate_forward: hipGetDevice");
-  if (dev < 0 || dev >= kMaxDevices) return fail(ENGRAM_ERR_UNSUPPORTED, "%s: device %d", fn, dev);
-  std::lock_guard<std::mutex> lock(g_scratch_mu);
-  GateScratch& g = g_scratch[dev];
-  if (g.done == nullptr) {
-    e = hipEventCreateWithFlags(&g.done, hipEventDisableTiming);
-    if (e != hipSuccess) {
-      g.done = nullptr;
-      return hip_fail(e, "engram_gate_forward: hipEventCreateWithFlags");
-    }
-  }
-  if (g.used && g.last != stream) {
-    e = hipStreamWaitEvent(stream, g.done, 0);
-    if (e != hipSuccess) return hip_fail(e, "engram_gate_forward: hipStreamWaitEvent");
-  }
-  if (g.bytes < bytes) {
-    if (g.ptr != nullptr) {
-      e = hipFreeAsync(g.ptr, stream);
-      g.ptr = nullptr;
-      g.bytes = 0;
-      if (e != hipSuccess) return hip_fail(e, "engram_gate_forward: hipFreeAsync(scratch)");
-    }
-    const size_t grow = bytes + bytes / 4;  // slack for slightly larger later calls
-    e = hipMallocAsync(&g.ptr, grow, stream);
-    if (e != hipSuccess) {
-      g.ptr = nullptr;
-      return hip_fail(e, "engram_gate_forward: hipMallocAsync(scratch)");
-    }
-    g.bytes = grow;
-  }
-  a.part_dot = (float*)g.ptr;
-  launch_gate_bf16(a, stream);
-  const engram_status st = check_launch(fn);
-  e = hipEventRecord(g.done, stream);
-  g.last = stream;
-  g.used = true;
-  if (st != ENGRAM_OK) return st;
-  if (e != hipSuccess) return hip_fail(e, "engram_gate_forward: hipEventRecord");
-  return ENGRAM_OK;
+  return with_scratch(fn, bytes, stream, [&](void* p) {
+    a.part_dot = (float*)p;
+    launch_gate_bf16(a, stream);
+  });
+}
+
+engram_status engram_conv_forward(const void* value, int32_t batch, int64_t seq, int32_t d_model,
+                                  const void* w, const void* gamma, int32_t taps, int32_t dilation,
+                                  float eps, engram_dtype dtype, void* out, hipStream_t stream) {
+  const char* fn = "engram_conv_forward";
+  if (batch < 0 || seq < 0 || d_model <= 0)
+    return fail(ENGRAM_ERR_INVALID_ARG, "%s: bad sizes batch=%d seq=%lld d_model=%d", fn, batch,
+                (long long)seq, d_model);
+  if (!valid_dtype(dtype)) return fail(ENGRAM_ERR_INVALID_ARG, "%s: unknown dtype", fn);
+  if (!(eps >= 0.f)) return fail(ENGRAM_ERR_INVALID_ARG, "%s: eps must be >= 0", fn);
+  if (taps < 1 || taps > ENGRAM_CONV_MAX_TAPS)
+    return fail(ENGRAM_ERR_UNSUPPORTED, "%s: taps %d not in [1, %d]", fn, taps, ENGRAM_CONV_MAX_TAPS);
+  if (dilation < 1 || dilation > ENGRAM_CONV_MAX_DILATION)
+    return fail(ENGRAM_ERR_UNSUPPORTED, "%s: dilation %d not in [1, %d]", fn, dilation,
+                ENGRAM_CONV_MAX_DILATION);
+  if (((int64_t)d_model * (int64_t)dtype_size(dtype)) % 16 != 0)
+    return fail(ENGRAM_ERR_UNSUPPORTED, "%s: d_model * element size must be a multiple of 16 (d_model %d)",
+                fn, d_model);
+  if (w == nullptr || gamma == nullptr || !aligned(w, 16) || !aligned(gamma, 16))
+    return fail(ENGRAM_ERR_INVALID_ARG, "%s: null or misaligned w/gamma", fn);
+  if (batch == 0 || seq == 0) return ENGRAM_OK;
+  if (value == nullptr || out == nullptr || !aligned(value, 16) || !aligned(out, 16))
+    return fail(ENGRAM_ERR_INVALID_ARG, "%s: null or misaligned value/out", fn);
+  const int64_t rows = (int64_t)batch * seq;
+  const size_t row_bytes = (size_t)d_model * dtype_size(dtype);
+  const char *v0 = (const char*)value, *o0 = (const char*)out;
+  if (v0 < o0 + rows * row_bytes && o0 < v0 + rows * row_bytes)
+    return fail(ENGRAM_ERR_INVALID_ARG, "%s: out overlaps value", fn);
+  // workgroups of the apply kernel: 64-token blocks x 512-byte column slabs per sequence
+  const int64_t slabs = ((int64_t)row_bytes / 16 + 31) / 32;
+  if (rows / 4 + 1 >= (1ll << 31) || (int64_t)batch * ((seq + 63) / 64) * slabs >= (1ll << 31))
+    return fail(ENGRAM_ERR_UNSUPPORTED, "%s: too many tokens for one launch", fn);
+  ConvArgs a;
+  memset(&a, 0, sizeof a);
+  a.value = value;
+  a.out = out;
+  a.w = w;
+  a.gamma = gamma;
+  a.seq = seq;
+  a.batch = batch;
+  a.d_model = d_model;
+  a.taps = taps;
+  a.dil = dilation;
+  a.eps = eps;
+  return with_scratch(fn, conv_scratch_bytes(a), stream, [&](void* p) {
+    a.inv = (float*)p;
+    launch_conv(a, dtype == ENGRAM_BF16, stream);
+  });
 }
 
 engram_status engram_host_alloc(size_t bytes, void** ptr) {

@@ -55,6 +55,7 @@ struct GateArgs {
   const void* gq[ENGRAM_MAX_BRANCHES];
   const void* gk[ENGRAM_MAX_BRANCHES];
   void* out[ENGRAM_MAX_BRANCHES];
+  void* vout[ENGRAM_MAX_BRANCHES];  // gated values alpha * v, or null per branch
   float* gate_out;   // [n_branch][n_tok] or null
   float* part_dot;   // scratch: [n_branch][n_ftiles][n_tok]
   float* part_hh;    // scratch: [n_branch][n_ftiles][n_tok]
@@ -70,5 +71,20 @@ struct GateArgs {
 size_t gate_bf16_scratch_bytes(GateArgs& a);
 void launch_gate_bf16(const GateArgs& a, hipStream_t s);
 void launch_gate_f32(const GateArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- short convolution
+struct ConvArgs {
+  const void* value;  // [batch * seq][d_model] gated values
+  void* out;          // same shape, updated in place
+  const void* w;      // [d_model][taps]
+  const void* gamma;  // [d_model]
+  float* inv;         // scratch [batch * seq]: 1 / rms of each value row
+  int64_t seq;
+  int32_t batch, d_model, taps, dil;
+  float eps;
+};
+// scratch bytes the convolution needs (its inv array); a.inv must point at that many
+size_t conv_scratch_bytes(const ConvArgs& a);
+void launch_conv(const ConvArgs& a, bool bf16, hipStream_t s);
 
 }  // namespace engram

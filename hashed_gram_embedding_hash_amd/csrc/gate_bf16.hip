@@ -629,26 +629,51 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
     lds_barrier();
     // Stream the tile out: 16-B chunk p = 256 i + tid is token tl = p / 32, physical
     // chunk p % 32; eight LDS reads are issued ahead of their eight stores.
-    uint16_t* Ot0 = (uint16_t*)a.out[m] + t0 * d_model;
     const bool full = t0 + BT <= n_tok && f0 + BF <= d_model;
+    auto stream_out = [&](uint16_t* dst) {
+      uint16_t* Ot0 = dst + t0 * d_model;
 #pragma unroll
-    for (int i0 = 0; i0 < H_LOADS; i0 += 8) {
-      u32x4 ov[8];
+      for (int i0 = 0; i0 < H_LOADS; i0 += 8) {
+        u32x4 ov[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int p = (i0 + u) * NTHR + etid;
-        const int tl = p / H_CH;
-        ov[u] = *reinterpret_cast<const u32x4*>(smem + ENGRAM_QSLOT(tl >> 6) + (tl & 63) * (BF * 2) +
-                                                (p % H_CH) * 16);
+        for (int u = 0; u < 8; ++u) {
+          const int p = (i0 + u) * NTHR + etid;
+          const int tl = p / H_CH;
+          ov[u] = *reinterpret_cast<const u32x4*>(smem + ENGRAM_QSLOT(tl >> 6) + (tl & 63) * (BF * 2) +
+                                                  (p % H_CH) * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int p = (i0 + u) * NTHR + etid;
+          const int tl = p / H_CH;
+          const int f = f0 + ((p % H_CH) ^ (tl & 31)) * 8;
+          if (full || (t0 + tl < n_tok && f < d_model))
+            *reinterpret_cast<u32x4*>(Ot0 + (uint32_t)tl * (uint32_t)d_model + f) = ov[u];
+        }
       }
+    };
+    stream_out((uint16_t*)a.out[m]);
+    if (a.vout[m] != nullptr) {
+      // the gated values alpha * v, staged through the same LDS tile
+      lds_barrier();
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int p = (i0 + u) * NTHR + etid;
-        const int tl = p / H_CH;
-        const int f = f0 + ((p % H_CH) ^ (tl & 31)) * 8;
-        if (full || (t0 + tl < n_tok && f < d_model))
-          *reinterpret_cast<u32x4*>(Ot0 + (uint32_t)tl * (uint32_t)d_model + f) = ov[u];
+      for (int j = 0; j < MT; ++j) {
+        const int tl = ewt * WT + j * 32 + (elane & 31);
+        const float alpha = s_alpha[tl];
+#pragma unroll
+        for (int i = 0; i < MF; ++i) {
+#pragma unroll
+          for (int gp = 0; gp < 2; ++gp) {
+            u32x4 ov;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              ov[q] = pack_bf16(alpha * acc[i][j][gp * 8 + 2 * q], alpha * acc[i][j][gp * 8 + 2 * q + 1]);
+            *reinterpret_cast<u32x4*>(smem + ENGRAM_HOFF(tl, (ewf * WF + i * 32 + gp * 16 + hsel) >> 3)) = ov;
+          }
+        }
       }
+      lds_barrier();
+      stream_out((uint16_t*)a.vout[m]);
     }
   }
 #undef ENGRAM_HOFF

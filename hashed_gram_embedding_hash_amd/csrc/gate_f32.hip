@@ -11,7 +11,8 @@
 //      W_K (coalesced) against the staged vector and reduce across the wave;
 //      q_i * k_i accumulates into the logit;
 //   4. alpha = sigmoid(logit / sqrt(d_model)), then the same row-per-wavefront
-//      loop over W_V writes out_i = h_i + alpha * v_i.
+//      loop over W_V writes out_i = h_i + alpha * v_i (and the gated value
+//      alpha * v_i when it is asked for).
 // All reductions run in a fixed order, so results are bit-reproducible.
 #include "engram_internal.h"
 
@@ -54,6 +55,7 @@ __global__ __launch_bounds__(NTHR) void gate_f32_kernel(const GateArgs a) {
   const float* gq = (const float*)a.gq[m];
   const float* gk = (const float*)a.gk[m];
   float* out = (float*)a.out[m] + t * d_model;
+  float* vout = a.vout[m] != nullptr ? (float*)a.vout[m] + t * d_model : nullptr;
 
   float ss = 0.f;
   for (int j = threadIdx.x; j < d_mem; j += NTHR) ss += e[j] * e[j];
@@ -89,7 +91,10 @@ __global__ __launch_bounds__(NTHR) void gate_f32_kernel(const GateArgs a) {
     for (int j = lane; j < d_mem; j += 64) v += row[j] * e[j];
     v = wave_sum(v);
     const float hi = h[i];
-    if (lane == 0) out[i] = hi + alpha * v;
+    if (lane == 0) {
+      out[i] = hi + alpha * v;
+      if (vout != nullptr) vout[i] = alpha * v;
+    }
   }
 }
 

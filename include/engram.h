@@ -7,6 +7,8 @@
  *   section 2.2  tokenizer compression, suffix n-grams, multi-head hashing into
  *                prime-sized tables (Eq. 1), concatenated memory vector (Eq. 2);
  *   section 2.3  context-aware gating (Eq. 3-4), gated value and residual add;
+ *                the short depthwise causal convolution over the gated values
+ *                (Eq. 5);
  *   section 2.4  several branches sharing one lookup (Eq. 6);
  *   section 2.5 / Figure 2(b) and section 6.4  host-memory offload with
  *                prefetch of the rows whose addresses are known in advance.
@@ -23,10 +25,10 @@
  *     the call returns after enqueueing.  Outputs are valid once the stream
  *     reaches that point.
  *   - Ownership: the library never frees or keeps caller buffers.  The gate
- *     keeps one grow-only scratch buffer per device (a few MB to a few hundred
- *     MB, by shape), allocated stream-ordered on first use and held until the
- *     process ends; a call on a different stream than the previous gate call
- *     first waits for that call's work on the scratch.
+ *     and the convolution share one grow-only scratch buffer per device (a few
+ *     MB to a few hundred MB, by shape), allocated stream-ordered on first use
+ *     and held until the process ends; a call on a different stream than the
+ *     previous user of the scratch first waits for that call's work on it.
  *   - Errors: arguments are validated on the host before anything is enqueued;
  *     a non-OK status means nothing was enqueued (ENGRAM_ERR_INVALID_ARG,
  *     ENGRAM_ERR_UNSUPPORTED) or a HIP call failed (ENGRAM_ERR_HIP).
@@ -64,6 +66,8 @@ typedef enum engram_dtype {
 #define ENGRAM_MAX_TABLES 32   /* n_orders * heads                       */
 #define ENGRAM_MAX_ORDER 4     /* largest n-gram order                   */
 #define ENGRAM_MAX_BRANCHES 8  /* gating branches per call               */
+#define ENGRAM_CONV_MAX_TAPS 8       /* kernel size of the short convolution  */
+#define ENGRAM_CONV_MAX_DILATION 16  /* its dilation                          */
 
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char* engram_last_error(void);
@@ -134,6 +138,10 @@ engram_status engram_gather(const int32_t* idx, int64_t n_tok, int32_t n_tables,
  *        row-major (output x input).  gq[m]: device [d_model]; gk[m]: [d_mem].
  *        All of `dtype`, 16-byte aligned.
  * gate_out: device float32 [n_branch][n_tok] receiving alpha, or NULL.
+ * value_out: NULL, or a host array of n_branch pointers, each NULL or device
+ *        [n_tok][d_model] of `dtype` (16-byte aligned, overlapping neither h[m]
+ *        nor out[m]) receiving the gated value alpha * v, rounded to `dtype`:
+ *        the input of the short convolution (engram_conv_forward).
  * Arithmetic: bf16 products with fp32 accumulation on the matrix cores
  * (RMSNorm(mem)*gk rounded to bf16 before the W_K product), fp32 elsewhere;
  * ENGRAM_F32 computes everything in fp32.
@@ -144,7 +152,34 @@ engram_status engram_gate_forward(const void* mem, int64_t n_tok, int32_t d_mem,
                                   int32_t n_branch, const void* const* h, const void* const* wk,
                                   const void* const* wv, const void* const* gq,
                                   const void* const* gk, float eps, engram_dtype dtype,
-                                  void* const* out, float* gate_out, hipStream_t stream);
+                                  void* const* out, float* gate_out, void* const* value_out,
+                                  hipStream_t stream);
+
+/*
+ * Short depthwise causal convolution -- section 2.3, Eq. (5): with V~ the
+ * gated values of one sequence (value_out of engram_gate_forward), the module's
+ * output is Y = SiLU(Conv1D(RMSNorm(V~))) + V~.  engram_gate_forward already
+ * adds V~ to the residual; this call adds the remaining term in place:
+ *   n_t      = V~_t / sqrt(mean_c(V~_t[c]^2) + eps) * gamma        (per token)
+ *   z_t[c]   = sum_{j < taps} w[c][j] * n_{t - j*dilation}[c]      (zero before the
+ *                                                                  sequence start)
+ *   out_t[c] = out_t[c] + SiLU(z_t[c]),   SiLU(z) = z / (1 + e^-z)
+ * so tap j looks j*dilation tokens back; the pages' configuration is taps = 4
+ * and dilation = the largest n-gram order.  Sequences never mix.
+ * value: device [batch * seq][d_model] (sequence-major: token t of sequence b is
+ *        row b*seq + t).  out: device, same shape, updated in place; it must not
+ *        overlap `value`.
+ * w:     device [d_model][taps] (channel-major: the taps of one channel are
+ *        contiguous).  gamma: device [d_model].  All of `dtype`, 16-byte aligned.
+ * Arithmetic: fp32, one rounding to `dtype` when `out` is written.
+ * Shapes: d_model * sizeof(dtype) % 16 == 0, 1 <= taps <= ENGRAM_CONV_MAX_TAPS,
+ * 1 <= dilation <= ENGRAM_CONV_MAX_DILATION (UNSUPPORTED otherwise).  batch == 0
+ * or seq == 0 is a no-op.  Uses the library's per-device scratch (4 bytes per
+ * token), like engram_gate_forward.
+ */
+engram_status engram_conv_forward(const void* value, int32_t batch, int64_t seq, int32_t d_model,
+                                  const void* w, const void* gamma, int32_t taps, int32_t dilation,
+                                  float eps, engram_dtype dtype, void* out, hipStream_t stream);
 
 /*
  * Prefetch from host-resident tables -- section 2.5 and Figure 2(b), section

@@ -275,6 +275,12 @@ STREAM_WK = 2 << 20       # + branch
 STREAM_WV = 3 << 20       # + branch
 STREAM_GQ = 4 << 20       # + branch
 STREAM_GK = 5 << 20       # + branch
+STREAM_CONV_W = 6 << 20   # + branch
+STREAM_CONV_G = 7 << 20   # + branch
+
+# the short convolution of the pages' configuration: kernel size 4, dilation = the
+# largest n-gram order
+CONV_TAPS = 4
 
 
 def rng_for(cfg: Config, what: str) -> np.random.Generator:
@@ -359,6 +365,26 @@ def gains(cfg: Config, m: int, device="cpu"):
     gq = counter_normal(cfg.seed, STREAM_GQ + m, zero, cfg.d_model, cfg.gamma_jitter, torch.float32, device)[0]
     gk = counter_normal(cfg.seed, STREAM_GK + m, zero, cfg.d_mem, cfg.gamma_jitter, torch.float32, device)[0]
     return (gq + 1.0).to(dt), (gk + 1.0).to(dt)
+
+
+def conv_dilation(cfg: Config) -> int:
+    return max(cfg.orders)
+
+
+def conv_params(cfg: Config, m: int, taps: int = CONV_TAPS, std: float = 0.5, device="cpu"):
+    """(w [d_model, taps], gamma [d_model]) of branch m's short convolution.
+
+    The pages start the kernel at zero (the module then adds nothing); the
+    synthetic kernel is ~N(0, std) so that every tap contributes, and gamma is
+    1 + jitter * N(0,1) like the other gains."""
+    import torch
+    dt = torch_dtype(cfg)
+    rows = torch.arange(cfg.d_model, dtype=torch.int64, device=device)
+    w = counter_normal(cfg.seed, STREAM_CONV_W + m, rows, taps, std, dt, device)
+    zero = torch.zeros(1, dtype=torch.int64, device=device)
+    jitter = cfg.gamma_jitter if cfg.gamma_jitter > 0 else 0.1
+    g = counter_normal(cfg.seed, STREAM_CONV_G + m, zero, cfg.d_model, jitter, torch.float32, device)[0]
+    return w, (g + 1.0).to(dt)
 
 
 def offload_rows(cfg: Config, mem_available_bytes: Optional[int]) -> int:

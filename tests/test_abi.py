@@ -100,7 +100,8 @@ def test_gate_argument_errors():
     one = (ctypes.c_void_p * 1)(4096)
     gf = lambda **kw: L.engram_gate_forward(
         ctypes.c_void_p(4096), kw.get("n", 8), kw.get("dm", 1280), kw.get("dmod", 2560), kw.get("nb", 1),
-        one, one, one, one, one, ctypes.c_float(kw.get("eps", 1e-6)), kw.get("dt", eg.BF16), one, None, None)
+        one, one, one, one, one, ctypes.c_float(kw.get("eps", 1e-6)), kw.get("dt", eg.BF16), one, None,
+        kw.get("vout"), None)
     assert gf(dm=1000) == _st("unsup")
     assert gf(dmod=2500) == _st("unsup")
     assert b"d_mem % 64" in L.engram_last_error()
@@ -109,7 +110,36 @@ def test_gate_argument_errors():
     assert gf(eps=-1.0) == _st("arg")
     assert gf(n=-2) == _st("arg")
     assert gf(dt=5) == _st("arg")
+    assert gf(vout=(ctypes.c_void_p * 1)(4104)) == _st("arg")   # misaligned gated-value output
     assert gf(n=0) == _st("ok")
+
+
+def test_conv_argument_errors():
+    L = eg.lib()
+    cf = lambda **kw: L.engram_conv_forward(
+        ctypes.c_void_p(kw.get("value", 4096)), kw.get("batch", 2), kw.get("seq", 100), kw.get("dmod", 2560),
+        ctypes.c_void_p(kw.get("w", 1 << 20)), ctypes.c_void_p(kw.get("g", 1 << 21)), kw.get("taps", 4),
+        kw.get("dil", 3), ctypes.c_float(kw.get("eps", 1e-6)), kw.get("dt", eg.BF16),
+        ctypes.c_void_p(kw.get("out", 1 << 30)), None)
+    assert cf(taps=0) == _st("unsup")
+    assert cf(taps=9) == _st("unsup")
+    assert cf(dil=0) == _st("unsup")
+    assert cf(dil=17) == _st("unsup")
+    assert cf(dmod=12) == _st("unsup")                # 24-byte bf16 rows
+    assert b"multiple of 16" in L.engram_last_error()
+    assert cf(dmod=6, dt=eg.F32) == _st("unsup")      # 24-byte fp32 rows
+    assert cf(batch=-1) == _st("arg")
+    assert cf(seq=-1) == _st("arg")
+    assert cf(dmod=0) == _st("arg")
+    assert cf(eps=-1.0) == _st("arg")
+    assert cf(dt=7) == _st("arg")
+    assert cf(w=0) == _st("arg")
+    assert cf(g=8) == _st("arg")                      # misaligned gamma
+    assert cf(value=4100) == _st("arg")               # misaligned value
+    assert cf(out=4096 + 5120 * 10) == _st("arg")     # out overlaps value
+    assert b"overlaps" in L.engram_last_error()
+    assert cf(batch=0) == _st("ok")
+    assert cf(seq=0, value=0, out=0) == _st("ok")
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
