@@ -303,9 +303,11 @@ def run_offload(args):
 
 def measure_conv(args, cfg, bufs, h, layer, outs, flush):
     """The short convolution of Eq. (5), measured beside the step (it is not part of the
-    hash+gather+gate metric): the gate writing the gated values as well, then
-    engram_conv_forward on every branch, each bracketed by events, with the cache flush
-    between them."""
+    hash+gather+gate metric).  Each rep, with the cache flush before each timed piece:
+    the plain gate; the gate writing the gated values as well, followed at once by
+    engram_conv_forward on every branch (the layer's own order: the values the
+    convolution reads were just written); and the convolution alone from cold caches.
+    Every piece is bracketed by events."""
     import torch
     import synth
     import hashed_gram_embedding_hash_amd as eg
@@ -327,27 +329,41 @@ def measure_conv(args, cfg, bufs, h, layer, outs, flush):
         conv()
     torch.cuda.synchronize()
     reps = max(5, args.steps)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(reps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(reps)]
     for i in range(reps):
-        for k, fn in enumerate((lambda: gate(False), lambda: gate(True), conv)):
-            if flush is not None:
-                flush.fill_(float(i + k))
-            ev[i][2 * k].record()
-            fn()
-            ev[i][2 * k + 1].record()
+        if flush is not None:
+            flush.fill_(float(i))
+        ev[i][0].record()
+        gate(False)
+        ev[i][1].record()
+        if flush is not None:
+            flush.fill_(float(i + 1))
+        ev[i][2].record()
+        gate(True)
+        ev[i][3].record()
+        conv()
+        ev[i][4].record()
+        if flush is not None:
+            flush.fill_(float(i + 2))
+        ev[i][5].record()
+        conv()
+        ev[i][6].record()
     torch.cuda.synchronize()
-    ms = [sum(ev[i][2 * k].elapsed_time(ev[i][2 * k + 1]) for i in range(reps)) / reps for k in range(3)]
+    avg = lambda a, b: sum(ev[i][a].elapsed_time(ev[i][b]) for i in range(reps)) / reps
+    gate_ms, gate_v_ms, conv_ms, conv_cold_ms = avg(0, 1), avg(2, 3), avg(3, 4), avg(5, 6)
     es = 2 if cfg.dtype == "bf16" else 4
     unit = cfg.tokens * cfg.d_model * es * cfg.n_branch     # one [tokens, d_model] array per branch
     conv_bytes = 3 * unit          # read the gated values once, read and write out
+    rate = lambda ms: conv_bytes / (ms * 1e-3) / 1e9
     return {"kernel": "engram_conv_forward: conv_rms_kernel + conv_apply_kernel",
             "taps": synth.CONV_TAPS, "dilation": dil, "branches": cfg.n_branch, "reps": reps,
-            "ms": round(ms[2], 5), "bytes_algorithmic": conv_bytes,
-            "GB/s": round(conv_bytes / (ms[2] * 1e-3) / 1e9, 1),
-            "hbm_frac": round(conv_bytes / (ms[2] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            "gate_ms": round(ms[0], 5), "gate_with_values_ms": round(ms[1], 5),
-            "values_write_GB/s": round(unit / max(1e-9, (ms[1] - ms[0]) * 1e-3) / 1e9, 1),
-            "gate_with_values_plus_conv_ms": round(ms[1] + ms[2], 5)}
+            "bytes_algorithmic": conv_bytes,
+            "ms_after_gate": round(conv_ms, 5), "GB/s_after_gate": round(rate(conv_ms), 1),
+            "ms_cold": round(conv_cold_ms, 5), "GB/s_cold": round(rate(conv_cold_ms), 1),
+            "hbm_frac_cold": round(rate(conv_cold_ms) / PEAK_HBM_GBS, 4),
+            "gate_ms": round(gate_ms, 5), "gate_with_values_ms": round(gate_v_ms, 5),
+            "values_write_GB/s": round(unit / max(1e-9, (gate_v_ms - gate_ms) * 1e-3) / 1e9, 1),
+            "gate_with_values_plus_conv_ms": round(gate_v_ms + conv_ms, 5)}
 
 
 def cpu_baseline(cfg, target_s):

@@ -375,8 +375,10 @@ engram_status engram_conv_forward(const void* value, int32_t batch, int64_t seq,
   const char *v0 = (const char*)value, *o0 = (const char*)out;
   if (v0 < o0 + rows * row_bytes && o0 < v0 + rows * row_bytes)
     return fail(ENGRAM_ERR_INVALID_ARG, "%s: out overlaps value", fn);
-  // workgroups of the apply kernel: 64-token blocks x 512-byte column slabs per sequence
-  const int64_t slabs = ((int64_t)row_bytes / 16 + 31) / 32;
+  if ((uint64_t)seq * row_bytes >= (1ull << 32))
+    return fail(ENGRAM_ERR_UNSUPPORTED, "%s: one sequence's values exceed 4 GiB", fn);
+  // workgroups of the apply kernel: 64-token blocks x 256-byte column slabs per sequence
+  const int64_t slabs = ((int64_t)row_bytes / 16 + 15) / 16;
   if (rows / 4 + 1 >= (1ll << 31) || (int64_t)batch * ((seq + 63) / 64) * slabs >= (1ll << 31))
     return fail(ENGRAM_ERR_UNSUPPORTED, "%s: too many tokens for one launch", fn);
   ConvArgs a;

@@ -11,15 +11,16 @@
 //   conv_rms_kernel    a wavefront per token row reduces sum(V~^2) and writes inv[t]
 //                      (4 bytes per token into the library scratch);
 //   conv_apply_kernel  a workgroup per (sequence, block of TB tokens, slab of SW
-//                      16-byte chunks).  Its threads take one chunk column each and
-//                      walk the block's tokens RPP rows apart, so every wavefront
-//                      reads and writes 512 contiguous bytes of two rows.  The kernel
-//                      weights of a chunk (CH channels x TAPS taps, contiguous) and
-//                      its gains stay in registers for the whole block; the block's
-//                      inv values, with the (TAPS-1)*dil rows of causal history
-//                      before it, are staged in LDS.  The taps j > 0 re-read rows
-//                      that tap 0 of a nearby row read a few passes earlier, so they
-//                      are served by the caches.
+//                      16-byte chunks).  It stages the slab's V~ rows of the block and
+//                      the (TAPS-1)*dil rows of causal history before it in LDS, already
+//                      normalized (V~ * inv, in fp32; rows before the sequence start are
+//                      zero, so every tap reads the tile without a branch), six rows per
+//                      thread in flight, with the thread's output chunks loaded alongside.
+//                      Each thread then takes one chunk column and TB / RPP tokens RPP
+//                      rows apart; its kernel weights (CH channels x TAPS taps, contiguous,
+//                      with gamma folded in) sit in registers, so a tap is one FMA per
+//                      element.  Global memory sees each V~ element once (plus the history
+//                      rows shared with the previous block).
 // Workgroups are numbered so that each XCD runs a contiguous range of (token block,
 // slab) pairs in order: the history rows a block needs were read by the block of the
 // same slab just before it on the same XCD and are still in that XCD's L2.
@@ -29,15 +30,25 @@ namespace engram {
 namespace {
 
 constexpr int NTHR_C = 256;
-constexpr int SW = 32;              // 16-byte chunks per slab
+constexpr int SW = 16;              // 16-byte chunks per slab
 constexpr int RPP = NTHR_C / SW;    // token rows per pass
 constexpr int TB = 64;              // tokens per workgroup
 constexpr int HALO_MAX = (ENGRAM_CONV_MAX_TAPS - 1) * ENGRAM_CONV_MAX_DILATION;
 constexpr int N_XCD = 8;
+// the normalized bf16 tile at the largest history fits one workgroup's LDS
+static_assert((TB + HALO_MAX) * SW * 8 * sizeof(float) <= 160 * 1024, "conv tile exceeds LDS");
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ float silu(float z) { return z / (1.f + expf(-z)); }
+// SiLU(z) = z / (1 + e^-z) from the hardware exp2 and reciprocal (each about 1 ulp in
+// fp32).  The IEEE expf and division cost ~40 instructions per element, which made the
+// kernel ALU-bound; this form is four.  Limits: z -> -inf gives e^-z = inf, 1/inf = 0 and
+// -0; z -> +inf gives z.
+__device__ __forceinline__ float silu(float z) {
+  return z * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(z * -1.44269504088896341f));
+}
 
 // One 16-byte chunk: CH elements of the storage type, converted to/from fp32.
 template <typename T> struct Chunk;
@@ -68,11 +79,8 @@ template <> struct Chunk<uint16_t> {  // bfloat16 bit patterns
   __device__ static void store(void* p, const float* x) {
     u32x4 v;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const __bf16 lo = (__bf16)x[2 * i], hi = (__bf16)x[2 * i + 1];  // round to nearest even
-      v[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-             ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-    }
+    for (int i = 0; i < 4; ++i)  // round to nearest even, two per v_cvt_pk_bf16_f32
+      v[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){x[2 * i], x[2 * i + 1]}, bf16x2));
     *reinterpret_cast<u32x4*>(p) = v;
   }
 };
@@ -88,12 +96,20 @@ __global__ __launch_bounds__(NTHR_C) void conv_rms_kernel(const ConvArgs a) {
   const int chunks = a.d_model / CH;
   const T* row = reinterpret_cast<const T*>(a.value) + r * a.d_model;
   float ss = 0.f;
-#pragma unroll 4
-  for (int c = lane; c < chunks; c += 64) {
-    float x[CH];
-    Chunk<T>::load(row + c * CH, x);
+  for (int c0 = lane; c0 < chunks; c0 += 8 * 64) {  // up to eight chunks per lane in flight
+    u32x4 v[8];
 #pragma unroll
-    for (int i = 0; i < CH; ++i) ss += x[i] * x[i];
+    for (int u = 0; u < 8; ++u) {
+      const int c = c0 + u * 64;
+      v[u] = c < chunks ? *reinterpret_cast<const u32x4*>(row + c * CH) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      float x[CH];
+      Chunk<T>::load(&v[u], x);
+#pragma unroll
+      for (int i = 0; i < CH; ++i) ss += x[i] * x[i];
+    }
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
@@ -103,7 +119,11 @@ __global__ __launch_bounds__(NTHR_C) void conv_rms_kernel(const ConvArgs a) {
 template <typename T, int TAPS>
 __global__ __launch_bounds__(NTHR_C) void conv_apply_kernel(const ConvArgs a, int nblk_t, int n_slab) {
   constexpr int CH = Chunk<T>::CH;
-  __shared__ float s_inv[TB + HALO_MAX];
+  constexpr int H = CH / 4;     // float4 pieces per chunk
+  constexpr int KT = TB / RPP;  // tokens per thread
+  // [TB + halo][H][SW] float4: the normalized rows V~ * inv of the slab (gamma is folded
+  // into the weights), zero before the sequence start
+  extern __shared__ float4 s_tile[];
   // XCD-contiguous numbering: hardware block id b goes to XCD b % N_XCD
   const int nb = gridDim.x, q = nb / N_XCD, rem = nb % N_XCD;
   const int xcd = blockIdx.x % N_XCD;
@@ -113,49 +133,91 @@ __global__ __launch_bounds__(NTHR_C) void conv_apply_kernel(const ConvArgs a, in
   const int b = L / (n_slab * nblk_t);
 
   const int halo = (TAPS - 1) * a.dil;
-  const int64_t t0 = (int64_t)tb * TB;
-  const int64_t first = t0 - halo;  // s_inv[i] belongs to position first + i
+  const int nrows = TB + halo;
+  const int seq = (int)a.seq;      // positions and byte offsets within one sequence fit
+  const int t0 = tb * TB;          // 32 bits (the caller limits a sequence to 4 GiB)
+  const int first = t0 - halo;     // tile row i holds position first + i
   const int64_t row0 = (int64_t)b * a.seq;
-  for (int i = threadIdx.x; i < TB + halo; i += NTHR_C) {
-    const int64_t ts = first + i;
-    s_inv[i] = (ts >= 0 && ts < a.seq) ? a.inv[row0 + ts] : 0.f;
-  }
-  __syncthreads();
-
   const int chunks = a.d_model / CH;
-  const int c = slab * SW + (int)(threadIdx.x % SW);
-  if (c >= chunks) return;  // no barrier follows
-  const int c0 = c * CH;
-  const T* V = reinterpret_cast<const T*>(a.value) + row0 * a.d_model + c0;
-  T* O = reinterpret_cast<T*>(a.out) + row0 * a.d_model + c0;
+  const int cl = (int)(threadIdx.x % SW), rr = (int)(threadIdx.x / SW);
+  const int c = slab * SW + cl;
+  const bool col_ok = c < chunks;
+  const int c0 = col_ok ? c * CH : 0;
+  const char* V = reinterpret_cast<const char*>(reinterpret_cast<const T*>(a.value) + row0 * a.d_model + c0);
+  char* O = reinterpret_cast<char*>(reinterpret_cast<T*>(a.out) + row0 * a.d_model + c0);
+  const float* inv = a.inv + row0;
+  const uint32_t ld = (uint32_t)a.d_model * (uint32_t)sizeof(T);
 
-  float g[CH], w[CH * TAPS];  // w[i * TAPS + j]: channel c0 + i, tap j
+  // this thread's output chunks (tokens t0 + rr + RPP k), loaded first: they are
+  // independent of the staging and the barrier
+  u32x4 ov[KT];
+#pragma unroll
+  for (int k = 0; k < KT; ++k) {
+    const int t = t0 + rr + RPP * k;
+    ov[k] = (col_ok && t < seq) ? *reinterpret_cast<const u32x4*>(O + (uint32_t)t * ld) : u32x4{0, 0, 0, 0};
+  }
+  // stage the tile, SR rows per thread in flight at once, normalized on the way in
+  constexpr int SR = 6;
+  for (int i0 = 0; i0 < nrows; i0 += SR * RPP) {
+    u32x4 v[SR];
+    float sc[SR];
+#pragma unroll
+    for (int u = 0; u < SR; ++u) {
+      const int i = i0 + u * RPP + rr;
+      const int ts = first + i;
+      const bool ok = i < nrows && ts >= 0 && ts < seq;
+      v[u] = (ok && col_ok) ? *reinterpret_cast<const u32x4*>(V + (uint32_t)ts * ld) : u32x4{0, 0, 0, 0};
+      sc[u] = ok ? inv[ts] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < SR; ++u) {
+      const int i = i0 + u * RPP + rr;
+      if (i < nrows) {
+        float x[CH];
+        Chunk<T>::load(&v[u], x);
+#pragma unroll
+        for (int hh = 0; hh < H; ++hh)
+          s_tile[(i * H + hh) * SW + cl] =
+              float4{x[4 * hh] * sc[u], x[4 * hh + 1] * sc[u], x[4 * hh + 2] * sc[u], x[4 * hh + 3] * sc[u]};
+      }
+    }
+  }
+  float g[CH], wg[CH * TAPS];  // wg[i * TAPS + j] = w[c0 + i][j] * gamma[c0 + i]
   Chunk<T>::load(reinterpret_cast<const T*>(a.gamma) + c0, g);
 #pragma unroll
   for (int k = 0; k < TAPS; ++k)
-    Chunk<T>::load(reinterpret_cast<const T*>(a.w) + (int64_t)c0 * TAPS + k * CH, w + k * CH);
+    Chunk<T>::load(reinterpret_cast<const T*>(a.w) + (int64_t)c0 * TAPS + k * CH, wg + k * CH);
+#pragma unroll
+  for (int i = 0; i < CH; ++i)
+#pragma unroll
+    for (int j = 0; j < TAPS; ++j) wg[i * TAPS + j] *= g[i];
+  __syncthreads();
+  if (!col_ok) return;  // no barrier follows
 
-  const int64_t t_end = (t0 + TB < a.seq) ? t0 + TB : a.seq;
-  for (int64_t t = t0 + (int)(threadIdx.x / SW); t < t_end; t += RPP) {
+#pragma unroll
+  for (int k = 0; k < KT; ++k) {
+    const int tl = rr + RPP * k;  // position t0 + tl, tile row tl + halo
+    if (t0 + tl >= seq) break;
     float z[CH];
 #pragma unroll
     for (int i = 0; i < CH; ++i) z[i] = 0.f;
 #pragma unroll
     for (int j = 0; j < TAPS; ++j) {
-      const int64_t ts = t - (int64_t)j * a.dil;
-      if (ts >= 0) {
-        float x[CH];
-        Chunk<T>::load(V + ts * a.d_model, x);
-        const float sc = s_inv[ts - first];
+      const int row = tl + halo - j * a.dil;  // >= 0; rows before the sequence start are zero
 #pragma unroll
-        for (int i = 0; i < CH; ++i) z[i] += w[i * TAPS + j] * (x[i] * sc * g[i]);
+      for (int hh = 0; hh < H; ++hh) {
+        const float4 n = s_tile[(row * H + hh) * SW + cl];
+        z[4 * hh] = fmaf(wg[(4 * hh) * TAPS + j], n.x, z[4 * hh]);
+        z[4 * hh + 1] = fmaf(wg[(4 * hh + 1) * TAPS + j], n.y, z[4 * hh + 1]);
+        z[4 * hh + 2] = fmaf(wg[(4 * hh + 2) * TAPS + j], n.z, z[4 * hh + 2]);
+        z[4 * hh + 3] = fmaf(wg[(4 * hh + 3) * TAPS + j], n.w, z[4 * hh + 3]);
       }
     }
     float o[CH];
-    Chunk<T>::load(O + t * a.d_model, o);
+    Chunk<T>::load(&ov[k], o);
 #pragma unroll
     for (int i = 0; i < CH; ++i) o[i] += silu(z[i]);
-    Chunk<T>::store(O + t * a.d_model, o);
+    Chunk<T>::store(O + (uint32_t)(t0 + tl) * ld, o);
   }
 }
 
@@ -167,9 +229,10 @@ void launch_conv_t(const ConvArgs& a, hipStream_t s) {
   const int chunks = a.d_model / Chunk<T>::CH;
   const int n_slab = (chunks + SW - 1) / SW;
   const dim3 grid((unsigned)((int64_t)a.batch * nblk_t * n_slab));
+  const size_t tile_bytes = (size_t)(TB + (a.taps - 1) * a.dil) * SW * Chunk<T>::CH * sizeof(float);
   switch (a.taps) {
 #define ENGRAM_CONV_CASE(K) \
-  case K: hipLaunchKernelGGL((conv_apply_kernel<T, K>), grid, dim3(NTHR_C), 0, s, a, nblk_t, n_slab); break;
+  case K: hipLaunchKernelGGL((conv_apply_kernel<T, K>), grid, dim3(NTHR_C), tile_bytes, s, a, nblk_t, n_slab); break;
     ENGRAM_CONV_CASE(1) ENGRAM_CONV_CASE(2) ENGRAM_CONV_CASE(3) ENGRAM_CONV_CASE(4)
     ENGRAM_CONV_CASE(5) ENGRAM_CONV_CASE(6) ENGRAM_CONV_CASE(7) ENGRAM_CONV_CASE(8)
 #undef ENGRAM_CONV_CASE

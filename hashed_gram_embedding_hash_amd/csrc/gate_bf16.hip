@@ -95,7 +95,9 @@ __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u 
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  // round-to-nearest-even conversion (v_cvt_pk_bf16_f32 on gfx950)
+  // round-to-nearest-even conversion (v_cvt_pk_bf16_f32 on gfx950).  Kept as two
+  // scalar conversions: the two-lane vector form saves a few instructions but changes
+  // the persistent kernel's register allocation (more spills, 2 % slower measured).
   const __bf16 a = (__bf16)lo, b = (__bf16)hi;
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
@@ -186,7 +188,10 @@ __device__ __forceinline__ bool decode_tile(const GateArgs& a, int x, int q, Til
 }
 
 // One K or V tile.  A single main loop serves both phases (one copy of the
-// loop keeps register allocation simple); only the epilogues differ.
+// loop keeps register allocation simple); only the epilogues differ.  VALUES: the
+// V epilogue also writes the gated values alpha * v where a branch asks for them (a
+// separate instantiation, so the plain gate keeps its register allocation).
+template <bool VALUES>
 __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, char* smem, int x,
                                           int& next_claim) {
   const int PHASE = tile.phase;
@@ -653,7 +658,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
       }
     };
     stream_out((uint16_t*)a.out[m]);
-    if (a.vout[m] != nullptr) {
+    if (VALUES && a.vout[m] != nullptr) {
       // the gated values alpha * v, staged through the same LDS tile
       lds_barrier();
 #pragma unroll
@@ -680,6 +685,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
 #undef ENGRAM_QSLOT
 }
 
+template <bool VALUES>
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gate_persistent_kernel(const GateArgs a) {
   // the operand ring, then the h tile and the epilogue scratch; between tiles its
@@ -696,7 +702,7 @@ void gate_persistent_kernel(const GateArgs a) {
     const bool have = decode_tile(a, x, *s_tile, t);
     lds_barrier();  // every thread has read the tile number before the ring is refilled
     if (!have) break;
-    gate_tile(a, t, smem, x, claim);
+    gate_tile<VALUES>(a, t, smem, x, claim);
     // LDS free for the next tile.  A full barrier: letting a V tile's 128 KB of output
     // stores drain behind the next tile's operand loads measured 8 % slower than
     // finishing them first.
@@ -784,7 +790,12 @@ void launch_gate_bf16(const GateArgs& a_in, hipStream_t s) {
 
   int grid = cu_count() / NQ * NQ;
   if (grid < NQ) grid = NQ;
-  hipLaunchKernelGGL(gate_persistent_kernel, dim3((unsigned)grid), dim3(NTHR), 0, s, a);
+  bool values = false;
+  for (int m = 0; m < a.n_branch; ++m) values = values || a.vout[m] != nullptr;
+  if (values)
+    hipLaunchKernelGGL(gate_persistent_kernel<true>, dim3((unsigned)grid), dim3(NTHR), 0, s, a);
+  else
+    hipLaunchKernelGGL(gate_persistent_kernel<false>, dim3((unsigned)grid), dim3(NTHR), 0, s, a);
 }
 
 }  // namespace engram

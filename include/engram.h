@@ -173,7 +173,8 @@ engram_status engram_gate_forward(const void* mem, int64_t n_tok, int32_t d_mem,
  *        contiguous).  gamma: device [d_model].  All of `dtype`, 16-byte aligned.
  * Arithmetic: fp32, one rounding to `dtype` when `out` is written.
  * Shapes: d_model * sizeof(dtype) % 16 == 0, 1 <= taps <= ENGRAM_CONV_MAX_TAPS,
- * 1 <= dilation <= ENGRAM_CONV_MAX_DILATION (UNSUPPORTED otherwise).  batch == 0
+ * 1 <= dilation <= ENGRAM_CONV_MAX_DILATION, seq * d_model * sizeof(dtype) < 4 GiB
+ * (UNSUPPORTED otherwise).  batch == 0
  * or seq == 0 is a no-op.  Uses the library's per-device scratch (4 bytes per
  * token), like engram_gate_forward.
  */
