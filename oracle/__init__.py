@@ -50,7 +50,8 @@ def lib():
         L.oracle_hash.restype = None
         L.oracle_gather.argtypes = [P, i64, i32, P, i32, P]
         L.oracle_gather.restype = None
-        L.oracle_gate.argtypes = [P, i64, i32, i32, P, P, P, P, P, ctypes.c_double, i32, P, P, P]
+        L.oracle_gate.argtypes = [P, i64, i32, i32, P, P, P, P, P, ctypes.c_double, i32, i32, P, P, P]
+        L.oracle_gate.restype = ctypes.c_int
         L.oracle_gate.restype = ctypes.c_int
         L.oracle_conv.argtypes = [P, i32, i64, i32, P, P, i32, i32, ctypes.c_double, i32, P, P]
         L.oracle_conv.restype = None
@@ -104,26 +105,34 @@ def gather(idx: np.ndarray, tables: Sequence[np.ndarray]):
     return out
 
 
+KEY_NORM_MEMORY = 0      # k = W_K RMSNorm_gk(e), gk over d_mem (the review page's pseudocode)
+KEY_NORM_PROJECTED = 1   # k = RMSNorm_gk(W_K e), gk over d_model (the paper's Eq. (4) / Eq. (6))
+
+
 def gate(mem: np.ndarray, h: np.ndarray, wk: np.ndarray, wv: np.ndarray, gq: np.ndarray,
-         gk: np.ndarray, eps: float, dtype: int, with_value: bool = False):
+         gk: np.ndarray, eps: float, dtype: int, with_value: bool = False,
+         key_norm: int = KEY_NORM_MEMORY):
     """One gating branch: (out [n_tok, d_model] float64, alpha [n_tok] float64), and the
     gated value alpha * v [n_tok, d_model] float64 as a third element when with_value.
 
     Arrays hold float32 values (dtype F32) or raw bfloat16 bits as uint16 (dtype BF16).
+    gk has d_mem entries for KEY_NORM_MEMORY and d_model for KEY_NORM_PROJECTED.
     """
     mem, h, wk, wv, gq, gk = (np.ascontiguousarray(a) for a in (mem, h, wk, wv, gq, gk))
     n_tok, d_mem = mem.shape
     d_model = h.shape[1]
     assert h.shape[0] == n_tok and wk.shape == (d_model, d_mem) and wv.shape == (d_model, d_mem)
-    assert gq.shape == (d_model,) and gk.shape == (d_mem,)
+    assert gq.shape == (d_model,)
+    assert gk.shape == ((d_mem,) if key_norm == KEY_NORM_MEMORY else (d_model,))
     want = np.float32 if dtype == F32 else np.uint16
     for a in (mem, h, wk, wv, gq, gk):
         assert a.dtype == want, a.dtype
     out = np.empty((n_tok, d_model), dtype=np.float64)
     alpha = np.empty(n_tok, dtype=np.float64)
     value = np.empty((n_tok, d_model), dtype=np.float64) if with_value else None
-    lib().oracle_gate(_p(mem), n_tok, d_mem, d_model, _p(h), _p(wk), _p(wv), _p(gq), _p(gk),
-                      float(eps), dtype, _p(out), _p(alpha), _p(value) if with_value else None)
+    rc = lib().oracle_gate(_p(mem), n_tok, d_mem, d_model, _p(h), _p(wk), _p(wv), _p(gq), _p(gk),
+                           float(eps), dtype, key_norm, _p(out), _p(alpha), _p(value) if with_value else None)
+    assert rc == 0, rc
     return (out, alpha, value) if with_value else (out, alpha)
 
 

@@ -26,6 +26,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define ORACLE_F32 0
@@ -120,21 +121,28 @@ void oracle_gather(const int32_t* idx, int64_t n_tok, int32_t n_tables, const vo
 
 /*
  * Context-aware gating of one branch (section 2.3, Eq. (3)-(4), the gated value
- * and the residual update; section 2.4, Eq. (6) for a branch m; the review
- * page's context_aware_gating pseudocode for where the key's RMSNorm sits):
+ * and the residual update; section 2.4, Eq. (6) for a branch m).  Two placements of
+ * the key's RMSNorm:
+ *   key_norm == 0 (the review page's context_aware_gating pseudocode):
+ *     k = W_K * RMSNorm_{gk}(e_t),   gk: [d_mem]
+ *   key_norm == 1 (the paper's Eq. (4) and Eq. (6): the key is normalised after W_K):
+ *     k = RMSNorm_{gk}(W_K * e_t),   gk: [d_model]
+ * and in both
  *   q     = RMSNorm_{gq}(h_t)
- *   k     = W_K * RMSNorm_{gk}(e_t)
  *   v     = W_V * e_t
  *   alpha = sigmoid( q . k / sqrt(d_model) )
  *   out   = h_t + alpha * v
+ * with RMSNorm_g(x) = x / sqrt(mean(x^2) + eps) * g.
  * mem: [n_tok][d_mem]; h, out: [n_tok][d_model]; W_K, W_V: [d_model][d_mem]
- * row-major (output x input); gq: [d_model]; gk: [d_mem]; all of `dtype`.
+ * row-major (output x input); gq: [d_model]; all of `dtype`.
  * out and alpha are double; `value` (double [n_tok][d_model], or NULL) receives the
- * gated value alpha * v that the convolution of Eq. (5) consumes.  Returns 0.
+ * gated value alpha * v that the convolution of Eq. (5) consumes.  Returns 0, or -1
+ * for an unknown key_norm.
  */
 int oracle_gate(const void* mem, int64_t n_tok, int32_t d_mem, int32_t d_model, const void* h,
                 const void* wk, const void* wv, const void* gq, const void* gk, double eps,
-                int32_t dtype, double* out, double* alpha, double* value) {
+                int32_t dtype, int32_t key_norm, double* out, double* alpha, double* value) {
+  if (key_norm != 0 && key_norm != 1) return -1;
   for (int64_t t = 0; t < n_tok; ++t) {
     /* RMSNorm of the memory vector and of the hidden state */
     double ss_e = 0.0;
@@ -152,14 +160,33 @@ int oracle_gate(const void* mem, int64_t n_tok, int32_t d_mem, int32_t d_model, 
 
     /* logit = sum_i q_i * k_i */
     double logit = 0.0;
-    for (int32_t i = 0; i < d_model; ++i) {
-      double k = 0.0;
-      for (int32_t j = 0; j < d_mem; ++j) {
-        const double en = load_elem(mem, t * d_mem + j, dtype) / rms_e * load_elem(gk, j, dtype);
-        k += load_elem(wk, (int64_t)i * d_mem + j, dtype) * en;
+    if (key_norm == 0) {
+      for (int32_t i = 0; i < d_model; ++i) {
+        double k = 0.0;
+        for (int32_t j = 0; j < d_mem; ++j) {
+          const double en = load_elem(mem, t * d_mem + j, dtype) / rms_e * load_elem(gk, j, dtype);
+          k += load_elem(wk, (int64_t)i * d_mem + j, dtype) * en;
+        }
+        const double q = load_elem(h, t * d_model + i, dtype) / rms_h * load_elem(gq, i, dtype);
+        logit += q * k;
       }
-      const double q = load_elem(h, t * d_model + i, dtype) / rms_h * load_elem(gq, i, dtype);
-      logit += q * k;
+    } else {
+      /* the raw projection first, then its RMSNorm over the d_model features */
+      double* k = (double*)malloc(sizeof(double) * (size_t)d_model);
+      if (k == NULL) return -2;
+      double ss_k = 0.0;
+      for (int32_t i = 0; i < d_model; ++i) {
+        k[i] = 0.0;
+        for (int32_t j = 0; j < d_mem; ++j)
+          k[i] += load_elem(wk, (int64_t)i * d_mem + j, dtype) * load_elem(mem, t * d_mem + j, dtype);
+        ss_k += k[i] * k[i];
+      }
+      const double rms_k = sqrt(ss_k / d_model + eps);
+      for (int32_t i = 0; i < d_model; ++i) {
+        const double q = load_elem(h, t * d_model + i, dtype) / rms_h * load_elem(gq, i, dtype);
+        logit += q * (k[i] / rms_k * load_elem(gk, i, dtype));
+      }
+      free(k);
     }
     logit /= sqrt((double)d_model);
     const double a = 1.0 / (1.0 + exp(-logit));

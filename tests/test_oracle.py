@@ -244,13 +244,15 @@ def _golden_gate():
     return ex
 
 
-@pytest.mark.parametrize("name", ["A", "B"])
+@pytest.mark.parametrize("name", ["A", "B", "C"])
 def test_gate_hand_examples(name):
     g = _golden_gate()[name]
     dm, dmod = int(g["d_mem"][0]), int(g["d_model"][0])
+    key_norm = int(g.get("key_norm", [0])[0])
     f = lambda k, shape: np.array(g[k], np.float32).reshape(shape)
     out, alpha = oracle.gate(f("e", (1, dm)), f("h", (1, dmod)), f("wk", (dmod, dm)), f("wv", (dmod, dm)),
-                             f("gq", (dmod,)), f("gk", (dm,)), g["eps"][0], oracle.F32)
+                             f("gq", (dmod,)), f("gk", (dm,) if key_norm == 0 else (dmod,)), g["eps"][0],
+                             oracle.F32, key_norm=key_norm)
     # the inputs are not all exactly representable in float32; 1e-6 covers that rounding
     assert abs(alpha[0] - 1 / (1 + math.exp(-g["logit"][0]))) < 1e-6
     assert abs(alpha[0] - g["alpha"][0]) < 1e-6
@@ -449,3 +451,49 @@ def test_gate_value_output_is_the_gated_value():
     assert np.allclose(value, out - h.astype(np.float64), rtol=1e-12, atol=1e-12)
     v = e.astype(np.float64) @ wv.astype(np.float64).T
     assert np.allclose(value, alpha[:, None] * v, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# The paper's key placement (Eq. (4) / Eq. (6)): RMSNorm after W_K
+
+def test_gate_projected_key_equals_memory_key_for_orthogonal_wk():
+    """For an orthogonal W_K (d_model = d_mem) and unit gains, RMSNorm(W_K e) = W_K RMSNorm(e),
+    so the two placements of the key's norm give the same gate."""
+    rng = np.random.default_rng(41)
+    d = 24
+    q_mat, _ = np.linalg.qr(rng.standard_normal((d, d)))
+    e, h, _, wv, gq, _ = _rand_gate(rng, 6, d, d)
+    wk = q_mat.astype(np.float32)
+    ones = np.ones(d, np.float32)
+    _, a_mem = oracle.gate(e, h, wk, wv, gq, ones, 0.0, oracle.F32, key_norm=oracle.KEY_NORM_MEMORY)
+    _, a_proj = oracle.gate(e, h, wk, wv, gq, ones, 0.0, oracle.F32, key_norm=oracle.KEY_NORM_PROJECTED)
+    # wk is orthogonal only to float32 rounding
+    np.testing.assert_allclose(a_proj, a_mem, rtol=0, atol=1e-6)
+
+
+def test_gate_projected_key_ignores_the_scale_of_wk():
+    """Normalising after the projection removes W_K's scale (eps = 0; the factor 4 is exact);
+    normalising the memory before it does not."""
+    rng = np.random.default_rng(42)
+    e, h, wk, wv, gq, _ = _rand_gate(rng, 7, 20, 12)
+    gk = (1 + 0.2 * rng.standard_normal(12)).astype(np.float32)
+    _, a1 = oracle.gate(e, h, wk, wv, gq, gk, 0.0, oracle.F32, key_norm=oracle.KEY_NORM_PROJECTED)
+    _, a4 = oracle.gate(e, h, 4 * wk, wv, gq, gk, 0.0, oracle.F32, key_norm=oracle.KEY_NORM_PROJECTED)
+    np.testing.assert_allclose(a4, a1, rtol=1e-12, atol=0)
+    gk_m = np.ones(20, np.float32)
+    _, m1 = oracle.gate(e, h, wk, wv, gq, gk_m, 0.0, oracle.F32)
+    _, m4 = oracle.gate(e, h, 4 * wk, wv, gq, gk_m, 0.0, oracle.F32)
+    assert np.abs(m4 - m1).max() > 1e-3
+
+
+def test_gate_projected_key_limits():
+    """W_K = 0 gives alpha = 1/2; out and the value projection do not depend on the key's form."""
+    rng = np.random.default_rng(43)
+    e, h, wk, wv, gq, gk = _rand_gate(rng, 5, 16, 8)
+    gk_d = np.ones(8, np.float32)
+    _, a0 = oracle.gate(e, h, np.zeros_like(wk), wv, gq, gk_d, 1e-6, oracle.F32, key_norm=1)
+    assert np.all(a0 == 0.5)
+    out_p, a_p, v_p = oracle.gate(e, h, wk, wv, gq, gk_d, 1e-6, oracle.F32, with_value=True, key_norm=1)
+    np.testing.assert_allclose(v_p, out_p - h.astype(np.float64), rtol=1e-12, atol=1e-12)
+    v = e.astype(np.float64) @ wv.astype(np.float64).T
+    np.testing.assert_allclose(v_p, a_p[:, None] * v, rtol=1e-12, atol=1e-12)
