@@ -210,7 +210,7 @@ def run_offload(args):
 
         def gate(s, buf):
             chk(L.engram_gate_forward(stg[buf].data_ptr(), B, cfg.d_mem, cfg.d_model, 1, h_a[s], wk_a, wv_a, gq_a,
-                                      gk_a, cfg.eps, eg.BF16, out_a, None, None, ms))
+                                      gk_a, cfg.eps, eg.BF16, eg.KEY_NORM_MEMORY, out_a, None, None, ms))
 
         def pipeline(mode):
             ready = [torch.cuda.Event() for _ in range(2)]

@@ -34,6 +34,8 @@ BF16 = 1
 MAX_TABLES = 32
 MAX_ORDER = 4
 MAX_BRANCHES = 8
+KEY_NORM_MEMORY = 0      # k = W_K RMSNorm_gk(e), gk over d_mem (the review page's pseudocode)
+KEY_NORM_PROJECTED = 1   # k = RMSNorm_gk(W_K e), gk over d_model (the paper's Eq. 4 / Eq. 6)
 CONV_MAX_TAPS = 8
 CONV_MAX_DILATION = 16
 
@@ -75,7 +77,7 @@ def lib() -> ctypes.CDLL:
         L.engram_compress.argtypes = [P, i64, P, i32, P, P, P]
         L.engram_hash.argtypes = [P, i32, i64, i64, i64, P, i32, i32, P, P, i32, P, P]
         L.engram_gather.argtypes = [P, i64, i32, P, P, i32, i32, P, P, P]
-        L.engram_gate_forward.argtypes = [P, i64, i32, i32, i32, P, P, P, P, P, ctypes.c_float, i32,
+        L.engram_gate_forward.argtypes = [P, i64, i32, i32, i32, P, P, P, P, P, ctypes.c_float, i32, i32,
                                           P, P, P, P]
         L.engram_conv_forward.argtypes = [P, i32, i64, i32, P, P, i32, i32, ctypes.c_float, i32, P, P]
         L.engram_prefetch_host.argtypes = [P, i64, i32, P, P, i32, i32, P, P, P]
@@ -194,8 +196,10 @@ def engram_gather(idx, tables: Sequence, out=None, err_count=None, stream=None):
 
 def engram_gate_forward(mem, h: Sequence, wk: Sequence, wv: Sequence, gq: Sequence, gk: Sequence,
                         eps: float = 1e-6, out: Optional[Sequence] = None, gate_out=None,
-                        value_out: Optional[Sequence] = None, stream=None):
-    """out[m] = h[m] + sigmoid(RMSNorm(h[m]) . W_K[m] RMSNorm(mem) / sqrt(d)) * W_V[m] mem.
+                        value_out: Optional[Sequence] = None, key_norm: int = KEY_NORM_MEMORY, stream=None):
+    """out[m] = h[m] + sigmoid(RMSNorm(h[m]) . k[m] / sqrt(d)) * W_V[m] mem, with
+    k[m] = W_K[m] RMSNorm(mem) (KEY_NORM_MEMORY, gk over d_mem) or RMSNorm(W_K[m] mem)
+    (KEY_NORM_PROJECTED, gk over d_model).
 
     Lists hold one tensor per branch; ``out`` defaults to new tensors (pass ``h``
     for in-place).  ``gate_out``: optional float32 [n_branch, n_tok] for alpha.
@@ -227,8 +231,15 @@ def engram_gate_forward(mem, h: Sequence, wk: Sequence, wv: Sequence, gq: Sequen
             raise ValueError("weights must be [d_model, d_mem]")
     arr = lambda seq: _ptr_array([x.data_ptr() for x in seq])
     varr = None if value_out is None else _ptr_array([0 if x is None else x.data_ptr() for x in value_out])
+    gk_len = d_mem if key_norm == KEY_NORM_MEMORY else d_model
+    for x in gq:
+        if tuple(x.shape) != (d_model,):
+            raise ValueError("gq must be [d_model]")
+    for x in gk:
+        if tuple(x.shape) != (gk_len,):
+            raise ValueError(f"gk must be [{gk_len}] for key_norm {key_norm}")
     _check(lib().engram_gate_forward(mem.data_ptr(), n_tok, d_mem, d_model, nb, arr(h), arr(wk), arr(wv),
-                                     arr(gq), arr(gk), float(eps), _edtype(mem), arr(out),
+                                     arr(gq), arr(gk), float(eps), _edtype(mem), int(key_norm), arr(out),
                                      _opt(gate_out, "gate_out", torch.float32), varr, _stream(stream)))
     return out
 

@@ -284,8 +284,8 @@ engram_status engram_gate_forward(const void* mem, int64_t n_tok, int32_t d_mem,
                                   int32_t n_branch, const void* const* h, const void* const* wk,
                                   const void* const* wv, const void* const* gq,
                                   const void* const* gk, float eps, engram_dtype dtype,
-                                  void* const* out, float* gate_out, void* const* value_out,
-                                  hipStream_t stream) {
+                                  engram_key_norm key_norm, void* const* out, float* gate_out,
+                                  void* const* value_out, hipStream_t stream) {
   const char* fn = "engram_gate_forward";
   if (n_tok < 0 || d_mem <= 0 || d_model <= 0)
     return fail(ENGRAM_ERR_INVALID_ARG, "%s: bad sizes n_tok=%lld d_mem=%d d_model=%d", fn,
@@ -295,6 +295,8 @@ engram_status engram_gate_forward(const void* mem, int64_t n_tok, int32_t d_mem,
                 ENGRAM_MAX_BRANCHES);
   if (!valid_dtype(dtype)) return fail(ENGRAM_ERR_INVALID_ARG, "%s: unknown dtype", fn);
   if (!(eps >= 0.f)) return fail(ENGRAM_ERR_INVALID_ARG, "%s: eps must be >= 0", fn);
+  if (key_norm != ENGRAM_KEY_NORM_MEMORY && key_norm != ENGRAM_KEY_NORM_PROJECTED)
+    return fail(ENGRAM_ERR_INVALID_ARG, "%s: unknown key_norm %d", fn, (int)key_norm);
   if (h == nullptr || wk == nullptr || wv == nullptr || gq == nullptr || gk == nullptr || out == nullptr)
     return fail(ENGRAM_ERR_INVALID_ARG, "%s: null pointer array", fn);
   if (dtype == ENGRAM_BF16 && (d_mem % 64 != 0 || d_model % 32 != 0))
@@ -333,10 +335,13 @@ engram_status engram_gate_forward(const void* mem, int64_t n_tok, int32_t d_mem,
   a.n_branch = n_branch;
   a.eps = eps;
   a.inv_sqrt_d = 1.0f / sqrtf((float)d_model);
+  a.key_norm = (int32_t)key_norm;
 
   if (dtype == ENGRAM_F32) {
-    if ((size_t)d_mem * 4 > 64 * 1024)
-      return fail(ENGRAM_ERR_UNSUPPORTED, "%s: fp32 path needs d_mem <= 16384", fn);
+    const size_t lds = (size_t)d_mem * 4 + (key_norm == ENGRAM_KEY_NORM_PROJECTED ? (size_t)d_model * 4 : 0);
+    if (lds > 64 * 1024)
+      return fail(ENGRAM_ERR_UNSUPPORTED, "%s: fp32 path needs d_mem (+ d_model for the projected key norm) "
+                  "<= 16384", fn);
     launch_gate_f32(a, stream);
     return check_launch(fn);
   }

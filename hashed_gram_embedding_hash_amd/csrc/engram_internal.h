@@ -62,8 +62,10 @@ struct GateArgs {
   float* ee;         // scratch: [n_branch][n_ftiles][n_tok] partial sums of e^2
   float* alpha;      // scratch: [n_branch][n_tok] gates, published by the last K tile of a token tile
   int32_t* counters; // scratch: per-queue tile heads, then per-(branch, token tile) done counts
+  float* kgain;      // scratch, projected key norm: [n_branch][d_model] gq * gk
   int64_t n_tok;
   int32_t d_mem, d_model, n_branch, n_ftiles, n_ttiles;
+  int32_t key_norm;  // engram_key_norm
   float eps, inv_sqrt_d;
 };
 // bf16 path: returns the scratch bytes it needs for these shapes (and sets a.n_ftiles).

@@ -45,16 +45,16 @@
 // lane's accumulator groups 0-1 and 2-3 each cover 8 consecutive features:
 // every epilogue access is a 16-byte vector.
 //
-// Main loop.  BK = 32 per k-step over a ring of four 32-KB LDS slots (weight rows
-// and memory rows of one k-step each).  Operands move global -> LDS with direct
-// loads (no registers), issued three k-steps ahead: three stages are in flight
-// while the fourth is read, enough to cover the latency of L2 misses that a
-// single register-staged stage could not.  The loads are issued from inline asm
-// and waited for with explicit vmcnt counts, because the compiler would otherwise
-// make every LDS read wait for all of them.  One LDS-only barrier per k-step both
-// publishes the next stage and frees the slot just read.  The fragment registers
-// are double-buffered so that a sub-step's MFMAs cover the next sub-step's LDS
-// reads.  Slot rows are 64 B; the 16-B chunk index is XOR-swizzled by slot_key so
+// Main loop.  BK = 64 per k-step over a ring of five 32-KB LDS slots, each holding
+// one operand of one k-step (256 weight rows or 256 memory rows of 128 B).
+// Operands move global -> LDS with direct loads (no registers); the refill of the
+// two slots a k-step frees is spread through that k-step's MFMA stream, so three
+// slots are in flight while two are read, enough to cover the latency of L2 misses.
+// The loads are issued from inline asm and waited for with explicit vmcnt counts,
+// because the compiler would otherwise make every LDS read wait for all of them.
+// One LDS-only barrier per k-step both publishes the next stage and frees the slots
+// just read.  The fragment reads are spread one per two MFMAs in the order the
+// MFMAs consume them.  The 16-B chunk index of a row is XOR-swizzled by row_key so
 // the fragment reads (32 consecutive rows, one chunk) are free of bank conflicts.
 //
 // Epilogue.  The slot ring is reused for the h tile (256 tokens x 256 features,
@@ -188,10 +188,14 @@ __device__ __forceinline__ bool decode_tile(const GateArgs& a, int x, int q, Til
 }
 
 // One K or V tile.  A single main loop serves both phases (one copy of the
-// loop keeps register allocation simple); only the epilogues differ.  VALUES: the
-// V epilogue also writes the gated values alpha * v where a branch asks for them (a
-// separate instantiation, so the plain gate keeps its register allocation).
-template <bool VALUES>
+// loop keeps register allocation simple); only the epilogues differ.  Two options,
+// each its own instantiation so that the plain gate keeps its register allocation:
+//   VALUES  the V epilogue also writes the gated values alpha * v where a branch asks
+//           for them;
+//   KEYP    the paper's key placement, k = RMSNorm_gk(W_K e) with gk over d_model: the
+//           K tiles run on the raw W_K, their epilogue weights h_f by gq_f gk_f (from
+//           LDS) and also reduces sum_f k_f^2, which takes the place of the e^2 partial.
+template <bool VALUES, bool KEYP>
 __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, char* smem, int x,
                                           int& next_claim) {
   const int PHASE = tile.phase;
@@ -206,7 +210,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
   const int d_mem = a.d_mem, d_model = a.d_model;
   int32_t* done = a.counters + NQ + m * a.n_ttiles + tile.ttile;
 
-  // phase K reads the gk-scaled copy of W_K (a.wk points at it here)
+  // phase K reads the gain-folded copy of W_K (a.wk points at it here), or KEYP W_K itself
   const uint16_t* W = (const uint16_t*)(PHASE == PHASE_K ? a.wk[m] : a.wv[m]);
   const uint16_t* E = (const uint16_t*)a.mem;
   const uint16_t* H = (const uint16_t*)a.h[m];
@@ -225,6 +229,8 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
     lds_barrier();  // the gate loads below are issued only after the count is seen
     if (t0 + tid < n_tok) alpha = ld_coherent(a.alpha + (int64_t)m * n_tok + t0 + tid);
   }
+  float kg = 0.f;  // KEYP K tiles: gq * gk of feature f0 + tid (to LDS in the epilogue)
+  if (KEYP && PHASE == PHASE_K && f0 + tid < d_model) kg = a.kgain[(int64_t)m * d_model + f0 + tid];
 
   // ---- operand stream.  Chunk c of the tile's stream lands in LDS slot c % NSLOT:
   // chunks 2 kt and 2 kt + 1 are the weight rows and the memory rows of k-step kt
@@ -365,7 +371,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
   float ee_acc[MT];
 #pragma unroll
   for (int j = 0; j < MT; ++j) ee_acc[j] = 0.f;
-  const bool ee_wave = PHASE == PHASE_K && wf == 0;
+  const bool ee_wave = !KEYP && PHASE == PHASE_K && wf == 0;
 #define ENGRAM_EE(buf)                                                                     \
   do {                                                                                     \
     _Pragma("unroll") for (int j = 0; j < MT; ++j)                                         \
@@ -509,8 +515,14 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
   // LDS byte offset of logical 16-B chunk c of token tl in the h tile
 #define ENGRAM_HOFF(tl, c) (ENGRAM_QSLOT((tl) >> 6) + ((tl) & 63) * (BF * 2) + (((c) ^ ((tl) & 31)) * 16))
   int* s_flag = reinterpret_cast<int*>(scratch + 5 * BT * sizeof(float));
+  float (*s_kk)[BT] = reinterpret_cast<float (*)[BT]>(scratch + 6 * BT * sizeof(float));  // KEYP
+  float* s_g = reinterpret_cast<float*>(scratch + 8 * BT * sizeof(float));               // KEYP, [BF]
   if (PHASE == PHASE_V) {
     s_alpha[etid] = alpha;
+    lds_barrier();
+  }
+  if (KEYP && PHASE == PHASE_K) {
+    s_g[etid] = kg;
     lds_barrier();
   }
 
@@ -532,28 +544,66 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
           hv[i][gp] = *reinterpret_cast<const u32x4*>(smem + ENGRAM_HOFF(tl, fl >> 3));
           if (f0 + fl >= d_model) hv[i][gp] = (u32x4){0u, 0u, 0u, 0u};
         }
-      float dot = 0.f, hh = 0.f, dot2 = 0.f, hh2 = 0.f;  // two chains each
+      if constexpr (!KEYP) {
+        float dot = 0.f, hh = 0.f, dot2 = 0.f, hh2 = 0.f;  // two chains each
 #pragma unroll
-      for (int i = 0; i < MF; ++i) {
+        for (int i = 0; i < MF; ++i) {
 #pragma unroll
-        for (int gp = 0; gp < 2; ++gp) {
+          for (int gp = 0; gp < 2; ++gp) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float h0 = bf16_lo(hv[i][gp][q]), h1 = bf16_hi(hv[i][gp][q]);
-            dot += h0 * acc[i][j][gp * 8 + 2 * q];
-            dot2 += h1 * acc[i][j][gp * 8 + 2 * q + 1];
-            hh += h0 * h0;
-            hh2 += h1 * h1;
+            for (int q = 0; q < 4; ++q) {
+              const float h0 = bf16_lo(hv[i][gp][q]), h1 = bf16_hi(hv[i][gp][q]);
+              dot += h0 * acc[i][j][gp * 8 + 2 * q];
+              dot2 += h1 * acc[i][j][gp * 8 + 2 * q + 1];
+              hh += h0 * h0;
+              hh2 += h1 * h1;
+            }
           }
         }
-      }
-      dot += dot2;
-      hh += hh2;
-      dot += __shfl_xor(dot, 32, 64);
-      hh += __shfl_xor(hh, 32, 64);
-      if (elane < 32) {
-        s_red[ewf][0][tl] = dot;
-        s_red[ewf][1][tl] = hh;
+        dot += dot2;
+        hh += hh2;
+        dot += __shfl_xor(dot, 32, 64);
+        hh += __shfl_xor(hh, 32, 64);
+        if (elane < 32) {
+          s_red[ewf][0][tl] = dot;
+          s_red[ewf][1][tl] = hh;
+        }
+      } else {
+        // q_f k_f with the gains from LDS; k_f^2 only over features that exist
+        float dot = 0.f, hh = 0.f, kk = 0.f, dot2 = 0.f, hh2 = 0.f, kk2 = 0.f;
+#pragma unroll
+        for (int i = 0; i < MF; ++i) {
+#pragma unroll
+          for (int gp = 0; gp < 2; ++gp) {
+            const int fl = ewf * WF + i * 32 + gp * 16 + hsel;
+            const float4 g0 = *reinterpret_cast<const float4*>(s_g + fl);
+            const float4 g1 = *reinterpret_cast<const float4*>(s_g + fl + 4);
+            const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+            const float vm = f0 + fl < d_model ? 1.f : 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float h0 = bf16_lo(hv[i][gp][q]), h1 = bf16_hi(hv[i][gp][q]);
+              const float a0 = acc[i][j][gp * 8 + 2 * q], a1 = acc[i][j][gp * 8 + 2 * q + 1];
+              dot += h0 * g[2 * q] * a0;
+              dot2 += h1 * g[2 * q + 1] * a1;
+              hh += h0 * h0;
+              hh2 += h1 * h1;
+              kk += vm * a0 * a0;
+              kk2 += vm * a1 * a1;
+            }
+          }
+        }
+        dot += dot2;
+        hh += hh2;
+        kk += kk2;
+        dot += __shfl_xor(dot, 32, 64);
+        hh += __shfl_xor(hh, 32, 64);
+        kk += __shfl_xor(kk, 32, 64);
+        if (elane < 32) {
+          s_red[ewf][0][tl] = dot;
+          s_red[ewf][1][tl] = hh;
+          s_kk[ewf][tl] = kk;
+        }
       }
     }
     __syncthreads();
@@ -562,6 +612,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
       const int64_t o = ((int64_t)m * a.n_ftiles + ftile) * n_tok + t;
       st_coherent(a.part_dot + o, s_red[0][0][etid] + s_red[1][0][etid]);
       st_coherent(a.part_hh + o, s_red[0][1][etid] + s_red[1][1][etid]);
+      if (KEYP) st_coherent(a.ee + o, s_kk[0][etid] + s_kk[1][etid]);
     }
     // publish: __syncthreads() waits until every wave's partial stores have completed,
     // then the count goes up
@@ -595,7 +646,8 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
           }
         }
         const float rms_h = sqrtf(hh / (float)d_model + a.eps);
-        const float rms_e = sqrtf(ee / (float)d_mem + a.eps);
+        // the key's norm: of the memory vector (d_mem wide), or KEYP of W_K e (d_model)
+        const float rms_e = sqrtf(ee / (float)(KEYP ? d_model : d_mem) + a.eps);
         const float logit = dot / (rms_h * rms_e) * a.inv_sqrt_d;
         const float g = 1.f / (1.f + expf(-logit));
         st_coherent(a.alpha + (int64_t)m * n_tok + t, g);
@@ -685,7 +737,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
 #undef ENGRAM_QSLOT
 }
 
-template <bool VALUES>
+template <bool VALUES, bool KEYP>
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gate_persistent_kernel(const GateArgs a) {
   // the operand ring, then the h tile and the epilogue scratch; between tiles its
@@ -702,12 +754,25 @@ void gate_persistent_kernel(const GateArgs a) {
     const bool have = decode_tile(a, x, *s_tile, t);
     lds_barrier();  // every thread has read the tile number before the ring is refilled
     if (!have) break;
-    gate_tile<VALUES>(a, t, smem, x, claim);
+    gate_tile<VALUES, KEYP>(a, t, smem, x, claim);
     // LDS free for the next tile.  A full barrier: letting a V tile's 128 KB of output
     // stores drain behind the next tile's operand loads measured 8 % slower than
     // finishing them first.
     __syncthreads();
   }
+}
+
+// KEYP: the per-feature key gain gq[m][f] * gk[m][f] in fp32 (exact: a product of two
+// bf16 values), and the tile queues / done counters cleared; the K tiles read W_K itself.
+__global__ __launch_bounds__(256) void gate_prep_projected_kernel(const GateArgs a, int n_counters) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n_counters) a.counters[i] = 0;
+  if (i >= (int64_t)a.n_branch * a.d_model) return;
+  const int m = (int)(i / a.d_model);
+  const int f = (int)(i - (int64_t)m * a.d_model);
+  const float gq = __uint_as_float((uint32_t)((const uint16_t*)a.gq[m])[f] << 16);
+  const float gk = __uint_as_float((uint32_t)((const uint16_t*)a.gk[m])[f] << 16);
+  a.kgain[i] = gq * gk;
 }
 
 // One launch before the gate: W'[m][f][c] = bf16(gq[m][f] * W_K[m][f][c] * gk[m][c])
@@ -732,6 +797,8 @@ __global__ __launch_bounds__(256) void gate_prep_kernel(const GateArgs a, uint16
   reinterpret_cast<u32x4*>(wk_scaled)[i] = o;
 }
 
+// wk_bytes: the gain-folded key weights (the memory-side key norm), or KEYP the fp32
+// per-feature key gains
 struct ScratchLayout {
   size_t wk_bytes, part_bytes, alpha_bytes, counter_bytes, total;
   int n_counters;
@@ -739,7 +806,9 @@ struct ScratchLayout {
 
 ScratchLayout layout_for(const GateArgs& a) {
   ScratchLayout L;
-  L.wk_bytes = ((size_t)a.n_branch * a.d_model * a.d_mem * 2 + 255) & ~(size_t)255;
+  L.wk_bytes = a.key_norm == ENGRAM_KEY_NORM_PROJECTED
+                   ? ((size_t)a.n_branch * a.d_model * 4 + 255) & ~(size_t)255
+                   : ((size_t)a.n_branch * a.d_model * a.d_mem * 2 + 255) & ~(size_t)255;
   const size_t part_elems = (size_t)a.n_branch * a.n_ftiles * (size_t)a.n_tok;
   L.part_bytes = (part_elems * 4 + 255) & ~(size_t)255;
   L.alpha_bytes = ((size_t)a.n_branch * (size_t)a.n_tok * 4 + 255) & ~(size_t)255;
@@ -782,20 +851,34 @@ void launch_gate_bf16(const GateArgs& a_in, hipStream_t s) {
   a.alpha = (float*)(base + L.wk_bytes + 3 * L.part_bytes);
   a.counters = (int32_t*)(base + L.wk_bytes + 3 * L.part_bytes + L.alpha_bytes);
 
-  const int64_t n8 = (int64_t)a.d_model * a.d_mem / 8;
-  const int64_t work = n8 * a.n_branch > L.n_counters ? n8 * a.n_branch : L.n_counters;
-  hipLaunchKernelGGL(gate_prep_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, a,
-                     wk_scaled, n8, L.n_counters);
-  for (int m = 0; m < a.n_branch; ++m) a.wk[m] = wk_scaled + (size_t)m * a.d_model * a.d_mem;
+  const bool keyp = a.key_norm == ENGRAM_KEY_NORM_PROJECTED;
+  if (keyp) {
+    a.kgain = (float*)base;
+    const int64_t work = (int64_t)a.n_branch * a.d_model > L.n_counters ? (int64_t)a.n_branch * a.d_model
+                                                                         : L.n_counters;
+    hipLaunchKernelGGL(gate_prep_projected_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, a,
+                       L.n_counters);
+  } else {
+    const int64_t n8 = (int64_t)a.d_model * a.d_mem / 8;
+    const int64_t work = n8 * a.n_branch > L.n_counters ? n8 * a.n_branch : L.n_counters;
+    hipLaunchKernelGGL(gate_prep_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, a,
+                       wk_scaled, n8, L.n_counters);
+    for (int m = 0; m < a.n_branch; ++m) a.wk[m] = wk_scaled + (size_t)m * a.d_model * a.d_mem;
+  }
 
   int grid = cu_count() / NQ * NQ;
   if (grid < NQ) grid = NQ;
   bool values = false;
   for (int m = 0; m < a.n_branch; ++m) values = values || a.vout[m] != nullptr;
-  if (values)
-    hipLaunchKernelGGL(gate_persistent_kernel<true>, dim3((unsigned)grid), dim3(NTHR), 0, s, a);
+  const dim3 g((unsigned)grid), b(NTHR);
+  if (values && keyp)
+    hipLaunchKernelGGL((gate_persistent_kernel<true, true>), g, b, 0, s, a);
+  else if (values)
+    hipLaunchKernelGGL((gate_persistent_kernel<true, false>), g, b, 0, s, a);
+  else if (keyp)
+    hipLaunchKernelGGL((gate_persistent_kernel<false, true>), g, b, 0, s, a);
   else
-    hipLaunchKernelGGL(gate_persistent_kernel<false>, dim3((unsigned)grid), dim3(NTHR), 0, s, a);
+    hipLaunchKernelGGL((gate_persistent_kernel<false, false>), g, b, 0, s, a);
 }
 
 }  // namespace engram

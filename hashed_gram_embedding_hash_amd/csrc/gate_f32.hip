@@ -9,7 +9,8 @@
 //   2. RMSNorm(e) * gk is staged in LDS;
 //   3. each wavefront takes output features in turn, its lanes read one row of
 //      W_K (coalesced) against the staged vector and reduce across the wave;
-//      q_i * k_i accumulates into the logit;
+//      q_i * k_i accumulates into the logit (with the projected key norm, the raw
+//      k = W_K e goes to LDS first and its RMSNorm is applied to the reduced sums);
 //   4. alpha = sigmoid(logit / sqrt(d_model)), then the same row-per-wavefront
 //      loop over W_V writes out_i = h_i + alpha * v_i (and the gated value
 //      alpha * v_i when it is asked for).
@@ -64,21 +65,42 @@ __global__ __launch_bounds__(NTHR) void gate_f32_kernel(const GateArgs a) {
   for (int i = threadIdx.x; i < d_model; i += NTHR) sh += h[i] * h[i];
   const float rms_h = sqrtf(block_sum(sh, red) / (float)d_model + a.eps);
 
-  for (int j = threadIdx.x; j < d_mem; j += NTHR) s_en[j] = e[j] / rms_e * gk[j];
-  __syncthreads();
-
-  float dot = 0.f;  // meaningful in lane 0 of each wave
-  for (int i = wave; i < d_model; i += NWAVE) {
-    const float* row = wk + (int64_t)i * d_mem;
-    float k = 0.f;
-    for (int j = lane; j < d_mem; j += 64) k += row[j] * s_en[j];
-    k = wave_sum(k);
-    dot += (h[i] / rms_h * gq[i]) * k;
-  }
-  if (lane == 0) s_dot[wave] = dot;
-  __syncthreads();
   float logit = 0.f;
-  for (int w = 0; w < NWAVE; ++w) logit += s_dot[w];
+  if (a.key_norm == ENGRAM_KEY_NORM_MEMORY) {
+    for (int j = threadIdx.x; j < d_mem; j += NTHR) s_en[j] = e[j] / rms_e * gk[j];
+    __syncthreads();
+    float dot = 0.f;  // meaningful in lane 0 of each wave
+    for (int i = wave; i < d_model; i += NWAVE) {
+      const float* row = wk + (int64_t)i * d_mem;
+      float k = 0.f;
+      for (int j = lane; j < d_mem; j += 64) k += row[j] * s_en[j];
+      k = wave_sum(k);
+      dot += (h[i] / rms_h * gq[i]) * k;
+    }
+    if (lane == 0) s_dot[wave] = dot;
+    __syncthreads();
+    for (int w = 0; w < NWAVE; ++w) logit += s_dot[w];
+  } else {
+    // the raw projection k = W_K e into LDS, then its RMSNorm over the d_model features
+    float* s_k = s_en + d_mem;
+    for (int j = threadIdx.x; j < d_mem; j += NTHR) s_en[j] = e[j];
+    __syncthreads();
+    for (int i = wave; i < d_model; i += NWAVE) {
+      const float* row = wk + (int64_t)i * d_mem;
+      float k = 0.f;
+      for (int j = lane; j < d_mem; j += 64) k += row[j] * s_en[j];
+      k = wave_sum(k);
+      if (lane == 0) s_k[i] = k;
+    }
+    __syncthreads();
+    float kk = 0.f, dot = 0.f;
+    for (int i = threadIdx.x; i < d_model; i += NTHR) {
+      kk += s_k[i] * s_k[i];
+      dot += (h[i] / rms_h * gq[i]) * s_k[i] * gk[i];
+    }
+    const float rms_k = sqrtf(block_sum(kk, red) / (float)d_model + a.eps);
+    logit = block_sum(dot, red) / rms_k;
+  }
   logit /= sqrtf((float)d_model);
   const float alpha = 1.f / (1.f + expf(-logit));
   if (threadIdx.x == 0 && a.gate_out != nullptr) a.gate_out[(int64_t)m * a.n_tok + t] = alpha;
@@ -102,7 +124,9 @@ __global__ __launch_bounds__(NTHR) void gate_f32_kernel(const GateArgs a) {
 
 void launch_gate_f32(const GateArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)a.n_tok, (unsigned)a.n_branch);
-  hipLaunchKernelGGL(gate_f32_kernel, grid, dim3(NTHR), (size_t)a.d_mem * sizeof(float), s, a);
+  const size_t lds = ((size_t)a.d_mem + (a.key_norm == ENGRAM_KEY_NORM_PROJECTED ? (size_t)a.d_model : 0)) *
+                     sizeof(float);
+  hipLaunchKernelGGL(gate_f32_kernel, grid, dim3(NTHR), lds, s, a);
 }
 
 }  // namespace engram

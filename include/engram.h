@@ -62,6 +62,15 @@ typedef enum engram_dtype {
   ENGRAM_BF16 = 1 /* bfloat16 (top 16 bits of binary32), round-to-nearest-even on output */
 } engram_dtype;
 
+/* Where the key's RMSNorm sits in the context-aware gate. */
+typedef enum engram_key_norm {
+  /* k = W_K * RMSNorm_gk(e), gk over d_mem: the context_aware_gating pseudocode of the
+   * review page (koala.ai.kr) */
+  ENGRAM_KEY_NORM_MEMORY = 0,
+  /* k = RMSNorm_gk(W_K * e), gk over d_model: the paper's Eq. (4) and Eq. (6) */
+  ENGRAM_KEY_NORM_PROJECTED = 1
+} engram_key_norm;
+
 /* Limits of this implementation. */
 #define ENGRAM_MAX_TABLES 32   /* n_orders * heads                       */
 #define ENGRAM_MAX_ORDER 4     /* largest n-gram order                   */
@@ -129,22 +138,25 @@ engram_status engram_gather(const int32_t* idx, int64_t n_tok, int32_t n_tables,
  * (every branch has its own W_K, W_V and gains; the paper's shared W_V is the
  * case of equal pointers):
  *   q     = RMSNorm_{gq[m]}(h[m]_t),  RMSNorm_g(x) = x / sqrt(mean(x^2) + eps) * g
- *   k     = Wk[m] * RMSNorm_{gk[m]}(mem_t)
+ *   k     = Wk[m] * RMSNorm_{gk[m]}(mem_t)      (key_norm ENGRAM_KEY_NORM_MEMORY)
+ *         = RMSNorm_{gk[m]}(Wk[m] * mem_t)      (key_norm ENGRAM_KEY_NORM_PROJECTED)
  *   v     = Wv[m] * mem_t
  *   alpha = sigmoid( q . k / sqrt(d_model) )
  *   out[m]_t = h[m]_t + alpha * v
  * mem:   device [n_tok][d_mem].   h[m], out[m]: device [n_tok][d_model]; out[m]
  *        may equal h[m] (in place).  Wk[m], Wv[m]: device [d_model][d_mem]
- *        row-major (output x input).  gq[m]: device [d_model]; gk[m]: [d_mem].
+ *        row-major (output x input).  gq[m]: device [d_model]; gk[m]: [d_mem]
+ *        (ENGRAM_KEY_NORM_MEMORY) or [d_model] (ENGRAM_KEY_NORM_PROJECTED).
  *        All of `dtype`, 16-byte aligned.
  * gate_out: device float32 [n_branch][n_tok] receiving alpha, or NULL.
  * value_out: NULL, or a host array of n_branch pointers, each NULL or device
  *        [n_tok][d_model] of `dtype` (16-byte aligned, overlapping neither h[m]
  *        nor out[m]) receiving the gated value alpha * v, rounded to `dtype`:
  *        the input of the short convolution (engram_conv_forward).
- * Arithmetic: bf16 products with fp32 accumulation on the matrix cores
- * (RMSNorm(mem)*gk rounded to bf16 before the W_K product), fp32 elsewhere;
- * ENGRAM_F32 computes everything in fp32.
+ * Arithmetic: bf16 products with fp32 accumulation on the matrix cores, fp32
+ * elsewhere; with ENGRAM_KEY_NORM_MEMORY the bf16 path folds both gains into a
+ * copy of W_K rounded once to bf16.  ENGRAM_F32 computes everything in fp32 (its
+ * ENGRAM_KEY_NORM_PROJECTED form needs d_mem + d_model <= 16384).
  * Shapes: ENGRAM_BF16 needs d_mem % 64 == 0 and d_model % 32 == 0; ENGRAM_F32
  * accepts any positive sizes.  n_tok == 0 is a no-op.
  */
@@ -152,8 +164,8 @@ engram_status engram_gate_forward(const void* mem, int64_t n_tok, int32_t d_mem,
                                   int32_t n_branch, const void* const* h, const void* const* wk,
                                   const void* const* wv, const void* const* gq,
                                   const void* const* gk, float eps, engram_dtype dtype,
-                                  void* const* out, float* gate_out, void* const* value_out,
-                                  hipStream_t stream);
+                                  engram_key_norm key_norm, void* const* out, float* gate_out,
+                                  void* const* value_out, hipStream_t stream);
 
 /*
  * Short depthwise causal convolution -- section 2.3, Eq. (5): with V~ the

@@ -277,6 +277,7 @@ STREAM_GQ = 4 << 20       # + branch
 STREAM_GK = 5 << 20       # + branch
 STREAM_CONV_W = 6 << 20   # + branch
 STREAM_CONV_G = 7 << 20   # + branch
+STREAM_GKP = 8 << 20      # + branch: the key gain over d_model (key normalised after W_K)
 
 # the short convolution of the pages' configuration: kernel size 4, dilation = the
 # largest n-gram order
@@ -354,16 +355,18 @@ def weights(cfg: Config, m: int, device="cpu"):
     return wk, wv
 
 
-def gains(cfg: Config, m: int, device="cpu"):
-    """(gamma_q [d_model], gamma_k [d_mem]) of branch m: 1 + jitter * N(0,1)."""
+def gains(cfg: Config, m: int, device="cpu", projected_key: bool = False):
+    """(gamma_q [d_model], gamma_k) of branch m: 1 + jitter * N(0,1).  gamma_k has d_mem
+    entries, or d_model with projected_key (the key normalised after W_K)."""
     import torch
     dt = torch_dtype(cfg)
+    nk = cfg.d_model if projected_key else cfg.d_mem
     if cfg.gamma_jitter == 0.0:
-        return (torch.ones(cfg.d_model, dtype=dt, device=device),
-                torch.ones(cfg.d_mem, dtype=dt, device=device))
+        return (torch.ones(cfg.d_model, dtype=dt, device=device), torch.ones(nk, dtype=dt, device=device))
     zero = torch.zeros(1, dtype=torch.int64, device=device)
     gq = counter_normal(cfg.seed, STREAM_GQ + m, zero, cfg.d_model, cfg.gamma_jitter, torch.float32, device)[0]
-    gk = counter_normal(cfg.seed, STREAM_GK + m, zero, cfg.d_mem, cfg.gamma_jitter, torch.float32, device)[0]
+    gk = counter_normal(cfg.seed, (STREAM_GKP if projected_key else STREAM_GK) + m, zero, nk, cfg.gamma_jitter,
+                        torch.float32, device)[0]
     return (gq + 1.0).to(dt), (gk + 1.0).to(dt)
 
 

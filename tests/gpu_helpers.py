@@ -52,13 +52,15 @@ def oracle_memory(cfg: synth.Config, idx_rows: np.ndarray, nrows=None) -> np.nda
     return oracle.gather(remap, subs)
 
 
-def oracle_gate_tokens(cfg: synth.Config, m: int, e: np.ndarray, tokens: np.ndarray):
+def oracle_gate_tokens(cfg: synth.Config, m: int, e: np.ndarray, tokens: np.ndarray,
+                       key_norm: int = oracle.KEY_NORM_MEMORY):
     """Oracle (out [n, d_model] float64, alpha [n]) of branch m for global token numbers `tokens`."""
     h = host_view(synth.hidden_rows(cfg, m, torch.from_numpy(tokens.astype(np.int64))))
     wk, wv = (host_view(x) for x in synth.weights(cfg, m))
-    gq, gk = (host_view(x) for x in synth.gains(cfg, m))
+    proj = key_norm == oracle.KEY_NORM_PROJECTED
+    gq, gk = (host_view(x) for x in synth.gains(cfg, m, projected_key=proj))
     dt = oracle.F32 if cfg.dtype == "f32" else oracle.BF16
-    return oracle.gate(e, h, wk, wv, gq, gk, cfg.eps, dt)
+    return oracle.gate(e, h, wk, wv, gq, gk, cfg.eps, dt, key_norm=key_norm)
 
 
 def sample_tokens(cfg: synth.Config, n: int, seed: int = 0) -> np.ndarray:

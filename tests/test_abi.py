@@ -100,8 +100,8 @@ def test_gate_argument_errors():
     one = (ctypes.c_void_p * 1)(4096)
     gf = lambda **kw: L.engram_gate_forward(
         ctypes.c_void_p(4096), kw.get("n", 8), kw.get("dm", 1280), kw.get("dmod", 2560), kw.get("nb", 1),
-        one, one, one, one, one, ctypes.c_float(kw.get("eps", 1e-6)), kw.get("dt", eg.BF16), one, None,
-        kw.get("vout"), None)
+        one, one, one, one, one, ctypes.c_float(kw.get("eps", 1e-6)), kw.get("dt", eg.BF16), kw.get("kn", 0),
+        one, None, kw.get("vout"), None)
     assert gf(dm=1000) == _st("unsup")
     assert gf(dmod=2500) == _st("unsup")
     assert b"d_mem % 64" in L.engram_last_error()
@@ -111,6 +111,8 @@ def test_gate_argument_errors():
     assert gf(n=-2) == _st("arg")
     assert gf(dt=5) == _st("arg")
     assert gf(vout=(ctypes.c_void_p * 1)(4104)) == _st("arg")   # misaligned gated-value output
+    assert gf(kn=2) == _st("arg")                                 # unknown key placement
+    assert b"key_norm" in L.engram_last_error()
     assert gf(n=0) == _st("ok")
 
 

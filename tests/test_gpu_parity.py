@@ -163,7 +163,8 @@ def test_gate_fp32_tiny_full_pipeline():
     assert np.abs(alpha.cpu().numpy()[0] - alpha_o).max() <= 1e-5
 
 
-def _gate_case(cfg, n_tok, seed, table_std=None, gamma_jitter=None, n_branch=None, inplace=False):
+def _gate_case(cfg, n_tok, seed, table_std=None, gamma_jitter=None, n_branch=None, inplace=False,
+               key_norm=eg.KEY_NORM_MEMORY):
     """Random-token gate check of the bf16 path against the oracle on n_tok tokens."""
     cfg = cfg.replace(**{k: v for k, v in dict(table_std=table_std, gamma_jitter=gamma_jitter,
                                                      n_branch=n_branch).items() if v is not None})
@@ -174,14 +175,16 @@ def _gate_case(cfg, n_tok, seed, table_std=None, gamma_jitter=None, n_branch=Non
     e_d = torch.from_numpy(e_o.view(np.int16)).to(DEV).view(torch.bfloat16)
     hs = [synth.hidden_rows(cfg, m, torch.from_numpy(tokens)).to(DEV) for m in range(cfg.n_branch)]
     ws = [synth.weights(cfg, m, DEV) for m in range(cfg.n_branch)]
-    gs = [synth.gains(cfg, m, DEV) for m in range(cfg.n_branch)]
+    proj = key_norm == eg.KEY_NORM_PROJECTED
+    gs = [synth.gains(cfg, m, DEV, projected_key=proj) for m in range(cfg.n_branch)]
     alpha = torch.empty((cfg.n_branch, n_tok), dtype=torch.float32, device=DEV)
     h_in = [h.clone() for h in hs]
     out = eg.engram_gate_forward(e_d, h_in, [w[0] for w in ws], [w[1] for w in ws], [g[0] for g in gs],
-                                 [g[1] for g in gs], cfg.eps, out=h_in if inplace else None, gate_out=alpha)
+                                 [g[1] for g in gs], cfg.eps, out=h_in if inplace else None, gate_out=alpha,
+                                 key_norm=key_norm)
     torch.cuda.synchronize()
     for m in range(cfg.n_branch):
-        out_o, alpha_o = oracle_gate_tokens(cfg, m, e_o, tokens)
+        out_o, alpha_o = oracle_gate_tokens(cfg, m, e_o, tokens, key_norm=key_norm)
         err = rel_err(out[m].float().cpu().numpy(), out_o)
         aerr = np.abs(alpha[m].cpu().numpy() - alpha_o).max()
         upd_err = rel_err((out[m].float() - hs[m].float()).cpu().numpy(), out_o - host_bf16_to_f64(hs[m]))
@@ -211,6 +214,43 @@ def test_gate_bf16_stress_unit_tables_and_gains():
 def test_gate_bf16_multi_branch_in_place():
     say("gate bf16 multi-branch in place")
     _gate_case(synth.CONFIGS["multi"], 130, seed=12, table_std=0.5, inplace=True)
+
+
+def test_gate_bf16_projected_key_small_ragged():
+    """The paper's key placement (RMSNorm after W_K, Eq. 4) with gains != 1, 300 tokens."""
+    say("gate bf16 projected key small 300")
+    _gate_case(synth.CONFIGS["small"], 300, seed=13, gamma_jitter=0.2, key_norm=eg.KEY_NORM_PROJECTED)
+
+
+def test_gate_bf16_projected_key_stress():
+    say("gate bf16 projected key stress")
+    _gate_case(synth.CONFIGS["small"], 97, seed=14, table_std=1.0, gamma_jitter=0.3,
+               key_norm=eg.KEY_NORM_PROJECTED)
+
+
+def test_gate_bf16_projected_key_multi_branch_in_place():
+    """Eq. (6): four branches, each with its own W_K and gains, d_model 4096."""
+    say("gate bf16 projected key multi-branch in place")
+    _gate_case(synth.CONFIGS["multi"], 130, seed=15, table_std=0.5, inplace=True, key_norm=eg.KEY_NORM_PROJECTED)
+
+
+def test_gate_fp32_projected_key_tiny():
+    cfg = synth.CONFIGS["tiny"].replace(gamma_jitter=0.2)
+    say("gate fp32 projected key tiny")
+    rng = np.random.default_rng(16)
+    idx = rng.integers(0, cfg.rows, (cfg.tokens, cfg.n_tables)).astype(np.int32)
+    e_o = oracle_memory(cfg, idx)
+    tokens = np.arange(cfg.tokens, dtype=np.int64)
+    h = synth.hidden_rows(cfg, 0, torch.from_numpy(tokens)).to(DEV)
+    wk, wv = synth.weights(cfg, 0, DEV)
+    gq, gk = synth.gains(cfg, 0, DEV, projected_key=True)
+    alpha = torch.empty((1, cfg.tokens), dtype=torch.float32, device=DEV)
+    out = eg.engram_gate_forward(torch.from_numpy(e_o).to(DEV), [h], [wk], [wv], [gq], [gk], cfg.eps,
+                                 gate_out=alpha, key_norm=eg.KEY_NORM_PROJECTED)[0]
+    out_o, alpha_o = oracle_gate_tokens(cfg, 0, e_o, tokens, key_norm=oracle.KEY_NORM_PROJECTED)
+    err, aerr = rel_err(out.cpu().numpy(), out_o), np.abs(alpha.cpu().numpy()[0] - alpha_o).max()
+    say(f"  out rel err {err:.2e}, alpha abs err {aerr:.2e}")
+    assert err <= 1e-5 and aerr <= 1e-5
 
 
 def test_gate_bf16_scratch_shared_across_streams_and_sizes():
