@@ -43,6 +43,10 @@ def parse():
     p.add_argument("--config", default="small")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time of the CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--shared-wv", action="store_true",
+                   help="every branch uses branch 0's W_V (the paper's Eq. 6): W_V e is computed once")
+    p.add_argument("--key-norm", choices=("memory", "projected"), default="memory",
+                   help="memory: k = W_K RMSNorm(e) (default); projected: k = RMSNorm(W_K e), Eq. 4")
     p.add_argument("--no-conv", action="store_true",
                    help="skip the separate measurement of the short convolution (Eq. 5)")
     p.add_argument("--flush-mb", type=int, default=512, help="cache-flush buffer rewritten between steps (0: off)")
@@ -57,8 +61,11 @@ def parse():
     return p.parse_args()
 
 
-def workload_desc(cfg):
-    return {
+def workload_desc(cfg, args=None):
+    extra = {}
+    if args is not None and (args.shared_wv or args.key_norm != "memory"):
+        extra = {"key_norm": args.key_norm, "shared_wv": bool(args.shared_wv)}
+    return {**extra,
         "workload": cfg.name,
         "tokens": cfg.tokens, "batch": cfg.batch, "seq_len": cfg.seq,
         "tables": f"{cfg.n_tables} x {cfg.rows} x {cfg.w} {cfg.dtype}",
@@ -67,17 +74,19 @@ def workload_desc(cfg):
     }
 
 
-def algorithmic(cfg):
-    """Algorithmic work of one step, per call (bytes moved to/from HBM, flops)."""
+def algorithmic(cfg, shared_wv=False):
+    """Algorithmic work of one step, per call (bytes moved to/from HBM, flops).  With a
+    shared W_V the value product is counted once, not once per branch."""
     T, nt, dm, d, M = cfg.tokens, cfg.n_tables, cfg.d_mem, cfg.d_model, cfg.n_branch
+    nv = 1 if shared_wv else M
     es = 4 if cfg.dtype == "f32" else 2
     return {
         "compress": {"bytes": 8 * T},
         "hash": {"bytes": 4 * T + 4 * nt * T},
         "gather": {"bytes": 4 * nt * T + 2 * dm * es * T},
         # weights once, memory vector once, hidden read + output written per branch
-        "gate": {"flops": 4 * dm * d * M * T,
-                 "bytes": dm * es * T + M * (2 * d * dm * es + 2 * d * es * T)},
+        "gate": {"flops": 2 * dm * d * (M + nv) * T,
+                 "bytes": dm * es * T + (M + nv) * d * dm * es + M * 2 * d * es * T},
     }
 
 
@@ -318,7 +327,7 @@ def measure_conv(args, cfg, bufs, h, layer, outs, flush):
 
     def gate(with_values):
         eg.engram_gate_forward(bufs["mem"], h, layer.wk, layer.wv, layer.gq, layer.gk, cfg.eps, out=outs,
-                               value_out=vals if with_values else None)
+                               value_out=vals if with_values else None, key_norm=layer.key_norm)
 
     def conv():
         for m in range(cfg.n_branch):
@@ -438,8 +447,13 @@ def main():
     dev = torch.device("cuda:0")
     print(f"[bench] building inputs for {cfg.name}", file=sys.stderr, flush=True)
     inp = synth.device_inputs(cfg, dev)
+    if args.shared_wv:
+        inp["wv"] = [inp["wv"][0]] * cfg.n_branch
+    key_norm = eg.KEY_NORM_PROJECTED if args.key_norm == "projected" else eg.KEY_NORM_MEMORY
+    if key_norm == eg.KEY_NORM_PROJECTED:
+        inp["gk"] = [synth.gains(cfg, m, dev, projected_key=True)[1] for m in range(cfg.n_branch)]
     layer = EngramLayer(inp["map"], cfg.orders, cfg.heads, inp["mult"], inp["tables"], inp["wk"], inp["wv"],
-                        inp["gq"], inp["gk"], cfg.eps, pad_id=cfg.vocab_c)
+                        inp["gq"], inp["gk"], cfg.eps, pad_id=cfg.vocab_c, key_norm=key_norm)
     outs = [torch.empty_like(h) for h in inp["h"]]
     bufs = layer.buffers(cfg.batch, cfg.seq)
     raw, h = inp["raw"], inp["h"]
@@ -457,7 +471,8 @@ def main():
         eg.engram_gather(bufs["idx"], layer.tables, out=bufs["mem"])
         if ev is not None:
             ev[3].record()
-        eg.engram_gate_forward(bufs["mem"], h, layer.wk, layer.wv, layer.gq, layer.gk, cfg.eps, out=outs)
+        eg.engram_gate_forward(bufs["mem"], h, layer.wk, layer.wv, layer.gq, layer.gk, cfg.eps, out=outs,
+                               key_norm=layer.key_norm)
         if ev is not None:
             ev[4].record()
 
@@ -484,7 +499,7 @@ def main():
     per = {n: sum(evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(args.steps)) / args.steps
            for k, n in enumerate(names)}
 
-    work = algorithmic(cfg)
+    work = algorithmic(cfg, args.shared_wv)
     kernels = {}
     for n in names:
         s = per[n] * 1e-3
@@ -501,7 +516,8 @@ def main():
     else:
         peak, dtype = PEAK_FP32_TFLOPS, "f32"
     achieved = work["gate"]["flops"] / gate_s / 1e12
-    traffic = measured_traffic(cfg) if cfg.dtype == "bf16" else None
+    default_gate = not args.shared_wv and args.key_norm == "memory"
+    traffic = measured_traffic(cfg) if cfg.dtype == "bf16" and default_gate else None
     roofline = {"kernel": "engram_gate_forward: gate_prep_kernel + gate_persistent_kernel "
                           "(events bracket both; the prep kernel is ~1% of the call)",
                 "bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
@@ -517,7 +533,7 @@ def main():
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": dtype, "data": "synthetic (seeded Zipf ids, counter-generated tables/weights/hidden)",
-        "config": workload_desc(cfg),
+        "config": workload_desc(cfg, args),
         "wall_s_timed": round(t_wall, 4),
         "cache_flush_mb_between_steps": args.flush_mb,
         "kernels": kernels,

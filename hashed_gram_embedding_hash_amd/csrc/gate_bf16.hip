@@ -171,16 +171,21 @@ struct Tile {
   int phase, m, ttile, ftile;
 };
 
-// Tile q of queue x; false once the queue is exhausted.
+// Tile q of queue x; false once the queue is exhausted.  SHAREDV (all branches share
+// W_V): one V tile per (token tile, feature tile) serves every branch, so the V phase
+// has n_branch times fewer tiles; its tiles carry m = 0.
+template <bool SHAREDV>
 __device__ __forceinline__ bool decode_tile(const GateArgs& a, int x, int q, Tile& t) {
   const int n_tt = a.n_ttiles > x ? (a.n_ttiles - x + NQ - 1) / NQ : 0;  // token tiles of queue x
   const int per_tt = a.n_branch * a.n_ftiles;
-  const int per_phase = n_tt * per_tt;
-  if (q >= 2 * per_phase) return false;
-  t.phase = q >= per_phase ? PHASE_V : PHASE_K;
-  const int r = q - t.phase * per_phase;
-  const int tl = r / per_tt;
-  const int r2 = r - tl * per_tt;
+  const int per_k = n_tt * per_tt;
+  const int per_v = SHAREDV ? n_tt * a.n_ftiles : per_k;
+  if (q >= per_k + per_v) return false;
+  t.phase = q >= per_k ? PHASE_V : PHASE_K;
+  const int r = q - (t.phase == PHASE_V ? per_k : 0);
+  const int per = (SHAREDV && t.phase == PHASE_V) ? a.n_ftiles : per_tt;
+  const int tl = r / per;
+  const int r2 = r - tl * per;
   t.m = r2 / a.n_ftiles;
   t.ftile = r2 - t.m * a.n_ftiles;
   t.ttile = tl * NQ + x;
@@ -194,8 +199,11 @@ __device__ __forceinline__ bool decode_tile(const GateArgs& a, int x, int q, Til
 //           for them;
 //   KEYP    the paper's key placement, k = RMSNorm_gk(W_K e) with gk over d_model: the
 //           K tiles run on the raw W_K, their epilogue weights h_f by gq_f gk_f (from
-//           LDS) and also reduces sum_f k_f^2, which takes the place of the e^2 partial.
-template <bool VALUES, bool KEYP>
+//           LDS) and also reduces sum_f k_f^2, which takes the place of the e^2 partial;
+//   SHAREDV every branch uses the same W_V (section 2.4, Eq. (6)): a V tile computes
+//           W_V e once, waits for the gates of all branches, and runs one epilogue per
+//           branch, loading that branch's h tile into the ring between them.
+template <bool VALUES, bool KEYP, bool SHAREDV>
 __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, char* smem, int x,
                                           int& next_claim) {
   const int PHASE = tile.phase;
@@ -222,9 +230,12 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
     // completes behind the main loop
     if (tid == 0) {
       int spin = 0;
-      while (__hip_atomic_load(done, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.n_ftiles + 1 &&
-             ++spin < SPIN_LIMIT)
-        __builtin_amdgcn_s_sleep(1);
+      for (int mb = SHAREDV ? 0 : m; mb < (SHAREDV ? a.n_branch : m + 1); ++mb) {
+        const int32_t* dn = a.counters + NQ + mb * a.n_ttiles + tile.ttile;
+        while (__hip_atomic_load(dn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.n_ftiles + 1 &&
+               ++spin < SPIN_LIMIT)
+          __builtin_amdgcn_s_sleep(1);
+      }
     }
     lds_barrier();  // the gate loads below are issued only after the count is seen
     if (t0 + tid < n_tok) alpha = ld_coherent(a.alpha + (int64_t)m * n_tok + t0 + tid);
@@ -657,33 +668,6 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
       if (etid == 0) __hip_atomic_fetch_add(done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   } else {
-#pragma unroll
-    for (int j = 0; j < MT; ++j) {
-      const int tl = ewt * WT + j * 32 + (elane & 31);
-      const float alpha = s_alpha[tl];
-      // all eight cells of this token column are read before any is written, so the
-      // reads are issued back to back (a write could alias a later read otherwise)
-      u32x4 hv[MF][2];
-#pragma unroll
-      for (int i = 0; i < MF; ++i)
-#pragma unroll
-        for (int gp = 0; gp < 2; ++gp)
-          hv[i][gp] = *reinterpret_cast<const u32x4*>(
-              smem + ENGRAM_HOFF(tl, (ewf * WF + i * 32 + gp * 16 + hsel) >> 3));
-#pragma unroll
-      for (int i = 0; i < MF; ++i) {
-#pragma unroll
-        for (int gp = 0; gp < 2; ++gp) {
-          u32x4 ov;
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            ov[q] = pack_bf16(bf16_lo(hv[i][gp][q]) + alpha * acc[i][j][gp * 8 + 2 * q],
-                              bf16_hi(hv[i][gp][q]) + alpha * acc[i][j][gp * 8 + 2 * q + 1]);
-          *reinterpret_cast<u32x4*>(smem + ENGRAM_HOFF(tl, (ewf * WF + i * 32 + gp * 16 + hsel) >> 3)) = ov;
-        }
-      }
-    }
-    lds_barrier();
     // Stream the tile out: 16-B chunk p = 256 i + tid is token tl = p / 32, physical
     // chunk p % 32; eight LDS reads are issued ahead of their eight stores.
     const bool full = t0 + BT <= n_tok && f0 + BF <= d_model;
@@ -709,14 +693,22 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
         }
       }
     };
-    stream_out((uint16_t*)a.out[m]);
-    if (VALUES && a.vout[m] != nullptr) {
-      // the gated values alpha * v, staged through the same LDS tile
-      lds_barrier();
+    // The epilogue of branch mb: its h tile is in the ring's quarter slots, its gates in
+    // s_alpha.
+    auto v_epilogue = [&](int mb) {
 #pragma unroll
       for (int j = 0; j < MT; ++j) {
         const int tl = ewt * WT + j * 32 + (elane & 31);
         const float alpha = s_alpha[tl];
+        // all eight cells of this token column are read before any is written, so the
+        // reads are issued back to back (a write could alias a later read otherwise)
+        u32x4 hv[MF][2];
+#pragma unroll
+        for (int i = 0; i < MF; ++i)
+#pragma unroll
+          for (int gp = 0; gp < 2; ++gp)
+            hv[i][gp] = *reinterpret_cast<const u32x4*>(
+                smem + ENGRAM_HOFF(tl, (ewf * WF + i * 32 + gp * 16 + hsel) >> 3));
 #pragma unroll
         for (int i = 0; i < MF; ++i) {
 #pragma unroll
@@ -724,20 +716,78 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
             u32x4 ov;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-              ov[q] = pack_bf16(alpha * acc[i][j][gp * 8 + 2 * q], alpha * acc[i][j][gp * 8 + 2 * q + 1]);
+              ov[q] = pack_bf16(bf16_lo(hv[i][gp][q]) + alpha * acc[i][j][gp * 8 + 2 * q],
+                                bf16_hi(hv[i][gp][q]) + alpha * acc[i][j][gp * 8 + 2 * q + 1]);
             *reinterpret_cast<u32x4*>(smem + ENGRAM_HOFF(tl, (ewf * WF + i * 32 + gp * 16 + hsel) >> 3)) = ov;
           }
         }
       }
       lds_barrier();
-      stream_out((uint16_t*)a.vout[m]);
+      stream_out((uint16_t*)a.out[mb]);
+      if (VALUES && a.vout[mb] != nullptr) {
+        // the gated values alpha * v, staged through the same LDS tile
+        lds_barrier();
+#pragma unroll
+        for (int j = 0; j < MT; ++j) {
+          const int tl = ewt * WT + j * 32 + (elane & 31);
+          const float alpha = s_alpha[tl];
+#pragma unroll
+          for (int i = 0; i < MF; ++i) {
+#pragma unroll
+            for (int gp = 0; gp < 2; ++gp) {
+              u32x4 ov;
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                ov[q] = pack_bf16(alpha * acc[i][j][gp * 8 + 2 * q], alpha * acc[i][j][gp * 8 + 2 * q + 1]);
+              *reinterpret_cast<u32x4*>(smem + ENGRAM_HOFF(tl, (ewf * WF + i * 32 + gp * 16 + hsel) >> 3)) = ov;
+            }
+          }
+        }
+        lds_barrier();
+        stream_out((uint16_t*)a.vout[mb]);
+      }
+    };
+    if constexpr (!SHAREDV) {
+      v_epilogue(m);
+    } else {
+      for (int mb = 0; mb < a.n_branch; ++mb) {
+        if (mb > 0) {
+          // branch mb's h tile and gates replace branch mb - 1's, once every read of the
+          // tile is done
+          lds_barrier();
+          // the h-tile loads of the main loop, with every address re-derived here from
+          // the opaque thread id (reusing the main loop's would keep them live through it)
+          const uint16_t* hb = (const uint16_t*)a.h[mb] + t0 * d_model;
+          const int ew = __builtin_amdgcn_readfirstlane(etid >> 6);
+          const int blim = (int)(n_tok - 1 - t0);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t dst = (uint32_t)(uintptr_t)(lds_ptr)smem + (uint32_t)(((q0slot + q) % NSLOT) * SLOT_BYTES);
+#pragma unroll
+            for (int i = 0; i < G_INSTR; ++i) {
+              const int blk = ew * G_INSTR + i;
+              const int tl = q * 64 + blk * 2 + (elane >> 5);
+              const int c = (elane & 31) ^ (tl & 31);
+              const int tr = tl < blim ? tl : blim;
+              int f = f0 + c * 8;
+              f = f < d_model ? f : 0;
+              dma16(hb + (uint32_t)tr * (uint32_t)d_model + f, dst + (uint32_t)(blk * 1024));
+            }
+          }
+          const float al = t0 + etid < n_tok ? ld_coherent(a.alpha + (int64_t)mb * n_tok + t0 + etid) : 0.f;
+          wait_vm_lgkm0<0>();
+          s_alpha[etid] = al;
+          lds_barrier();
+        }
+        v_epilogue(mb);
+      }
     }
   }
 #undef ENGRAM_HOFF
 #undef ENGRAM_QSLOT
 }
 
-template <bool VALUES, bool KEYP>
+template <bool VALUES, bool KEYP, bool SHAREDV>
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gate_persistent_kernel(const GateArgs a) {
   // the operand ring, then the h tile and the epilogue scratch; between tiles its
@@ -751,10 +801,10 @@ void gate_persistent_kernel(const GateArgs a) {
     if (threadIdx.x == 0) *s_tile = claim;
     lds_barrier();
     Tile t;
-    const bool have = decode_tile(a, x, *s_tile, t);
+    const bool have = decode_tile<SHAREDV>(a, x, *s_tile, t);
     lds_barrier();  // every thread has read the tile number before the ring is refilled
     if (!have) break;
-    gate_tile<VALUES, KEYP>(a, t, smem, x, claim);
+    gate_tile<VALUES, KEYP, SHAREDV>(a, t, smem, x, claim);
     // LDS free for the next tile.  A full barrier: letting a V tile's 128 KB of output
     // stores drain behind the next tile's operand loads measured 8 % slower than
     // finishing them first.
@@ -868,17 +918,24 @@ void launch_gate_bf16(const GateArgs& a_in, hipStream_t s) {
 
   int grid = cu_count() / NQ * NQ;
   if (grid < NQ) grid = NQ;
-  bool values = false;
-  for (int m = 0; m < a.n_branch; ++m) values = values || a.vout[m] != nullptr;
+  bool values = false, shared_v = a.n_branch > 1;
+  for (int m = 0; m < a.n_branch; ++m) {
+    values = values || a.vout[m] != nullptr;
+    shared_v = shared_v && a.wv[m] == a.wv[0];
+  }
   const dim3 g((unsigned)grid), b(NTHR);
-  if (values && keyp)
-    hipLaunchKernelGGL((gate_persistent_kernel<true, true>), g, b, 0, s, a);
-  else if (values)
-    hipLaunchKernelGGL((gate_persistent_kernel<true, false>), g, b, 0, s, a);
-  else if (keyp)
-    hipLaunchKernelGGL((gate_persistent_kernel<false, true>), g, b, 0, s, a);
-  else
-    hipLaunchKernelGGL((gate_persistent_kernel<false, false>), g, b, 0, s, a);
+#define ENGRAM_GATE_LAUNCH(V_, K_, S_)                                                     \
+  if (values == V_ && keyp == K_ && shared_v == S_)                                        \
+    hipLaunchKernelGGL((gate_persistent_kernel<V_, K_, S_>), g, b, 0, s, a);
+  ENGRAM_GATE_LAUNCH(false, false, false)
+  ENGRAM_GATE_LAUNCH(false, false, true)
+  ENGRAM_GATE_LAUNCH(false, true, false)
+  ENGRAM_GATE_LAUNCH(false, true, true)
+  ENGRAM_GATE_LAUNCH(true, false, false)
+  ENGRAM_GATE_LAUNCH(true, false, true)
+  ENGRAM_GATE_LAUNCH(true, true, false)
+  ENGRAM_GATE_LAUNCH(true, true, true)
+#undef ENGRAM_GATE_LAUNCH
 }
 
 }  // namespace engram

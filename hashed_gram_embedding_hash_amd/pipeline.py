@@ -5,7 +5,8 @@ compress the raw ids, hash every suffix n-gram into its tables, gather and
 concatenate the rows, then gate the memory against each branch's hidden
 state and add it to the residual.  This class only owns the parameters and
 the intermediate device buffers and issues the four calls on one stream; the
-arithmetic is in the HIP kernels.
+arithmetic is in the HIP kernels.  Passing one W_V tensor for every branch
+(section 2.4, Eq. (6)) lets the gate compute W_V e once for all of them.
 """
 from __future__ import annotations
 
@@ -14,14 +15,14 @@ from typing import List, Optional, Sequence
 import numpy as np
 import torch
 
-from . import (engram_compress, engram_gate_forward, engram_gather, engram_hash)
+from . import (KEY_NORM_MEMORY, engram_compress, engram_gate_forward, engram_gather, engram_hash)
 
 
 class EngramLayer:
     def __init__(self, cmap: torch.Tensor, orders: Sequence[int], heads: int, mult: np.ndarray,
                  tables: Sequence[torch.Tensor], wk: Sequence[torch.Tensor], wv: Sequence[torch.Tensor],
                  gq: Sequence[torch.Tensor], gk: Sequence[torch.Tensor], eps: float = 1e-6,
-                 pad_id: Optional[int] = None):
+                 pad_id: Optional[int] = None, key_norm: int = KEY_NORM_MEMORY):
         self.cmap = cmap
         self.orders = tuple(orders)
         self.heads = heads
@@ -30,6 +31,7 @@ class EngramLayer:
         self.rows = np.array([t.shape[0] for t in tables], dtype=np.uint32)
         self.wk, self.wv, self.gq, self.gk = list(wk), list(wv), list(gq), list(gk)
         self.eps = eps
+        self.key_norm = key_norm
         # default padding id: one past the largest canonical id
         self.pad_id = int(cmap.max().item()) + 1 if pad_id is None else pad_id
         self._bufs = {}
@@ -61,4 +63,4 @@ class EngramLayer:
                     stream=stream)
         engram_gather(b["idx"], self.tables, out=b["mem"], stream=stream)
         return engram_gate_forward(b["mem"], h, self.wk, self.wv, self.gq, self.gk, self.eps, out=out,
-                                   gate_out=gate_out, stream=stream)
+                                   gate_out=gate_out, key_norm=self.key_norm, stream=stream)

@@ -253,6 +253,81 @@ def test_gate_fp32_projected_key_tiny():
     assert err <= 1e-5 and aerr <= 1e-5
 
 
+def _shared_wv_inputs(cfg, n_tok, seed, key_norm):
+    rng = np.random.default_rng(seed)
+    idx = rng.integers(0, cfg.rows, (n_tok, cfg.n_tables)).astype(np.int32)
+    e_o = oracle_memory(cfg, idx)
+    e_d = torch.from_numpy(e_o.view(np.int16)).to(DEV).view(torch.bfloat16)
+    tokens = rng.choice(1 << 20, n_tok, replace=False).astype(np.int64)
+    hs = [synth.hidden_rows(cfg, m, torch.from_numpy(tokens)).to(DEV) for m in range(cfg.n_branch)]
+    wks = [synth.weights(cfg, m, DEV)[0] for m in range(cfg.n_branch)]
+    wv0 = synth.weights(cfg, 0, DEV)[1]                 # one W_V for every branch (Eq. 6)
+    proj = key_norm == eg.KEY_NORM_PROJECTED
+    gs = [synth.gains(cfg, m, DEV, projected_key=proj) for m in range(cfg.n_branch)]
+    return e_o, e_d, tokens, hs, wks, wv0, gs
+
+
+def _oracle_shared_wv(cfg, m, e_o, tokens, wv0, key_norm):
+    h = host_view(synth.hidden_rows(cfg, m, torch.from_numpy(tokens)))
+    wk = host_view(synth.weights(cfg, m)[0])
+    proj = key_norm == eg.KEY_NORM_PROJECTED
+    gq, gk = (host_view(x) for x in synth.gains(cfg, m, projected_key=proj))
+    return oracle.gate(e_o, h, wk, host_view(wv0.cpu()), gq, gk, cfg.eps, oracle.BF16, with_value=True,
+                       key_norm=key_norm)
+
+
+@pytest.mark.parametrize("key_norm", [eg.KEY_NORM_MEMORY, eg.KEY_NORM_PROJECTED])
+def test_gate_bf16_shared_wv_equals_copies_and_oracle(key_norm):
+    """Eq. (6): four branches passing the same W_V pointer take the shared path (one W_V
+    product per tile for all branches); passing four copies takes the per-branch path.
+    Both must agree bit for bit (same tile arithmetic), values included, and match the
+    oracle; 300 tokens = one full and one ragged token tile."""
+    cfg = synth.CONFIGS["multi"].replace(table_std=0.5)
+    n_tok = 300
+    say(f"gate bf16 shared W_V, key_norm {key_norm}")
+    e_o, e_d, tokens, hs, wks, wv0, gs = _shared_wv_inputs(cfg, n_tok, 17 + key_norm, key_norm)
+    M = cfg.n_branch
+    runs = {}
+    for name, wvs in (("shared", [wv0] * M), ("copies", [wv0.clone() for _ in range(M)])):
+        alpha = torch.empty((M, n_tok), dtype=torch.float32, device=DEV)
+        vals = [torch.empty_like(h) for h in hs]
+        out = eg.engram_gate_forward(e_d, hs, wks, wvs, [g[0] for g in gs], [g[1] for g in gs], cfg.eps,
+                                     gate_out=alpha, value_out=vals, key_norm=key_norm)
+        torch.cuda.synchronize()
+        runs[name] = (out, alpha, vals)
+    for m in range(M):
+        assert torch.equal(runs["shared"][0][m].view(torch.int16), runs["copies"][0][m].view(torch.int16)), m
+        assert torch.equal(runs["shared"][2][m].view(torch.int16), runs["copies"][2][m].view(torch.int16)), m
+    assert torch.equal(runs["shared"][1], runs["copies"][1])
+    out, alpha, vals = runs["shared"]
+    for m in range(M):
+        out_o, alpha_o, val_o = _oracle_shared_wv(cfg, m, e_o, tokens, wv0, key_norm)
+        err = rel_err(out[m].float().cpu().numpy(), out_o)
+        verr = rel_err(vals[m].float().cpu().numpy(), val_o)
+        aerr = np.abs(alpha[m].cpu().numpy() - alpha_o).max()
+        say(f"  branch {m}: out rel err {err:.2e}, value rel err {verr:.2e}, alpha abs err {aerr:.2e}")
+        assert err <= 1e-2 and verr <= 1e-2 and aerr <= ALPHA_TOL_BF16
+
+
+def test_gate_bf16_shared_wv_in_place_large_shape():
+    """Shared W_V with out = h (in place), 2 branches at d_model 4096 (the large
+    configuration's shape), 1000 tokens: four token tiles, the last ragged."""
+    cfg = synth.CONFIGS["large"].replace(table_std=0.5)
+    n_tok = 1000
+    say("gate bf16 shared W_V in place, large shape")
+    e_o, e_d, tokens, hs, wks, wv0, gs = _shared_wv_inputs(cfg, n_tok, 19, eg.KEY_NORM_MEMORY)
+    h_in = [h.clone() for h in hs]
+    eg.engram_gate_forward(e_d, h_in, wks, [wv0] * cfg.n_branch, [g[0] for g in gs], [g[1] for g in gs],
+                           cfg.eps, out=h_in)
+    torch.cuda.synchronize()
+    sample = np.random.default_rng(20).choice(n_tok, 96, replace=False)
+    for m in range(cfg.n_branch):
+        out_o, _, _ = _oracle_shared_wv(cfg, m, e_o[sample], tokens[sample], wv0, eg.KEY_NORM_MEMORY)
+        err = rel_err(h_in[m][torch.from_numpy(sample).to(DEV)].float().cpu().numpy(), out_o)
+        say(f"  branch {m}: out rel err {err:.2e}")
+        assert err <= 1e-2
+
+
 def test_gate_bf16_scratch_shared_across_streams_and_sizes():
     """The gate keeps one scratch buffer per device.  Calls alternating between two
     streams, with a larger shape in between (the buffer grows), must give exactly the
