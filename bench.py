@@ -53,6 +53,8 @@ def parse():
     p.add_argument("--offload-rows", type=int, default=0,
                    help="offload config: rows per table (default: 100B parameters, scaled to 60%% of free host RAM)")
     p.add_argument("--offload-reps", type=int, default=3)
+    p.add_argument("--offload-cache-gb", type=float, default=1.0,
+                   help="HBM cache of the rows most frequent in the decode histories (0: off)")
     p.add_argument("--offload-host-gb", type=float, default=48.0,
                    help="offload config: cap on pinned host table bytes (the GPU's system-memory aperture is "
                         "shared with the runtime; on the measured host, pinning beyond ~64 GB fails)")
@@ -142,7 +144,9 @@ def run_offload(args):
     the rows of step s+1 are hashed and fetched on a side stream while step s gates.
     The same two-stream pipeline runs once with the tables in pinned host memory
     (engram_prefetch_host over PCIe) and once with the same tables in HBM
-    (engram_gather); the overhead is the ratio of the steady-state step times."""
+    (engram_gather); the overhead is the ratio of the steady-state step times.  A third
+    run puts an HBM cache of the rows most frequent in the sequences' histories in front
+    of the host tables (engram_prefetch_host_cached)."""
     import ctypes
     import numpy as np
     import torch
@@ -209,10 +213,40 @@ def run_offload(args):
         h_a = [arr([h[s]]) for s in range(S)]
         chk = lambda st: st == 0 or eg._check(st)
 
+        # the HBM row cache: the rows most frequent in the histories of the sequences
+        cache = None
+        modes = ("hbm", "host")
+        if args.offload_cache_gb > 0:
+            capacity = int(args.offload_cache_gb * 1e9 / (cfg.n_tables * row_bytes))
+            t_sel = time.perf_counter()
+            hist_idx = eg.engram_hash(ids, cfg.orders, cfg.heads, mult, rows_u32, cfg.vocab_c, t_begin=0, t_count=T0)
+            hot = eg.engram_cache_select(hist_idx.cpu().numpy(), capacity)
+            del hist_idx
+            t_sel = time.perf_counter() - t_sel
+            t_build = time.perf_counter()
+            ctab, crows = eg.engram_cache_build(haddr, hrows, cfg.w, torch.bfloat16, hot)
+            t_build = time.perf_counter() - t_build
+            cache = {"capacity": capacity, "slots": ctab.shape[1], "table": ctab, "rows": crows,
+                     "hits": torch.zeros(1, dtype=torch.int32, device=dev),
+                     "select_s": round(t_sel, 2), "build_s": round(t_build, 2),
+                     "hbm_bytes": ctab.numel() * 4 + crows.numel() * 2}
+            modes = ("hbm", "host", "cached")
+            say(f"row cache: {capacity} rows per table ({cache['hbm_bytes'] / 1e9:.2f} GB of HBM), "
+                f"selected in {t_sel:.1f} s, built in {t_build:.1f} s")
+
+        def cached_prefetch(buf, st, hits=None):
+            chk(L.engram_prefetch_host_cached(idx[buf].data_ptr(), B, cfg.n_tables, hptrs, rows64.ctypes.data, cfg.w,
+                                              eg.BF16, P(cache["table"].data_ptr()), cache["slots"],
+                                              P(cache["rows"].data_ptr()), stg[buf].data_ptr(),
+                                              None if hits is None else P(hits.data_ptr()), None, st))
+
         def fetch(mode, s, buf, stream):
             st = ss if stream is side else ms
             chk(L.engram_hash(ids.data_ptr(), B, ids.shape[1], T0 + s, 1, orders_a.ctypes.data, len(cfg.orders),
                               cfg.heads, mult_a.ctypes.data, rows_u32.ctypes.data, cfg.vocab_c, idx[buf].data_ptr(), st))
+            if mode == "cached":
+                cached_prefetch(buf, st)
+                return
             fn = L.engram_prefetch_host if mode == "host" else L.engram_gather
             chk(fn(idx[buf].data_ptr(), B, cfg.n_tables, hptrs if mode == "host" else dptrs, rows64.ctypes.data,
                    cfg.w, eg.BF16, stg[buf].data_ptr(), None, st))
@@ -256,11 +290,11 @@ def run_offload(args):
             return a.elapsed_time(b) * 1e3 / n
 
         host_us = []
-        for mode in ("hbm", "host"):
+        for mode in modes:
             pipeline(mode)                             # warm-up
-        steps = {"hbm": [], "host": []}
+        steps = {m: [] for m in modes}
         for _ in range(args.offload_reps):
-            for mode in ("hbm", "host"):
+            for mode in modes:
                 steps[mode].append(pipeline(mode))
         med = {k: float(np.median(v)) for k, v in steps.items()}
         comp = {
@@ -276,6 +310,16 @@ def run_offload(args):
                                                                          stg[0].data_ptr(), None, ms))),
             "gate_us": serial(lambda s: gate(s, 0)),
         }
+        if cache is not None:
+            # hit rate over every decode step's indices
+            for s_ in range(S):
+                chk(L.engram_hash(ids.data_ptr(), B, ids.shape[1], T0 + s_, 1, orders_a.ctypes.data, len(cfg.orders),
+                                  cfg.heads, mult_a.ctypes.data, rows_u32.ctypes.data, cfg.vocab_c, idx[0].data_ptr(),
+                                  ms))
+                cached_prefetch(0, ms, cache["hits"])
+            torch.cuda.synchronize()
+            cache["hit_rate"] = int(cache["hits"].item()) / (S * B * cfg.n_tables)
+            comp["prefetch_cached_us"] = serial(lambda s: cached_prefetch(0, ms))
         pcie_bytes = B * cfg.n_tables * row_bytes
         comp["prefetch_host_GBps"] = pcie_bytes / (comp["prefetch_host_us"] * 1e-6) / 1e9
         # reference: pinned host-to-device copy of one contiguous 256 MiB block
@@ -302,6 +346,15 @@ def run_offload(args):
             "components_serial": {k: round(v, 2) for k, v in comp.items()},
             "pcie_bytes_per_step": pcie_bytes,
         }
+        if cache is not None:
+            res["row_cache"] = {
+                "overhead_pct": round(100.0 * (med["cached"] / med["hbm"] - 1.0), 2),
+                "rows_per_table": cache["capacity"], "hash_slots_per_table": cache["slots"],
+                "hbm_GB": round(cache["hbm_bytes"] / 1e9, 3),
+                "selected_from": f"hash indices of the {B} x {T0}-token histories",
+                "hit_rate": round(cache["hit_rate"], 4),
+                "pcie_bytes_per_step": round(pcie_bytes * (1.0 - cache["hit_rate"])),
+                "select_s": cache["select_s"], "build_s": cache["build_s"]}
         print(json.dumps(res), flush=True)
     finally:
         dtabs.clear()

@@ -15,7 +15,9 @@ The functions carry the C names:
 * ``engram_conv_forward`` -- the short depthwise causal convolution over the
   gated values (section 2.3, Eq. 5);
 * ``engram_prefetch_host`` -- the same gather from pinned host-memory tables
-  over PCIe (section 2.5, Figure 2(b); section 6.4).
+  over PCIe (section 2.5, Figure 2(b); section 6.4);
+* ``engram_cache_select`` / ``engram_cache_build`` / ``engram_prefetch_host_cached``
+  -- an HBM cache of the most frequent rows in front of those tables (section 2.5).
 
 There is no fallback: if the library is missing or fails to load, every call
 raises.
@@ -45,7 +47,7 @@ _STATUS = {0: "ENGRAM_OK", 1: "ENGRAM_ERR_INVALID_ARG", 2: "ENGRAM_ERR_UNSUPPORT
 EXPORTS = (
     "engram_last_error", "engram_version", "engram_compress", "engram_hash", "engram_gather",
     "engram_gate_forward", "engram_conv_forward", "engram_prefetch_host", "engram_host_alloc",
-    "engram_host_free",
+    "engram_host_free", "engram_cache_select", "engram_cache_build", "engram_prefetch_host_cached",
 )
 
 
@@ -83,8 +85,12 @@ def lib() -> ctypes.CDLL:
         L.engram_prefetch_host.argtypes = [P, i64, i32, P, P, i32, i32, P, P, P]
         L.engram_host_alloc.argtypes = [ctypes.c_size_t, ctypes.POINTER(ctypes.c_void_p)]
         L.engram_host_free.argtypes = [P]
+        L.engram_cache_select.argtypes = [P, i64, i32, i32, P]
+        L.engram_cache_build.argtypes = [P, P, i32, i32, i32, P, i32, i32, P, P, P]
+        L.engram_prefetch_host_cached.argtypes = [P, i64, i32, P, P, i32, i32, P, i32, P, P, P, P, P]
         for f in ("engram_compress", "engram_hash", "engram_gather", "engram_gate_forward",
-                  "engram_conv_forward", "engram_prefetch_host", "engram_host_alloc", "engram_host_free"):
+                  "engram_conv_forward", "engram_prefetch_host", "engram_host_alloc", "engram_host_free",
+                  "engram_cache_select", "engram_cache_build", "engram_prefetch_host_cached"):
             getattr(L, f).restype = st
         _lib = L
     return _lib
@@ -286,6 +292,75 @@ def engram_prefetch_host(idx, host_tables: Sequence, rows: Sequence[int], w: int
                                       rows_a.ctypes.data, w, BF16 if dtype == torch.bfloat16 else F32,
                                       _dev(staging, "staging", dtype), _opt(err_count, "err_count", torch.int32),
                                       _stream(stream)))
+    return staging
+
+
+def _host_table_ptrs(host_tables):
+    import torch
+    ptrs = []
+    for t in host_tables:
+        if torch.is_tensor(t):
+            if t.is_cuda or not t.is_pinned():
+                raise ValueError("host tables must be pinned host memory")
+            ptrs.append(t.data_ptr())
+        else:
+            ptrs.append(int(t))
+    return ptrs
+
+
+def engram_cache_select(idx, capacity: int):
+    """Per table, the ``capacity`` most frequent rows of the sample ``idx`` [n, n_tables]
+    (host array or tensor, int32); ties to the smaller row, -1 padding.  Returns a numpy
+    int32 array [n_tables, capacity].  Pure host computation."""
+    import numpy as np
+    import torch
+    if torch.is_tensor(idx):
+        idx = idx.detach().cpu().numpy()
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    n, n_tables = idx.shape
+    hot = np.empty((n_tables, capacity), dtype=np.int32)
+    _check(lib().engram_cache_select(idx.ctypes.data, n, n_tables, capacity, hot.ctypes.data))
+    return hot
+
+
+def engram_cache_build(host_tables: Sequence, rows: Sequence[int], w: int, dtype, hot, slots: Optional[int] = None,
+                       stream=None):
+    """Build the HBM row cache for the rows ``hot`` [n_tables, capacity] (from
+    ``engram_cache_select``).  Returns (table int32 [n_tables, slots, 2], cache_rows
+    [capacity, n_tables * w]) on the current device; the call waits for the build."""
+    import numpy as np
+    import torch
+    hot = np.ascontiguousarray(hot, dtype=np.int32)
+    n_tables, capacity = hot.shape
+    if slots is None:
+        slots = 1
+        while slots < 2 * capacity:
+            slots *= 2
+    rows_a = np.ascontiguousarray(rows, dtype=np.int64)
+    dev = torch.device("cuda", torch.cuda.current_device())
+    table = torch.empty((n_tables, slots, 2), dtype=torch.int32, device=dev)
+    cache_rows = torch.empty((capacity, n_tables * w), dtype=dtype, device=dev)
+    _check(lib().engram_cache_build(_ptr_array(_host_table_ptrs(host_tables)), rows_a.ctypes.data, n_tables, w,
+                                    BF16 if dtype == torch.bfloat16 else F32, hot.ctypes.data, capacity, slots,
+                                    _dev(table, "table", torch.int32), _dev(cache_rows, "cache_rows", dtype),
+                                    _stream(stream)))
+    return table, cache_rows
+
+
+def engram_prefetch_host_cached(idx, host_tables: Sequence, rows: Sequence[int], w: int, dtype, table, cache_rows,
+                                staging=None, hits=None, err_count=None, stream=None):
+    """``engram_prefetch_host`` through the HBM row cache of ``engram_cache_build``."""
+    import numpy as np
+    import torch
+    n_tok, n_tables = idx.shape
+    rows_a = np.ascontiguousarray(rows, dtype=np.int64)
+    if staging is None:
+        staging = torch.empty((n_tok, n_tables * w), dtype=dtype, device=idx.device)
+    _check(lib().engram_prefetch_host_cached(
+        _dev(idx, "idx", torch.int32), n_tok, n_tables, _ptr_array(_host_table_ptrs(host_tables)),
+        rows_a.ctypes.data, w, BF16 if dtype == torch.bfloat16 else F32, _dev(table, "table", torch.int32),
+        table.shape[1], _dev(cache_rows, "cache_rows", dtype), _dev(staging, "staging", dtype),
+        _opt(hits, "hits", torch.int32), _opt(err_count, "err_count", torch.int32), _stream(stream)))
     return staging
 
 

@@ -280,6 +280,40 @@ engram_status engram_prefetch_host(const int32_t* idx, int64_t n_tok, int32_t n_
   return check_launch(fn);
 }
 
+engram_status engram_prefetch_host_cached(const int32_t* idx, int64_t n_tok, int32_t n_tables,
+                                          const void* const* host_tables, const int64_t* rows, int32_t w,
+                                          engram_dtype dtype, const void* table, int32_t slots,
+                                          const void* cache_rows, void* staging, int32_t* hits,
+                                          int32_t* err_count, hipStream_t stream) {
+  const char* fn = "engram_prefetch_host_cached";
+  const engram_status st = check_gather(fn, idx, n_tok, n_tables, host_tables, rows, w, dtype, staging);
+  if (st != ENGRAM_OK) return st;
+  int l2 = 0;
+  while (l2 < 31 && (1 << l2) < slots) ++l2;
+  if (slots < 2 || (1 << l2) != slots || l2 > 30)
+    return fail(ENGRAM_ERR_INVALID_ARG, "%s: slots %d must be a power of two", fn, slots);
+  if (table == nullptr || cache_rows == nullptr || !aligned(table, 8) || !aligned(cache_rows, 16))
+    return fail(ENGRAM_ERR_INVALID_ARG, "%s: null or misaligned cache table/rows", fn);
+  GatherArgs a;
+  memset(&a, 0, sizeof a);
+  for (int b = 0; b < n_tables; ++b) {
+    const void* d = mapped_host_pointer(host_tables[b]);
+    if (d == nullptr)
+      return fail(ENGRAM_ERR_INVALID_ARG, "%s: table %d is not pinned, device-mapped host memory", fn, b);
+    a.table[b] = (const char*)d;
+    a.rows[b] = rows[b];
+  }
+  if (n_tok == 0) return ENGRAM_OK;
+  a.idx = idx;
+  a.out = (char*)staging;
+  a.err_count = err_count;
+  a.n_tok = n_tok;
+  a.n_tables = n_tables;
+  a.chunks_per_row = (int32_t)(w * dtype_size(dtype) / 16);
+  launch_prefetch_cached(a, (const int2*)table, l2, (const char*)cache_rows, hits, stream);
+  return check_launch(fn);
+}
+
 engram_status engram_gate_forward(const void* mem, int64_t n_tok, int32_t d_mem, int32_t d_model,
                                   int32_t n_branch, const void* const* h, const void* const* wk,
                                   const void* const* wv, const void* const* gq,

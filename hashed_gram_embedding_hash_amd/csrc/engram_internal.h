@@ -45,6 +45,9 @@ struct GatherArgs {
 };
 // `host_source`: the tables are pinned host memory read over PCIe (launch tuned for that).
 void launch_gather(const GatherArgs& a, bool host_source, hipStream_t s);
+// prefetch from host tables through the HBM row cache (table: [n_tables][2^log2_slots])
+void launch_prefetch_cached(const GatherArgs& a, const int2* table, int log2_slots, const char* cache_rows,
+                            int32_t* hits, hipStream_t s);
 
 // ---------------------------------------------------------------- gate
 struct GateArgs {

@@ -211,6 +211,46 @@ engram_status engram_prefetch_host(const int32_t* idx, int64_t n_tok, int32_t n_
                                    engram_dtype dtype, void* staging, int32_t* err_count,
                                    hipStream_t stream);
 
+/*
+ * HBM cache of the hottest rows of host-resident tables -- section 2.5: n-gram
+ * frequencies follow a Zipf law, so keeping the most used rows in a faster tier
+ * (HBM, in front of the pinned host tables of Figure 2(b)) removes most of the
+ * prefetch's PCIe traffic.  Three calls:
+ *
+ * engram_cache_select (host only, no GPU work): per table b, the `capacity` rows
+ *   that occur most often in column b of the sample idx (host int32 [n][n_tables],
+ *   e.g. the hash indices of the sequences being decoded); ties go to the smaller
+ *   row, negative entries are ignored.  hot: host int32 [n_tables][capacity],
+ *   padded with -1 when a column has fewer distinct rows.
+ *
+ * engram_cache_build: builds, on `stream`, and waits for it to finish:
+ *   table:      device, [n_tables][slots] entries of two int32 {row, cache slot}
+ *               (8-byte aligned; slots a power of two above capacity), an open-
+ *               addressing hash table per table: the home entry of row r is the top
+ *               log2(slots) bits of r * 0x9E3779B1 mod 2^32, collisions probe
+ *               linearly, empty entries are {-1, -1};
+ *   cache_rows: device [capacity][n_tables * w] of `dtype` (16-byte aligned): cache
+ *               slot j of table b holds row hot[b][j] of host_tables[b] (zeros for -1).
+ *   host_tables are pinned, device-mapped host memory, as for engram_prefetch_host.
+ *   A hot row outside [0, rows[b]) is INVALID_ARG.
+ *
+ * engram_prefetch_host_cached: engram_prefetch_host through the cache: a (token,
+ *   table) whose row is in the cache is read from cache_rows, any other from the
+ *   host table over PCIe.  staging receives exactly engram_gather's result.
+ *   hits: device int32 counter incremented once per cached (token, table), or NULL;
+ *   err_count as for engram_gather.
+ */
+engram_status engram_cache_select(const int32_t* idx, int64_t n, int32_t n_tables, int32_t capacity,
+                                  int32_t* hot);
+engram_status engram_cache_build(const void* const* host_tables, const int64_t* rows, int32_t n_tables, int32_t w,
+                                 engram_dtype dtype, const int32_t* hot, int32_t capacity, int32_t slots,
+                                 void* table, void* cache_rows, hipStream_t stream);
+engram_status engram_prefetch_host_cached(const int32_t* idx, int64_t n_tok, int32_t n_tables,
+                                          const void* const* host_tables, const int64_t* rows, int32_t w,
+                                          engram_dtype dtype, const void* table, int32_t slots,
+                                          const void* cache_rows, void* staging, int32_t* hits,
+                                          int32_t* err_count, hipStream_t stream);
+
 /* Pinned, device-mapped host allocation for offloaded tables (hipHostMalloc,
  * hipHostMallocMapped | hipHostMallocPortable). *ptr is NULL on failure. */
 engram_status engram_host_alloc(size_t bytes, void** ptr);

@@ -581,3 +581,41 @@ def test_gate_value_out_then_conv_fp32_tiny():
     err = rel_err(_f64(out), want)
     say(f"  value rel err {verr:.2e}, out rel err {err:.2e}")
     assert verr <= 1e-5 and err <= 1e-5
+
+
+# ---------------------------------------------------------------------------
+# HBM cache of hot rows in front of host tables (section 2.5)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,w,capacity,slots", [
+    (torch.bfloat16, 80, 2000, None),   # 160-byte rows, hash table half full
+    (torch.bfloat16, 80, 1000, 1024),   # nearly full table: long probe chains
+    (torch.float32, 32, 300, None),     # 128-byte fp32 rows
+])
+def test_prefetch_host_cached_equals_gather(dtype, w, capacity, slots):
+    say(f"prefetch cached {dtype} w {w} capacity {capacity} slots {slots}")
+    rows, nt = 50_021, 16
+    g = torch.Generator().manual_seed(6)
+    tables = [torch.randn(rows, w, generator=g).to(dtype) for _ in range(nt)]
+    pinned = [t.pin_memory() for t in tables]
+    dev_t = [t.to(DEV) for t in tables]
+    rng = np.random.default_rng(7)
+    perm = rng.permutation(rows).astype(np.int32)
+    zipf = lambda n: perm[(rng.zipf(1.2, size=(n, nt)) - 1) % rows].astype(np.int32)
+    hot = eg.engram_cache_select(zipf(30_000), capacity)
+    table, cache_rows = eg.engram_cache_build(pinned, [rows] * nt, w, dtype, hot, slots=slots)
+    idx = zipf(3000)
+    idx[5, 3], idx[100, 15], idx[2999, 0] = rows, -1, 1 << 30   # out of range: zero rows, counted
+    idx_d = torch.from_numpy(idx).to(DEV)
+    e1 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    e2 = torch.zeros(1, dtype=torch.int32, device=DEV)
+    hits = torch.zeros(1, dtype=torch.int32, device=DEV)
+    want = eg.engram_gather(idx_d, dev_t, err_count=e1)
+    got = eg.engram_prefetch_host_cached(idx_d, pinned, [rows] * nt, w, dtype, table, cache_rows, hits=hits,
+                                         err_count=e2)
+    torch.cuda.synchronize()
+    view = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(got.view(view), want.view(view))
+    assert int(e1.item()) == int(e2.item()) == 3
+    expect_hits = sum(int(np.isin(idx[:, b], hot[b][hot[b] >= 0]).sum()) for b in range(nt))
+    say(f"  hits {int(hits.item())} of {idx.size} ({int(hits.item()) / idx.size:.1%})")
+    assert int(hits.item()) == expect_hits > 0
