@@ -12,7 +12,10 @@ dominant kernel (the gate) and the CPU oracle's tokens/s on a bounded sample.
     python bench.py --config offload         # decode steps: host-resident vs HBM-resident tables
 
 Between timed steps (outside the timed events) a scratch buffer larger than the
-last-level cache is rewritten, so every step starts with cold L2 and MALL.
+last-level cache is rewritten, so every step starts with cold L2 and MALL.  The
+step is timed twice: launched call by call (which gives the per-call breakdown
+and the gate's roofline), then captured once in a HIP graph and replayed (the
+reported value; --no-graph reports the eager step instead).
 """
 from __future__ import annotations
 
@@ -47,6 +50,9 @@ def parse():
                    help="every branch uses branch 0's W_V (the paper's Eq. 6): W_V e is computed once")
     p.add_argument("--key-norm", choices=("memory", "projected"), default="memory",
                    help="memory: k = W_K RMSNorm(e) (default); projected: k = RMSNorm(W_K e), Eq. 4")
+    p.add_argument("--no-graph", action="store_true",
+                   help="time the eagerly launched step only (default: the step is also captured in a HIP graph "
+                        "and the graph replay is the reported value)")
     p.add_argument("--no-conv", action="store_true",
                    help="skip the separate measurement of the short convolution (Eq. 5)")
     p.add_argument("--flush-mb", type=int, default=512, help="cache-flush buffer rewritten between steps (0: off)")
@@ -551,6 +557,39 @@ def main():
     names = ["compress", "hash", "gather", "gate"]
     per = {n: sum(evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(args.steps)) / args.steps
            for k, n in enumerate(names)}
+    ms_eager, wall_eager = ms_step, t_wall
+
+    # The same step captured once in a HIP graph and replayed: the five kernel launches
+    # (the gate is two) then cost one launch.  Two eager steps on the capture stream come
+    # first, so the gate's scratch is sized and last used on that stream (no allocation
+    # or cross-stream wait is recorded).
+    if not args.no_graph:
+        gs = torch.cuda.Stream()
+        gs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(gs):
+            step()
+            step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=gs):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(5):
+            graph.replay()
+        torch.cuda.synchronize()
+        gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        print(f"[bench] timing {args.steps} graph replays", file=sys.stderr, flush=True)
+        t_wall = time.perf_counter()
+        for i in range(args.steps):
+            if flush is not None:
+                flush.fill_(float(i))
+            gev[i][0].record()
+            graph.replay()
+            gev[i][1].record()
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter() - t_wall
+        ms_step = sum(a.elapsed_time(b) for a, b in gev) / args.steps
 
     work = algorithmic(cfg, args.shared_wv)
     kernels = {}
@@ -584,10 +623,13 @@ def main():
         "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "step_launch": "eager" if args.no_graph else "hip graph replay (one launch per step)",
+        "ms_per_step_eager": round(ms_eager, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": dtype, "data": "synthetic (seeded Zipf ids, counter-generated tables/weights/hidden)",
         "config": workload_desc(cfg, args),
         "wall_s_timed": round(t_wall, 4),
+        "wall_s_timed_eager": round(wall_eager, 4),
         "cache_flush_mb_between_steps": args.flush_mb,
         "kernels": kernels,
         "roofline": roofline,
