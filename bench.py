@@ -12,10 +12,11 @@ dominant kernel (the gate) and the CPU oracle's tokens/s on a bounded sample.
     python bench.py --config offload         # decode steps: host-resident vs HBM-resident tables
 
 Between timed steps (outside the timed events) a scratch buffer larger than the
-last-level cache is rewritten, so every step starts with cold L2 and MALL.  The
-step is timed twice: launched call by call (which gives the per-call breakdown
-and the gate's roofline), then captured once in a HIP graph and replayed (the
-reported value; --no-graph reports the eager step instead).
+last-level cache is rewritten, so every step starts with cold L2 and MALL.  Each
+timed iteration runs the step twice, each time after the flush: launched call by
+call (events between the calls give the per-call breakdown and the gate's
+roofline), then as one replay of a HIP graph captured from it (the reported
+value; --no-graph reports the eager step instead).  wall_s_timed covers both.
 """
 from __future__ import annotations
 
@@ -89,8 +90,8 @@ def algorithmic(cfg, shared_wv=False):
     nv = 1 if shared_wv else M
     es = 4 if cfg.dtype == "f32" else 2
     return {
-        "compress": {"bytes": 8 * T},
-        "hash": {"bytes": 4 * T + 4 * nt * T},
+        # raw ids in, indices out (the 517-KB compression map stays in L2)
+        "compress_hash": {"bytes": 4 * T + 4 * nt * T},
         "gather": {"bytes": 4 * nt * T + 2 * dm * es * T},
         # weights once, memory vector once, hidden read + output written per branch
         "gate": {"flops": 2 * dm * d * (M + nv) * T,
@@ -518,22 +519,20 @@ def main():
     raw, h = inp["raw"], inp["h"]
 
     def step(ev=None):
+        # compress and hash in one kernel (engram_compress_hash), then gather, then gate
         if ev is not None:
             ev[0].record()
-        eg.engram_compress(raw, layer.cmap, out=bufs["ids"])
+        eg.engram_compress_hash(raw, layer.cmap, layer.orders, layer.heads, layer.mult, layer.rows, layer.pad_id,
+                                out=bufs["idx"])
         if ev is not None:
             ev[1].record()
-        eg.engram_hash(bufs["ids"], layer.orders, layer.heads, layer.mult, layer.rows, layer.pad_id,
-                       out=bufs["idx"])
-        if ev is not None:
-            ev[2].record()
         eg.engram_gather(bufs["idx"], layer.tables, out=bufs["mem"])
         if ev is not None:
-            ev[3].record()
+            ev[2].record()
         eg.engram_gate_forward(bufs["mem"], h, layer.wk, layer.wv, layer.gq, layer.gk, cfg.eps, out=outs,
                                key_norm=layer.key_norm)
         if ev is not None:
-            ev[4].record()
+            ev[3].record()
 
     flush = (torch.empty(args.flush_mb << 18, dtype=torch.float32, device=dev) if args.flush_mb > 0 else None)
 
@@ -542,27 +541,10 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    for i in range(args.steps):
-        if flush is not None:
-            flush.fill_(float(i))       # evicts L2 and MALL; outside the step's events
-        step(evs[i])
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    # per-step time: first to last event of each step (the flush between steps excluded)
-    ms_step = sum(evs[i][0].elapsed_time(evs[i][4]) for i in range(args.steps)) / args.steps
-    names = ["compress", "hash", "gather", "gate"]
-    per = {n: sum(evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(args.steps)) / args.steps
-           for k, n in enumerate(names)}
-    ms_eager, wall_eager = ms_step, t_wall
-
-    # The same step captured once in a HIP graph and replayed: the five kernel launches
-    # (the gate is two) then cost one launch.  Two eager steps on the capture stream come
-    # first, so the gate's scratch is sized and last used on that stream (no allocation
-    # or cross-stream wait is recorded).
+    # The same step captured once in a HIP graph (a launch per step instead of one per
+    # kernel).  Two eager steps on the capture stream come first, so the gate's scratch is
+    # sized and last used on that stream (no allocation or cross-stream wait is recorded).
+    graph = None
     if not args.no_graph:
         gs = torch.cuda.Stream()
         gs.wait_stream(torch.cuda.current_stream())
@@ -577,19 +559,34 @@ def main():
         for _ in range(5):
             graph.replay()
         torch.cuda.synchronize()
-        gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-        print(f"[bench] timing {args.steps} graph replays", file=sys.stderr, flush=True)
-        t_wall = time.perf_counter()
-        for i in range(args.steps):
+
+    # Timed: each iteration runs the eager step (events between its calls give the
+    # per-call breakdown and the gate's time) and then the graph replay, each after the
+    # cache flush, so both see the same clocks and the same cold caches.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps" + ("" if graph is None else " and graph replays"),
+          file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(float(i))       # evicts L2 and MALL; outside the step's events
+        step(evs[i])
+        if graph is not None:
             if flush is not None:
-                flush.fill_(float(i))
+                flush.fill_(float(i) + 0.5)
             gev[i][0].record()
             graph.replay()
             gev[i][1].record()
-        torch.cuda.synchronize()
-        t_wall = time.perf_counter() - t_wall
-        ms_step = sum(a.elapsed_time(b) for a, b in gev) / args.steps
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    # per-step time: first to last event of each step (the flush between steps excluded)
+    ms_eager = sum(evs[i][0].elapsed_time(evs[i][3]) for i in range(args.steps)) / args.steps
+    ms_step = ms_eager if graph is None else sum(a.elapsed_time(b) for a, b in gev) / args.steps
+    names = ["compress_hash", "gather", "gate"]
+    per = {n: sum(evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(args.steps)) / args.steps
+           for k, n in enumerate(names)}
 
     work = algorithmic(cfg, args.shared_wv)
     kernels = {}
@@ -629,7 +626,6 @@ def main():
         "dtype": dtype, "data": "synthetic (seeded Zipf ids, counter-generated tables/weights/hidden)",
         "config": workload_desc(cfg, args),
         "wall_s_timed": round(t_wall, 4),
-        "wall_s_timed_eager": round(wall_eager, 4),
         "cache_flush_mb_between_steps": args.flush_mb,
         "kernels": kernels,
         "roofline": roofline,

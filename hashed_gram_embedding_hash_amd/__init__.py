@@ -9,6 +9,7 @@ The functions carry the C names:
   Scalable Lookup", section 2.2);
 * ``engram_hash``      -- multi-head multiply-XOR hashing of suffix n-grams
   (section 2.2, Eq. 1);
+* ``engram_compress_hash`` -- both of the above in one kernel;
 * ``engram_gather``    -- table lookup and concatenation (Eq. 1-2);
 * ``engram_gate_forward`` -- context-aware gating and residual update
   (section 2.3, Eq. 3-4; section 2.4, Eq. 6 for several branches);
@@ -48,6 +49,7 @@ EXPORTS = (
     "engram_last_error", "engram_version", "engram_compress", "engram_hash", "engram_gather",
     "engram_gate_forward", "engram_conv_forward", "engram_prefetch_host", "engram_host_alloc",
     "engram_host_free", "engram_cache_select", "engram_cache_build", "engram_prefetch_host_cached",
+    "engram_compress_hash",
 )
 
 
@@ -78,6 +80,7 @@ def lib() -> ctypes.CDLL:
         L.engram_version.argtypes = []
         L.engram_compress.argtypes = [P, i64, P, i32, P, P, P]
         L.engram_hash.argtypes = [P, i32, i64, i64, i64, P, i32, i32, P, P, i32, P, P]
+        L.engram_compress_hash.argtypes = [P, i32, i64, i64, i64, P, i32, P, i32, i32, P, P, i32, P, P, P, P]
         L.engram_gather.argtypes = [P, i64, i32, P, P, i32, i32, P, P, P]
         L.engram_gate_forward.argtypes = [P, i64, i32, i32, i32, P, P, P, P, P, ctypes.c_float, i32, i32,
                                           P, P, P, P]
@@ -90,7 +93,8 @@ def lib() -> ctypes.CDLL:
         L.engram_prefetch_host_cached.argtypes = [P, i64, i32, P, P, i32, i32, P, i32, P, P, P, P, P]
         for f in ("engram_compress", "engram_hash", "engram_gather", "engram_gate_forward",
                   "engram_conv_forward", "engram_prefetch_host", "engram_host_alloc", "engram_host_free",
-                  "engram_cache_select", "engram_cache_build", "engram_prefetch_host_cached"):
+                  "engram_cache_select", "engram_cache_build", "engram_prefetch_host_cached",
+                  "engram_compress_hash"):
             getattr(L, f).restype = st
         _lib = L
     return _lib
@@ -176,6 +180,34 @@ def engram_hash(ids, orders: Sequence[int], heads: int, mult, rows, pad_id: int,
     _check(lib().engram_hash(_dev(ids, "ids", torch.int32), batch, ld, t_begin, t_count,
                              orders_a.ctypes.data, len(orders), heads, mult_a.ctypes.data,
                              rows_a.ctypes.data, pad_id, _dev(out, "idx", torch.int32), _stream(stream)))
+    return out
+
+
+def engram_compress_hash(raw, cmap, orders: Sequence[int], heads: int, mult, rows, pad_id: int, t_begin: int = 0,
+                         t_count: Optional[int] = None, out=None, ids_out=None, err_count=None, stream=None):
+    """engram_compress then engram_hash in one kernel: hash indices [batch * t_count,
+    len(orders) * heads] of the raw ids [batch, ld]; ``ids_out`` [batch, ld] optionally
+    receives the window's canonical ids."""
+    import numpy as np
+    import torch
+    batch, ld = raw.shape
+    if t_count is None:
+        t_count = ld - t_begin
+    orders_a = np.ascontiguousarray(orders, dtype=np.int32)
+    mult_a = np.ascontiguousarray(mult, dtype=np.uint64)
+    rows_a = np.ascontiguousarray(rows, dtype=np.uint32)
+    n_tables = len(orders) * heads
+    if mult_a.shape != (len(orders), heads, max(orders)) or rows_a.shape != (n_tables,):
+        raise ValueError("mult must be [n_orders][heads][max_order] and rows [n_tables]")
+    if ids_out is not None and tuple(ids_out.shape) != (batch, ld):
+        raise ValueError("ids_out must be [batch, ld]")
+    if out is None:
+        out = torch.empty((batch * t_count, n_tables), dtype=torch.int32, device=raw.device)
+    _check(lib().engram_compress_hash(_dev(raw, "raw", torch.int32), batch, ld, t_begin, t_count,
+                                      _dev(cmap, "map", torch.int32), cmap.numel(), orders_a.ctypes.data,
+                                      len(orders), heads, mult_a.ctypes.data, rows_a.ctypes.data, pad_id,
+                                      _opt(ids_out, "ids_out", torch.int32), _dev(out, "idx", torch.int32),
+                                      _opt(err_count, "err_count", torch.int32), _stream(stream)))
     return out
 
 

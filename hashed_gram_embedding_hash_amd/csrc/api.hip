@@ -175,11 +175,15 @@ engram_status engram_compress(const int32_t* raw, int64_t n, const int32_t* map,
   return check_launch("engram_compress");
 }
 
-engram_status engram_hash(const int32_t* ids, int32_t batch, int64_t ld, int64_t t_begin,
-                          int64_t t_count, const int32_t* orders, int32_t n_orders, int32_t heads,
-                          const uint64_t* mult, const uint32_t* rows, int32_t pad_id, int32_t* idx,
-                          hipStream_t stream) {
-  const char* fn = "engram_hash";
+}  // extern "C"
+
+namespace {
+
+// engram_hash, and with `map` set engram_compress_hash
+engram_status hash_impl(const char* fn, const int32_t* ids, int32_t batch, int64_t ld, int64_t t_begin,
+                        int64_t t_count, const int32_t* map, int32_t vocab, const int32_t* orders,
+                        int32_t n_orders, int32_t heads, const uint64_t* mult, const uint32_t* rows,
+                        int32_t pad_id, int32_t* ids_out, int32_t* idx, int32_t* err_count, hipStream_t stream) {
   if (batch < 0 || ld < 0 || t_begin < 0 || t_count < 0)
     return fail(ENGRAM_ERR_INVALID_ARG, "%s: negative size", fn);
   if (t_begin + t_count > ld)
@@ -226,9 +230,37 @@ engram_status engram_hash(const int32_t* ids, int32_t batch, int64_t ld, int64_t
   a.n_tables = nt;
   a.max_order = max_order;
   a.pad_id = pad_id;
+  a.map = map;
+  a.vocab = vocab;
+  a.ids_out = ids_out;
+  a.err_count = err_count;
   a.batch = batch;
   launch_hash(a, stream);
   return check_launch(fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+engram_status engram_hash(const int32_t* ids, int32_t batch, int64_t ld, int64_t t_begin,
+                          int64_t t_count, const int32_t* orders, int32_t n_orders, int32_t heads,
+                          const uint64_t* mult, const uint32_t* rows, int32_t pad_id, int32_t* idx,
+                          hipStream_t stream) {
+  return hash_impl("engram_hash", ids, batch, ld, t_begin, t_count, nullptr, 0, orders, n_orders, heads, mult,
+                   rows, pad_id, nullptr, idx, nullptr, stream);
+}
+
+engram_status engram_compress_hash(const int32_t* raw, int32_t batch, int64_t ld, int64_t t_begin,
+                                   int64_t t_count, const int32_t* map, int32_t vocab, const int32_t* orders,
+                                   int32_t n_orders, int32_t heads, const uint64_t* mult, const uint32_t* rows,
+                                   int32_t pad_id, int32_t* ids_out, int32_t* idx, int32_t* err_count,
+                                   hipStream_t stream) {
+  const char* fn = "engram_compress_hash";
+  if (map == nullptr) return fail(ENGRAM_ERR_INVALID_ARG, "%s: null map", fn);
+  if (vocab <= 0) return fail(ENGRAM_ERR_INVALID_ARG, "%s: vocab must be positive", fn);
+  return hash_impl(fn, raw, batch, ld, t_begin, t_count, map, vocab, orders, n_orders, heads, mult, rows, pad_id,
+                   ids_out, idx, err_count, stream);
 }
 
 engram_status engram_gather(const int32_t* idx, int64_t n_tok, int32_t n_tables,

@@ -27,8 +27,13 @@ struct HashArgs {
   int32_t order[ENGRAM_MAX_TABLES];                     // n of the table's order
   const int32_t* ids;
   int32_t* idx;
+  // compress fused in (engram_compress_hash): ids are raw ids mapped through `map` as
+  // they are staged; the window's canonical ids go to ids_out when it is set
+  const int32_t* map;   // null: ids are canonical already
+  int32_t* ids_out;
+  int32_t* err_count;
   int64_t ld, t_begin, t_count;
-  int32_t n_tables, max_order, pad_id, batch;
+  int32_t n_tables, max_order, pad_id, batch, vocab;
 };
 void launch_hash(const HashArgs& a, hipStream_t s);
 

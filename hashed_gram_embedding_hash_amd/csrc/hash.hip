@@ -9,7 +9,9 @@
 // fastest, so a wavefront writes consecutive int32 entries of the token-major
 // index matrix [tokens][tables].  A workgroup owns POS consecutive positions of
 // one sequence and first stages their ids plus the (max_order - 1) ids before
-// them in LDS; every thread then reads its n ids from LDS.
+// them in LDS; every thread then reads its n ids from LDS.  engram_compress_hash
+// reads raw ids instead and maps them through the compression table as it stages
+// them, which saves the compress kernel's launch and its pass over the ids.
 //
 // The 64-bit reduction modulo a prime M < 2^31 uses a Barrett quotient with the
 // host-computed constant m = floor((2^64 - 1) / M):  q = mulhi(h, m) is either
@@ -37,9 +39,26 @@ __global__ __launch_bounds__(256) void hash_kernel(const HashArgs a) {
   const int64_t npos = (a.t_count - p0) < POS ? (a.t_count - p0) : POS;
   const int32_t* row = a.ids + (int64_t)b * a.ld;
 
+  int bad = 0;
   for (int i = threadIdx.x; i < npos + halo; i += blockDim.x) {
     const int64_t t = t0 - halo + i;
-    s_ids[i] = t >= 0 ? row[t] : a.pad_id;
+    int32_t x = a.pad_id;
+    if (t >= 0) {
+      x = row[t];
+      if (a.map != nullptr) {  // tokenizer compression on the way in (section 2.2)
+        const bool ok = (uint32_t)x < (uint32_t)a.vocab;
+        x = ok ? a.map[x] : -1;
+        if (i >= halo) {  // positions of this workgroup's window: write and count once
+          if (a.ids_out != nullptr) a.ids_out[(int64_t)b * a.ld + t] = x;
+          bad += ok ? 0 : 1;
+        }
+      }
+    }
+    s_ids[i] = x;
+  }
+  if (a.err_count != nullptr) {
+    for (int off = 32; off > 0; off >>= 1) bad += __shfl_xor(bad, off, 64);
+    if ((threadIdx.x & 63) == 0 && bad != 0) atomicAdd(a.err_count, bad);
   }
   __syncthreads();
 

@@ -4,7 +4,8 @@
 compress the raw ids, hash every suffix n-gram into its tables, gather and
 concatenate the rows, then gate the memory against each branch's hidden
 state and add it to the residual.  This class only owns the parameters and
-the intermediate device buffers and issues the four calls on one stream; the
+the intermediate device buffers and issues the calls on one stream
+(compression and hashing as one fused call, then gather, then gate); the
 arithmetic is in the HIP kernels.  Passing one W_V tensor for every branch
 (section 2.4, Eq. (6)) lets the gate compute W_V e once for all of them.
 """
@@ -15,7 +16,7 @@ from typing import List, Optional, Sequence
 import numpy as np
 import torch
 
-from . import (KEY_NORM_MEMORY, engram_compress, engram_gate_forward, engram_gather, engram_hash)
+from . import KEY_NORM_MEMORY, engram_compress_hash, engram_gate_forward, engram_gather
 
 
 class EngramLayer:
@@ -58,9 +59,8 @@ class EngramLayer:
         """raw: int32 [batch, seq]; h: per-branch [batch*seq, d_model]; returns per-branch outputs."""
         batch, seq = raw.shape
         b = self.buffers(batch, seq)
-        engram_compress(raw, self.cmap, out=b["ids"], stream=stream)
-        engram_hash(b["ids"], self.orders, self.heads, self.mult, self.rows, self.pad_id, out=b["idx"],
-                    stream=stream)
+        engram_compress_hash(raw, self.cmap, self.orders, self.heads, self.mult, self.rows, self.pad_id,
+                             out=b["idx"], ids_out=b["ids"], stream=stream)
         engram_gather(b["idx"], self.tables, out=b["mem"], stream=stream)
         return engram_gate_forward(b["mem"], h, self.wk, self.wv, self.gq, self.gk, self.eps, out=out,
                                    gate_out=gate_out, key_norm=self.key_norm, stream=stream)

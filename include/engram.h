@@ -118,6 +118,22 @@ engram_status engram_hash(const int32_t* ids, int32_t batch, int64_t ld, int64_t
                           int32_t* idx, hipStream_t stream);
 
 /*
+ * Tokenizer compression fused into the hashing -- section 2.2: exactly
+ * engram_compress of raw into canonical ids followed by engram_hash of those ids,
+ * in one kernel that maps each raw id through `map` as it loads it.
+ * raw: device int32 [batch][ld] raw ids.  map, vocab: as for engram_compress (an
+ * id outside [0, vocab) becomes -1 and counts once in *err_count, for positions
+ * in the window).  ids_out: device int32 [batch][ld] receiving the canonical ids
+ * of the window's positions, or NULL.  All other arguments and idx as for
+ * engram_hash.
+ */
+engram_status engram_compress_hash(const int32_t* raw, int32_t batch, int64_t ld, int64_t t_begin,
+                                   int64_t t_count, const int32_t* map, int32_t vocab, const int32_t* orders,
+                                   int32_t n_orders, int32_t heads, const uint64_t* mult, const uint32_t* rows,
+                                   int32_t pad_id, int32_t* ids_out, int32_t* idx, int32_t* err_count,
+                                   hipStream_t stream);
+
+/*
  * Table lookup and concatenation -- section 2.2, Eq. (1)-(2):
  *   out[t][b*w : (b+1)*w] = tables[b][idx[t][b]][0 : w]     (bitwise copy)
  * idx:    device int32 [n_tok][n_tables].

@@ -158,3 +158,20 @@ def test_product_path_does_not_use_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), f
+
+
+def test_compress_hash_argument_errors():
+    L = eg.lib()
+    orders = np.array([2, 3], np.int32)
+    mult = np.ones((2, 2, 3), np.uint64)
+    rows = np.full(4, 1009, np.uint32)
+    cmap = np.zeros(10, np.int32)
+    ch = lambda **kw: L.engram_compress_hash(
+        ctypes.c_void_p(4096), kw.get("batch", 2), kw.get("ld", 100), kw.get("tb", 0), kw.get("tc", 100),
+        ctypes.c_void_p(kw.get("map", cmap.ctypes.data)), kw.get("vocab", 10), orders.ctypes.data, 2, 2,
+        mult.ctypes.data, rows.ctypes.data, 10, None, ctypes.c_void_p(kw.get("idx", 8192)), None, None)
+    assert ch(map=0) == _st("arg")
+    assert ch(vocab=0) == _st("arg")
+    assert ch(tb=50, tc=60) == _st("arg")       # window past the row
+    assert ch(batch=-1) == _st("arg")
+    assert ch(tc=0) == _st("ok")

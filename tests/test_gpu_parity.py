@@ -89,6 +89,52 @@ def test_hash_config_bit_exact(name):
     assert idx_o.min() >= 0 and idx_o.max() < cfg.rows
 
 
+@pytest.mark.parametrize("name", ["tiny", "small", "multi"])
+def test_compress_hash_fused_equals_separate_and_oracle(name):
+    """engram_compress_hash = engram_compress then engram_hash, bit for bit, and the oracle's."""
+    cfg = synth.CONFIGS[name]
+    say("compress+hash fused", name)
+    raw = synth.raw_ids(cfg)
+    _, idx_o = oracle_ids_idx(cfg, raw)
+    raw_d, map_d = torch.from_numpy(raw).to(DEV), torch.from_numpy(synth.comp_map(cfg)).to(DEV)
+    ids_out = torch.full_like(raw_d, -7)
+    fused = eg.engram_compress_hash(raw_d, map_d, cfg.orders, cfg.heads, synth.multipliers(cfg),
+                                    synth.table_rows_u32(cfg), cfg.vocab_c, ids_out=ids_out)
+    ids_d = eg.engram_compress(raw_d, map_d)
+    sep = eg.engram_hash(ids_d, cfg.orders, cfg.heads, synth.multipliers(cfg), synth.table_rows_u32(cfg), cfg.vocab_c)
+    assert torch.equal(fused, sep)
+    assert torch.equal(ids_out, ids_d)
+    assert np.array_equal(fused.cpu().numpy(), idx_o)
+
+
+def test_compress_hash_fused_windows_and_bad_ids():
+    """Windows that start mid-row (the halo is compressed too, but neither written nor
+    counted), decode-style single positions, and out-of-range raw ids."""
+    say("compress+hash fused windows")
+    rng = np.random.default_rng(8)
+    V, Vc = 5000, 3001
+    cmap = rng.integers(0, Vc, V).astype(np.int32)
+    raw = rng.integers(0, V, (3, 300)).astype(np.int32)
+    raw[0, 10], raw[1, 150], raw[2, 299], raw[2, 0] = V, -5, V + 99, 1 << 30
+    orders, heads = (1, 2, 3, 4), 2
+    mult = synth.hash_multipliers(9, orders, heads)
+    rows = np.array([synth.next_prime(int(x)) for x in rng.integers(1000, 2**31 - 100, 8)], np.uint32)
+    raw_d, map_d = torch.from_numpy(raw).to(DEV), torch.from_numpy(cmap).to(DEV)
+    ids_d = eg.engram_compress(raw_d, map_d)
+    for t_begin, t_count in ((0, 300), (5, 100), (150, 1), (299, 1), (12, 288)):
+        err = torch.zeros(1, dtype=torch.int32, device=DEV)
+        ids_out = torch.full_like(raw_d, -7)
+        got = eg.engram_compress_hash(raw_d, map_d, orders, heads, mult, rows, Vc, t_begin=t_begin, t_count=t_count,
+                                      ids_out=ids_out, err_count=err)
+        want = eg.engram_hash(ids_d, orders, heads, mult, rows, Vc, t_begin=t_begin, t_count=t_count)
+        assert torch.equal(got, want), (t_begin, t_count)
+        win = slice(t_begin, t_begin + t_count)
+        assert torch.equal(ids_out[:, win], ids_d[:, win])
+        assert bool((ids_out[:, :t_begin] == -7).all()) and bool((ids_out[:, t_begin + t_count:] == -7).all())
+        bad = int(((raw[:, win] < 0) | (raw[:, win] >= V)).sum())
+        assert int(err.item()) == bad, (t_begin, t_count)
+
+
 def test_hash_windows_orders_and_large_primes():
     """Ragged windows, orders 1..4, per-table primes up to 2^31 - 1, decode-style t_count = 1."""
     say("hash windows")
