@@ -374,6 +374,45 @@ def test_gate_bf16_shared_wv_in_place_large_shape():
         assert err <= 1e-2
 
 
+@pytest.mark.parametrize("d_mem,d_model,key_norm,shared", [
+    (1216, 2592, eg.KEY_NORM_MEMORY, False),     # 19 k-steps (odd), last feature tile 32 wide
+    (1344, 2080, eg.KEY_NORM_PROJECTED, False),  # 21 k-steps, last feature tile 32 wide
+    (1216, 2336, eg.KEY_NORM_MEMORY, True),      # 3 branches sharing W_V, ragged feature tile
+])
+def test_gate_bf16_ragged_feature_tile_and_odd_k(d_mem, d_model, key_norm, shared):
+    """Shapes off the 256 x 64 tiling: d_model not a multiple of 256 (the last feature
+    tile is partly past the end: clamped weight rows, masked h and outputs) and d_mem/64
+    odd (the operand ring's slot arithmetic wraps differently); 333 tokens."""
+    say(f"gate bf16 ragged d_mem {d_mem} d_model {d_model} key_norm {key_norm} shared W_V {shared}")
+    M = 3 if shared else 1
+    n_tok = 333
+    g = torch.Generator().manual_seed(d_mem + d_model)
+    # unit-scale memory, as in the stress cases, so that |alpha v| ~ 0.5 and the update
+    # bar (the output's bf16 rounding over |alpha v|) applies
+    e = torch.randn(n_tok, d_mem, generator=g).to(torch.bfloat16)
+    hs = [torch.randn(n_tok, d_model, generator=g).to(torch.bfloat16) for _ in range(M)]
+    wks = [(torch.randn(d_model, d_mem, generator=g) / d_mem ** 0.5).to(torch.bfloat16) for _ in range(M)]
+    wv = (torch.randn(d_model, d_mem, generator=g) / d_mem ** 0.5).to(torch.bfloat16)
+    wvs = [wv] * M if shared else [(torch.randn(d_model, d_mem, generator=g) / d_mem ** 0.5).to(torch.bfloat16)]
+    nk = d_mem if key_norm == eg.KEY_NORM_MEMORY else d_model
+    gqs = [(1 + 0.2 * torch.randn(d_model, generator=g)).to(torch.bfloat16) for _ in range(M)]
+    gks = [(1 + 0.2 * torch.randn(nk, generator=g)).to(torch.bfloat16) for _ in range(M)]
+    alpha = torch.empty((M, n_tok), dtype=torch.float32, device=DEV)
+    dv = lambda xs: [x.to(DEV) for x in xs]
+    wv_d = dv([wv])[0]
+    out = eg.engram_gate_forward(e.to(DEV), dv(hs), dv(wks), [wv_d] * M if shared else dv(wvs), dv(gqs), dv(gks),
+                                 1e-6, gate_out=alpha, key_norm=key_norm)
+    torch.cuda.synchronize()
+    for m in range(M):
+        out_o, alpha_o = oracle.gate(host_view(e), host_view(hs[m]), host_view(wks[m]), host_view(wvs[0 if shared else m]),
+                                     host_view(gqs[m]), host_view(gks[m]), 1e-6, oracle.BF16, key_norm=key_norm)
+        err = rel_err(out[m].float().cpu().numpy(), out_o)
+        aerr = np.abs(alpha[m].cpu().numpy() - alpha_o).max()
+        upd = rel_err((out[m].float() - hs[m].float().to(DEV)).cpu().numpy(), out_o - host_bf16_to_f64(hs[m]))
+        say(f"  branch {m}: out rel err {err:.2e}, alpha abs err {aerr:.2e}, update rel err {upd:.2e}")
+        assert err <= 1e-2 and aerr <= ALPHA_TOL_BF16 and upd <= UPDATE_TOL_STRESS
+
+
 def test_gate_bf16_scratch_shared_across_streams_and_sizes():
     """The gate keeps one scratch buffer per device.  Calls alternating between two
     streams, with a larger shape in between (the buffer grows), must give exactly the
