@@ -54,6 +54,13 @@ def lib():
         L.oracle_gate.restype = ctypes.c_int
         L.oracle_gate.restype = ctypes.c_int
         L.oracle_conv.argtypes = [P, i32, i64, i32, P, P, i32, i32, ctypes.c_double, i32, P, P]
+        L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3_decode.restype = ctypes.c_double
+        L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        L.oracle_e4m3_encode.restype = ctypes.c_uint8
+        L.oracle_quant_rows.argtypes = [P, i64, i32, P, P]
+        L.oracle_gate_fp8.argtypes = [P, i64, i32, i32, P, P, P, P, P, ctypes.c_double, i32, i32, P, P]
+        L.oracle_gate_fp8.restype = ctypes.c_int
         L.oracle_conv.restype = None
         _lib = L
     return _lib
@@ -155,3 +162,45 @@ def conv(value: np.ndarray, batch: int, seq: int, w: np.ndarray, gamma: np.ndarr
     lib().oracle_conv(_p(value), batch, seq, d_model, _p(w), _p(gamma), taps, dil, float(eps), dtype,
                       _p(base), _p(out))
     return out
+
+
+# ---------------------------------------------------------------------------
+# FP8 (OCP E4M3) quantization and the gate with FP8 projections
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Values (float64) of E4M3 codes (uint8 array-like); NaN for 0x7F and 0xFF."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.array([lib().oracle_e4m3_decode(int(x)) for x in c.ravel()], dtype=np.float64).reshape(c.shape)
+
+
+def e4m3_encode(values) -> np.ndarray:
+    """Nearest E4M3 codes (ties to even, saturating at +-448) of float32 values."""
+    v = np.asarray(values, dtype=np.float32)
+    return np.array([lib().oracle_e4m3_encode(float(x)) for x in v.ravel()], dtype=np.uint8).reshape(v.shape)
+
+
+def quant_rows(x: np.ndarray):
+    """Per-row FP8 quantization of float32 x [rows, cols]: (codes uint8 [rows, cols],
+    scales float32 [rows]) with scale = max|row| / 448 in fp32 (1 for a zero row)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, cols = x.shape
+    codes = np.empty((rows, cols), dtype=np.uint8)
+    scales = np.empty(rows, dtype=np.float32)
+    lib().oracle_quant_rows(_p(x), rows, cols, _p(codes), _p(scales))
+    return codes, scales
+
+
+def gate_fp8(mem, h, wk, wv, gq, gk, eps: float, dtype: int, key_norm: int = KEY_NORM_MEMORY):
+    """oracle.gate with both projections in FP8 (per-token / per-row scales):
+    (out [n_tok, d_model] float64, alpha [n_tok] float64)."""
+    mem, h, wk, wv, gq, gk = (np.ascontiguousarray(a) for a in (mem, h, wk, wv, gq, gk))
+    n_tok, d_mem = mem.shape
+    d_model = h.shape[1]
+    assert wk.shape == (d_model, d_mem) and wv.shape == (d_model, d_mem) and gq.shape == (d_model,)
+    assert gk.shape == ((d_mem,) if key_norm == KEY_NORM_MEMORY else (d_model,))
+    out = np.empty((n_tok, d_model), dtype=np.float64)
+    alpha = np.empty(n_tok, dtype=np.float64)
+    rc = lib().oracle_gate_fp8(_p(mem), n_tok, d_mem, d_model, _p(h), _p(wk), _p(wv), _p(gq), _p(gk), float(eps),
+                               dtype, key_norm, _p(out), _p(alpha))
+    assert rc == 0, rc
+    return out, alpha

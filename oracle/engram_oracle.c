@@ -16,9 +16,14 @@
  *   - hash: z = (XOR_j  x'_{t-j} * c[n][k][j]  mod 2^64) mod M[n][k], one odd
  *     64-bit multiplier per (order, head, position in the gram); positions
  *     before the start of a sequence read the id `pad_id`;
- *   - gate: key = W_K * RMSNorm(e) (normalised before the projection), the
- *     scale is 1/sqrt(d_model), RMSNorm(x) = x / sqrt(mean(x^2) + eps) * gamma;
- *   - the short causal convolution is not part of this path.
+ *   - gate: key = W_K * RMSNorm(e) (normalised before the projection; the paper's
+ *     Eq. (4) placement, RMSNorm after W_K, is the key_norm = 1 mode), the scale is
+ *     1/sqrt(d_model), RMSNorm(x) = x / sqrt(mean(x^2) + eps) * gamma;
+ *   - short causal convolution (Eq. (5)): tap j looks j * dilation tokens back;
+ *   - FP8 projections (section 2.4 names FP8 for the fused projection GEMM, without a
+ *     format or a scaling): OCP E4M3, a scale per row of each operand (per token for
+ *     the memory vector, per output feature for the weights) equal to max|x| / 448 in
+ *     fp32, codes by round-to-nearest-even with saturation to +-448.
  *
  * Arithmetic: integers in uint64 with C's own '%' (no reduction tricks);
  * floating point decoded exactly to double, accumulated in double, sigmoid as
@@ -241,4 +246,142 @@ void oracle_conv(const double* value, int32_t batch, int64_t seq, int32_t d_mode
       }
     }
   }
+}
+
+/*
+ * FP8 E4M3 (the OCP 8-bit floating point format, E4M3 variant): 1 sign bit, 4 exponent
+ * bits with bias 7, 3 mantissa bits.  Exponent field 0 holds the subnormals m * 2^-9;
+ * field e > 0 the normals (1 + m/8) * 2^(e-7); 0x7F and 0xFF are NaN, so the largest
+ * finite magnitude is 0x7E = 1.75 * 2^8 = 448.  No infinities.
+ */
+double oracle_e4m3_decode(uint8_t c) {
+  const int e = (c >> 3) & 15, m = c & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0) v = ldexp((double)m, -9);
+  else v = ldexp(1.0 + m / 8.0, e - 7);
+  return (c & 0x80) ? -v : v;
+}
+
+/* The code nearest to v (ties to the even code), magnitudes of 448 and above saturate
+ * to 448.  Works on the exact value of v in double: the representable magnitudes in
+ * [2^E, 2^(E+1)) are spaced 2^(E-3) for E >= -6 and 2^-9 below (the subnormals). */
+uint8_t oracle_e4m3_encode(float v) {
+  const uint8_t sign = signbit(v) ? 0x80 : 0;
+  const double a = fabs((double)v);
+  if (a >= 448.0) return sign | 0x7E;
+  if (a == 0.0) return sign;
+  int e2;
+  frexp(a, &e2);            /* a = f * 2^e2, f in [0.5, 1): a in [2^(e2-1), 2^e2) */
+  const int E = e2 - 1;
+  const double quantum = E < -6 ? ldexp(1.0, -9) : ldexp(1.0, E - 3);
+  double q = a / quantum;   /* exact: a power-of-two division */
+  double r = floor(q);
+  const double frac = q - r;
+  if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+  const double val = r * quantum;
+  if (val == 0.0) return sign;
+  if (val >= 448.0) return sign | 0x7E;
+  int f2;
+  frexp(val, &f2);
+  const int E2 = f2 - 1;
+  if (E2 < -6) return sign | (uint8_t)(val / ldexp(1.0, -9));            /* subnormal */
+  const int mant = (int)(val / ldexp(1.0, E2 - 3)) - 8;                    /* 0..7 */
+  return sign | (uint8_t)(((E2 + 7) << 3) | mant);
+}
+
+/* Per row r of x [rows][cols] (float): s = max|x[r][:]| / 448 in fp32 (1 for an all-zero
+ * row), codes[r][c] = encode(x[r][c] / s) with the division in fp32. */
+void oracle_quant_rows(const float* x, int64_t rows, int32_t cols, uint8_t* codes, float* scales) {
+  for (int64_t r = 0; r < rows; ++r) {
+    const float* xr = x + r * cols;
+    float mx = 0.f;
+    for (int32_t c = 0; c < cols; ++c) mx = fmaxf(mx, fabsf(xr[c]));
+    const float s = mx > 0.f ? mx / 448.0f : 1.0f;
+    scales[r] = s;
+    for (int32_t c = 0; c < cols; ++c) codes[r * cols + c] = oracle_e4m3_encode(xr[c] / s);
+  }
+}
+
+/*
+ * The gate of oracle_gate with its two projections in FP8 (the reading in the header):
+ *   e          quantized per token:              e^  = s_e[t]  * code_e
+ *   key weights: key_norm 0: W'' = (gq[f] * W_K[f][c]) * gk[c] in fp32, quantized per
+ *              row f; key_norm 1: W_K quantized per row
+ *   W_V        quantized per row
+ * then, in double from the dequantized values,
+ *   key_norm 0:  k_f = (W''^ e^)_f / rms(e^)          q_f = h_f / rms(h)
+ *   key_norm 1:  k_f = (W_K^ e^)_f / rms(W_K^ e^) * gk[f],  q_f = h_f / rms(h) * gq[f]
+ *   alpha = sigmoid(q . k / sqrt(d_model)),   out = h + alpha * (W_V^ e^)
+ * Inputs as for oracle_gate (bf16 or f32); returns 0, or -1/-2 for a bad mode/alloc.
+ */
+int oracle_gate_fp8(const void* mem, int64_t n_tok, int32_t d_mem, int32_t d_model, const void* h,
+                    const void* wk, const void* wv, const void* gq, const void* gk, double eps, int32_t dtype,
+                    int32_t key_norm, double* out, double* alpha) {
+  if (key_norm != 0 && key_norm != 1) return -1;
+  const size_t nw = (size_t)d_model * d_mem;
+  float* wf = (float*)malloc(sizeof(float) * nw);
+  float* ef = (float*)malloc(sizeof(float) * (size_t)d_mem);
+  uint8_t* ck = (uint8_t*)malloc(nw);
+  uint8_t* cv = (uint8_t*)malloc(nw);
+  uint8_t* ce = (uint8_t*)malloc((size_t)d_mem);
+  float* sk = (float*)malloc(sizeof(float) * (size_t)d_model);
+  float* sv = (float*)malloc(sizeof(float) * (size_t)d_model);
+  double* k = (double*)malloc(sizeof(double) * (size_t)d_model);
+  if (!wf || !ef || !ck || !cv || !ce || !sk || !sv || !k) return -2;
+  /* key weights */
+  for (int32_t f = 0; f < d_model; ++f)
+    for (int32_t c = 0; c < d_mem; ++c) {
+      const float w = (float)load_elem(wk, (int64_t)f * d_mem + c, dtype);
+      wf[(size_t)f * d_mem + c] =
+          key_norm == 0 ? ((float)load_elem(gq, f, dtype) * w) * (float)load_elem(gk, c, dtype) : w;
+    }
+  oracle_quant_rows(wf, d_model, d_mem, ck, sk);
+  for (size_t i = 0; i < nw; ++i) wf[i] = (float)load_elem(wv, (int64_t)i, dtype);
+  oracle_quant_rows(wf, d_model, d_mem, cv, sv);
+  for (int64_t t = 0; t < n_tok; ++t) {
+    for (int32_t c = 0; c < d_mem; ++c) ef[c] = (float)load_elem(mem, t * d_mem + c, dtype);
+    float se;
+    oracle_quant_rows(ef, 1, d_mem, ce, &se);
+    double ss_e = 0.0;
+    for (int32_t c = 0; c < d_mem; ++c) {
+      const double x = se * oracle_e4m3_decode(ce[c]);
+      ss_e += x * x;
+    }
+    double ss_h = 0.0;
+    for (int32_t i = 0; i < d_model; ++i) {
+      const double x = load_elem(h, t * d_model + i, dtype);
+      ss_h += x * x;
+    }
+    const double rms_h = sqrt(ss_h / d_model + eps);
+    double ss_k = 0.0;
+    for (int32_t f = 0; f < d_model; ++f) {
+      double acc = 0.0;
+      for (int32_t c = 0; c < d_mem; ++c)
+        acc += oracle_e4m3_decode(ck[(size_t)f * d_mem + c]) * oracle_e4m3_decode(ce[c]);
+      k[f] = (double)sk[f] * se * acc;
+      ss_k += k[f] * k[f];
+    }
+    double logit = 0.0;
+    if (key_norm == 0) {
+      const double rms_e = sqrt(ss_e / d_mem + eps);
+      for (int32_t f = 0; f < d_model; ++f) logit += load_elem(h, t * d_model + f, dtype) / rms_h * (k[f] / rms_e);
+    } else {
+      const double rms_k = sqrt(ss_k / d_model + eps);
+      for (int32_t f = 0; f < d_model; ++f)
+        logit += load_elem(h, t * d_model + f, dtype) / rms_h * load_elem(gq, f, dtype) *
+                 (k[f] / rms_k * load_elem(gk, f, dtype));
+    }
+    logit /= sqrt((double)d_model);
+    const double a = 1.0 / (1.0 + exp(-logit));
+    alpha[t] = a;
+    for (int32_t f = 0; f < d_model; ++f) {
+      double acc = 0.0;
+      for (int32_t c = 0; c < d_mem; ++c)
+        acc += oracle_e4m3_decode(cv[(size_t)f * d_mem + c]) * oracle_e4m3_decode(ce[c]);
+      out[t * d_model + f] = load_elem(h, t * d_model + f, dtype) + a * ((double)sv[f] * se * acc);
+    }
+  }
+  free(wf); free(ef); free(ck); free(cv); free(ce); free(sk); free(sv); free(k);
+  return 0;
 }

@@ -497,3 +497,106 @@ def test_gate_projected_key_limits():
     np.testing.assert_allclose(v_p, out_p - h.astype(np.float64), rtol=1e-12, atol=1e-12)
     v = e.astype(np.float64) @ wv.astype(np.float64).T
     np.testing.assert_allclose(v_p, a_p[:, None] * v, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# FP8 (OCP E4M3) codes and the FP8 gate
+
+FINITE = [c for c in range(256) if c not in (0x7F, 0xFF)]
+
+
+def test_e4m3_known_codes():
+    d = dict(zip(range(256), oracle.e4m3_decode(np.arange(256))))
+    assert d[0x38] == 1.0 and d[0x40] == 2.0 and d[0x3C] == 1.5 and d[0x37] == 0.9375
+    assert d[0x7E] == 448.0 and d[0xFE] == -448.0 and d[0xB8] == -1.0
+    assert d[0x01] == 2.0 ** -9 and d[0x07] == 7 * 2.0 ** -9 and d[0x08] == 2.0 ** -6
+    assert d[0x00] == 0.0 and np.signbit(d[0x80])
+    assert np.isnan(d[0x7F]) and np.isnan(d[0xFF])
+    pos = oracle.e4m3_decode(np.arange(0x7F))
+    assert np.all(np.diff(pos) > 0)                    # strictly increasing magnitudes
+
+
+def test_e4m3_encode_round_trips_every_finite_code():
+    vals = oracle.e4m3_decode(np.array(FINITE, np.uint8)).astype(np.float32)
+    assert np.array_equal(oracle.e4m3_encode(vals), np.array(FINITE, np.uint8))
+
+
+def test_e4m3_encode_ties_to_even_and_neighbours():
+    lo = oracle.e4m3_decode(np.arange(0x7E))
+    hi = oracle.e4m3_decode(np.arange(1, 0x7F))
+    mid = ((lo + hi) / 2).astype(np.float32)            # exact: at most 5 significant bits
+    assert np.array_equal(mid.astype(np.float64), (lo + hi) / 2)
+    got = oracle.e4m3_encode(mid)
+    even = np.where(np.arange(0x7E) % 2 == 0, np.arange(0x7E), np.arange(1, 0x7F)).astype(np.uint8)
+    assert np.array_equal(got, even)
+    assert np.array_equal(oracle.e4m3_encode(np.nextafter(mid, np.float32(np.inf))), np.arange(1, 0x7F, dtype=np.uint8))
+    assert np.array_equal(oracle.e4m3_encode(np.nextafter(mid, np.float32(0))), np.arange(0x7E, dtype=np.uint8))
+    assert np.array_equal(oracle.e4m3_encode(-mid), even | 0x80)
+
+
+def test_e4m3_encode_saturates():
+    assert list(oracle.e4m3_encode([448.0, 460.0, 464.0, 1e30, -1e30, -470.0])) == [0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE]
+    assert oracle.e4m3_encode([2.0 ** -10])[0] == 0x00          # tie between 0 and 2^-9 -> even (0)
+    assert oracle.e4m3_encode([3 * 2.0 ** -10])[0] == 0x02      # tie between 2^-9 and 2^-8 -> even
+
+
+def test_quant_rows_scale_and_error_bound():
+    rng = np.random.default_rng(50)
+    x = (rng.standard_normal((40, 300)) * np.exp(rng.uniform(-8, 8, (40, 1)))).astype(np.float32)
+    x[3] = 0.0
+    codes, scales = oracle.quant_rows(x)
+    mx = np.abs(x).max(axis=1)
+    assert np.array_equal(scales, np.where(mx > 0, mx / np.float32(448), np.float32(1)).astype(np.float32))
+    assert np.all(codes[3] == 0) and scales[3] == 1.0
+    deq = oracle.e4m3_decode(codes) * scales[:, None].astype(np.float64)
+    err = np.abs(deq - x.astype(np.float64))
+    # half a spacing: 2^-4 of the value for normals, 2^-10 of the scale for subnormals
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, scales[:, None] * 2.0 ** -10) * (1 + 1e-6)
+    assert np.all(err <= bound)
+    amax = np.abs(x).argmax(axis=1)
+    for r in range(40):
+        if r != 3:
+            assert codes[r, amax[r]] & 0x7F == 0x7E    # the largest element maps to 448
+
+
+def _fp8_exact_gate_inputs(rng, n, dm, d):
+    """Inputs that E4M3 with the per-row scales represents exactly: rows of grid values
+    times a power of two, each row holding +-448 times that power."""
+    grid = oracle.e4m3_decode(np.array([c for c in FINITE if c not in (0x80,)], np.uint8))
+    def rows(r, c, p2):
+        x = rng.choice(grid, size=(r, c)) * 2.0 ** p2
+        x[:, 0] = 448.0 * 2.0 ** p2 * rng.choice([-1, 1], size=r)
+        return x.astype(np.float32)
+    return rows(n, dm, -8), rows(d, dm, -10), rows(d, dm, -10)
+
+
+@pytest.mark.parametrize("key_norm", [0, 1])
+def test_gate_fp8_equals_gate_on_exactly_representable_inputs(key_norm):
+    rng = np.random.default_rng(51 + key_norm)
+    n, dm, d = 6, 48, 20
+    e, wk, wv = _fp8_exact_gate_inputs(rng, n, dm, d)
+    h = rng.standard_normal((n, d)).astype(np.float32)
+    gq = (1 + 0.2 * rng.standard_normal(d)).astype(np.float32) if key_norm else np.ones(d, np.float32)
+    gk = (1 + 0.2 * rng.standard_normal(d if key_norm else dm)).astype(np.float32) if key_norm \
+        else np.ones(dm, np.float32)
+    out8, a8 = oracle.gate_fp8(e, h, wk, wv, gq, gk, 1e-6, oracle.F32, key_norm=key_norm)
+    out, a = oracle.gate(e, h, wk, wv, gq, gk, 1e-6, oracle.F32, key_norm=key_norm)
+    np.testing.assert_allclose(a8, a, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(out8, out, rtol=1e-12, atol=1e-13)
+
+
+def test_gate_fp8_close_to_gate_on_random_inputs():
+    """Quantization moves each operand element by at most 2^-4 of itself, so alpha and the
+    update stay within a few percent of the unquantized gate."""
+    rng = np.random.default_rng(53)
+    n, dm, d = 8, 64, 32
+    e = rng.standard_normal((n, dm)).astype(np.float32)
+    h = rng.standard_normal((n, d)).astype(np.float32)
+    wk = (rng.standard_normal((d, dm)) / 8).astype(np.float32)
+    wv = (rng.standard_normal((d, dm)) / 8).astype(np.float32)
+    ones_d, ones_m = np.ones(d, np.float32), np.ones(dm, np.float32)
+    out8, a8 = oracle.gate_fp8(e, h, wk, wv, ones_d, ones_m, 1e-6, oracle.F32)
+    out, a = oracle.gate(e, h, wk, wv, ones_d, ones_m, 1e-6, oracle.F32)
+    assert np.abs(a8 - a).max() < 0.05
+    upd8, upd = out8 - h, out - h
+    assert np.abs(upd8 - upd).max() < 0.08 * np.abs(upd).max()
