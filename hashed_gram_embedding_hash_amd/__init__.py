@@ -49,7 +49,7 @@ EXPORTS = (
     "engram_last_error", "engram_version", "engram_compress", "engram_hash", "engram_gather",
     "engram_gate_forward", "engram_conv_forward", "engram_prefetch_host", "engram_host_alloc",
     "engram_host_free", "engram_cache_select", "engram_cache_build", "engram_prefetch_host_cached",
-    "engram_compress_hash",
+    "engram_compress_hash", "engram_quantize_fp8",
 )
 
 
@@ -81,6 +81,7 @@ def lib() -> ctypes.CDLL:
         L.engram_compress.argtypes = [P, i64, P, i32, P, P, P]
         L.engram_hash.argtypes = [P, i32, i64, i64, i64, P, i32, i32, P, P, i32, P, P]
         L.engram_compress_hash.argtypes = [P, i32, i64, i64, i64, P, i32, P, i32, i32, P, P, i32, P, P, P, P]
+        L.engram_quantize_fp8.argtypes = [P, i64, i32, i32, P, P, P, P]
         L.engram_gather.argtypes = [P, i64, i32, P, P, i32, i32, P, P, P]
         L.engram_gate_forward.argtypes = [P, i64, i32, i32, i32, P, P, P, P, P, ctypes.c_float, i32, i32,
                                           P, P, P, P]
@@ -94,7 +95,7 @@ def lib() -> ctypes.CDLL:
         for f in ("engram_compress", "engram_hash", "engram_gather", "engram_gate_forward",
                   "engram_conv_forward", "engram_prefetch_host", "engram_host_alloc", "engram_host_free",
                   "engram_cache_select", "engram_cache_build", "engram_prefetch_host_cached",
-                  "engram_compress_hash"):
+                  "engram_compress_hash", "engram_quantize_fp8"):
             getattr(L, f).restype = st
         _lib = L
     return _lib
@@ -394,6 +395,20 @@ def engram_prefetch_host_cached(idx, host_tables: Sequence, rows: Sequence[int],
         table.shape[1], _dev(cache_rows, "cache_rows", dtype), _dev(staging, "staging", dtype),
         _opt(hits, "hits", torch.int32), _opt(err_count, "err_count", torch.int32), _stream(stream)))
     return staging
+
+
+def engram_quantize_fp8(x, with_sumsq: bool = False, stream=None):
+    """Per-row FP8 (OCP E4M3) codes of x [rows, cols]: (codes uint8 [rows, cols], scales
+    float32 [rows]) and, with_sumsq, the rows' sums of squares of the dequantized values."""
+    import torch
+    rows, cols = x.shape
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    scales = torch.empty(rows, dtype=torch.float32, device=x.device)
+    sumsq = torch.empty(rows, dtype=torch.float32, device=x.device) if with_sumsq else None
+    _check(lib().engram_quantize_fp8(_dev(x, "x"), rows, cols, _edtype(x), _dev(codes, "codes", torch.uint8),
+                                     _dev(scales, "scales", torch.float32), _opt(sumsq, "sumsq", torch.float32),
+                                     _stream(stream)))
+    return (codes, scales, sumsq) if with_sumsq else (codes, scales)
 
 
 def host_alloc(nbytes: int) -> int:

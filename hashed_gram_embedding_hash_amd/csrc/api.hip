@@ -470,6 +470,21 @@ engram_status engram_conv_forward(const void* value, int32_t batch, int64_t seq,
   });
 }
 
+engram_status engram_quantize_fp8(const void* src, int64_t rows, int32_t cols, engram_dtype dtype, uint8_t* codes,
+                                  float* scales, float* sumsq, hipStream_t stream) {
+  const char* fn = "engram_quantize_fp8";
+  if (rows < 0 || cols <= 0) return fail(ENGRAM_ERR_INVALID_ARG, "%s: bad sizes", fn);
+  if (!valid_dtype(dtype)) return fail(ENGRAM_ERR_INVALID_ARG, "%s: unknown dtype", fn);
+  if (cols % 16 != 0) return fail(ENGRAM_ERR_UNSUPPORTED, "%s: cols %d not a multiple of 16", fn, cols);
+  if (rows == 0) return ENGRAM_OK;
+  if (src == nullptr || codes == nullptr || scales == nullptr || !aligned(src, 16) || !aligned(codes, 16) ||
+      !aligned(scales, 4) || (sumsq != nullptr && !aligned(sumsq, 4)))
+    return fail(ENGRAM_ERR_INVALID_ARG, "%s: null or misaligned pointer", fn);
+  if ((rows + 3) / 4 >= (1ll << 31)) return fail(ENGRAM_ERR_UNSUPPORTED, "%s: too many rows", fn);
+  launch_quant_rows(src, dtype == ENGRAM_BF16, rows, cols, nullptr, nullptr, codes, scales, sumsq, stream);
+  return check_launch(fn);
+}
+
 engram_status engram_host_alloc(size_t bytes, void** ptr) {
   if (ptr == nullptr) return fail(ENGRAM_ERR_INVALID_ARG, "engram_host_alloc: null ptr");
   *ptr = nullptr;

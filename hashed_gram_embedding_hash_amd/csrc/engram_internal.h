@@ -54,6 +54,12 @@ void launch_gather(const GatherArgs& a, bool host_source, hipStream_t s);
 void launch_prefetch_cached(const GatherArgs& a, const int2* table, int log2_slots, const char* cache_rows,
                             int32_t* hits, hipStream_t s);
 
+// ---------------------------------------------------------------- FP8 quantization
+// per-row E4M3 codes and fp32 scales of src [rows][cols] (cols % 16 == 0); grow [rows] /
+// gcol [cols] optional gains folded in first; sumsq [rows] optional
+void launch_quant_rows(const void* src, bool bf16, int64_t rows, int32_t cols, const void* grow, const void* gcol,
+                       uint8_t* codes, float* scales, float* sumsq, hipStream_t s);
+
 // ---------------------------------------------------------------- gate
 struct GateArgs {
   const void* mem;

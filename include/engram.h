@@ -267,6 +267,22 @@ engram_status engram_prefetch_host_cached(const int32_t* idx, int64_t n_tok, int
                                           const void* cache_rows, void* staging, int32_t* hits,
                                           int32_t* err_count, hipStream_t stream);
 
+/*
+ * FP8 quantization of a row-major matrix -- section 2.4 names FP8 for the projection
+ * GEMM but no format or scaling; this library's reading (the one its FP8 gate uses):
+ * OCP E4M3 (sign, 4 exponent bits with bias 7, 3 mantissa bits; 0x7E = 448 is the
+ * largest finite value) with one fp32 scale per row:
+ *   scales[r]     = max_c |src[r][c]| / 448   (1 for an all-zero row), in fp32
+ *   codes[r][c]   = E4M3 code nearest to src[r][c] / scales[r] (the division in fp32;
+ *                   ties to the even code; magnitudes >= 448 saturate to 448)
+ *   sumsq[r]      = sum_c (value(codes[r][c]) * scales[r])^2 in fp32, or NULL
+ * src: device [rows][cols] of dtype; codes: device uint8 [rows][cols]; scales, sumsq:
+ * device float [rows].  cols % 16 == 0 (UNSUPPORTED otherwise); 16-byte aligned src
+ * and codes.
+ */
+engram_status engram_quantize_fp8(const void* src, int64_t rows, int32_t cols, engram_dtype dtype, uint8_t* codes,
+                                  float* scales, float* sumsq, hipStream_t stream);
+
 /* Pinned, device-mapped host allocation for offloaded tables (hipHostMalloc,
  * hipHostMallocMapped | hipHostMallocPortable). *ptr is NULL on failure. */
 engram_status engram_host_alloc(size_t bytes, void** ptr);

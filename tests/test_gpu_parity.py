@@ -704,3 +704,35 @@ def test_prefetch_host_cached_equals_gather(dtype, w, capacity, slots):
     expect_hits = sum(int(np.isin(idx[:, b], hot[b][hot[b] >= 0]).sum()) for b in range(nt))
     say(f"  hits {int(hits.item())} of {idx.size} ({int(hits.item()) / idx.size:.1%})")
     assert int(hits.item()) == expect_hits > 0
+
+
+# ---------------------------------------------------------------------------
+# FP8 (OCP E4M3) quantization and the FP8 gate
+# ---------------------------------------------------------------------------
+def test_quantize_fp8_codes_bit_exact():
+    """Per-row codes and scales equal the oracle's bit for bit: bf16 rows over 2^-40 ..
+    2^40 (subnormal codes included) with an all-zero row, and fp32 rows with max 448
+    (scale 1) whose other elements are the exact midpoints between neighbouring codes."""
+    say("fp8 quantization")
+    rng = np.random.default_rng(60)
+    x = (rng.standard_normal((300, 1280)) * np.exp2(rng.uniform(-40, 40, (300, 1)))).astype(np.float32)
+    x[7] = 0.0
+    x[11, :600] *= 1e-6                                   # many elements in the subnormal range
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    codes, scales, ss = eg.engram_quantize_fp8(xb.to(DEV), with_sumsq=True)
+    want_c, want_s = oracle.quant_rows(xb.float().numpy())
+    assert np.array_equal(codes.cpu().numpy(), want_c)
+    assert np.array_equal(scales.cpu().numpy(), want_s)
+    deq = oracle.e4m3_decode(want_c) * want_s[:, None].astype(np.float64)
+    np.testing.assert_allclose(ss.cpu().numpy(), (deq ** 2).sum(axis=1), rtol=1e-5, atol=0)
+    lo = oracle.e4m3_decode(np.arange(0x7E))
+    hi = oracle.e4m3_decode(np.arange(1, 0x7F))
+    mids = ((lo + hi) / 2).astype(np.float32)
+    xt = np.concatenate([mids, -mids, np.full(2, 448.0, np.float32)])
+    xt = np.resize(xt, (4, 512)).astype(np.float32)
+    xt[:, 0] = 448.0
+    codes2, scales2 = eg.engram_quantize_fp8(torch.from_numpy(xt).to(DEV))
+    want_c2, want_s2 = oracle.quant_rows(xt)
+    assert np.all(want_s2 == 1.0)
+    assert np.array_equal(codes2.cpu().numpy(), want_c2)
+    assert np.array_equal(scales2.cpu().numpy(), want_s2)
