@@ -34,6 +34,7 @@ METRIC = "Engram tokens/s (hash+gather+gate); gather HBM GB/s & MFMA util vs pea
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3       # fp32 vector / matrix
+PEAK_FP8_TFLOPS = 5000.0       # dense fp8 MFMA
 GATE_SOURCE = os.path.join(ROOT, "hashed_gram_embedding_hash_amd", "csrc", "gate_bf16.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_persistent_kernel_small_hbm_traffic.txt")
 
@@ -51,6 +52,8 @@ def parse():
                    help="every branch uses branch 0's W_V (the paper's Eq. 6): W_V e is computed once")
     p.add_argument("--key-norm", choices=("memory", "projected"), default="memory",
                    help="memory: k = W_K RMSNorm(e) (default); projected: k = RMSNorm(W_K e), Eq. 4")
+    p.add_argument("--fp8", action="store_true",
+                   help="gate projections on E4M3 codes (engram_gate_forward_fp8; quantization inside the call)")
     p.add_argument("--no-graph", action="store_true",
                    help="time the eagerly launched step only (default: the step is also captured in a HIP graph "
                         "and the graph replay is the reported value)")
@@ -72,8 +75,9 @@ def parse():
 
 def workload_desc(cfg, args=None):
     extra = {}
-    if args is not None and (args.shared_wv or args.key_norm != "memory"):
-        extra = {"key_norm": args.key_norm, "shared_wv": bool(args.shared_wv)}
+    if args is not None and (args.shared_wv or args.key_norm != "memory" or args.fp8):
+        extra = {"key_norm": args.key_norm, "shared_wv": bool(args.shared_wv),
+                 "gate_projections": "fp8 e4m3, per-row scales" if args.fp8 else "bf16"}
     return {**extra,
         "workload": cfg.name,
         "tokens": cfg.tokens, "batch": cfg.batch, "seq_len": cfg.seq,
@@ -435,9 +439,10 @@ def measure_conv(args, cfg, bufs, h, layer, outs, flush):
             "gate_with_values_plus_conv_ms": round(gate_v_ms + conv_ms, 5)}
 
 
-def cpu_baseline(cfg, target_s):
+def cpu_baseline(cfg, target_s, fp8=False):
     """The oracle (single thread) on the first tokens of sequence 0: compress, hash,
-    gather and gate.  Table rows are regenerated outside the timed region."""
+    gather and gate (its FP8 form with fp8).  Table rows are regenerated outside the
+    timed region."""
     import numpy as np
     import torch
     import oracle
@@ -470,8 +475,9 @@ def cpu_baseline(cfg, target_s):
         h = [host_view(synth.hidden_rows(cfg, m, torch.arange(n))) for m in range(cfg.n_branch)]
         t1 = time.perf_counter()
         e = oracle.gather(remap, subs)
+        gate = oracle.gate_fp8 if fp8 else oracle.gate
         for m in range(cfg.n_branch):
-            oracle.gate(e, h[m], wts[m][0], wts[m][1], gns[m][0], gns[m][1], cfg.eps, dt)
+            gate(e, h[m], wts[m][0], wts[m][1], gns[m][0], gns[m][1], cfg.eps, dt)
         return t_int + time.perf_counter() - t1
 
     probe = 8
@@ -480,7 +486,8 @@ def cpu_baseline(cfg, target_s):
     t = run(n)
     return {"value": n / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"first {n} tokens of sequence 0 of the {cfg.name} workload: compress, hash, "
-                      f"gather and all {cfg.n_branch} gate branch(es), one thread, {t:.1f} s"}
+                      f"gather and all {cfg.n_branch} {'fp8 ' if fp8 else ''}gate branch(es), one thread, "
+                      f"{t:.1f} s"}
 
 
 def main():
@@ -530,7 +537,7 @@ def main():
         if ev is not None:
             ev[2].record()
         eg.engram_gate_forward(bufs["mem"], h, layer.wk, layer.wv, layer.gq, layer.gk, cfg.eps, out=outs,
-                               key_norm=layer.key_norm)
+                               key_norm=layer.key_norm, fp8=args.fp8)
         if ev is not None:
             ev[3].record()
 
@@ -600,15 +607,20 @@ def main():
             d["TFLOP/s"] = round(work[n]["flops"] / s / 1e12, 2)
         kernels[n] = d
     gate_s = per["gate"] * 1e-3
-    if cfg.dtype == "bf16":
+    if cfg.dtype == "bf16" and args.fp8:
+        peak, dtype = PEAK_FP8_TFLOPS, "fp8e4m3 projections, bf16 storage"
+    elif cfg.dtype == "bf16":
         peak, dtype = PEAK_BF16_TFLOPS, "bf16"
     else:
         peak, dtype = PEAK_FP32_TFLOPS, "f32"
     achieved = work["gate"]["flops"] / gate_s / 1e12
-    default_gate = not args.shared_wv and args.key_norm == "memory"
+    default_gate = not args.shared_wv and args.key_norm == "memory" and not args.fp8
     traffic = measured_traffic(cfg) if cfg.dtype == "bf16" and default_gate else None
-    roofline = {"kernel": "engram_gate_forward: gate_prep_kernel + gate_persistent_kernel "
-                          "(events bracket both; the prep kernel is ~1% of the call)",
+    kernel = ("engram_gate_forward_fp8: gate_prep_projected_kernel + quant_rows_kernel (W_K, W_V, mem) + "
+              "gate_persistent_kernel (events bracket all)" if args.fp8 else
+              "engram_gate_forward: gate_prep_kernel + gate_persistent_kernel "
+              "(events bracket both; the prep kernel is ~1% of the call)")
+    roofline = {"kernel": kernel,
                 "bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic,
                 "traffic_algorithmic": work["gate"]["bytes"],
@@ -635,7 +647,7 @@ def main():
         result["conv"] = measure_conv(args, cfg, bufs, h, layer, outs, flush)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds, fp8=args.fp8)
     print(json.dumps(result), flush=True)
 
 

@@ -13,6 +13,7 @@ The functions carry the C names:
 * ``engram_gather``    -- table lookup and concatenation (Eq. 1-2);
 * ``engram_gate_forward`` -- context-aware gating and residual update
   (section 2.3, Eq. 3-4; section 2.4, Eq. 6 for several branches);
+  ``fp8=True`` runs both projections on E4M3 codes (section 2.4);
 * ``engram_conv_forward`` -- the short depthwise causal convolution over the
   gated values (section 2.3, Eq. 5);
 * ``engram_prefetch_host`` -- the same gather from pinned host-memory tables
@@ -49,7 +50,7 @@ EXPORTS = (
     "engram_last_error", "engram_version", "engram_compress", "engram_hash", "engram_gather",
     "engram_gate_forward", "engram_conv_forward", "engram_prefetch_host", "engram_host_alloc",
     "engram_host_free", "engram_cache_select", "engram_cache_build", "engram_prefetch_host_cached",
-    "engram_compress_hash", "engram_quantize_fp8",
+    "engram_compress_hash", "engram_quantize_fp8", "engram_gate_forward_fp8",
 )
 
 
@@ -85,6 +86,7 @@ def lib() -> ctypes.CDLL:
         L.engram_gather.argtypes = [P, i64, i32, P, P, i32, i32, P, P, P]
         L.engram_gate_forward.argtypes = [P, i64, i32, i32, i32, P, P, P, P, P, ctypes.c_float, i32, i32,
                                           P, P, P, P]
+        L.engram_gate_forward_fp8.argtypes = L.engram_gate_forward.argtypes
         L.engram_conv_forward.argtypes = [P, i32, i64, i32, P, P, i32, i32, ctypes.c_float, i32, P, P]
         L.engram_prefetch_host.argtypes = [P, i64, i32, P, P, i32, i32, P, P, P]
         L.engram_host_alloc.argtypes = [ctypes.c_size_t, ctypes.POINTER(ctypes.c_void_p)]
@@ -95,7 +97,7 @@ def lib() -> ctypes.CDLL:
         for f in ("engram_compress", "engram_hash", "engram_gather", "engram_gate_forward",
                   "engram_conv_forward", "engram_prefetch_host", "engram_host_alloc", "engram_host_free",
                   "engram_cache_select", "engram_cache_build", "engram_prefetch_host_cached",
-                  "engram_compress_hash", "engram_quantize_fp8"):
+                  "engram_compress_hash", "engram_quantize_fp8", "engram_gate_forward_fp8"):
             getattr(L, f).restype = st
         _lib = L
     return _lib
@@ -235,10 +237,14 @@ def engram_gather(idx, tables: Sequence, out=None, err_count=None, stream=None):
 
 def engram_gate_forward(mem, h: Sequence, wk: Sequence, wv: Sequence, gq: Sequence, gk: Sequence,
                         eps: float = 1e-6, out: Optional[Sequence] = None, gate_out=None,
-                        value_out: Optional[Sequence] = None, key_norm: int = KEY_NORM_MEMORY, stream=None):
+                        value_out: Optional[Sequence] = None, key_norm: int = KEY_NORM_MEMORY, stream=None,
+                        fp8: bool = False):
     """out[m] = h[m] + sigmoid(RMSNorm(h[m]) . k[m] / sqrt(d)) * W_V[m] mem, with
     k[m] = W_K[m] RMSNorm(mem) (KEY_NORM_MEMORY, gk over d_mem) or RMSNorm(W_K[m] mem)
     (KEY_NORM_PROJECTED, gk over d_model).
+
+    ``fp8``: both projections on per-row E4M3 codes of the weights and of mem
+    (engram_gate_forward_fp8; bf16 operands, d_mem % 128 == 0).
 
     Lists hold one tensor per branch; ``out`` defaults to new tensors (pass ``h``
     for in-place).  ``gate_out``: optional float32 [n_branch, n_tok] for alpha.
@@ -277,9 +283,10 @@ def engram_gate_forward(mem, h: Sequence, wk: Sequence, wv: Sequence, gq: Sequen
     for x in gk:
         if tuple(x.shape) != (gk_len,):
             raise ValueError(f"gk must be [{gk_len}] for key_norm {key_norm}")
-    _check(lib().engram_gate_forward(mem.data_ptr(), n_tok, d_mem, d_model, nb, arr(h), arr(wk), arr(wv),
-                                     arr(gq), arr(gk), float(eps), _edtype(mem), int(key_norm), arr(out),
-                                     _opt(gate_out, "gate_out", torch.float32), varr, _stream(stream)))
+    fn = lib().engram_gate_forward_fp8 if fp8 else lib().engram_gate_forward
+    _check(fn(mem.data_ptr(), n_tok, d_mem, d_model, nb, arr(h), arr(wk), arr(wv), arr(gq), arr(gk), float(eps),
+              _edtype(mem), int(key_norm), arr(out), _opt(gate_out, "gate_out", torch.float32), varr,
+              _stream(stream)))
     return out
 
 

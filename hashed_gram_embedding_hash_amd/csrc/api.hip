@@ -346,13 +346,17 @@ engram_status engram_prefetch_host_cached(const int32_t* idx, int64_t n_tok, int
   return check_launch(fn);
 }
 
-engram_status engram_gate_forward(const void* mem, int64_t n_tok, int32_t d_mem, int32_t d_model,
-                                  int32_t n_branch, const void* const* h, const void* const* wk,
-                                  const void* const* wv, const void* const* gq,
-                                  const void* const* gk, float eps, engram_dtype dtype,
-                                  engram_key_norm key_norm, void* const* out, float* gate_out,
-                                  void* const* value_out, hipStream_t stream) {
-  const char* fn = "engram_gate_forward";
+}  // extern "C"
+
+namespace {
+
+// The arguments of both gate entry points: checked, and copied into `a` (n_tok == 0
+// leaves `a` unfilled: nothing to launch).
+engram_status gate_args(const char* fn, const void* mem, int64_t n_tok, int32_t d_mem, int32_t d_model,
+                        int32_t n_branch, const void* const* h, const void* const* wk, const void* const* wv,
+                        const void* const* gq, const void* const* gk, float eps, engram_dtype dtype,
+                        engram_key_norm key_norm, void* const* out, float* gate_out, void* const* value_out,
+                        GateArgs& a) {
   if (n_tok < 0 || d_mem <= 0 || d_model <= 0)
     return fail(ENGRAM_ERR_INVALID_ARG, "%s: bad sizes n_tok=%lld d_mem=%d d_model=%d", fn,
                 (long long)n_tok, d_mem, d_model);
@@ -374,7 +378,6 @@ engram_status engram_gate_forward(const void* mem, int64_t n_tok, int32_t d_mem,
     return fail(ENGRAM_ERR_INVALID_ARG, "%s: null or misaligned mem", fn);
   if (gate_out != nullptr && !aligned(gate_out, 4))
     return fail(ENGRAM_ERR_INVALID_ARG, "%s: misaligned gate_out", fn);
-  GateArgs a;
   memset(&a, 0, sizeof a);
   for (int m = 0; m < n_branch; ++m) {
     if (wk[m] == nullptr || wv[m] == nullptr || gq[m] == nullptr || gk[m] == nullptr ||
@@ -392,7 +395,6 @@ engram_status engram_gate_forward(const void* mem, int64_t n_tok, int32_t d_mem,
     if (n_tok > 0 && a.vout[m] != nullptr && !aligned(a.vout[m], al))
       return fail(ENGRAM_ERR_INVALID_ARG, "%s: branch %d: misaligned value_out", fn, m);
   }
-  if (n_tok == 0) return ENGRAM_OK;
   a.mem = mem;
   a.gate_out = gate_out;
   a.n_tok = n_tok;
@@ -402,6 +404,24 @@ engram_status engram_gate_forward(const void* mem, int64_t n_tok, int32_t d_mem,
   a.eps = eps;
   a.inv_sqrt_d = 1.0f / sqrtf((float)d_model);
   a.key_norm = (int32_t)key_norm;
+  return ENGRAM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+engram_status engram_gate_forward(const void* mem, int64_t n_tok, int32_t d_mem, int32_t d_model,
+                                  int32_t n_branch, const void* const* h, const void* const* wk,
+                                  const void* const* wv, const void* const* gq,
+                                  const void* const* gk, float eps, engram_dtype dtype,
+                                  engram_key_norm key_norm, void* const* out, float* gate_out,
+                                  void* const* value_out, hipStream_t stream) {
+  const char* fn = "engram_gate_forward";
+  GateArgs a;
+  const engram_status st = gate_args(fn, mem, n_tok, d_mem, d_model, n_branch, h, wk, wv, gq, gk, eps, dtype,
+                                     key_norm, out, gate_out, value_out, a);
+  if (st != ENGRAM_OK || n_tok == 0) return st;
 
   if (dtype == ENGRAM_F32) {
     const size_t lds = (size_t)d_mem * 4 + (key_norm == ENGRAM_KEY_NORM_PROJECTED ? (size_t)d_model * 4 : 0);
@@ -412,10 +432,31 @@ engram_status engram_gate_forward(const void* mem, int64_t n_tok, int32_t d_mem,
     return check_launch(fn);
   }
 
-  const size_t bytes = gate_bf16_scratch_bytes(a);
+  const size_t bytes = gate_bf16_scratch_bytes(a, false);
   return with_scratch(fn, bytes, stream, [&](void* p) {
     a.part_dot = (float*)p;
-    launch_gate_bf16(a, stream);
+    launch_gate_bf16(a, false, stream);
+  });
+}
+
+engram_status engram_gate_forward_fp8(const void* mem, int64_t n_tok, int32_t d_mem, int32_t d_model,
+                                      int32_t n_branch, const void* const* h, const void* const* wk,
+                                      const void* const* wv, const void* const* gq,
+                                      const void* const* gk, float eps, engram_dtype dtype,
+                                      engram_key_norm key_norm, void* const* out, float* gate_out,
+                                      void* const* value_out, hipStream_t stream) {
+  const char* fn = "engram_gate_forward_fp8";
+  if (dtype != ENGRAM_BF16) return fail(ENGRAM_ERR_UNSUPPORTED, "%s: operands must be bf16", fn);
+  if (d_mem % 128 != 0)
+    return fail(ENGRAM_ERR_UNSUPPORTED, "%s: d_mem must be a multiple of 128 (got %d)", fn, d_mem);
+  GateArgs a;
+  const engram_status st = gate_args(fn, mem, n_tok, d_mem, d_model, n_branch, h, wk, wv, gq, gk, eps, dtype,
+                                     key_norm, out, gate_out, value_out, a);
+  if (st != ENGRAM_OK || n_tok == 0) return st;
+  const size_t bytes = gate_bf16_scratch_bytes(a, true);
+  return with_scratch(fn, bytes, stream, [&](void* p) {
+    a.part_dot = (float*)p;
+    launch_gate_bf16(a, true, stream);
   });
 }
 

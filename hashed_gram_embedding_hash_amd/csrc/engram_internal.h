@@ -81,11 +81,19 @@ struct GateArgs {
   int32_t d_mem, d_model, n_branch, n_ftiles, n_ttiles;
   int32_t key_norm;  // engram_key_norm
   float eps, inv_sqrt_d;
+  // FP8 projections (scratch, written by the quantization kernels): per-feature scales
+  // of the key and value weight codes ([n_branch][d_model]; one shared W_V: row 0), and
+  // per token the scale and the sum of squares of the dequantized memory vector
+  const float* sk;
+  const float* sv;
+  const float* se;
+  const float* e_ssq;
 };
 // bf16 path: returns the scratch bytes it needs for these shapes (and sets a.n_ftiles).
-// launch_gate_bf16 expects a.part_dot to point at a scratch block of that size.
-size_t gate_bf16_scratch_bytes(GateArgs& a);
-void launch_gate_bf16(const GateArgs& a, hipStream_t s);
+// launch_gate_bf16 expects a.part_dot to point at a scratch block of that size.  With
+// fp8, the projections run on E4M3 codes that it quantizes first (d_mem % 128 == 0).
+size_t gate_bf16_scratch_bytes(GateArgs& a, bool fp8);
+void launch_gate_bf16(const GateArgs& a, bool fp8, hipStream_t s);
 void launch_gate_f32(const GateArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- short convolution

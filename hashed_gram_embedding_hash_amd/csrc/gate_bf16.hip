@@ -71,6 +71,8 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16-B chunk (native: stays in registers)
+typedef int v8i __attribute__((ext_vector_type(8)));          // FP8 MFMA operand: 32 E4M3 codes
+typedef int v4i_t __attribute__((ext_vector_type(4)));
 
 constexpr int BF = 256;   // features per tile
 constexpr int BT = 256;   // tokens per tile
@@ -202,8 +204,13 @@ __device__ __forceinline__ bool decode_tile(const GateArgs& a, int x, int q, Til
 //           LDS) and also reduces sum_f k_f^2, which takes the place of the e^2 partial;
 //   SHAREDV every branch uses the same W_V (section 2.4, Eq. (6)): a V tile computes
 //           W_V e once, waits for the gates of all branches, and runs one epilogue per
-//           branch, loading that branch's h tile into the ring between them.
-template <bool VALUES, bool KEYP, bool SHAREDV>
+//           branch, loading that branch's h tile into the ring between them;
+//   F8      the projections in FP8 (section 2.4): both operands are E4M3 codes with one
+//           fp32 scale per row (per token for e, per feature for the weights), prepared
+//           by the quantization kernels.  A 128-byte ring row then holds 128 k-values,
+//           and each MFMA (32x32x64 E4M3) takes one 64-value half; the feature scales
+//           weight the epilogues from LDS, the token scale joins the reduced scalars.
+template <bool VALUES, bool KEYP, bool SHAREDV, bool F8>
 __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, char* smem, int x,
                                           int& next_claim) {
   const int PHASE = tile.phase;
@@ -242,6 +249,13 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
   }
   float kg = 0.f;  // KEYP K tiles: gq * gk of feature f0 + tid (to LDS in the epilogue)
   if (KEYP && PHASE == PHASE_K && f0 + tid < d_model) kg = a.kgain[(int64_t)m * d_model + f0 + tid];
+  // F8: the weight scale of feature f0 + tid (K or V weights; 0 past d_model), and for V
+  // tiles the token scale of token t0 + tid; both to LDS in the epilogue
+  float fs = 0.f, ts = 0.f;
+  if constexpr (F8) {
+    if (f0 + tid < d_model) fs = (PHASE == PHASE_K ? a.sk : a.sv)[(int64_t)m * d_model + f0 + tid];
+    if (PHASE == PHASE_V && t0 + tid < n_tok) ts = a.se[t0 + tid];
+  }
 
   // ---- operand stream.  Chunk c of the tile's stream lands in LDS slot c % NSLOT:
   // chunks 2 kt and 2 kt + 1 are the weight rows and the memory rows of k-step kt
@@ -256,7 +270,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
   //
   // Instruction i of wave w fills rows 64 w + 8 i .. + 7 of a chunk: lane l reads
   // row 64 w + 8 i + l / 8 at physical chunk l % 8 (logical (l % 8) ^ row_key).
-  const int nk = d_mem / BK;
+  const int nk = d_mem / (F8 ? 2 * BK : BK);  // k-steps of 128 bytes per row
   const uint16_t* Et0 = E + t0 * d_mem;   // memory rows of this token tile
   const uint16_t* Ht0 = H + t0 * d_model;
   const int b_lim = (int)(n_tok - 1 - t0);  // last valid row of the token tile
@@ -267,8 +281,8 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
     const int cl = (lane & 7) ^ row_key(r);
     // weight rows are permuted (tile_row_feature); rows past the end are clamped to
     // the last valid one (their results are unused)
-    off_a[i] = (uint32_t)min(f0 + tile_row_feature(r), d_model - 1) * (uint32_t)d_mem + cl * 8;
-    off_b[i] = (uint32_t)min(r, b_lim) * (uint32_t)d_mem + cl * 8;
+    off_a[i] = (uint32_t)min(f0 + tile_row_feature(r), d_model - 1) * (uint32_t)d_mem + cl * (F8 ? 16 : 8);
+    off_b[i] = (uint32_t)min(r, b_lim) * (uint32_t)d_mem + cl * (F8 ? 16 : 8);
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr)smem;
   const uint32_t wave_dst = lds0 + (uint32_t)(wave * G_INSTR * 1024);
@@ -298,12 +312,27 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
       dma16(Ht0 + (uint32_t)tr * (uint32_t)d_model + f, dst + (uint32_t)(blk * 1024));
     }
   };
+  // FP8: the operands are byte arrays (offsets above are in bytes)
+  const uint8_t* W8 = (const uint8_t*)W;
+  const uint8_t* Et8 = (const uint8_t*)E + t0 * d_mem;
+#define ENGRAM_ISSUE8(base_, off_, kt_, slot_)                                             \
+  do {                                                                                     \
+    const uint8_t* src_ = (base_) + (kt_) * (2 * BK);                                      \
+    const uint32_t dst_ = wave_dst + (uint32_t)((slot_) * SLOT_BYTES);                     \
+    _Pragma("unroll") for (int i = 0; i < G_INSTR; ++i)                                    \
+        dma16((const uint16_t*)(src_ + off_[i]), dst_ + i * 1024);                        \
+  } while (0)
   // any chunk (the prologue and the last k-steps)
   auto issue_chunk = [&](int c) {
     const int slot = c % NSLOT;
     if (c < 2 * nk) {
-      if (c & 1) ENGRAM_ISSUE(Et0, off_b, c >> 1, slot);
-      else ENGRAM_ISSUE(W, off_a, c >> 1, slot);
+      if constexpr (F8) {
+        if (c & 1) ENGRAM_ISSUE8(Et8, off_b, c >> 1, slot);
+        else ENGRAM_ISSUE8(W8, off_a, c >> 1, slot);
+      } else {
+        if (c & 1) ENGRAM_ISSUE(Et0, off_b, c >> 1, slot);
+        else ENGRAM_ISSUE(W, off_a, c >> 1, slot);
+      }
     } else {
       issue_hq(c - 2 * nk, slot);
     }
@@ -382,7 +411,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
   float ee_acc[MT];
 #pragma unroll
   for (int j = 0; j < MT; ++j) ee_acc[j] = 0.f;
-  const bool ee_wave = !KEYP && PHASE == PHASE_K && wf == 0;
+  const bool ee_wave = !KEYP && !F8 && PHASE == PHASE_K && wf == 0;
 #define ENGRAM_EE(buf)                                                                     \
   do {                                                                                     \
     _Pragma("unroll") for (int j = 0; j < MT; ++j)                                         \
@@ -397,6 +426,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  if constexpr (!F8) {
   for (int c = 0; c < NSLOT; ++c) issue_chunk(c);
   wait_vm_lgkm0<3 * G_INSTR>();
   lds_barrier();
@@ -478,10 +508,91 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
   issue_chunk(2 * nk + 3);
   ENGRAM_MFMAS(1);
   if (ee_now) ENGRAM_EE(1);
+  } else {
+    // ---- FP8 main loop.  The same ring and chunk numbering; a 128-byte k-step is two
+    // halves of 64 k-values, and the fragment of a half is the two 16-byte chunks that
+    // the bf16 loop reads for two consecutive sub-steps (logical chunks 4 p + khalf and
+    // 4 p + 2 + khalf), for both operands alike.  Each fragment register is reloaded as
+    // soon as its last MFMA has issued (row i of A after MFMA (i, MT-1), column j of B
+    // after MFMA (MF-1, j)):
+    //   half 0 of k-step kt, reading half 1 of kt;
+    //   wait + barrier: k-step kt + 1 has landed, k-step kt's slots are free;
+    //   half 1 of kt, reading half 0 of kt + 1 and refilling kt's slots with chunks
+    //   2 kt + 5 (memory rows) and 2 kt + 6 (weight rows), one load after every MFMA;
+    //   in the last three k-steps, where these are h-tile quarters or nothing, as a
+    //   burst before the MFMAs.
+    // Chunk 2 kt + 3 is issued during half 1 of kt - 1 and needed at the barrier of kt,
+    // when only chunk 2 kt + 4 may still be in flight.  No branch may enter the MFMA
+    // sequences (the compiler would move the MFMAs past it): the last k-step reads
+    // fragments it does not use.
+    v8i fa8[MF], fb8[MT];
+    auto frag8 = [&](int base, uint32_t o0, uint32_t o1) -> v8i {
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(smem + base + o0);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(smem + base + o1);
+      return __builtin_shufflevector(__builtin_bit_cast(v4i_t, lo), __builtin_bit_cast(v4i_t, hi), 0, 1, 2, 3, 4,
+                                     5, 6, 7);
+    };
+#define ENGRAM_F8_A(sa_, p_, i_) fa8[i_] = frag8((sa_) + (i_) * 32 * 2 * BK, fr_a[2 * (p_)], fr_a[2 * (p_) + 1])
+#define ENGRAM_F8_B(sb_, p_, j_) fb8[j_] = frag8((sb_) + (j_) * 32 * 2 * BK, fr_b[2 * (p_)], fr_b[2 * (p_) + 1])
+#define ENGRAM_F8_MFMA(i_, j_)                                                             \
+  acc[i_][j_] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa8[i_], fb8[j_], acc[i_][j_], 0, 0, 0, 127, 0, 127)
+#define ENGRAM_F8_KSTEP(spread_)                                                           \
+  do {                                                                                     \
+    const int sa = ((2 * kt) % NSLOT) * SLOT_BYTES;                                        \
+    const int sb = ((2 * kt + 1) % NSLOT) * SLOT_BYTES;                                    \
+    __builtin_amdgcn_sched_barrier(0);                                                     \
+    _Pragma("unroll") for (int k = 0; k < MF * MT; ++k) {                                  \
+      ENGRAM_F8_MFMA(k / MT, k % MT);                                                      \
+      __builtin_amdgcn_sched_barrier(0);                                                   \
+      if (k / MT == MF - 1) ENGRAM_F8_B(sb, 1, k % MT);                                    \
+      if (k % MT == MT - 1) ENGRAM_F8_A(sa, 1, k / MT);                                    \
+      __builtin_amdgcn_sched_barrier(0);                                                   \
+    }                                                                                      \
+    wait_vm_lgkm0<G_INSTR>();                                                              \
+    lds_barrier();                                                                         \
+    if (!(spread_)) {                                                                      \
+      issue_chunk(2 * kt + 5);                                                             \
+      if (2 * kt + 6 <= 2 * nk + 3) issue_chunk(2 * kt + 6);                               \
+    }                                                                                      \
+    const int sa2 = ((2 * kt + 2) % NSLOT) * SLOT_BYTES;                                   \
+    const int sb2 = ((2 * kt + 3) % NSLOT) * SLOT_BYTES;                                   \
+    const uint8_t* srcE = Et8 + (kt + 2) * (2 * BK);                                       \
+    const uint8_t* srcW = W8 + (kt + 3) * (2 * BK);                                        \
+    const uint32_t dstE = wave_dst + (uint32_t)sa, dstW = wave_dst + (uint32_t)sb;         \
+    __builtin_amdgcn_sched_barrier(0);                                                     \
+    _Pragma("unroll") for (int k = 0; k < MF * MT; ++k) {                                  \
+      ENGRAM_F8_MFMA(k / MT, k % MT);                                                      \
+      __builtin_amdgcn_sched_barrier(0);                                                   \
+      if (k / MT == MF - 1) ENGRAM_F8_B(sb2, 0, k % MT);                                   \
+      if (k % MT == MT - 1) ENGRAM_F8_A(sa2, 0, k / MT);                                   \
+      if (spread_) {                                                                       \
+        if (k < G_INSTR) dma16((const uint16_t*)(srcE + off_b[k]), dstE + k * 1024);      \
+        else dma16((const uint16_t*)(srcW + off_a[k - G_INSTR]), dstW + (k - G_INSTR) * 1024); \
+      }                                                                                    \
+      __builtin_amdgcn_sched_barrier(0);                                                   \
+    }                                                                                      \
+  } while (0)
+    for (int c = 0; c < NSLOT; ++c) issue_chunk(c);
+    wait_vm_lgkm0<3 * G_INSTR>();
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < MT; ++j) ENGRAM_F8_B(SLOT_BYTES, 0, j);
+#pragma unroll
+    for (int i = 0; i < MF; ++i) ENGRAM_F8_A(0, 0, i);
+    int kt = 0;
+    // chunks 2 kt + 5 and 2 kt + 6 are both operand rows while kt + 3 < nk
+    for (; kt + 3 < nk; ++kt) ENGRAM_F8_KSTEP(true);
+    for (; kt < nk; ++kt) ENGRAM_F8_KSTEP(false);
+#undef ENGRAM_F8_KSTEP
+#undef ENGRAM_F8_A
+#undef ENGRAM_F8_B
+#undef ENGRAM_F8_MFMA
+  }
 #undef ENGRAM_KSTEP
 #undef ENGRAM_GROUP
 #undef ENGRAM_READ1
 #undef ENGRAM_ISSUE
+#undef ENGRAM_ISSUE8
 #undef ENGRAM_EE
 #undef ENGRAM_LOAD_FRAGS
 #undef ENGRAM_MFMAS
@@ -528,8 +639,10 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
   int* s_flag = reinterpret_cast<int*>(scratch + 5 * BT * sizeof(float));
   float (*s_kk)[BT] = reinterpret_cast<float (*)[BT]>(scratch + 6 * BT * sizeof(float));  // KEYP
   float* s_g = reinterpret_cast<float*>(scratch + 8 * BT * sizeof(float));               // KEYP, [BF]
+  float* s_fs = reinterpret_cast<float*>(scratch + 8 * BT * sizeof(float) + BF * sizeof(float));  // F8, [BF]
   if (PHASE == PHASE_V) {
-    s_alpha[etid] = alpha;
+    if constexpr (F8) s_alpha[etid] = alpha * ts;  // the token scale rides on the gate
+    else s_alpha[etid] = alpha;
     lds_barrier();
   }
   if (KEYP && PHASE == PHASE_K) {
@@ -540,6 +653,25 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
   // Lane (token column tl) holds, for MFMA tile (i, j) and pair gp, features
   // fl = wf*WF + i*32 + gp*16 + (lane>>5)*8 + 0..7 in acc[i][j][8*gp + 0..7].
   const int hsel = (elane >> 5) * 8;
+  if constexpr (F8) {
+    // the weight scales: acc becomes W e / s_e (per feature: k_f or v_f over the token
+    // scale), after which the epilogues are those of the bf16 operands
+    s_fs[etid] = fs;
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < MF; ++i)
+#pragma unroll
+      for (int gp = 0; gp < 2; ++gp) {
+        const int fl = ewf * WF + i * 32 + gp * 16 + hsel;
+        const float4 g0 = *reinterpret_cast<const float4*>(s_fs + fl);
+        const float4 g1 = *reinterpret_cast<const float4*>(s_fs + fl + 4);
+        const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+        for (int j = 0; j < MT; ++j)
+#pragma unroll
+          for (int r = 0; r < 8; ++r) acc[i][j][gp * 8 + r] *= g[r];
+      }
+  }
   if (PHASE == PHASE_K) {
 #pragma unroll
     for (int j = 0; j < MT; ++j) {
@@ -647,7 +779,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
             const int64_t o = base + (int64_t)(ok ? j0 + u : 0) * n_tok;
             vd[u] = ok ? ld_coherent(a.part_dot + o) : 0.f;
             vh[u] = ok ? ld_coherent(a.part_hh + o) : 0.f;
-            ve[u] = ok ? ld_coherent(a.ee + o) : 0.f;
+            ve[u] = ok && (KEYP || !F8) ? ld_coherent(a.ee + o) : 0.f;
           }
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
@@ -655,6 +787,13 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
             hh += vh[u];
             ee += ve[u];
           }
+        }
+        if constexpr (F8) {
+          // the token scale of e: k = s_e * (the partials' k / s_e); the memory-side
+          // norm takes the quantized row's own sum of squares
+          const float se = a.se[t];
+          dot *= se;
+          ee = KEYP ? ee * se * se : a.e_ssq[t];
         }
         const float rms_h = sqrtf(hh / (float)d_model + a.eps);
         // the key's norm: of the memory vector (d_mem wide), or KEYP of W_K e (d_model)
@@ -774,7 +913,8 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
               dma16(hb + (uint32_t)tr * (uint32_t)d_model + f, dst + (uint32_t)(blk * 1024));
             }
           }
-          const float al = t0 + etid < n_tok ? ld_coherent(a.alpha + (int64_t)mb * n_tok + t0 + etid) : 0.f;
+          float al = t0 + etid < n_tok ? ld_coherent(a.alpha + (int64_t)mb * n_tok + t0 + etid) : 0.f;
+          if constexpr (F8) al = t0 + etid < n_tok ? al * a.se[t0 + etid] : 0.f;
           wait_vm_lgkm0<0>();
           s_alpha[etid] = al;
           lds_barrier();
@@ -787,7 +927,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
 #undef ENGRAM_QSLOT
 }
 
-template <bool VALUES, bool KEYP, bool SHAREDV>
+template <bool VALUES, bool KEYP, bool SHAREDV, bool F8>
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gate_persistent_kernel(const GateArgs a) {
   // the operand ring, then the h tile and the epilogue scratch; between tiles its
@@ -804,7 +944,7 @@ void gate_persistent_kernel(const GateArgs a) {
     const bool have = decode_tile<SHAREDV>(a, x, *s_tile, t);
     lds_barrier();  // every thread has read the tile number before the ring is refilled
     if (!have) break;
-    gate_tile<VALUES, KEYP, SHAREDV>(a, t, smem, x, claim);
+    gate_tile<VALUES, KEYP, SHAREDV, F8>(a, t, smem, x, claim);
     // LDS free for the next tile.  A full barrier: letting a V tile's 128 KB of output
     // stores drain behind the next tile's operand loads measured 8 % slower than
     // finishing them first.
@@ -847,24 +987,45 @@ __global__ __launch_bounds__(256) void gate_prep_kernel(const GateArgs a, uint16
   reinterpret_cast<u32x4*>(wk_scaled)[i] = o;
 }
 
-// wk_bytes: the gain-folded key weights (the memory-side key norm), or KEYP the fp32
-// per-feature key gains
+// One W_V for every branch (the same pointer): W_V e is computed once per tile.
+bool shared_wv(const GateArgs& a) {
+  bool shared = a.n_branch > 1;
+  for (int m = 0; m < a.n_branch; ++m) shared = shared && a.wv[m] == a.wv[0];
+  return shared;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// wk_bytes: the gain-folded key weights (the memory-side key norm), or KEYP and fp8 the
+// fp32 per-feature key gains.  fp8 adds the codes and scales of both weights (W_V once
+// when shared) and of the memory vectors.
 struct ScratchLayout {
   size_t wk_bytes, part_bytes, alpha_bytes, counter_bytes, total;
+  size_t k8_bytes, v8_bytes, sk_bytes, sv_bytes, e8_bytes, tok_bytes;
   int n_counters;
 };
 
-ScratchLayout layout_for(const GateArgs& a) {
+ScratchLayout layout_for(const GateArgs& a, bool fp8) {
   ScratchLayout L;
-  L.wk_bytes = a.key_norm == ENGRAM_KEY_NORM_PROJECTED
-                   ? ((size_t)a.n_branch * a.d_model * 4 + 255) & ~(size_t)255
-                   : ((size_t)a.n_branch * a.d_model * a.d_mem * 2 + 255) & ~(size_t)255;
+  L.wk_bytes = (a.key_norm == ENGRAM_KEY_NORM_PROJECTED || fp8) ? round256((size_t)a.n_branch * a.d_model * 4)
+                                                                 : round256((size_t)a.n_branch * a.d_model * a.d_mem * 2);
   const size_t part_elems = (size_t)a.n_branch * a.n_ftiles * (size_t)a.n_tok;
-  L.part_bytes = (part_elems * 4 + 255) & ~(size_t)255;
-  L.alpha_bytes = ((size_t)a.n_branch * (size_t)a.n_tok * 4 + 255) & ~(size_t)255;
+  L.part_bytes = round256(part_elems * 4);
+  L.alpha_bytes = round256((size_t)a.n_branch * (size_t)a.n_tok * 4);
   L.n_counters = NQ + a.n_branch * a.n_ttiles;
-  L.counter_bytes = ((size_t)L.n_counters * 4 + 255) & ~(size_t)255;
+  L.counter_bytes = round256((size_t)L.n_counters * 4);
   L.total = L.wk_bytes + 3 * L.part_bytes + L.alpha_bytes + L.counter_bytes;
+  L.k8_bytes = L.v8_bytes = L.sk_bytes = L.sv_bytes = L.e8_bytes = L.tok_bytes = 0;
+  if (fp8) {
+    const size_t n_wv = shared_wv(a) ? 1 : (size_t)a.n_branch;
+    L.k8_bytes = round256((size_t)a.n_branch * a.d_model * a.d_mem);
+    L.v8_bytes = round256(n_wv * a.d_model * a.d_mem);
+    L.sk_bytes = round256((size_t)a.n_branch * a.d_model * 4);
+    L.sv_bytes = round256(n_wv * a.d_model * 4);
+    L.e8_bytes = round256((size_t)a.n_tok * a.d_mem);
+    L.tok_bytes = round256((size_t)a.n_tok * 4);
+    L.total += L.k8_bytes + L.v8_bytes + L.sk_bytes + L.sv_bytes + L.e8_bytes + 2 * L.tok_bytes;
+  }
   return L;
 }
 
@@ -882,17 +1043,18 @@ int cu_count() {
 
 }  // namespace
 
-size_t gate_bf16_scratch_bytes(GateArgs& a) {
+size_t gate_bf16_scratch_bytes(GateArgs& a, bool fp8) {
   a.n_ftiles = (a.d_model + BF - 1) / BF;
   a.n_ttiles = (int32_t)((a.n_tok + BT - 1) / BT);
-  return layout_for(a).total;
+  return layout_for(a, fp8).total;
 }
 
 // `a.part_dot` must point at the scratch block of gate_bf16_scratch_bytes(a) bytes;
 // the other scratch pointers are carved from it here.
-void launch_gate_bf16(const GateArgs& a_in, hipStream_t s) {
+void launch_gate_bf16(const GateArgs& a_in, bool fp8, hipStream_t s) {
   GateArgs a = a_in;
-  const ScratchLayout L = layout_for(a);
+  const ScratchLayout L = layout_for(a, fp8);
+  const bool shared_v = shared_wv(a);
   char* base = (char*)a_in.part_dot;
   uint16_t* wk_scaled = (uint16_t*)base;
   a.part_dot = (float*)(base + L.wk_bytes);
@@ -902,7 +1064,42 @@ void launch_gate_bf16(const GateArgs& a_in, hipStream_t s) {
   a.counters = (int32_t*)(base + L.wk_bytes + 3 * L.part_bytes + L.alpha_bytes);
 
   const bool keyp = a.key_norm == ENGRAM_KEY_NORM_PROJECTED;
-  if (keyp) {
+  if (fp8) {
+    // the key gains and the counters, then the E4M3 codes: W_K with both gains folded
+    // in (memory-side key norm) or as is, W_V, and the memory vectors with their sums
+    // of squares
+    a.kgain = (float*)base;
+    const int64_t work = (int64_t)a.n_branch * a.d_model > L.n_counters ? (int64_t)a.n_branch * a.d_model
+                                                                         : L.n_counters;
+    hipLaunchKernelGGL(gate_prep_projected_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, a,
+                       L.n_counters);
+    char* p = base + L.total - (L.k8_bytes + L.v8_bytes + L.sk_bytes + L.sv_bytes + L.e8_bytes + 2 * L.tok_bytes);
+    uint8_t* k8 = (uint8_t*)p;
+    uint8_t* v8 = (uint8_t*)(p += L.k8_bytes);
+    float* sk = (float*)(p += L.v8_bytes);
+    float* sv = (float*)(p += L.sk_bytes);
+    uint8_t* e8 = (uint8_t*)(p += L.sv_bytes);
+    float* se = (float*)(p += L.e8_bytes);
+    float* essq = (float*)(p += L.tok_bytes);
+    const size_t wsz = (size_t)a.d_model * a.d_mem;
+    for (int m = 0; m < a.n_branch; ++m) {
+      launch_quant_rows(a.wk[m], true, a.d_model, a.d_mem, keyp ? nullptr : a.gq[m], keyp ? nullptr : a.gk[m],
+                        k8 + m * wsz, sk + (size_t)m * a.d_model, nullptr, s);
+      if (m == 0 || !shared_v)
+        launch_quant_rows(a.wv[m], true, a.d_model, a.d_mem, nullptr, nullptr, v8 + m * wsz,
+                          sv + (size_t)m * a.d_model, nullptr, s);
+    }
+    launch_quant_rows(a.mem, true, a.n_tok, a.d_mem, nullptr, nullptr, e8, se, essq, s);
+    for (int m = 0; m < a.n_branch; ++m) {
+      a.wk[m] = k8 + m * wsz;
+      a.wv[m] = v8 + (shared_v ? 0 : m) * wsz;
+    }
+    a.mem = e8;
+    a.sk = sk;
+    a.sv = sv;
+    a.se = se;
+    a.e_ssq = essq;
+  } else if (keyp) {
     a.kgain = (float*)base;
     const int64_t work = (int64_t)a.n_branch * a.d_model > L.n_counters ? (int64_t)a.n_branch * a.d_model
                                                                          : L.n_counters;
@@ -918,23 +1115,28 @@ void launch_gate_bf16(const GateArgs& a_in, hipStream_t s) {
 
   int grid = cu_count() / NQ * NQ;
   if (grid < NQ) grid = NQ;
-  bool values = false, shared_v = a.n_branch > 1;
-  for (int m = 0; m < a.n_branch; ++m) {
-    values = values || a.vout[m] != nullptr;
-    shared_v = shared_v && a.wv[m] == a.wv[0];
-  }
+  bool values = false;
+  for (int m = 0; m < a.n_branch; ++m) values = values || a.vout[m] != nullptr;
   const dim3 g((unsigned)grid), b(NTHR);
-#define ENGRAM_GATE_LAUNCH(V_, K_, S_)                                                     \
-  if (values == V_ && keyp == K_ && shared_v == S_)                                        \
-    hipLaunchKernelGGL((gate_persistent_kernel<V_, K_, S_>), g, b, 0, s, a);
-  ENGRAM_GATE_LAUNCH(false, false, false)
-  ENGRAM_GATE_LAUNCH(false, false, true)
-  ENGRAM_GATE_LAUNCH(false, true, false)
-  ENGRAM_GATE_LAUNCH(false, true, true)
-  ENGRAM_GATE_LAUNCH(true, false, false)
-  ENGRAM_GATE_LAUNCH(true, false, true)
-  ENGRAM_GATE_LAUNCH(true, true, false)
-  ENGRAM_GATE_LAUNCH(true, true, true)
+#define ENGRAM_GATE_LAUNCH(V_, K_, S_, F_)                                                 \
+  if (values == V_ && keyp == K_ && shared_v == S_ && fp8 == F_)                           \
+    hipLaunchKernelGGL((gate_persistent_kernel<V_, K_, S_, F_>), g, b, 0, s, a);
+  ENGRAM_GATE_LAUNCH(false, false, false, false)
+  ENGRAM_GATE_LAUNCH(false, false, true, false)
+  ENGRAM_GATE_LAUNCH(false, true, false, false)
+  ENGRAM_GATE_LAUNCH(false, true, true, false)
+  ENGRAM_GATE_LAUNCH(true, false, false, false)
+  ENGRAM_GATE_LAUNCH(true, false, true, false)
+  ENGRAM_GATE_LAUNCH(true, true, false, false)
+  ENGRAM_GATE_LAUNCH(true, true, true, false)
+  ENGRAM_GATE_LAUNCH(false, false, false, true)
+  ENGRAM_GATE_LAUNCH(false, false, true, true)
+  ENGRAM_GATE_LAUNCH(false, true, false, true)
+  ENGRAM_GATE_LAUNCH(false, true, true, true)
+  ENGRAM_GATE_LAUNCH(true, false, false, true)
+  ENGRAM_GATE_LAUNCH(true, false, true, true)
+  ENGRAM_GATE_LAUNCH(true, true, false, true)
+  ENGRAM_GATE_LAUNCH(true, true, true, true)
 #undef ENGRAM_GATE_LAUNCH
 }
 

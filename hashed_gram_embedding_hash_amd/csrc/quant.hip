@@ -9,12 +9,14 @@
 // so that the largest element of every row lands on the largest finite code.
 //
 // E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent field 0 holds the
-// subnormals m * 2^-9; 0x7E = 1.75 * 2^8 = 448 is the largest finite value.
+// subnormals m * 2^-9; 0x7E = 1.75 * 2^8 = 448 is the largest finite value.  This is
+// the format of gfx950's FP8 conversion and matrix instructions.
 //
-// One wavefront per row.  Rows are read twice (max, then codes) as 16-byte chunks; the
-// second read hits L2 for the row just scanned.  Optionally the row's gains are folded
-// in first (x[r][c] = (grow[r] * x[r][c]) * gcol[c] in fp32) and the sum of squares of
-// the dequantized row is returned (the memory vector's RMS for the gate).
+// One wavefront per row.  Rows of up to 4096 columns are read once into registers
+// (R 8-value chunks per lane) and encoded from there; longer rows are read twice (max,
+// then codes), the second read mostly from cache.  Optionally the row's gains are
+// folded in first (x[r][c] = (grow[r] * x[r][c]) * gcol[c] in fp32) and the sum of
+// squares of the dequantized row is returned (the memory vector's RMS for the gate).
 #include "engram_internal.h"
 
 namespace engram {
@@ -22,33 +24,29 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// E4M3 code of v (round to nearest even, saturating), from v's binary32 fields.
-__device__ __forceinline__ uint32_t e4m3_code(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t mag = u & 0x7fffffffu;
-  if (mag >= 0x43e00000u) return sign | 0x7eu;  // |v| >= 448
-  const int ex = (int)(mag >> 23) - 127;         // |v| in [2^ex, 2^(ex+1)) (fp32 normals)
-  if (ex < -6) {
-    // subnormal range of E4M3: spacing 2^-9; 8 * 2^-9 is the smallest normal (code 0x08)
-    const float r = __builtin_rintf(__builtin_ldexpf(__uint_as_float(mag), 9));
-    return sign | (uint32_t)r;
-  }
-  // normal range: 8 steps of 2^(ex-3) per binade; r in [8, 16]
-  uint32_t r = (uint32_t)__builtin_rintf(__builtin_ldexpf(__uint_as_float(mag), 3 - ex));
-  int e = ex;
-  if (r == 16u) {
-    r = 8u;
-    ++e;
-  }
-  const uint32_t code = ((uint32_t)(e + 7) << 3) | (r - 8u);
-  return sign | (code > 0x7eu ? 0x7eu : code);
+// The codes of four quotients x / s, packed little-endian.  gfx950's conversion
+// instruction rounds to the nearest E4M3 value, ties to even, exactly as the
+// definition above (checked for every finite fp32 input below 464 in magnitude); the
+// clamp makes it saturate like the definition where a quotient could exceed that (an
+// fp32 row whose maximum underflows the scale to zero).  Inputs are finite.
+__device__ __forceinline__ uint32_t e4m3_pack4(float q0, float q1, float q2, float q3) {
+  auto sat = [](float q) { return fminf(fmaxf(q, -448.0f), 448.0f); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(q0), sat(q1), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(q2), sat(q3), w, true);
+  return (uint32_t)w;
 }
 
-__device__ __forceinline__ float e4m3_value(uint32_t c) {
-  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  const float v = e == 0 ? __builtin_ldexpf((float)m, -9) : __builtin_ldexpf((float)(8u + m), (int)e - 10);
-  return (c & 0x80u) ? -v : v;
+// The value of byte B of a packed word of codes (exact).
+template <int B>
+__device__ __forceinline__ float e4m3_byte(uint32_t w) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)w, B);
+}
+
+// The sum of squares of the four dequantized values d = value(code) * s of a word.
+__device__ __forceinline__ float sumsq4(uint32_t w, float s) {
+  const float d0 = e4m3_byte<0>(w) * s, d1 = e4m3_byte<1>(w) * s;
+  const float d2 = e4m3_byte<2>(w) * s, d3 = e4m3_byte<3>(w) * s;
+  return ((d0 * d0 + d1 * d1) + d2 * d2) + d3 * d3;
 }
 
 __device__ __forceinline__ float bf16_at(const uint16_t* p, int64_t i) {
@@ -119,14 +117,8 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* src, int64_
       fold(2 * c16 + h, x);
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const uint32_t c = e4m3_code(x[4 * q + b] / s);
-          const float d = e4m3_value(c) * s;
-          ss += d * d;
-          w |= c << (8 * b);
-        }
+        const uint32_t w = e4m3_pack4(x[4 * q] / s, x[4 * q + 1] / s, x[4 * q + 2] / s, x[4 * q + 3] / s);
+        ss += sumsq4(w, s);
         o[2 * h + q] = w;
       }
     }
@@ -142,17 +134,95 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* src, int64_
   }
 }
 
+// Rows held in registers: lane l owns 8-value chunks l, l + 64, .., l + 64 (R - 1).
+template <bool BF16, int R>
+__global__ __launch_bounds__(256) void quant_rows_reg_kernel(const void* src, int64_t rows, int32_t cols,
+                                                             const void* grow, const void* gcol, uint8_t* codes,
+                                                             float* scales, float* sumsq) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;  // uniform per wavefront
+  const int lane = threadIdx.x & 63;
+  const int n8 = cols / 8;
+  const char* row = (const char*)src + r * (int64_t)cols * (BF16 ? 2 : 4);
+  const float gr = grow == nullptr ? 1.f
+                                   : (BF16 ? bf16_at((const uint16_t*)grow, r) : ((const float*)grow)[r]);
+  float x[R][8];
+  float mx = 0.f;
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int c8 = lane + 64 * k;
+    if (c8 < n8) {
+      load8<BF16>(row, c8, x[k]);
+      if (grow != nullptr || gcol != nullptr) {
+        float gc[8];
+        if (gcol != nullptr) load8<BF16>(gcol, c8, gc);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[k][i] = (gr * x[k][i]) * (gcol != nullptr ? gc[i] : 1.f);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(x[k][i]));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  const float s = mx > 0.f ? mx / 448.0f : 1.0f;
+  float ss = 0.f;
+  uint8_t* out = codes + r * (int64_t)cols;
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int c8 = lane + 64 * k;
+    if (c8 < n8) {
+      uint32_t w[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const float* v = x[k] + 4 * q;
+        w[q] = e4m3_pack4(v[0] / s, v[1] / s, v[2] / s, v[3] / s);
+        ss += sumsq4(w[q], s);
+      }
+      *reinterpret_cast<uint2*>(out + c8 * 8) = make_uint2(w[0], w[1]);
+    }
+  }
+  if (sumsq != nullptr) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+  }
+  if (lane == 0) {
+    scales[r] = s;
+    if (sumsq != nullptr) sumsq[r] = ss;
+  }
+}
+
+template <bool BF16>
+void launch_rows(const void* src, int64_t rows, int32_t cols, const void* grow, const void* gcol, uint8_t* codes,
+                 float* scales, float* sumsq, hipStream_t s) {
+  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  const int per_lane = (cols / 8 + 63) / 64;
+  if (per_lane <= 1)
+    hipLaunchKernelGGL((quant_rows_reg_kernel<BF16, 1>), grid, block, 0, s, src, rows, cols, grow, gcol, codes,
+                       scales, sumsq);
+  else if (per_lane <= 2)
+    hipLaunchKernelGGL((quant_rows_reg_kernel<BF16, 2>), grid, block, 0, s, src, rows, cols, grow, gcol, codes,
+                       scales, sumsq);
+  else if (per_lane <= 3)
+    hipLaunchKernelGGL((quant_rows_reg_kernel<BF16, 3>), grid, block, 0, s, src, rows, cols, grow, gcol, codes,
+                       scales, sumsq);
+  else if (per_lane <= 4)
+    hipLaunchKernelGGL((quant_rows_reg_kernel<BF16, 4>), grid, block, 0, s, src, rows, cols, grow, gcol, codes,
+                       scales, sumsq);
+  else if (per_lane <= 8)
+    hipLaunchKernelGGL((quant_rows_reg_kernel<BF16, 8>), grid, block, 0, s, src, rows, cols, grow, gcol, codes,
+                       scales, sumsq);
+  else
+    hipLaunchKernelGGL(quant_rows_kernel<BF16>, grid, block, 0, s, src, rows, cols, grow, gcol, codes, scales,
+                       sumsq);
+}
+
 }  // namespace
 
 void launch_quant_rows(const void* src, bool bf16, int64_t rows, int32_t cols, const void* grow, const void* gcol,
                        uint8_t* codes, float* scales, float* sumsq, hipStream_t s) {
-  const dim3 grid((unsigned)((rows + 3) / 4));
-  if (bf16)
-    hipLaunchKernelGGL(quant_rows_kernel<true>, grid, dim3(256), 0, s, src, rows, cols, grow, gcol, codes, scales,
-                       sumsq);
-  else
-    hipLaunchKernelGGL(quant_rows_kernel<false>, grid, dim3(256), 0, s, src, rows, cols, grow, gcol, codes, scales,
-                       sumsq);
+  if (bf16) launch_rows<true>(src, rows, cols, grow, gcol, codes, scales, sumsq, s);
+  else launch_rows<false>(src, rows, cols, grow, gcol, codes, scales, sumsq, s);
 }
 
 }  // namespace engram

@@ -283,6 +283,27 @@ engram_status engram_prefetch_host_cached(const int32_t* idx, int64_t n_tok, int
 engram_status engram_quantize_fp8(const void* src, int64_t rows, int32_t cols, engram_dtype dtype, uint8_t* codes,
                                   float* scales, float* sumsq, hipStream_t stream);
 
+/*
+ * Context-aware gating with FP8 projections -- section 2.4 (the projections as FP8
+ * matrix multiplications) applied to engram_gate_forward's computation.  The same
+ * arguments and results as engram_gate_forward, with these differences:
+ *   - the operands of both projections are the per-row E4M3 quantizations of
+ *     engram_quantize_fp8: the key weights (with ENGRAM_KEY_NORM_MEMORY the matrix
+ *     gq[m][f] * Wk[m][f][c] * gk[m][c], formed in fp32, otherwise Wk[m] itself), Wv[m],
+ *     and every memory vector mem_t; k and v are the exact products of the decoded
+ *     codes times the two rows' scales, accumulated in fp32;
+ *   - with ENGRAM_KEY_NORM_MEMORY the memory vector's norm is that of its quantized
+ *     (decoded and scaled) form;
+ *   - dtype must be ENGRAM_BF16 and d_mem % 128 == 0 (UNSUPPORTED otherwise).
+ * The codes are made on every call, in library-owned scratch.
+ */
+engram_status engram_gate_forward_fp8(const void* mem, int64_t n_tok, int32_t d_mem, int32_t d_model,
+                                      int32_t n_branch, const void* const* h, const void* const* wk,
+                                      const void* const* wv, const void* const* gq,
+                                      const void* const* gk, float eps, engram_dtype dtype,
+                                      engram_key_norm key_norm, void* const* out, float* gate_out,
+                                      void* const* value_out, hipStream_t stream);
+
 /* Pinned, device-mapped host allocation for offloaded tables (hipHostMalloc,
  * hipHostMallocMapped | hipHostMallocPortable). *ptr is NULL on failure. */
 engram_status engram_host_alloc(size_t bytes, void** ptr);

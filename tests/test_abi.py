@@ -116,6 +116,22 @@ def test_gate_argument_errors():
     assert gf(n=0) == _st("ok")
 
 
+def test_gate_fp8_argument_errors():
+    L = eg.lib()
+    one = (ctypes.c_void_p * 1)(4096)
+    gf = lambda **kw: L.engram_gate_forward_fp8(
+        ctypes.c_void_p(4096), kw.get("n", 8), kw.get("dm", 1280), kw.get("dmod", 2560), kw.get("nb", 1),
+        one, one, one, one, one, ctypes.c_float(1e-6), kw.get("dt", eg.BF16), kw.get("kn", 0), one, None, None,
+        None)
+    assert gf(dm=1216) == _st("unsup")             # a multiple of 64 but not of 128
+    assert b"multiple of 128" in L.engram_last_error()
+    assert gf(dt=eg.F32) == _st("unsup")
+    assert gf(dmod=2500) == _st("unsup")
+    assert gf(nb=0) == _st("arg")
+    assert gf(kn=3) == _st("arg")
+    assert gf(n=0) == _st("ok")
+
+
 def test_conv_argument_errors():
     L = eg.lib()
     cf = lambda **kw: L.engram_conv_forward(

@@ -736,3 +736,116 @@ def test_quantize_fp8_codes_bit_exact():
     assert np.all(want_s2 == 1.0)
     assert np.array_equal(codes2.cpu().numpy(), want_c2)
     assert np.array_equal(scales2.cpu().numpy(), want_s2)
+
+
+@pytest.mark.parametrize("cols", [16, 1024, 2064, 4096, 4112, 8192])
+def test_quantize_fp8_row_widths(cols):
+    """Every row width class of the quantizer: rows held in registers as 1, 2, 3, 4 or 8
+    chunks of 8 per lane (16 .. 4096 columns, ragged last chunks included) and the
+    two-pass form beyond 4096 columns; codes and scales bit-exact, sums of squares to
+    fp32 summation error."""
+    say(f"fp8 quantization, {cols} columns")
+    rng = np.random.default_rng(cols)
+    x = (rng.standard_normal((37, cols)) * np.exp2(rng.uniform(-8, 8, (37, 1)))).astype(np.float32)
+    x[5] = 0.0
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    codes, scales, ss = eg.engram_quantize_fp8(xb.to(DEV), with_sumsq=True)
+    want_c, want_s = oracle.quant_rows(xb.float().numpy())
+    assert np.array_equal(codes.cpu().numpy(), want_c)
+    assert np.array_equal(scales.cpu().numpy(), want_s)
+    deq = oracle.e4m3_decode(want_c) * want_s[:, None].astype(np.float64)
+    np.testing.assert_allclose(ss.cpu().numpy(), (deq ** 2).sum(axis=1), rtol=1e-5, atol=0)
+
+
+def _gate_fp8_case(n_tok, d_mem, d_model, key_norm, n_branch=1, shared=False, inplace=False, values=False,
+                   seed=0, e_std=1.0):
+    """engram_gate_forward_fp8 against oracle.gate_fp8 (the same E4M3 codes; the two
+    differ only in fp32 against fp64 arithmetic and the bf16 rounding of the outputs),
+    on unit-scale memory so that |alpha v| ~ 0.5 and the update bar applies."""
+    g = torch.Generator().manual_seed(seed)
+    e = (torch.randn(n_tok, d_mem, generator=g) * e_std).to(torch.bfloat16)
+    hs = [torch.randn(n_tok, d_model, generator=g).to(torch.bfloat16) for _ in range(n_branch)]
+    wks = [(torch.randn(d_model, d_mem, generator=g) / d_mem ** 0.5).to(torch.bfloat16) for _ in range(n_branch)]
+    nwv = 1 if shared else n_branch
+    wvs = [(torch.randn(d_model, d_mem, generator=g) / d_mem ** 0.5).to(torch.bfloat16) for _ in range(nwv)]
+    nk = d_mem if key_norm == eg.KEY_NORM_MEMORY else d_model
+    gqs = [(1 + 0.2 * torch.randn(d_model, generator=g)).to(torch.bfloat16) for _ in range(n_branch)]
+    gks = [(1 + 0.2 * torch.randn(nk, generator=g)).to(torch.bfloat16) for _ in range(n_branch)]
+    dv = lambda xs: [x.to(DEV) for x in xs]
+    wv_d = dv(wvs)
+    h_d = dv(hs)
+    alpha = torch.empty((n_branch, n_tok), dtype=torch.float32, device=DEV)
+    vout = [torch.empty_like(h) for h in h_d] if values else None
+    out = eg.engram_gate_forward(e.to(DEV), h_d, dv(wks), [wv_d[0]] * n_branch if shared else wv_d, dv(gqs),
+                                 dv(gks), 1e-6, out=h_d if inplace else None, gate_out=alpha, value_out=vout,
+                                 key_norm=key_norm, fp8=True)
+    torch.cuda.synchronize()
+    for m in range(n_branch):
+        out_o, alpha_o = oracle.gate_fp8(host_view(e), host_view(hs[m]), host_view(wks[m]),
+                                         host_view(wvs[0 if shared else m]), host_view(gqs[m]), host_view(gks[m]),
+                                         1e-6, oracle.BF16, key_norm=key_norm)
+        err = rel_err(out[m].float().cpu().numpy(), out_o)
+        aerr = np.abs(alpha[m].cpu().numpy() - alpha_o).max()
+        upd_o = out_o - host_bf16_to_f64(hs[m])
+        upd = rel_err(out[m].float().cpu().numpy() - host_bf16_to_f64(hs[m]), upd_o)
+        msg = f"  branch {m}: out rel err {err:.2e}, alpha abs err {aerr:.2e}, update rel err {upd:.2e}"
+        if values:
+            verr = rel_err(vout[m].float().cpu().numpy(), upd_o)
+            msg += f", value rel err {verr:.2e}"
+            assert verr <= 1e-2
+        say(msg)
+        assert err <= 1e-2 and aerr <= ALPHA_TOL_BF16 and upd <= UPDATE_TOL_STRESS
+
+
+@pytest.mark.parametrize("key_norm", [eg.KEY_NORM_MEMORY, eg.KEY_NORM_PROJECTED])
+def test_gate_fp8_small_ragged(key_norm):
+    """d_mem 1280 (10 k-steps of 128), d_model 2560; 300 tokens = one full and one
+    ragged token tile."""
+    say(f"gate fp8 small 300 key_norm {key_norm}")
+    _gate_fp8_case(300, 1280, 2560, key_norm, seed=70 + key_norm)
+
+
+@pytest.mark.parametrize("d_mem,d_model,key_norm", [
+    (128, 544, eg.KEY_NORM_MEMORY),       # one k-step (every chunk of the tail path), ragged feature tile
+    (384, 800, eg.KEY_NORM_PROJECTED),    # three k-steps: no steady k-step
+    (512, 1056, eg.KEY_NORM_MEMORY),      # four: one steady k-step
+    (1152, 2080, eg.KEY_NORM_PROJECTED),  # nine (odd), last feature tile 32 wide
+])
+def test_gate_fp8_k_steps_and_feature_tiles(d_mem, d_model, key_norm):
+    say(f"gate fp8 d_mem {d_mem} d_model {d_model} key_norm {key_norm}")
+    _gate_fp8_case(333, d_mem, d_model, key_norm, seed=d_mem + d_model)
+
+
+def test_gate_fp8_branches_shared_wv_values_in_place():
+    """Three branches sharing W_V (one quantized copy, one V tile per token tile for all
+    branches), in place, with the gated values written too."""
+    say("gate fp8 3 branches shared W_V, value_out, in place")
+    _gate_fp8_case(600, 1280, 1536, eg.KEY_NORM_MEMORY, n_branch=3, shared=True, inplace=True, values=True,
+                   seed=77)
+
+
+def test_gate_fp8_two_branches_own_weights_projected():
+    say("gate fp8 2 branches own W_V, projected key")
+    _gate_fp8_case(280, 640, 1024, eg.KEY_NORM_PROJECTED, n_branch=2, seed=78)
+
+
+def test_gate_fp8_scale_invariance_of_memory():
+    """Per-token scaling makes the FP8 gate's alpha invariant to scaling mem by a power
+    of two (the codes are unchanged, the scale absorbs it; RMSNorm removes it from the
+    key): alpha equal to 1e-6 for mem x 1 and mem x 2^-20 (eps then matters: 1e-20)."""
+    say("gate fp8 power-of-two scale of mem")
+    g = torch.Generator().manual_seed(79)
+    n, d_mem, d_model = 200, 640, 768
+    e = torch.randn(n, d_mem, generator=g).to(torch.bfloat16)
+    h = torch.randn(n, d_model, generator=g).to(torch.bfloat16).to(DEV)
+    wk = (torch.randn(d_model, d_mem, generator=g) / d_mem ** 0.5).to(torch.bfloat16).to(DEV)
+    wv = (torch.randn(d_model, d_mem, generator=g) / d_mem ** 0.5).to(torch.bfloat16).to(DEV)
+    gq = torch.ones(d_model, dtype=torch.bfloat16, device=DEV)
+    gk = torch.ones(d_mem, dtype=torch.bfloat16, device=DEV)
+    alphas = []
+    for s in (1.0, 2.0 ** -20):
+        a = torch.empty((1, n), dtype=torch.float32, device=DEV)
+        eg.engram_gate_forward((e.float() * s).to(torch.bfloat16).to(DEV), [h], [wk], [wv], [gq], [gk], 1e-20,
+                               gate_out=a, fp8=True)
+        alphas.append(a.cpu().numpy())
+    assert np.abs(alphas[0] - alphas[1]).max() <= 1e-6
