@@ -54,6 +54,7 @@ def parse():
                    help="memory: k = W_K RMSNorm(e) (default); projected: k = RMSNorm(W_K e), Eq. 4")
     p.add_argument("--fp8", action="store_true",
                    help="gate projections on E4M3 codes (engram_gate_forward_fp8; quantization inside the call)")
+    p.add_argument("--no-fp8", action="store_true", help="skip the extra fp8-gate step measurement")
     p.add_argument("--no-graph", action="store_true",
                    help="time the eagerly launched step only (default: the step is also captured in a HIP graph "
                         "and the graph replay is the reported value)")
@@ -525,75 +526,81 @@ def main():
     bufs = layer.buffers(cfg.batch, cfg.seq)
     raw, h = inp["raw"], inp["h"]
 
-    def step(ev=None):
-        # compress and hash in one kernel (engram_compress_hash), then gather, then gate
-        if ev is not None:
-            ev[0].record()
-        eg.engram_compress_hash(raw, layer.cmap, layer.orders, layer.heads, layer.mult, layer.rows, layer.pad_id,
-                                out=bufs["idx"])
-        if ev is not None:
-            ev[1].record()
-        eg.engram_gather(bufs["idx"], layer.tables, out=bufs["mem"])
-        if ev is not None:
-            ev[2].record()
-        eg.engram_gate_forward(bufs["mem"], h, layer.wk, layer.wv, layer.gq, layer.gk, cfg.eps, out=outs,
-                               key_norm=layer.key_norm, fp8=args.fp8)
-        if ev is not None:
-            ev[3].record()
+    def make_step(fp8):
+        def step(ev=None):
+            # compress and hash in one kernel (engram_compress_hash), then gather, then gate
+            if ev is not None:
+                ev[0].record()
+            eg.engram_compress_hash(raw, layer.cmap, layer.orders, layer.heads, layer.mult, layer.rows,
+                                    layer.pad_id, out=bufs["idx"])
+            if ev is not None:
+                ev[1].record()
+            eg.engram_gather(bufs["idx"], layer.tables, out=bufs["mem"])
+            if ev is not None:
+                ev[2].record()
+            eg.engram_gate_forward(bufs["mem"], h, layer.wk, layer.wv, layer.gq, layer.gk, cfg.eps, out=outs,
+                                   key_norm=layer.key_norm, fp8=fp8)
+            if ev is not None:
+                ev[3].record()
+        return step
 
     flush = (torch.empty(args.flush_mb << 18, dtype=torch.float32, device=dev) if args.flush_mb > 0 else None)
-
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # The same step captured once in a HIP graph (a launch per step instead of one per
-    # kernel).  Two eager steps on the capture stream come first, so the gate's scratch is
-    # sized and last used on that stream (no allocation or cross-stream wait is recorded).
-    graph = None
-    if not args.no_graph:
-        gs = torch.cuda.Stream()
-        gs.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(gs):
-            step()
-            step()
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=gs):
-            step()
-        torch.cuda.synchronize()
-        for _ in range(5):
-            graph.replay()
-        torch.cuda.synchronize()
-
-    # Timed: each iteration runs the eager step (events between its calls give the
-    # per-call breakdown and the gate's time) and then the graph replay, each after the
-    # cache flush, so both see the same clocks and the same cold caches.
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    print(f"[bench] timing {args.steps} steps" + ("" if graph is None else " and graph replays"),
-          file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    for i in range(args.steps):
-        if flush is not None:
-            flush.fill_(float(i))       # evicts L2 and MALL; outside the step's events
-        step(evs[i])
-        if graph is not None:
-            if flush is not None:
-                flush.fill_(float(i) + 0.5)
-            gev[i][0].record()
-            graph.replay()
-            gev[i][1].record()
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    # per-step time: first to last event of each step (the flush between steps excluded)
-    ms_eager = sum(evs[i][0].elapsed_time(evs[i][3]) for i in range(args.steps)) / args.steps
-    ms_step = ms_eager if graph is None else sum(a.elapsed_time(b) for a, b in gev) / args.steps
     names = ["compress_hash", "gather", "gate"]
-    per = {n: sum(evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(args.steps)) / args.steps
-           for k, n in enumerate(names)}
+
+    def time_steps(step, n_steps, n_warm, use_graph):
+        """Warm-up, then n_steps iterations of: the eager step (events between its calls give
+        the per-call breakdown) and the graph replay, each after the cache flush, so both see
+        the same clocks and the same cold caches.  Returns (ms per step, ms eager, per-call
+        ms, wall seconds)."""
+        print(f"[bench] warmup {n_warm}", file=sys.stderr, flush=True)
+        for _ in range(n_warm):
+            step()
+        torch.cuda.synchronize()
+        # The same step captured once in a HIP graph (a launch per step instead of one per
+        # kernel).  Two eager steps on the capture stream come first, so the gate's scratch
+        # is sized and last used on that stream (no allocation or cross-stream wait is
+        # recorded).
+        graph = None
+        if use_graph:
+            gs = torch.cuda.Stream()
+            gs.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(gs):
+                step()
+                step()
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph, stream=gs):
+                step()
+            torch.cuda.synchronize()
+            for _ in range(5):
+                graph.replay()
+            torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_steps)]
+        gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_steps)]
+        print(f"[bench] timing {n_steps} steps" + ("" if graph is None else " and graph replays"),
+              file=sys.stderr, flush=True)
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter()
+        for i in range(n_steps):
+            if flush is not None:
+                flush.fill_(float(i))       # evicts L2 and MALL; outside the step's events
+            step(evs[i])
+            if graph is not None:
+                if flush is not None:
+                    flush.fill_(float(i) + 0.5)
+                gev[i][0].record()
+                graph.replay()
+                gev[i][1].record()
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter() - t_wall
+        # per-step time: first to last event of each step (the flush between steps excluded)
+        ms_eager = sum(evs[i][0].elapsed_time(evs[i][3]) for i in range(n_steps)) / n_steps
+        ms_step = ms_eager if graph is None else sum(a.elapsed_time(b) for a, b in gev) / n_steps
+        per = {n: sum(evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(n_steps)) / n_steps
+               for k, n in enumerate(names)}
+        return ms_step, ms_eager, per, t_wall
+
+    ms_step, ms_eager, per, t_wall = time_steps(make_step(args.fp8), args.steps, args.warmup, not args.no_graph)
 
     work = algorithmic(cfg, args.shared_wv)
     kernels = {}
@@ -642,6 +649,22 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
     }
+    if cfg.dtype == "bf16" and not args.fp8 and not args.no_fp8:
+        # the same step with the gate's projections on E4M3 codes (engram_gate_forward_fp8,
+        # quantization of W_K, W_V and the memory vectors inside the call)
+        print("[bench] fp8 gate step", file=sys.stderr, flush=True)
+        f_ms, f_eager, f_per, _ = time_steps(make_step(True), args.steps, max(3, args.warmup // 2), not args.no_graph)
+        f_tf = work["gate"]["flops"] / (f_per["gate"] * 1e-3) / 1e12
+        result["fp8_step"] = {
+            "value": round(cfg.tokens / (f_ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(f_ms, 5),
+            "ms_per_step_eager": round(f_eager, 5),
+            "dtype": "fp8e4m3 projections (per-row scales), bf16 storage",
+            "kernels_ms": {n: round(f_per[n], 5) for n in names},
+            "gate": {"TFLOP/s": round(f_tf, 2), "peak": PEAK_FP8_TFLOPS, "frac": round(f_tf / PEAK_FP8_TFLOPS, 4),
+                     "frac_of_bf16_peak": round(f_tf / PEAK_BF16_TFLOPS, 4),
+                     "note": "events bracket the whole call: counter clear, three quantization launches "
+                             "and the persistent kernel"},
+        }
     if not args.no_conv:
         print("[bench] short convolution", file=sys.stderr, flush=True)
         result["conv"] = measure_conv(args, cfg, bufs, h, layer, outs, flush)
