@@ -3,9 +3,11 @@
 
 One step = one pass of the whole path over one batch of seeded synthetic input
 already resident in HBM: the "small" workload (4 x 4096 Zipf(1.1) tokens, 16
-bf16 tables of 1,000,003 x 80, memory dim 1280, d_model 2560, one branch).
-Prints ONE JSON line with tokens/s, the per-call breakdown, the roofline of the
-dominant kernel (the gate) and the CPU oracle's tokens/s on a bounded sample.
+bf16 tables of 1,000,003 x 80, memory dim 1280, d_model 2560, one branch), as two
+calls: engram_lookup (compression, hashing and the gather in one kernel) and
+engram_gate_forward.  Prints ONE JSON line with tokens/s, the per-call breakdown,
+the roofline of the dominant kernel (the gate), the same step with the FP8 gate,
+the short convolution beside it and the CPU oracle's tokens/s on a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--config small|multi|large|tiny]
     python bench.py --calibrate-copy MIB     # plain device copy, for HBM counter scaling
@@ -95,9 +97,9 @@ def algorithmic(cfg, shared_wv=False):
     nv = 1 if shared_wv else M
     es = 4 if cfg.dtype == "f32" else 2
     return {
-        # raw ids in, indices out (the 517-KB compression map stays in L2)
-        "compress_hash": {"bytes": 4 * T + 4 * nt * T},
-        "gather": {"bytes": 4 * nt * T + 2 * dm * es * T},
+        # raw ids in, rows read and the memory vectors written (the indices stay on chip;
+        # the 517-KB compression map stays in L2)
+        "lookup": {"bytes": 4 * T + 2 * dm * es * T},
         # weights once, memory vector once, hidden read + output written per branch
         "gate": {"flops": 2 * dm * d * (M + nv) * T,
                  "bytes": dm * es * T + (M + nv) * d * dm * es + M * 2 * d * es * T},
@@ -528,24 +530,21 @@ def main():
 
     def make_step(fp8):
         def step(ev=None):
-            # compress and hash in one kernel (engram_compress_hash), then gather, then gate
+            # compression, hashing and the gather in one kernel (engram_lookup), then the gate
             if ev is not None:
                 ev[0].record()
-            eg.engram_compress_hash(raw, layer.cmap, layer.orders, layer.heads, layer.mult, layer.rows,
-                                    layer.pad_id, out=bufs["idx"])
+            eg.engram_lookup(raw, layer.cmap, layer.orders, layer.heads, layer.mult, layer.tables, layer.pad_id,
+                             out=bufs["mem"])
             if ev is not None:
                 ev[1].record()
-            eg.engram_gather(bufs["idx"], layer.tables, out=bufs["mem"])
-            if ev is not None:
-                ev[2].record()
             eg.engram_gate_forward(bufs["mem"], h, layer.wk, layer.wv, layer.gq, layer.gk, cfg.eps, out=outs,
                                    key_norm=layer.key_norm, fp8=fp8)
             if ev is not None:
-                ev[3].record()
+                ev[2].record()
         return step
 
     flush = (torch.empty(args.flush_mb << 18, dtype=torch.float32, device=dev) if args.flush_mb > 0 else None)
-    names = ["compress_hash", "gather", "gate"]
+    names = ["lookup", "gate"]
 
     def time_steps(step, n_steps, n_warm, use_graph):
         """Warm-up, then n_steps iterations of: the eager step (events between its calls give
@@ -575,7 +574,7 @@ def main():
             for _ in range(5):
                 graph.replay()
             torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n_steps)]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(n_steps)]
         gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_steps)]
         print(f"[bench] timing {n_steps} steps" + ("" if graph is None else " and graph replays"),
               file=sys.stderr, flush=True)
@@ -594,7 +593,7 @@ def main():
         torch.cuda.synchronize()
         t_wall = time.perf_counter() - t_wall
         # per-step time: first to last event of each step (the flush between steps excluded)
-        ms_eager = sum(evs[i][0].elapsed_time(evs[i][3]) for i in range(n_steps)) / n_steps
+        ms_eager = sum(evs[i][0].elapsed_time(evs[i][-1]) for i in range(n_steps)) / n_steps
         ms_step = ms_eager if graph is None else sum(a.elapsed_time(b) for a, b in gev) / n_steps
         per = {n: sum(evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(n_steps)) / n_steps
                for k, n in enumerate(names)}

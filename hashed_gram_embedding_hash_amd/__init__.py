@@ -11,6 +11,7 @@ The functions carry the C names:
   (section 2.2, Eq. 1);
 * ``engram_compress_hash`` -- both of the above in one kernel;
 * ``engram_gather``    -- table lookup and concatenation (Eq. 1-2);
+* ``engram_lookup``    -- compression, hashing and the gather in one kernel;
 * ``engram_gate_forward`` -- context-aware gating and residual update
   (section 2.3, Eq. 3-4; section 2.4, Eq. 6 for several branches);
   ``fp8=True`` runs both projections on E4M3 codes (section 2.4);
@@ -50,7 +51,7 @@ EXPORTS = (
     "engram_last_error", "engram_version", "engram_compress", "engram_hash", "engram_gather",
     "engram_gate_forward", "engram_conv_forward", "engram_prefetch_host", "engram_host_alloc",
     "engram_host_free", "engram_cache_select", "engram_cache_build", "engram_prefetch_host_cached",
-    "engram_compress_hash", "engram_quantize_fp8", "engram_gate_forward_fp8",
+    "engram_compress_hash", "engram_quantize_fp8", "engram_gate_forward_fp8", "engram_lookup",
 )
 
 
@@ -84,6 +85,8 @@ def lib() -> ctypes.CDLL:
         L.engram_compress_hash.argtypes = [P, i32, i64, i64, i64, P, i32, P, i32, i32, P, P, i32, P, P, P, P]
         L.engram_quantize_fp8.argtypes = [P, i64, i32, i32, P, P, P, P]
         L.engram_gather.argtypes = [P, i64, i32, P, P, i32, i32, P, P, P]
+        L.engram_lookup.argtypes = [P, i32, i64, i64, i64, P, i32, P, i32, i32, P, P, i32, P, i32, i32, P, P, P, P,
+                                    P]
         L.engram_gate_forward.argtypes = [P, i64, i32, i32, i32, P, P, P, P, P, ctypes.c_float, i32, i32,
                                           P, P, P, P]
         L.engram_gate_forward_fp8.argtypes = L.engram_gate_forward.argtypes
@@ -97,7 +100,7 @@ def lib() -> ctypes.CDLL:
         for f in ("engram_compress", "engram_hash", "engram_gather", "engram_gate_forward",
                   "engram_conv_forward", "engram_prefetch_host", "engram_host_alloc", "engram_host_free",
                   "engram_cache_select", "engram_cache_build", "engram_prefetch_host_cached",
-                  "engram_compress_hash", "engram_quantize_fp8", "engram_gate_forward_fp8"):
+                  "engram_compress_hash", "engram_quantize_fp8", "engram_gate_forward_fp8", "engram_lookup"):
             getattr(L, f).restype = st
         _lib = L
     return _lib
@@ -232,6 +235,47 @@ def engram_gather(idx, tables: Sequence, out=None, err_count=None, stream=None):
     _check(lib().engram_gather(_dev(idx, "idx", torch.int32), n_tok, n_tables, ptrs, rows.ctypes.data, w,
                                _edtype(tables[0]), _dev(out, "out", dt), _opt(err_count, "err_count", torch.int32),
                                _stream(stream)))
+    return out
+
+
+def engram_lookup(raw, cmap, orders: Sequence[int], heads: int, mult, tables: Sequence, pad_id: int,
+                  t_begin: int = 0, t_count: Optional[int] = None, out=None, ids_out=None, idx_out=None,
+                  err_count=None, stream=None):
+    """engram_compress_hash then engram_gather in one kernel: the memory vectors
+    [batch * t_count, len(orders) * heads * w] of the raw ids [batch, ld].  ``cmap`` may be
+    None (raw ids are canonical); each table's row count is its hash modulus.  ``idx_out``
+    [batch * t_count, n_tables] and ``ids_out`` [batch, ld] optionally receive the indices
+    and the canonical ids."""
+    import numpy as np
+    import torch
+    batch, ld = raw.shape
+    if t_count is None:
+        t_count = ld - t_begin
+    orders_a = np.ascontiguousarray(orders, dtype=np.int32)
+    mult_a = np.ascontiguousarray(mult, dtype=np.uint64)
+    n_tables = len(orders) * heads
+    if mult_a.shape != (len(orders), heads, max(orders)) or len(tables) != n_tables:
+        raise ValueError("mult must be [n_orders][heads][max_order], one table per (order, head)")
+    w = tables[0].shape[1]
+    dt = tables[0].dtype
+    for t in tables:
+        if t.shape[1] != w or t.dtype != dt:
+            raise ValueError("all tables need the same width and dtype")
+        _dev(t, "table")
+    rows_a = np.array([t.shape[0] for t in tables], dtype=np.uint32)
+    if ids_out is not None and tuple(ids_out.shape) != (batch, ld):
+        raise ValueError("ids_out must be [batch, ld]")
+    if idx_out is not None and tuple(idx_out.shape) != (batch * t_count, n_tables):
+        raise ValueError("idx_out must be [batch * t_count, n_tables]")
+    if out is None:
+        out = torch.empty((batch * t_count, n_tables * w), dtype=dt, device=raw.device)
+    ptrs = _ptr_array([t.data_ptr() for t in tables])
+    _check(lib().engram_lookup(_dev(raw, "raw", torch.int32), batch, ld, t_begin, t_count,
+                               _opt(cmap, "map", torch.int32), 0 if cmap is None else cmap.numel(),
+                               orders_a.ctypes.data, len(orders), heads, mult_a.ctypes.data, rows_a.ctypes.data,
+                               pad_id, ptrs, w, _edtype(tables[0]), _opt(ids_out, "ids_out", torch.int32),
+                               _opt(idx_out, "idx_out", torch.int32), _dev(out, "out", dt),
+                               _opt(err_count, "err_count", torch.int32), _stream(stream)))
     return out
 
 

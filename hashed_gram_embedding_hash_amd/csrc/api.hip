@@ -180,10 +180,14 @@ engram_status engram_compress(const int32_t* raw, int64_t n, const int32_t* map,
 namespace {
 
 // engram_hash, and with `map` set engram_compress_hash
-engram_status hash_impl(const char* fn, const int32_t* ids, int32_t batch, int64_t ld, int64_t t_begin,
+// The hashing arguments, checked and copied into `a`.  *empty: nothing to launch (batch or
+// t_count is 0); then the pointers are not checked.  need_idx: idx must be non-null.
+engram_status hash_args(const char* fn, const int32_t* ids, int32_t batch, int64_t ld, int64_t t_begin,
                         int64_t t_count, const int32_t* map, int32_t vocab, const int32_t* orders,
                         int32_t n_orders, int32_t heads, const uint64_t* mult, const uint32_t* rows,
-                        int32_t pad_id, int32_t* ids_out, int32_t* idx, int32_t* err_count, hipStream_t stream) {
+                        int32_t pad_id, int32_t* ids_out, int32_t* idx, int32_t* err_count, bool need_idx,
+                        HashArgs& a, bool* empty) {
+  *empty = false;
   if (batch < 0 || ld < 0 || t_begin < 0 || t_count < 0)
     return fail(ENGRAM_ERR_INVALID_ARG, "%s: negative size", fn);
   if (t_begin + t_count > ld)
@@ -201,7 +205,6 @@ engram_status hash_impl(const char* fn, const int32_t* ids, int32_t batch, int64
                   ENGRAM_MAX_ORDER);
     if (orders[o] > max_order) max_order = orders[o];
   }
-  HashArgs a;
   memset(&a, 0, sizeof a);
   const int nt = n_orders * heads;
   for (int o = 0; o < n_orders; ++o) {
@@ -216,8 +219,11 @@ engram_status hash_impl(const char* fn, const int32_t* ids, int32_t batch, int64
       for (int j = 0; j < orders[o]; ++j) a.mult[tb][j] = mult[((int64_t)o * heads + k) * max_order + j];
     }
   }
-  if (batch == 0 || t_count == 0) return ENGRAM_OK;
-  if (ids == nullptr || idx == nullptr) return fail(ENGRAM_ERR_INVALID_ARG, "%s: null ids/idx", fn);
+  if (batch == 0 || t_count == 0) {
+    *empty = true;
+    return ENGRAM_OK;
+  }
+  if (ids == nullptr || (need_idx && idx == nullptr)) return fail(ENGRAM_ERR_INVALID_ARG, "%s: null ids/idx", fn);
   const uint64_t blocks = (uint64_t)((t_count + 63) / 64) * (uint64_t)batch;
   if (blocks >= (1ull << 31))
     return fail(ENGRAM_ERR_UNSUPPORTED, "%s: %llu workgroups exceed one launch", fn,
@@ -235,6 +241,18 @@ engram_status hash_impl(const char* fn, const int32_t* ids, int32_t batch, int64
   a.ids_out = ids_out;
   a.err_count = err_count;
   a.batch = batch;
+  return ENGRAM_OK;
+}
+
+engram_status hash_impl(const char* fn, const int32_t* ids, int32_t batch, int64_t ld, int64_t t_begin,
+                        int64_t t_count, const int32_t* map, int32_t vocab, const int32_t* orders,
+                        int32_t n_orders, int32_t heads, const uint64_t* mult, const uint32_t* rows,
+                        int32_t pad_id, int32_t* ids_out, int32_t* idx, int32_t* err_count, hipStream_t stream) {
+  HashArgs a;
+  bool empty = false;
+  const engram_status st = hash_args(fn, ids, batch, ld, t_begin, t_count, map, vocab, orders, n_orders, heads,
+                                     mult, rows, pad_id, ids_out, idx, err_count, true, a, &empty);
+  if (st != ENGRAM_OK || empty) return st;
   launch_hash(a, stream);
   return check_launch(fn);
 }
@@ -283,6 +301,42 @@ engram_status engram_gather(const int32_t* idx, int64_t n_tok, int32_t n_tables,
   a.chunks_per_row = (int32_t)(w * dtype_size(dtype) / 16);
   launch_gather(a, false, stream);
   return check_launch("engram_gather");
+}
+
+engram_status engram_lookup(const int32_t* raw, int32_t batch, int64_t ld, int64_t t_begin, int64_t t_count,
+                            const int32_t* map, int32_t vocab, const int32_t* orders, int32_t n_orders,
+                            int32_t heads, const uint64_t* mult, const uint32_t* rows, int32_t pad_id,
+                            const void* const* tables, int32_t w, engram_dtype dtype, int32_t* ids_out,
+                            int32_t* idx_out, void* out, int32_t* err_count, hipStream_t stream) {
+  const char* fn = "engram_lookup";
+  HashArgs h;
+  bool empty = false;
+  engram_status st = hash_args(fn, raw, batch, ld, t_begin, t_count, map, vocab, orders, n_orders, heads, mult,
+                               rows, pad_id, ids_out, idx_out, err_count, false, h, &empty);
+  if (st != ENGRAM_OK) return st;
+  const int nt = n_orders * heads;
+  int64_t rows64[ENGRAM_MAX_TABLES];
+  for (int b = 0; b < nt; ++b) rows64[b] = rows[b];
+  const int64_t n_tok = empty ? 0 : (int64_t)batch * t_count;
+  // the gather's checks (idx is not read: a stand-in keeps the null check quiet)
+  static const int32_t no_idx = 0;
+  st = check_gather(fn, &no_idx, n_tok, nt, tables, rows64, w, dtype, out);
+  if (st != ENGRAM_OK || empty) return st;
+  if (idx_out != nullptr && !aligned(idx_out, 4)) return fail(ENGRAM_ERR_INVALID_ARG, "%s: misaligned idx_out", fn);
+  if ((uint64_t)((t_count + 7) / 8) * (uint64_t)batch >= (1ull << 31))  // at least 8 positions per workgroup
+    return fail(ENGRAM_ERR_UNSUPPORTED, "%s: too many positions for one launch", fn);
+  GatherArgs g;
+  memset(&g, 0, sizeof g);
+  for (int b = 0; b < nt; ++b) {
+    g.table[b] = (const char*)tables[b];
+    g.rows[b] = rows64[b];
+  }
+  g.out = (char*)out;
+  g.n_tok = n_tok;
+  g.n_tables = nt;
+  g.chunks_per_row = (int32_t)(w * dtype_size(dtype) / 16);
+  launch_lookup(h, g, stream);
+  return check_launch(fn);
 }
 
 engram_status engram_prefetch_host(const int32_t* idx, int64_t n_tok, int32_t n_tables,

@@ -37,6 +37,15 @@ struct HashArgs {
 };
 void launch_hash(const HashArgs& a, hipStream_t s);
 
+// h mod M for a prime M < 2^31, with the Barrett constant m = floor((2^64 - 1) / M):
+// q = mulhi(h, m) is floor(h / M) or one less, so one conditional subtraction remains.
+__device__ __forceinline__ uint32_t mod_barrett(uint64_t h, uint32_t M, uint64_t m) {
+  const uint64_t q = __umul64hi(h, m);
+  const uint64_t r = h - q * (uint64_t)M;
+  return (uint32_t)(r >= M ? r - M : r);
+}
+
+
 // ---------------------------------------------------------------- gather / prefetch
 struct GatherArgs {
   const char* table[ENGRAM_MAX_TABLES];  // device-accessible base of each table
@@ -50,6 +59,10 @@ struct GatherArgs {
 };
 // `host_source`: the tables are pinned host memory read over PCIe (launch tuned for that).
 void launch_gather(const GatherArgs& a, bool host_source, hipStream_t s);
+// engram_lookup: the hash kernel's staging and index computation for a block of
+// positions, then the gather of their rows, in one kernel (h.idx may be null: the
+// indices then stay in LDS; g.idx is unused).
+void launch_lookup(const HashArgs& h, const GatherArgs& g, hipStream_t s);
 // prefetch from host tables through the HBM row cache (table: [n_tables][2^log2_slots])
 void launch_prefetch_cached(const GatherArgs& a, const int2* table, int log2_slots, const char* cache_rows,
                             int32_t* hits, hipStream_t s);

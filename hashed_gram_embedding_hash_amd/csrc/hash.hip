@@ -23,12 +23,6 @@ namespace {
 
 constexpr int POS = 64;  // positions per workgroup
 
-__device__ __forceinline__ uint32_t mod_barrett(uint64_t h, uint32_t M, uint64_t m) {
-  const uint64_t q = __umul64hi(h, m);
-  const uint64_t r = h - q * (uint64_t)M;
-  return (uint32_t)(r >= M ? r - M : r);
-}
-
 __global__ __launch_bounds__(256) void hash_kernel(const HashArgs a) {
   __shared__ int32_t s_ids[POS + ENGRAM_MAX_ORDER - 1];
   const uint32_t nblk = (uint32_t)((a.t_count + POS - 1) / POS);  // workgroups per sequence

@@ -5,7 +5,7 @@ compress the raw ids, hash every suffix n-gram into its tables, gather and
 concatenate the rows, then gate the memory against each branch's hidden
 state and add it to the residual.  This class only owns the parameters and
 the intermediate device buffers and issues the calls on one stream
-(compression and hashing as one fused call, then gather, then gate); the
+(compression, hashing and the gather as one fused call, then the gate); the
 arithmetic is in the HIP kernels.  Passing one W_V tensor for every branch
 (section 2.4, Eq. (6)) lets the gate compute W_V e once for all of them.
 """
@@ -16,7 +16,7 @@ from typing import List, Optional, Sequence
 import numpy as np
 import torch
 
-from . import KEY_NORM_MEMORY, engram_compress_hash, engram_gate_forward, engram_gather
+from . import KEY_NORM_MEMORY, engram_gate_forward, engram_lookup
 
 
 class EngramLayer:
@@ -59,8 +59,7 @@ class EngramLayer:
         """raw: int32 [batch, seq]; h: per-branch [batch*seq, d_model]; returns per-branch outputs."""
         batch, seq = raw.shape
         b = self.buffers(batch, seq)
-        engram_compress_hash(raw, self.cmap, self.orders, self.heads, self.mult, self.rows, self.pad_id,
-                             out=b["idx"], ids_out=b["ids"], stream=stream)
-        engram_gather(b["idx"], self.tables, out=b["mem"], stream=stream)
+        engram_lookup(raw, self.cmap, self.orders, self.heads, self.mult, self.tables, self.pad_id,
+                      out=b["mem"], ids_out=b["ids"], idx_out=b["idx"], stream=stream)
         return engram_gate_forward(b["mem"], h, self.wk, self.wv, self.gq, self.gk, self.eps, out=out,
                                    gate_out=gate_out, key_norm=self.key_norm, stream=stream)

@@ -149,6 +149,31 @@ engram_status engram_gather(const int32_t* idx, int64_t n_tok, int32_t n_tables,
                             engram_dtype dtype, void* out, int32_t* err_count, hipStream_t stream);
 
 /*
+ * Compression, hashing and lookup in one call -- section 2.2, Eq. (1)-(2): exactly
+ * engram_compress_hash of raw into canonical ids and indices, followed by
+ * engram_gather of those indices from `tables`, in one kernel that keeps the
+ * indices on chip.
+ * raw, batch, ld, t_begin, t_count, map, vocab, orders, n_orders, heads, mult,
+ *   pad_id, ids_out: as for engram_compress_hash; map may be NULL (raw holds
+ *   canonical ids already; vocab is then ignored).
+ * rows:   host uint32[n_orders*heads]: the prime row count of each table, the
+ *         modulus of its hash.
+ * tables, w, dtype: as for engram_gather; table b has rows[b] rows.
+ * idx_out: device int32 [batch*t_count][n_orders*heads] receiving the indices (the
+ *         engram_hash result), or NULL.
+ * out:    device [batch*t_count][n_orders*heads*w] of dtype, 16-byte aligned: row
+ *         b*t_count + p is position t_begin + p of sequence b.
+ * err_count: device int32, incremented once per window position whose raw id is
+ *         outside [0, vocab) (with map), or NULL.
+ * Requires what engram_compress_hash and engram_gather require.
+ */
+engram_status engram_lookup(const int32_t* raw, int32_t batch, int64_t ld, int64_t t_begin, int64_t t_count,
+                            const int32_t* map, int32_t vocab, const int32_t* orders, int32_t n_orders,
+                            int32_t heads, const uint64_t* mult, const uint32_t* rows, int32_t pad_id,
+                            const void* const* tables, int32_t w, engram_dtype dtype, int32_t* ids_out,
+                            int32_t* idx_out, void* out, int32_t* err_count, hipStream_t stream);
+
+/*
  * Context-aware gating -- section 2.3, Eq. (3)-(4), the gated value and the
  * residual update; section 2.4, Eq. (6) for branches m < n_branch sharing `mem`
  * (every branch has its own W_K, W_V and gains; the paper's shared W_V is the

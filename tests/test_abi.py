@@ -116,6 +116,31 @@ def test_gate_argument_errors():
     assert gf(n=0) == _st("ok")
 
 
+def test_lookup_argument_errors():
+    import numpy as np
+    L = eg.lib()
+    orders = np.array([2, 3], np.int32)
+    mult = np.ones((2, 2, 3), np.uint64)
+    rows = np.full(4, 1009, np.uint32)
+    tabs = (ctypes.c_void_p * 4)(4096, 8192, 12288, 16384)
+    lk = lambda **kw: L.engram_lookup(
+        ctypes.c_void_p(kw.get("raw", 4096)), kw.get("batch", 2), kw.get("ld", 100), kw.get("tb", 0),
+        kw.get("tc", 100), None, 0, kw.get("orders", orders).ctypes.data, kw.get("no", 2), 2, mult.ctypes.data,
+        kw.get("rows", rows).ctypes.data, 7, kw.get("tabs", tabs), kw.get("w", 80), kw.get("dt", eg.BF16), None,
+        ctypes.c_void_p(kw.get("idx", 0)), ctypes.c_void_p(kw.get("out", 1 << 20)), None, None)
+    assert lk(w=12) == _st("unsup")                              # 24-byte bf16 rows
+    assert lk(tb=50, tc=60) == _st("arg")                        # window past the row
+    assert lk(orders=np.array([2, 5], np.int32)) == _st("arg")   # order above the maximum
+    assert lk(rows=np.zeros(4, np.uint32)) == _st("arg")
+    assert lk(tabs=(ctypes.c_void_p * 4)(4096, 8200, 12288, 16384)) == _st("arg")  # misaligned table
+    assert lk(out=(1 << 20) + 8) == _st("arg")                   # misaligned output
+    assert lk(idx=4098) == _st("arg")                            # misaligned index output
+    assert lk(raw=0) == _st("arg")
+    assert lk(dt=9) == _st("arg")
+    assert lk(tc=0, raw=0, out=0) == _st("ok")
+    assert lk(batch=0, raw=0, out=0) == _st("ok")
+
+
 def test_gate_fp8_argument_errors():
     L = eg.lib()
     one = (ctypes.c_void_p * 1)(4096)

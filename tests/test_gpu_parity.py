@@ -135,6 +135,79 @@ def test_compress_hash_fused_windows_and_bad_ids():
         assert int(err.item()) == bad, (t_begin, t_count)
 
 
+@pytest.mark.parametrize("name", ["tiny", "small"])
+def test_lookup_equals_compress_hash_gather_and_oracle(name):
+    """engram_lookup = engram_compress_hash then engram_gather, bit for bit (memory
+    vectors, indices, canonical ids), and the oracle's memory vectors (tiny: every
+    token; small: a sample of tokens)."""
+    cfg = synth.CONFIGS[name]
+    say("lookup fused", name)
+    inp = synth.device_inputs(cfg, DEV)
+    raw = synth.raw_ids(cfg)
+    _, idx_o = oracle_ids_idx(cfg, raw)
+    ids_out = torch.full_like(inp["raw"], -7)
+    idx_out = torch.full((cfg.tokens, cfg.n_tables), -7, dtype=torch.int32, device=DEV)
+    e = eg.engram_lookup(inp["raw"], inp["map"], cfg.orders, cfg.heads, inp["mult"], inp["tables"], cfg.vocab_c,
+                         ids_out=ids_out, idx_out=idx_out)
+    ids_d = torch.full_like(inp["raw"], -7)
+    idx_d = eg.engram_compress_hash(inp["raw"], inp["map"], cfg.orders, cfg.heads, inp["mult"], inp["rows"],
+                                    cfg.vocab_c, ids_out=ids_d)
+    e_d = eg.engram_gather(idx_d, inp["tables"])
+    torch.cuda.synchronize()
+    assert torch.equal(e.view(torch.int16) if e.dtype == torch.bfloat16 else e,
+                       e_d.view(torch.int16) if e_d.dtype == torch.bfloat16 else e_d)
+    assert torch.equal(idx_out, idx_d) and torch.equal(ids_out, ids_d)
+    assert np.array_equal(idx_out.cpu().numpy(), idx_o)
+    sample = np.arange(cfg.tokens) if cfg.tokens <= 4096 else sample_tokens(cfg, 600, seed=3)
+    want = oracle_memory(cfg, idx_o[sample])
+    assert np.array_equal(host_view(e[torch.from_numpy(sample).to(DEV)]), want)
+
+
+@pytest.mark.parametrize("w,dt", [(8, torch.float32), (80, torch.bfloat16), (128, torch.float32)])
+def test_lookup_windows_bad_ids_and_no_map(w, dt):
+    """Windows starting mid-row and single positions, orders 1..4, out-of-range raw ids
+    (zero-width error count, canonical ids still written), with and without the
+    compression map; rows of 32, 160 and 512 bytes (64, 8 and 8 positions per workgroup)."""
+    say(f"lookup windows w {w} {dt}")
+    rng = np.random.default_rng(9 + w)
+    V, Vc = 5000, 3001
+    cmap = rng.integers(0, Vc, V).astype(np.int32)
+    raw = rng.integers(0, V, (3, 300)).astype(np.int32)
+    raw[0, 10], raw[1, 150], raw[2, 299], raw[2, 0] = V, -5, V + 99, 1 << 30
+    orders, heads = (1, 2, 3, 4), 2
+    mult = synth.hash_multipliers(9, orders, heads)
+    rows = [synth.next_prime(int(x)) for x in rng.integers(500, 4000, 8)]
+    tables = [torch.randn(r, w, generator=torch.Generator().manual_seed(r)).to(dt).to(DEV) for r in rows]
+    rows_a = np.array(rows, np.uint32)
+    raw_d, map_d = torch.from_numpy(raw).to(DEV), torch.from_numpy(cmap).to(DEV)
+    for use_map in (True, False):
+        src = raw_d if use_map else eg.engram_compress(raw_d, map_d)
+        for t_begin, t_count in ((0, 300), (5, 100), (150, 1), (299, 1), (12, 288), (7, 0)):
+            err = torch.zeros(1, dtype=torch.int32, device=DEV)
+            err2 = torch.zeros(1, dtype=torch.int32, device=DEV)
+            ids_out = torch.full_like(raw_d, -7)
+            ids_ref = torch.full_like(raw_d, -7)
+            idx_out = torch.full((3 * t_count, 8), -7, dtype=torch.int32, device=DEV)
+            got = eg.engram_lookup(src, map_d if use_map else None, orders, heads, mult, tables, Vc,
+                                   t_begin=t_begin, t_count=t_count, ids_out=ids_out, idx_out=idx_out,
+                                   err_count=err)
+            if use_map:
+                idx = eg.engram_compress_hash(src, map_d, orders, heads, mult, rows_a, Vc, t_begin=t_begin,
+                                              t_count=t_count, ids_out=ids_ref, err_count=err2)
+            else:
+                idx = eg.engram_hash(src, orders, heads, mult, rows_a, Vc, t_begin=t_begin, t_count=t_count)
+            want = eg.engram_gather(idx, tables)
+            torch.cuda.synchronize()
+            assert torch.equal(idx_out, idx), (use_map, t_begin, t_count)
+            assert torch.equal(got.view(torch.int16) if dt == torch.bfloat16 else got,
+                               want.view(torch.int16) if dt == torch.bfloat16 else want), (use_map, t_begin, t_count)
+            if use_map:
+                assert torch.equal(ids_out, ids_ref)
+                assert int(err.item()) == int(err2.item())
+            else:
+                assert bool((ids_out == -7).all()) and int(err.item()) == 0
+
+
 def test_hash_windows_orders_and_large_primes():
     """Ragged windows, orders 1..4, per-table primes up to 2^31 - 1, decode-style t_count = 1."""
     say("hash windows")
