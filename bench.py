@@ -100,6 +100,9 @@ def algorithmic(cfg, shared_wv=False):
         # raw ids in, rows read and the memory vectors written (the indices stay on chip;
         # the 517-KB compression map stays in L2)
         "lookup": {"bytes": 4 * T + 2 * dm * es * T},
+        # the same as two calls: raw ids in, indices out; indices in, rows read, vectors out
+        "compress_hash": {"bytes": 4 * T + 4 * nt * T},
+        "gather": {"bytes": 4 * nt * T + 2 * dm * es * T},
         # weights once, memory vector once, hidden read + output written per branch
         "gate": {"flops": 2 * dm * d * (M + nv) * T,
                  "bytes": dm * es * T + (M + nv) * d * dm * es + M * 2 * d * es * T},
@@ -546,7 +549,7 @@ def main():
     flush = (torch.empty(args.flush_mb << 18, dtype=torch.float32, device=dev) if args.flush_mb > 0 else None)
     names = ["lookup", "gate"]
 
-    def time_steps(step, n_steps, n_warm, use_graph):
+    def time_steps(step, n_steps, n_warm, use_graph, names=names):
         """Warm-up, then n_steps iterations of: the eager step (events between its calls give
         the per-call breakdown) and the graph replay, each after the cache flush, so both see
         the same clocks and the same cold caches.  Returns (ms per step, ms eager, per-call
@@ -601,17 +604,36 @@ def main():
 
     ms_step, ms_eager, per, t_wall = time_steps(make_step(args.fp8), args.steps, args.warmup, not args.no_graph)
 
+    # the lookup as its separate calls (engram_compress_hash, then engram_gather), for each
+    # call's own rate
+    def separate(ev=None):
+        if ev is not None:
+            ev[0].record()
+        eg.engram_compress_hash(raw, layer.cmap, layer.orders, layer.heads, layer.mult, layer.rows, layer.pad_id,
+                                out=bufs["idx"])
+        if ev is not None:
+            ev[1].record()
+        eg.engram_gather(bufs["idx"], layer.tables, out=bufs["mem"])
+        if ev is not None:
+            ev[2].record()
+    sep_names = ["compress_hash", "gather"]
+    _, _, sep_per, _ = time_steps(separate, args.steps, 3, False, names=sep_names)
+
     work = algorithmic(cfg, args.shared_wv)
-    kernels = {}
-    for n in names:
-        s = per[n] * 1e-3
-        d = {"ms": round(per[n], 5)}
+    def rates(n, ms):
+        s = ms * 1e-3
+        d = {"ms": round(ms, 5)}
         if "bytes" in work[n]:
             d["GB/s"] = round(work[n]["bytes"] / s / 1e9, 1)
             d["hbm_frac"] = round(work[n]["bytes"] / s / 1e9 / PEAK_HBM_GBS, 4)
+        return d
+    kernels = {}
+    for n in names:
+        d = rates(n, per[n])
         if "flops" in work[n]:
-            d["TFLOP/s"] = round(work[n]["flops"] / s / 1e12, 2)
+            d["TFLOP/s"] = round(work[n]["flops"] / (per[n] * 1e-3) / 1e12, 2)
         kernels[n] = d
+    separate_calls = {n: rates(n, sep_per[n]) for n in sep_names}
     gate_s = per["gate"] * 1e-3
     if cfg.dtype == "bf16" and args.fp8:
         peak, dtype = PEAK_FP8_TFLOPS, "fp8e4m3 projections, bf16 storage"
@@ -646,6 +668,8 @@ def main():
         "wall_s_timed": round(t_wall, 4),
         "cache_flush_mb_between_steps": args.flush_mb,
         "kernels": kernels,
+        "separate_calls": {**separate_calls, "note": "the lookup as engram_compress_hash + engram_gather, "
+                                                     "timed eagerly in the same run (not part of the step)"},
         "roofline": roofline,
     }
     if cfg.dtype == "bf16" and not args.fp8 and not args.no_fp8:
