@@ -688,6 +688,36 @@ def main():
                      "note": "events bracket the whole call: counter clear, three quantization launches "
                              "and the persistent kernel"},
         }
+        # the FP8 pipeline with its operands made once: the weights quantized before timing
+        # (engram_gate_prepare_fp8), the lookup writing E4M3 memory vectors (engram_lookup_fp8),
+        # the gate on the codes (engram_gate_forward_fp8q)
+        print("[bench] fp8 step with prepared operands", file=sys.stderr, flush=True)
+        prep = eg.engram_gate_prepare_fp8(layer.wk, layer.wv, layer.gq, layer.gk, key_norm=layer.key_norm)
+        q_codes = torch.empty((cfg.tokens, cfg.d_mem), dtype=torch.uint8, device=dev)
+        q_scales = torch.empty(cfg.tokens, dtype=torch.float32, device=dev)
+        q_ss = torch.empty(cfg.tokens, dtype=torch.float32, device=dev)
+
+        def step_q(ev=None):
+            if ev is not None:
+                ev[0].record()
+            eg.engram_lookup_fp8(raw, layer.cmap, layer.orders, layer.heads, layer.mult, layer.tables, layer.pad_id,
+                                 codes=q_codes, scales=q_scales, sumsq=q_ss)
+            if ev is not None:
+                ev[1].record()
+            eg.engram_gate_forward_fp8q(q_codes, q_scales, q_ss, h, prep, layer.gq, layer.gk, cfg.eps, out=outs)
+            if ev is not None:
+                ev[2].record()
+        q_ms, q_eager, q_per, _ = time_steps(step_q, args.steps, max(3, args.warmup // 2), not args.no_graph,
+                                             names=["lookup_fp8", "gate"])
+        q_tf = work["gate"]["flops"] / (q_per["gate"] * 1e-3) / 1e12
+        result["fp8_step"]["with_prepared_operands"] = {
+            "value": round(cfg.tokens / (q_ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(q_ms, 5),
+            "ms_per_step_eager": round(q_eager, 5), "kernels_ms": {n: round(q_per[n], 5) for n in q_per},
+            "gate": {"TFLOP/s": round(q_tf, 2), "frac": round(q_tf / PEAK_FP8_TFLOPS, 4),
+                     "frac_of_bf16_peak": round(q_tf / PEAK_BF16_TFLOPS, 4)},
+            "note": "weights quantized once before timing (engram_gate_prepare_fp8); per step: engram_lookup_fp8 "
+                    "(compress, hash, gather and per-token quantization) and engram_gate_forward_fp8q",
+        }
     if not args.no_conv:
         print("[bench] short convolution", file=sys.stderr, flush=True)
         result["conv"] = measure_conv(args, cfg, bufs, h, layer, outs, flush)

@@ -15,6 +15,9 @@ The functions carry the C names:
 * ``engram_gate_forward`` -- context-aware gating and residual update
   (section 2.3, Eq. 3-4; section 2.4, Eq. 6 for several branches);
   ``fp8=True`` runs both projections on E4M3 codes (section 2.4);
+* ``engram_lookup_fp8``, ``engram_gate_prepare_fp8``, ``engram_gate_forward_fp8q``
+  -- the FP8 gate's operands made once: the lookup quantizing its memory vectors,
+  the weights quantized ahead, and the gate on the codes;
 * ``engram_conv_forward`` -- the short depthwise causal convolution over the
   gated values (section 2.3, Eq. 5);
 * ``engram_prefetch_host`` -- the same gather from pinned host-memory tables
@@ -52,6 +55,7 @@ EXPORTS = (
     "engram_gate_forward", "engram_conv_forward", "engram_prefetch_host", "engram_host_alloc",
     "engram_host_free", "engram_cache_select", "engram_cache_build", "engram_prefetch_host_cached",
     "engram_compress_hash", "engram_quantize_fp8", "engram_gate_forward_fp8", "engram_lookup",
+    "engram_lookup_fp8", "engram_gate_prepare_fp8", "engram_gate_forward_fp8q",
 )
 
 
@@ -90,6 +94,11 @@ def lib() -> ctypes.CDLL:
         L.engram_gate_forward.argtypes = [P, i64, i32, i32, i32, P, P, P, P, P, ctypes.c_float, i32, i32,
                                           P, P, P, P]
         L.engram_gate_forward_fp8.argtypes = L.engram_gate_forward.argtypes
+        L.engram_lookup_fp8.argtypes = [P, i32, i64, i64, i64, P, i32, P, i32, i32, P, P, i32, P, i32, P, P, P, P, P,
+                                        P, P]
+        L.engram_gate_prepare_fp8.argtypes = [i32, i32, i32, P, P, P, P, i32, P, P, P, P, P]
+        L.engram_gate_forward_fp8q.argtypes = [P, P, P, i64, i32, i32, i32, P, P, P, P, P, P, P, ctypes.c_float, i32,
+                                               P, P, P, P]
         L.engram_conv_forward.argtypes = [P, i32, i64, i32, P, P, i32, i32, ctypes.c_float, i32, P, P]
         L.engram_prefetch_host.argtypes = [P, i64, i32, P, P, i32, i32, P, P, P]
         L.engram_host_alloc.argtypes = [ctypes.c_size_t, ctypes.POINTER(ctypes.c_void_p)]
@@ -100,7 +109,8 @@ def lib() -> ctypes.CDLL:
         for f in ("engram_compress", "engram_hash", "engram_gather", "engram_gate_forward",
                   "engram_conv_forward", "engram_prefetch_host", "engram_host_alloc", "engram_host_free",
                   "engram_cache_select", "engram_cache_build", "engram_prefetch_host_cached",
-                  "engram_compress_hash", "engram_quantize_fp8", "engram_gate_forward_fp8", "engram_lookup"):
+                  "engram_compress_hash", "engram_quantize_fp8", "engram_gate_forward_fp8", "engram_lookup",
+                  "engram_lookup_fp8", "engram_gate_prepare_fp8", "engram_gate_forward_fp8q"):
             getattr(L, f).restype = st
         _lib = L
     return _lib
@@ -276,6 +286,104 @@ def engram_lookup(raw, cmap, orders: Sequence[int], heads: int, mult, tables: Se
                                pad_id, ptrs, w, _edtype(tables[0]), _opt(ids_out, "ids_out", torch.int32),
                                _opt(idx_out, "idx_out", torch.int32), _dev(out, "out", dt),
                                _opt(err_count, "err_count", torch.int32), _stream(stream)))
+    return out
+
+
+def engram_lookup_fp8(raw, cmap, orders: Sequence[int], heads: int, mult, tables: Sequence, pad_id: int,
+                      t_begin: int = 0, t_count: Optional[int] = None, codes=None, scales=None, sumsq=None,
+                      with_sumsq: bool = True, ids_out=None, idx_out=None, err_count=None, stream=None):
+    """engram_lookup on bf16 tables with the memory vectors quantized per row to E4M3:
+    (codes uint8 [n, d_mem], scales float32 [n], sumsq float32 [n] or None), n = batch *
+    t_count."""
+    import numpy as np
+    import torch
+    batch, ld = raw.shape
+    if t_count is None:
+        t_count = ld - t_begin
+    orders_a = np.ascontiguousarray(orders, dtype=np.int32)
+    mult_a = np.ascontiguousarray(mult, dtype=np.uint64)
+    n_tables = len(orders) * heads
+    if mult_a.shape != (len(orders), heads, max(orders)) or len(tables) != n_tables:
+        raise ValueError("mult must be [n_orders][heads][max_order], one table per (order, head)")
+    w = tables[0].shape[1]
+    for t in tables:
+        if t.shape[1] != w:
+            raise ValueError("all tables need the same width")
+        _dev(t, "table", torch.bfloat16)
+    rows_a = np.array([t.shape[0] for t in tables], dtype=np.uint32)
+    n = batch * t_count
+    dev = raw.device
+    if codes is None:
+        codes = torch.empty((n, n_tables * w), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty(n, dtype=torch.float32, device=dev)
+    if sumsq is None and with_sumsq:
+        sumsq = torch.empty(n, dtype=torch.float32, device=dev)
+    ptrs = _ptr_array([t.data_ptr() for t in tables])
+    _check(lib().engram_lookup_fp8(_dev(raw, "raw", torch.int32), batch, ld, t_begin, t_count,
+                                   _opt(cmap, "map", torch.int32), 0 if cmap is None else cmap.numel(),
+                                   orders_a.ctypes.data, len(orders), heads, mult_a.ctypes.data, rows_a.ctypes.data,
+                                   pad_id, ptrs, w, _opt(ids_out, "ids_out", torch.int32),
+                                   _opt(idx_out, "idx_out", torch.int32), _dev(codes, "codes", torch.uint8),
+                                   _dev(scales, "scales", torch.float32), _opt(sumsq, "sumsq", torch.float32),
+                                   _opt(err_count, "err_count", torch.int32), _stream(stream)))
+    return codes, scales, sumsq
+
+
+def engram_gate_prepare_fp8(wk: Sequence, wv: Sequence, gq: Optional[Sequence] = None, gk: Optional[Sequence] = None,
+                            key_norm: int = KEY_NORM_MEMORY, stream=None):
+    """The FP8 gate's weights, quantized once: a dict of per-branch lists wk_codes,
+    wk_scales, wv_codes, wv_scales.  Branches passing the same W_V tensor share one copy
+    of its codes (the gate then computes W_V e once)."""
+    import torch
+    nb = len(wk)
+    d_model, d_mem = wk[0].shape
+    wk_codes = [torch.empty((d_model, d_mem), dtype=torch.uint8, device=w.device) for w in wk]
+    wk_scales = [torch.empty(d_model, dtype=torch.float32, device=w.device) for w in wk]
+    wv_codes, wv_scales, seen = [], [], {}
+    for w in wv:
+        if w.data_ptr() not in seen:
+            seen[w.data_ptr()] = (torch.empty((d_model, d_mem), dtype=torch.uint8, device=w.device),
+                                  torch.empty(d_model, dtype=torch.float32, device=w.device))
+        wv_codes.append(seen[w.data_ptr()][0])
+        wv_scales.append(seen[w.data_ptr()][1])
+    arr = lambda seq: _ptr_array([0 if x is None else x.data_ptr() for x in seq])
+    for x in list(wk) + list(wv):
+        _dev(x, "weights", torch.bfloat16)
+        if tuple(x.shape) != (d_model, d_mem):
+            raise ValueError("weights must be [d_model, d_mem]")
+    gq_a = arr(gq) if gq is not None else None
+    gk_a = arr(gk) if gk is not None else None
+    _check(lib().engram_gate_prepare_fp8(d_mem, d_model, nb, arr(wk), arr(wv), gq_a, gk_a, int(key_norm),
+                                         arr(wk_codes), arr(wk_scales), arr(wv_codes), arr(wv_scales),
+                                         _stream(stream)))
+    return {"wk_codes": wk_codes, "wk_scales": wk_scales, "wv_codes": wv_codes, "wv_scales": wv_scales,
+            "key_norm": int(key_norm)}
+
+
+def engram_gate_forward_fp8q(codes, scales, sumsq, h: Sequence, prepared, gq: Sequence, gk: Sequence,
+                             eps: float = 1e-6, out: Optional[Sequence] = None, gate_out=None,
+                             value_out: Optional[Sequence] = None, stream=None):
+    """engram_gate_forward(..., fp8=True) on operands quantized ahead: the memory vectors'
+    (codes, scales, sumsq) from engram_lookup_fp8 or engram_quantize_fp8 and the weights
+    from engram_gate_prepare_fp8 (its key_norm applies)."""
+    import torch
+    n_tok, d_mem = codes.shape
+    nb = len(h)
+    d_model = h[0].shape[1]
+    if out is None:
+        out = [torch.empty_like(x) for x in h]
+    for name, seq in (("h", h), ("gq", gq), ("gk", gk), ("out", out)):
+        for x in seq:
+            _dev(x, name, torch.bfloat16)
+    arr = lambda seq: _ptr_array([x.data_ptr() for x in seq])
+    varr = None if value_out is None else _ptr_array([0 if x is None else x.data_ptr() for x in value_out])
+    _check(lib().engram_gate_forward_fp8q(_dev(codes, "codes", torch.uint8), _dev(scales, "scales", torch.float32),
+                                          _opt(sumsq, "sumsq", torch.float32), n_tok, d_mem, d_model, nb, arr(h),
+                                          arr(prepared["wk_codes"]), arr(prepared["wk_scales"]),
+                                          arr(prepared["wv_codes"]), arr(prepared["wv_scales"]), arr(gq), arr(gk),
+                                          float(eps), prepared["key_norm"], arr(out),
+                                          _opt(gate_out, "gate_out", torch.float32), varr, _stream(stream)))
     return out
 
 

@@ -335,7 +335,45 @@ engram_status engram_lookup(const int32_t* raw, int32_t batch, int64_t ld, int64
   g.n_tok = n_tok;
   g.n_tables = nt;
   g.chunks_per_row = (int32_t)(w * dtype_size(dtype) / 16);
-  launch_lookup(h, g, stream);
+  launch_lookup(h, g, nullptr, stream);
+  return check_launch(fn);
+}
+
+engram_status engram_lookup_fp8(const int32_t* raw, int32_t batch, int64_t ld, int64_t t_begin, int64_t t_count,
+                                const int32_t* map, int32_t vocab, const int32_t* orders, int32_t n_orders,
+                                int32_t heads, const uint64_t* mult, const uint32_t* rows, int32_t pad_id,
+                                const void* const* tables, int32_t w, int32_t* ids_out, int32_t* idx_out,
+                                uint8_t* codes, float* scales, float* sumsq, int32_t* err_count, hipStream_t stream) {
+  const char* fn = "engram_lookup_fp8";
+  HashArgs h;
+  bool empty = false;
+  engram_status st = hash_args(fn, raw, batch, ld, t_begin, t_count, map, vocab, orders, n_orders, heads, mult,
+                               rows, pad_id, ids_out, idx_out, err_count, false, h, &empty);
+  if (st != ENGRAM_OK) return st;
+  const int nt = n_orders * heads;
+  int64_t rows64[ENGRAM_MAX_TABLES];
+  for (int b = 0; b < nt; ++b) rows64[b] = rows[b];
+  const int64_t n_tok = empty ? 0 : (int64_t)batch * t_count;
+  static const int32_t no_idx = 0;
+  // the gather's checks on bf16 rows (codes stands in for the output)
+  st = check_gather(fn, &no_idx, n_tok, nt, tables, rows64, w, ENGRAM_BF16, codes);
+  if (st != ENGRAM_OK || empty) return st;
+  if (scales == nullptr || !aligned(scales, 4) || (sumsq != nullptr && !aligned(sumsq, 4)))
+    return fail(ENGRAM_ERR_INVALID_ARG, "%s: null or misaligned scales/sumsq", fn);
+  if (idx_out != nullptr && !aligned(idx_out, 4)) return fail(ENGRAM_ERR_INVALID_ARG, "%s: misaligned idx_out", fn);
+  if ((uint64_t)((t_count + 7) / 8) * (uint64_t)batch >= (1ull << 31))
+    return fail(ENGRAM_ERR_UNSUPPORTED, "%s: too many positions for one launch", fn);
+  GatherArgs g;
+  memset(&g, 0, sizeof g);
+  for (int b = 0; b < nt; ++b) {
+    g.table[b] = (const char*)tables[b];
+    g.rows[b] = rows64[b];
+  }
+  g.n_tok = n_tok;
+  g.n_tables = nt;
+  g.chunks_per_row = (int32_t)(w * 2 / 16);
+  const Q8Out q{codes, scales, sumsq};
+  launch_lookup(h, g, &q, stream);
   return check_launch(fn);
 }
 
@@ -511,6 +549,81 @@ engram_status engram_gate_forward_fp8(const void* mem, int64_t n_tok, int32_t d_
   return with_scratch(fn, bytes, stream, [&](void* p) {
     a.part_dot = (float*)p;
     launch_gate_bf16(a, true, stream);
+  });
+}
+
+engram_status engram_gate_prepare_fp8(int32_t d_mem, int32_t d_model, int32_t n_branch, const void* const* wk,
+                                      const void* const* wv, const void* const* gq, const void* const* gk,
+                                      engram_key_norm key_norm, uint8_t* const* wk_codes, float* const* wk_scales,
+                                      uint8_t* const* wv_codes, float* const* wv_scales, hipStream_t stream) {
+  const char* fn = "engram_gate_prepare_fp8";
+  if (d_mem <= 0 || d_model <= 0 || d_mem % 128 != 0 || d_model % 32 != 0)
+    return fail(ENGRAM_ERR_UNSUPPORTED, "%s: d_mem must be a positive multiple of 128 and d_model of 32 (got %d, %d)",
+                fn, d_mem, d_model);
+  if (n_branch <= 0 || n_branch > ENGRAM_MAX_BRANCHES)
+    return fail(ENGRAM_ERR_INVALID_ARG, "%s: n_branch %d not in [1, %d]", fn, n_branch, ENGRAM_MAX_BRANCHES);
+  if (key_norm != ENGRAM_KEY_NORM_MEMORY && key_norm != ENGRAM_KEY_NORM_PROJECTED)
+    return fail(ENGRAM_ERR_INVALID_ARG, "%s: unknown key_norm %d", fn, (int)key_norm);
+  if (wk == nullptr || wv == nullptr || wk_codes == nullptr || wk_scales == nullptr || wv_codes == nullptr ||
+      wv_scales == nullptr || (key_norm == ENGRAM_KEY_NORM_MEMORY && (gq == nullptr || gk == nullptr)))
+    return fail(ENGRAM_ERR_INVALID_ARG, "%s: null pointer array", fn);
+  GateArgs a;
+  memset(&a, 0, sizeof a);
+  for (int m = 0; m < n_branch; ++m) {
+    const bool gains_ok = key_norm == ENGRAM_KEY_NORM_PROJECTED ||
+                          (gq[m] != nullptr && gk[m] != nullptr && aligned(gq[m], 16) && aligned(gk[m], 16));
+    if (wk[m] == nullptr || wv[m] == nullptr || !aligned(wk[m], 16) || !aligned(wv[m], 16) || !gains_ok ||
+        wk_codes[m] == nullptr || wv_codes[m] == nullptr || !aligned(wk_codes[m], 16) || !aligned(wv_codes[m], 16) ||
+        wk_scales[m] == nullptr || wv_scales[m] == nullptr || !aligned(wk_scales[m], 4) || !aligned(wv_scales[m], 4))
+      return fail(ENGRAM_ERR_INVALID_ARG, "%s: branch %d: null or misaligned weights, gains or outputs", fn, m);
+    a.wk[m] = wk[m];
+    a.wv[m] = wv[m];
+    if (key_norm == ENGRAM_KEY_NORM_MEMORY) {
+      a.gq[m] = gq[m];
+      a.gk[m] = gk[m];
+    }
+  }
+  a.d_mem = d_mem;
+  a.d_model = d_model;
+  a.n_branch = n_branch;
+  a.key_norm = (int32_t)key_norm;
+  launch_prepare_fp8(a, wk_codes, wk_scales, wv_codes, wv_scales, stream);
+  return check_launch(fn);
+}
+
+engram_status engram_gate_forward_fp8q(const uint8_t* codes, const float* scales, const float* sumsq, int64_t n_tok,
+                                       int32_t d_mem, int32_t d_model, int32_t n_branch, const void* const* h,
+                                       const uint8_t* const* wk_codes, const float* const* wk_scales,
+                                       const uint8_t* const* wv_codes, const float* const* wv_scales,
+                                       const void* const* gq, const void* const* gk, float eps,
+                                       engram_key_norm key_norm, void* const* out, float* gate_out,
+                                       void* const* value_out, hipStream_t stream) {
+  const char* fn = "engram_gate_forward_fp8q";
+  if (d_mem % 128 != 0)
+    return fail(ENGRAM_ERR_UNSUPPORTED, "%s: d_mem must be a multiple of 128 (got %d)", fn, d_mem);
+  if (wk_scales == nullptr || wv_scales == nullptr) return fail(ENGRAM_ERR_INVALID_ARG, "%s: null scale array", fn);
+  GateArgs a;
+  const engram_status st = gate_args(fn, codes, n_tok, d_mem, d_model, n_branch, h, (const void* const*)wk_codes,
+                                     (const void* const*)wv_codes, gq, gk, eps, ENGRAM_BF16, key_norm, out, gate_out,
+                                     value_out, a);
+  if (st != ENGRAM_OK) return st;
+  for (int m = 0; m < n_branch; ++m) {
+    if (wk_scales[m] == nullptr || wv_scales[m] == nullptr || !aligned(wk_scales[m], 4) || !aligned(wv_scales[m], 4))
+      return fail(ENGRAM_ERR_INVALID_ARG, "%s: branch %d: null or misaligned weight scales", fn, m);
+    a.sk[m] = wk_scales[m];
+    a.sv[m] = wv_scales[m];
+  }
+  if (n_tok == 0) return ENGRAM_OK;
+  if (scales == nullptr || !aligned(scales, 4) || (sumsq != nullptr && !aligned(sumsq, 4)) ||
+      (key_norm == ENGRAM_KEY_NORM_MEMORY && sumsq == nullptr))
+    return fail(ENGRAM_ERR_INVALID_ARG, "%s: null or misaligned scales/sumsq (sumsq is needed for the "
+                "memory-side key norm)", fn);
+  a.se = scales;
+  a.e_ssq = sumsq;
+  const size_t bytes = gate_bf16_scratch_bytes(a, true, true);
+  return with_scratch(fn, bytes, stream, [&](void* p) {
+    a.part_dot = (float*)p;
+    launch_gate_bf16(a, true, stream, true);
   });
 }
 

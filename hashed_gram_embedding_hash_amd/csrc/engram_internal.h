@@ -61,8 +61,14 @@ struct GatherArgs {
 void launch_gather(const GatherArgs& a, bool host_source, hipStream_t s);
 // engram_lookup: the hash kernel's staging and index computation for a block of
 // positions, then the gather of their rows, in one kernel (h.idx may be null: the
-// indices then stay in LDS; g.idx is unused).
-void launch_lookup(const HashArgs& h, const GatherArgs& g, hipStream_t s);
+// indices then stay in LDS; g.idx is unused).  With q8 (bf16 rows only), each
+// position's memory vector is quantized to E4M3 instead of stored (g.out unused).
+struct Q8Out {
+  uint8_t* codes;  // [positions][d_mem]
+  float* scales;   // [positions]
+  float* sumsq;    // [positions] or null
+};
+void launch_lookup(const HashArgs& h, const GatherArgs& g, const Q8Out* q8, hipStream_t s);
 // prefetch from host tables through the HBM row cache (table: [n_tables][2^log2_slots])
 void launch_prefetch_cached(const GatherArgs& a, const int2* table, int log2_slots, const char* cache_rows,
                             int32_t* hits, hipStream_t s);
@@ -94,20 +100,53 @@ struct GateArgs {
   int32_t d_mem, d_model, n_branch, n_ftiles, n_ttiles;
   int32_t key_norm;  // engram_key_norm
   float eps, inv_sqrt_d;
-  // FP8 projections (scratch, written by the quantization kernels): per-feature scales
-  // of the key and value weight codes ([n_branch][d_model]; one shared W_V: row 0), and
-  // per token the scale and the sum of squares of the dequantized memory vector
-  const float* sk;
-  const float* sv;
+  // FP8 projections: per branch the per-feature scales of the key and value weight codes
+  // ([d_model] each; with one shared W_V, branch 0's), and per token the scale and the
+  // sum of squares of the dequantized memory vector
   const float* se;
   const float* e_ssq;
+  const float* sk[ENGRAM_MAX_BRANCHES];
+  const float* sv[ENGRAM_MAX_BRANCHES];
 };
 // bf16 path: returns the scratch bytes it needs for these shapes (and sets a.n_ftiles).
 // launch_gate_bf16 expects a.part_dot to point at a scratch block of that size.  With
 // fp8, the projections run on E4M3 codes that it quantizes first (d_mem % 128 == 0).
-size_t gate_bf16_scratch_bytes(GateArgs& a, bool fp8);
-void launch_gate_bf16(const GateArgs& a, bool fp8, hipStream_t s);
+size_t gate_bf16_scratch_bytes(GateArgs& a, bool fp8, bool prequant = false);
+void launch_gate_bf16(const GateArgs& a, bool fp8, hipStream_t s, bool prequant = false);
+// The FP8 weights as the gate uses them: E4M3 codes of W_K (with the memory-side key
+// norm, of gq[f] * W_K[f][c] * gk[c] formed in fp32) and of W_V, per branch, with their
+// per-feature scales (one launch of the quantizer per matrix).
+void launch_prepare_fp8(const GateArgs& a, uint8_t* const* wk_codes, float* const* wk_scales,
+                        uint8_t* const* wv_codes, float* const* wv_scales, hipStream_t s);
 void launch_gate_f32(const GateArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- FP8 (E4M3) encoding
+// Shared by the quantization kernels and the quantizing lookup (their codes must agree).
+// The codes of four quotients x / s, packed little-endian.  The library's code of a
+// value is the nearest E4M3 value, ties to the even code, magnitudes at or above 448
+// saturated to 448 (see engram_quantize_fp8 in engram.h).  gfx950's conversion
+// instruction rounds exactly so for every finite fp32 input below 464 in magnitude
+// (checked exhaustively); the clamp makes it saturate where a quotient could exceed
+// that (an fp32 row whose maximum underflows the scale to zero).  Inputs are finite.
+__device__ __forceinline__ uint32_t e4m3_pack4(float q0, float q1, float q2, float q3) {
+  auto sat = [](float q) { return fminf(fmaxf(q, -448.0f), 448.0f); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(q0), sat(q1), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(q2), sat(q3), w, true);
+  return (uint32_t)w;
+}
+
+// The value of byte B of a packed word of codes (exact).
+template <int B>
+__device__ __forceinline__ float e4m3_byte(uint32_t w) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)w, B);
+}
+
+// The sum of squares of the four dequantized values d = value(code) * s of a word.
+__device__ __forceinline__ float sumsq4(uint32_t w, float s) {
+  const float d0 = e4m3_byte<0>(w) * s, d1 = e4m3_byte<1>(w) * s;
+  const float d2 = e4m3_byte<2>(w) * s, d3 = e4m3_byte<3>(w) * s;
+  return ((d0 * d0 + d1 * d1) + d2 * d2) + d3 * d3;
+}
 
 // ---------------------------------------------------------------- short convolution
 struct ConvArgs {

@@ -253,7 +253,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
   // tiles the token scale of token t0 + tid; both to LDS in the epilogue
   float fs = 0.f, ts = 0.f;
   if constexpr (F8) {
-    if (f0 + tid < d_model) fs = (PHASE == PHASE_K ? a.sk : a.sv)[(int64_t)m * d_model + f0 + tid];
+    if (f0 + tid < d_model) fs = (PHASE == PHASE_K ? a.sk[m] : a.sv[m])[f0 + tid];
     if (PHASE == PHASE_V && t0 + tid < n_tok) ts = a.se[t0 + tid];
   }
 
@@ -954,10 +954,12 @@ void gate_persistent_kernel(const GateArgs a) {
 
 // KEYP: the per-feature key gain gq[m][f] * gk[m][f] in fp32 (exact: a product of two
 // bf16 values), and the tile queues / done counters cleared; the K tiles read W_K itself.
-__global__ __launch_bounds__(256) void gate_prep_projected_kernel(const GateArgs a, int n_counters) {
+// Without gains (the FP8 gate with the memory-side key norm, whose gk spans d_mem) only
+// the counters are cleared.
+__global__ __launch_bounds__(256) void gate_prep_projected_kernel(const GateArgs a, int n_counters, bool gains) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n_counters) a.counters[i] = 0;
-  if (i >= (int64_t)a.n_branch * a.d_model) return;
+  if (!gains || i >= (int64_t)a.n_branch * a.d_model) return;
   const int m = (int)(i / a.d_model);
   const int f = (int)(i - (int64_t)m * a.d_model);
   const float gq = __uint_as_float((uint32_t)((const uint16_t*)a.gq[m])[f] << 16);
@@ -1005,7 +1007,7 @@ struct ScratchLayout {
   int n_counters;
 };
 
-ScratchLayout layout_for(const GateArgs& a, bool fp8) {
+ScratchLayout layout_for(const GateArgs& a, bool fp8, bool prequant) {
   ScratchLayout L;
   L.wk_bytes = (a.key_norm == ENGRAM_KEY_NORM_PROJECTED || fp8) ? round256((size_t)a.n_branch * a.d_model * 4)
                                                                  : round256((size_t)a.n_branch * a.d_model * a.d_mem * 2);
@@ -1016,7 +1018,7 @@ ScratchLayout layout_for(const GateArgs& a, bool fp8) {
   L.counter_bytes = round256((size_t)L.n_counters * 4);
   L.total = L.wk_bytes + 3 * L.part_bytes + L.alpha_bytes + L.counter_bytes;
   L.k8_bytes = L.v8_bytes = L.sk_bytes = L.sv_bytes = L.e8_bytes = L.tok_bytes = 0;
-  if (fp8) {
+  if (fp8 && !prequant) {
     const size_t n_wv = shared_wv(a) ? 1 : (size_t)a.n_branch;
     L.k8_bytes = round256((size_t)a.n_branch * a.d_model * a.d_mem);
     L.v8_bytes = round256(n_wv * a.d_model * a.d_mem);
@@ -1043,17 +1045,19 @@ int cu_count() {
 
 }  // namespace
 
-size_t gate_bf16_scratch_bytes(GateArgs& a, bool fp8) {
+size_t gate_bf16_scratch_bytes(GateArgs& a, bool fp8, bool prequant) {
   a.n_ftiles = (a.d_model + BF - 1) / BF;
   a.n_ttiles = (int32_t)((a.n_tok + BT - 1) / BT);
-  return layout_for(a, fp8).total;
+  return layout_for(a, fp8, prequant).total;
 }
 
 // `a.part_dot` must point at the scratch block of gate_bf16_scratch_bytes(a) bytes;
 // the other scratch pointers are carved from it here.
-void launch_gate_bf16(const GateArgs& a_in, bool fp8, hipStream_t s) {
+// prequant (fp8 only): a.mem, a.se, a.e_ssq, a.wk, a.wv, a.sk and a.sv already hold
+// the codes and scales; only the counters and the key gains are prepared here.
+void launch_gate_bf16(const GateArgs& a_in, bool fp8, hipStream_t s, bool prequant) {
   GateArgs a = a_in;
-  const ScratchLayout L = layout_for(a, fp8);
+  const ScratchLayout L = layout_for(a, fp8, prequant);
   const bool shared_v = shared_wv(a);
   char* base = (char*)a_in.part_dot;
   uint16_t* wk_scaled = (uint16_t*)base;
@@ -1069,42 +1073,44 @@ void launch_gate_bf16(const GateArgs& a_in, bool fp8, hipStream_t s) {
     // in (memory-side key norm) or as is, W_V, and the memory vectors with their sums
     // of squares
     a.kgain = (float*)base;
-    const int64_t work = (int64_t)a.n_branch * a.d_model > L.n_counters ? (int64_t)a.n_branch * a.d_model
-                                                                         : L.n_counters;
+    const int64_t gain_work = keyp ? (int64_t)a.n_branch * a.d_model : 0;
+    const int64_t work = gain_work > L.n_counters ? gain_work : L.n_counters;
     hipLaunchKernelGGL(gate_prep_projected_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, a,
-                       L.n_counters);
-    char* p = base + L.total - (L.k8_bytes + L.v8_bytes + L.sk_bytes + L.sv_bytes + L.e8_bytes + 2 * L.tok_bytes);
-    uint8_t* k8 = (uint8_t*)p;
-    uint8_t* v8 = (uint8_t*)(p += L.k8_bytes);
-    float* sk = (float*)(p += L.v8_bytes);
-    float* sv = (float*)(p += L.sk_bytes);
-    uint8_t* e8 = (uint8_t*)(p += L.sv_bytes);
-    float* se = (float*)(p += L.e8_bytes);
-    float* essq = (float*)(p += L.tok_bytes);
-    const size_t wsz = (size_t)a.d_model * a.d_mem;
-    for (int m = 0; m < a.n_branch; ++m) {
-      launch_quant_rows(a.wk[m], true, a.d_model, a.d_mem, keyp ? nullptr : a.gq[m], keyp ? nullptr : a.gk[m],
-                        k8 + m * wsz, sk + (size_t)m * a.d_model, nullptr, s);
-      if (m == 0 || !shared_v)
-        launch_quant_rows(a.wv[m], true, a.d_model, a.d_mem, nullptr, nullptr, v8 + m * wsz,
-                          sv + (size_t)m * a.d_model, nullptr, s);
+                       L.n_counters, keyp);
+    if (!prequant) {
+      char* p = base + L.total - (L.k8_bytes + L.v8_bytes + L.sk_bytes + L.sv_bytes + L.e8_bytes + 2 * L.tok_bytes);
+      uint8_t* k8 = (uint8_t*)p;
+      uint8_t* v8 = (uint8_t*)(p += L.k8_bytes);
+      float* sk = (float*)(p += L.v8_bytes);
+      float* sv = (float*)(p += L.sk_bytes);
+      uint8_t* e8 = (uint8_t*)(p += L.sv_bytes);
+      float* se = (float*)(p += L.e8_bytes);
+      float* essq = (float*)(p += L.tok_bytes);
+      const size_t wsz = (size_t)a.d_model * a.d_mem;
+      for (int m = 0; m < a.n_branch; ++m) {
+        launch_quant_rows(a.wk[m], true, a.d_model, a.d_mem, keyp ? nullptr : a.gq[m], keyp ? nullptr : a.gk[m],
+                          k8 + m * wsz, sk + (size_t)m * a.d_model, nullptr, s);
+        if (m == 0 || !shared_v)
+          launch_quant_rows(a.wv[m], true, a.d_model, a.d_mem, nullptr, nullptr, v8 + m * wsz,
+                            sv + (size_t)m * a.d_model, nullptr, s);
+      }
+      launch_quant_rows(a.mem, true, a.n_tok, a.d_mem, nullptr, nullptr, e8, se, essq, s);
+      for (int m = 0; m < a.n_branch; ++m) {
+        a.wk[m] = k8 + m * wsz;
+        a.wv[m] = v8 + (shared_v ? 0 : m) * wsz;
+        a.sk[m] = sk + (size_t)m * a.d_model;
+        a.sv[m] = sv + (size_t)(shared_v ? 0 : m) * a.d_model;
+      }
+      a.mem = e8;
+      a.se = se;
+      a.e_ssq = essq;
     }
-    launch_quant_rows(a.mem, true, a.n_tok, a.d_mem, nullptr, nullptr, e8, se, essq, s);
-    for (int m = 0; m < a.n_branch; ++m) {
-      a.wk[m] = k8 + m * wsz;
-      a.wv[m] = v8 + (shared_v ? 0 : m) * wsz;
-    }
-    a.mem = e8;
-    a.sk = sk;
-    a.sv = sv;
-    a.se = se;
-    a.e_ssq = essq;
   } else if (keyp) {
     a.kgain = (float*)base;
     const int64_t work = (int64_t)a.n_branch * a.d_model > L.n_counters ? (int64_t)a.n_branch * a.d_model
                                                                          : L.n_counters;
     hipLaunchKernelGGL(gate_prep_projected_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, a,
-                       L.n_counters);
+                       L.n_counters, true);
   } else {
     const int64_t n8 = (int64_t)a.d_model * a.d_mem / 8;
     const int64_t work = n8 * a.n_branch > L.n_counters ? n8 * a.n_branch : L.n_counters;
@@ -1138,6 +1144,16 @@ void launch_gate_bf16(const GateArgs& a_in, bool fp8, hipStream_t s) {
   ENGRAM_GATE_LAUNCH(true, true, false, true)
   ENGRAM_GATE_LAUNCH(true, true, true, true)
 #undef ENGRAM_GATE_LAUNCH
+}
+
+void launch_prepare_fp8(const GateArgs& a, uint8_t* const* wk_codes, float* const* wk_scales,
+                        uint8_t* const* wv_codes, float* const* wv_scales, hipStream_t s) {
+  const bool keyp = a.key_norm == ENGRAM_KEY_NORM_PROJECTED;
+  for (int m = 0; m < a.n_branch; ++m) {
+    launch_quant_rows(a.wk[m], true, a.d_model, a.d_mem, keyp ? nullptr : a.gq[m], keyp ? nullptr : a.gk[m],
+                      wk_codes[m], wk_scales[m], nullptr, s);
+    launch_quant_rows(a.wv[m], true, a.d_model, a.d_mem, nullptr, nullptr, wv_codes[m], wv_scales[m], nullptr, s);
+  }
 }
 
 }  // namespace engram

@@ -24,31 +24,6 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// The codes of four quotients x / s, packed little-endian.  gfx950's conversion
-// instruction rounds to the nearest E4M3 value, ties to even, exactly as the
-// definition above (checked for every finite fp32 input below 464 in magnitude); the
-// clamp makes it saturate like the definition where a quotient could exceed that (an
-// fp32 row whose maximum underflows the scale to zero).  Inputs are finite.
-__device__ __forceinline__ uint32_t e4m3_pack4(float q0, float q1, float q2, float q3) {
-  auto sat = [](float q) { return fminf(fmaxf(q, -448.0f), 448.0f); };
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(q0), sat(q1), 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(sat(q2), sat(q3), w, true);
-  return (uint32_t)w;
-}
-
-// The value of byte B of a packed word of codes (exact).
-template <int B>
-__device__ __forceinline__ float e4m3_byte(uint32_t w) {
-  return __builtin_amdgcn_cvt_f32_fp8((int)w, B);
-}
-
-// The sum of squares of the four dequantized values d = value(code) * s of a word.
-__device__ __forceinline__ float sumsq4(uint32_t w, float s) {
-  const float d0 = e4m3_byte<0>(w) * s, d1 = e4m3_byte<1>(w) * s;
-  const float d2 = e4m3_byte<2>(w) * s, d3 = e4m3_byte<3>(w) * s;
-  return ((d0 * d0 + d1 * d1) + d2 * d2) + d3 * d3;
-}
-
 __device__ __forceinline__ float bf16_at(const uint16_t* p, int64_t i) {
   return __uint_as_float((uint32_t)p[i] << 16);
 }

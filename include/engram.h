@@ -174,6 +174,23 @@ engram_status engram_lookup(const int32_t* raw, int32_t batch, int64_t ld, int64
                             int32_t* idx_out, void* out, int32_t* err_count, hipStream_t stream);
 
 /*
+ * The lookup with its memory vectors quantized -- section 2.2, Eq. (1)-(2), and the
+ * FP8 projections of section 2.4: exactly engram_lookup on bf16 tables followed by
+ * engram_quantize_fp8 of its output with sums of squares, in one kernel that never
+ * stores the bf16 vectors (the input of engram_gate_forward_fp8q).
+ * raw .. w, ids_out, idx_out, err_count: as for engram_lookup, tables in bf16.
+ * codes:  device uint8 [batch*t_count][n_orders*heads*w], 16-byte aligned.
+ * scales: device float [batch*t_count]: each vector's scale.
+ * sumsq:  device float [batch*t_count]: each vector's sum of squares of its dequantized
+ *         values (summed in a fixed order, but not in engram_quantize_fp8's), or NULL.
+ */
+engram_status engram_lookup_fp8(const int32_t* raw, int32_t batch, int64_t ld, int64_t t_begin, int64_t t_count,
+                                const int32_t* map, int32_t vocab, const int32_t* orders, int32_t n_orders,
+                                int32_t heads, const uint64_t* mult, const uint32_t* rows, int32_t pad_id,
+                                const void* const* tables, int32_t w, int32_t* ids_out, int32_t* idx_out,
+                                uint8_t* codes, float* scales, float* sumsq, int32_t* err_count, hipStream_t stream);
+
+/*
  * Context-aware gating -- section 2.3, Eq. (3)-(4), the gated value and the
  * residual update; section 2.4, Eq. (6) for branches m < n_branch sharing `mem`
  * (every branch has its own W_K, W_V and gains; the paper's shared W_V is the
@@ -328,6 +345,45 @@ engram_status engram_gate_forward_fp8(const void* mem, int64_t n_tok, int32_t d_
                                       const void* const* gk, float eps, engram_dtype dtype,
                                       engram_key_norm key_norm, void* const* out, float* gate_out,
                                       void* const* value_out, hipStream_t stream);
+
+/*
+ * The FP8 gate's weights, prepared once -- section 2.4.  Per branch m, the E4M3 codes
+ * and per-feature scales (engram_quantize_fp8's definition) of the key weights and of
+ * W_V[m], exactly as engram_gate_forward_fp8 makes them on every call: the key weights
+ * are gq[m][f] * W_K[m][f][c] * gk[m][c] formed in fp32 for ENGRAM_KEY_NORM_MEMORY and
+ * W_K[m] itself for ENGRAM_KEY_NORM_PROJECTED (gq, gk are then not read and may be NULL).
+ * wk, wv: host arrays of n_branch device bf16 [d_model][d_mem] (16-byte aligned); gq:
+ *         [d_model], gk: [d_mem] bf16.
+ * wk_codes, wv_codes: host arrays of n_branch device uint8 [d_model][d_mem], 16-byte
+ *         aligned; wk_scales, wv_scales: host arrays of n_branch device float [d_model].
+ * d_mem % 128 == 0 and d_model % 32 == 0 (UNSUPPORTED otherwise).
+ */
+engram_status engram_gate_prepare_fp8(int32_t d_mem, int32_t d_model, int32_t n_branch, const void* const* wk,
+                                      const void* const* wv, const void* const* gq, const void* const* gk,
+                                      engram_key_norm key_norm, uint8_t* const* wk_codes, float* const* wk_scales,
+                                      uint8_t* const* wv_codes, float* const* wv_scales, hipStream_t stream);
+
+/*
+ * The FP8 gate on quantized operands -- section 2.3, Eq. (3)-(4), section 2.4: the
+ * results of engram_gate_forward_fp8 given the quantizations it would make itself.
+ * codes, scales, sumsq: the memory vectors as engram_lookup_fp8 or engram_quantize_fp8
+ *         write them ([n_tok][d_mem] uint8, 16-byte aligned; [n_tok] float); sumsq may
+ *         be NULL for ENGRAM_KEY_NORM_PROJECTED.
+ * wk_codes .. wv_scales: as engram_gate_prepare_fp8 writes them, with the same key_norm;
+ *         branches sharing one W_V pass the same codes and scales pointers (W_V e is then
+ *         computed once).
+ * h, gq, gk, eps, key_norm, out, gate_out, value_out: as for engram_gate_forward (bf16;
+ *         gq and gk are read for ENGRAM_KEY_NORM_PROJECTED, and must be valid pointers
+ *         either way).
+ * d_mem % 128 == 0 and d_model % 32 == 0 (UNSUPPORTED otherwise).
+ */
+engram_status engram_gate_forward_fp8q(const uint8_t* codes, const float* scales, const float* sumsq, int64_t n_tok,
+                                       int32_t d_mem, int32_t d_model, int32_t n_branch, const void* const* h,
+                                       const uint8_t* const* wk_codes, const float* const* wk_scales,
+                                       const uint8_t* const* wv_codes, const float* const* wv_scales,
+                                       const void* const* gq, const void* const* gk, float eps,
+                                       engram_key_norm key_norm, void* const* out, float* gate_out,
+                                       void* const* value_out, hipStream_t stream);
 
 /* Pinned, device-mapped host allocation for offloaded tables (hipHostMalloc,
  * hipHostMallocMapped | hipHostMallocPortable). *ptr is NULL on failure. */

@@ -141,6 +141,42 @@ def test_lookup_argument_errors():
     assert lk(batch=0, raw=0, out=0) == _st("ok")
 
 
+def test_fp8_operand_calls_argument_errors():
+    import numpy as np
+    L = eg.lib()
+    one = (ctypes.c_void_p * 1)(4096)
+    p1 = lambda **kw: L.engram_gate_prepare_fp8(
+        kw.get("dm", 1280), kw.get("dmod", 2560), kw.get("nb", 1), one, one, kw.get("gq", one), kw.get("gk", one),
+        kw.get("kn", 0), kw.get("codes", one), one, one, one, None)
+    assert p1(dm=1216) == _st("unsup")
+    assert p1(dmod=2500) == _st("unsup")
+    assert p1(nb=0) == _st("arg")
+    assert p1(kn=4) == _st("arg")
+    assert p1(gq=None) == _st("arg")                                   # the memory-side key needs the gains
+    assert p1(codes=(ctypes.c_void_p * 1)(4100)) == _st("arg")         # misaligned codes
+    q = lambda **kw: L.engram_gate_forward_fp8q(
+        ctypes.c_void_p(kw.get("codes", 4096)), ctypes.c_void_p(kw.get("scales", 8192)),
+        ctypes.c_void_p(kw.get("ss", 8192)), kw.get("n", 8), kw.get("dm", 1280), 2560, 1, one, one, one, one, one, one,
+        one, ctypes.c_float(1e-6), kw.get("kn", 0), one, None, None, None)
+    assert q(dm=1216) == _st("unsup")
+    assert q(ss=0) == _st("arg")                                       # sums of squares needed (memory key)
+    assert q(scales=8194) == _st("arg")
+    assert q(codes=4100) == _st("arg")
+    assert q(n=0) == _st("ok")
+    orders = np.array([2, 3], np.int32)
+    mult = np.ones((2, 2, 3), np.uint64)
+    rows = np.full(4, 1009, np.uint32)
+    tabs = (ctypes.c_void_p * 4)(4096, 8192, 12288, 16384)
+    lf = lambda **kw: L.engram_lookup_fp8(
+        ctypes.c_void_p(4096), 2, 100, 0, kw.get("tc", 100), None, 0, orders.ctypes.data, 2, 2, mult.ctypes.data,
+        rows.ctypes.data, 7, tabs, kw.get("w", 80), None, None, ctypes.c_void_p(kw.get("codes", 1 << 20)),
+        ctypes.c_void_p(kw.get("scales", 1 << 21)), None, None, None)
+    assert lf(w=12) == _st("unsup")
+    assert lf(codes=(1 << 20) + 8) == _st("arg")
+    assert lf(scales=0) == _st("arg")
+    assert lf(tc=0) == _st("ok")
+
+
 def test_gate_fp8_argument_errors():
     L = eg.lib()
     one = (ctypes.c_void_p * 1)(4096)

@@ -922,3 +922,131 @@ def test_gate_fp8_scale_invariance_of_memory():
                                gate_out=a, fp8=True)
         alphas.append(a.cpu().numpy())
     assert np.abs(alphas[0] - alphas[1]).max() <= 1e-6
+
+
+# ---------------------------------------------------------------------------
+# FP8 operands made once: the quantizing lookup, prepared weights, the gate on codes
+# ---------------------------------------------------------------------------
+def test_lookup_fp8_equals_quantized_lookup_and_oracle():
+    """engram_lookup_fp8 = engram_quantize_fp8(engram_lookup(...)): codes and scales bit
+    for bit (small configuration, and the oracle's quantization of the oracle's memory
+    vectors on sampled tokens), sums of squares to fp32 summation error."""
+    cfg = synth.CONFIGS["small"]
+    say("lookup fp8, small")
+    inp = synth.device_inputs(cfg, DEV)
+    raw = synth.raw_ids(cfg)
+    _, idx_o = oracle_ids_idx(cfg, raw)
+    codes, scales, ss = eg.engram_lookup_fp8(inp["raw"], inp["map"], cfg.orders, cfg.heads, inp["mult"],
+                                             inp["tables"], cfg.vocab_c)
+    e = eg.engram_lookup(inp["raw"], inp["map"], cfg.orders, cfg.heads, inp["mult"], inp["tables"], cfg.vocab_c)
+    c2, s2, ss2 = eg.engram_quantize_fp8(e, with_sumsq=True)
+    torch.cuda.synchronize()
+    assert torch.equal(codes, c2) and torch.equal(scales, s2)
+    np.testing.assert_allclose(ss.cpu().numpy(), ss2.cpu().numpy(), rtol=2e-6, atol=0)
+    sample = sample_tokens(cfg, 400, seed=4)
+    bits = oracle_memory(cfg, idx_o[sample]).astype(np.uint32) << 16   # bf16 bits -> fp32 values
+    want_c, want_s = oracle.quant_rows(bits.view(np.float32))
+    sel = torch.from_numpy(sample).to(DEV)
+    assert np.array_equal(codes[sel].cpu().numpy(), want_c)
+    assert np.array_equal(scales[sel].cpu().numpy(), want_s)
+
+
+@pytest.mark.parametrize("w,n_heads", [(80, 8), (16, 4)])
+def test_lookup_fp8_windows_and_small_rows(w, n_heads):
+    """Windows starting mid-row, single positions, no map; 160-byte rows (8 positions
+    per workgroup) and 32-byte rows (64 positions per workgroup, several rows per wave)."""
+    say(f"lookup fp8 windows w {w}")
+    rng = np.random.default_rng(40 + w)
+    V, Vc = 4000, 2503
+    cmap = rng.integers(0, Vc, V).astype(np.int32)
+    raw = rng.integers(0, V, (2, 333)).astype(np.int32)
+    orders = (2, 3)
+    mult = synth.hash_multipliers(11, orders, n_heads)
+    rows = [synth.next_prime(int(x)) for x in rng.integers(300, 3000, len(orders) * n_heads)]
+    g = torch.Generator().manual_seed(w)
+    tables = [(torch.randn(r, w, generator=g) * torch.exp(torch.randn(r, 1, generator=g))).to(torch.bfloat16).to(DEV)
+              for r in rows]
+    raw_d, map_d = torch.from_numpy(raw).to(DEV), torch.from_numpy(cmap).to(DEV)
+    for use_map in (True, False):
+        src = raw_d if use_map else eg.engram_compress(raw_d, map_d)
+        for t_begin, t_count in ((0, 333), (7, 200), (332, 1), (100, 0)):
+            codes, scales, ss = eg.engram_lookup_fp8(src, map_d if use_map else None, orders, n_heads, mult, tables,
+                                                     Vc, t_begin=t_begin, t_count=t_count)
+            e = eg.engram_lookup(src, map_d if use_map else None, orders, n_heads, mult, tables, Vc,
+                                 t_begin=t_begin, t_count=t_count)
+            if t_count == 0:
+                assert codes.numel() == 0
+                continue
+            c2, s2, ss2 = eg.engram_quantize_fp8(e, with_sumsq=True)
+            torch.cuda.synchronize()
+            assert torch.equal(codes, c2) and torch.equal(scales, s2), (use_map, t_begin, t_count)
+            np.testing.assert_allclose(ss.cpu().numpy(), ss2.cpu().numpy(), rtol=2e-6, atol=0)
+
+
+def _fp8q_inputs(n_tok, d_mem, d_model, n_branch, shared, key_norm, seed):
+    g = torch.Generator().manual_seed(seed)
+    e = torch.randn(n_tok, d_mem, generator=g).to(torch.bfloat16).to(DEV)
+    hs = [torch.randn(n_tok, d_model, generator=g).to(torch.bfloat16).to(DEV) for _ in range(n_branch)]
+    wks = [(torch.randn(d_model, d_mem, generator=g) / d_mem ** 0.5).to(torch.bfloat16).to(DEV) for _ in range(n_branch)]
+    wv0 = (torch.randn(d_model, d_mem, generator=g) / d_mem ** 0.5).to(torch.bfloat16).to(DEV)
+    wvs = [wv0] * n_branch if shared else [(torch.randn(d_model, d_mem, generator=g) / d_mem ** 0.5)
+                                           .to(torch.bfloat16).to(DEV) for _ in range(n_branch)]
+    nk = d_mem if key_norm == eg.KEY_NORM_MEMORY else d_model
+    gqs = [(1 + 0.2 * torch.randn(d_model, generator=g)).to(torch.bfloat16).to(DEV) for _ in range(n_branch)]
+    gks = [(1 + 0.2 * torch.randn(nk, generator=g)).to(torch.bfloat16).to(DEV) for _ in range(n_branch)]
+    return e, hs, wks, wvs, gqs, gks
+
+
+@pytest.mark.parametrize("key_norm,n_branch,shared", [
+    (eg.KEY_NORM_MEMORY, 1, False), (eg.KEY_NORM_PROJECTED, 1, False), (eg.KEY_NORM_MEMORY, 3, True),
+    (eg.KEY_NORM_PROJECTED, 2, False)])
+def test_gate_fp8q_equals_gate_fp8(key_norm, n_branch, shared):
+    """The gate on prepared operands (engram_gate_prepare_fp8 weights, engram_quantize_fp8
+    memory vectors) gives engram_gate_forward_fp8's outputs, gates and gated values bit
+    for bit: the same codes, scales and sums, the same kernel."""
+    say(f"gate fp8q key_norm {key_norm} branches {n_branch} shared {shared}")
+    n_tok, d_mem, d_model = 333, 640, 800
+    e, hs, wks, wvs, gqs, gks = _fp8q_inputs(n_tok, d_mem, d_model, n_branch, shared, key_norm, 80 + n_branch)
+    a1 = torch.empty((n_branch, n_tok), dtype=torch.float32, device=DEV)
+    a2 = torch.empty_like(a1)
+    v1 = [torch.empty_like(h) for h in hs]
+    v2 = [torch.empty_like(h) for h in hs]
+    o1 = eg.engram_gate_forward(e, hs, wks, wvs, gqs, gks, 1e-6, gate_out=a1, value_out=v1, key_norm=key_norm,
+                                fp8=True)
+    prep = eg.engram_gate_prepare_fp8(wks, wvs, gqs, gks, key_norm=key_norm)
+    codes, scales, ss = eg.engram_quantize_fp8(e, with_sumsq=True)
+    o2 = eg.engram_gate_forward_fp8q(codes, scales, ss, hs, prep, gqs, gks, 1e-6, gate_out=a2, value_out=v2)
+    torch.cuda.synchronize()
+    assert torch.equal(a1, a2)
+    for m in range(n_branch):
+        assert torch.equal(o1[m].view(torch.int16), o2[m].view(torch.int16))
+        assert torch.equal(v1[m].view(torch.int16), v2[m].view(torch.int16))
+
+
+def test_lookup_fp8_then_gate_fp8q_against_oracle():
+    """The whole FP8 pipeline (engram_lookup_fp8, prepared weights, engram_gate_forward_fp8q)
+    on the small configuration against the oracle's FP8 gate on the oracle's memory vectors
+    (300 sampled tokens)."""
+    cfg = synth.CONFIGS["small"]
+    say("fp8 pipeline vs oracle, small")
+    inp = synth.device_inputs(cfg, DEV)
+    raw = synth.raw_ids(cfg)
+    _, idx_o = oracle_ids_idx(cfg, raw)
+    codes, scales, ss = eg.engram_lookup_fp8(inp["raw"], inp["map"], cfg.orders, cfg.heads, inp["mult"],
+                                             inp["tables"], cfg.vocab_c)
+    prep = eg.engram_gate_prepare_fp8(inp["wk"], inp["wv"], inp["gq"], inp["gk"])
+    alpha = torch.empty((1, cfg.tokens), dtype=torch.float32, device=DEV)
+    out = eg.engram_gate_forward_fp8q(codes, scales, ss, inp["h"], prep, inp["gq"], inp["gk"], cfg.eps,
+                                      gate_out=alpha)[0]
+    torch.cuda.synchronize()
+    sample = sample_tokens(cfg, 300, seed=5)
+    e_o = oracle_memory(cfg, idx_o[sample])
+    h = host_view(synth.hidden_rows(cfg, 0, torch.from_numpy(sample.astype(np.int64))))
+    wk, wv = (host_view(x) for x in synth.weights(cfg, 0))
+    gq, gk = (host_view(x) for x in synth.gains(cfg, 0))
+    out_o, alpha_o = oracle.gate_fp8(e_o, h, wk, wv, gq, gk, cfg.eps, oracle.BF16)
+    sel = torch.from_numpy(sample).to(DEV)
+    err = rel_err(out[sel].float().cpu().numpy(), out_o)
+    aerr = np.abs(alpha[0][sel].cpu().numpy() - alpha_o).max()
+    say(f"  out rel err {err:.2e}, alpha abs err {aerr:.2e}")
+    assert err <= 1e-2 and aerr <= ALPHA_TOL_BF16
