@@ -136,3 +136,39 @@ def test_pipeline_graph_replay_equals_eager():
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(outs[0].view(torch.int16), want[0].view(torch.int16)), rep
+
+
+@pytest.mark.parametrize("key_norm", [eg.KEY_NORM_MEMORY, eg.KEY_NORM_PROJECTED])
+def test_full_multi_config_fp8_pipeline_sampled(key_norm):
+    """The FP8 operand pipeline at the multi-branch workload's full size (4 branches,
+    d_model 4096, 65,536 tokens): engram_lookup_fp8, weights prepared once,
+    engram_gate_forward_fp8q; sampled tokens against the oracle's FP8 gate on the
+    oracle's memory vectors."""
+    import oracle
+    cfg = synth.CONFIGS["multi"]
+    say(f"fp8 pipeline, full multi config, key_norm {key_norm}")
+    inp = synth.device_inputs(cfg, DEV)
+    gks = inp["gk"] if key_norm == eg.KEY_NORM_MEMORY else [
+        synth.gains(cfg, m, DEV, projected_key=True)[1] for m in range(cfg.n_branch)]
+    codes, scales, ss = eg.engram_lookup_fp8(inp["raw"], inp["map"], cfg.orders, cfg.heads, inp["mult"],
+                                             inp["tables"], cfg.vocab_c)
+    prep = eg.engram_gate_prepare_fp8(inp["wk"], inp["wv"], inp["gq"], gks, key_norm=key_norm)
+    alpha = torch.empty((cfg.n_branch, cfg.tokens), dtype=torch.float32, device=DEV)
+    out = eg.engram_gate_forward_fp8q(codes, scales, ss, inp["h"], prep, inp["gq"], gks, cfg.eps, gate_out=alpha)
+    torch.cuda.synchronize()
+    raw = synth.raw_ids(cfg)
+    _, idx_o = oracle_ids_idx(cfg, raw)
+    tok = sample_tokens(cfg, 40)
+    e_o = oracle_memory(cfg, idx_o[tok])
+    sel = torch.from_numpy(tok).to(DEV)
+    for m in range(cfg.n_branch):
+        h = host_view(synth.hidden_rows(cfg, m, torch.from_numpy(tok.astype(np.int64))))
+        wk, wv = (host_view(x) for x in synth.weights(cfg, m))
+        gq = host_view(inp["gq"][m].cpu())
+        gk = host_view(gks[m].cpu())
+        out_o, alpha_o = oracle.gate_fp8(e_o, h, wk, wv, gq, gk, cfg.eps, oracle.BF16, key_norm=key_norm)
+        err = rel_err(out[m][sel].float().cpu().numpy(), out_o)
+        aerr = np.abs(alpha[m][sel].cpu().numpy() - alpha_o).max()
+        say(f"  branch {m}: out rel err {err:.2e}, alpha abs err {aerr:.2e}")
+        assert err <= 1e-2 and aerr <= 2e-3
+    assert torch.all((alpha > 0) & (alpha < 1))
