@@ -109,9 +109,18 @@ def algorithmic(cfg, shared_wv=False):
     }
 
 
+def code_sha(text: str) -> str:
+    """sha256 of C++ source with its comments and whitespace removed: changes when the
+    code does, not when a comment does (the source holds no string with a comment marker)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256("".join(text.split()).encode()).hexdigest()
+
+
 def gate_source_sha():
-    with open(GATE_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    with open(GATE_SOURCE) as f:
+        return code_sha(f.read())
 
 
 def measured_traffic(cfg):

@@ -1,4 +1,5 @@
-// gate_bf16.hip -- context-aware gating on the gfx950 matrix cores (bf16 in, fp32 accumulate).
+// gate_bf16.hip -- context-aware gating on the gfx950 matrix cores (bf16 operands, or E4M3
+// codes for the FP8 form; fp32 accumulation).
 //
 // "Conditional Memory via Scalable Lookup", section 2.3, Eq. (3)-(4) with the
 // gated value and residual update, and section 2.4, Eq. (6) for branches that
@@ -63,6 +64,11 @@
 // are swizzled by (token & 31) so that 32 lanes reading 32 tokens hit distinct
 // banks.  A V tile writes out into the same LDS tile and then streams it to
 // HBM with coalesced 16-byte stores.
+//
+// Variants.  The persistent kernel is instantiated per option (gate_tile lists them):
+// the gated-value output, the paper's projected key norm, one W_V shared by all
+// branches, and FP8 operands (E4M3 codes, 32x32x64 MFMA, 128 k-values per ring row).
+// Each is its own instantiation so that the plain gate keeps its register allocation.
 #include "engram_internal.h"
 
 namespace engram {
