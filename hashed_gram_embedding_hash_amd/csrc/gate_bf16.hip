@@ -518,20 +518,21 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
     // ---- FP8 main loop.  The same ring and chunk numbering; a 128-byte k-step is two
     // halves of 64 k-values, and the fragment of a half is the two 16-byte chunks that
     // the bf16 loop reads for two consecutive sub-steps (logical chunks 4 p + khalf and
-    // 4 p + 2 + khalf), for both operands alike.  Each fragment register is reloaded as
-    // soon as its last MFMA has issued (row i of A after MFMA (i, MT-1), column j of B
-    // after MFMA (MF-1, j)):
-    //   half 0 of k-step kt, reading half 1 of kt;
+    // 4 p + 2 + khalf), for both operands alike.  A weight fragment register is reloaded
+    // as soon as its last MFMA has issued (row i after MFMA (i, MT-1)); the memory
+    // fragments, each used by every row, are double-buffered (half p in set p) and read
+    // one after every second MFMA from the start of the other half:
+    //   half 0 of k-step kt, reading half 1 of kt and loading chunk 2 kt + 4 (weight
+    //   rows of kt + 2) into the slot k-step kt - 1's memory rows left;
     //   wait + barrier: k-step kt + 1 has landed, k-step kt's slots are free;
-    //   half 1 of kt, reading half 0 of kt + 1 and refilling kt's slots with chunks
-    //   2 kt + 5 (memory rows) and 2 kt + 6 (weight rows), one load after every MFMA;
-    //   in the last three k-steps, where these are h-tile quarters or nothing, as a
-    //   burst before the MFMAs.
-    // Chunk 2 kt + 3 is issued during half 1 of kt - 1 and needed at the barrier of kt,
-    // when only chunk 2 kt + 4 may still be in flight.  No branch may enter the MFMA
-    // sequences (the compiler would move the MFMAs past it): the last k-step reads
+    //   half 1 of kt, reading half 0 of kt + 1 and loading chunk 2 kt + 5 (memory rows
+    //   of kt + 2) into kt's weight slot.
+    // The loads go one after every second MFMA, as in the bf16 loop; in the last two
+    // k-steps, where the chunks are h-tile quarters, as a burst before the MFMAs.  Only
+    // chunk 2 kt + 4 may be in flight at the barrier of kt.  No branch may enter the
+    // MFMA sequences (the compiler would move the MFMAs past it): the last k-step reads
     // fragments it does not use.
-    v8i fa8[MF], fb8[MT];
+    v8i fa8[MF], fb8[2][MT];  // B fragments double-buffered: half 0 in set 0, half 1 in set 1
     auto frag8 = [&](int base, uint32_t o0, uint32_t o1) -> v8i {
       const u32x4 lo = *reinterpret_cast<const u32x4*>(smem + base + o0);
       const u32x4 hi = *reinterpret_cast<const u32x4*>(smem + base + o1);
@@ -539,55 +540,53 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
                                      5, 6, 7);
     };
 #define ENGRAM_F8_A(sa_, p_, i_) fa8[i_] = frag8((sa_) + (i_) * 32 * 2 * BK, fr_a[2 * (p_)], fr_a[2 * (p_) + 1])
-#define ENGRAM_F8_B(sb_, p_, j_) fb8[j_] = frag8((sb_) + (j_) * 32 * 2 * BK, fr_b[2 * (p_)], fr_b[2 * (p_) + 1])
-#define ENGRAM_F8_MFMA(i_, j_)                                                             \
-  acc[i_][j_] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa8[i_], fb8[j_], acc[i_][j_], 0, 0, 0, 127, 0, 127)
+#define ENGRAM_F8_B(sb_, p_, j_) fb8[p_][j_] = frag8((sb_) + (j_) * 32 * 2 * BK, fr_b[2 * (p_)], fr_b[2 * (p_) + 1])
+#define ENGRAM_F8_MFMA(p_, i_, j_)                                                         \
+  acc[i_][j_] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa8[i_], fb8[p_][j_], acc[i_][j_], 0, 0, 0, 127, 0, 127)
 #define ENGRAM_F8_KSTEP(spread_)                                                           \
   do {                                                                                     \
     const int sa = ((2 * kt) % NSLOT) * SLOT_BYTES;                                        \
     const int sb = ((2 * kt + 1) % NSLOT) * SLOT_BYTES;                                    \
+    if (!(spread_)) issue_chunk(2 * kt + 4);                                               \
+    const uint8_t* srcW = W8 + (kt + 2) * (2 * BK);                                        \
+    const uint32_t dstW = wave_dst + (uint32_t)(((2 * kt + 4) % NSLOT) * SLOT_BYTES);      \
     __builtin_amdgcn_sched_barrier(0);                                                     \
     _Pragma("unroll") for (int k = 0; k < MF * MT; ++k) {                                  \
-      ENGRAM_F8_MFMA(k / MT, k % MT);                                                      \
+      ENGRAM_F8_MFMA(0, k / MT, k % MT);                                                   \
       __builtin_amdgcn_sched_barrier(0);                                                   \
-      if (k / MT == MF - 1) ENGRAM_F8_B(sb, 1, k % MT);                                    \
+      if ((k & 1) == 0 && k < 2 * MT) ENGRAM_F8_B(sb, 1, k >> 1);                          \
       if (k % MT == MT - 1) ENGRAM_F8_A(sa, 1, k / MT);                                    \
+      if ((spread_) && (k & 1)) dma16((const uint16_t*)(srcW + off_a[k >> 1]), dstW + (k >> 1) * 1024); \
       __builtin_amdgcn_sched_barrier(0);                                                   \
     }                                                                                      \
     wait_vm_lgkm0<G_INSTR>();                                                              \
     lds_barrier();                                                                         \
-    if (!(spread_)) {                                                                      \
-      issue_chunk(2 * kt + 5);                                                             \
-      if (2 * kt + 6 <= 2 * nk + 3) issue_chunk(2 * kt + 6);                               \
-    }                                                                                      \
+    if (!(spread_)) issue_chunk(2 * kt + 5);                                               \
     const int sa2 = ((2 * kt + 2) % NSLOT) * SLOT_BYTES;                                   \
     const int sb2 = ((2 * kt + 3) % NSLOT) * SLOT_BYTES;                                   \
     const uint8_t* srcE = Et8 + (kt + 2) * (2 * BK);                                       \
-    const uint8_t* srcW = W8 + (kt + 3) * (2 * BK);                                        \
-    const uint32_t dstE = wave_dst + (uint32_t)sa, dstW = wave_dst + (uint32_t)sb;         \
+    const uint32_t dstE = wave_dst + (uint32_t)sa;                                         \
     __builtin_amdgcn_sched_barrier(0);                                                     \
     _Pragma("unroll") for (int k = 0; k < MF * MT; ++k) {                                  \
-      ENGRAM_F8_MFMA(k / MT, k % MT);                                                      \
+      ENGRAM_F8_MFMA(1, k / MT, k % MT);                                                   \
       __builtin_amdgcn_sched_barrier(0);                                                   \
-      if (k / MT == MF - 1) ENGRAM_F8_B(sb2, 0, k % MT);                                   \
+      if ((k & 1) == 0 && k < 2 * MT) ENGRAM_F8_B(sb2, 0, k >> 1);                         \
       if (k % MT == MT - 1) ENGRAM_F8_A(sa2, 0, k / MT);                                   \
-      if (spread_) {                                                                       \
-        if (k < G_INSTR) dma16((const uint16_t*)(srcE + off_b[k]), dstE + k * 1024);      \
-        else dma16((const uint16_t*)(srcW + off_a[k - G_INSTR]), dstW + (k - G_INSTR) * 1024); \
-      }                                                                                    \
+      if ((spread_) && (k & 1)) dma16((const uint16_t*)(srcE + off_b[k >> 1]), dstE + (k >> 1) * 1024); \
       __builtin_amdgcn_sched_barrier(0);                                                   \
     }                                                                                      \
   } while (0)
-    for (int c = 0; c < NSLOT; ++c) issue_chunk(c);
-    wait_vm_lgkm0<3 * G_INSTR>();
+    // chunks 0-3 (k-steps 0 and 1) up front; k-step 0 waits for its own two
+    for (int c = 0; c < 4; ++c) issue_chunk(c);
+    wait_vm_lgkm0<2 * G_INSTR>();
     lds_barrier();
 #pragma unroll
     for (int j = 0; j < MT; ++j) ENGRAM_F8_B(SLOT_BYTES, 0, j);
 #pragma unroll
     for (int i = 0; i < MF; ++i) ENGRAM_F8_A(0, 0, i);
     int kt = 0;
-    // chunks 2 kt + 5 and 2 kt + 6 are both operand rows while kt + 3 < nk
-    for (; kt + 3 < nk; ++kt) ENGRAM_F8_KSTEP(true);
+    // chunks 2 kt + 4 and 2 kt + 5 are both operand rows while kt + 3 <= nk
+    for (; kt + 3 <= nk; ++kt) ENGRAM_F8_KSTEP(true);
     for (; kt < nk; ++kt) ENGRAM_F8_KSTEP(false);
 #undef ENGRAM_F8_KSTEP
 #undef ENGRAM_F8_A
