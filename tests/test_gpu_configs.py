@@ -106,7 +106,7 @@ def test_decode_prefetch_pipeline():
 
 
 def test_pipeline_graph_replay_equals_eager():
-    """The layer's step (compress, hash, gather, gate: five kernels) captured in a HIP
+    """The layer's step (the fused lookup and the gate: three kernels) captured in a HIP
     graph: every replay, with eager work on the same buffers in between, reproduces the
     eager result bit for bit (1 x 2048 tokens of the small configuration's shapes)."""
     cfg = synth.CONFIGS["small"].replace(batch=1, seq=2048)
@@ -135,6 +135,53 @@ def test_pipeline_graph_replay_equals_eager():
         assert torch.equal(eager[0].view(torch.int16), other[0].view(torch.int16)), rep
         g.replay()
         torch.cuda.synchronize()
+        assert torch.equal(outs[0].view(torch.int16), want[0].view(torch.int16)), rep
+
+
+def test_fp8_operand_step_graph_replay_equals_eager():
+    """The FP8 operand step (engram_lookup_fp8, engram_gate_forward_fp8q with weights
+    prepared once) captured in a HIP graph: every replay, with eager FP8 work on the same
+    buffers and scratch in between, reproduces the eager codes, scales, sums and outputs
+    bit for bit (1 x 2048 tokens of the small configuration's shapes)."""
+    cfg = synth.CONFIGS["small"].replace(batch=1, seq=2048)
+    say("graph replay of the fp8 operand step")
+    inp = synth.device_inputs(cfg, DEV)
+    prep = eg.engram_gate_prepare_fp8(inp["wk"], inp["wv"], inp["gq"], inp["gk"])
+    n = cfg.tokens
+    codes = torch.empty((n, cfg.d_mem), dtype=torch.uint8, device=DEV)
+    scales = torch.empty(n, dtype=torch.float32, device=DEV)
+    ss = torch.empty(n, dtype=torch.float32, device=DEV)
+    outs = [torch.empty_like(x) for x in inp["h"]]
+
+    def step(raw, out):
+        eg.engram_lookup_fp8(raw, inp["map"], cfg.orders, cfg.heads, inp["mult"], inp["tables"], cfg.vocab_c,
+                             codes=codes, scales=scales, sumsq=ss)
+        return eg.engram_gate_forward_fp8q(codes, scales, ss, inp["h"], prep, inp["gq"], inp["gk"], cfg.eps,
+                                           out=out)
+
+    raw = inp["raw"]
+    raw2 = torch.roll(raw, 7, dims=1).contiguous()
+    want = [x.clone() for x in step(raw, None)]
+    want_q = (codes.clone(), scales.clone(), ss.clone())
+    other = [x.clone() for x in step(raw2, None)]
+    assert not torch.equal(other[0], want[0])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(raw, outs)                    # the gate's scratch is sized on the capture stream
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step(raw, outs)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        outs[0].zero_()
+        eager = step(raw2, None)           # eager work on the same operand buffers and scratch
+        torch.cuda.synchronize()
+        assert torch.equal(eager[0].view(torch.int16), other[0].view(torch.int16)), rep
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(codes, want_q[0]) and torch.equal(scales, want_q[1]) and torch.equal(ss, want_q[2]), rep
         assert torch.equal(outs[0].view(torch.int16), want[0].view(torch.int16)), rep
 
 
