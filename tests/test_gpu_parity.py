@@ -1050,3 +1050,32 @@ def test_lookup_fp8_then_gate_fp8q_against_oracle():
     aerr = np.abs(alpha[0][sel].cpu().numpy() - alpha_o).max()
     say(f"  out rel err {err:.2e}, alpha abs err {aerr:.2e}")
     assert err <= 1e-2 and aerr <= ALPHA_TOL_BF16
+
+
+@pytest.mark.parametrize("n_tok", [1, 2, 255, 256, 257])
+@pytest.mark.parametrize("fp8", [False, True])
+def test_gate_token_counts_at_tile_edges(n_tok, fp8):
+    """A single token (a decode step of one sequence), two, and one token either side of the
+    256-token tile: the bf16 and FP8 gates against the oracle (d_mem 1280, d_model 800:
+    a ragged last feature tile as well)."""
+    say(f"gate n_tok {n_tok} fp8 {fp8}")
+    d_mem, d_model = 1280, 800
+    g = torch.Generator().manual_seed(1000 + n_tok)
+    e = torch.randn(n_tok, d_mem, generator=g).to(torch.bfloat16)
+    h = torch.randn(n_tok, d_model, generator=g).to(torch.bfloat16)
+    wk = (torch.randn(d_model, d_mem, generator=g) / d_mem ** 0.5).to(torch.bfloat16)
+    wv = (torch.randn(d_model, d_mem, generator=g) / d_mem ** 0.5).to(torch.bfloat16)
+    gq = (1 + 0.2 * torch.randn(d_model, generator=g)).to(torch.bfloat16)
+    gk = (1 + 0.2 * torch.randn(d_mem, generator=g)).to(torch.bfloat16)
+    alpha = torch.empty((1, n_tok), dtype=torch.float32, device=DEV)
+    out = eg.engram_gate_forward(e.to(DEV), [h.to(DEV)], [wk.to(DEV)], [wv.to(DEV)], [gq.to(DEV)], [gk.to(DEV)],
+                                 1e-6, gate_out=alpha, fp8=fp8)[0]
+    torch.cuda.synchronize()
+    ref = oracle.gate_fp8 if fp8 else oracle.gate
+    out_o, alpha_o = ref(host_view(e), host_view(h), host_view(wk), host_view(wv), host_view(gq), host_view(gk),
+                         1e-6, oracle.BF16)
+    err = rel_err(out.float().cpu().numpy(), out_o)
+    aerr = np.abs(alpha[0].cpu().numpy() - alpha_o).max()
+    upd = rel_err(out.float().cpu().numpy() - host_bf16_to_f64(h), out_o - host_bf16_to_f64(h))
+    say(f"  out rel err {err:.2e}, alpha abs err {aerr:.2e}, update rel err {upd:.2e}")
+    assert err <= 1e-2 and aerr <= ALPHA_TOL_BF16 and upd <= UPDATE_TOL_STRESS
