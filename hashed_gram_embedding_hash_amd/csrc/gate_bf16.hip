@@ -21,8 +21,8 @@
 //           every tile does 1/n_ftiles of it.  The last K tile of a (branch, token
 //           tile) to finish turns the partials into alpha (fixed-order sums:
 //           bit-reproducible) and publishes it;
-//   V tile: waits until alpha of its (branch, token tile) is published, computes
-//           acc = W_V e^T and writes out = h + alpha acc.
+//   V tile: computes acc = W_V e^T, waits until alpha of its (branch, token tile)
+//           is published (usually long before) and writes out = h + alpha acc.
 // Since q . k = (sum_f h_f gq_f k~_f) / (rms(h) rms(e)) with k~ = W_K diag(gk) e,
 // the RMSNorm scales are applied to the reduced scalar, never to a tensor.
 //
@@ -31,12 +31,12 @@
 // tiles T with T % 8 == b % 8: first all their K tiles, then all their V tiles,
 // feature tile fastest.  A workgroup claims the next tile of its queue with an
 // atomic increment (the next one already when the current tile's epilogue
-// starts, so the claim's latency is hidden); a V tile spins until the done-counter of its K tiles is
-// full.  Those K tiles sit earlier in the same queue, so they were claimed
-// before by running workgroups that never wait: the spin always ends.  The
-// single queue per XCD removes the partial last round of a two-launch design
-// (640 + 640 tiles on 256 CUs become 1280 = 5 x 256) and keeps a token tile's
-// memory rows in one XCD's L2.
+// starts, so the claim's latency is hidden); before its epilogue a V tile spins
+// until the done-counter of its K tiles is full.  Those K tiles sit earlier in the
+// same queue, so they were claimed before by running workgroups that never wait:
+// the spin always ends.  The single queue per XCD removes the partial last round of
+// a two-launch design (640 + 640 tiles on 256 CUs become 1280 = 5 x 256) and keeps
+// a token tile's memory rows in one XCD's L2.
 //
 // Tiling.  256 features x 256 tokens per tile, four wavefronts in 2 x 2, each
 // owning 128 x 128 outputs = 4 x 4 MFMA 32x32 tiles (256 fp32 accumulators per
@@ -236,22 +236,23 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
   const uint16_t* E = (const uint16_t*)a.mem;
   const uint16_t* H = (const uint16_t*)a.h[m];
 
+  // ---- V tiles need the gates of their (branch, token tile), published by its last K
+  // tile (done count n_ftiles + 1), only in the epilogue.  Each wave looks at the count
+  // once here: if the gates are out, it fetches its tokens' gates now and the loads
+  // complete behind the main loop; if not, it runs the main loop anyway and waits after
+  // it (with few tiles in flight, as in a decode step, V tiles then overlap K tiles).
   float alpha = 0.f;  // V tiles: the gate of token t0 + tid (to LDS once the ring drains)
+  bool gates_ready = true;  // wave-uniform
   if (PHASE == PHASE_V) {
-    // ---- wait until the last K tile of this (branch, token tile) has published its
-    // gates (done count n_ftiles + 1), then fetch this thread's token's gate; the load
-    // completes behind the main loop
-    if (tid == 0) {
-      int spin = 0;
-      for (int mb = SHAREDV ? 0 : m; mb < (SHAREDV ? a.n_branch : m + 1); ++mb) {
-        const int32_t* dn = a.counters + NQ + mb * a.n_ttiles + tile.ttile;
-        while (__hip_atomic_load(dn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.n_ftiles + 1 &&
-               ++spin < SPIN_LIMIT)
-          __builtin_amdgcn_s_sleep(1);
-      }
+    int seen = 1;
+    if (lane == 0) {
+      for (int mb = SHAREDV ? 0 : m; mb < (SHAREDV ? a.n_branch : m + 1); ++mb)
+        seen &= __hip_atomic_load(a.counters + NQ + mb * a.n_ttiles + tile.ttile, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT) >= a.n_ftiles + 1;
     }
-    lds_barrier();  // the gate loads below are issued only after the count is seen
-    if (t0 + tid < n_tok) alpha = ld_coherent(a.alpha + (int64_t)m * n_tok + t0 + tid);
+    gates_ready = __builtin_amdgcn_readfirstlane(seen) != 0;
+    // issued only after lane 0's count came back (the branch depends on it)
+    if (gates_ready && t0 + tid < n_tok) alpha = ld_coherent(a.alpha + (int64_t)m * n_tok + t0 + tid);
   }
   float kg = 0.f;  // KEYP K tiles: gq * gk of feature f0 + tid (to LDS in the epilogue)
   if (KEYP && PHASE == PHASE_K && f0 + tid < d_model) kg = a.kgain[(int64_t)m * d_model + f0 + tid];
@@ -646,6 +647,20 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
   float* s_g = reinterpret_cast<float*>(scratch + 8 * BT * sizeof(float));               // KEYP, [BF]
   float* s_fs = reinterpret_cast<float*>(scratch + 8 * BT * sizeof(float) + BF * sizeof(float));  // F8, [BF]
   if (PHASE == PHASE_V) {
+    if (!gates_ready) {
+      // the wait deferred from the tile's start: lane 0 polls the done count(s), bounded
+      // by SPIN_LIMIT, and the wave's gate loads follow once it has seen them
+      if (elane == 0) {
+        int spin = 0;
+        for (int mb = SHAREDV ? 0 : m; mb < (SHAREDV ? a.n_branch : m + 1); ++mb) {
+          const int32_t* dn = a.counters + NQ + mb * a.n_ttiles + tile.ttile;
+          while (__hip_atomic_load(dn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.n_ftiles + 1 &&
+                 ++spin < SPIN_LIMIT)
+            __builtin_amdgcn_s_sleep(1);
+        }
+      }
+      if (t0 + etid < n_tok) alpha = ld_coherent(a.alpha + (int64_t)m * n_tok + t0 + etid);
+    }
     if constexpr (F8) s_alpha[etid] = alpha * ts;  // the token scale rides on the gate
     else s_alpha[etid] = alpha;
     lds_barrier();
