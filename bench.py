@@ -703,7 +703,7 @@ def main():
     kernel = ("engram_gate_forward_fp8: gate_prep_projected_kernel + quant_rows_kernel (W_K, W_V, mem) + "
               "gate_persistent_kernel (events bracket all)" if args.fp8 else
               "engram_gate_forward: gate_prep_kernel + gate_persistent_kernel "
-              "(events bracket both; the prep kernel is ~1% of the call)")
+              "(events bracket both; the prep kernel is about 3 % of the call)")
     roofline = {"kernel": kernel,
                 "bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic,
