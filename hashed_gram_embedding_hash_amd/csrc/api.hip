@@ -94,8 +94,9 @@ const void* mapped_host_pointer(const void* p) {
 // nothing more (stream order); a call on another stream first waits for an event
 // recorded after the previous use.  Growing frees the old buffer in stream order behind
 // that wait.  The lock is held from acquiring the buffer until the launches and the
-// event record are enqueued, so concurrent host threads take turns.  Buffers live until
-// the process ends.
+// event record are enqueued, so concurrent host threads take turns.  The current buffer
+// lives until the process ends; a replaced one is freed behind the growing call, which
+// invalidates graphs captured with it.
 struct Scratch {
   void* ptr = nullptr;
   size_t bytes = 0;

@@ -28,7 +28,11 @@
  *     and the convolution share one grow-only scratch buffer per device (a few
  *     MB to a few hundred MB, by shape), allocated stream-ordered on first use
  *     and held until the process ends; a call on a different stream than the
- *     previous user of the scratch first waits for that call's work on it.
+ *     previous user of the scratch first waits for that call's work on it.  A
+ *     call that needs more scratch than any call before it replaces the buffer
+ *     (the old one is freed in stream order), so a HIP graph captured earlier
+ *     must not be replayed after such a call: capture after a call of the
+ *     largest shape the graph will be used with.
  *   - Errors: arguments are validated on the host before anything is enqueued;
  *     a non-OK status means nothing was enqueued (ENGRAM_ERR_INVALID_ARG,
  *     ENGRAM_ERR_UNSUPPORTED) or a HIP call failed (ENGRAM_ERR_HIP).
