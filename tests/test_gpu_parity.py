@@ -1079,3 +1079,39 @@ def test_gate_token_counts_at_tile_edges(n_tok, fp8):
     upd = rel_err(out.float().cpu().numpy() - host_bf16_to_f64(h), out_o - host_bf16_to_f64(h))
     say(f"  out rel err {err:.2e}, alpha abs err {aerr:.2e}, update rel err {upd:.2e}")
     assert err <= 1e-2 and aerr <= ALPHA_TOL_BF16 and upd <= UPDATE_TOL_STRESS
+
+
+# ---------------------------------------------------------------------------
+# the largest shapes the library accepts
+# ---------------------------------------------------------------------------
+def test_lookup_and_gather_at_the_maximum_table_count_and_row_size():
+    """32 tables (orders 1-4 x 8 heads, ENGRAM_MAX_TABLES) of 512-byte bf16 rows: a 16 KiB
+    concatenated memory vector, the largest the gather accepts; fused lookup and plain
+    gather both bit-exact against the oracle's compress, hash and gather."""
+    say("lookup/gather at 32 tables x 512-byte rows")
+    rng = np.random.default_rng(321)
+    V, Vc, heads, w = 5000, 3001, 8, 256
+    orders = (1, 2, 3, 4)
+    cmap = rng.integers(0, Vc, V).astype(np.int32)
+    raw = rng.integers(0, V, (2, 100)).astype(np.int32)
+    mult = synth.hash_multipliers(321, orders, heads)
+    rows = np.array([synth.next_prime(int(x)) for x in rng.integers(500, 3000, len(orders) * heads)], np.uint32)
+    tabs = [torch.randn(int(r), w, generator=torch.Generator().manual_seed(int(r))).to(torch.bfloat16) for r in rows]
+    ids_o, _ = oracle.compress(raw, cmap)
+    idx_o = oracle.hash_ids(ids_o, orders, heads, mult, rows, Vc)
+    e_o = oracle.gather(idx_o, [t.view(torch.int16).numpy() for t in tabs])
+    assert e_o.shape == (200, 32 * w) and e_o.nbytes // 200 == 16384
+    tabs_d = [t.to(DEV) for t in tabs]
+    got = eg.engram_lookup(torch.from_numpy(raw).to(DEV), torch.from_numpy(cmap).to(DEV), orders, heads, mult,
+                           tabs_d, Vc)
+    got2 = eg.engram_gather(torch.from_numpy(idx_o).to(DEV), tabs_d)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.view(torch.int16).cpu().numpy(), e_o)
+    assert np.array_equal(got2.view(torch.int16).cpu().numpy(), e_o)
+
+
+def test_gate_bf16_maximum_branches_in_place():
+    """ENGRAM_MAX_BRANCHES = 8 branches sharing one memory vector, each with its own
+    weights and gains, written in place, on a ragged token count."""
+    say("gate bf16, 8 branches")
+    _gate_case(synth.CONFIGS["small"], 300, seed=92, n_branch=8, inplace=True)
