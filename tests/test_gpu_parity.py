@@ -1115,3 +1115,39 @@ def test_gate_bf16_maximum_branches_in_place():
     weights and gains, written in place, on a ragged token count."""
     say("gate bf16, 8 branches")
     _gate_case(synth.CONFIGS["small"], 300, seed=92, n_branch=8, inplace=True)
+
+
+def test_empty_inputs_through_the_bindings():
+    """Zero tokens (or zero positions) through every binding: empty results and no error
+    (empty tensors have null data pointers, which the library accepts for empty calls)."""
+    say("empty inputs")
+    rng = np.random.default_rng(5)
+    orders, heads, w = (2, 3), 2, 80
+    mult = synth.hash_multipliers(5, orders, heads)
+    rows = [synth.next_prime(int(x)) for x in rng.integers(500, 900, 4)]
+    tabs = [torch.randn(r, w).to(torch.bfloat16).to(DEV) for r in rows]
+    cmap = torch.from_numpy(rng.integers(0, 700, 1000).astype(np.int32)).to(DEV)
+    raw = torch.from_numpy(rng.integers(0, 1000, (2, 50)).astype(np.int32)).to(DEV)
+    assert eg.engram_lookup(raw, cmap, orders, heads, mult, tabs, 700, t_begin=10, t_count=0).shape == (0, 4 * w)
+    codes, scales, sumsq = eg.engram_lookup_fp8(raw, cmap, orders, heads, mult, tabs, 700, t_count=0)
+    assert codes.shape == (0, 4 * w) and scales.shape == (0,) and sumsq.shape == (0,)
+    assert eg.engram_gather(torch.empty((0, 4), dtype=torch.int32, device=DEV), tabs).shape == (0, 4 * w)
+    assert eg.engram_quantize_fp8(torch.empty((0, 256), dtype=torch.bfloat16, device=DEV))[0].shape == (0, 256)
+    d_mem, d_model = 256, 512
+    mem = torch.empty((0, d_mem), dtype=torch.bfloat16, device=DEV)
+    h = [torch.empty((0, d_model), dtype=torch.bfloat16, device=DEV)]
+    wk = [torch.randn(d_model, d_mem).to(torch.bfloat16).to(DEV)]
+    wv = [torch.randn(d_model, d_mem).to(torch.bfloat16).to(DEV)]
+    gq = [torch.ones(d_model, dtype=torch.bfloat16, device=DEV)]
+    gk = [torch.ones(d_mem, dtype=torch.bfloat16, device=DEV)]
+    alpha = torch.full((1, 0), 7.0, device=DEV)
+    for fp8 in (False, True):
+        out = eg.engram_gate_forward(mem, h, wk, wv, gq, gk, gate_out=alpha, fp8=fp8)
+        assert out[0].shape == (0, d_model)
+    prep = eg.engram_gate_prepare_fp8(wk, wv, gq, gk)
+    e8 = eg.engram_quantize_fp8(mem, with_sumsq=True)
+    assert eg.engram_gate_forward_fp8q(*e8, h, prep, gq, gk)[0].shape == (0, d_model)
+    val = torch.empty((0, d_model), dtype=torch.bfloat16, device=DEV)
+    cw = torch.randn(d_model, 4).to(torch.bfloat16).to(DEV)
+    assert eg.engram_conv_forward(val, 0, 7, cw, gq[0], 3, val.clone()).shape == (0, d_model)
+    torch.cuda.synchronize()
