@@ -675,6 +675,20 @@ def main():
     sep_names = ["compress_hash", "gather"]
     _, _, sep_per, _ = time_steps(separate, args.steps, 3, False, names=sep_names)
 
+    # the bf16 gate on key weights folded once (engram_gate_prepare): the same results, without
+    # the per-call folding kernel
+    prepared = None
+    if cfg.dtype == "bf16" and layer.key_norm == eg.KEY_NORM_MEMORY and not args.fp8:
+        folded = eg.engram_gate_prepare(layer.wk, layer.gq, layer.gk)
+        def gate_prepared(ev=None):
+            if ev is not None:
+                ev[0].record()
+            eg.engram_gate_forward_prepared(bufs["mem"], h, folded, layer.wv, cfg.eps, out=outs)
+            if ev is not None:
+                ev[1].record()
+        _, _, prep_per, _ = time_steps(gate_prepared, args.steps, 3, False, names=["gate"])
+        prepared = prep_per["gate"]
+
     work = algorithmic(cfg, args.shared_wv)
     def rates(n, ms):
         s = ms * 1e-3
@@ -690,6 +704,11 @@ def main():
             d["TFLOP/s"] = round(work[n]["flops"] / (per[n] * 1e-3) / 1e12, 2)
         kernels[n] = d
     separate_calls = {n: rates(n, sep_per[n]) for n in sep_names}
+    if prepared is not None:
+        separate_calls["gate_prepared_weights"] = {
+            "ms": round(prepared, 5), "TFLOP/s": round(work["gate"]["flops"] / (prepared * 1e-3) / 1e12, 2),
+            "note": "engram_gate_forward_prepared on key weights folded once by engram_gate_prepare "
+                    "(bit-identical results; no per-call folding kernel), timed eagerly after the cache flush"}
     gate_s = per["gate"] * 1e-3
     if cfg.dtype == "bf16" and args.fp8:
         peak, dtype = PEAK_FP8_TFLOPS, "fp8e4m3 projections, bf16 storage"
@@ -724,7 +743,7 @@ def main():
         "wall_s_timed": round(t_wall, 4),
         "cache_flush_mb_between_steps": args.flush_mb,
         "kernels": kernels,
-        "separate_calls": {**separate_calls, "note": "the lookup as engram_compress_hash + engram_gather, "
+        "separate_calls": {**separate_calls, "note": "the lookup as engram_compress_hash + engram_gather, and the gate on prepared weights, "
                                                      "timed eagerly in the same run (not part of the step)"},
         "roofline": roofline,
     }

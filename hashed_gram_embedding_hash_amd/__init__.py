@@ -55,7 +55,8 @@ EXPORTS = (
     "engram_gate_forward", "engram_conv_forward", "engram_prefetch_host", "engram_host_alloc",
     "engram_host_free", "engram_cache_select", "engram_cache_build", "engram_prefetch_host_cached",
     "engram_compress_hash", "engram_quantize_fp8", "engram_gate_forward_fp8", "engram_lookup",
-    "engram_lookup_fp8", "engram_gate_prepare_fp8", "engram_gate_forward_fp8q",
+    "engram_lookup_fp8", "engram_gate_prepare_fp8", "engram_gate_forward_fp8q", "engram_gate_prepare",
+    "engram_gate_forward_prepared",
 )
 
 
@@ -96,6 +97,8 @@ def lib() -> ctypes.CDLL:
         L.engram_gate_forward_fp8.argtypes = L.engram_gate_forward.argtypes
         L.engram_lookup_fp8.argtypes = [P, i32, i64, i64, i64, P, i32, P, i32, i32, P, P, i32, P, i32, P, P, P, P, P,
                                         P, P]
+        L.engram_gate_prepare.argtypes = [i32, i32, i32, P, P, P, P, P]
+        L.engram_gate_forward_prepared.argtypes = [P, i64, i32, i32, i32, P, P, P, ctypes.c_float, P, P, P, P]
         L.engram_gate_prepare_fp8.argtypes = [i32, i32, i32, P, P, P, P, i32, P, P, P, P, P]
         L.engram_gate_forward_fp8q.argtypes = [P, P, P, i64, i32, i32, i32, P, P, P, P, P, P, P, ctypes.c_float, i32,
                                                P, P, P, P]
@@ -439,6 +442,66 @@ def engram_gate_forward(mem, h: Sequence, wk: Sequence, wv: Sequence, gq: Sequen
     _check(fn(mem.data_ptr(), n_tok, d_mem, d_model, nb, arr(h), arr(wk), arr(wv), arr(gq), arr(gk), float(eps),
               _edtype(mem), int(key_norm), arr(out), _opt(gate_out, "gate_out", torch.float32), varr,
               _stream(stream)))
+    return out
+
+
+def engram_gate_prepare(wk: Sequence, gq: Sequence, gk: Sequence, stream=None):
+    """The bf16 gate's key weights with both RMSNorm gains folded in (memory-side key
+    norm): one [d_model, d_mem] bf16 tensor per branch, for engram_gate_forward_prepared."""
+    import torch
+    nb = len(wk)
+    d_model, d_mem = wk[0].shape
+    if not (len(gq) == len(gk) == nb):
+        raise ValueError("one wk/gq/gk per branch")
+    for x in wk:
+        _dev(x, "wk", torch.bfloat16)
+        if tuple(x.shape) != (d_model, d_mem):
+            raise ValueError("weights must be [d_model, d_mem]")
+    for x in gq:
+        _dev(x, "gq", torch.bfloat16)
+        if tuple(x.shape) != (d_model,):
+            raise ValueError("gq must be [d_model]")
+    for x in gk:
+        _dev(x, "gk", torch.bfloat16)
+        if tuple(x.shape) != (d_mem,):
+            raise ValueError("gk must be [d_mem]")
+    folded = [torch.empty_like(x) for x in wk]
+    arr = lambda seq: _ptr_array([x.data_ptr() for x in seq])
+    _check(lib().engram_gate_prepare(d_mem, d_model, nb, arr(wk), arr(gq), arr(gk), arr(folded), _stream(stream)))
+    return folded
+
+
+def engram_gate_forward_prepared(mem, h: Sequence, wk_folded: Sequence, wv: Sequence, eps: float = 1e-6,
+                                 out: Optional[Sequence] = None, gate_out=None, value_out: Optional[Sequence] = None,
+                                 stream=None):
+    """engram_gate_forward (bf16, KEY_NORM_MEMORY) on key weights from engram_gate_prepare;
+    bit-identical to it."""
+    import torch
+    n_tok, d_mem = mem.shape
+    nb = len(h)
+    d_model = h[0].shape[1]
+    _dev(mem, "mem", torch.bfloat16)
+    if out is None:
+        out = [torch.empty_like(x) for x in h]
+    if not (len(wk_folded) == len(wv) == len(out) == nb):
+        raise ValueError("one h/wk_folded/wv/out per branch")
+    if value_out is not None and len(value_out) != nb:
+        raise ValueError("one value_out entry per branch")
+    vals = [x for x in (value_out or []) if x is not None]
+    for name, seq in (("h", h), ("wk_folded", wk_folded), ("wv", wv), ("out", out), ("value_out", vals)):
+        for x in seq:
+            _dev(x, name, torch.bfloat16)
+    for x in list(h) + list(out) + vals:
+        if tuple(x.shape) != (n_tok, d_model):
+            raise ValueError("h/out/value_out must be [n_tok, d_model]")
+    for x in list(wk_folded) + list(wv):
+        if tuple(x.shape) != (d_model, d_mem):
+            raise ValueError("weights must be [d_model, d_mem]")
+    arr = lambda seq: _ptr_array([x.data_ptr() for x in seq])
+    varr = None if value_out is None else _ptr_array([0 if x is None else x.data_ptr() for x in value_out])
+    _check(lib().engram_gate_forward_prepared(mem.data_ptr(), n_tok, d_mem, d_model, nb, arr(h), arr(wk_folded),
+                                              arr(wv), float(eps), arr(out),
+                                              _opt(gate_out, "gate_out", torch.float32), varr, _stream(stream)))
     return out
 
 

@@ -592,6 +592,42 @@ engram_status engram_gate_prepare_fp8(int32_t d_mem, int32_t d_model, int32_t n_
   return check_launch(fn);
 }
 
+engram_status engram_gate_prepare(int32_t d_mem, int32_t d_model, int32_t n_branch, const void* const* wk,
+                                  const void* const* gq, const void* const* gk, void* const* wk_folded,
+                                  hipStream_t stream) {
+  const char* fn = "engram_gate_prepare";
+  if (wk_folded == nullptr) return fail(ENGRAM_ERR_INVALID_ARG, "%s: null output array", fn);
+  GateArgs a;
+  // the shape and weight checks of the bf16 gate (h and out are not used: no tokens)
+  const engram_status st = gate_args(fn, nullptr, 0, d_mem, d_model, n_branch, wk, wk, wk, gq, gk, 0.f, ENGRAM_BF16,
+                                     ENGRAM_KEY_NORM_MEMORY, wk_folded, nullptr, nullptr, a);
+  if (st != ENGRAM_OK) return st;
+  for (int m = 0; m < n_branch; ++m)
+    if (wk_folded[m] == nullptr || !aligned(wk_folded[m], 16))
+      return fail(ENGRAM_ERR_INVALID_ARG, "%s: branch %d: null or misaligned output", fn, m);
+  launch_gate_fold(a, (uint16_t* const*)wk_folded, stream);
+  return check_launch(fn);
+}
+
+engram_status engram_gate_forward_prepared(const void* mem, int64_t n_tok, int32_t d_mem, int32_t d_model,
+                                           int32_t n_branch, const void* const* h, const void* const* wk_folded,
+                                           const void* const* wv, float eps, void* const* out, float* gate_out,
+                                           void* const* value_out, hipStream_t stream) {
+  const char* fn = "engram_gate_forward_prepared";
+  GateArgs a;
+  // the gains are folded into wk_folded: the gain arguments of the checks get the
+  // weights (valid, aligned and never read)
+  const engram_status st = gate_args(fn, mem, n_tok, d_mem, d_model, n_branch, h, wk_folded, wv, wk_folded,
+                                     wk_folded, eps, ENGRAM_BF16, ENGRAM_KEY_NORM_MEMORY, out, gate_out, value_out,
+                                     a);
+  if (st != ENGRAM_OK || n_tok == 0) return st;
+  const size_t bytes = gate_bf16_scratch_bytes(a, false, true);
+  return with_scratch(fn, bytes, stream, [&](void* p) {
+    a.part_dot = (float*)p;
+    launch_gate_bf16(a, false, stream, true);
+  });
+}
+
 engram_status engram_gate_forward_fp8q(const uint8_t* codes, const float* scales, const float* sumsq, int64_t n_tok,
                                        int32_t d_mem, int32_t d_model, int32_t n_branch, const void* const* h,
                                        const uint8_t* const* wk_codes, const float* const* wk_scales,

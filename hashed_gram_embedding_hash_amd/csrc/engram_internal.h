@@ -118,6 +118,10 @@ void launch_gate_bf16(const GateArgs& a, bool fp8, hipStream_t s, bool prequant 
 // per-feature scales (one launch of the quantizer per matrix).
 void launch_prepare_fp8(const GateArgs& a, uint8_t* const* wk_codes, float* const* wk_scales,
                         uint8_t* const* wv_codes, float* const* wv_scales, hipStream_t s);
+// The gain-folded key weights of the bf16 gate (memory-side key norm), per branch:
+// wk_folded[m][f][c] = bf16(gq[m][f] * wk[m][f][c] * gk[m][c]), as every bf16 call
+// without prepared weights computes them (uses a.wk, a.gq, a.gk, d_mem, d_model, n_branch).
+void launch_gate_fold(const GateArgs& a, uint16_t* const* wk_folded, hipStream_t s);
 void launch_gate_f32(const GateArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- FP8 (E4M3) encoding

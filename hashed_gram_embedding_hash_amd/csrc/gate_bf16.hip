@@ -1029,7 +1029,7 @@ struct ScratchLayout {
 
 ScratchLayout layout_for(const GateArgs& a, bool fp8, bool prequant) {
   ScratchLayout L;
-  L.wk_bytes = (a.key_norm == ENGRAM_KEY_NORM_PROJECTED || fp8) ? round256((size_t)a.n_branch * a.d_model * 4)
+  L.wk_bytes = (a.key_norm == ENGRAM_KEY_NORM_PROJECTED || fp8 || prequant) ? round256((size_t)a.n_branch * a.d_model * 4)
                                                                  : round256((size_t)a.n_branch * a.d_model * a.d_mem * 2);
   const size_t part_elems = (size_t)a.n_branch * a.n_ftiles * (size_t)a.n_tok;
   L.part_bytes = round256(part_elems * 4);
@@ -1073,8 +1073,10 @@ size_t gate_bf16_scratch_bytes(GateArgs& a, bool fp8, bool prequant) {
 
 // `a.part_dot` must point at the scratch block of gate_bf16_scratch_bytes(a) bytes;
 // the other scratch pointers are carved from it here.
-// prequant (fp8 only): a.mem, a.se, a.e_ssq, a.wk, a.wv, a.sk and a.sv already hold
-// the codes and scales; only the counters and the key gains are prepared here.
+// prequant, fp8: a.mem, a.se, a.e_ssq, a.wk, a.wv, a.sk and a.sv already hold the codes
+// and scales; only the counters and the key gains are prepared here.  prequant, bf16
+// with the memory-side key norm: a.wk already holds the gain-folded key weights
+// (launch_gate_fold); only the counters are cleared.
 void launch_gate_bf16(const GateArgs& a_in, bool fp8, hipStream_t s, bool prequant) {
   GateArgs a = a_in;
   const ScratchLayout L = layout_for(a, fp8, prequant);
@@ -1131,6 +1133,9 @@ void launch_gate_bf16(const GateArgs& a_in, bool fp8, hipStream_t s, bool prequa
                                                                          : L.n_counters;
     hipLaunchKernelGGL(gate_prep_projected_kernel, dim3((unsigned)((work + 255) / 256)), dim3(256), 0, s, a,
                        L.n_counters, true);
+  } else if (prequant) {
+    hipLaunchKernelGGL(gate_prep_projected_kernel, dim3((unsigned)((L.n_counters + 255) / 256)), dim3(256), 0, s,
+                       a, L.n_counters, false);
   } else {
     const int64_t n8 = (int64_t)a.d_model * a.d_mem / 8;
     const int64_t work = n8 * a.n_branch > L.n_counters ? n8 * a.n_branch : L.n_counters;
@@ -1164,6 +1169,19 @@ void launch_gate_bf16(const GateArgs& a_in, bool fp8, hipStream_t s, bool prequa
   ENGRAM_GATE_LAUNCH(true, true, false, true)
   ENGRAM_GATE_LAUNCH(true, true, true, true)
 #undef ENGRAM_GATE_LAUNCH
+}
+
+void launch_gate_fold(const GateArgs& a_in, uint16_t* const* wk_folded, hipStream_t s) {
+  const int64_t n8 = (int64_t)a_in.d_model * a_in.d_mem / 8;
+  for (int m = 0; m < a_in.n_branch; ++m) {
+    GateArgs a = a_in;  // branch m alone, written to its own output
+    a.n_branch = 1;
+    a.wk[0] = a_in.wk[m];
+    a.gq[0] = a_in.gq[m];
+    a.gk[0] = a_in.gk[m];
+    hipLaunchKernelGGL(gate_prep_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, a, wk_folded[m], n8,
+                       0);
+  }
 }
 
 void launch_prepare_fp8(const GateArgs& a, uint8_t* const* wk_codes, float* const* wk_scales,

@@ -230,6 +230,30 @@ engram_status engram_gate_forward(const void* mem, int64_t n_tok, int32_t d_mem,
                                   void* const* value_out, hipStream_t stream);
 
 /*
+ * The bf16 gate with the memory-side key norm, its weights prepared once -- section
+ * 2.3, Eq. (3)-(4), as engram_gate_forward computes them.  With this key placement
+ * q . k = sum_f h_f gq_f (W_K diag(gk) e)_f / (rms(h) rms(e)), so both RMSNorm gains fold
+ * into the key weights; engram_gate_forward folds them on every call, and these two
+ * calls let constant weights be folded once.
+ * engram_gate_prepare: wk_folded[m][f][c] = bf16(gq[m][f] * wk[m][f][c] * gk[m][c]),
+ *   computed in fp32 and rounded to nearest even.
+ *   wk, wk_folded: host arrays of n_branch device pointers to [d_model][d_mem] bf16
+ *   (wk_folded caller-allocated, 16-byte aligned).  gq[m]: [d_model]; gk[m]: [d_mem] bf16.
+ * engram_gate_forward_prepared: engram_gate_forward(dtype ENGRAM_BF16, key_norm
+ *   ENGRAM_KEY_NORM_MEMORY) with W_K replaced by wk_folded and no gains.  Its outputs are
+ *   bit-identical to that call's with the weights and gains that were folded.  The other
+ *   arguments are as for engram_gate_forward.
+ * Both require d_mem % 64 == 0 and d_model % 32 == 0 (ENGRAM_ERR_UNSUPPORTED otherwise).
+ */
+engram_status engram_gate_prepare(int32_t d_mem, int32_t d_model, int32_t n_branch, const void* const* wk,
+                                  const void* const* gq, const void* const* gk, void* const* wk_folded,
+                                  hipStream_t stream);
+engram_status engram_gate_forward_prepared(const void* mem, int64_t n_tok, int32_t d_mem, int32_t d_model,
+                                           int32_t n_branch, const void* const* h, const void* const* wk_folded,
+                                           const void* const* wv, float eps, void* const* out, float* gate_out,
+                                           void* const* value_out, hipStream_t stream);
+
+/*
  * Short depthwise causal convolution -- section 2.3, Eq. (5): with V~ the
  * gated values of one sequence (value_out of engram_gate_forward), the module's
  * output is Y = SiLU(Conv1D(RMSNorm(V~))) + V~.  engram_gate_forward already

@@ -252,3 +252,23 @@ def test_compress_hash_argument_errors():
     assert ch(tb=50, tc=60) == _st("arg")       # window past the row
     assert ch(batch=-1) == _st("arg")
     assert ch(tc=0) == _st("ok")
+
+
+def test_gate_prepared_argument_errors():
+    L = eg.lib()
+    one = (ctypes.c_void_p * 1)(4096)
+    pr = lambda **kw: L.engram_gate_prepare(kw.get("dm", 1280), kw.get("dmod", 2560), kw.get("nb", 1), one, one, one,
+                                            kw.get("out", one), None)
+    assert pr(dm=1000) == _st("unsup")              # d_mem not a multiple of 64
+    assert pr(dmod=2500) == _st("unsup")
+    assert pr(nb=0) == _st("arg")
+    assert pr(nb=9) == _st("arg")
+    assert pr(out=None) == _st("arg")
+    assert pr(out=(ctypes.c_void_p * 1)(4100)) == _st("arg")   # misaligned output
+    fp = lambda **kw: L.engram_gate_forward_prepared(
+        ctypes.c_void_p(kw.get("mem", 4096)), kw.get("n", 8), kw.get("dm", 1280), 2560, 1, one, one, one,
+        ctypes.c_float(kw.get("eps", 1e-6)), one, None, None, None)
+    assert fp(dm=1216 + 32) == _st("unsup")
+    assert fp(eps=-1.0) == _st("arg")
+    assert fp(mem=4100) == _st("arg")               # misaligned memory vectors
+    assert fp(n=0, mem=0) == _st("ok")

@@ -1151,3 +1151,43 @@ def test_empty_inputs_through_the_bindings():
     cw = torch.randn(d_model, 4).to(torch.bfloat16).to(DEV)
     assert eg.engram_conv_forward(val, 0, 7, cw, gq[0], 3, val.clone()).shape == (0, d_model)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("n_branch,shared", [(1, False), (3, True)])
+def test_gate_prepared_weights_bit_identical(n_branch, shared):
+    """engram_gate_prepare + engram_gate_forward_prepared against engram_gate_forward on
+    the same weights and gains: out, alpha and the gated values bit for bit (ragged token
+    count; three branches sharing one W_V, in place, with values)."""
+    say(f"gate prepared, {n_branch} branches, shared W_V {shared}")
+    cfg = synth.CONFIGS["small"].replace(n_branch=n_branch)
+    n_tok = 333
+    rng = np.random.default_rng(40 + n_branch)
+    idx = rng.integers(0, cfg.rows, (n_tok, cfg.n_tables)).astype(np.int32)
+    e_d = torch.from_numpy(oracle_memory(cfg, idx).view(np.int16)).to(DEV).view(torch.bfloat16)
+    tokens = torch.from_numpy(rng.choice(1 << 20, n_tok, replace=False).astype(np.int64))
+    hs = [synth.hidden_rows(cfg, m, tokens).to(DEV) for m in range(n_branch)]
+    ws = [synth.weights(cfg, m, DEV) for m in range(n_branch)]
+    wk = [w[0] for w in ws]
+    wv = [ws[0][1]] * n_branch if shared else [w[1] for w in ws]
+    gs = [synth.gains(cfg, m, DEV) for m in range(n_branch)]
+    gq, gk = [g[0] for g in gs], [g[1] for g in gs]
+    runs = []
+    for prepared in (False, True):
+        h_in = [h.clone() for h in hs]
+        alpha = torch.empty((n_branch, n_tok), dtype=torch.float32, device=DEV)
+        vals = [torch.empty_like(h) for h in hs] if shared else None
+        outs = h_in if shared else None
+        if prepared:
+            folded = eg.engram_gate_prepare(wk, gq, gk)
+            o = eg.engram_gate_forward_prepared(e_d, h_in, folded, wv, cfg.eps, out=outs, gate_out=alpha,
+                                                value_out=vals)
+        else:
+            o = eg.engram_gate_forward(e_d, h_in, wk, wv, gq, gk, cfg.eps, out=outs, gate_out=alpha, value_out=vals)
+        torch.cuda.synchronize()
+        runs.append((o, alpha, vals))
+    (o1, a1, v1), (o2, a2, v2) = runs
+    assert torch.equal(a1, a2)
+    for m in range(n_branch):
+        assert torch.equal(o1[m].view(torch.int16), o2[m].view(torch.int16)), m
+        if shared:
+            assert torch.equal(v1[m].view(torch.int16), v2[m].view(torch.int16)), m
