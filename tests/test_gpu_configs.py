@@ -219,3 +219,78 @@ def test_full_multi_config_fp8_pipeline_sampled(key_norm):
         say(f"  branch {m}: out rel err {err:.2e}, alpha abs err {aerr:.2e}")
         assert err <= 1e-2 and aerr <= 2e-3
     assert torch.all((alpha > 0) & (alpha < 1))
+
+
+def test_decode_two_stream_graph_replay_equals_eager():
+    """The offload decode pipeline as the benchmark times it: a side stream hashes step s+1
+    and prefetches its rows from pinned host tables into one of two staging buffers while
+    the main stream gates step s; events order the buffers.  Captured as one HIP graph over
+    both streams, every replay (with eager work on the same buffers in between) reproduces
+    the eager outputs bit for bit."""
+    cfg = synth.CONFIGS["offload"].replace(rows=100_003)
+    S, B = 4, cfg.batch
+    say(f"decode graph: {S} steps, {B} sequences, host tables {cfg.n_tables} x {cfg.rows}")
+    raw = synth.raw_ids(cfg)
+    host = []
+    for b in range(cfg.n_tables):
+        t = torch.empty((cfg.rows, cfg.w), dtype=torch.bfloat16, pin_memory=True)
+        t.copy_(synth.table_rows(cfg, b, torch.arange(cfg.rows, device=DEV)))
+        host.append(t)
+    rows = [cfg.rows] * cfg.n_tables
+    ids_d = eg.engram_compress(torch.from_numpy(raw).to(DEV), torch.from_numpy(synth.comp_map(cfg)).to(DEV))
+    mult, rows_u32 = synth.multipliers(cfg), synth.table_rows_u32(cfg)
+    wk, wv = synth.weights(cfg, 0, DEV)
+    gq, gk = synth.gains(cfg, 0, DEV)
+    tok = torch.arange(B, dtype=torch.int64) * (cfg.seq + cfg.decode_steps)
+    hs = [synth.hidden_rows(cfg, 0, tok + cfg.seq + s).to(DEV) for s in range(S)]
+    idx = [torch.empty((B, cfg.n_tables), dtype=torch.int32, device=DEV) for _ in range(2)]
+    stg = [torch.empty((B, cfg.n_tables * cfg.w), dtype=torch.bfloat16, device=DEV) for _ in range(2)]
+    outs = [torch.empty((B, cfg.d_model), dtype=torch.bfloat16, device=DEV) for _ in range(S)]
+    side = torch.cuda.Stream()
+
+    def fetch(s, buf):
+        eg.engram_hash(ids_d, cfg.orders, cfg.heads, mult, rows_u32, cfg.vocab_c, t_begin=cfg.seq + s, t_count=1,
+                       out=idx[buf], stream=side)
+        eg.engram_prefetch_host(idx[buf], host, rows, cfg.w, torch.bfloat16, staging=stg[buf], stream=side)
+
+    def enqueue(main):
+        ready = [torch.cuda.Event() for _ in range(2)]
+        free = [torch.cuda.Event() for _ in range(2)]
+        freed = [False, False]
+        side.wait_stream(main)
+        fetch(0, 0)
+        ready[0].record(side)
+        for s in range(S):
+            cur, nxt = s % 2, (s + 1) % 2
+            if s + 1 < S:
+                if freed[nxt]:
+                    side.wait_event(free[nxt])
+                fetch(s + 1, nxt)
+                ready[nxt].record(side)
+            main.wait_event(ready[cur])
+            eg.engram_gate_forward(stg[cur], [hs[s]], [wk], [wv], [gq], [gk], cfg.eps, out=[outs[s]], stream=main)
+            free[cur].record(main)
+            freed[cur] = True
+        main.wait_stream(side)
+
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cs):
+        enqueue(cs)
+    torch.cuda.synchronize()
+    want = [o.clone() for o in outs]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=cs):
+        enqueue(cs)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o in outs:
+            o.fill_(float(rep + 3))                     # eager work on the graph's buffers
+        for st in stg:
+            st.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for s in range(S):
+            assert torch.equal(outs[s].view(torch.int16), want[s].view(torch.int16)), (rep, s)
+    say("  3 replays bit-identical to the eager pipeline")
