@@ -52,7 +52,6 @@ def lib():
         L.oracle_gather.restype = None
         L.oracle_gate.argtypes = [P, i64, i32, i32, P, P, P, P, P, ctypes.c_double, i32, i32, P, P, P]
         L.oracle_gate.restype = ctypes.c_int
-        L.oracle_gate.restype = ctypes.c_int
         L.oracle_conv.argtypes = [P, i32, i64, i32, P, P, i32, i32, ctypes.c_double, i32, P, P]
         L.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
         L.oracle_e4m3_decode.restype = ctypes.c_double

@@ -328,7 +328,10 @@ int oracle_gate_fp8(const void* mem, int64_t n_tok, int32_t d_mem, int32_t d_mod
   float* sk = (float*)malloc(sizeof(float) * (size_t)d_model);
   float* sv = (float*)malloc(sizeof(float) * (size_t)d_model);
   double* k = (double*)malloc(sizeof(double) * (size_t)d_model);
-  if (!wf || !ef || !ck || !cv || !ce || !sk || !sv || !k) return -2;
+  if (!wf || !ef || !ck || !cv || !ce || !sk || !sv || !k) {
+    free(wf); free(ef); free(ck); free(cv); free(ce); free(sk); free(sv); free(k);
+    return -2;
+  }
   /* key weights */
   for (int32_t f = 0; f < d_model; ++f)
     for (int32_t c = 0; c < d_mem; ++c) {

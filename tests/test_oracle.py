@@ -244,19 +244,26 @@ def _golden_gate():
     return ex
 
 
-@pytest.mark.parametrize("name", ["A", "B", "C"])
+@pytest.mark.parametrize("name", ["A", "B", "C", "D", "E"])
 def test_gate_hand_examples(name):
+    """Hand-worked gate values (tests/golden/gate_micro.txt).  Examples marked fp8 have
+    operands that E4M3 represents exactly with the per-row scales, so the FP8 gate must
+    reproduce them too: D pins gq on the paper's key placement, E pins both gains with
+    the key normalised before W_K (a gain applied twice or left out of the key moves the
+    logit, see the fixture)."""
     g = _golden_gate()[name]
     dm, dmod = int(g["d_mem"][0]), int(g["d_model"][0])
     key_norm = int(g.get("key_norm", [0])[0])
     f = lambda k, shape: np.array(g[k], np.float32).reshape(shape)
-    out, alpha = oracle.gate(f("e", (1, dm)), f("h", (1, dmod)), f("wk", (dmod, dm)), f("wv", (dmod, dm)),
-                             f("gq", (dmod,)), f("gk", (dm,) if key_norm == 0 else (dmod,)), g["eps"][0],
-                             oracle.F32, key_norm=key_norm)
-    # the inputs are not all exactly representable in float32; 1e-6 covers that rounding
-    assert abs(alpha[0] - 1 / (1 + math.exp(-g["logit"][0]))) < 1e-6
-    assert abs(alpha[0] - g["alpha"][0]) < 1e-6
-    np.testing.assert_allclose(out[0], g["out"], rtol=0, atol=2e-6)
+    args = (f("e", (1, dm)), f("h", (1, dmod)), f("wk", (dmod, dm)), f("wv", (dmod, dm)),
+            f("gq", (dmod,)), f("gk", (dm,) if key_norm == 0 else (dmod,)), g["eps"][0], oracle.F32)
+    gates = [oracle.gate] + ([oracle.gate_fp8] if int(g.get("fp8", [0])[0]) else [])
+    for gate in gates:
+        out, alpha = gate(*args, key_norm=key_norm)
+        # the inputs are not all exactly representable in float32; 1e-6 covers that rounding
+        assert abs(alpha[0] - 1 / (1 + math.exp(-g["logit"][0]))) < 1e-6, gate
+        assert abs(alpha[0] - g["alpha"][0]) < 1e-6, gate
+        np.testing.assert_allclose(out[0], g["out"], rtol=0, atol=2e-6)
 
 
 def _rand_gate(rng, n, dm, dmod, dtype=np.float32):
@@ -406,6 +413,25 @@ def test_conv_delta_reaches_exactly_the_dilated_taps():
         expect[t0 + j * dil, :] = _silu_lib(np.float64(taps[j]))
     assert np.allclose(out, expect, rtol=1e-10, atol=1e-12)
     assert np.count_nonzero(out[s:]) == 0 and np.count_nonzero(out[:t0]) == 0
+
+
+def test_conv_delta_with_gamma_hand_values():
+    """tests/golden/conv_delta_gamma.txt: one constant token row, gains != 1 and a
+    different kernel per channel; the output is SiLU(w[c][j] * gamma_c) exactly j * dil
+    tokens later, which pins gamma after the normalisation (rms(gamma) != 1)."""
+    g = {r[0]: r[1:] for r in read_golden("conv_delta_gamma.txt")}
+    d, t0, dil, a = int(g["d_model"][0]), int(g["t0"][0]), int(g["dil"][0]), float(g["a"][0])
+    gamma = np.array(g["gamma"], np.float32)
+    w = np.array([g[f"w{c}"] for c in range(d)], np.float32)
+    y = np.array([g[f"y{c}"] for c in range(d)], np.float64)
+    s = t0 + 3 * dil + 4
+    v = np.zeros((s, d))
+    v[t0, :] = a
+    out = oracle.conv(v, 1, s, w, gamma, dil, 1e-12, oracle.F32, np.zeros_like(v))
+    expect = np.zeros_like(v)
+    for j in range(4):
+        expect[t0 + j * dil, :] = y[:, j]
+    np.testing.assert_allclose(out, expect, rtol=1e-10, atol=1e-12)
 
 
 def test_conv_is_causal_per_sequence_with_dilated_reach():
