@@ -2,14 +2,17 @@
 """Throughput of the Engram forward pass (compress -> hash -> gather -> gate) on one MI355X.
 
 One step = one pass of the whole path over one batch of seeded synthetic input
-already resident in HBM: the "small" workload (4 x 4096 Zipf(1.1) tokens, 16
-bf16 tables of 1,000,003 x 80, memory dim 1280, d_model 2560, one branch), as two
-calls: engram_lookup (compression, hashing and the gather in one kernel) and
+already resident in HBM.  The default workload is the largest that fits one GPU,
+"large": 8 x 32768 Zipf(1.05) tokens, 16 bf16 tables of 10,156,253 x 80 (26 GB),
+memory dim 1280, d_model 4096, two gating branches; the step is two calls:
+engram_lookup (compression, hashing and the gather in one kernel) and
 engram_gate_forward.  Prints ONE JSON line with tokens/s, the per-call breakdown,
 the roofline of the dominant kernel (the gate), the same step with the FP8 gate,
-the short convolution beside it and the CPU oracle's tokens/s on a bounded sample.
+the short convolution beside it, the "small" workload (4 x 4096 tokens, 1,000,003-row
+tables, d_model 2560, one branch) as a secondary line, and the CPU oracle's tokens/s
+on a bounded sample.
 
-    python bench.py [--steps K] [--warmup W] [--config small|multi|large|tiny]
+    python bench.py [--steps K] [--warmup W] [--config large|small|multi|tiny]
     python bench.py --calibrate-copy MIB     # plain device copy, for HBM counter scaling
     python bench.py --config offload         # decode steps: host-resident vs HBM-resident tables
 
@@ -38,7 +41,11 @@ PEAK_BF16_TFLOPS = 2500.0      # dense bf16 MFMA
 PEAK_FP32_TFLOPS = 157.3       # fp32 vector / matrix
 PEAK_FP8_TFLOPS = 5000.0       # dense fp8 MFMA
 GATE_SOURCE = os.path.join(ROOT, "hashed_gram_embedding_hash_amd", "csrc", "gate_bf16.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_persistent_kernel_small_hbm_traffic.txt")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def traffic_file(workload: str) -> str:
+    return os.path.join(PROFILES, f"gate_persistent_kernel_{workload}_hbm_traffic.txt")
 
 
 def parse():
@@ -47,7 +54,11 @@ def parse():
     p.add_argument("--steps", type=int, default=30)
     # the GPU's clocks settle over the first ~10-20 steps of this workload
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", default="small")
+    # the largest single-GPU workload (262,144 tokens, 26 GB of tables, two branches); the
+    # small one is measured after it as a secondary line (--no-secondary skips it)
+    p.add_argument("--config", default="large")
+    p.add_argument("--no-secondary", action="store_true",
+                   help="with the large workload: skip the secondary measurement of the small one")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle time of the CPU baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--shared-wv", action="store_true",
@@ -128,10 +139,11 @@ def measured_traffic(cfg):
     summary (FETCH_SIZE + WRITE_SIZE scaled by a plain copy of known size).  None when
     the summary is missing, covers another workload, or the kernel source has changed
     since the counters were taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+    path = traffic_file(cfg.name)
+    if not os.path.exists(path):
         return None
     kv = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith(" "):
                 k, v = line.split(":", 1)
@@ -542,37 +554,48 @@ def cpu_baseline(cfg, target_s, fp8=False):
             gate(e, h[m], wts[m][0], wts[m][1], gns[m][0], gns[m][1], cfg.eps, dt)
         return t_int + time.perf_counter() - t1
 
-    probe = 8
-    t = run(probe)
-    n = int(max(probe, min(cfg.seq, probe * target_s / max(t, 1e-9))))
-    t = run(n)
+    # one thread, pinned to one core of those this process may use, for the timed runs
+    allowed = sorted(os.sched_getaffinity(0))
+    core = allowed[0]
+    os.sched_setaffinity(0, {core})
+    try:
+        probe = 8
+        t = run(probe)
+        n = int(max(probe, min(cfg.seq, probe * target_s / max(t, 1e-9))))
+        t = run(n)
+    finally:
+        os.sched_setaffinity(0, set(allowed))
     return {"value": n / t, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "pinned_core": core, "host_cores": os.cpu_count(), "cores_available": len(allowed),
+            "cpu_model": cpu_model(),
             "sample": f"first {n} tokens of sequence 0 of the {cfg.name} workload: compress, hash, "
-                      f"gather and all {cfg.n_branch} {'fp8 ' if fp8 else ''}gate branch(es), one thread, "
-                      f"{t:.1f} s"}
+                      f"gather and all {cfg.n_branch} {'fp8 ' if fp8 else ''}gate branch(es), one thread pinned "
+                      f"to core {core}, {t:.1f} s"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(json.dumps({"error": f"--gpus {args.gpus}: this benchmark runs on exactly one GPU; "
-                                   "the Engram path here is single-GPU (no multi-GPU runs)"}))
-        sys.exit(2)
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
-    if args.calibrate_copy:
-        calibrate_copy(args.calibrate_copy)
-        return
 
-    if args.config == "offload":
-        run_offload(args)
-        return
-
+def run_workload(args, name, secondary=False):
+    """One workload's measurement: the step (engram_lookup + engram_gate_forward) timed
+    eagerly and as a graph replay, with the per-call breakdown and the gate's roofline;
+    unless secondary, also the separate calls, the prepared-weight gate, the FP8 steps and
+    the convolution.  Returns the result dict (without the CPU baseline)."""
     import torch
     import synth
     import hashed_gram_embedding_hash_amd as eg
     from hashed_gram_embedding_hash_amd.pipeline import EngramLayer
 
-    cfg = synth.CONFIGS[args.config]
+    cfg = synth.CONFIGS[name]
     dev = torch.device("cuda:0")
     print(f"[bench] building inputs for {cfg.name}", file=sys.stderr, flush=True)
     inp = synth.device_inputs(cfg, dev)
@@ -659,6 +682,18 @@ def main():
         return ms_step, ms_eager, per, t_wall
 
     ms_step, ms_eager, per, t_wall = time_steps(make_step(args.fp8), args.steps, args.warmup, not args.no_graph)
+    if secondary:
+        work = algorithmic(cfg, args.shared_wv)
+        gate_tf = work["gate"]["flops"] / (per["gate"] * 1e-3) / 1e12
+        lk = work["lookup"]["bytes"] / (per["lookup"] * 1e-3) / 1e9
+        return {"workload": cfg.name, "tokens": cfg.tokens, "value": round(cfg.tokens / (ms_step * 1e-3), 1),
+                "unit": "tokens/s", "ms_per_step": round(ms_step, 5), "ms_per_step_eager": round(ms_eager, 5),
+                "steps": args.steps, "warmup": args.warmup,
+                "kernels": {"lookup": {"ms": round(per["lookup"], 5), "GB/s": round(lk, 1),
+                                       "hbm_frac": round(lk / PEAK_HBM_GBS, 4)},
+                            "gate": {"ms": round(per["gate"], 5), "TFLOP/s": round(gate_tf, 2),
+                                     "frac": round(gate_tf / PEAK_BF16_TFLOPS, 4)}},
+                "config": workload_desc(cfg, args)}
 
     # the lookup as its separate calls (engram_compress_hash, then engram_gather), for each
     # call's own rate
@@ -796,9 +831,37 @@ def main():
     if not args.no_conv:
         print("[bench] short convolution", file=sys.stderr, flush=True)
         result["conv"] = measure_conv(args, cfg, bufs, h, layer, outs, flush)
+    return result
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": f"--gpus {args.gpus}: this benchmark runs on exactly one GPU; "
+                                   "the Engram path here is single-GPU (no multi-GPU runs)"}))
+        sys.exit(2)
+
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
+
+    if args.config == "offload":
+        run_offload(args)
+        return
+
+    result = run_workload(args, args.config)
+    if args.config == "large" and not args.no_secondary:
+        import torch
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        print("[bench] secondary workload: small", file=sys.stderr, flush=True)
+        result["secondary"] = {"small": run_workload(args, "small", secondary=True),
+                               "note": "the small workload (4 x 4096 tokens, d_model 2560, one branch), step "
+                                       "timed by the same procedure after the main line"}
     if not args.no_cpu_baseline:
+        import synth
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds, fp8=args.fp8)
+        result["cpu_baseline"] = cpu_baseline(synth.CONFIGS[args.config], args.cpu_seconds, fp8=args.fp8)
     print(json.dumps(result), flush=True)
 
 

@@ -56,7 +56,7 @@ EXPORTS = (
     "engram_host_free", "engram_cache_select", "engram_cache_build", "engram_prefetch_host_cached",
     "engram_compress_hash", "engram_quantize_fp8", "engram_gate_forward_fp8", "engram_lookup",
     "engram_lookup_fp8", "engram_gate_prepare_fp8", "engram_gate_forward_fp8q", "engram_gate_prepare",
-    "engram_gate_forward_prepared",
+    "engram_gate_forward_prepared", "engram_gate_wait_timeouts", "engram_debug_force_gate_timeout",
 )
 
 
@@ -109,11 +109,15 @@ def lib() -> ctypes.CDLL:
         L.engram_cache_select.argtypes = [P, i64, i32, i32, P]
         L.engram_cache_build.argtypes = [P, P, i32, i32, i32, P, i32, i32, P, P, P]
         L.engram_prefetch_host_cached.argtypes = [P, i64, i32, P, P, i32, i32, P, i32, P, P, P, P, P]
+        L.engram_gate_wait_timeouts.argtypes = [ctypes.POINTER(i32), i32]
+        L.engram_debug_force_gate_timeout.argtypes = [i32]
         for f in ("engram_compress", "engram_hash", "engram_gather", "engram_gate_forward",
                   "engram_conv_forward", "engram_prefetch_host", "engram_host_alloc", "engram_host_free",
                   "engram_cache_select", "engram_cache_build", "engram_prefetch_host_cached",
                   "engram_compress_hash", "engram_quantize_fp8", "engram_gate_forward_fp8", "engram_lookup",
-                  "engram_lookup_fp8", "engram_gate_prepare_fp8", "engram_gate_forward_fp8q"):
+                  "engram_lookup_fp8", "engram_gate_prepare_fp8", "engram_gate_forward_fp8q",
+                  "engram_gate_prepare", "engram_gate_forward_prepared", "engram_gate_wait_timeouts",
+                  "engram_debug_force_gate_timeout"):
             getattr(L, f).restype = st
         _lib = L
     return _lib
@@ -631,6 +635,20 @@ def engram_quantize_fp8(x, with_sumsq: bool = False, stream=None):
                                      _dev(scales, "scales", torch.float32), _opt(sumsq, "sumsq", torch.float32),
                                      _stream(stream)))
     return (codes, scales, sumsq) if with_sumsq else (codes, scales)
+
+
+def engram_gate_wait_timeouts(reset: bool = False) -> int:
+    """Value-tile wavefronts of gate calls on the current device whose bounded wait for
+    their gates ran out (they wrote NaN) since load or the last reset; synchronizes the
+    device.  0 in normal operation."""
+    n = ctypes.c_int32(0)
+    _check(lib().engram_gate_wait_timeouts(ctypes.byref(n), 1 if reset else 0))
+    return int(n.value)
+
+
+def engram_debug_force_gate_timeout(on: bool):
+    """Test hook: make every later gate launch's value-tile wait give up (see engram.h)."""
+    _check(lib().engram_debug_force_gate_timeout(1 if on else 0))
 
 
 def host_alloc(nbytes: int) -> int:

@@ -142,6 +142,7 @@ engram_status with_scratch(const char* fn, size_t bytes, hipStream_t stream, Lau
     e = hipMallocAsync(&g.ptr, grow, stream);
     if (e != hipSuccess) {
       g.ptr = nullptr;
+      (void)hipGetLastError();  // the failed allocation must not be reported by a later call's launch check
       return hip_fail(e, "hipMallocAsync(scratch)");
     }
     g.bytes = grow;
@@ -466,6 +467,17 @@ engram_status gate_args(const char* fn, const void* mem, int64_t n_tok, int32_t 
     return fail(ENGRAM_ERR_UNSUPPORTED, "%s: bf16 needs d_mem %% 64 == 0 and d_model %% 32 == 0 (got %d, %d)",
                 fn, d_mem, d_model);
   if (n_tok > 0x7fffffffLL) return fail(ENGRAM_ERR_UNSUPPORTED, "%s: n_tok >= 2^31", fn);
+  if (dtype == ENGRAM_BF16) {
+    // the persistent kernel forms weight offsets (row * d_mem + column, in elements or
+    // FP8 bytes) in 32 bits and numbers its tiles in int
+    if ((int64_t)d_model * (int64_t)d_mem >= (1ll << 32))
+      return fail(ENGRAM_ERR_UNSUPPORTED, "%s: d_model * d_mem = %lld >= 2^32", fn,
+                  (long long)d_model * (long long)d_mem);
+    const int64_t tiles = ((n_tok + 255) / 256) * (int64_t)n_branch * (((int64_t)d_model + 255) / 256);
+    if (tiles > (1ll << 29))
+      return fail(ENGRAM_ERR_UNSUPPORTED, "%s: %lld tiles of 256 x 256 exceed 2^29 per launch", fn,
+                  (long long)tiles);
+  }
   const size_t al = dtype == ENGRAM_BF16 ? 16 : 4;
   if (n_tok > 0 && (mem == nullptr || !aligned(mem, al)))
     return fail(ENGRAM_ERR_INVALID_ARG, "%s: null or misaligned mem", fn);
@@ -530,6 +542,18 @@ engram_status engram_gate_forward(const void* mem, int64_t n_tok, int32_t d_mem,
     a.part_dot = (float*)p;
     launch_gate_bf16(a, false, stream);
   });
+}
+
+engram_status engram_gate_wait_timeouts(int32_t* count, int32_t reset) {
+  if (count == nullptr) return fail(ENGRAM_ERR_INVALID_ARG, "engram_gate_wait_timeouts: null count");
+  const hipError_t e = gate_wait_timeouts(count, reset != 0);
+  if (e != hipSuccess) return hip_fail(e, "engram_gate_wait_timeouts");
+  return ENGRAM_OK;
+}
+
+engram_status engram_debug_force_gate_timeout(int32_t on) {
+  set_gate_forced_wait_timeout(on != 0);
+  return ENGRAM_OK;
 }
 
 engram_status engram_gate_forward_fp8(const void* mem, int64_t n_tok, int32_t d_mem, int32_t d_model,
@@ -737,6 +761,7 @@ engram_status engram_host_alloc(size_t bytes, void** ptr) {
   const hipError_t e = hipHostMalloc(ptr, bytes, hipHostMallocMapped | hipHostMallocPortable);
   if (e != hipSuccess) {
     *ptr = nullptr;
+    (void)hipGetLastError();  // not to be reported again by a later call's launch check
     return hip_fail(e, "engram_host_alloc: hipHostMalloc");
   }
   return ENGRAM_OK;

@@ -61,7 +61,9 @@ __global__ __launch_bounds__(1024) void prefetch_cached_kernel(const GatherArgs 
     const uint32_t mask = (1u << log2_slots) - 1u;
     uint32_t s = home_slot((int32_t)r, log2_slots);
     int2 e = tb[s];
-    while (e.x != (int32_t)r && e.x != -1) {  // the table always has empty entries
+    // a table built with these slots always has empty entries; the bound keeps a table
+    // of fewer slots than the caller claims from looping forever (it reads as a miss)
+    for (uint32_t probes = 1; e.x != (int32_t)r && e.x != -1 && probes <= mask; ++probes) {
       s = (s + 1u) & mask;
       e = tb[s];
     }

@@ -107,6 +107,10 @@ struct GateArgs {
   const float* e_ssq;
   const float* sk[ENGRAM_MAX_BRANCHES];
   const float* sv[ENGRAM_MAX_BRANCHES];
+  // the V tiles' bounded wait: the done count it needs is n_ftiles + 1 + wait_extra
+  // (wait_extra is 0 except under the forced-timeout test hook), polled at most
+  // spin_limit times (set by launch_gate_bf16)
+  int32_t wait_extra, spin_limit;
 };
 // bf16 path: returns the scratch bytes it needs for these shapes (and sets a.n_ftiles).
 // launch_gate_bf16 expects a.part_dot to point at a scratch block of that size.  With
@@ -123,6 +127,11 @@ void launch_prepare_fp8(const GateArgs& a, uint8_t* const* wk_codes, float* cons
 // without prepared weights computes them (uses a.wk, a.gq, a.gk, d_mem, d_model, n_branch).
 void launch_gate_fold(const GateArgs& a, uint16_t* const* wk_folded, hipStream_t s);
 void launch_gate_f32(const GateArgs& a, hipStream_t s);
+// Reads (and with reset zeroes) the current device's count of V-tile wavefronts whose
+// wait for the gates ran out; synchronizes the device first.
+hipError_t gate_wait_timeouts(int32_t* count, bool reset);
+// Test hook behind engram_debug_force_gate_timeout.
+void set_gate_forced_wait_timeout(bool on);
 
 // ---------------------------------------------------------------- FP8 (E4M3) encoding
 // Shared by the quantization kernels and the quantizing lookup (their codes must agree).

@@ -69,9 +69,16 @@
 // the gated-value output, the paper's projected key norm, one W_V shared by all
 // branches, and FP8 operands (E4M3 codes, 32x32x64 MFMA, 128 k-values per ring row).
 // Each is its own instantiation so that the plain gate keeps its register allocation.
+#include <atomic>
+
 #include "engram_internal.h"
 
 namespace engram {
+
+// Wavefronts of V tiles whose bounded wait for their gates ran out (they wrote NaN),
+// per device, since the library was loaded or the count was last reset.
+__device__ int32_t g_gate_wait_timeouts;
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -96,6 +103,7 @@ static_assert(4 * SLOT_BYTES == BT * BF * 2, "the h tile is four slots");
 static_assert(G_INSTR == 8 && BF == 256 && BT == 256, "load and wait counts below assume these");
 constexpr int NQ = 8;                       // work queues (one per XCD)
 constexpr int SPIN_LIMIT = 1 << 18;         // polls (each one L2 round trip plus s_sleep 1: 0.1-0.5 s) before a V tile gives up
+constexpr int FORCED_SPIN_LIMIT = 64;       // polls of a wait made unsatisfiable on purpose (test hook)
 
 enum { PHASE_K = 0, PHASE_V = 1 };
 
@@ -163,11 +171,17 @@ __device__ __forceinline__ float sumsq8(const u32x4& v) {
 
 // Partials cross workgroups (K tiles write, V tiles of the same token tile read).
 // They travel as device-coherent relaxed atomic stores/loads, which are performed
-// at the device coherence point without flushing or invalidating whole caches; the
-// done counter is incremented only after the writers' stores completed (workgroup
-// barrier), and a reader issues its loads only after it saw the full count.
-// Full acquire/release at device scope would write back and invalidate the XCD's
-// L2 on every tile, evicting the operand tiles the other CUs are streaming.
+// at the device coherence point without flushing or invalidating whole caches.
+// Publishing is ordered by hand: every wave waits for its own stores with
+// s_waitcnt vmcnt(0) (on gfx9 a store leaves the vmcnt count only once the memory
+// side has acknowledged it, and an agent-scope store is acknowledged at the device
+// coherence point), then the workgroup barrier, and only then one thread
+// increments the done counter.  __syncthreads() alone is not enough: on gfx950 its
+// workgroup-scope fence waits for LDS operations but not for global stores.  A
+// reader issues its loads only after the load of the count that showed them
+// complete has returned (its branch depends on the value).  Full acquire/release at
+// device scope would write back and invalidate the XCD's L2 on every tile,
+// evicting the operand tiles the other CUs are streaming.
 __device__ __forceinline__ void st_coherent(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -248,7 +262,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
     if (lane == 0) {
       for (int mb = SHAREDV ? 0 : m; mb < (SHAREDV ? a.n_branch : m + 1); ++mb)
         seen &= __hip_atomic_load(a.counters + NQ + mb * a.n_ttiles + tile.ttile, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT) >= a.n_ftiles + 1;
+                                  __HIP_MEMORY_SCOPE_AGENT) >= a.n_ftiles + 1 + a.wait_extra;
     }
     gates_ready = __builtin_amdgcn_readfirstlane(seen) != 0;
     // issued only after lane 0's count came back (the branch depends on it)
@@ -646,20 +660,32 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
   float (*s_kk)[BT] = reinterpret_cast<float (*)[BT]>(scratch + 6 * BT * sizeof(float));  // KEYP
   float* s_g = reinterpret_cast<float*>(scratch + 8 * BT * sizeof(float));               // KEYP, [BF]
   float* s_fs = reinterpret_cast<float*>(scratch + 8 * BT * sizeof(float) + BF * sizeof(float));  // F8, [BF]
+  bool gave_up = false;  // wave-uniform: this wave's bounded wait for the gates ran out
   if (PHASE == PHASE_V) {
     if (!gates_ready) {
       // the wait deferred from the tile's start: lane 0 polls the done count(s), bounded
-      // by SPIN_LIMIT, and the wave's gate loads follow once it has seen them
+      // by a.spin_limit polls, and the wave's gate loads follow once it has seen them.
+      // A wave that gives up counts itself in g_gate_wait_timeouts and takes NaN for
+      // its gates, so its outputs are NaN rather than silently wrong.
+      int out_of_polls = 0;
       if (elane == 0) {
         int spin = 0;
-        for (int mb = SHAREDV ? 0 : m; mb < (SHAREDV ? a.n_branch : m + 1); ++mb) {
+        for (int mb = SHAREDV ? 0 : m; mb < (SHAREDV ? a.n_branch : m + 1) && !out_of_polls; ++mb) {
           const int32_t* dn = a.counters + NQ + mb * a.n_ttiles + tile.ttile;
-          while (__hip_atomic_load(dn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.n_ftiles + 1 &&
-                 ++spin < SPIN_LIMIT)
+          while (__hip_atomic_load(dn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.n_ftiles + 1 + a.wait_extra) {
+            if (++spin >= a.spin_limit) {
+              out_of_polls = 1;
+              break;
+            }
             __builtin_amdgcn_s_sleep(1);
+          }
         }
+        if (out_of_polls)
+          __hip_atomic_fetch_add(&g_gate_wait_timeouts, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      if (t0 + etid < n_tok) alpha = ld_coherent(a.alpha + (int64_t)m * n_tok + t0 + etid);
+      gave_up = __builtin_amdgcn_readfirstlane(out_of_polls) != 0;
+      if (gave_up) alpha = __builtin_nanf("");
+      else if (t0 + etid < n_tok) alpha = ld_coherent(a.alpha + (int64_t)m * n_tok + t0 + etid);
     }
     if constexpr (F8) s_alpha[etid] = alpha * ts;  // the token scale rides on the gate
     else s_alpha[etid] = alpha;
@@ -777,8 +803,9 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
       st_coherent(a.part_hh + o, s_red[0][1][etid] + s_red[1][1][etid]);
       if (KEYP) st_coherent(a.ee + o, s_kk[0][etid] + s_kk[1][etid]);
     }
-    // publish: __syncthreads() waits until every wave's partial stores have completed,
-    // then the count goes up
+    // publish: every wave waits for its own partial stores, then the barrier, then the
+    // count goes up
+    wait_vm_lgkm0<0>();
     __syncthreads();
     if (etid == 0) *s_flag = __hip_atomic_fetch_add(done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     lds_barrier();
@@ -823,7 +850,8 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
         st_coherent(a.alpha + (int64_t)m * n_tok + t, g);
         if (a.gate_out != nullptr) a.gate_out[(int64_t)m * n_tok + t] = g;
       }
-      __syncthreads();  // the gate stores have completed
+      wait_vm_lgkm0<0>();  // this wave's gate stores have completed
+      __syncthreads();     // ... and every other wave's
       if (etid == 0) __hip_atomic_fetch_add(done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   } else {
@@ -933,7 +961,8 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
               dma16(hb + (uint32_t)tr * (uint32_t)d_model + f, dst + (uint32_t)(blk * 1024));
             }
           }
-          float al = t0 + etid < n_tok ? ld_coherent(a.alpha + (int64_t)mb * n_tok + t0 + etid) : 0.f;
+          float al = gave_up ? __builtin_nanf("")
+                             : t0 + etid < n_tok ? ld_coherent(a.alpha + (int64_t)mb * n_tok + t0 + etid) : 0.f;
           if constexpr (F8) al = t0 + etid < n_tok ? al * a.se[t0 + etid] : 0.f;
           wait_vm_lgkm0<0>();
           s_alpha[etid] = al;
@@ -1051,6 +1080,10 @@ ScratchLayout layout_for(const GateArgs& a, bool fp8, bool prequant) {
   return L;
 }
 
+// Test hook: every later gate launch waits for a done count its K tiles never reach,
+// bounded by FORCED_SPIN_LIMIT polls, so the give-up path runs (and the kernel ends).
+std::atomic<bool> g_force_wait_timeout{false};
+
 int cu_count() {
   static int n[64] = {0};
   int dev = 0;
@@ -1144,6 +1177,9 @@ void launch_gate_bf16(const GateArgs& a_in, bool fp8, hipStream_t s, bool prequa
     for (int m = 0; m < a.n_branch; ++m) a.wk[m] = wk_scaled + (size_t)m * a.d_model * a.d_mem;
   }
 
+  const bool forced = g_force_wait_timeout.load(std::memory_order_relaxed);
+  a.wait_extra = forced ? 1 : 0;
+  a.spin_limit = forced ? FORCED_SPIN_LIMIT : SPIN_LIMIT;
   int grid = cu_count() / NQ * NQ;
   if (grid < NQ) grid = NQ;
   bool values = false;
@@ -1170,6 +1206,17 @@ void launch_gate_bf16(const GateArgs& a_in, bool fp8, hipStream_t s, bool prequa
   ENGRAM_GATE_LAUNCH(true, true, true, true)
 #undef ENGRAM_GATE_LAUNCH
 }
+
+hipError_t gate_wait_timeouts(int32_t* count, bool reset) {
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return e;
+  e = hipMemcpyFromSymbol(count, HIP_SYMBOL(g_gate_wait_timeouts), sizeof(int32_t), 0, hipMemcpyDeviceToHost);
+  if (e != hipSuccess || !reset) return e;
+  const int32_t zero = 0;
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_gate_wait_timeouts), &zero, sizeof(int32_t), 0, hipMemcpyHostToDevice);
+}
+
+void set_gate_forced_wait_timeout(bool on) { g_force_wait_timeout.store(on, std::memory_order_relaxed); }
 
 void launch_gate_fold(const GateArgs& a_in, uint16_t* const* wk_folded, hipStream_t s) {
   const int64_t n8 = (int64_t)a_in.d_model * a_in.d_mem / 8;

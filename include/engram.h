@@ -219,8 +219,14 @@ engram_status engram_lookup_fp8(const int32_t* raw, int32_t batch, int64_t ld, i
  * elsewhere; with ENGRAM_KEY_NORM_MEMORY the bf16 path folds both gains into a
  * copy of W_K rounded once to bf16.  ENGRAM_F32 computes everything in fp32 (its
  * ENGRAM_KEY_NORM_PROJECTED form needs d_mem + d_model <= 16384).
- * Shapes: ENGRAM_BF16 needs d_mem % 64 == 0 and d_model % 32 == 0; ENGRAM_F32
- * accepts any positive sizes.  n_tok == 0 is a no-op.
+ * Shapes: ENGRAM_BF16 needs d_mem % 64 == 0 and d_model % 32 == 0, d_model * d_mem
+ * < 2^32 and n_tok < 2^31, and at most 2^29 tiles of 256 tokens x 256 features over
+ * all branches; ENGRAM_F32 accepts any positive sizes with n_tok < 2^31.  Larger
+ * requests return ENGRAM_ERR_UNSUPPORTED.  n_tok == 0 is a no-op.
+ * Cross-workgroup wait: in the bf16 and FP8 paths the value tiles of a token tile
+ * wait, bounded, for its gates (published by the key tiles of the same launch, which
+ * always run first).  A wavefront whose wait runs out writes NaN for its tokens'
+ * outputs and is counted; engram_gate_wait_timeouts reads that count.
  */
 engram_status engram_gate_forward(const void* mem, int64_t n_tok, int32_t d_mem, int32_t d_model,
                                   int32_t n_branch, const void* const* h, const void* const* wk,
@@ -228,6 +234,25 @@ engram_status engram_gate_forward(const void* mem, int64_t n_tok, int32_t d_mem,
                                   const void* const* gk, float eps, engram_dtype dtype,
                                   engram_key_norm key_norm, void* const* out, float* gate_out,
                                   void* const* value_out, hipStream_t stream);
+
+/*
+ * Health of the gate's cross-workgroup wait (see engram_gate_forward): *count receives
+ * the number of value-tile wavefronts on the current device whose bounded wait for
+ * their gates ran out since the library was loaded or the count was last reset; their
+ * outputs were written as NaN.  0 in normal operation.  reset != 0 zeroes the count
+ * after reading it.  Synchronizes the current device (hipDeviceSynchronize) first.
+ * Errors: INVALID_ARG for a null count; HIP if a runtime call fails.
+ */
+engram_status engram_gate_wait_timeouts(int32_t* count, int32_t reset);
+
+/*
+ * Test hook for the path above, for tests that must see it run: with on != 0, every
+ * later bf16 or FP8 gate launch (any device, until called again with 0) waits for a
+ * done count its key tiles never reach, giving up after 64 polls, so every value-tile
+ * wavefront writes NaN and is counted; every kernel still completes.  Never set it
+ * outside such a test.  Always returns ENGRAM_OK.
+ */
+engram_status engram_debug_force_gate_timeout(int32_t on);
 
 /*
  * The bf16 gate with the memory-side key norm, its weights prepared once -- section
@@ -324,7 +349,9 @@ engram_status engram_prefetch_host(const int32_t* idx, int64_t n_tok, int32_t n_
  *   table) whose row is in the cache is read from cache_rows, any other from the
  *   host table over PCIe.  staging receives exactly engram_gather's result.
  *   hits: device int32 counter incremented once per cached (token, table), or NULL;
- *   err_count as for engram_gather.
+ *   err_count as for engram_gather.  slots must be the value the table was built
+ *   with: the kernel reads table[b][0 .. slots-1].  A probe stops after slots entries
+ *   (a smaller table than claimed then reads as misses, never loops).
  */
 engram_status engram_cache_select(const int32_t* idx, int64_t n, int32_t n_tables, int32_t capacity,
                                   int32_t* hot);

@@ -114,6 +114,20 @@ def test_gate_argument_errors():
     assert gf(kn=2) == _st("arg")                                 # unknown key placement
     assert b"key_norm" in L.engram_last_error()
     assert gf(n=0) == _st("ok")
+    # shapes whose 32-bit weight offsets or int tile numbers would wrap are refused on the
+    # host (the pointers are never dereferenced)
+    assert gf(dm=65536, dmod=65536) == _st("unsup")               # d_model * d_mem = 2^32
+    assert b"2^32" in L.engram_last_error()
+    assert gf(dm=1 << 16, dmod=1 << 17) == _st("unsup")           # 2^33 weight elements
+    assert gf(n=(1 << 31) - 1, dm=64, dmod=1 << 16, nb=8) == _st("unsup")   # 2^33 tiles
+    assert b"tiles" in L.engram_last_error()
+    assert gf(dm=65536 - 64, dmod=65504, n=0) == _st("ok")         # just below 2^32: accepted (no tokens)
+
+
+def test_gate_wait_timeout_query_argument_errors():
+    L = eg.lib()
+    assert L.engram_gate_wait_timeouts(None, 0) == _st("arg")
+    assert L.engram_debug_force_gate_timeout(0) == _st("ok")
 
 
 def test_lookup_argument_errors():

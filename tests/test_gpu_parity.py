@@ -1,13 +1,13 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle on seeded inputs.
 
 Bar: bit-exact for compressed ids, hash indices and gathered/staged memory
-vectors; max relative error (gpu_helpers.rel_err: |g - r| / max(|r|, rms(r)))
-<= 1e-5 for fp32 outputs and <= 1e-2 for bf16 outputs.  Because tables of
-std 0.02 make alpha * v small next to h, the bf16 cases also check alpha
-(absolute error <= 2e-3: the key's bf16 operands carry a relative rounding of
-up to 2^-8, bf16's unit roundoff, when the gains differ from 1) and, in the
-stress cases whose tables have std >= 0.5, the update out - h itself (rel_err
-<= 5e-2: bf16 rounding of out, up to 2^-8 |out|, over |alpha v| of about 0.5).
+vectors; max relative error (gpu_helpers.rel_err: |g - r| / max(|r|, 1e-2 rms(r)))
+<= 1e-5 for fp32 outputs and <= 1e-2 for bf16 outputs.  Gate outputs are judged
+by gpu_helpers.check_gate: against the oracle on the operands the kernel
+multiplies (the bf16 memory-side key folds gq W_K gk into one bf16 copy) with
+alpha within 1e-4, and alpha against the unrounded definition within 2e-3.
+Because tables of std 0.02 make alpha * v small next to h, stress cases with
+tables of std >= 0.5 also bound the update out - h.
 """
 import math
 
@@ -18,13 +18,11 @@ import torch
 import hashed_gram_embedding_hash_amd as eg
 import oracle
 import synth
-from gpu_helpers import (host_view, oracle_gate_tokens, oracle_ids_idx, oracle_memory, rel_err,
-                         sample_tokens)
+from gpu_helpers import (check_gate, check_gate_tokens, gate_inputs_tokens, host_view,
+                         oracle_ids_idx, oracle_memory, rel_err, sample_tokens, sentinel_like)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
-ALPHA_TOL_BF16 = 2e-3
-UPDATE_TOL_STRESS = 5e-2
 
 
 def say(*a):
@@ -272,14 +270,13 @@ def test_gate_fp32_tiny_full_pipeline():
     ids_d = eg.engram_compress(inp["raw"], inp["map"])
     idx_d = eg.engram_hash(ids_d, cfg.orders, cfg.heads, inp["mult"], inp["rows"], cfg.vocab_c)
     e_d = eg.engram_gather(idx_d, inp["tables"])
-    alpha = torch.empty((1, cfg.tokens), dtype=torch.float32, device=DEV)
+    alpha = sentinel_like(torch.empty((1, cfg.tokens), dtype=torch.float32, device=DEV))
     out = eg.engram_gate_forward(e_d, inp["h"], inp["wk"], inp["wv"], inp["gq"], inp["gk"], cfg.eps,
-                                 gate_out=alpha)[0]
+                                 out=[sentinel_like(torch.empty_like(inp["h"][0]))], gate_out=alpha)[0]
     e_o = oracle_memory(cfg, idx_o)
     assert np.array_equal(host_view(e_d), e_o)
-    out_o, alpha_o = oracle_gate_tokens(cfg, 0, e_o, np.arange(cfg.tokens))
-    assert rel_err(out.cpu().numpy(), out_o) <= 1e-5
-    assert np.abs(alpha.cpu().numpy()[0] - alpha_o).max() <= 1e-5
+    check_gate_tokens("fp32 tiny", cfg, 0, out.cpu().numpy(), alpha.cpu().numpy()[0], e_o, np.arange(cfg.tokens),
+                      say=say)
 
 
 def _gate_case(cfg, n_tok, seed, table_std=None, gamma_jitter=None, n_branch=None, inplace=False,
@@ -296,21 +293,15 @@ def _gate_case(cfg, n_tok, seed, table_std=None, gamma_jitter=None, n_branch=Non
     ws = [synth.weights(cfg, m, DEV) for m in range(cfg.n_branch)]
     proj = key_norm == eg.KEY_NORM_PROJECTED
     gs = [synth.gains(cfg, m, DEV, projected_key=proj) for m in range(cfg.n_branch)]
-    alpha = torch.empty((cfg.n_branch, n_tok), dtype=torch.float32, device=DEV)
+    alpha = sentinel_like(torch.empty((cfg.n_branch, n_tok), dtype=torch.float32, device=DEV))
     h_in = [h.clone() for h in hs]
+    outs = h_in if inplace else [sentinel_like(torch.empty_like(h)) for h in hs]
     out = eg.engram_gate_forward(e_d, h_in, [w[0] for w in ws], [w[1] for w in ws], [g[0] for g in gs],
-                                 [g[1] for g in gs], cfg.eps, out=h_in if inplace else None, gate_out=alpha,
-                                 key_norm=key_norm)
+                                 [g[1] for g in gs], cfg.eps, out=outs, gate_out=alpha, key_norm=key_norm)
     torch.cuda.synchronize()
     for m in range(cfg.n_branch):
-        out_o, alpha_o = oracle_gate_tokens(cfg, m, e_o, tokens, key_norm=key_norm)
-        err = rel_err(out[m].float().cpu().numpy(), out_o)
-        aerr = np.abs(alpha[m].cpu().numpy() - alpha_o).max()
-        upd_err = rel_err((out[m].float() - hs[m].float()).cpu().numpy(), out_o - host_bf16_to_f64(hs[m]))
-        say(f"  branch {m}: out rel err {err:.2e}, alpha abs err {aerr:.2e}, update rel err {upd_err:.2e}")
-        assert err <= 1e-2 and aerr <= ALPHA_TOL_BF16
-        if cfg.table_std >= 0.5:
-            assert upd_err <= UPDATE_TOL_STRESS
+        check_gate_tokens(f"branch {m}", cfg, m, out[m].float().cpu().numpy(), alpha[m].cpu().numpy(), e_o, tokens,
+                          key_norm=key_norm, update=cfg.table_std >= 0.5, say=say)
     return out, alpha
 
 
@@ -363,13 +354,13 @@ def test_gate_fp32_projected_key_tiny():
     h = synth.hidden_rows(cfg, 0, torch.from_numpy(tokens)).to(DEV)
     wk, wv = synth.weights(cfg, 0, DEV)
     gq, gk = synth.gains(cfg, 0, DEV, projected_key=True)
-    alpha = torch.empty((1, cfg.tokens), dtype=torch.float32, device=DEV)
+    alpha = sentinel_like(torch.empty((1, cfg.tokens), dtype=torch.float32, device=DEV))
     out = eg.engram_gate_forward(torch.from_numpy(e_o).to(DEV), [h], [wk], [wv], [gq], [gk], cfg.eps,
-                                 gate_out=alpha, key_norm=eg.KEY_NORM_PROJECTED)[0]
-    out_o, alpha_o = oracle_gate_tokens(cfg, 0, e_o, tokens, key_norm=oracle.KEY_NORM_PROJECTED)
-    err, aerr = rel_err(out.cpu().numpy(), out_o), np.abs(alpha.cpu().numpy()[0] - alpha_o).max()
-    say(f"  out rel err {err:.2e}, alpha abs err {aerr:.2e}")
-    assert err <= 1e-5 and aerr <= 1e-5
+                                 out=[sentinel_like(torch.empty_like(h))], gate_out=alpha,
+                                 key_norm=eg.KEY_NORM_PROJECTED)[0]
+    hh, wk_h, wv_h, gq_h, gk_h = gate_inputs_tokens(cfg, 0, tokens, key_norm=oracle.KEY_NORM_PROJECTED)
+    check_gate("fp32 projected tiny", out.cpu().numpy(), alpha.cpu().numpy()[0], e_o, hh, wk_h, wv_h, gq_h, gk_h,
+               cfg.eps, key_norm=oracle.KEY_NORM_PROJECTED, dtype=oracle.F32, say=say)
 
 
 def _shared_wv_inputs(cfg, n_tok, seed, key_norm):
@@ -386,13 +377,13 @@ def _shared_wv_inputs(cfg, n_tok, seed, key_norm):
     return e_o, e_d, tokens, hs, wks, wv0, gs
 
 
-def _oracle_shared_wv(cfg, m, e_o, tokens, wv0, key_norm):
+def _check_shared_wv(label, cfg, m, out, alpha, e_o, tokens, wv0, key_norm, vals=None, update=False):
     h = host_view(synth.hidden_rows(cfg, m, torch.from_numpy(tokens)))
     wk = host_view(synth.weights(cfg, m)[0])
     proj = key_norm == eg.KEY_NORM_PROJECTED
     gq, gk = (host_view(x) for x in synth.gains(cfg, m, projected_key=proj))
-    return oracle.gate(e_o, h, wk, host_view(wv0.cpu()), gq, gk, cfg.eps, oracle.BF16, with_value=True,
-                       key_norm=key_norm)
+    return check_gate(label, out, alpha, e_o, h, wk, host_view(wv0.cpu()), gq, gk, cfg.eps, key_norm=key_norm,
+                      vals=vals, update=update, say=say)
 
 
 @pytest.mark.parametrize("key_norm", [eg.KEY_NORM_MEMORY, eg.KEY_NORM_PROJECTED])
@@ -408,10 +399,11 @@ def test_gate_bf16_shared_wv_equals_copies_and_oracle(key_norm):
     M = cfg.n_branch
     runs = {}
     for name, wvs in (("shared", [wv0] * M), ("copies", [wv0.clone() for _ in range(M)])):
-        alpha = torch.empty((M, n_tok), dtype=torch.float32, device=DEV)
-        vals = [torch.empty_like(h) for h in hs]
+        alpha = sentinel_like(torch.empty((M, n_tok), dtype=torch.float32, device=DEV))
+        vals = [sentinel_like(torch.empty_like(h)) for h in hs]
+        outs = [sentinel_like(torch.empty_like(h)) for h in hs]
         out = eg.engram_gate_forward(e_d, hs, wks, wvs, [g[0] for g in gs], [g[1] for g in gs], cfg.eps,
-                                     gate_out=alpha, value_out=vals, key_norm=key_norm)
+                                     out=outs, gate_out=alpha, value_out=vals, key_norm=key_norm)
         torch.cuda.synchronize()
         runs[name] = (out, alpha, vals)
     for m in range(M):
@@ -420,12 +412,8 @@ def test_gate_bf16_shared_wv_equals_copies_and_oracle(key_norm):
     assert torch.equal(runs["shared"][1], runs["copies"][1])
     out, alpha, vals = runs["shared"]
     for m in range(M):
-        out_o, alpha_o, val_o = _oracle_shared_wv(cfg, m, e_o, tokens, wv0, key_norm)
-        err = rel_err(out[m].float().cpu().numpy(), out_o)
-        verr = rel_err(vals[m].float().cpu().numpy(), val_o)
-        aerr = np.abs(alpha[m].cpu().numpy() - alpha_o).max()
-        say(f"  branch {m}: out rel err {err:.2e}, value rel err {verr:.2e}, alpha abs err {aerr:.2e}")
-        assert err <= 1e-2 and verr <= 1e-2 and aerr <= ALPHA_TOL_BF16
+        _check_shared_wv(f"branch {m}", cfg, m, out[m].float().cpu().numpy(), alpha[m].cpu().numpy(), e_o, tokens,
+                         wv0, key_norm, vals=vals[m].float().cpu().numpy(), update=True)
 
 
 def test_gate_bf16_shared_wv_in_place_large_shape():
@@ -439,12 +427,18 @@ def test_gate_bf16_shared_wv_in_place_large_shape():
     eg.engram_gate_forward(e_d, h_in, wks, [wv0] * cfg.n_branch, [g[0] for g in gs], [g[1] for g in gs],
                            cfg.eps, out=h_in)
     torch.cuda.synchronize()
+    alpha = sentinel_like(torch.empty((cfg.n_branch, n_tok), dtype=torch.float32, device=DEV))
+    h_in2 = [h.clone() for h in hs]
+    eg.engram_gate_forward(e_d, h_in2, wks, [wv0] * cfg.n_branch, [g[0] for g in gs], [g[1] for g in gs],
+                           cfg.eps, out=h_in2, gate_out=alpha)
+    torch.cuda.synchronize()
+    for m in range(cfg.n_branch):   # the same call again, with the gates written: identical outputs
+        assert torch.equal(h_in[m].view(torch.int16), h_in2[m].view(torch.int16))
     sample = np.random.default_rng(20).choice(n_tok, 96, replace=False)
+    sel = torch.from_numpy(sample).to(DEV)
     for m in range(cfg.n_branch):
-        out_o, _, _ = _oracle_shared_wv(cfg, m, e_o[sample], tokens[sample], wv0, eg.KEY_NORM_MEMORY)
-        err = rel_err(h_in[m][torch.from_numpy(sample).to(DEV)].float().cpu().numpy(), out_o)
-        say(f"  branch {m}: out rel err {err:.2e}")
-        assert err <= 1e-2
+        _check_shared_wv(f"branch {m}", cfg, m, h_in[m][sel].float().cpu().numpy(), alpha[m][sel].cpu().numpy(),
+                         e_o[sample], tokens[sample], wv0, eg.KEY_NORM_MEMORY, update=True)
 
 
 @pytest.mark.parametrize("d_mem,d_model,key_norm,shared", [
@@ -470,20 +464,18 @@ def test_gate_bf16_ragged_feature_tile_and_odd_k(d_mem, d_model, key_norm, share
     nk = d_mem if key_norm == eg.KEY_NORM_MEMORY else d_model
     gqs = [(1 + 0.2 * torch.randn(d_model, generator=g)).to(torch.bfloat16) for _ in range(M)]
     gks = [(1 + 0.2 * torch.randn(nk, generator=g)).to(torch.bfloat16) for _ in range(M)]
-    alpha = torch.empty((M, n_tok), dtype=torch.float32, device=DEV)
+    alpha = sentinel_like(torch.empty((M, n_tok), dtype=torch.float32, device=DEV))
     dv = lambda xs: [x.to(DEV) for x in xs]
     wv_d = dv([wv])[0]
     out = eg.engram_gate_forward(e.to(DEV), dv(hs), dv(wks), [wv_d] * M if shared else dv(wvs), dv(gqs), dv(gks),
-                                 1e-6, gate_out=alpha, key_norm=key_norm)
+                                 1e-6, out=[sentinel_like(torch.empty(n_tok, d_model, dtype=torch.bfloat16,
+                                                                      device=DEV)) for _ in range(M)],
+                                 gate_out=alpha, key_norm=key_norm)
     torch.cuda.synchronize()
     for m in range(M):
-        out_o, alpha_o = oracle.gate(host_view(e), host_view(hs[m]), host_view(wks[m]), host_view(wvs[0 if shared else m]),
-                                     host_view(gqs[m]), host_view(gks[m]), 1e-6, oracle.BF16, key_norm=key_norm)
-        err = rel_err(out[m].float().cpu().numpy(), out_o)
-        aerr = np.abs(alpha[m].cpu().numpy() - alpha_o).max()
-        upd = rel_err((out[m].float() - hs[m].float().to(DEV)).cpu().numpy(), out_o - host_bf16_to_f64(hs[m]))
-        say(f"  branch {m}: out rel err {err:.2e}, alpha abs err {aerr:.2e}, update rel err {upd:.2e}")
-        assert err <= 1e-2 and aerr <= ALPHA_TOL_BF16 and upd <= UPDATE_TOL_STRESS
+        check_gate(f"branch {m}", out[m].float().cpu().numpy(), alpha[m].cpu().numpy(), host_view(e),
+                   host_view(hs[m]), host_view(wks[m]), host_view(wvs[0 if shared else m]), host_view(gqs[m]),
+                   host_view(gks[m]), 1e-6, key_norm=key_norm, update=True, say=say)
 
 
 def test_gate_bf16_scratch_shared_across_streams_and_sizes():
@@ -768,15 +760,77 @@ def test_prefetch_host_cached_equals_gather(dtype, w, capacity, slots):
     e2 = torch.zeros(1, dtype=torch.int32, device=DEV)
     hits = torch.zeros(1, dtype=torch.int32, device=DEV)
     want = eg.engram_gather(idx_d, dev_t, err_count=e1)
-    got = eg.engram_prefetch_host_cached(idx_d, pinned, [rows] * nt, w, dtype, table, cache_rows, hits=hits,
-                                         err_count=e2)
+    staging = sentinel_like(torch.empty((idx.shape[0], nt * w), dtype=dtype, device=DEV))
+    got = eg.engram_prefetch_host_cached(idx_d, pinned, [rows] * nt, w, dtype, table, cache_rows, staging=staging,
+                                         hits=hits, err_count=e2)
     torch.cuda.synchronize()
     view = torch.int16 if dtype == torch.bfloat16 else torch.int32
     assert torch.equal(got.view(view), want.view(view))
     assert int(e1.item()) == int(e2.item()) == 3
+    # against the oracle's gather (Eq. 2) of the same host tables; the oracle's gather is
+    # defined for in-range rows, so the three out-of-range pairs are gathered as row 0
+    # and then set to the zero row the library documents for them
+    ok = (idx >= 0) & (idx < rows)
+    tabs_h = [host_view(t) for t in tables]
+    e_o = oracle.gather(np.where(ok, idx, 0).astype(np.int32), tabs_h)
+    for t_, b_ in zip(*np.nonzero(~ok)):
+        e_o[t_, b_ * w:(b_ + 1) * w] = 0
+    assert np.array_equal(host_view(got), e_o)
     expect_hits = sum(int(np.isin(idx[:, b], hot[b][hot[b] >= 0]).sum()) for b in range(nt))
     say(f"  hits {int(hits.item())} of {idx.size} ({int(hits.item()) / idx.size:.1%})")
     assert int(hits.item()) == expect_hits > 0
+
+
+def test_gate_wait_timeout_is_reported_and_writes_nan():
+    """The value tiles' bounded wait for their gates, forced from the host to run out (the
+    test hook makes the done count it waits for unreachable and bounds it at 64 polls):
+    every value-tile wavefront writes NaN for its tokens and is counted, the gates themselves
+    are still published, and every kernel completes.  bf16 and FP8, one and three branches
+    (shared W_V); then, with the hook off, the same calls are correct and count nothing."""
+    say("gate forced wait timeout")
+    d_mem, d_model, n_tok = 640, 1024, 300
+    g = torch.Generator().manual_seed(123)
+    e = torch.randn(n_tok, d_mem, generator=g).to(torch.bfloat16).to(DEV)
+    hs = [torch.randn(n_tok, d_model, generator=g).to(torch.bfloat16).to(DEV) for _ in range(3)]
+    wk = (torch.randn(d_model, d_mem, generator=g) / d_mem ** 0.5).to(torch.bfloat16).to(DEV)
+    wv = (torch.randn(d_model, d_mem, generator=g) / d_mem ** 0.5).to(torch.bfloat16).to(DEV)
+    gq = torch.ones(d_model, dtype=torch.bfloat16, device=DEV)
+    gk = torch.ones(d_mem, dtype=torch.bfloat16, device=DEV)
+    n_tt, n_ft = (n_tok + 255) // 256, (d_model + 255) // 256
+    eg.engram_gate_wait_timeouts(reset=True)
+    cases = [(1, False), (1, True), (3, False), (3, True)]          # (branches, fp8); 3 share W_V
+    try:
+        eg.engram_debug_force_gate_timeout(True)
+        for nb, fp8 in cases:
+            alpha = sentinel_like(torch.empty((nb, n_tok), dtype=torch.float32, device=DEV))
+            outs = eg.engram_gate_forward(e, hs[:nb], [wk] * nb, [wv] * nb, [gq] * nb, [gk] * nb, 1e-6,
+                                          gate_out=alpha, fp8=fp8)
+            n = eg.engram_gate_wait_timeouts(reset=True)
+            say(f"  {nb} branch(es), fp8 {fp8}: {n} wavefronts gave up")
+            # one V tile per (token tile, feature tile), per branch unless W_V is shared; 4 waves each
+            assert n == n_tt * n_ft * 4
+            for o in outs:
+                assert torch.isnan(o.float()).all()
+            assert torch.isfinite(alpha).all() and bool(((alpha > 0) & (alpha < 1)).all())
+    finally:
+        eg.engram_debug_force_gate_timeout(False)
+    for nb, fp8 in cases:
+        outs = eg.engram_gate_forward(e, hs[:nb], [wk] * nb, [wv] * nb, [gq] * nb, [gk] * nb, 1e-6, fp8=fp8)
+        assert eg.engram_gate_wait_timeouts() == 0
+        for o in outs:
+            assert torch.isfinite(o.float()).all()
+
+
+def test_hip_failure_maps_to_err_hip_and_clears():
+    """A HIP runtime failure forced from the host (pinned memory of 2^60 bytes cannot be
+    allocated) returns ENGRAM_ERR_HIP with a message, and the next call is unaffected."""
+    say("forced HIP error")
+    with pytest.raises(eg.EngramError) as ex:
+        eg.host_alloc(1 << 60)
+    assert ex.value.status == 3 and "hipHostMalloc" in str(ex.value)
+    cmap = torch.arange(10, dtype=torch.int32, device=DEV)
+    raw = torch.arange(10, dtype=torch.int32, device=DEV).flip(0).contiguous()
+    assert torch.equal(eg.engram_compress(raw, cmap), raw)
 
 
 # ---------------------------------------------------------------------------
@@ -847,27 +901,17 @@ def _gate_fp8_case(n_tok, d_mem, d_model, key_norm, n_branch=1, shared=False, in
     dv = lambda xs: [x.to(DEV) for x in xs]
     wv_d = dv(wvs)
     h_d = dv(hs)
-    alpha = torch.empty((n_branch, n_tok), dtype=torch.float32, device=DEV)
-    vout = [torch.empty_like(h) for h in h_d] if values else None
+    alpha = sentinel_like(torch.empty((n_branch, n_tok), dtype=torch.float32, device=DEV))
+    vout = [sentinel_like(torch.empty_like(h)) for h in h_d] if values else None
+    outs = h_d if inplace else [sentinel_like(torch.empty_like(h)) for h in h_d]
     out = eg.engram_gate_forward(e.to(DEV), h_d, dv(wks), [wv_d[0]] * n_branch if shared else wv_d, dv(gqs),
-                                 dv(gks), 1e-6, out=h_d if inplace else None, gate_out=alpha, value_out=vout,
-                                 key_norm=key_norm, fp8=True)
+                                 dv(gks), 1e-6, out=outs, gate_out=alpha, value_out=vout, key_norm=key_norm, fp8=True)
     torch.cuda.synchronize()
     for m in range(n_branch):
-        out_o, alpha_o = oracle.gate_fp8(host_view(e), host_view(hs[m]), host_view(wks[m]),
-                                         host_view(wvs[0 if shared else m]), host_view(gqs[m]), host_view(gks[m]),
-                                         1e-6, oracle.BF16, key_norm=key_norm)
-        err = rel_err(out[m].float().cpu().numpy(), out_o)
-        aerr = np.abs(alpha[m].cpu().numpy() - alpha_o).max()
-        upd_o = out_o - host_bf16_to_f64(hs[m])
-        upd = rel_err(out[m].float().cpu().numpy() - host_bf16_to_f64(hs[m]), upd_o)
-        msg = f"  branch {m}: out rel err {err:.2e}, alpha abs err {aerr:.2e}, update rel err {upd:.2e}"
-        if values:
-            verr = rel_err(vout[m].float().cpu().numpy(), upd_o)
-            msg += f", value rel err {verr:.2e}"
-            assert verr <= 1e-2
-        say(msg)
-        assert err <= 1e-2 and aerr <= ALPHA_TOL_BF16 and upd <= UPDATE_TOL_STRESS
+        check_gate(f"branch {m}", out[m].float().cpu().numpy(), alpha[m].cpu().numpy(), host_view(e),
+                   host_view(hs[m]), host_view(wks[m]), host_view(wvs[0 if shared else m]), host_view(gqs[m]),
+                   host_view(gks[m]), 1e-6, key_norm=key_norm, fp8=True,
+                   vals=vout[m].float().cpu().numpy() if values else None, update=True, say=say)
 
 
 @pytest.mark.parametrize("key_norm", [eg.KEY_NORM_MEMORY, eg.KEY_NORM_PROJECTED])
@@ -1035,21 +1079,16 @@ def test_lookup_fp8_then_gate_fp8q_against_oracle():
     codes, scales, ss = eg.engram_lookup_fp8(inp["raw"], inp["map"], cfg.orders, cfg.heads, inp["mult"],
                                              inp["tables"], cfg.vocab_c)
     prep = eg.engram_gate_prepare_fp8(inp["wk"], inp["wv"], inp["gq"], inp["gk"])
-    alpha = torch.empty((1, cfg.tokens), dtype=torch.float32, device=DEV)
+    alpha = sentinel_like(torch.empty((1, cfg.tokens), dtype=torch.float32, device=DEV))
     out = eg.engram_gate_forward_fp8q(codes, scales, ss, inp["h"], prep, inp["gq"], inp["gk"], cfg.eps,
-                                      gate_out=alpha)[0]
+                                      out=[sentinel_like(torch.empty_like(inp["h"][0]))], gate_out=alpha)[0]
     torch.cuda.synchronize()
     sample = sample_tokens(cfg, 300, seed=5)
     e_o = oracle_memory(cfg, idx_o[sample])
-    h = host_view(synth.hidden_rows(cfg, 0, torch.from_numpy(sample.astype(np.int64))))
-    wk, wv = (host_view(x) for x in synth.weights(cfg, 0))
-    gq, gk = (host_view(x) for x in synth.gains(cfg, 0))
-    out_o, alpha_o = oracle.gate_fp8(e_o, h, wk, wv, gq, gk, cfg.eps, oracle.BF16)
+    h, wk, wv, gq, gk = gate_inputs_tokens(cfg, 0, sample)
     sel = torch.from_numpy(sample).to(DEV)
-    err = rel_err(out[sel].float().cpu().numpy(), out_o)
-    aerr = np.abs(alpha[0][sel].cpu().numpy() - alpha_o).max()
-    say(f"  out rel err {err:.2e}, alpha abs err {aerr:.2e}")
-    assert err <= 1e-2 and aerr <= ALPHA_TOL_BF16
+    check_gate("fp8 pipeline", out[sel].float().cpu().numpy(), alpha[0][sel].cpu().numpy(), e_o, h, wk, wv, gq, gk,
+               cfg.eps, fp8=True, say=say)
 
 
 @pytest.mark.parametrize("n_tok", [1, 2, 255, 256, 257])
@@ -1067,18 +1106,13 @@ def test_gate_token_counts_at_tile_edges(n_tok, fp8):
     wv = (torch.randn(d_model, d_mem, generator=g) / d_mem ** 0.5).to(torch.bfloat16)
     gq = (1 + 0.2 * torch.randn(d_model, generator=g)).to(torch.bfloat16)
     gk = (1 + 0.2 * torch.randn(d_mem, generator=g)).to(torch.bfloat16)
-    alpha = torch.empty((1, n_tok), dtype=torch.float32, device=DEV)
+    alpha = sentinel_like(torch.empty((1, n_tok), dtype=torch.float32, device=DEV))
     out = eg.engram_gate_forward(e.to(DEV), [h.to(DEV)], [wk.to(DEV)], [wv.to(DEV)], [gq.to(DEV)], [gk.to(DEV)],
-                                 1e-6, gate_out=alpha, fp8=fp8)[0]
+                                 1e-6, out=[sentinel_like(torch.empty(n_tok, d_model, dtype=torch.bfloat16, device=DEV))],
+                                 gate_out=alpha, fp8=fp8)[0]
     torch.cuda.synchronize()
-    ref = oracle.gate_fp8 if fp8 else oracle.gate
-    out_o, alpha_o = ref(host_view(e), host_view(h), host_view(wk), host_view(wv), host_view(gq), host_view(gk),
-                         1e-6, oracle.BF16)
-    err = rel_err(out.float().cpu().numpy(), out_o)
-    aerr = np.abs(alpha[0].cpu().numpy() - alpha_o).max()
-    upd = rel_err(out.float().cpu().numpy() - host_bf16_to_f64(h), out_o - host_bf16_to_f64(h))
-    say(f"  out rel err {err:.2e}, alpha abs err {aerr:.2e}, update rel err {upd:.2e}")
-    assert err <= 1e-2 and aerr <= ALPHA_TOL_BF16 and upd <= UPDATE_TOL_STRESS
+    check_gate(f"{n_tok} tokens", out.float().cpu().numpy(), alpha[0].cpu().numpy(), host_view(e), host_view(h),
+               host_view(wk), host_view(wv), host_view(gq), host_view(gk), 1e-6, fp8=fp8, update=True, say=say)
 
 
 # ---------------------------------------------------------------------------
