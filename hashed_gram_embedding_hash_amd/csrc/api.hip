@@ -39,19 +39,21 @@ namespace {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-size_t dtype_size(engram_dtype dt) { return dt == ENGRAM_F32 ? 4 : 2; }
+size_t dtype_size(int dt) { return dt == ENGRAM_F32 ? 4 : 2; }
 
-bool valid_dtype(engram_dtype dt) { return dt == ENGRAM_F32 || dt == ENGRAM_BF16; }
+bool valid_dtype(int dt) { return dt == ENGRAM_F32 || dt == ENGRAM_BF16; }
+
+bool valid_key_norm(int kn) { return kn == ENGRAM_KEY_NORM_MEMORY || kn == ENGRAM_KEY_NORM_PROJECTED; }
 
 // Shared validation of engram_gather / engram_prefetch_host.
 engram_status check_gather(const char* fn, const int32_t* idx, int64_t n_tok, int32_t n_tables,
                            const void* const* tables, const int64_t* rows, int32_t w,
-                           engram_dtype dtype, void* out) {
+                           int dtype, void* out) {
   if (n_tok < 0) return fail(ENGRAM_ERR_INVALID_ARG, "%s: n_tok < 0", fn);
   if (n_tables <= 0 || n_tables > ENGRAM_MAX_TABLES)
     return fail(ENGRAM_ERR_INVALID_ARG, "%s: n_tables %d not in [1, %d]", fn, n_tables,
                 ENGRAM_MAX_TABLES);
-  if (!valid_dtype(dtype)) return fail(ENGRAM_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dtype);
+  if (!valid_dtype(dtype)) return fail(ENGRAM_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, dtype);
   if (w <= 0) return fail(ENGRAM_ERR_INVALID_ARG, "%s: w must be positive", fn);
   if (tables == nullptr || rows == nullptr)
     return fail(ENGRAM_ERR_INVALID_ARG, "%s: null tables or rows array", fn);
@@ -286,7 +288,7 @@ engram_status engram_compress_hash(const int32_t* raw, int32_t batch, int64_t ld
 engram_status engram_gather(const int32_t* idx, int64_t n_tok, int32_t n_tables,
                             const void* const* tables, const int64_t* rows, int32_t w,
                             engram_dtype dtype, void* out, int32_t* err_count, hipStream_t stream) {
-  const engram_status st = check_gather("engram_gather", idx, n_tok, n_tables, tables, rows, w, dtype, out);
+  const engram_status st = check_gather("engram_gather", idx, n_tok, n_tables, tables, rows, w, enum_arg(dtype), out);
   if (st != ENGRAM_OK) return st;
   if (n_tok == 0) return ENGRAM_OK;
   GatherArgs a;
@@ -322,7 +324,7 @@ engram_status engram_lookup(const int32_t* raw, int32_t batch, int64_t ld, int64
   const int64_t n_tok = empty ? 0 : (int64_t)batch * t_count;
   // the gather's checks (idx is not read: a stand-in keeps the null check quiet)
   static const int32_t no_idx = 0;
-  st = check_gather(fn, &no_idx, n_tok, nt, tables, rows64, w, dtype, out);
+  st = check_gather(fn, &no_idx, n_tok, nt, tables, rows64, w, enum_arg(dtype), out);
   if (st != ENGRAM_OK || empty) return st;
   if (idx_out != nullptr && !aligned(idx_out, 4)) return fail(ENGRAM_ERR_INVALID_ARG, "%s: misaligned idx_out", fn);
   if ((uint64_t)((t_count + 7) / 8) * (uint64_t)batch >= (1ull << 31))  // at least 8 positions per workgroup
@@ -384,7 +386,7 @@ engram_status engram_prefetch_host(const int32_t* idx, int64_t n_tok, int32_t n_
                                    engram_dtype dtype, void* staging, int32_t* err_count,
                                    hipStream_t stream) {
   const char* fn = "engram_prefetch_host";
-  const engram_status st = check_gather(fn, idx, n_tok, n_tables, host_tables, rows, w, dtype, staging);
+  const engram_status st = check_gather(fn, idx, n_tok, n_tables, host_tables, rows, w, enum_arg(dtype), staging);
   if (st != ENGRAM_OK) return st;
   GatherArgs a;
   memset(&a, 0, sizeof a);
@@ -412,7 +414,7 @@ engram_status engram_prefetch_host_cached(const int32_t* idx, int64_t n_tok, int
                                           const void* cache_rows, void* staging, int32_t* hits,
                                           int32_t* err_count, hipStream_t stream) {
   const char* fn = "engram_prefetch_host_cached";
-  const engram_status st = check_gather(fn, idx, n_tok, n_tables, host_tables, rows, w, dtype, staging);
+  const engram_status st = check_gather(fn, idx, n_tok, n_tables, host_tables, rows, w, enum_arg(dtype), staging);
   if (st != ENGRAM_OK) return st;
   int l2 = 0;
   while (l2 < 31 && (1 << l2) < slots) ++l2;
@@ -448,8 +450,8 @@ namespace {
 // leaves `a` unfilled: nothing to launch).
 engram_status gate_args(const char* fn, const void* mem, int64_t n_tok, int32_t d_mem, int32_t d_model,
                         int32_t n_branch, const void* const* h, const void* const* wk, const void* const* wv,
-                        const void* const* gq, const void* const* gk, float eps, engram_dtype dtype,
-                        engram_key_norm key_norm, void* const* out, float* gate_out, void* const* value_out,
+                        const void* const* gq, const void* const* gk, float eps, int dtype,
+                        int key_norm, void* const* out, float* gate_out, void* const* value_out,
                         GateArgs& a) {
   if (n_tok < 0 || d_mem <= 0 || d_model <= 0)
     return fail(ENGRAM_ERR_INVALID_ARG, "%s: bad sizes n_tok=%lld d_mem=%d d_model=%d", fn,
@@ -459,8 +461,8 @@ engram_status gate_args(const char* fn, const void* mem, int64_t n_tok, int32_t 
                 ENGRAM_MAX_BRANCHES);
   if (!valid_dtype(dtype)) return fail(ENGRAM_ERR_INVALID_ARG, "%s: unknown dtype", fn);
   if (!(eps >= 0.f)) return fail(ENGRAM_ERR_INVALID_ARG, "%s: eps must be >= 0", fn);
-  if (key_norm != ENGRAM_KEY_NORM_MEMORY && key_norm != ENGRAM_KEY_NORM_PROJECTED)
-    return fail(ENGRAM_ERR_INVALID_ARG, "%s: unknown key_norm %d", fn, (int)key_norm);
+  if (!valid_key_norm(key_norm))
+    return fail(ENGRAM_ERR_INVALID_ARG, "%s: unknown key_norm %d", fn, key_norm);
   if (h == nullptr || wk == nullptr || wv == nullptr || gq == nullptr || gk == nullptr || out == nullptr)
     return fail(ENGRAM_ERR_INVALID_ARG, "%s: null pointer array", fn);
   if (dtype == ENGRAM_BF16 && (d_mem % 64 != 0 || d_model % 32 != 0))
@@ -524,12 +526,13 @@ engram_status engram_gate_forward(const void* mem, int64_t n_tok, int32_t d_mem,
                                   void* const* value_out, hipStream_t stream) {
   const char* fn = "engram_gate_forward";
   GateArgs a;
-  const engram_status st = gate_args(fn, mem, n_tok, d_mem, d_model, n_branch, h, wk, wv, gq, gk, eps, dtype,
-                                     key_norm, out, gate_out, value_out, a);
+  const int dt = enum_arg(dtype), kn = enum_arg(key_norm);
+  const engram_status st = gate_args(fn, mem, n_tok, d_mem, d_model, n_branch, h, wk, wv, gq, gk, eps, dt, kn, out,
+                                     gate_out, value_out, a);
   if (st != ENGRAM_OK || n_tok == 0) return st;
 
-  if (dtype == ENGRAM_F32) {
-    const size_t lds = (size_t)d_mem * 4 + (key_norm == ENGRAM_KEY_NORM_PROJECTED ? (size_t)d_model * 4 : 0);
+  if (dt == ENGRAM_F32) {
+    const size_t lds = (size_t)d_mem * 4 + (kn == ENGRAM_KEY_NORM_PROJECTED ? (size_t)d_model * 4 : 0);
     if (lds > 64 * 1024)
       return fail(ENGRAM_ERR_UNSUPPORTED, "%s: fp32 path needs d_mem (+ d_model for the projected key norm) "
                   "<= 16384", fn);
@@ -563,12 +566,12 @@ engram_status engram_gate_forward_fp8(const void* mem, int64_t n_tok, int32_t d_
                                       engram_key_norm key_norm, void* const* out, float* gate_out,
                                       void* const* value_out, hipStream_t stream) {
   const char* fn = "engram_gate_forward_fp8";
-  if (dtype != ENGRAM_BF16) return fail(ENGRAM_ERR_UNSUPPORTED, "%s: operands must be bf16", fn);
+  if (enum_arg(dtype) != ENGRAM_BF16) return fail(ENGRAM_ERR_UNSUPPORTED, "%s: operands must be bf16", fn);
   if (d_mem % 128 != 0)
     return fail(ENGRAM_ERR_UNSUPPORTED, "%s: d_mem must be a multiple of 128 (got %d)", fn, d_mem);
   GateArgs a;
-  const engram_status st = gate_args(fn, mem, n_tok, d_mem, d_model, n_branch, h, wk, wv, gq, gk, eps, dtype,
-                                     key_norm, out, gate_out, value_out, a);
+  const engram_status st = gate_args(fn, mem, n_tok, d_mem, d_model, n_branch, h, wk, wv, gq, gk, eps, ENGRAM_BF16,
+                                     enum_arg(key_norm), out, gate_out, value_out, a);
   if (st != ENGRAM_OK || n_tok == 0) return st;
   const size_t bytes = gate_bf16_scratch_bytes(a, true);
   return with_scratch(fn, bytes, stream, [&](void* p) {
@@ -587,8 +590,8 @@ engram_status engram_gate_prepare_fp8(int32_t d_mem, int32_t d_model, int32_t n_
                 fn, d_mem, d_model);
   if (n_branch <= 0 || n_branch > ENGRAM_MAX_BRANCHES)
     return fail(ENGRAM_ERR_INVALID_ARG, "%s: n_branch %d not in [1, %d]", fn, n_branch, ENGRAM_MAX_BRANCHES);
-  if (key_norm != ENGRAM_KEY_NORM_MEMORY && key_norm != ENGRAM_KEY_NORM_PROJECTED)
-    return fail(ENGRAM_ERR_INVALID_ARG, "%s: unknown key_norm %d", fn, (int)key_norm);
+  if (!valid_key_norm(enum_arg(key_norm)))
+    return fail(ENGRAM_ERR_INVALID_ARG, "%s: unknown key_norm %d", fn, enum_arg(key_norm));
   if (wk == nullptr || wv == nullptr || wk_codes == nullptr || wk_scales == nullptr || wv_codes == nullptr ||
       wv_scales == nullptr || (key_norm == ENGRAM_KEY_NORM_MEMORY && (gq == nullptr || gk == nullptr)))
     return fail(ENGRAM_ERR_INVALID_ARG, "%s: null pointer array", fn);
@@ -665,8 +668,8 @@ engram_status engram_gate_forward_fp8q(const uint8_t* codes, const float* scales
   if (wk_scales == nullptr || wv_scales == nullptr) return fail(ENGRAM_ERR_INVALID_ARG, "%s: null scale array", fn);
   GateArgs a;
   const engram_status st = gate_args(fn, codes, n_tok, d_mem, d_model, n_branch, h, (const void* const*)wk_codes,
-                                     (const void* const*)wv_codes, gq, gk, eps, ENGRAM_BF16, key_norm, out, gate_out,
-                                     value_out, a);
+                                     (const void* const*)wv_codes, gq, gk, eps, ENGRAM_BF16, enum_arg(key_norm), out,
+                                     gate_out, value_out, a);
   if (st != ENGRAM_OK) return st;
   for (int m = 0; m < n_branch; ++m) {
     if (wk_scales[m] == nullptr || wv_scales[m] == nullptr || !aligned(wk_scales[m], 4) || !aligned(wv_scales[m], 4))
@@ -695,7 +698,7 @@ engram_status engram_conv_forward(const void* value, int32_t batch, int64_t seq,
   if (batch < 0 || seq < 0 || d_model <= 0)
     return fail(ENGRAM_ERR_INVALID_ARG, "%s: bad sizes batch=%d seq=%lld d_model=%d", fn, batch,
                 (long long)seq, d_model);
-  if (!valid_dtype(dtype)) return fail(ENGRAM_ERR_INVALID_ARG, "%s: unknown dtype", fn);
+  if (!valid_dtype(enum_arg(dtype))) return fail(ENGRAM_ERR_INVALID_ARG, "%s: unknown dtype", fn);
   if (!(eps >= 0.f)) return fail(ENGRAM_ERR_INVALID_ARG, "%s: eps must be >= 0", fn);
   if (taps < 1 || taps > ENGRAM_CONV_MAX_TAPS)
     return fail(ENGRAM_ERR_UNSUPPORTED, "%s: taps %d not in [1, %d]", fn, taps, ENGRAM_CONV_MAX_TAPS);
@@ -743,7 +746,7 @@ engram_status engram_quantize_fp8(const void* src, int64_t rows, int32_t cols, e
                                   float* scales, float* sumsq, hipStream_t stream) {
   const char* fn = "engram_quantize_fp8";
   if (rows < 0 || cols <= 0) return fail(ENGRAM_ERR_INVALID_ARG, "%s: bad sizes", fn);
-  if (!valid_dtype(dtype)) return fail(ENGRAM_ERR_INVALID_ARG, "%s: unknown dtype", fn);
+  if (!valid_dtype(enum_arg(dtype))) return fail(ENGRAM_ERR_INVALID_ARG, "%s: unknown dtype", fn);
   if (cols % 16 != 0) return fail(ENGRAM_ERR_UNSUPPORTED, "%s: cols %d not a multiple of 16", fn, cols);
   if (rows == 0) return ENGRAM_OK;
   if (src == nullptr || codes == nullptr || scales == nullptr || !aligned(src, 16) || !aligned(codes, 16) ||

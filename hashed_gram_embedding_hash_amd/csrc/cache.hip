@@ -140,7 +140,8 @@ engram_status engram_cache_build(const void* const* host_tables, const int64_t* 
   const int l2 = log2_exact(slots);
   if (l2 < 1 || l2 > 30 || slots <= capacity)
     return fail(ENGRAM_ERR_INVALID_ARG, "%s: slots %d must be a power of two above capacity %d", fn, slots, capacity);
-  if (dtype != ENGRAM_F32 && dtype != ENGRAM_BF16) return fail(ENGRAM_ERR_INVALID_ARG, "%s: unknown dtype", fn);
+  if (enum_arg(dtype) != ENGRAM_F32 && enum_arg(dtype) != ENGRAM_BF16)
+    return fail(ENGRAM_ERR_INVALID_ARG, "%s: unknown dtype", fn);
   if (w <= 0 || ((int64_t)w * (dtype == ENGRAM_F32 ? 4 : 2)) % 16 != 0)
     return fail(ENGRAM_ERR_UNSUPPORTED, "%s: row bytes must be a positive multiple of 16", fn);
   if (hot == nullptr || rows == nullptr || host_tables == nullptr || table == nullptr || cache_rows == nullptr ||

@@ -9,6 +9,19 @@
 
 namespace engram {
 
+// ---------------------------------------------------------------- enum arguments
+// The int value of an enum argument, which a C caller may have set to any int: read
+// through memcpy, because loading a C++ enum object that holds a value outside its
+// enumerators' range is undefined behaviour.  Entry points validate this value before
+// they use the enum itself.
+template <class E>
+inline int enum_arg(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "enum arguments are int-sized");
+  int v;
+  __builtin_memcpy(&v, &e, sizeof v);
+  return v;
+}
+
 // ---------------------------------------------------------------- errors
 engram_status fail(engram_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 engram_status hip_fail(hipError_t e, const char* what);
