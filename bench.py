@@ -79,7 +79,7 @@ def parse():
     p.add_argument("--offload-reps", type=int, default=3)
     p.add_argument("--offload-cache-gb", type=float, default=1.0,
                    help="HBM cache of the rows most frequent in the decode histories (0: off)")
-    p.add_argument("--offload-host-gb", type=float, default=48.0,
+    p.add_argument("--offload-host-gb", type=float, default=48.0,  # synth.OFFLOAD_HOST_GB
                    help="offload config: cap on pinned host table bytes (the GPU's system-memory aperture is "
                         "shared with the runtime; on the measured host, pinning beyond ~64 GB fails)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -169,14 +169,6 @@ def calibrate_copy(mib):
                       "kib_read": 2 * n / 1024, "kib_written": 2 * n / 1024}), flush=True)
 
 
-def mem_available_bytes():
-    with open("/proc/meminfo") as f:
-        for line in f:
-            if line.startswith("MemAvailable:"):
-                return int(line.split()[1]) * 1024
-    return None
-
-
 def run_offload(args):
     """Decode steps of the host-offload workload (256 sequences, one new token each):
     the rows of step s+1 are hashed and fetched on a side stream while step s gates.
@@ -196,15 +188,10 @@ def run_offload(args):
     cfg = synth.CONFIGS["offload"]
     dev = torch.device("cuda:0")
     say = lambda *a: print("[bench]", *a, file=sys.stderr, flush=True)
-    avail = mem_available_bytes()
-    rows = args.offload_rows or synth.offload_rows(cfg, avail)
+    avail = synth.mem_available_bytes()
     row_bytes = cfg.w * 2
-    cap_rows = int(args.offload_host_gb * 1e9 / (cfg.n_tables * row_bytes))
-    if not args.offload_rows and rows > cap_rows:
-        rows = synth.next_prime(cap_rows)
     free_hbm, _ = torch.cuda.mem_get_info()
-    if cfg.n_tables * rows * row_bytes > 0.8 * free_hbm:  # the HBM-resident copy must fit as well
-        rows = synth.next_prime(int(0.8 * free_hbm / (cfg.n_tables * row_bytes)))
+    rows = args.offload_rows or synth.offload_table_rows(cfg, avail, free_hbm, args.offload_host_gb)
     say(f"offload: target {cfg.n_tables} tables x {rows} rows = {cfg.n_tables * rows * row_bytes / 1e9:.1f} GB "
         f"(host MemAvailable {avail / 1e9 if avail else float('nan'):.0f} GB)")
 

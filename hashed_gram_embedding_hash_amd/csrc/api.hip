@@ -532,8 +532,9 @@ engram_status engram_gate_forward(const void* mem, int64_t n_tok, int32_t d_mem,
   if (st != ENGRAM_OK || n_tok == 0) return st;
 
   if (dt == ENGRAM_F32) {
-    const size_t lds = (size_t)d_mem * 4 + (kn == ENGRAM_KEY_NORM_PROJECTED ? (size_t)d_model * 4 : 0);
-    if (lds > 64 * 1024)
+    // the fp32 path stages the normalised memory vector (and the projected key) in fp64
+    const size_t lds = (size_t)d_mem * 8 + (kn == ENGRAM_KEY_NORM_PROJECTED ? (size_t)d_model * 8 : 0);
+    if (lds > 128 * 1024)
       return fail(ENGRAM_ERR_UNSUPPORTED, "%s: fp32 path needs d_mem (+ d_model for the projected key norm) "
                   "<= 16384", fn);
     launch_gate_f32(a, stream);
@@ -736,9 +737,10 @@ engram_status engram_conv_forward(const void* value, int32_t batch, int64_t seq,
   a.taps = taps;
   a.dil = dilation;
   a.eps = eps;
-  return with_scratch(fn, conv_scratch_bytes(a), stream, [&](void* p) {
-    a.inv = (float*)p;
-    launch_conv(a, dtype == ENGRAM_BF16, stream);
+  const bool bf16 = enum_arg(dtype) == ENGRAM_BF16;
+  return with_scratch(fn, conv_scratch_bytes(a, bf16), stream, [&](void* p) {
+    a.inv = p;
+    launch_conv(a, bf16, stream);
   });
 }
 

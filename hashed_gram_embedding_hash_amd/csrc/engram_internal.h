@@ -180,13 +180,13 @@ struct ConvArgs {
   void* out;          // same shape, updated in place
   const void* w;      // [d_model][taps]
   const void* gamma;  // [d_model]
-  float* inv;         // scratch [batch * seq]: 1 / rms of each value row
+  void* inv;          // scratch [batch * seq]: 1 / rms of each value row (fp32 for bf16 values, fp64 for fp32)
   int64_t seq;
   int32_t batch, d_model, taps, dil;
   float eps;
 };
 // scratch bytes the convolution needs (its inv array); a.inv must point at that many
-size_t conv_scratch_bytes(const ConvArgs& a);
+size_t conv_scratch_bytes(const ConvArgs& a, bool bf16);
 void launch_conv(const ConvArgs& a, bool bf16, hipStream_t s);
 
 }  // namespace engram

@@ -1,4 +1,4 @@
-// gate_f32.hip -- context-aware gating with every operation in fp32.
+// gate_f32.hip -- context-aware gating for fp32 operands.
 //
 // Same definition as the bf16 path ("Conditional Memory via Scalable Lookup",
 // section 2.3, Eq. (3)-(4), gated value, residual; section 2.4 Eq. (6) per
@@ -14,6 +14,11 @@
 //   4. alpha = sigmoid(logit / sqrt(d_model)), then the same row-per-wavefront
 //      loop over W_V writes out_i = h_i + alpha * v_i (and the gated value
 //      alpha * v_i when it is asked for).
+// The fp32 inputs are exact in fp64, and every product, sum, norm and the sigmoid are
+// computed in fp64; each output is rounded to fp32 once.  fp32 sums over d_mem terms
+// would carry errors of several units in the last place of their largest terms, which
+// an output that nearly cancels (h + alpha v ~ 0, or v ~ 0 in the gated value) turns
+// into a large relative error; this path costs nothing measurable either way.
 // All reductions run in a fixed order, so results are bit-reproducible.
 #include "engram_internal.h"
 
@@ -23,27 +28,27 @@ namespace {
 constexpr int NTHR = 256;
 constexpr int NWAVE = NTHR / 64;
 
-__device__ __forceinline__ float wave_sum(float v) {
+__device__ __forceinline__ double wave_sum(double v) {
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
 }
 
 // Sum over the workgroup; every thread gets the result.
-__device__ __forceinline__ float block_sum(float v, float* red) {
+__device__ __forceinline__ double block_sum(double v, double* red) {
   v = wave_sum(v);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) red[wave] = v;
   __syncthreads();
-  float s = 0.f;
+  double s = 0.0;
   for (int w = 0; w < NWAVE; ++w) s += red[w];
   __syncthreads();
   return s;
 }
 
 __global__ __launch_bounds__(NTHR) void gate_f32_kernel(const GateArgs a) {
-  extern __shared__ float s_en[];  // [d_mem]
-  __shared__ float red[NWAVE];
-  __shared__ float s_dot[NWAVE];
+  extern __shared__ double s_en[];  // [d_mem] (+ [d_model] with the projected key norm)
+  __shared__ double red[NWAVE];
+  __shared__ double s_dot[NWAVE];
 
   const int64_t t = blockIdx.x;
   const int m = blockIdx.y;
@@ -57,65 +62,66 @@ __global__ __launch_bounds__(NTHR) void gate_f32_kernel(const GateArgs a) {
   const float* gk = (const float*)a.gk[m];
   float* out = (float*)a.out[m] + t * d_model;
   float* vout = a.vout[m] != nullptr ? (float*)a.vout[m] + t * d_model : nullptr;
+  const double eps = a.eps;
 
-  float ss = 0.f;
-  for (int j = threadIdx.x; j < d_mem; j += NTHR) ss += e[j] * e[j];
-  const float rms_e = sqrtf(block_sum(ss, red) / (float)d_mem + a.eps);
-  float sh = 0.f;
-  for (int i = threadIdx.x; i < d_model; i += NTHR) sh += h[i] * h[i];
-  const float rms_h = sqrtf(block_sum(sh, red) / (float)d_model + a.eps);
+  double ss = 0.0;
+  for (int j = threadIdx.x; j < d_mem; j += NTHR) ss += (double)e[j] * e[j];
+  const double rms_e = sqrt(block_sum(ss, red) / d_mem + eps);
+  double sh = 0.0;
+  for (int i = threadIdx.x; i < d_model; i += NTHR) sh += (double)h[i] * h[i];
+  const double rms_h = sqrt(block_sum(sh, red) / d_model + eps);
 
-  float logit = 0.f;
+  double logit = 0.0;
   if (a.key_norm == ENGRAM_KEY_NORM_MEMORY) {
-    for (int j = threadIdx.x; j < d_mem; j += NTHR) s_en[j] = e[j] / rms_e * gk[j];
+    for (int j = threadIdx.x; j < d_mem; j += NTHR) s_en[j] = (double)e[j] / rms_e * gk[j];
     __syncthreads();
-    float dot = 0.f;  // meaningful in lane 0 of each wave
+    double dot = 0.0;  // meaningful in lane 0 of each wave
     for (int i = wave; i < d_model; i += NWAVE) {
       const float* row = wk + (int64_t)i * d_mem;
-      float k = 0.f;
-      for (int j = lane; j < d_mem; j += 64) k += row[j] * s_en[j];
+      double k = 0.0;
+      for (int j = lane; j < d_mem; j += 64) k += (double)row[j] * s_en[j];
       k = wave_sum(k);
-      dot += (h[i] / rms_h * gq[i]) * k;
+      dot += ((double)h[i] / rms_h * gq[i]) * k;
     }
     if (lane == 0) s_dot[wave] = dot;
     __syncthreads();
     for (int w = 0; w < NWAVE; ++w) logit += s_dot[w];
   } else {
     // the raw projection k = W_K e into LDS, then its RMSNorm over the d_model features
-    float* s_k = s_en + d_mem;
+    double* s_k = s_en + d_mem;
     for (int j = threadIdx.x; j < d_mem; j += NTHR) s_en[j] = e[j];
     __syncthreads();
     for (int i = wave; i < d_model; i += NWAVE) {
       const float* row = wk + (int64_t)i * d_mem;
-      float k = 0.f;
-      for (int j = lane; j < d_mem; j += 64) k += row[j] * s_en[j];
+      double k = 0.0;
+      for (int j = lane; j < d_mem; j += 64) k += (double)row[j] * s_en[j];
       k = wave_sum(k);
       if (lane == 0) s_k[i] = k;
     }
     __syncthreads();
-    float kk = 0.f, dot = 0.f;
+    double kk = 0.0, dot = 0.0;
     for (int i = threadIdx.x; i < d_model; i += NTHR) {
       kk += s_k[i] * s_k[i];
-      dot += (h[i] / rms_h * gq[i]) * s_k[i] * gk[i];
+      dot += ((double)h[i] / rms_h * gq[i]) * s_k[i] * gk[i];
     }
-    const float rms_k = sqrtf(block_sum(kk, red) / (float)d_model + a.eps);
+    const double rms_k = sqrt(block_sum(kk, red) / d_model + eps);
     logit = block_sum(dot, red) / rms_k;
   }
-  logit /= sqrtf((float)d_model);
-  const float alpha = 1.f / (1.f + expf(-logit));
-  if (threadIdx.x == 0 && a.gate_out != nullptr) a.gate_out[(int64_t)m * a.n_tok + t] = alpha;
+  logit /= sqrt((double)d_model);
+  const double alpha = 1.0 / (1.0 + exp(-logit));
+  if (threadIdx.x == 0 && a.gate_out != nullptr) a.gate_out[(int64_t)m * a.n_tok + t] = (float)alpha;
 
   // every thread of the wave holds h[i]; stores happen after the last read of h
   // in this loop iteration, so out may alias h
   for (int i = wave; i < d_model; i += NWAVE) {
     const float* row = wv + (int64_t)i * d_mem;
-    float v = 0.f;
-    for (int j = lane; j < d_mem; j += 64) v += row[j] * e[j];
+    double v = 0.0;
+    for (int j = lane; j < d_mem; j += 64) v += (double)row[j] * e[j];
     v = wave_sum(v);
-    const float hi = h[i];
+    const double hi = h[i];
     if (lane == 0) {
-      out[i] = hi + alpha * v;
-      if (vout != nullptr) vout[i] = alpha * v;
+      out[i] = (float)(hi + alpha * v);
+      if (vout != nullptr) vout[i] = (float)(alpha * v);
     }
   }
 }
@@ -125,7 +131,7 @@ __global__ __launch_bounds__(NTHR) void gate_f32_kernel(const GateArgs a) {
 void launch_gate_f32(const GateArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)a.n_tok, (unsigned)a.n_branch);
   const size_t lds = ((size_t)a.d_mem + (a.key_norm == ENGRAM_KEY_NORM_PROJECTED ? (size_t)a.d_model : 0)) *
-                     sizeof(float);
+                     sizeof(double);
   hipLaunchKernelGGL(gate_f32_kernel, grid, dim3(NTHR), lds, s, a);
 }
 

@@ -217,11 +217,12 @@ engram_status engram_lookup_fp8(const int32_t* raw, int32_t batch, int64_t ld, i
  *        the input of the short convolution (engram_conv_forward).
  * Arithmetic: bf16 products with fp32 accumulation on the matrix cores, fp32
  * elsewhere; with ENGRAM_KEY_NORM_MEMORY the bf16 path folds both gains into a
- * copy of W_K rounded once to bf16.  ENGRAM_F32 computes everything in fp32 (its
- * ENGRAM_KEY_NORM_PROJECTED form needs d_mem + d_model <= 16384).
+ * copy of W_K rounded once to bf16.  ENGRAM_F32 (fp32 storage) computes every sum,
+ * norm and the sigmoid in fp64 and rounds each output to fp32 once.
  * Shapes: ENGRAM_BF16 needs d_mem % 64 == 0 and d_model % 32 == 0, d_model * d_mem
  * < 2^32 and n_tok < 2^31, and at most 2^29 tiles of 256 tokens x 256 features over
- * all branches; ENGRAM_F32 accepts any positive sizes with n_tok < 2^31.  Larger
+ * all branches; ENGRAM_F32 needs d_mem <= 16384 (d_mem + d_model <= 16384 with
+ * ENGRAM_KEY_NORM_PROJECTED) and n_tok < 2^31.  Larger
  * requests return ENGRAM_ERR_UNSUPPORTED.  n_tok == 0 is a no-op.
  * Cross-workgroup wait: in the bf16 and FP8 paths the value tiles of a token tile
  * wait, bounded, for its gates (published by the key tiles of the same launch, which
@@ -294,7 +295,8 @@ engram_status engram_gate_forward_prepared(const void* mem, int64_t n_tok, int32
  *        overlap `value`.
  * w:     device [d_model][taps] (channel-major: the taps of one channel are
  *        contiguous).  gamma: device [d_model].  All of `dtype`, 16-byte aligned.
- * Arithmetic: fp32, one rounding to `dtype` when `out` is written.
+ * Arithmetic: fp32 for bf16 values, fp64 for fp32 values; one rounding to `dtype` when
+ * `out` is written.
  * Shapes: d_model * sizeof(dtype) % 16 == 0, 1 <= taps <= ENGRAM_CONV_MAX_TAPS,
  * 1 <= dilation <= ENGRAM_CONV_MAX_DILATION, seq * d_model * sizeof(dtype) < 4 GiB
  * (UNSUPPORTED otherwise).  batch == 0

@@ -401,6 +401,35 @@ def offload_rows(cfg: Config, mem_available_bytes: Optional[int]) -> int:
     return next_prime(int(cfg.rows * f))
 
 
+OFFLOAD_HOST_GB = 48.0   # cap on pinned host table bytes (the GPU's system-memory aperture is shared)
+
+
+def offload_table_rows(cfg: Config, mem_available_bytes: Optional[int], hbm_free_bytes: Optional[int],
+                       host_gb: float = OFFLOAD_HOST_GB) -> int:
+    """Rows per table of the offload workload as it is measured: the full size
+    (offload_rows), capped at host_gb of pinned host memory and at 80 % of free HBM (the
+    HBM-resident copy it is compared with must fit too); a prime each time it is cut."""
+    rows = offload_rows(cfg, mem_available_bytes)
+    row_bytes = cfg.w * (4 if cfg.dtype == "f32" else 2)
+    cap_rows = int(host_gb * 1e9 / (cfg.n_tables * row_bytes))
+    if rows > cap_rows:
+        rows = next_prime(cap_rows)
+    if hbm_free_bytes is not None and cfg.n_tables * rows * row_bytes > 0.8 * hbm_free_bytes:
+        rows = next_prime(int(0.8 * hbm_free_bytes / (cfg.n_tables * row_bytes)))
+    return rows
+
+
+def mem_available_bytes() -> Optional[int]:
+    try:
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemAvailable:"):
+                    return int(line.split()[1]) * 1024
+    except OSError:
+        pass
+    return None
+
+
 def device_inputs(cfg: Config, device, tables: bool = True, table_rows_override: Optional[int] = None):
     """All inputs of one configuration, generated directly on ``device``.
 

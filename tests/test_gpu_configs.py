@@ -106,6 +106,87 @@ def test_decode_prefetch_pipeline():
                           e_o[sel], tokens, say=say)
 
 
+def test_decode_offload_at_benchmark_size_every_step():
+    """The offload decode workload at the size bench.py --config offload measures (the
+    100B-parameter tables scaled by synth.offload_table_rows: 48 GB of pinned host memory
+    on the measured hosts), all of its decode steps: per step, hash the new position of
+    the 256 sequences and prefetch their rows from the host tables, directly and through
+    the HBM row cache (1 GB, rows most frequent in the histories); indices and both staged
+    buffers bit-exact against the oracle every step; the gate on 64 sequences at 8 steps."""
+    import ctypes
+    import oracle
+    from gpu_helpers import sentinel_like
+    cfg = synth.CONFIGS["offload"]
+    free_hbm, _ = torch.cuda.mem_get_info()
+    rows = synth.offload_table_rows(cfg, synth.mem_available_bytes(), free_hbm)
+    cfg = cfg.replace(rows=rows)
+    nt, w, S, B, T0 = cfg.n_tables, cfg.w, cfg.decode_steps, cfg.batch, cfg.seq
+    say(f"decode offload at benchmark size: {nt} x {rows} rows = {nt * rows * w * 2 / 1e9:.1f} GB host tables, "
+        f"{S} steps")
+    addrs = []
+    try:
+        chunk = 1 << 22
+        for b in range(nt):
+            p = eg.host_alloc(rows * w * 2)
+            addrs.append(p)
+            host = torch.from_numpy(np.ctypeslib.as_array((ctypes.c_int16 * (rows * w)).from_address(p)))
+            host = host.view(torch.bfloat16).view(rows, w)
+            for r0 in range(0, rows, chunk):
+                r1 = min(rows, r0 + chunk)
+                host[r0:r1].copy_(synth.table_rows(cfg, b, torch.arange(r0, r1, device=DEV), DEV))
+        torch.cuda.synchronize()
+        say("  host tables filled")
+        raw = synth.raw_ids(cfg)
+        cmap = synth.comp_map(cfg)
+        mult, rows_u32 = synth.multipliers(cfg), synth.table_rows_u32(cfg)
+        ids_d = eg.engram_compress(torch.from_numpy(raw).to(DEV), torch.from_numpy(cmap).to(DEV))
+        ids_o, bad = oracle.compress(raw, cmap)
+        assert bad == 0
+        # the row cache, selected from the histories' indices as the benchmark does
+        capacity = int(1e9 / (nt * w * 2))
+        hist = eg.engram_hash(ids_d, cfg.orders, cfg.heads, mult, rows_u32, cfg.vocab_c, t_begin=0, t_count=T0)
+        hot = eg.engram_cache_select(hist.cpu().numpy(), capacity)
+        del hist
+        table, cache_rows = eg.engram_cache_build(addrs, [rows] * nt, w, torch.bfloat16, hot)
+        say("  row cache built")
+        wk, wv = synth.weights(cfg, 0, DEV)
+        gq, gk = synth.gains(cfg, 0, DEV)
+        stg = torch.empty((B, nt * w), dtype=torch.bfloat16, device=DEV)
+        stg_c = torch.empty_like(stg)
+        hits = torch.zeros(1, dtype=torch.int32, device=DEV)
+        gate_steps = {0, 1, 2, 31, 64, 97, S - 2, S - 1}
+        sel = np.arange(0, B, 4)                                   # 64 of the 256 sequences
+        for s in range(S):
+            t = T0 + s
+            idx = eg.engram_hash(ids_d, cfg.orders, cfg.heads, mult, rows_u32, cfg.vocab_c, t_begin=t, t_count=1)
+            eg.engram_prefetch_host(idx, addrs, [rows] * nt, w, torch.bfloat16, staging=sentinel_like(stg))
+            eg.engram_prefetch_host_cached(idx, addrs, [rows] * nt, w, torch.bfloat16, table, cache_rows,
+                                           staging=sentinel_like(stg_c), hits=hits)
+            torch.cuda.synchronize()
+            idx_o = oracle.hash_ids(ids_o, cfg.orders, cfg.heads, mult, rows_u32, cfg.vocab_c, t_begin=t, t_count=1)
+            assert np.array_equal(idx.cpu().numpy(), idx_o), s
+            e_o = oracle_memory(cfg, idx_o)
+            assert np.array_equal(host_view(stg), e_o), s
+            assert np.array_equal(host_view(stg_c), e_o), s
+            if s in gate_steps:
+                tokens = sel * (T0 + S) + t
+                h = synth.hidden_rows(cfg, 0, torch.from_numpy(tokens)).to(DEV)
+                alpha = sentinel_like(torch.empty((1, len(sel)), dtype=torch.float32, device=DEV))
+                out = eg.engram_gate_forward(stg[torch.from_numpy(sel).to(DEV)].contiguous(), [h], [wk], [wv], [gq],
+                                             [gk], cfg.eps, out=[sentinel_like(torch.empty_like(h))],
+                                             gate_out=alpha)[0]
+                check_gate_tokens(f"step {s} gate", cfg, 0, out.float().cpu().numpy(), alpha.cpu().numpy()[0],
+                                  e_o[sel], tokens, say=say)
+        hit_rate = int(hits.item()) / (S * B * nt)
+        say(f"  {S} steps: indices and staged rows (direct and cached) bit-exact; cache hit rate {hit_rate:.3f}")
+        assert hit_rate > 0.05
+        del table, cache_rows
+    finally:
+        torch.cuda.synchronize()
+        for p in addrs:
+            eg.host_free(p)
+
+
 def test_pipeline_graph_replay_equals_eager():
     """The layer's step (the fused lookup and the gate: three kernels) captured in a HIP
     graph: every replay, with eager work on the same buffers in between, reproduces the
