@@ -500,6 +500,80 @@ def measure_conv(args, cfg, bufs, h, layer, outs, flush):
             "gate_with_values_plus_conv_ms": round(gate_v_ms + conv_ms, 5)}
 
 
+def measure_ceiling(args, cfg, layer, bufs, sep_per, per, flush):
+    """What the memory system delivers for the gather's access pattern, from the probes
+    of libengram_probe.so (not part of the path): the same index matrix, read-only from
+    one table (the rows' bytes, nothing written), a contiguous read of the same number of
+    bytes, and a contiguous device copy of the memory vectors (read + write), each timed
+    with events after the cache flush.  The gather (engram_gather) and the fused lookup
+    are then stated against these as well as against the 8 TB/s spec."""
+    import ctypes
+    import torch
+    from hashed_gram_embedding_hash_amd import build as hb
+    L = ctypes.CDLL(hb.PROBE_LIB)
+    P = ctypes.c_void_p
+    L.engram_probe_rows_sink_words.restype = ctypes.c_int64
+    L.engram_probe_rows_sink_words.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
+    L.engram_probe_row_reads.argtypes = [P, ctypes.c_int32, P, ctypes.c_int64, ctypes.c_int32, P, P]
+    L.engram_probe_stream_reads.argtypes = [P, ctypes.c_int64, P, P]
+    dev = bufs["mem"].device
+    T, nt = cfg.tokens, cfg.n_tables
+    row_bytes = cfg.w * (4 if cfg.dtype == "f32" else 2)
+    idx = bufs["idx"]                      # [tokens, n_tables], written by engram_compress_hash
+    table0 = layer.tables[0]
+    sink = torch.empty(max(int(L.engram_probe_rows_sink_words(T, row_bytes, nt)), 8192 * 256), dtype=torch.int32,
+                       device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    row_total = T * nt * row_bytes
+    stream_bytes = min(row_total, table0.numel() * table0.element_size()) // 16 * 16
+    copy_dst = torch.empty_like(bufs["mem"])
+
+    def rows():
+        assert L.engram_probe_row_reads(P(table0.data_ptr()), row_bytes, P(idx.data_ptr()), T, nt,
+                                        P(sink.data_ptr()), stream) == 0
+
+    def stream_read():
+        assert L.engram_probe_stream_reads(P(table0.data_ptr()), stream_bytes, P(sink.data_ptr()), stream) == 0
+
+    def copy():
+        copy_dst.copy_(bufs["mem"])
+
+    def timed(fn, reps):
+        ts = []
+        for i in range(reps):
+            if flush is not None:
+                flush.fill_(float(i))
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            ts.append((a, b))
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in ts) / reps
+    for fn in (rows, stream_read, copy):
+        fn()
+    reps = max(5, args.steps)
+    t_rows, t_stream, t_copy = timed(rows, reps), timed(stream_read, reps), timed(copy, reps)
+    gbs = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
+    ceil_rows = gbs(row_total, t_rows)
+    g_ms, l_ms = sep_per["gather"], per["lookup"]
+    return {
+        "probe": "libengram_probe.so (measurement only): engram_probe_row_reads / engram_probe_stream_reads",
+        "random_rows_read_only": {"ms": round(t_rows, 5), "row_GB/s": round(ceil_rows, 1),
+                                  "note": f"the step's {T} x {nt} row indices, all read from table 0 "
+                                          f"({row_bytes}-byte rows), nothing written"},
+        "stream_read": {"ms": round(t_stream, 5), "GB/s": round(gbs(stream_bytes, t_stream), 1),
+                        "bytes": stream_bytes},
+        "device_copy_of_memory_vectors": {"ms": round(t_copy, 5),
+                                          "GB/s_read_plus_write": round(gbs(2 * bufs["mem"].numel() *
+                                                                            bufs["mem"].element_size(), t_copy), 1)},
+        "gather": {"ms": round(g_ms, 5), "row_read_GB/s": round(gbs(row_total, g_ms), 1),
+                   "row_read_frac_of_random_row_ceiling": round(t_rows / g_ms, 4)},
+        "lookup": {"ms": round(l_ms, 5), "row_read_GB/s": round(gbs(row_total, l_ms), 1),
+                   "row_read_frac_of_random_row_ceiling": round(t_rows / l_ms, 4)},
+    }
+
+
 def cpu_baseline(cfg, target_s, fp8=False):
     """The oracle (single thread) on the first tokens of sequence 0: compress, hash,
     gather and gate (its FP8 form with fp8).  Table rows are regenerated outside the
@@ -818,6 +892,8 @@ def run_workload(args, name, secondary=False):
     if not args.no_conv:
         print("[bench] short convolution", file=sys.stderr, flush=True)
         result["conv"] = measure_conv(args, cfg, bufs, h, layer, outs, flush)
+    print("[bench] gather ceiling probes", file=sys.stderr, flush=True)
+    result["gather_ceiling"] = measure_ceiling(args, cfg, layer, bufs, sep_per, per, flush)
     return result
 
 
