@@ -46,6 +46,7 @@ KEY_NORM_MEMORY = 0      # k = W_K RMSNorm_gk(e), gk over d_mem (the review page
 KEY_NORM_PROJECTED = 1   # k = RMSNorm_gk(W_K e), gk over d_model (the paper's Eq. 4 / Eq. 6)
 CONV_MAX_TAPS = 8
 CONV_MAX_DILATION = 16
+NOALLOC_SCRATCH_BYTES = 128 << 20   # ENGRAM_NOALLOC_SCRATCH_BYTES
 
 _STATUS = {0: "ENGRAM_OK", 1: "ENGRAM_ERR_INVALID_ARG", 2: "ENGRAM_ERR_UNSUPPORTED", 3: "ENGRAM_ERR_HIP"}
 
@@ -57,6 +58,7 @@ EXPORTS = (
     "engram_compress_hash", "engram_quantize_fp8", "engram_gate_forward_fp8", "engram_lookup",
     "engram_lookup_fp8", "engram_gate_prepare_fp8", "engram_gate_forward_fp8q", "engram_gate_prepare",
     "engram_gate_forward_prepared", "engram_gate_wait_timeouts", "engram_debug_force_gate_timeout",
+    "engram_gate_forward_noalloc",
 )
 
 
@@ -95,6 +97,7 @@ def lib() -> ctypes.CDLL:
         L.engram_gate_forward.argtypes = [P, i64, i32, i32, i32, P, P, P, P, P, ctypes.c_float, i32, i32,
                                           P, P, P, P]
         L.engram_gate_forward_fp8.argtypes = L.engram_gate_forward.argtypes
+        L.engram_gate_forward_noalloc.argtypes = L.engram_gate_forward.argtypes
         L.engram_lookup_fp8.argtypes = [P, i32, i64, i64, i64, P, i32, P, i32, i32, P, P, i32, P, i32, P, P, P, P, P,
                                         P, P]
         L.engram_gate_prepare.argtypes = [i32, i32, i32, P, P, P, P, P]
@@ -117,7 +120,7 @@ def lib() -> ctypes.CDLL:
                   "engram_compress_hash", "engram_quantize_fp8", "engram_gate_forward_fp8", "engram_lookup",
                   "engram_lookup_fp8", "engram_gate_prepare_fp8", "engram_gate_forward_fp8q",
                   "engram_gate_prepare", "engram_gate_forward_prepared", "engram_gate_wait_timeouts",
-                  "engram_debug_force_gate_timeout"):
+                  "engram_debug_force_gate_timeout", "engram_gate_forward_noalloc"):
             getattr(L, f).restype = st
         _lib = L
     return _lib
@@ -397,13 +400,15 @@ def engram_gate_forward_fp8q(codes, scales, sumsq, h: Sequence, prepared, gq: Se
 def engram_gate_forward(mem, h: Sequence, wk: Sequence, wv: Sequence, gq: Sequence, gk: Sequence,
                         eps: float = 1e-6, out: Optional[Sequence] = None, gate_out=None,
                         value_out: Optional[Sequence] = None, key_norm: int = KEY_NORM_MEMORY, stream=None,
-                        fp8: bool = False):
+                        fp8: bool = False, noalloc: bool = False):
     """out[m] = h[m] + sigmoid(RMSNorm(h[m]) . k[m] / sqrt(d)) * W_V[m] mem, with
     k[m] = W_K[m] RMSNorm(mem) (KEY_NORM_MEMORY, gk over d_mem) or RMSNorm(W_K[m] mem)
     (KEY_NORM_PROJECTED, gk over d_model).
 
     ``fp8``: both projections on per-row E4M3 codes of the weights and of mem
     (engram_gate_forward_fp8; bf16 operands, d_mem % 128 == 0).
+    ``noalloc``: engram_gate_forward_noalloc (no allocation; the library's fixed
+    scratch array; the output tensors must be passed or are allocated here by torch).
 
     Lists hold one tensor per branch; ``out`` defaults to new tensors (pass ``h``
     for in-place).  ``gate_out``: optional float32 [n_branch, n_tok] for alpha.
@@ -442,7 +447,10 @@ def engram_gate_forward(mem, h: Sequence, wk: Sequence, wv: Sequence, gq: Sequen
     for x in gk:
         if tuple(x.shape) != (gk_len,):
             raise ValueError(f"gk must be [{gk_len}] for key_norm {key_norm}")
-    fn = lib().engram_gate_forward_fp8 if fp8 else lib().engram_gate_forward
+    if fp8 and noalloc:
+        raise ValueError("the allocation-free gate has no FP8 form")
+    fn = (lib().engram_gate_forward_fp8 if fp8 else
+          lib().engram_gate_forward_noalloc if noalloc else lib().engram_gate_forward)
     _check(fn(mem.data_ptr(), n_tok, d_mem, d_model, nb, arr(h), arr(wk), arr(wv), arr(gq), arr(gk), float(eps),
               _edtype(mem), int(key_norm), arr(out), _opt(gate_out, "gate_out", torch.float32), varr,
               _stream(stream)))

@@ -548,6 +548,28 @@ engram_status engram_gate_forward(const void* mem, int64_t n_tok, int32_t d_mem,
   });
 }
 
+engram_status engram_gate_forward_noalloc(const void* mem, int64_t n_tok, int32_t d_mem, int32_t d_model,
+                                          int32_t n_branch, const void* const* h, const void* const* wk,
+                                          const void* const* wv, const void* const* gq, const void* const* gk,
+                                          float eps, engram_dtype dtype, engram_key_norm key_norm, void* const* out,
+                                          float* gate_out, void* const* value_out, hipStream_t stream) {
+  const char* fn = "engram_gate_forward_noalloc";
+  GateArgs a;
+  const int dt = enum_arg(dtype), kn = enum_arg(key_norm);
+  const engram_status st = gate_args(fn, mem, n_tok, d_mem, d_model, n_branch, h, wk, wv, gq, gk, eps, dt, kn, out,
+                                     gate_out, value_out, a);
+  if (st != ENGRAM_OK || n_tok == 0) return st;
+  if (dt == ENGRAM_F32) {  // the fp32 path uses no scratch
+    const size_t lds = (size_t)d_mem * 8 + (kn == ENGRAM_KEY_NORM_PROJECTED ? (size_t)d_model * 8 : 0);
+    if (lds > 128 * 1024)
+      return fail(ENGRAM_ERR_UNSUPPORTED, "%s: fp32 path needs d_mem (+ d_model for the projected key norm) "
+                  "<= 16384", fn);
+    launch_gate_f32(a, stream);
+    return check_launch(fn);
+  }
+  return gate_forward_noalloc(fn, a, stream);
+}
+
 engram_status engram_gate_wait_timeouts(int32_t* count, int32_t reset) {
   if (count == nullptr) return fail(ENGRAM_ERR_INVALID_ARG, "engram_gate_wait_timeouts: null count");
   const hipError_t e = gate_wait_timeouts(count, reset != 0);

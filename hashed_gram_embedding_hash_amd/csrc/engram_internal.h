@@ -145,6 +145,9 @@ void launch_gate_f32(const GateArgs& a, hipStream_t s);
 hipError_t gate_wait_timeouts(int32_t* count, bool reset);
 // Test hook behind engram_debug_force_gate_timeout.
 void set_gate_forced_wait_timeout(bool on);
+// engram_gate_forward_noalloc's bf16 launch on the library's fixed device array (a is
+// checked and filled by the caller; the scratch pointer is set here).
+engram_status gate_forward_noalloc(const char* fn, GateArgs& a, hipStream_t stream);
 
 // ---------------------------------------------------------------- FP8 (E4M3) encoding
 // Shared by the quantization kernels and the quantizing lookup (their codes must agree).

@@ -75,6 +75,9 @@ typedef enum engram_key_norm {
   ENGRAM_KEY_NORM_PROJECTED = 1
 } engram_key_norm;
 
+/* Size of the fixed device array behind engram_gate_forward_noalloc (128 MiB). */
+#define ENGRAM_NOALLOC_SCRATCH_BYTES (128u << 20)
+
 /* Limits of this implementation. */
 #define ENGRAM_MAX_TABLES 32   /* n_orders * heads                       */
 #define ENGRAM_MAX_ORDER 4     /* largest n-gram order                   */
@@ -235,6 +238,28 @@ engram_status engram_gate_forward(const void* mem, int64_t n_tok, int32_t d_mem,
                                   const void* const* gk, float eps, engram_dtype dtype,
                                   engram_key_norm key_norm, void* const* out, float* gate_out,
                                   void* const* value_out, hipStream_t stream);
+
+/*
+ * engram_gate_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): same
+ * arguments, same results bit for bit, but no allocation of any kind.  The bf16 path's
+ * scratch (gain-folded key weights, partial sums, gates, work-queue counters) is a
+ * fixed device array of ENGRAM_NOALLOC_SCRATCH_BYTES that each device the library runs
+ * on holds until the process ends; shapes needing more return ENGRAM_ERR_UNSUPPORTED:
+ *   n_branch * d_model * d_mem * 2 + 12 * n_branch * ceil(d_model / 256) * n_tok
+ *   + 4 * n_branch * n_tok (+ a few KB of counters) bytes, each term rounded up to 256.
+ * (The large workload -- 262,144 tokens, d_model 4096, d_mem 1280, 2 branches -- needs
+ * 124 MB.)  All calls on one device share the array and it keeps the last call's
+ * contents: calls that overlap on one device race, so order them (one stream, or events).
+ * The first call on a device looks the array's address up (hipGetSymbolAddress); a
+ * failure there is ENGRAM_ERR_HIP.  ENGRAM_F32 uses no scratch and behaves as
+ * engram_gate_forward.
+ */
+engram_status engram_gate_forward_noalloc(const void* mem, int64_t n_tok, int32_t d_mem, int32_t d_model,
+                                          int32_t n_branch, const void* const* h, const void* const* wk,
+                                          const void* const* wv, const void* const* gq, const void* const* gk,
+                                          float eps, engram_dtype dtype, engram_key_norm key_norm, void* const* out,
+                                          float* gate_out, void* const* value_out, hipStream_t stream);
 
 /*
  * Health of the gate's cross-workgroup wait (see engram_gate_forward): *count receives
