@@ -77,6 +77,9 @@ def parse():
     p.add_argument("--offload-rows", type=int, default=0,
                    help="offload config: rows per table (default: 100B parameters, scaled to 60%% of free host RAM)")
     p.add_argument("--offload-reps", type=int, default=3)
+    p.add_argument("--offload-fold-each-step", action="store_true",
+                   help="offload config: call engram_gate_forward every step (it folds the key weights with "
+                        "their gains on every call) instead of engram_gate_forward_prepared on weights folded once")
     p.add_argument("--offload-cache-gb", type=float, default=4.0,
                    help="HBM cache of the rows most frequent in the decode histories (0: off); 4 GB holds "
                         "every row the 256 x 4096-token histories use")
@@ -279,9 +282,20 @@ def run_offload(args):
             chk(fn(idx[buf].data_ptr(), B, cfg.n_tables, hptrs if mode == "host" else dptrs, rows64.ctypes.data,
                    cfg.w, eg.BF16, stg[buf].data_ptr(), None, st))
 
+        # The decode loop's weights are constant: by default the key weights are folded with
+        # their gains once (engram_gate_prepare) and every step calls engram_gate_forward_prepared
+        # (the same results bit for bit); --offload-fold-each-step calls engram_gate_forward,
+        # which folds them again on every call.
+        folded = eg.engram_gate_prepare([wk], [gq], [gk])
+        folded_a = arr(folded)
+
         def gate(s, buf, st=ms):
-            chk(L.engram_gate_forward(stg[buf].data_ptr(), B, cfg.d_mem, cfg.d_model, 1, h_a[s], wk_a, wv_a, gq_a,
-                                      gk_a, cfg.eps, eg.BF16, eg.KEY_NORM_MEMORY, out_a, None, None, st))
+            if args.offload_fold_each_step:
+                chk(L.engram_gate_forward(stg[buf].data_ptr(), B, cfg.d_mem, cfg.d_model, 1, h_a[s], wk_a, wv_a,
+                                          gq_a, gk_a, cfg.eps, eg.BF16, eg.KEY_NORM_MEMORY, out_a, None, None, st))
+            else:
+                chk(L.engram_gate_forward_prepared(stg[buf].data_ptr(), B, cfg.d_mem, cfg.d_model, 1, h_a[s],
+                                                   folded_a, wv_a, ctypes.c_float(cfg.eps), out_a, None, None, st))
 
         def enqueue(mode, mstream):
             """The S decode steps on `mstream` (gates) and `side` (hash + fetch of the next
@@ -407,7 +421,9 @@ def run_offload(args):
                        "sizing": f"100B parameters scaled to min(60% of free host RAM, {args.offload_host_gb:g} GB "
                                  "of pinned host memory, 80% of free HBM)",
                        "d_mem": cfg.d_mem, "d_model": cfg.d_model, "branches": 1,
-                       "pipeline": "side stream: hash + fetch of step s+1; main stream: gate of step s"},
+                       "pipeline": "side stream: hash + fetch of step s+1; main stream: gate of step s",
+                       "gate_call": ("engram_gate_forward (key weights folded every step)" if args.offload_fold_each_step
+                                     else "engram_gate_forward_prepared (key weights folded once)")},
             "step_us": {k: round(v, 2) for k, v in med.items()},
             "step_us_all": {k: [round(x, 2) for x in v] for k, v in steps.items()},
             "step_timing": "graph replay of the whole two-stream pipeline (GPU-paced)",
