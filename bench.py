@@ -68,6 +68,8 @@ def parse():
     p.add_argument("--fp8", action="store_true",
                    help="gate projections on E4M3 codes (engram_gate_forward_fp8; quantization inside the call)")
     p.add_argument("--no-fp8", action="store_true", help="skip the extra fp8-gate step measurement")
+    p.add_argument("--no-fused", action="store_true",
+                   help="skip the one-call step (engram_lookup_gate) measured beside the two-call step")
     p.add_argument("--no-graph", action="store_true",
                    help="time the eagerly launched step only (default: the step is also captured in a HIP graph "
                         "and the graph replay is the reported value)")
@@ -760,6 +762,26 @@ def run_workload(args, name, secondary=False):
         return ms_step, ms_eager, per, t_wall
 
     ms_step, ms_eager, per, t_wall = time_steps(make_step(args.fp8), args.steps, args.warmup, not args.no_graph)
+
+    # The same step as one call, engram_lookup_gate: the gate's kernel hashes each token and
+    # loads the table rows itself (the memory vectors are never stored); bit-identical results.
+    fused_step = None
+    if cfg.dtype == "bf16" and not args.fp8 and not args.no_fused:
+        def fused(ev=None):
+            if ev is not None:
+                ev[0].record()
+            eg.engram_lookup_gate(raw, layer.cmap, layer.orders, layer.heads, layer.mult, layer.tables,
+                                  layer.pad_id, h, layer.wk, layer.wv, layer.gq, layer.gk, cfg.eps, out=outs,
+                                  key_norm=layer.key_norm)
+            if ev is not None:
+                ev[1].record()
+        ms_f, ms_fe, _, _ = time_steps(fused, args.steps, 3, not args.no_graph, names=["step"])
+        fused_step = {"call": "engram_lookup_gate", "ms_per_step": round(ms_f, 5),
+                      "ms_per_step_eager": round(ms_fe, 5), "tokens/s": round(cfg.tokens / (ms_f * 1e-3), 1),
+                      "speedup_vs_two_calls": round(ms_step / ms_f, 4),
+                      "note": "lookup and gate in one pass: the gate kernel hashes each token's n-grams and "
+                              "loads the table rows into its operand tiles (no memory-vector array); timed "
+                              "like the step, in the same run"}
     if secondary:
         work = algorithmic(cfg, args.shared_wv)
         gate_tf = work["gate"]["flops"] / (per["gate"] * 1e-3) / 1e12
@@ -771,6 +793,7 @@ def run_workload(args, name, secondary=False):
                                        "hbm_frac": round(lk / PEAK_HBM_GBS, 4)},
                             "gate": {"ms": round(per["gate"], 5), "TFLOP/s": round(gate_tf, 2),
                                      "frac": round(gate_tf / PEAK_BF16_TFLOPS, 4)}},
+                "fused_step": fused_step,
                 "config": workload_desc(cfg, args)}
 
     # the lookup as its separate calls (engram_compress_hash, then engram_gather), for each
@@ -856,6 +879,7 @@ def run_workload(args, name, secondary=False):
         "wall_s_timed": round(t_wall, 4),
         "cache_flush_mb_between_steps": args.flush_mb,
         "kernels": kernels,
+        "fused_step": fused_step,
         "separate_calls": {**separate_calls, "note": "the lookup as engram_compress_hash + engram_gather, and the gate on prepared weights, "
                                                      "timed eagerly in the same run (not part of the step)"},
         "roofline": roofline,

@@ -15,6 +15,8 @@ The functions carry the C names:
 * ``engram_gate_forward`` -- context-aware gating and residual update
   (section 2.3, Eq. 3-4; section 2.4, Eq. 6 for several branches);
   ``fp8=True`` runs both projections on E4M3 codes (section 2.4);
+* ``engram_lookup_gate`` -- the lookup and the gate in one pass, the gate's
+  matrix-core kernel loading the table rows itself (section 2.2 into 2.3);
 * ``engram_lookup_fp8``, ``engram_gate_prepare_fp8``, ``engram_gate_forward_fp8q``
   -- the FP8 gate's operands made once: the lookup quantizing its memory vectors,
   the weights quantized ahead, and the gate on the codes;
@@ -58,7 +60,7 @@ EXPORTS = (
     "engram_compress_hash", "engram_quantize_fp8", "engram_gate_forward_fp8", "engram_lookup",
     "engram_lookup_fp8", "engram_gate_prepare_fp8", "engram_gate_forward_fp8q", "engram_gate_prepare",
     "engram_gate_forward_prepared", "engram_gate_wait_timeouts", "engram_debug_force_gate_timeout",
-    "engram_gate_forward_noalloc",
+    "engram_gate_forward_noalloc", "engram_lookup_gate",
 )
 
 
@@ -114,13 +116,15 @@ def lib() -> ctypes.CDLL:
         L.engram_prefetch_host_cached.argtypes = [P, i64, i32, P, P, i32, i32, P, i32, P, P, P, P, P]
         L.engram_gate_wait_timeouts.argtypes = [ctypes.POINTER(i32), i32]
         L.engram_debug_force_gate_timeout.argtypes = [i32]
+        L.engram_lookup_gate.argtypes = [P, i32, i64, i64, i64, P, i32, P, i32, i32, P, P, i32, P, i32, i32, i32,
+                                         P, P, P, P, P, ctypes.c_float, i32, P, P, P, P, P, P]
         for f in ("engram_compress", "engram_hash", "engram_gather", "engram_gate_forward",
                   "engram_conv_forward", "engram_prefetch_host", "engram_host_alloc", "engram_host_free",
                   "engram_cache_select", "engram_cache_build", "engram_prefetch_host_cached",
                   "engram_compress_hash", "engram_quantize_fp8", "engram_gate_forward_fp8", "engram_lookup",
                   "engram_lookup_fp8", "engram_gate_prepare_fp8", "engram_gate_forward_fp8q",
                   "engram_gate_prepare", "engram_gate_forward_prepared", "engram_gate_wait_timeouts",
-                  "engram_debug_force_gate_timeout", "engram_gate_forward_noalloc"):
+                  "engram_debug_force_gate_timeout", "engram_gate_forward_noalloc", "engram_lookup_gate"):
             getattr(L, f).restype = st
         _lib = L
     return _lib
@@ -296,6 +300,74 @@ def engram_lookup(raw, cmap, orders: Sequence[int], heads: int, mult, tables: Se
                                pad_id, ptrs, w, _edtype(tables[0]), _opt(ids_out, "ids_out", torch.int32),
                                _opt(idx_out, "idx_out", torch.int32), _dev(out, "out", dt),
                                _opt(err_count, "err_count", torch.int32), _stream(stream)))
+    return out
+
+
+def engram_lookup_gate(raw, cmap, orders: Sequence[int], heads: int, mult, tables: Sequence, pad_id: int,
+                       h: Sequence, wk: Sequence, wv: Sequence, gq: Sequence, gk: Sequence, eps: float = 1e-6,
+                       t_begin: int = 0, t_count: Optional[int] = None, out: Optional[Sequence] = None,
+                       gate_out=None, value_out: Optional[Sequence] = None, key_norm: int = KEY_NORM_MEMORY,
+                       ids_out=None, err_count=None, stream=None):
+    """engram_lookup (bf16 tables) followed by engram_gate_forward, in one pass that never
+    stores the memory vectors; the results are those of the two calls bit for bit.
+    Arguments as for those two functions (h, out, value_out: [batch * t_count, d_model])."""
+    import numpy as np
+    import torch
+    batch, ld = raw.shape
+    if t_count is None:
+        t_count = ld - t_begin
+    orders_a = np.ascontiguousarray(orders, dtype=np.int32)
+    mult_a = np.ascontiguousarray(mult, dtype=np.uint64)
+    n_tables = len(orders) * heads
+    if mult_a.shape != (len(orders), heads, max(orders)) or len(tables) != n_tables:
+        raise ValueError("mult must be [n_orders][heads][max_order], one table per (order, head)")
+    w = tables[0].shape[1]
+    for t in tables:
+        if t.shape[1] != w:
+            raise ValueError("all tables need the same width")
+        _dev(t, "table", torch.bfloat16)
+    rows_a = np.array([t.shape[0] for t in tables], dtype=np.uint32)
+    if ids_out is not None and tuple(ids_out.shape) != (batch, ld):
+        raise ValueError("ids_out must be [batch, ld]")
+    n_tok = batch * t_count
+    d_mem = n_tables * w
+    nb = len(h)
+    d_model = h[0].shape[1]
+    if out is None:
+        out = [torch.empty_like(x) for x in h]
+    if not (len(wk) == len(wv) == len(gq) == len(gk) == len(out) == nb):
+        raise ValueError("one h/wk/wv/gq/gk/out per branch")
+    if value_out is not None and len(value_out) != nb:
+        raise ValueError("one value_out entry per branch")
+    for name, seq in (("h", h), ("wk", wk), ("wv", wv), ("gq", gq), ("gk", gk), ("out", out)):
+        for x in seq:
+            _dev(x, name, torch.bfloat16)
+    vals = [x for x in (value_out or []) if x is not None]
+    for x in vals:
+        _dev(x, "value_out", torch.bfloat16)
+    for x in list(h) + list(out) + vals:
+        if tuple(x.shape) != (n_tok, d_model):
+            raise ValueError("h/out/value_out must be [batch * t_count, d_model]")
+    for x in list(wk) + list(wv):
+        if tuple(x.shape) != (d_model, d_mem):
+            raise ValueError("weights must be [d_model, d_mem]")
+    gk_len = d_mem if key_norm == KEY_NORM_MEMORY else d_model
+    for x in gq:
+        if tuple(x.shape) != (d_model,):
+            raise ValueError("gq must be [d_model]")
+    for x in gk:
+        if tuple(x.shape) != (gk_len,):
+            raise ValueError(f"gk must be [{gk_len}] for key_norm {key_norm}")
+    arr = lambda seq: _ptr_array([x.data_ptr() for x in seq])
+    varr = None if value_out is None else _ptr_array([0 if x is None else x.data_ptr() for x in value_out])
+    _check(lib().engram_lookup_gate(_dev(raw, "raw", torch.int32), batch, ld, t_begin, t_count,
+                                    _opt(cmap, "map", torch.int32), 0 if cmap is None else cmap.numel(),
+                                    orders_a.ctypes.data, len(orders), heads, mult_a.ctypes.data,
+                                    rows_a.ctypes.data, pad_id, arr(tables), w, d_model, nb, arr(h), arr(wk),
+                                    arr(wv), arr(gq), arr(gk), float(eps), int(key_norm), arr(out),
+                                    _opt(gate_out, "gate_out", torch.float32), varr,
+                                    _opt(ids_out, "ids_out", torch.int32), _opt(err_count, "err_count", torch.int32),
+                                    _stream(stream)))
     return out
 
 

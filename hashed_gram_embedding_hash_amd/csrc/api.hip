@@ -678,6 +678,60 @@ engram_status engram_gate_forward_prepared(const void* mem, int64_t n_tok, int32
   });
 }
 
+engram_status engram_lookup_gate(const int32_t* raw, int32_t batch, int64_t ld, int64_t t_begin, int64_t t_count,
+                                 const int32_t* map, int32_t vocab, const int32_t* orders, int32_t n_orders,
+                                 int32_t heads, const uint64_t* mult, const uint32_t* rows, int32_t pad_id,
+                                 const void* const* tables, int32_t w, int32_t d_model, int32_t n_branch,
+                                 const void* const* h, const void* const* wk, const void* const* wv,
+                                 const void* const* gq, const void* const* gk, float eps, engram_key_norm key_norm,
+                                 void* const* out, float* gate_out, void* const* value_out, int32_t* ids_out,
+                                 int32_t* err_count, hipStream_t stream) {
+  const char* fn = "engram_lookup_gate";
+  HashArgs hs;
+  bool empty = false;
+  engram_status st = hash_args(fn, raw, batch, ld, t_begin, t_count, map, vocab, orders, n_orders, heads, mult,
+                               rows, pad_id, ids_out, nullptr, err_count, false, hs, &empty);
+  if (st != ENGRAM_OK) return st;
+  const int nt = n_orders * heads;
+  int64_t rows64[ENGRAM_MAX_TABLES];
+  for (int b = 0; b < nt; ++b) rows64[b] = rows[b];
+  const int64_t n_tok = empty ? 0 : (int64_t)batch * t_count;
+  // the lookup's table checks (no index or memory-vector array: stand-ins keep the
+  // null checks quiet)
+  static const int32_t no_idx = 0;
+  alignas(16) static char no_out[16];
+  st = check_gather(fn, &no_idx, n_tok, nt, tables, rows64, w, ENGRAM_BF16, no_out);
+  if (st != ENGRAM_OK) return st;
+  // (check_gather has made w a multiple of 8) a k-step's 64 values of a token then span
+  // at most two tables
+  if (w < 64) return fail(ENGRAM_ERR_UNSUPPORTED, "%s: table rows of %d values; needs at least 64", fn, w);
+  if (ids_out != nullptr && !aligned(ids_out, 4)) return fail(ENGRAM_ERR_INVALID_ARG, "%s: misaligned ids_out", fn);
+  GateArgs a;
+  // the gate's checks; the memory vectors are never stored (table 0 stands in for them)
+  st = gate_args(fn, tables[0], n_tok, nt * w, d_model, n_branch, h, wk, wv, gq, gk, eps, ENGRAM_BF16,
+                 enum_arg(key_norm), out, gate_out, value_out, a);
+  if (st != ENGRAM_OK || n_tok == 0) return st;
+  GatherSrc g;
+  memset(&g, 0, sizeof g);
+  for (int b = 0; b < nt; ++b) {
+    g.tab[b] = (const char*)tables[b];
+    g.rows[b] = hs.rows[b];
+    g.barrett[b] = hs.barrett[b];
+    g.order[b] = hs.order[b];
+    for (int j = 0; j < ENGRAM_MAX_ORDER; ++j) g.mult[b][j] = hs.mult[b][j];
+  }
+  g.n_tables = nt;
+  g.cpr = w / 8;
+  const size_t gate_bytes = gate_bf16_scratch_bytes(a, false);
+  const size_t bytes = gate_bytes + (((size_t)n_tok * sizeof(int4) + 255) & ~(size_t)255);
+  return with_scratch(fn, bytes, stream, [&](void* p) {
+    a.part_dot = (float*)p;
+    g.ids = (const int4*)((char*)p + gate_bytes);
+    launch_gate_ids(hs, (int4*)g.ids, stream);
+    launch_gate_bf16(a, false, stream, false, &g);
+  });
+}
+
 engram_status engram_gate_forward_fp8q(const uint8_t* codes, const float* scales, const float* sumsq, int64_t n_tok,
                                        int32_t d_mem, int32_t d_model, int32_t n_branch, const void* const* h,
                                        const uint8_t* const* wk_codes, const float* const* wk_scales,

@@ -125,11 +125,33 @@ struct GateArgs {
   // spin_limit times (set by launch_gate_bf16)
   int32_t wait_extra, spin_limit;
 };
+// engram_lookup_gate: the bf16 gate reads its memory rows straight from the tables.
+// Position p's row in table b starts at tab[b] + z * cpr * 16 bytes, with
+// z = (XOR_{j < order[b]} x'_{t-j} * mult[b][j] mod 2^64) mod rows[b] and the canonical
+// ids x'_{t-j} of the position in ids[p] (j = 0..3, the pad id before a sequence's
+// start).  The memory vector is the concatenation of the rows (cpr 16-byte chunks each,
+// cpr >= 8, n_tables * cpr * 8 == d_mem).
+struct GatherSrc {
+  const int4* ids;  // [n_tok]
+  const char* tab[ENGRAM_MAX_TABLES];
+  uint64_t mult[ENGRAM_MAX_TABLES][ENGRAM_MAX_ORDER];
+  uint64_t barrett[ENGRAM_MAX_TABLES];  // floor((2^64 - 1) / rows)
+  uint32_t rows[ENGRAM_MAX_TABLES];
+  int32_t order[ENGRAM_MAX_TABLES];
+  int32_t n_tables, cpr;
+};
+// The ids GatherSrc::ids holds, for positions [batch][t_count] of the hashing window of h
+// (compression through h.map as in engram_compress_hash, counted in h.err_count and
+// written to h.ids_out when set).
+void launch_gate_ids(const HashArgs& h, int4* ids, hipStream_t s);
+
 // bf16 path: returns the scratch bytes it needs for these shapes (and sets a.n_ftiles).
 // launch_gate_bf16 expects a.part_dot to point at a scratch block of that size.  With
 // fp8, the projections run on E4M3 codes that it quantizes first (d_mem % 128 == 0).
+// With gs (bf16 only), the memory rows come from the tables gs describes (a.mem unused).
 size_t gate_bf16_scratch_bytes(GateArgs& a, bool fp8, bool prequant = false);
-void launch_gate_bf16(const GateArgs& a, bool fp8, hipStream_t s, bool prequant = false);
+void launch_gate_bf16(const GateArgs& a, bool fp8, hipStream_t s, bool prequant = false,
+                      const GatherSrc* gs = nullptr);
 // The FP8 weights as the gate uses them: E4M3 codes of W_K (with the memory-side key
 // norm, of gq[f] * W_K[f][c] * gk[c] formed in fp32) and of W_V, per branch, with their
 // per-feature scales (one launch of the quantizer per matrix).

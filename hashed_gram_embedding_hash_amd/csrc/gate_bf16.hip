@@ -251,10 +251,16 @@ __device__ __forceinline__ bool decode_tile(const GateArgs& a, int x, int q, Til
 //           fp32 scale per row (per token for e, per feature for the weights), prepared
 //           by the quantization kernels.  A 128-byte ring row then holds 128 k-values,
 //           and each MFMA (32x32x64 E4M3) takes one 64-value half; the feature scales
-//           weight the epilogues from LDS, the token scale joins the reduced scalars.
-template <bool VALUES, bool KEYP, bool SHAREDV, bool F8>
-__device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, char* smem, int x,
+//           weight the epilogues from LDS, the token scale joins the reduced scalars;
+//   GATHER  (bf16) the memory rows are not read from a memory-vector array: each lane
+//           hashes its token's n-grams and its direct loads read the table rows in
+//           place (gs, a GatherSrc; NoGather otherwise).
+struct NoGather {};
+
+template <bool VALUES, bool KEYP, bool SHAREDV, bool F8, bool GATHER, class GS>
+__device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const Tile& tile, char* smem, int x,
                                           int& next_claim) {
+  static_assert(!(GATHER && F8), "the gathering gate is bf16");
   const int PHASE = tile.phase;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -329,6 +335,82 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr)smem;
   const uint32_t wave_dst = lds0 + (uint32_t)(wave * G_INSTR * 1024);
+
+  // ---- GATHER: the memory rows of k-step k are chunks 8 k .. 8 k + 7 of each token's
+  // concatenated row: chunk gO + c of its row in table gT, or past that row's end chunk
+  // gO + c - cpr of its row in table gT + 1 (gO = 8 k - gT * cpr < cpr, and cpr >= 8, so
+  // no k-step reaches a third table).  Lane L of wave w keeps token w * 64 + L's
+  // canonical ids and its row numbers in tables gT and gT + 1, hashing the next table's
+  // as gT advances; instruction i of the wave loads tokens w * 64 + 8 i + L / 8, whose
+  // row numbers it takes from lane 8 i + L / 8 (ds_bpermute).  Memory rows are issued in
+  // k-step order, each k-step's once, so gather_prep walks the tables forward.
+  const uint16_t* gsrc[G_INSTR];  // GATHER: the addresses of the next memory chunk
+  uint32_t gpv0[G_INSTR], gpv1[G_INSTR];
+  int gpo = 0, gpt = 0;
+  uint32_t gx0 = 0, gx1 = 0, gx2 = 0, gx3 = 0, gi0 = 0, gi1 = 0;
+  int gT = 0, gO = 0;
+  auto ghash = [&](int tb) -> uint32_t {
+    if constexpr (GATHER) {
+      const int n = gs.order[tb];
+      uint64_t hv = (uint64_t)gx0 * gs.mult[tb][0];
+      if (n > 1) hv ^= (uint64_t)gx1 * gs.mult[tb][1];
+      if (n > 2) hv ^= (uint64_t)gx2 * gs.mult[tb][2];
+      if (n > 3) hv ^= (uint64_t)gx3 * gs.mult[tb][3];
+      return mod_barrett(hv, gs.rows[tb], gs.barrett[tb]);
+    } else {
+      return 0u;
+    }
+  };
+  // the row numbers of the next k-step's tokens (into v0, v1) and its table and offset;
+  // then the state moves to the k-step after it
+  auto gather_prep = [&](uint32_t (&v0)[G_INSTR], uint32_t (&v1)[G_INSTR], int& o, int& tb) {
+    if constexpr (GATHER) {
+#pragma unroll
+      for (int i = 0; i < G_INSTR; ++i) {
+        const int src = (i * 8 + (lane >> 3)) * 4;
+        v0[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)gi0);
+        v1[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)gi1);
+      }
+      o = gO;
+      tb = gT;
+      gO += 8;
+      if (gO >= gs.cpr) {
+        gO -= gs.cpr;
+        ++gT;
+        gi0 = gi1;
+        gi1 = gT + 1 < gs.n_tables ? ghash(gT + 1) : 0u;
+      }
+    }
+  };
+  // the addresses of instruction i's 16-byte chunks (lane l: logical chunk
+  // (l % 8) ^ row_key(row), as for the memory-vector array)
+  auto gather_addr = [&](const uint32_t (&v0)[G_INSTR], const uint32_t (&v1)[G_INSTR], int o, int tb,
+                         const uint16_t* (&src)[G_INSTR]) {
+    if constexpr (GATHER) {
+      const char* b0 = gs.tab[tb];
+      const char* b1 = gs.tab[tb + 1 < gs.n_tables ? tb + 1 : tb];
+      const int cpr = gs.cpr;
+      const uint32_t rb = (uint32_t)cpr * 16u;
+#pragma unroll
+      for (int i = 0; i < G_INSTR; ++i) {
+        const int r = wave * 64 + i * 8 + (lane >> 3);
+        const int q = o + ((lane & 7) ^ row_key(r));
+        const bool next = q >= cpr;
+        const uint32_t z = next ? v1[i] : v0[i];
+        const char* base = next ? b1 : b0;
+        src[i] = (const uint16_t*)(base + (uint64_t)z * rb + (uint32_t)(next ? q - cpr : q) * 16u);
+      }
+    }
+  };
+  if constexpr (GATHER) {
+    const int4 v = gs.ids[t0 + min(wave * 64 + lane, b_lim)];
+    gx0 = (uint32_t)v.x;
+    gx1 = (uint32_t)v.y;
+    gx2 = (uint32_t)v.z;
+    gx3 = (uint32_t)v.w;
+    gi0 = ghash(0);
+    gi1 = gs.n_tables > 1 ? ghash(1) : 0u;
+  }
 #define ENGRAM_ISSUE(base_, off_, kt_, slot_)                                              \
   do {                                                                                     \
     const uint16_t* src_ = (base_) + (kt_) * BK;                                           \
@@ -372,6 +454,19 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
       if constexpr (F8) {
         if (c & 1) ENGRAM_ISSUE8(Et8, off_b, c >> 1, slot);
         else ENGRAM_ISSUE8(W8, off_a, c >> 1, slot);
+      } else if constexpr (GATHER) {
+        if (c & 1) {
+          uint32_t v0[G_INSTR], v1[G_INSTR];
+          int o, tb;
+          gather_prep(v0, v1, o, tb);
+          const uint16_t* src[G_INSTR];
+          gather_addr(v0, v1, o, tb, src);
+          const uint32_t dst = wave_dst + (uint32_t)(slot * SLOT_BYTES);
+#pragma unroll
+          for (int i = 0; i < G_INSTR; ++i) dma16(src[i], dst + i * 1024);
+        } else {
+          ENGRAM_ISSUE(W, off_a, c >> 1, slot);
+        }
       } else {
         if (c & 1) ENGRAM_ISSUE(Et0, off_b, c >> 1, slot);
         else ENGRAM_ISSUE(W, off_a, c >> 1, slot);
@@ -430,7 +525,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
   // dma_, load instructions q0 .. q0 + 3 of an operand chunk one after every fourth.
   // Spreading the reads (rather than issuing all eight at once) measured 12 % faster:
   // bursts of fragment reads and direct-to-LDS writes contend for the LDS.
-#define ENGRAM_GROUP(bm, br, rs, sa_, sb_, dma_, base_, off_, kt_, slot_, q0)              \
+#define ENGRAM_GROUP(bm, br, rs, sa_, sb_, dma_, gat_, base_, off_, kt_, slot_, q0)        \
   do {                                                                                     \
     const uint16_t* src_ = (base_) + (kt_) * BK;                                           \
     const uint32_t dst_ = wave_dst + (uint32_t)((slot_) * SLOT_BYTES);                     \
@@ -443,7 +538,10 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
         __builtin_amdgcn_sched_barrier(0);                                                 \
       }                                                                                    \
       if ((dma_) && (k_ % MT) == MT - 1) {                                                 \
-        dma16(src_ + off_[(q0) + k_ / MT], dst_ + ((q0) + k_ / MT) * 1024);                \
+        if (GATHER && (gat_))                                                              \
+          dma16(gsrc[(q0) + k_ / MT], dst_ + ((q0) + k_ / MT) * 1024);                     \
+        else                                                                               \
+          dma16(src_ + off_[(q0) + k_ / MT], dst_ + ((q0) + k_ / MT) * 1024);              \
         __builtin_amdgcn_sched_barrier(0);                                                 \
       }                                                                                    \
     }                                                                                      \
@@ -485,8 +583,10 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
   ENGRAM_LOAD_FRAGS(1, 0, SLOT_BYTES, 3);
   ENGRAM_MFMAS(0);
   if (ee_now) ENGRAM_EE(0);
+  if (GATHER && 3 < nk) gather_prep(gpv0, gpv1, gpo, gpt);  // k-step 2, the main loop's first
   wait_vm_lgkm0<G_INSTR>();
   lds_barrier();
+  if (GATHER && 3 < nk) gather_addr(gpv0, gpv1, gpo, gpt, gsrc);
 
   // k-step kt: the MFMAs of sub-step 3 of k-step kt-1 (fragments in registers) cover
   // this step's first fragment reads, each later sub-step's MFMAs cover the next one's
@@ -497,18 +597,22 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
     const int sa_ = ((2 * (kt)) % NSLOT) * SLOT_BYTES;                                     \
     const int sb_ = ((2 * (kt) + 1) % NSLOT) * SLOT_BYTES;                                 \
     __builtin_amdgcn_sched_barrier(0);                                                     \
-    ENGRAM_GROUP(1, 0, 0, sa_, sb_, dma_, b0_, o0_, k0_, s0_, 0);                          \
+    ENGRAM_GROUP(1, 0, 0, sa_, sb_, dma_, true, b0_, o0_, k0_, s0_, 0);                    \
     if (ee_now) ENGRAM_EE(1);                                                              \
     ee_now = ee_wave && ((kt) % a.n_ftiles) == ftile;                                      \
-    ENGRAM_GROUP(0, 1, 1, sa_, sb_, dma_, b0_, o0_, k0_, s0_, 4);                          \
+    ENGRAM_GROUP(0, 1, 1, sa_, sb_, dma_, true, b0_, o0_, k0_, s0_, 4);                    \
     if (ee_now) ENGRAM_EE(0);                                                              \
-    ENGRAM_GROUP(1, 0, 2, sa_, sb_, dma_, b1_, o1_, k1_, s1_, 0);                          \
+    ENGRAM_GROUP(1, 0, 2, sa_, sb_, dma_, false, b1_, o1_, k1_, s1_, 0);                   \
     if (ee_now) ENGRAM_EE(1);                                                              \
-    ENGRAM_GROUP(0, 1, 3, sa_, sb_, dma_, b1_, o1_, k1_, s1_, 4);                          \
+    ENGRAM_GROUP(0, 1, 3, sa_, sb_, dma_, false, b1_, o1_, k1_, s1_, 4);                   \
     if (ee_now) ENGRAM_EE(0);                                                              \
     __builtin_amdgcn_sched_barrier(0);                                                     \
+    /* GATHER: the row numbers of the next iteration's memory chunk, whose LDS */          \
+    /* round trips the wait below covers */                                                \
+    if (GATHER && (kt) + 3 < nk) gather_prep(gpv0, gpv1, gpo, gpt);                        \
     wait_vm_lgkm0<G_INSTR>();                                                              \
     lds_barrier();                                                                         \
+    if (GATHER && (kt) + 3 < nk) gather_addr(gpv0, gpv1, gpo, gpt, gsrc);                  \
   } while (0)
   int kt = 1;
   // chunks 2 kt + 3 (memory rows of k-step kt + 1) and 2 kt + 4 (weight rows of
@@ -998,12 +1102,11 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const Tile& tile, c
 #undef ENGRAM_QSLOT
 }
 
-template <bool VALUES, bool KEYP, bool SHAREDV, bool F8>
-__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gate_persistent_kernel(const GateArgs a) {
-  // the operand ring, then the h tile and the epilogue scratch; between tiles its
-  // first word broadcasts the claimed tile number
-  __shared__ __attribute__((aligned(16))) char smem[SMEM_BYTES];
+// The persistent workgroup: claims tiles from its queue until the queue is exhausted.
+// smem: the operand ring, then the h tile and the epilogue scratch; between tiles its
+// first word broadcasts the claimed tile number.
+template <bool VALUES, bool KEYP, bool SHAREDV, bool F8, bool GATHER, class GS>
+__device__ __forceinline__ void persistent_loop(const GateArgs& a, const GS& gs, char* smem) {
   int* s_tile = reinterpret_cast<int*>(smem);
   const int x = blockIdx.x % NQ;
   int claim = 0;  // thread 0: the tile claimed for after the current one
@@ -1015,12 +1118,27 @@ void gate_persistent_kernel(const GateArgs a) {
     const bool have = decode_tile<SHAREDV>(a, x, *s_tile, t);
     lds_barrier();  // every thread has read the tile number before the ring is refilled
     if (!have) break;
-    gate_tile<VALUES, KEYP, SHAREDV, F8>(a, t, smem, x, claim);
+    gate_tile<VALUES, KEYP, SHAREDV, F8, GATHER>(a, gs, t, smem, x, claim);
     // LDS free for the next tile.  A full barrier: letting a V tile's 128 KB of output
     // stores drain behind the next tile's operand loads measured 8 % slower than
     // finishing them first.
     __syncthreads();
   }
+}
+
+template <bool VALUES, bool KEYP, bool SHAREDV, bool F8>
+__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gate_persistent_kernel(const GateArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[SMEM_BYTES];
+  persistent_loop<VALUES, KEYP, SHAREDV, F8, false>(a, NoGather{}, smem);
+}
+
+// engram_lookup_gate: the same kernel reading its memory rows from the tables.
+template <bool VALUES, bool KEYP, bool SHAREDV>
+__global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gate_gather_kernel(const GateArgs a, const GatherSrc gs) {
+  __shared__ __attribute__((aligned(16))) char smem[SMEM_BYTES];
+  persistent_loop<VALUES, KEYP, SHAREDV, false, true>(a, gs, smem);
 }
 
 // KEYP: the per-feature key gain gq[m][f] * gk[m][f] in fp32 (exact: a product of two
@@ -1132,7 +1250,7 @@ size_t gate_bf16_scratch_bytes(GateArgs& a, bool fp8, bool prequant) {
 // and scales; only the counters and the key gains are prepared here.  prequant, bf16
 // with the memory-side key norm: a.wk already holds the gain-folded key weights
 // (launch_gate_fold); only the counters are cleared.
-void launch_gate_bf16(const GateArgs& a_in, bool fp8, hipStream_t s, bool prequant) {
+void launch_gate_bf16(const GateArgs& a_in, bool fp8, hipStream_t s, bool prequant, const GatherSrc* gs) {
   GateArgs a = a_in;
   const ScratchLayout L = layout_for(a, fp8, prequant);
   const bool shared_v = shared_wv(a);
@@ -1207,6 +1325,21 @@ void launch_gate_bf16(const GateArgs& a_in, bool fp8, hipStream_t s, bool prequa
   bool values = false;
   for (int m = 0; m < a.n_branch; ++m) values = values || a.vout[m] != nullptr;
   const dim3 g((unsigned)grid), b(NTHR);
+  if (gs != nullptr) {
+#define ENGRAM_GATHER_LAUNCH(V_, K_, S_)                                                   \
+  if (values == V_ && keyp == K_ && shared_v == S_)                                        \
+    hipLaunchKernelGGL((gate_gather_kernel<V_, K_, S_>), g, b, 0, s, a, *gs);
+    ENGRAM_GATHER_LAUNCH(false, false, false)
+    ENGRAM_GATHER_LAUNCH(false, false, true)
+    ENGRAM_GATHER_LAUNCH(false, true, false)
+    ENGRAM_GATHER_LAUNCH(false, true, true)
+    ENGRAM_GATHER_LAUNCH(true, false, false)
+    ENGRAM_GATHER_LAUNCH(true, false, true)
+    ENGRAM_GATHER_LAUNCH(true, true, false)
+    ENGRAM_GATHER_LAUNCH(true, true, true)
+#undef ENGRAM_GATHER_LAUNCH
+    return;
+  }
 #define ENGRAM_GATE_LAUNCH(V_, K_, S_, F_)                                                 \
   if (values == V_ && keyp == K_ && shared_v == S_ && fp8 == F_)                           \
     hipLaunchKernelGGL((gate_persistent_kernel<V_, K_, S_, F_>), g, b, 0, s, a);

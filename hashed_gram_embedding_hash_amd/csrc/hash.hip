@@ -70,7 +70,42 @@ __global__ __launch_bounds__(256) void hash_kernel(const HashArgs a) {
   }
 }
 
+// For the gate that gathers its own rows: per position of the window, its canonical id
+// and the three before it (the pad id before the sequence's start), one int4 per
+// position.  Raw ids are mapped as the hash kernel maps them, and each window position's
+// own id is written to ids_out and counted (once) there too.
+__global__ __launch_bounds__(256) void gate_ids_kernel(const HashArgs a, int4* ids) {
+  const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (p >= (int64_t)a.batch * a.t_count) return;
+  const int64_t b = p / a.t_count;
+  const int64_t t = a.t_begin + (p - b * a.t_count);
+  const int32_t* row = a.ids + b * a.ld;
+  int32_t x[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[j] = a.pad_id;
+    if (t - j >= 0) {
+      int32_t v = row[t - j];
+      if (a.map != nullptr) {
+        const bool ok = (uint32_t)v < (uint32_t)a.vocab;
+        v = ok ? a.map[v] : -1;
+        if (j == 0) {
+          if (a.ids_out != nullptr) a.ids_out[b * a.ld + t] = v;
+          if (!ok && a.err_count != nullptr) atomicAdd(a.err_count, 1);
+        }
+      }
+      x[j] = v;
+    }
+  }
+  ids[p] = make_int4(x[0], x[1], x[2], x[3]);
+}
+
 }  // namespace
+
+void launch_gate_ids(const HashArgs& a, int4* ids, hipStream_t s) {
+  const int64_t n = (int64_t)a.batch * a.t_count;
+  hipLaunchKernelGGL(gate_ids_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a, ids);
+}
 
 void launch_hash(const HashArgs& a, hipStream_t s) {
   const uint64_t nblk = (uint64_t)((a.t_count + POS - 1) / POS);

@@ -305,6 +305,31 @@ engram_status engram_gate_forward_prepared(const void* mem, int64_t n_tok, int32
                                            void* const* value_out, hipStream_t stream);
 
 /*
+ * Lookup and gate in one pass, the memory vectors never stored -- section 2.2, Eq. (1)-(2)
+ * feeding section 2.3, Eq. (3)-(4) (and section 2.4, Eq. (6) for several branches):
+ * exactly engram_lookup of raw (bf16 tables) into memory vectors e [batch*t_count][d_mem],
+ * d_mem = n_orders*heads*w, followed by engram_gate_forward(e, batch*t_count, d_mem, ...,
+ * ENGRAM_BF16, key_norm, ...); the outputs are bit-identical to those two calls'.  The
+ * gate's matrix-core kernel hashes each token's n-grams itself and loads the table rows
+ * straight into its operand tiles, so e makes no round trip through device memory.
+ * raw .. w, ids_out, err_count: as for engram_lookup (dtype ENGRAM_BF16; no index output).
+ * d_model .. value_out: as for engram_gate_forward with dtype ENGRAM_BF16 and
+ *         n_tok = batch * t_count; gk[m] is [d_mem] for ENGRAM_KEY_NORM_MEMORY.
+ * Requires what engram_lookup and engram_gate_forward require, and w >= 64
+ * (UNSUPPORTED otherwise).  Uses the library's per-device scratch as
+ * engram_gate_forward does, plus 16 bytes per token.  batch == 0 or t_count == 0 is a
+ * no-op.
+ */
+engram_status engram_lookup_gate(const int32_t* raw, int32_t batch, int64_t ld, int64_t t_begin, int64_t t_count,
+                                 const int32_t* map, int32_t vocab, const int32_t* orders, int32_t n_orders,
+                                 int32_t heads, const uint64_t* mult, const uint32_t* rows, int32_t pad_id,
+                                 const void* const* tables, int32_t w, int32_t d_model, int32_t n_branch,
+                                 const void* const* h, const void* const* wk, const void* const* wv,
+                                 const void* const* gq, const void* const* gk, float eps, engram_key_norm key_norm,
+                                 void* const* out, float* gate_out, void* const* value_out, int32_t* ids_out,
+                                 int32_t* err_count, hipStream_t stream);
+
+/*
  * Short depthwise causal convolution -- section 2.3, Eq. (5): with V~ the
  * gated values of one sequence (value_out of engram_gate_forward), the module's
  * output is Y = SiLU(Conv1D(RMSNorm(V~))) + V~.  engram_gate_forward already

@@ -286,3 +286,31 @@ def test_gate_prepared_argument_errors():
     assert fp(eps=-1.0) == _st("arg")
     assert fp(mem=4100) == _st("arg")               # misaligned memory vectors
     assert fp(n=0, mem=0) == _st("ok")
+
+
+def test_lookup_gate_argument_errors():
+    L = eg.lib()
+    orders = np.array([2, 3], np.int32)
+    mult = np.ones((2, 2, 3), np.uint64)
+    rows = np.full(4, 1009, np.uint32)
+    tabs = (ctypes.c_void_p * 4)(4096, 8192, 12288, 16384)
+    one = (ctypes.c_void_p * 1)(4096)
+    lg = lambda **kw: L.engram_lookup_gate(
+        ctypes.c_void_p(kw.get("raw", 4096)), kw.get("batch", 2), kw.get("ld", 100), kw.get("tb", 0),
+        kw.get("tc", 100), None, 0, orders.ctypes.data, 2, 2, mult.ctypes.data, rows.ctypes.data, 7,
+        kw.get("tabs", tabs), kw.get("w", 80), kw.get("dmod", 2560), kw.get("nb", 1), kw.get("h", one), one, one,
+        one, one, ctypes.c_float(1e-6), kw.get("kn", eg.KEY_NORM_MEMORY), kw.get("out", one), None, None,
+        ctypes.c_void_p(kw.get("ids", 0)), None, None)
+    assert lg(w=32) == _st("unsup")           # rows under 64 values: a k-step would span three tables
+    assert lg(w=12) == _st("unsup")           # 24-byte rows
+    assert lg(w=72) == _st("unsup")           # d_mem = 288, not a multiple of 64
+    assert lg(dmod=2500) == _st("unsup")      # d_model not a multiple of 32
+    assert lg(tb=50, tc=60) == _st("arg")     # window past the row
+    assert lg(tabs=(ctypes.c_void_p * 4)(4096, 8200, 12288, 16384)) == _st("arg")  # misaligned table
+    assert lg(raw=0) == _st("arg")
+    assert lg(nb=0) == _st("arg")
+    assert lg(kn=5) == _st("arg")
+    assert lg(ids=4098) == _st("arg")         # misaligned ids output
+    assert lg(out=(ctypes.c_void_p * 1)(0)) == _st("arg")
+    assert lg(tc=0, raw=0) == _st("ok")
+    assert lg(batch=0, raw=0) == _st("ok")

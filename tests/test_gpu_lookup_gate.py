@@ -1,0 +1,184 @@
+"""GPU parity of engram_lookup_gate: the lookup and the gate in one pass, the gate's
+matrix-core kernel hashing each token's n-grams and loading the table rows into its
+operand tiles itself.
+
+Bar: every output (the updated hidden states, the gates, the gated values, the canonical
+ids and the error count) bit-identical to engram_lookup followed by engram_gate_forward,
+whose parity with the oracle the other GPU tests establish; and, independently, the gate
+against the oracle (gpu_helpers.check_gate's bars) on memory vectors the oracle builds
+from the same raw ids.  The cases span one to 25 k-steps, table rows of 8 to 25 16-byte
+chunks (a k-step then covers up to two tables), orders 1 to 4, ragged token and feature
+tiles, windows, out-of-vocabulary ids, several branches, a shared W_V and both key norms.
+"""
+import numpy as np
+import pytest
+import torch
+
+import hashed_gram_embedding_hash_amd as eg
+import oracle
+import synth
+from gpu_helpers import check_gate, host_view, sentinel_like
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0")
+MEM, PROJ = eg.KEY_NORM_MEMORY, eg.KEY_NORM_PROJECTED
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def _inputs(orders, heads, w, rows, batch, seq, d_model, n_branch, shared, key_norm, seed, table_std=0.5):
+    """Seeded inputs of one case (tables of std 0.5, so that alpha * v is not small next to h;
+    the gated values, checked on their own where a case asks for them, bound the update)."""
+    g = torch.Generator().manual_seed(seed)
+    vocab, vocab_c = 3000, 2200
+    nt = len(orders) * heads
+    d_mem = nt * w
+    raw = torch.randint(0, vocab, (batch, seq), generator=g, dtype=torch.int32)
+    bad = torch.rand((batch, seq), generator=g) < 0.01  # out-of-vocabulary raw ids
+    raw[bad] = vocab + 7
+    cmap = torch.randint(0, vocab_c, (vocab,), generator=g, dtype=torch.int32)
+    mult = (torch.randint(0, 2 ** 62, (len(orders), heads, max(orders)), generator=g, dtype=torch.int64) * 2 + 1)
+    tables = [(torch.randn((rows + b, w), generator=g) * table_std).to(torch.bfloat16) for b in range(nt)]
+    n_tok = batch * seq
+    h = [torch.randn((n_tok, d_model), generator=g).to(torch.bfloat16) for _ in range(n_branch)]
+    wk = [(torch.randn((d_model, d_mem), generator=g) / d_mem ** 0.5).to(torch.bfloat16) for _ in range(n_branch)]
+    wv0 = [(torch.randn((d_model, d_mem), generator=g) / d_mem ** 0.5).to(torch.bfloat16) for _ in range(n_branch)]
+    gk_len = d_mem if key_norm == MEM else d_model
+    gq = [(1 + 0.2 * torch.randn(d_model, generator=g)).to(torch.bfloat16) for _ in range(n_branch)]
+    gk = [(1 + 0.2 * torch.randn(gk_len, generator=g)).to(torch.bfloat16) for _ in range(n_branch)]
+    return dict(raw=raw, cmap=cmap, mult=mult.numpy().view(np.uint64), tables=tables, h=h, wk=wk, wv0=wv0, gq=gq,
+                gk=gk, vocab_c=vocab_c)
+
+
+def _dev(x):
+    return [t.to(DEV) for t in x] if isinstance(x, list) else x.to(DEV)
+
+
+CASES = [
+    # orders, heads, w, rows, batch, seq, t_begin, d_model, n_branch, shared, key_norm, values
+    ((2, 3), 8, 80, 4099, 3, 700, 0, 640, 1, False, MEM, False),      # 20 k-steps, ragged tiles
+    ((2,), 2, 64, 1021, 2, 300, 5, 256, 3, True, MEM, True),          # 2 k-steps, shared W_V, window
+    ((1, 2, 3, 4), 2, 72, 2003, 2, 257, 0, 320, 2, False, PROJ, True),  # 9 chunks a row, orders 1-4
+    ((2,), 1, 64, 509, 1, 1, 0, 64, 1, False, MEM, False),            # one token, one k-step
+    ((1, 2, 3), 1, 64, 509, 2, 129, 3, 128, 1, False, MEM, True),     # 3 k-steps
+    ((2, 3), 2, 64, 2017, 1, 515, 0, 96, 2, False, MEM, False),       # 4 k-steps (one main-loop step)
+    ((2, 3), 4, 128, 8191, 2, 1000, 0, 512, 2, True, PROJ, False),    # 16 chunks a row, shared, projected
+    ((3,), 8, 200, 3001, 1, 513, 0, 256, 1, False, MEM, False),       # 25 chunks a row, 25 k-steps
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"case{i}" for i in range(len(CASES))])
+def test_lookup_gate_bit_identical_to_lookup_then_gate(case):
+    orders, heads, w, rows, batch, ld, t_begin, d_model, nb, shared, key_norm, values = case
+    t_count = ld - t_begin
+    say(f"lookup_gate case: orders {orders} x {heads} heads, w {w}, {batch} x {t_count} tokens (t_begin "
+        f"{t_begin}), d_model {d_model}, {nb} branches, shared W_V {shared}, key_norm {key_norm}")
+    inp = _inputs(orders, heads, w, rows, batch, ld, d_model, nb, shared, key_norm, seed=CASES.index(case))
+    raw, cmap, tables = _dev(inp["raw"]), _dev(inp["cmap"]), _dev(inp["tables"])
+    n_tok = batch * t_count
+    h = [x[: n_tok].contiguous() for x in _dev(inp["h"])]
+    wk, gq, gk = _dev(inp["wk"]), _dev(inp["gq"]), _dev(inp["gk"])
+    wv = [_dev(inp["wv0"][0])] * nb if shared else _dev(inp["wv0"])
+    pad = inp["vocab_c"]
+
+    def outputs():
+        return dict(out=[sentinel_like(torch.empty_like(x)) for x in h],
+                    alpha=sentinel_like(torch.empty((nb, n_tok), dtype=torch.float32, device=DEV)),
+                    vals=[sentinel_like(torch.empty_like(x)) for x in h] if values else None,
+                    ids=sentinel_like(torch.empty((batch, ld), dtype=torch.int32, device=DEV)),
+                    err=torch.zeros(1, dtype=torch.int32, device=DEV))
+
+    ref = outputs()
+    mem = eg.engram_lookup(raw, cmap, orders, heads, inp["mult"], tables, pad, t_begin=t_begin, t_count=t_count,
+                           ids_out=ref["ids"], err_count=ref["err"])
+    eg.engram_gate_forward(mem, h, wk, wv, gq, gk, 1e-6, out=ref["out"], gate_out=ref["alpha"],
+                           value_out=ref["vals"], key_norm=key_norm)
+    got = outputs()
+    eg.engram_lookup_gate(raw, cmap, orders, heads, inp["mult"], tables, pad, h, wk, wv, gq, gk, 1e-6,
+                          t_begin=t_begin, t_count=t_count, out=got["out"], gate_out=got["alpha"],
+                          value_out=got["vals"], key_norm=key_norm, ids_out=got["ids"], err_count=got["err"])
+    torch.cuda.synchronize()
+    say(f"  {int(got['err'].item())} out-of-vocabulary ids")
+    assert int(got["err"].item()) == int(ref["err"].item())
+    assert int(ref["err"].item()) > 0 or n_tok < 50
+    # the window's ids are written; positions before t_begin keep their sentinel in both
+    assert torch.equal(got["ids"], ref["ids"])
+    assert torch.equal(got["alpha"].view(torch.int32), ref["alpha"].view(torch.int32))
+    assert not torch.isnan(got["alpha"]).any()
+    for m in range(nb):
+        assert torch.equal(got["out"][m].view(torch.int16), ref["out"][m].view(torch.int16)), f"branch {m}"
+        if values:
+            assert torch.equal(got["vals"][m].view(torch.int16), ref["vals"][m].view(torch.int16)), f"values {m}"
+    say("  bit-identical to engram_lookup + engram_gate_forward")
+
+    # independently: the oracle's memory vectors from the same raw ids, then its gate
+    if n_tok <= 2100:
+        raw_h, cmap_h = inp["raw"].numpy(), inp["cmap"].numpy()
+        ids_o, _ = oracle.compress(raw_h, cmap_h)
+        rows_u32 = np.array([t.shape[0] for t in inp["tables"]], np.uint32)
+        idx_o = oracle.hash_ids(ids_o, orders, heads, inp["mult"], rows_u32, pad, t_begin=t_begin, t_count=t_count)
+        e_o = oracle.gather(idx_o, [host_view(t) for t in inp["tables"]])
+        for m in range(nb):
+            check_gate(f"branch {m}", got["out"][m].float().cpu().numpy(), got["alpha"][m].cpu().numpy(), e_o,
+                       host_view(h[m]), host_view(inp["wk"][m]), host_view(inp["wv0"][0 if shared else m]),
+                       host_view(inp["gq"][m]), host_view(inp["gk"][m]), 1e-6, key_norm=key_norm,
+                       vals=got["vals"][m].float().cpu().numpy() if values else None, say=say)
+
+
+def test_lookup_gate_small_config_against_oracle_sampled():
+    """The small workload (16 tables x 1,000,003 rows, 16,384 tokens, d_model 2560): every
+    output bit-identical to the two calls, and sampled tokens against the oracle."""
+    from gpu_helpers import check_gate_tokens, oracle_ids_idx, oracle_memory, sample_tokens
+    from hashed_gram_embedding_hash_amd.pipeline import EngramLayer
+    cfg = synth.CONFIGS["small"]
+    say(f"lookup_gate on the small workload: {cfg.tokens} tokens")
+    inp = synth.device_inputs(cfg, DEV)
+    layer = EngramLayer(inp["map"], cfg.orders, cfg.heads, inp["mult"], inp["tables"], inp["wk"], inp["wv"],
+                        inp["gq"], inp["gk"], cfg.eps, pad_id=cfg.vocab_c)
+    ref = [torch.empty_like(x) for x in inp["h"]]
+    ref_a = torch.empty((cfg.n_branch, cfg.tokens), dtype=torch.float32, device=DEV)
+    layer(inp["raw"], inp["h"], out=ref, gate_out=ref_a)
+    got = [sentinel_like(torch.empty_like(x)) for x in inp["h"]]
+    got_a = sentinel_like(torch.empty_like(ref_a))
+    eg.engram_lookup_gate(inp["raw"], inp["map"], cfg.orders, cfg.heads, inp["mult"], inp["tables"], cfg.vocab_c,
+                          inp["h"], inp["wk"], inp["wv"], inp["gq"], inp["gk"], cfg.eps, out=got, gate_out=got_a)
+    torch.cuda.synchronize()
+    assert torch.equal(got_a.view(torch.int32), ref_a.view(torch.int32))
+    for m in range(cfg.n_branch):
+        assert torch.equal(got[m].view(torch.int16), ref[m].view(torch.int16))
+    say("  bit-identical to the two calls")
+    raw_h = inp["raw"].cpu().numpy()
+    _, idx = oracle_ids_idx(cfg, raw_h)
+    tokens = sample_tokens(cfg, 96, seed=3)
+    e = oracle_memory(cfg, idx[tokens])
+    for m in range(cfg.n_branch):
+        check_gate_tokens(f"branch {m}", cfg, m, got[m][tokens].float().cpu().numpy(), got_a[m][tokens].cpu().numpy(),
+                          e, tokens, say=say)
+
+
+def test_lookup_gate_large_workload_bit_identical():
+    """The large workload (26 GB of tables, 262,144 tokens, d_model 4096, two branches) in
+    the benchmark's launch configuration: every output bit-identical to the two calls."""
+    from hashed_gram_embedding_hash_amd.pipeline import EngramLayer
+    cfg = synth.CONFIGS["large"]
+    say(f"lookup_gate on the large workload: {cfg.tokens} tokens, {cfg.n_tables} x {cfg.rows} rows")
+    inp = synth.device_inputs(cfg, DEV)
+    layer = EngramLayer(inp["map"], cfg.orders, cfg.heads, inp["mult"], inp["tables"], inp["wk"], inp["wv"],
+                        inp["gq"], inp["gk"], cfg.eps, pad_id=cfg.vocab_c)
+    ref = [torch.empty_like(x) for x in inp["h"]]
+    ref_a = torch.empty((cfg.n_branch, cfg.tokens), dtype=torch.float32, device=DEV)
+    layer(inp["raw"], inp["h"], out=ref, gate_out=ref_a)
+    torch.cuda.synchronize()
+    say("  two-call pass done")
+    got = [sentinel_like(torch.empty_like(x)) for x in inp["h"]]
+    got_a = sentinel_like(torch.empty_like(ref_a))
+    eg.engram_lookup_gate(inp["raw"], inp["map"], cfg.orders, cfg.heads, inp["mult"], inp["tables"], cfg.vocab_c,
+                          inp["h"], inp["wk"], inp["wv"], inp["gq"], inp["gk"], cfg.eps, out=got, gate_out=got_a)
+    torch.cuda.synchronize()
+    say("  fused pass done")
+    assert torch.equal(got_a.view(torch.int32), ref_a.view(torch.int32))
+    for m in range(cfg.n_branch):
+        assert torch.equal(got[m].view(torch.int16), ref[m].view(torch.int16)), f"branch {m}"
+    say("  bit-identical to the two calls")
