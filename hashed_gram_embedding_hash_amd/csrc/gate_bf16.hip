@@ -203,22 +203,26 @@ struct Tile {
 // has n_branch times fewer tiles; its tiles carry m = 0.
 constexpr int TT_GROUP = 4;   // token tiles per group
 constexpr int CB = 8;         // (branch, feature tile) combinations per block
+// the gathering gate (its memory tiles are random table rows): the same, its own sizes
+constexpr int TT_GROUP_G = 4;
+constexpr int CB_G = 8;
 
 // Tile r of a phase whose tiles are the n_tt token tiles of a queue x `per` combinations
-// (branch, feature tile), ordered so that 32 consecutive tiles cover TT_GROUP token tiles x
-// CB combinations (each memory tile shared by CB tiles, each weight panel by TT_GROUP).
+// (branch, feature tile), ordered so that 32 consecutive tiles cover TTG token tiles x CBN
+// combinations (each memory tile shared by CBN tiles, each weight panel by TTG).
+template <int TTG, int CBN>
 __device__ __forceinline__ void blocked(int r, int n_tt, int per, int& tt, int& combo) {
-  const int g = r / (TT_GROUP * per);
-  const int ntt = min(TT_GROUP, n_tt - g * TT_GROUP);
-  const int rg = r - g * TT_GROUP * per;
-  const int cb = rg / (ntt * CB);
-  const int cbs = min(CB, per - cb * CB);
-  const int rb = rg - cb * ntt * CB;
-  tt = g * TT_GROUP + rb / cbs;
-  combo = cb * CB + rb % cbs;
+  const int g = r / (TTG * per);
+  const int ntt = min(TTG, n_tt - g * TTG);
+  const int rg = r - g * TTG * per;
+  const int cb = rg / (ntt * CBN);
+  const int cbs = min(CBN, per - cb * CBN);
+  const int rb = rg - cb * ntt * CBN;
+  tt = g * TTG + rb / cbs;
+  combo = cb * CBN + rb % cbs;
 }
 
-template <bool SHAREDV>
+template <bool SHAREDV, bool GATHER>
 __device__ __forceinline__ bool decode_tile(const GateArgs& a, int x, int q, Tile& t) {
   const int n_tt = a.n_ttiles > x ? (a.n_ttiles - x + NQ - 1) / NQ : 0;  // token tiles of queue x
   const int per_tt = a.n_branch * a.n_ftiles;
@@ -229,7 +233,8 @@ __device__ __forceinline__ bool decode_tile(const GateArgs& a, int x, int q, Til
   const int r = q - (t.phase == PHASE_V ? per_k : 0);
   const int per = (SHAREDV && t.phase == PHASE_V) ? a.n_ftiles : per_tt;
   int tl, combo;
-  blocked(r, n_tt, per, tl, combo);
+  if constexpr (GATHER) blocked<TT_GROUP_G, CB_G>(r, n_tt, per, tl, combo);
+  else blocked<TT_GROUP, CB>(r, n_tt, per, tl, combo);
   t.m = combo / a.n_ftiles;
   t.ftile = combo - t.m * a.n_ftiles;
   t.ttile = tl * NQ + x;
@@ -343,27 +348,50 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
   // canonical ids and its row numbers in tables gT and gT + 1, hashing the next table's
   // as gT advances; instruction i of the wave loads tokens w * 64 + 8 i + L / 8, whose
   // row numbers it takes from lane 8 i + L / 8 (ds_bpermute).  Memory rows are issued in
-  // k-step order, each k-step's once, so gather_prep walks the tables forward.
-  const uint16_t* gsrc[G_INSTR];  // GATHER: the addresses of the next memory chunk
-  uint32_t gpv0[G_INSTR], gpv1[G_INSTR];
-  int gpo = 0, gpt = 0;
-  uint32_t gx0 = 0, gx1 = 0, gx2 = 0, gx3 = 0, gi0 = 0, gi1 = 0;
-  int gT = 0, gO = 0;
-  auto ghash = [&](int tb) -> uint32_t {
-    if constexpr (GATHER) {
-      const int n = gs.order[tb];
-      uint64_t hv = (uint64_t)gx0 * gs.mult[tb][0];
-      if (n > 1) hv ^= (uint64_t)gx1 * gs.mult[tb][1];
-      if (n > 2) hv ^= (uint64_t)gx2 * gs.mult[tb][2];
-      if (n > 3) hv ^= (uint64_t)gx3 * gs.mult[tb][3];
-      return mod_barrett(hv, gs.rows[tb], gs.barrett[tb]);
-    } else {
-      return 0u;
-    }
+  // k-step order, each k-step's once, and each k-step's preparation is three steps:
+  //   gather_prep   the permutes (LDS operations only);
+  //   gather_fetch  the scalar loads of the tables' bases and, if the state will enter a
+  //                 new table, that table's hash constants; waited for at once (an
+  //                 outstanding scalar load would turn every later LDS wait into a full
+  //                 one), so the main loop calls it just before the end-of-k-step wait,
+  //                 which waits for everything anyway;
+  //   gather_step   the state moves on, hashing with the fetched constants.
+  // In the main loop the permutes for the next iteration go out once this iteration's
+  // memory loads are issued, and each load's address is formed right before it, in the
+  // shadow of an MFMA.
+  struct GHash {
+    uint64_t m0, m1, m2, m3, bar;
+    uint32_t rows;
+    int order;
+    bool adv;
   };
-  // the row numbers of the next k-step's tokens (into v0, v1) and its table and offset;
-  // then the state moves to the k-step after it
-  auto gather_prep = [&](uint32_t (&v0)[G_INSTR], uint32_t (&v1)[G_INSTR], int& o, int& tb) {
+  uint32_t gpv0[G_INSTR], gpv1[G_INSTR];  // row numbers of the next memory chunk
+  int gpo = 0;                            // ... its offset in its first table
+  const char* gpb[2] = {nullptr, nullptr};  // ... the bases of its two tables
+  GHash gph{};                            // ... and what the state needs after it
+  uint32_t gx0 = 0, gx1 = 0, gx2 = 0, gx3 = 0, gi0 = 0, gi1 = 0;
+  int gT = 0, gO = 0, gcpr = 8, gnt = 1;
+  auto hash_row = [&](const GHash& c) -> uint32_t {
+    uint64_t hv = (uint64_t)gx0 * c.m0;
+    if (c.order > 1) hv ^= (uint64_t)gx1 * c.m1;
+    if (c.order > 2) hv ^= (uint64_t)gx2 * c.m2;
+    if (c.order > 3) hv ^= (uint64_t)gx3 * c.m3;
+    return mod_barrett(hv, c.rows, c.bar);
+  };
+  auto hash_consts = [&](int tb) -> GHash {
+    GHash c{};
+    if constexpr (GATHER) {
+      c.m0 = gs.mult[tb][0];
+      c.m1 = gs.mult[tb][1];
+      c.m2 = gs.mult[tb][2];
+      c.m3 = gs.mult[tb][3];
+      c.bar = gs.barrett[tb];
+      c.rows = gs.rows[tb];
+      c.order = gs.order[tb];
+    }
+    return c;
+  };
+  auto gather_prep = [&](uint32_t (&v0)[G_INSTR], uint32_t (&v1)[G_INSTR], int& o) {
     if constexpr (GATHER) {
 #pragma unroll
       for (int i = 0; i < G_INSTR; ++i) {
@@ -372,44 +400,62 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
         v1[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)gi1);
       }
       o = gO;
-      tb = gT;
+    }
+  };
+  // (the fetched values are made opaque wave-uniform values: a per-lane choice between
+  // the two bases must select values, not become a per-lane load)
+  auto gather_fetch = [&](const char* (&base)[2], GHash& c) {
+    if constexpr (GATHER) {
+      base[0] = gs.tab[gT];
+      base[1] = gs.tab[gT + 1 < gnt ? gT + 1 : gT];
+      c.adv = gO + 8 >= gcpr;
+      if (c.adv && gT + 2 < gnt) {
+        const GHash h = hash_consts(gT + 2);
+        c.m0 = h.m0;
+        c.m1 = h.m1;
+        c.m2 = h.m2;
+        c.m3 = h.m3;
+        c.bar = h.bar;
+        c.rows = h.rows;
+        c.order = h.order;
+      }
+      asm volatile("" : "+s"(base[0]), "+s"(base[1]), "+s"(c.m0), "+s"(c.m1), "+s"(c.m2), "+s"(c.m3),
+                   "+s"(c.bar), "+s"(c.rows), "+s"(c.order));
+    }
+  };
+  auto gather_step = [&](const GHash& c) {
+    if constexpr (GATHER) {
       gO += 8;
-      if (gO >= gs.cpr) {
-        gO -= gs.cpr;
+      if (c.adv) {
+        gO -= gcpr;
         ++gT;
         gi0 = gi1;
-        gi1 = gT + 1 < gs.n_tables ? ghash(gT + 1) : 0u;
+        gi1 = gT + 1 < gnt ? hash_row(c) : 0u;
       }
     }
   };
-  // the addresses of instruction i's 16-byte chunks (lane l: logical chunk
+  // the address of load instruction i's 16-byte chunk (lane l: logical chunk
   // (l % 8) ^ row_key(row), as for the memory-vector array)
-  auto gather_addr = [&](const uint32_t (&v0)[G_INSTR], const uint32_t (&v1)[G_INSTR], int o, int tb,
-                         const uint16_t* (&src)[G_INSTR]) {
-    if constexpr (GATHER) {
-      const char* b0 = gs.tab[tb];
-      const char* b1 = gs.tab[tb + 1 < gs.n_tables ? tb + 1 : tb];
-      const int cpr = gs.cpr;
-      const uint32_t rb = (uint32_t)cpr * 16u;
-#pragma unroll
-      for (int i = 0; i < G_INSTR; ++i) {
-        const int r = wave * 64 + i * 8 + (lane >> 3);
-        const int q = o + ((lane & 7) ^ row_key(r));
-        const bool next = q >= cpr;
-        const uint32_t z = next ? v1[i] : v0[i];
-        const char* base = next ? b1 : b0;
-        src[i] = (const uint16_t*)(base + (uint64_t)z * rb + (uint32_t)(next ? q - cpr : q) * 16u);
-      }
-    }
+  auto gather_addr = [&](int i, const uint32_t (&v0)[G_INSTR], const uint32_t (&v1)[G_INSTR], int o,
+                         const char* const (&base)[2]) -> const uint16_t* {
+    const int r = wave * 64 + i * 8 + (lane >> 3);
+    const int q = o + ((lane & 7) ^ row_key(r));
+    const bool next = q >= gcpr;
+    const uint32_t z = next ? v1[i] : v0[i];
+    const char* bp = next ? base[1] : base[0];
+    return (const uint16_t*)(bp + (uint64_t)z * ((uint32_t)gcpr * 16u) + (uint32_t)(next ? q - gcpr : q) * 16u);
   };
   if constexpr (GATHER) {
+    gcpr = gs.cpr;
+    gnt = gs.n_tables;
+    asm volatile("" : "+s"(gcpr), "+s"(gnt));
     const int4 v = gs.ids[t0 + min(wave * 64 + lane, b_lim)];
     gx0 = (uint32_t)v.x;
     gx1 = (uint32_t)v.y;
     gx2 = (uint32_t)v.z;
     gx3 = (uint32_t)v.w;
-    gi0 = ghash(0);
-    gi1 = gs.n_tables > 1 ? ghash(1) : 0u;
+    gi0 = hash_row(hash_consts(0));
+    gi1 = gnt > 1 ? hash_row(hash_consts(1)) : 0u;
   }
 #define ENGRAM_ISSUE(base_, off_, kt_, slot_)                                              \
   do {                                                                                     \
@@ -457,13 +503,15 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
       } else if constexpr (GATHER) {
         if (c & 1) {
           uint32_t v0[G_INSTR], v1[G_INSTR];
-          int o, tb;
-          gather_prep(v0, v1, o, tb);
-          const uint16_t* src[G_INSTR];
-          gather_addr(v0, v1, o, tb, src);
+          int o;
+          const char* base[2];
+          GHash c{};
+          gather_prep(v0, v1, o);
+          gather_fetch(base, c);
+          gather_step(c);
           const uint32_t dst = wave_dst + (uint32_t)(slot * SLOT_BYTES);
 #pragma unroll
-          for (int i = 0; i < G_INSTR; ++i) dma16(src[i], dst + i * 1024);
+          for (int i = 0; i < G_INSTR; ++i) dma16(gather_addr(i, v0, v1, o, base), dst + i * 1024);
         } else {
           ENGRAM_ISSUE(W, off_a, c >> 1, slot);
         }
@@ -539,7 +587,8 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
       }                                                                                    \
       if ((dma_) && (k_ % MT) == MT - 1) {                                                 \
         if (GATHER && (gat_))                                                              \
-          dma16(gsrc[(q0) + k_ / MT], dst_ + ((q0) + k_ / MT) * 1024);                     \
+          dma16(gather_addr((q0) + k_ / MT, gpv0, gpv1, gpo, gpb),                         \
+                dst_ + ((q0) + k_ / MT) * 1024);                                           \
         else                                                                               \
           dma16(src_ + off_[(q0) + k_ / MT], dst_ + ((q0) + k_ / MT) * 1024);              \
         __builtin_amdgcn_sched_barrier(0);                                                 \
@@ -580,13 +629,14 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
   ENGRAM_LOAD_FRAGS(0, 0, SLOT_BYTES, 2);
   ENGRAM_MFMAS(1);
   if (ee_now) ENGRAM_EE(1);
+  if (GATHER && 3 < nk) gather_prep(gpv0, gpv1, gpo);  // k-step 2, the main loop's first
   ENGRAM_LOAD_FRAGS(1, 0, SLOT_BYTES, 3);
   ENGRAM_MFMAS(0);
   if (ee_now) ENGRAM_EE(0);
-  if (GATHER && 3 < nk) gather_prep(gpv0, gpv1, gpo, gpt);  // k-step 2, the main loop's first
+  if (GATHER && 3 < nk) gather_fetch(gpb, gph);
   wait_vm_lgkm0<G_INSTR>();
   lds_barrier();
-  if (GATHER && 3 < nk) gather_addr(gpv0, gpv1, gpo, gpt, gsrc);
+  if (GATHER && 3 < nk) gather_step(gph);
 
   // k-step kt: the MFMAs of sub-step 3 of k-step kt-1 (fragments in registers) cover
   // this step's first fragment reads, each later sub-step's MFMAs cover the next one's
@@ -602,17 +652,17 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
     ee_now = ee_wave && ((kt) % a.n_ftiles) == ftile;                                      \
     ENGRAM_GROUP(0, 1, 1, sa_, sb_, dma_, true, b0_, o0_, k0_, s0_, 4);                    \
     if (ee_now) ENGRAM_EE(0);                                                              \
+    /* GATHER: the next iteration's row numbers; the wait at the end covers them */      \
+    if (GATHER && (kt) + 3 < nk) gather_prep(gpv0, gpv1, gpo);                             \
     ENGRAM_GROUP(1, 0, 2, sa_, sb_, dma_, false, b1_, o1_, k1_, s1_, 0);                   \
     if (ee_now) ENGRAM_EE(1);                                                              \
     ENGRAM_GROUP(0, 1, 3, sa_, sb_, dma_, false, b1_, o1_, k1_, s1_, 4);                   \
     if (ee_now) ENGRAM_EE(0);                                                              \
     __builtin_amdgcn_sched_barrier(0);                                                     \
-    /* GATHER: the row numbers of the next iteration's memory chunk, whose LDS */          \
-    /* round trips the wait below covers */                                                \
-    if (GATHER && (kt) + 3 < nk) gather_prep(gpv0, gpv1, gpo, gpt);                        \
+    if (GATHER && (kt) + 3 < nk) gather_fetch(gpb, gph);                                   \
     wait_vm_lgkm0<G_INSTR>();                                                              \
     lds_barrier();                                                                         \
-    if (GATHER && (kt) + 3 < nk) gather_addr(gpv0, gpv1, gpo, gpt, gsrc);                  \
+    if (GATHER && (kt) + 3 < nk) gather_step(gph);                                         \
   } while (0)
   int kt = 1;
   // chunks 2 kt + 3 (memory rows of k-step kt + 1) and 2 kt + 4 (weight rows of
@@ -1115,7 +1165,7 @@ __device__ __forceinline__ void persistent_loop(const GateArgs& a, const GS& gs,
     if (threadIdx.x == 0) *s_tile = claim;
     lds_barrier();
     Tile t;
-    const bool have = decode_tile<SHAREDV>(a, x, *s_tile, t);
+    const bool have = decode_tile<SHAREDV, GATHER>(a, x, *s_tile, t);
     lds_barrier();  // every thread has read the tile number before the ring is refilled
     if (!have) break;
     gate_tile<VALUES, KEYP, SHAREDV, F8, GATHER>(a, gs, t, smem, x, claim);
