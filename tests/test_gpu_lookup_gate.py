@@ -182,3 +182,59 @@ def test_lookup_gate_large_workload_bit_identical():
     for m in range(cfg.n_branch):
         assert torch.equal(got[m].view(torch.int16), ref[m].view(torch.int16)), f"branch {m}"
     say("  bit-identical to the two calls")
+
+
+def test_lookup_gate_graph_replay_equals_eager():
+    """engram_lookup_gate (three kernels: ids, key-weight fold, gathering gate) captured in a
+    HIP graph: every replay, with eager calls on other ids in between (they share the
+    library's scratch), reproduces the eager result bit for bit, gates and gated values
+    included."""
+    orders, heads, w, rows, batch, ld, d_model, nb = (2, 3), 4, 80, 4099, 2, 600, 512, 2
+    say("graph replay of engram_lookup_gate")
+    inp = _inputs(orders, heads, w, rows, batch, ld, d_model, nb, False, MEM, seed=77)
+    raw, cmap, tables = _dev(inp["raw"]), _dev(inp["cmap"]), _dev(inp["tables"])
+    h, wk, wv = _dev(inp["h"]), _dev(inp["wk"]), _dev(inp["wv0"])
+    gq, gk = _dev(inp["gq"]), _dev(inp["gk"])
+    pad = inp["vocab_c"]
+    n_tok = batch * ld
+
+    def call(ids, out, alpha, vals):
+        eg.engram_lookup_gate(ids, cmap, orders, heads, inp["mult"], tables, pad, h, wk, wv, gq, gk, 1e-6,
+                              out=out, gate_out=alpha, value_out=vals)
+
+    def bufs():
+        return ([torch.empty_like(x) for x in h], torch.empty((nb, n_tok), dtype=torch.float32, device=DEV),
+                [torch.empty_like(x) for x in h])
+
+    want = bufs()
+    call(raw, *want)
+    raw2 = torch.roll(raw, 5, dims=1).contiguous()
+    other = bufs()
+    call(raw2, *other)
+    torch.cuda.synchronize()
+    assert not torch.equal(other[0][0], want[0][0])
+    got = bufs()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call(raw, *got)                    # the scratch is sized on the capture stream
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call(raw, *got)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for x in got[0] + got[2]:
+            sentinel_like(x)
+        sentinel_like(got[1])
+        eager = bufs()
+        call(raw2, *eager)                 # eager work on the same scratch in between
+        torch.cuda.synchronize()
+        assert torch.equal(eager[0][0].view(torch.int16), other[0][0].view(torch.int16)), rep
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(got[1].view(torch.int32), want[1].view(torch.int32)), rep
+        for m in range(nb):
+            assert torch.equal(got[0][m].view(torch.int16), want[0][m].view(torch.int16)), (rep, m)
+            assert torch.equal(got[2][m].view(torch.int16), want[2][m].view(torch.int16)), (rep, m)
+    say("  three replays bit-identical to the eager call")
