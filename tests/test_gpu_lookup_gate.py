@@ -238,3 +238,29 @@ def test_lookup_gate_graph_replay_equals_eager():
             assert torch.equal(got[0][m].view(torch.int16), want[0][m].view(torch.int16)), (rep, m)
             assert torch.equal(got[2][m].view(torch.int16), want[2][m].view(torch.int16)), (rep, m)
     say("  three replays bit-identical to the eager call")
+
+
+def test_lookup_gate_no_map_most_tables_and_branches():
+    """Canonical ids passed straight in (no compression map), the most tables a call takes
+    (32: orders 1-4 x 8 heads, 64-value rows, d_mem 2048) and the most branches (8, in place),
+    against the two calls bit for bit."""
+    orders, heads, w, rows, batch, ld, d_model, nb = (1, 2, 3, 4), 8, 64, 997, 3, 111, 64, 8
+    say("lookup_gate: no map, 32 tables, 8 branches in place")
+    inp = _inputs(orders, heads, w, rows, batch, ld, d_model, nb, False, MEM, seed=91)
+    raw = (inp["raw"] % inp["vocab_c"]).to(DEV)           # canonical ids already
+    tables = _dev(inp["tables"])
+    wk, wv, gq, gk = _dev(inp["wk"]), _dev(inp["wv0"]), _dev(inp["gq"]), _dev(inp["gk"])
+    pad = inp["vocab_c"]
+    h_ref = _dev(inp["h"])
+    h_got = [x.clone() for x in h_ref]
+    a_ref = torch.empty((nb, batch * ld), dtype=torch.float32, device=DEV)
+    a_got = sentinel_like(torch.empty_like(a_ref))
+    mem = eg.engram_lookup(raw, None, orders, heads, inp["mult"], tables, pad)
+    eg.engram_gate_forward(mem, h_ref, wk, wv, gq, gk, 1e-6, out=h_ref, gate_out=a_ref)
+    eg.engram_lookup_gate(raw, None, orders, heads, inp["mult"], tables, pad, h_got, wk, wv, gq, gk, 1e-6,
+                          out=h_got, gate_out=a_got)
+    torch.cuda.synchronize()
+    assert torch.equal(a_got.view(torch.int32), a_ref.view(torch.int32))
+    for m in range(nb):
+        assert torch.equal(h_got[m].view(torch.int16), h_ref[m].view(torch.int16)), m
+    say("  bit-identical")
