@@ -394,10 +394,13 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
   auto gather_prep = [&](uint32_t (&v0)[G_INSTR], uint32_t (&v1)[G_INSTR], int& o) {
     if constexpr (GATHER) {
 #pragma unroll
-      for (int i = 0; i < G_INSTR; ++i) {
-        const int src = (i * 8 + (lane >> 3)) * 4;
-        v0[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)gi0);
-        v1[i] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)gi1);
+      for (int i = 0; i < G_INSTR; ++i)
+        v0[i] = (uint32_t)__builtin_amdgcn_ds_bpermute((i * 8 + (lane >> 3)) * 4, (int)gi0);
+      // table gT + 1 only if some chunk of the k-step lies in it (otherwise no lane selects v1)
+      if (gO + 7 >= gcpr) {
+#pragma unroll
+        for (int i = 0; i < G_INSTR; ++i)
+          v1[i] = (uint32_t)__builtin_amdgcn_ds_bpermute((i * 8 + (lane >> 3)) * 4, (int)gi1);
       }
       o = gO;
     }
