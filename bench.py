@@ -593,6 +593,45 @@ def measure_ceiling(args, cfg, layer, bufs, sep_per, per, flush):
     }
 
 
+def measure_gemm_reference(args, cfg, layer, bufs, per, flush):
+    """The library's plain bf16 GEMM (torch.mm on ROCm: hipBLASLt) on the gate's contraction:
+    the memory vectors [tokens, d_mem] times every projection matrix of the call at once
+    ([d_mem, 2 * n_branch * d_model], contiguous), written out as bf16; no norms, gate or
+    residual.  Timed with events after the cache flush, as the gate is.  A reference for the
+    gate's matrix-core rate, not part of the path."""
+    import torch
+    mats = [w for m in range(cfg.n_branch) for w in (layer.wk[m], layer.wv[m])]
+    w_t = torch.cat(mats, dim=0).t().contiguous()          # [d_mem, N]
+    mem = bufs["mem"]
+    out = torch.empty((mem.shape[0], w_t.shape[1]), dtype=mem.dtype, device=mem.device)
+    for _ in range(2):
+        torch.mm(mem, w_t, out=out)
+    torch.cuda.synchronize()
+    reps = max(5, args.steps // 2)
+    ts = []
+    for i in range(reps):
+        if flush is not None:
+            flush.fill_(float(i))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.mm(mem, w_t, out=out)
+        b.record()
+        ts.append((a, b))
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ts) / reps
+    flops = 2.0 * mem.shape[0] * mem.shape[1] * w_t.shape[1]
+    tf = flops / (ms * 1e-3) / 1e12
+    gate_tf = flops / (per["gate"] * 1e-3) / 1e12
+    del out, w_t
+    return {"call": "torch.mm (hipBLASLt), bf16 in and out, fp32 accumulation",
+            "shape": [int(mem.shape[0]), int(mem.shape[1]), len(mats) * cfg.d_model],
+            "ms": round(ms, 5), "TFLOP/s": round(tf, 2), "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+            "gate_TFLOP/s": round(gate_tf, 2), "gate_vs_gemm": round(gate_tf / tf, 4),
+            "note": "the same FLOPs as the gate's two projections per branch, as one plain GEMM that writes "
+                    "its products to HBM (the gate never stores them and adds the norms, the gate and the "
+                    "residual); a reference, not part of the path"}
+
+
 def cpu_baseline(cfg, target_s, fp8=False):
     """The oracle (single thread) on the first tokens of sequence 0: compress, hash,
     gather and gate (its FP8 form with fp8).  Table rows are regenerated outside the
@@ -935,6 +974,9 @@ def run_workload(args, name, secondary=False):
         result["conv"] = measure_conv(args, cfg, bufs, h, layer, outs, flush)
     print("[bench] gather ceiling probes", file=sys.stderr, flush=True)
     result["gather_ceiling"] = measure_ceiling(args, cfg, layer, bufs, sep_per, per, flush)
+    if cfg.dtype == "bf16" and not args.fp8 and not args.shared_wv:
+        print("[bench] library GEMM reference", file=sys.stderr, flush=True)
+        result["gemm_reference"] = measure_gemm_reference(args, cfg, layer, bufs, per, flush)
     return result
 
 
