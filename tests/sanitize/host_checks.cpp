@@ -79,6 +79,18 @@ int main() {
   EXPECT(gate(((int64_t)1 << 31) - 1, 64, 1 << 16, 8, 1e-6f, ENGRAM_BF16, 0) == ENGRAM_ERR_UNSUPPORTED);
   EXPECT(gate((int64_t)1 << 31, 64, 64, 1, 1e-6f, ENGRAM_BF16, 0) == ENGRAM_ERR_UNSUPPORTED);
   EXPECT(gate(0, 1280, 2560, 1, 1e-6f, ENGRAM_BF16, 0) == ENGRAM_OK);
+  // lookup and gate in one call: the lookup's and the gate's checks, and rows under 64 values
+  const void* tabs4[4] = {fake(256), fake(512), fake(768), fake(1024)};  // one per (order, head)
+  auto lookup_gate = [&](int w, int dmod, int nb, int kn) {
+    return engram_lookup_gate((const int32_t*)fake(256), 1, 10, 0, 10, map, 100, orders, 2, 2, mult, rows, 0, tabs4,
+                              w, dmod, nb, one, one, one, one, one, 1e-6f, (engram_key_norm)kn, out1, nullptr,
+                              nullptr, nullptr, nullptr, 0);
+  };
+  EXPECT(lookup_gate(32, 2560, 1, 0) == ENGRAM_ERR_UNSUPPORTED);
+  EXPECT(lookup_gate(12, 2560, 1, 0) == ENGRAM_ERR_UNSUPPORTED);
+  EXPECT(lookup_gate(80, 2500, 1, 0) == ENGRAM_ERR_UNSUPPORTED);
+  EXPECT(lookup_gate(80, 2560, 0, 0) == ENGRAM_ERR_INVALID_ARG);
+  EXPECT(lookup_gate(80, 2560, 1, 7) == ENGRAM_ERR_INVALID_ARG);
   EXPECT(engram_gate_wait_timeouts(nullptr, 0) == ENGRAM_ERR_INVALID_ARG);
   // convolution
   EXPECT(engram_conv_forward(fake(256), 1, 10, 2560, fake(256), fake(256), 9, 3, 1e-6f, ENGRAM_BF16, fake(4096), 0) ==
