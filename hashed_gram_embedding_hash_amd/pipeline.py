@@ -8,6 +8,8 @@ the intermediate device buffers and issues the calls on one stream
 (compression, hashing and the gather as one fused call, then the gate); the
 arithmetic is in the HIP kernels.  Passing one W_V tensor for every branch
 (section 2.4, Eq. (6)) lets the gate compute W_V e once for all of them.
+With fused=True the whole pass is one call, engram_lookup_gate, whose gate kernel
+loads the table rows itself (same results bit for bit; no memory-vector buffer).
 """
 from __future__ import annotations
 
@@ -16,7 +18,7 @@ from typing import List, Optional, Sequence
 import numpy as np
 import torch
 
-from . import KEY_NORM_MEMORY, engram_gate_forward, engram_lookup
+from . import KEY_NORM_MEMORY, engram_gate_forward, engram_lookup, engram_lookup_gate
 
 
 class EngramLayer:
@@ -55,9 +57,15 @@ class EngramLayer:
         return self._bufs[key]
 
     def __call__(self, raw: torch.Tensor, h: Sequence[torch.Tensor], out: Optional[Sequence[torch.Tensor]] = None,
-                 gate_out: Optional[torch.Tensor] = None, stream=None) -> List[torch.Tensor]:
-        """raw: int32 [batch, seq]; h: per-branch [batch*seq, d_model]; returns per-branch outputs."""
+                 gate_out: Optional[torch.Tensor] = None, stream=None, fused: bool = False) -> List[torch.Tensor]:
+        """raw: int32 [batch, seq]; h: per-branch [batch*seq, d_model]; returns per-branch outputs.
+        fused: one engram_lookup_gate call (bf16 tables; nothing but the outputs is stored, so
+        the layer's buffers are neither used nor allocated)."""
         batch, seq = raw.shape
+        if fused:
+            return engram_lookup_gate(raw, self.cmap, self.orders, self.heads, self.mult, self.tables, self.pad_id,
+                                      h, self.wk, self.wv, self.gq, self.gk, self.eps, out=out, gate_out=gate_out,
+                                      key_norm=self.key_norm, stream=stream)
         b = self.buffers(batch, seq)
         engram_lookup(raw, self.cmap, self.orders, self.heads, self.mult, self.tables, self.pad_id,
                       out=b["mem"], ids_out=b["ids"], idx_out=b["idx"], stream=stream)

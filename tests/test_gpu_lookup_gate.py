@@ -142,8 +142,7 @@ def test_lookup_gate_small_config_against_oracle_sampled():
     layer(inp["raw"], inp["h"], out=ref, gate_out=ref_a)
     got = [sentinel_like(torch.empty_like(x)) for x in inp["h"]]
     got_a = sentinel_like(torch.empty_like(ref_a))
-    eg.engram_lookup_gate(inp["raw"], inp["map"], cfg.orders, cfg.heads, inp["mult"], inp["tables"], cfg.vocab_c,
-                          inp["h"], inp["wk"], inp["wv"], inp["gq"], inp["gk"], cfg.eps, out=got, gate_out=got_a)
+    layer(inp["raw"], inp["h"], out=got, gate_out=got_a, fused=True)   # the layer's one-call form
     torch.cuda.synchronize()
     assert torch.equal(got_a.view(torch.int32), ref_a.view(torch.int32))
     for m in range(cfg.n_branch):
