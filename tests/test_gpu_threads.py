@@ -2,9 +2,10 @@
 
 engram.h states that calls are thread-safe and that calls on different streams may run
 concurrently; the gate and the convolution share one scratch buffer per device, handed
-from stream to stream with an event.  Here four threads issue gate and lookup calls of
-different shapes on their own streams, interleaved; every result must equal the same call
-made alone (the kernels' sums have a fixed order, so equal means bit-identical).
+from stream to stream with an event.  Here four threads issue lookup + gate calls and
+engram_lookup_gate calls of different shapes on their own streams, interleaved; every
+result must equal the same work done alone (the kernels' sums have a fixed order, so equal
+means bit-identical).
 """
 import threading
 
@@ -22,7 +23,7 @@ def say(*a):
     print(*a, flush=True)
 
 
-def test_gate_and_lookup_from_four_host_threads():
+def test_lookup_and_gate_calls_from_four_host_threads():
     cfg = synth.CONFIGS["small"].replace(batch=1, seq=1024)
     say("four host threads, each on its own stream")
     inp = synth.device_inputs(cfg, DEV, table_rows_override=65537)
@@ -66,7 +67,11 @@ def test_gate_and_lookup_from_four_host_threads():
             raw, h = work[i]
             for r in range(reps):
                 mem, out, alpha = bufs[i][r]
-                one(raw, h, mem, out, alpha, stream=streams[i])
+                if r % 2 == 0:
+                    one(raw, h, mem, out, alpha, stream=streams[i])
+                else:  # the one-call form: its ids live in the same scratch
+                    eg.engram_lookup_gate(*args(raw), [h], [wk], [wv], [gq], [gk], cfg.eps, out=[out],
+                                          gate_out=alpha, stream=streams[i])
         except Exception as exc:  # reported by the main thread
             errors.append(exc)
 
