@@ -68,6 +68,10 @@ def parse():
     p.add_argument("--fp8", action="store_true",
                    help="gate projections on E4M3 codes (engram_gate_forward_fp8; quantization inside the call)")
     p.add_argument("--no-fp8", action="store_true", help="skip the extra fp8-gate step measurement")
+    p.add_argument("--probes", action="store_true",
+                   help="run the probe library's measurements of what bounds the gate's main loop (operand "
+                        "stream into LDS, the main loop with parts switched off, the MFMA rate and the clock), "
+                        "print one JSON line and exit")
     p.add_argument("--no-fused", action="store_true",
                    help="skip the one-call step (engram_lookup_gate) measured beside the two-call step")
     p.add_argument("--no-graph", action="store_true",
@@ -160,6 +164,97 @@ def measured_traffic(cfg):
         return int(float(kv["traffic_bytes_per_launch"]))
     except (KeyError, ValueError):
         return None
+
+
+def probes():
+    """Measurements behind the gate's limiter (libengram_probe.so, not part of the path), each
+    timed with events; one JSON line.
+    operand_stream: one workgroup of 256 threads per CU moving 64 KB per iteration from a 2-MB
+      L2-resident buffer into LDS, by direct global->LDS loads and through registers;
+    mainloop: the gate's k-step alone (256 x 256 tile, 20 k-steps of 64, the five-slot ring)
+      over synthetic operands, whole and with its operand loads, fragment reads or MFMAs
+      switched off, four waves as in the gate and eight; with the clock the chip ran at
+      (s_memtime cycles over s_memrealtime's 100-MHz ticks) and cycles per k-step;
+    mfma: back-to-back 32x32x16 bf16 MFMAs, one wave per SIMD on every CU, with the clock."""
+    import ctypes
+    import torch
+    from hashed_gram_embedding_hash_amd import build as hb
+    L = ctypes.CDLL(hb.PROBE_LIB)
+    P = ctypes.c_void_p
+    for f in (L.engram_probe_lds_dma, L.engram_probe_lds_vgpr):
+        f.argtypes = [P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, P, P]
+        f.restype = ctypes.c_int
+    L.engram_probe_mainloop.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P, ctypes.c_int32, P, P, P]
+    L.engram_probe_mainloop.restype = ctypes.c_int
+    L.engram_probe_mainloop_tokens.argtypes = [ctypes.c_int32]
+    L.engram_probe_mainloop_tokens.restype = ctypes.c_int64
+    L.engram_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P, P]
+    L.engram_probe_mfma.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    stream = P(torch.cuda.current_stream().cuda_stream)
+
+    def timed(run, reps=5):
+        assert run() == 0
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            assert run() == 0
+            b.record()
+            ts.append((a, b))
+        torch.cuda.synchronize()
+        return sorted(x.elapsed_time(y) for x, y in ts)[reps // 2]
+
+    def clock(clk, blocks):
+        c = clk[: 2 * blocks].view(blocks, 2).double().cpu()
+        cycles, ticks = c[:, 0].median().item(), c[:, 1].median().item()
+        return cycles, cycles / (ticks / 100e6) / 1e9  # s_memrealtime ticks at 100 MHz
+
+    out = {"probe": "libengram_probe.so (measurement only)", "cus": cus}
+    n_bytes, iters = 2 << 20, 4000
+    src = torch.arange(n_bytes // 4, dtype=torch.int32, device=dev)
+    sink = torch.empty(cus * 512, dtype=torch.float32, device=dev)
+    clk = torch.zeros(cus * 2, dtype=torch.int64, device=dev)
+    o = {"bytes_per_workgroup_iteration": 65536, "iterations": iters, "source_bytes": n_bytes}
+    for name, fn in (("direct_to_lds", L.engram_probe_lds_dma), ("through_registers", L.engram_probe_lds_vgpr)):
+        ms = timed(lambda: fn(P(src.data_ptr()), n_bytes, cus, iters, P(sink.data_ptr()), stream))
+        total = cus * iters * 65536
+        o[name] = {"ms": round(ms, 4), "TB/s_all_CUs": round(total / (ms * 1e-3) / 1e12, 3),
+                   "GB/s_per_CU": round(total / cus / (ms * 1e-3) / 1e9, 2)}
+    out["operand_stream"] = o
+    del src
+
+    if cus == 256:  # the main-loop probe's tile schedule assumes 256 workgroups
+        rounds = 8
+        g = torch.Generator(device=dev).manual_seed(5)
+        W = (torch.randn(4096 * 1280, device=dev, generator=g) * 0.05).to(torch.bfloat16)
+        E = (torch.randn(L.engram_probe_mainloop_tokens(rounds) * 1280, device=dev, generator=g) * 0.05
+             ).to(torch.bfloat16)
+        ksteps = rounds * 20
+        flops = cus * rounds * 2 * 256 * 256 * 1280
+        o = {"tile": "256 x 256 outputs, 20 k-steps of 64 (d_mem 1280)", "tiles_per_workgroup": rounds}
+        modes = [(4, 0, "whole"), (4, 1, "no operand loads"), (4, 2, "no fragment reads"),
+                 (4, 3, "no loads, no reads"), (4, 4, "no MFMAs"), (4, 6, "operand loads only"),
+                 (8, 0, "whole, eight waves"), (8, 3, "no loads, no reads, eight waves")]
+        for waves, mode, name in modes:
+            ms = timed(lambda: L.engram_probe_mainloop(mode, waves, P(W.data_ptr()), P(E.data_ptr()), rounds,
+                                                       P(sink.data_ptr()), P(clk.data_ptr()), stream))
+            cycles, ghz = clock(clk, 256)
+            o[name] = {"us_per_kstep": round(ms * 1e3 / ksteps, 3), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1),
+                       "clock_GHz": round(ghz, 3), "cycles_per_kstep": round(cycles / ksteps, 1)}
+        out["mainloop"] = o
+        del W, E
+
+    iters = 20000
+    ms = timed(lambda: L.engram_probe_mfma(cus, iters, P(sink.data_ptr()), P(clk.data_ptr()), stream), reps=3)
+    cycles, ghz = clock(clk, cus)
+    n_mfma = iters * 16
+    out["mfma"] = {"instruction": "v_mfma_f32_32x32x16_bf16", "mfma_per_wave": n_mfma, "ms": round(ms, 4),
+                   "TFLOP/s": round(cus * 4 * n_mfma * 32768 / (ms * 1e-3) / 1e12, 1),
+                   "clock_GHz": round(ghz, 3), "cycles_per_mfma": round(cycles / n_mfma, 2)}
+    print(json.dumps(out), flush=True)
 
 
 def calibrate_copy(mib):
@@ -989,6 +1084,10 @@ def main():
 
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+
+    if args.probes:
+        probes()
         return
 
     if args.config == "offload":

@@ -1,8 +1,8 @@
 """Build the HIP library libengram.so (gfx950) in-tree with hipcc.
 
 Each csrc/*.hip file is compiled to an object in parallel, then linked into
-hashed_gram_embedding_hash_amd/libengram.so.  The benchmark's memory probes
-(probe/row_ceiling.hip, not part of the method) go to libengram_probe.so.  Always recompiles (the caller
+hashed_gram_embedding_hash_amd/libengram.so.  The benchmark's measurement probes
+(probe/*.hip, not part of the method) go to libengram_probe.so.  Always recompiles (the caller
 asked for a build); objects go to _build/ at the repository root.
 """
 from __future__ import annotations
@@ -53,20 +53,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-PROBE_SRC = os.path.join(PKG, "probe", "row_ceiling.hip")
+PROBE_DIR = os.path.join(PKG, "probe")
 PROBE_LIB = os.path.join(PKG, "libengram_probe.so")
+
+
+def probe_sources():
+    return sorted(os.path.join(PROBE_DIR, f) for f in os.listdir(PROBE_DIR) if f.endswith(".hip"))
 
 
 def build(verbose: bool = False) -> str:
     """Build libengram.so, and the benchmark's measurement probes (libengram_probe.so)."""
     os.makedirs(OBJ, exist_ok=True)
     srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + 1)) as ex:
-        probe = ex.submit(_compile, PROBE_SRC)
+    psrcs = probe_sources()
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(psrcs))) as ex:
+        probes = [ex.submit(_compile, p) for p in psrcs]
         objs = list(ex.map(_compile, srcs))
-        probe_obj = probe.result()
+        probe_objs = [p.result() for p in probes]
     tmp = PROBE_LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, probe_obj]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *probe_objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
