@@ -72,6 +72,9 @@ def parse():
                    help="run the probe library's measurements of what bounds the gate's main loop (operand "
                         "stream into LDS, the main loop with parts switched off, the MFMA rate and the clock), "
                         "print one JSON line and exit")
+    p.add_argument("--timeline", action="store_true",
+                   help="run one gate call of --config with libengram_timeline.so (the gate stamping each "
+                        "tile's phase boundaries), print the per-tile breakdown as one JSON line and exit")
     p.add_argument("--no-fused", action="store_true",
                    help="skip the one-call step (engram_lookup_gate) measured beside the two-call step")
     p.add_argument("--no-graph", action="store_true",
@@ -254,6 +257,88 @@ def probes():
     out["mfma"] = {"instruction": "v_mfma_f32_32x32x16_bf16", "mfma_per_wave": n_mfma, "ms": round(ms, 4),
                    "TFLOP/s": round(cus * 4 * n_mfma * 32768 / (ms * 1e-3) / 1e12, 1),
                    "clock_GHz": round(ghz, 3), "cycles_per_mfma": round(cycles / n_mfma, 2)}
+    print(json.dumps(out), flush=True)
+
+
+TIMELINE_PARTS = {
+    # (from point, to point): name; points as the gate's timeline build numbers them
+    "K": [((0, 1), "claim and decode"), ((1, 2), "first operands"), ((2, 3), "main loop"),
+          ((3, 4), "h tile wait"), ((5, 8), "dot pass"), ((8, 9), "partial stores"), ((9, 10), "store ack"),
+          ((10, 11), "count"), ((11, 6), "gates (last K tile)"), ((6, 7), "end barrier")],
+    "V": [((0, 1), "claim and decode"), ((1, 2), "first operands"), ((2, 3), "main loop"),
+          ((3, 4), "h tile wait"), ((4, 5), "gate wait"), ((5, 12), "output into LDS"), ((12, 13), "stream out"),
+          ((13, 6), "rest"), ((6, 7), "end barrier")],
+}
+
+
+def timeline(args):
+    """One engram_gate_forward call of the workload's step (bf16, default options) run with
+    libengram_timeline.so, the library whose gate stamps s_memrealtime (100 MHz) at each tile's
+    phase boundaries; after three warm-up calls.  Per phase (K, V): the mean, median and 90th
+    percentile of each part of a tile in microseconds and its share of all workgroups' time;
+    the workgroups' start skew and end spread.  One JSON line."""
+    import ctypes
+    import numpy as np
+    import torch
+    import synth
+    import hashed_gram_embedding_hash_amd as eg
+    from hashed_gram_embedding_hash_amd import build as hb
+    eg.LIB_PATH = hb.TIMELINE_LIB  # before anything loads the library
+    L = eg.lib()
+    L.engram_gate_timeline_read.argtypes = [ctypes.c_void_p, ctypes.c_int64]
+    L.engram_gate_timeline_read.restype = ctypes.c_int
+    L.engram_gate_timeline_clear.argtypes = []
+    L.engram_gate_timeline_clear.restype = ctypes.c_int
+    cfg = synth.CONFIGS[args.config]
+    dev = torch.device("cuda:0")
+    inp = synth.device_inputs(cfg, dev)
+    mem = torch.empty((cfg.tokens, cfg.d_mem), dtype=torch.bfloat16, device=dev)
+    eg.engram_lookup(inp["raw"], inp["map"], cfg.orders, cfg.heads, inp["mult"], inp["tables"], cfg.vocab_c,
+                     out=mem)
+    outs = [torch.empty_like(h) for h in inp["h"]]
+
+    def gate():
+        eg.engram_gate_forward(mem, inp["h"], inp["wk"], inp["wv"], inp["gq"], inp["gk"], cfg.eps, out=outs)
+    for _ in range(3):
+        gate()
+    torch.cuda.synchronize()
+    assert L.engram_gate_timeline_clear() == 0
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    gate()
+    b.record()
+    torch.cuda.synchronize()
+    wgs, tiles, points = 256, 512, 16
+    buf = np.zeros(wgs * tiles * points, dtype=np.uint64)
+    assert L.engram_gate_timeline_read(buf.ctypes.data, buf.nbytes) == 0
+    t = buf.reshape(wgs, tiles, points).astype(np.int64)
+    done = t[:, :, 7] > 0
+    used = done.any(axis=1)
+    assert done.sum() > 0, "no tile stamped"
+    t0 = t[:, :, 0][t[:, :, 0] > 0].min()
+    us = 0.01  # one s_memrealtime tick is 10 ns
+    starts = np.where(done, t[:, :, 0], np.iinfo(np.int64).max).min(axis=1)[used]
+    ends = np.where(done, t[:, :, 7], 0).max(axis=1)[used]
+    span = (ends.max() - t0) * us
+    out = {"timeline": cfg.name, "gate_call_ms_events": round(a.elapsed_time(b), 4),
+           "workgroups": int(used.sum()), "tiles": int(done.sum()),
+           "span_us": round(span, 1), "start_skew_us_max": round(float((starts - t0).max()) * us, 2),
+           "end_us": {"min": round(float((ends - t0).min()) * us, 1), "median": round(float(np.median(ends - t0)) * us, 1),
+                      "max": round(float((ends - t0).max()) * us, 1)}}
+    phase = t[:, :, 15] & 1
+    for ph, name in ((0, "K"), (1, "V")):
+        sel = done & (phase == ph)
+        if not sel.any():
+            continue
+        rows = {}
+        for (p0, p1), part in TIMELINE_PARTS[name]:
+            d = (t[:, :, p1] - t[:, :, p0])[sel] * us
+            rows[part] = {"mean": round(float(d.mean()), 3), "median": round(float(np.median(d)), 3),
+                          "p90": round(float(np.percentile(d, 90)), 3),
+                          "share": round(float(d.sum()) / (int(used.sum()) * span), 4)}
+        tot = (t[:, :, 7] - t[:, :, 0])[sel] * us
+        rows["tile"] = {"mean": round(float(tot.mean()), 3), "share": round(float(tot.sum()) / (int(used.sum()) * span), 4)}
+        out[name] = {"tiles": int(sel.sum()), "parts_us": rows}
     print(json.dumps(out), flush=True)
 
 
@@ -1088,6 +1173,10 @@ def main():
 
     if args.probes:
         probes()
+        return
+
+    if args.timeline:
+        timeline(args)
         return
 
     if args.config == "offload":

@@ -2,8 +2,10 @@
 
 Each csrc/*.hip file is compiled to an object in parallel, then linked into
 hashed_gram_embedding_hash_amd/libengram.so.  The benchmark's measurement probes
-(probe/*.hip, not part of the method) go to libengram_probe.so.  Always recompiles (the caller
-asked for a build); objects go to _build/ at the repository root.
+(probe/*.hip, not part of the method) go to libengram_probe.so, and a diagnostic copy of the
+library whose gate stamps a per-tile timeline (gate_bf16.hip compiled with ENGRAM_GATE_TIMELINE)
+to libengram_timeline.so.  Always recompiles (the caller asked for a build); objects go to
+_build/ at the repository root.
 """
 from __future__ import annotations
 
@@ -44,9 +46,9 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+def _compile(src: str, timeline: bool = False) -> str:
+    obj = os.path.join(OBJ, os.path.basename(src) + (".timeline.o" if timeline else ".o"))
+    cmd = [HIPCC, *FLAGS, *(["-DENGRAM_GATE_TIMELINE"] if timeline else []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -55,6 +57,8 @@ def _compile(src: str) -> str:
 
 PROBE_DIR = os.path.join(PKG, "probe")
 PROBE_LIB = os.path.join(PKG, "libengram_probe.so")
+TIMELINE_LIB = os.path.join(PKG, "libengram_timeline.so")
+TIMELINE_SRC = os.path.join(CSRC, "gate_bf16.hip")
 
 
 def probe_sources():
@@ -62,26 +66,26 @@ def probe_sources():
 
 
 def build(verbose: bool = False) -> str:
-    """Build libengram.so, and the benchmark's measurement probes (libengram_probe.so)."""
+    """Build libengram.so, the benchmark's measurement probes (libengram_probe.so) and the
+    timeline build (libengram_timeline.so)."""
     os.makedirs(OBJ, exist_ok=True)
     srcs = sources()
     psrcs = probe_sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(psrcs))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=8) as ex:
+        timeline = ex.submit(_compile, TIMELINE_SRC, True)  # the slowest file: start it first
         probes = [ex.submit(_compile, p) for p in psrcs]
         objs = list(ex.map(_compile, srcs))
         probe_objs = [p.result() for p in probes]
-    tmp = PROBE_LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *probe_objs]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, PROBE_LIB)
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+        timeline_obj = timeline.result()
+    timeline_objs = [timeline_obj if os.path.basename(o) == os.path.basename(TIMELINE_SRC) + ".o" else o for o in objs]
+    assert timeline_obj in timeline_objs
+    for out, parts in ((PROBE_LIB, probe_objs), (TIMELINE_LIB, timeline_objs), (LIB, objs)):
+        tmp = out + ".tmp"
+        cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *parts]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        os.replace(tmp, out)
     if verbose:
         print(f"built {LIB}", file=sys.stderr)
     return LIB

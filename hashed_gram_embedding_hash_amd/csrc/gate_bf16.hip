@@ -84,6 +84,39 @@ namespace engram {
 // per device, since the library was loaded or the count was last reset.
 __device__ int32_t g_gate_wait_timeouts;
 
+// Tile timeline (a diagnostic build only, libengram_timeline.so, compiled with
+// ENGRAM_GATE_TIMELINE): thread 0 of each workgroup stamps s_memrealtime (100 MHz) at the
+// phase boundaries of each of its first TL_TILES tiles, in g_timeline[workgroup][tile][point]:
+//   0 loop top (claim published)  1 tile decoded  2 first operands landed  3 main loop done
+//   4 h tile landed  5 V gates in LDS  6 epilogue done  7 after the end-of-tile barrier
+//   K tiles: 8 dot pass done  9 partial stores issued  10 stores acknowledged  11 count raised
+//   V tiles: 12 output tile in LDS  13 output streamed
+//   15: the tile (phase | branch << 1 | feature tile << 4 | token tile << 16)
+// In the normal build ENGRAM_STAMP expands to nothing.
+#ifdef ENGRAM_GATE_TIMELINE
+constexpr int TL_WGS = 256, TL_TILES = 512, TL_POINTS = 16;
+__device__ uint64_t g_timeline[TL_WGS * TL_TILES * TL_POINTS];
+#define ENGRAM_TL_SLOT(k) g_timeline[((int64_t)blockIdx.x * TL_TILES + tl_n) * TL_POINTS + (k)]
+#define ENGRAM_STAMP(k)                                                        \
+  do {                                                                         \
+    if (threadIdx.x == 0 && blockIdx.x < TL_WGS && tl_n < TL_TILES)            \
+      ENGRAM_TL_SLOT(k) = __builtin_amdgcn_s_memrealtime();                    \
+  } while (0)
+#define ENGRAM_STAMP_TILE(t)                                                   \
+  do {                                                                         \
+    if (threadIdx.x == 0 && blockIdx.x < TL_WGS && tl_n < TL_TILES)            \
+      ENGRAM_TL_SLOT(15) = (uint64_t)(t).phase | ((uint64_t)(t).m << 1) |      \
+                           ((uint64_t)(t).ftile << 4) | ((uint64_t)(t).ttile << 16); \
+  } while (0)
+#else
+#define ENGRAM_STAMP(k) \
+  do {                  \
+  } while (0)
+#define ENGRAM_STAMP_TILE(t) \
+  do {                       \
+  } while (0)
+#endif
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -264,7 +297,9 @@ struct NoGather {};
 
 template <bool VALUES, bool KEYP, bool SHAREDV, bool F8, bool GATHER, class GS>
 __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const Tile& tile, char* smem, int x,
-                                          int& next_claim) {
+                                          int& next_claim, int tl_n) {
+  ENGRAM_STAMP(1);
+  ENGRAM_STAMP_TILE(tile);
   static_assert(!(GATHER && F8), "the gathering gate is bf16");
   const int PHASE = tile.phase;
   const int tid = threadIdx.x;
@@ -623,6 +658,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
   for (int c = 0; c < NSLOT; ++c) issue_chunk(c);
   wait_vm_lgkm0<3 * G_INSTR>();
   lds_barrier();
+  ENGRAM_STAMP(2);
   // k-step 0, sub-steps 0-2 (sub-step 3's MFMAs open k-step 1); no slot is free yet
   bool ee_now = ee_wave && ftile == 0;
   ENGRAM_LOAD_FRAGS(0, 0, SLOT_BYTES, 0);
@@ -774,6 +810,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
     for (int c = 0; c < 4; ++c) issue_chunk(c);
     wait_vm_lgkm0<2 * G_INSTR>();
     lds_barrier();
+    ENGRAM_STAMP(2);
 #pragma unroll
     for (int j = 0; j < MT; ++j) ENGRAM_F8_B(SLOT_BYTES, 0, j);
 #pragma unroll
@@ -799,6 +836,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
   // Nothing of the epilogue may be scheduled into the last k-steps (measured: 8 %
   // slower when the compiler is free to interleave them).
   __builtin_amdgcn_sched_barrier(0);
+  ENGRAM_STAMP(3);
 
   // Everything below re-derives its indices from an opaque copy of the thread id, so
   // the compiler cannot compute epilogue addresses before the loop and keep them
@@ -824,6 +862,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
   // fifth slot, (2 nk + 4) % NSLOT, holds the epilogue's cross-wave scratch
   wait_vm_lgkm0<0>();
   lds_barrier();
+  ENGRAM_STAMP(4);
   // claim this workgroup's next tile now; the atomic's latency hides behind the epilogue
   if (tid == 0) next_claim = atomicAdd(a.counters + x, 1);
   // byte offset of h-tile quarter q (a runtime q must not index a local array: that
@@ -870,6 +909,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
     else s_alpha[etid] = alpha;
     lds_barrier();
   }
+  ENGRAM_STAMP(5);
   if (KEYP && PHASE == PHASE_K) {
     s_g[etid] = kg;
     lds_barrier();
@@ -974,6 +1014,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
         }
       }
     }
+    ENGRAM_STAMP(8);
     __syncthreads();
     const int64_t t = t0 + etid;
     if (t < n_tok) {
@@ -984,10 +1025,13 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
     }
     // publish: every wave waits for its own partial stores, then the barrier, then the
     // count goes up
+    ENGRAM_STAMP(9);
     wait_vm_lgkm0<0>();
     __syncthreads();
+    ENGRAM_STAMP(10);
     if (etid == 0) *s_flag = __hip_atomic_fetch_add(done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     lds_barrier();
+    ENGRAM_STAMP(11);
     if (*s_flag == a.n_ftiles - 1) {
       // The last K tile of this (branch, token tile): every other one stored its
       // partials before its increment, so all are in L2.  Turn them into gates
@@ -1089,7 +1133,9 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
         }
       }
       lds_barrier();
+      ENGRAM_STAMP(12);
       stream_out((uint16_t*)a.out[mb]);
+      ENGRAM_STAMP(13);
       if (VALUES && a.vout[mb] != nullptr) {
         // the gated values alpha * v, staged through the same LDS tile
         lds_barrier();
@@ -1151,6 +1197,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
       }
     }
   }
+  ENGRAM_STAMP(6);
 #undef ENGRAM_HOFF
 #undef ENGRAM_QSLOT
 }
@@ -1164,18 +1211,20 @@ __device__ __forceinline__ void persistent_loop(const GateArgs& a, const GS& gs,
   const int x = blockIdx.x % NQ;
   int claim = 0;  // thread 0: the tile claimed for after the current one
   if (threadIdx.x == 0) claim = atomicAdd(a.counters + x, 1);
-  for (;;) {
+  for (int tl_n = 0;; ++tl_n) {
+    ENGRAM_STAMP(0);
     if (threadIdx.x == 0) *s_tile = claim;
     lds_barrier();
     Tile t;
     const bool have = decode_tile<SHAREDV, GATHER>(a, x, *s_tile, t);
     lds_barrier();  // every thread has read the tile number before the ring is refilled
     if (!have) break;
-    gate_tile<VALUES, KEYP, SHAREDV, F8, GATHER>(a, gs, t, smem, x, claim);
+    gate_tile<VALUES, KEYP, SHAREDV, F8, GATHER>(a, gs, t, smem, x, claim, tl_n);
     // LDS free for the next tile.  A full barrier: letting a V tile's 128 KB of output
     // stores drain behind the next tile's operand loads measured 8 % slower than
     // finishing them first.
     __syncthreads();
+    ENGRAM_STAMP(7);
   }
 }
 
@@ -1450,3 +1499,21 @@ void launch_prepare_fp8(const GateArgs& a, uint8_t* const* wk_codes, float* cons
 }
 
 }  // namespace engram
+
+#ifdef ENGRAM_GATE_TIMELINE
+// The timeline build's two extra exports (not in engram.h): copy g_timeline (uint64
+// [256][512][16]) to host memory after synchronising the device, and clear it.  0 or -1.
+extern "C" int engram_gate_timeline_read(void* host, int64_t bytes) {
+  if (host == nullptr || bytes <= 0 || bytes > (int64_t)sizeof(engram::g_timeline)) return -1;
+  if (hipDeviceSynchronize() != hipSuccess) return -1;
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(engram::g_timeline), (size_t)bytes, 0, hipMemcpyDeviceToHost) ==
+                 hipSuccess ? 0 : -1;
+}
+
+extern "C" int engram_gate_timeline_clear() {
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(engram::g_timeline)) != hipSuccess) return -1;
+  if (hipMemset(p, 0, sizeof(engram::g_timeline)) != hipSuccess) return -1;
+  return hipDeviceSynchronize() == hipSuccess ? 0 : -1;
+}
+#endif
