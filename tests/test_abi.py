@@ -3,6 +3,7 @@ and rejects bad arguments on the host (no GPU work is started by these calls).""
 import ctypes
 import os
 import re
+import subprocess
 
 import numpy as np
 import pytest
@@ -36,6 +37,24 @@ def test_library_exports_every_declared_symbol():
 def test_library_is_gfx950_code_object():
     data = open(eg.LIB_PATH, "rb").read()
     assert b"gfx950" in data
+
+
+def _dynamic_symbols(path):
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True).stdout
+    return {line.split()[-1] for line in out.splitlines() if line.strip()}
+
+
+def test_timeline_build_exports_the_api_and_its_two_calls():
+    """libengram_timeline.so (the gate compiled with its per-tile stamps) carries every entry point
+    of engram.h plus engram_gate_timeline_read / _clear; the normal library has neither of those."""
+    from hashed_gram_embedding_hash_amd import build as hb
+    timeline = _dynamic_symbols(hb.TIMELINE_LIB)
+    normal = _dynamic_symbols(eg.LIB_PATH)
+    extra = {"engram_gate_timeline_read", "engram_gate_timeline_clear"}
+    assert set(declared_functions()) <= timeline
+    assert extra <= timeline
+    assert not (extra & normal)
+    assert set(declared_functions()) <= normal
 
 
 def _st(name):
