@@ -178,7 +178,8 @@ def probes():
       over synthetic operands, whole and with its operand loads, fragment reads or MFMAs
       switched off, four waves as in the gate and eight; with the clock the chip ran at
       (s_memtime cycles over s_memrealtime's 100-MHz ticks) and cycles per k-step;
-    mfma: back-to-back 32x32x16 bf16 MFMAs, one wave per SIMD on every CU, with the clock."""
+    mfma: back-to-back 32x32x16 bf16 MFMAs and 32x32x64 E4M3 MFMAs (the FP8 gate's scaled form),
+      one wave per SIMD on every CU, with the clock."""
     import ctypes
     import torch
     from hashed_gram_embedding_hash_amd import build as hb
@@ -191,7 +192,7 @@ def probes():
     L.engram_probe_mainloop.restype = ctypes.c_int
     L.engram_probe_mainloop_tokens.argtypes = [ctypes.c_int32]
     L.engram_probe_mainloop_tokens.restype = ctypes.c_int64
-    L.engram_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P, P]
+    L.engram_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P]
     L.engram_probe_mfma.restype = ctypes.c_int
     dev = torch.device("cuda:0")
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
@@ -251,12 +252,16 @@ def probes():
         del W, E
 
     iters = 20000
-    ms = timed(lambda: L.engram_probe_mfma(cus, iters, P(sink.data_ptr()), P(clk.data_ptr()), stream), reps=3)
-    cycles, ghz = clock(clk, cus)
-    n_mfma = iters * 16
-    out["mfma"] = {"instruction": "v_mfma_f32_32x32x16_bf16", "mfma_per_wave": n_mfma, "ms": round(ms, 4),
-                   "TFLOP/s": round(cus * 4 * n_mfma * 32768 / (ms * 1e-3) / 1e12, 1),
-                   "clock_GHz": round(ghz, 3), "cycles_per_mfma": round(cycles / n_mfma, 2)}
+    out["mfma"] = {}
+    for kind, name, flop in ((0, "v_mfma_f32_32x32x16_bf16", 32 * 32 * 16 * 2),
+                             (1, "v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3)", 32 * 32 * 64 * 2)):
+        ms = timed(lambda: L.engram_probe_mfma(kind, cus, iters, P(sink.data_ptr()), P(clk.data_ptr()), stream),
+                   reps=3)
+        cycles, ghz = clock(clk, cus)
+        n_mfma = iters * 16
+        out["mfma"][name] = {"mfma_per_wave": n_mfma, "ms": round(ms, 4),
+                             "TFLOP/s": round(cus * 4 * n_mfma * flop / (ms * 1e-3) / 1e12, 1),
+                             "clock_GHz": round(ghz, 3), "cycles_per_mfma": round(cycles / n_mfma, 2)}
     print(json.dumps(out), flush=True)
 
 

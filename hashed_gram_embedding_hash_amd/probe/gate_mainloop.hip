@@ -9,8 +9,10 @@
 //     bit 0 no operand loads in the steady k-steps, bit 1 no fragment reads (the MFMAs reuse
 //     the registers), bit 2 no MFMAs.  Four waves (2 x 2, 128 x 128 outputs each) as in the
 //     gate, or eight (2 x 4, 128 x 64 each, two waves per SIMD).
-//   engram_probe_mfma: back-to-back v_mfma_f32_32x32x16_bf16 (16 independent accumulators,
-//     4 x 4 distinct operand registers as in a 128 x 128 wave tile), one wave per SIMD.
+//   engram_probe_mfma: back-to-back MFMAs (16 independent accumulators, 4 x 4 distinct operand
+//     registers as in a 128 x 128 wave tile), one wave per SIMD: kind 0 the bf16 gate's
+//     v_mfma_f32_32x32x16_bf16, kind 1 the FP8 gate's v_mfma_scale_f32_32x32x64_f8f6f4 (E4M3
+//     operands, unit block scales).
 //
 // Both record, per workgroup, the shader-clock counter (s_memtime) and the constant 100-MHz
 // counter (s_memrealtime) around the work, so the clock the chip actually ran at and the
@@ -22,6 +24,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 
 constexpr int BK = 64, NSLOT = 5, SLOT_BYTES = 256 * BK * 2;
@@ -199,10 +202,12 @@ void probe_mainloop_kernel(const uint16_t* __restrict__ W, const uint16_t* __res
   }
 }
 
+template <int KIND>
 __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, float* __restrict__ sink,
                                                          uint64_t* __restrict__ clk) {
   const int tid = threadIdx.x;
   bf16x8 fa[4], fb[4];
+  v8i qa[4], qb[4];  // KIND 1: E4M3 codes (any byte pattern but NaN; 0x7f / 0xff are NaN, cleared)
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -210,6 +215,8 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, float* __res
       const uint32_t h = (uint32_t)(tid * 8 + e + i * 4096) * 2654435761u;
       fa[i][e] = (__bf16)((float)(h >> 16) / 65536.f - 0.5f);
       fb[i][e] = (__bf16)((float)((h * 2246822519u) >> 16) / 65536.f - 0.5f);
+      qa[i][e] = (int)(h & 0xbfbfbfbfu);
+      qb[i][e] = (int)((h * 2246822519u) & 0xbfbfbfbfu);
     }
   floatx16 acc[16];
 #pragma unroll
@@ -219,7 +226,12 @@ __global__ __launch_bounds__(256) void probe_mfma_kernel(int iters, float* __res
   const uint64_t c0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[j / 4], fb[j % 4], acc[j], 0, 0, 0);
+    for (int j = 0; j < 16; ++j) {
+      if (KIND == 0)
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[j / 4], fb[j % 4], acc[j], 0, 0, 0);
+      else  // E4M3 x E4M3, block scales 127 (2^0)
+        acc[j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[j / 4], qb[j % 4], acc[j], 0, 0, 0, 127, 0, 127);
+    }
   }
   float total = 0.f;
 #pragma unroll
@@ -264,11 +276,14 @@ int engram_probe_mainloop(int32_t mode, int32_t waves, const void* W, const void
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-// blocks workgroups of 256 threads; sink: device float [blocks * 256]; clk: device uint64
-// [blocks * 2].  Returns 0, or -1 for bad arguments.
-int engram_probe_mfma(int32_t blocks, int32_t iters, float* sink, uint64_t* clk, hipStream_t stream) {
-  if (sink == nullptr || clk == nullptr || blocks <= 0 || iters <= 0) return -1;
-  hipLaunchKernelGGL(probe_mfma_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, iters, sink, clk);
+// kind 0 (bf16) or 1 (FP8); blocks workgroups of 256 threads; sink: device float
+// [blocks * 256]; clk: device uint64 [blocks * 2].  Returns 0, or -1 for bad arguments.
+int engram_probe_mfma(int32_t kind, int32_t blocks, int32_t iters, float* sink, uint64_t* clk, hipStream_t stream) {
+  if (sink == nullptr || clk == nullptr || blocks <= 0 || iters <= 0 || (kind != 0 && kind != 1)) return -1;
+  if (kind == 0)
+    hipLaunchKernelGGL(probe_mfma_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, stream, iters, sink, clk);
+  else
+    hipLaunchKernelGGL(probe_mfma_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, iters, sink, clk);
   return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
