@@ -178,6 +178,7 @@ def probes():
       over synthetic operands, whole and with its operand loads, fragment reads or MFMAs
       switched off, four waves as in the gate and eight; with the clock the chip ran at
       (s_memtime cycles over s_memrealtime's 100-MHz ticks) and cycles per k-step;
+    mainloop_fp8: the FP8 gate's k-step (128 E4M3 values per ring row, 32x32x64 MFMAs) the same way;
     mfma: back-to-back 32x32x16 bf16 MFMAs and 32x32x64 E4M3 MFMAs (the FP8 gate's scaled form),
       one wave per SIMD on every CU, with the clock."""
     import ctypes
@@ -190,6 +191,8 @@ def probes():
         f.restype = ctypes.c_int
     L.engram_probe_mainloop.argtypes = [ctypes.c_int32, ctypes.c_int32, P, P, ctypes.c_int32, P, P, P]
     L.engram_probe_mainloop.restype = ctypes.c_int
+    L.engram_probe_mainloop_fp8.argtypes = [ctypes.c_int32, P, P, ctypes.c_int32, P, P, P]
+    L.engram_probe_mainloop_fp8.restype = ctypes.c_int
     L.engram_probe_mainloop_tokens.argtypes = [ctypes.c_int32]
     L.engram_probe_mainloop_tokens.restype = ctypes.c_int64
     L.engram_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P]
@@ -249,6 +252,16 @@ def probes():
             o[name] = {"us_per_kstep": round(ms * 1e3 / ksteps, 3), "TFLOP/s": round(flops / (ms * 1e-3) / 1e12, 1),
                        "clock_GHz": round(ghz, 3), "cycles_per_kstep": round(cycles / ksteps, 1)}
         out["mainloop"] = o
+        o = {"tile": "256 x 256 outputs, 20 k-steps of 128 E4M3 values (the same bytes as the bf16 probe)",
+             "tiles_per_workgroup": rounds}
+        for mode, name in ((0, "whole"), (1, "no operand loads"), (2, "no fragment reads"), (3, "no loads, no reads")):
+            ms = timed(lambda: L.engram_probe_mainloop_fp8(mode, P(W.data_ptr()), P(E.data_ptr()), rounds,
+                                                           P(sink.data_ptr()), P(clk.data_ptr()), stream))
+            cycles, ghz = clock(clk, 256)
+            o[name] = {"us_per_kstep": round(ms * 1e3 / ksteps, 3),
+                       "TFLOP/s": round(2 * flops / (ms * 1e-3) / 1e12, 1),
+                       "clock_GHz": round(ghz, 3), "cycles_per_kstep": round(cycles / ksteps, 1)}
+        out["mainloop_fp8"] = o
         del W, E
 
     iters = 20000
@@ -277,7 +290,7 @@ TIMELINE_PARTS = {
 
 
 def timeline(args):
-    """One engram_gate_forward call of the workload's step (bf16, default options) run with
+    """One engram_gate_forward call of the workload's step (bf16, or with --fp8 the FP8 gate) run with
     libengram_timeline.so, the library whose gate stamps s_memrealtime (100 MHz) at each tile's
     phase boundaries; after three warm-up calls.  Per phase (K, V): the mean, median and 90th
     percentile of each part of a tile in microseconds and its share of all workgroups' time;
@@ -303,7 +316,8 @@ def timeline(args):
     outs = [torch.empty_like(h) for h in inp["h"]]
 
     def gate():
-        eg.engram_gate_forward(mem, inp["h"], inp["wk"], inp["wv"], inp["gq"], inp["gk"], cfg.eps, out=outs)
+        eg.engram_gate_forward(mem, inp["h"], inp["wk"], inp["wv"], inp["gq"], inp["gk"], cfg.eps, out=outs,
+                               fp8=args.fp8)
     for _ in range(3):
         gate()
     torch.cuda.synchronize()
@@ -325,7 +339,8 @@ def timeline(args):
     starts = np.where(done, t[:, :, 0], np.iinfo(np.int64).max).min(axis=1)[used]
     ends = np.where(done, t[:, :, 7], 0).max(axis=1)[used]
     span = (ends.max() - t0) * us
-    out = {"timeline": cfg.name, "gate_call_ms_events": round(a.elapsed_time(b), 4),
+    out = {"timeline": cfg.name, "gate": "fp8" if args.fp8 else "bf16",
+           "gate_call_ms_events": round(a.elapsed_time(b), 4),
            "workgroups": int(used.sum()), "tiles": int(done.sum()),
            "span_us": round(span, 1), "start_skew_us_max": round(float((starts - t0).max()) * us, 2),
            "end_us": {"min": round(float((ends - t0).min()) * us, 1), "median": round(float(np.median(ends - t0)) * us, 1),
