@@ -918,11 +918,19 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
   // Lane (token column tl) holds, for MFMA tile (i, j) and pair gp, features
   // fl = wf*WF + i*32 + gp*16 + (lane>>5)*8 + 0..7 in acc[i][j][8*gp + 0..7].
   const int hsel = (elane >> 5) * 8;
+  // F8: acc holds W e over each feature's weight scale.  The epilogues multiply each
+  // accumulator by its feature's scale (from LDS) as they read it (FOLD; ENGRAM_WS: the
+  // eight scales of features fl .. fl + 7), which gives the values the bf16 epilogues take
+  // (k_f or v_f over the token scale), rounded the same way, without writing every scaled
+  // accumulator back first.  With a shared W_V the V epilogue runs once per branch, so
+  // there the accumulators are scaled once up front instead (fewer spills measured).  The
+  // bf16 instantiations keep their own copies of those loops.
+  constexpr bool FOLD = F8 && !SHAREDV;
   if constexpr (F8) {
-    // the weight scales: acc becomes W e / s_e (per feature: k_f or v_f over the token
-    // scale), after which the epilogues are those of the bf16 operands
     s_fs[etid] = fs;
     lds_barrier();
+  }
+  if constexpr (F8 && !FOLD) {
 #pragma unroll
     for (int i = 0; i < MF; ++i)
 #pragma unroll
@@ -937,6 +945,11 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
           for (int r = 0; r < 8; ++r) acc[i][j][gp * 8 + r] *= g[r];
       }
   }
+#define ENGRAM_WS(fl_, ws_)                                                                 \
+  const float4 ws_##_lo = *reinterpret_cast<const float4*>(s_fs + (fl_));                   \
+  const float4 ws_##_hi = *reinterpret_cast<const float4*>(s_fs + (fl_) + 4);               \
+  const float ws_[8] = {ws_##_lo.x, ws_##_lo.y, ws_##_lo.z, ws_##_lo.w,                     \
+                        ws_##_hi.x, ws_##_hi.y, ws_##_hi.z, ws_##_hi.w}
   if (PHASE == PHASE_K) {
 #pragma unroll
     for (int j = 0; j < MT; ++j) {
@@ -954,6 +967,23 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
         }
       if constexpr (!KEYP) {
         float dot = 0.f, hh = 0.f, dot2 = 0.f, hh2 = 0.f;  // two chains each
+        if constexpr (FOLD) {
+#pragma unroll
+          for (int i = 0; i < MF; ++i) {
+#pragma unroll
+            for (int gp = 0; gp < 2; ++gp) {
+              ENGRAM_WS(ewf * WF + i * 32 + gp * 16 + hsel, ws);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const float h0 = bf16_lo(hv[i][gp][q]), h1 = bf16_hi(hv[i][gp][q]);
+                dot += h0 * (acc[i][j][gp * 8 + 2 * q] * ws[2 * q]);
+                dot2 += h1 * (acc[i][j][gp * 8 + 2 * q + 1] * ws[2 * q + 1]);
+                hh += h0 * h0;
+                hh2 += h1 * h1;
+              }
+            }
+          }
+        } else {
 #pragma unroll
         for (int i = 0; i < MF; ++i) {
 #pragma unroll
@@ -967,6 +997,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
               hh2 += h1 * h1;
             }
           }
+        }
         }
         dot += dot2;
         hh += hh2;
@@ -988,10 +1019,20 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
             const float4 g1 = *reinterpret_cast<const float4*>(s_g + fl + 4);
             const float g[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
             const float vm = f0 + fl < d_model ? 1.f : 0.f;
+            float ws[8] = {};
+            if constexpr (FOLD) {
+              ENGRAM_WS(fl, wf8);
+#pragma unroll
+              for (int r = 0; r < 8; ++r) ws[r] = wf8[r];
+            }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const float h0 = bf16_lo(hv[i][gp][q]), h1 = bf16_hi(hv[i][gp][q]);
-              const float a0 = acc[i][j][gp * 8 + 2 * q], a1 = acc[i][j][gp * 8 + 2 * q + 1];
+              float a0 = acc[i][j][gp * 8 + 2 * q], a1 = acc[i][j][gp * 8 + 2 * q + 1];
+              if constexpr (FOLD) {
+                a0 *= ws[2 * q];
+                a1 *= ws[2 * q + 1];
+              }
               dot += h0 * g[2 * q] * a0;
               dot2 += h1 * g[2 * q + 1] * a1;
               hh += h0 * h0;
@@ -1119,6 +1160,21 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
           for (int gp = 0; gp < 2; ++gp)
             hv[i][gp] = *reinterpret_cast<const u32x4*>(
                 smem + ENGRAM_HOFF(tl, (ewf * WF + i * 32 + gp * 16 + hsel) >> 3));
+        if constexpr (FOLD) {
+#pragma unroll
+          for (int i = 0; i < MF; ++i) {
+#pragma unroll
+            for (int gp = 0; gp < 2; ++gp) {
+              ENGRAM_WS(ewf * WF + i * 32 + gp * 16 + hsel, ws);
+              u32x4 ov;
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                ov[q] = pack_bf16(bf16_lo(hv[i][gp][q]) + alpha * (acc[i][j][gp * 8 + 2 * q] * ws[2 * q]),
+                                  bf16_hi(hv[i][gp][q]) + alpha * (acc[i][j][gp * 8 + 2 * q + 1] * ws[2 * q + 1]));
+              *reinterpret_cast<u32x4*>(smem + ENGRAM_HOFF(tl, (ewf * WF + i * 32 + gp * 16 + hsel) >> 3)) = ov;
+            }
+          }
+        } else {
 #pragma unroll
         for (int i = 0; i < MF; ++i) {
 #pragma unroll
@@ -1130,6 +1186,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
                                 bf16_hi(hv[i][gp][q]) + alpha * acc[i][j][gp * 8 + 2 * q + 1]);
             *reinterpret_cast<u32x4*>(smem + ENGRAM_HOFF(tl, (ewf * WF + i * 32 + gp * 16 + hsel) >> 3)) = ov;
           }
+        }
         }
       }
       lds_barrier();
@@ -1148,9 +1205,17 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
 #pragma unroll
             for (int gp = 0; gp < 2; ++gp) {
               u32x4 ov;
+              if constexpr (FOLD) {
+                ENGRAM_WS(ewf * WF + i * 32 + gp * 16 + hsel, ws);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                  ov[q] = pack_bf16(alpha * (acc[i][j][gp * 8 + 2 * q] * ws[2 * q]),
+                                    alpha * (acc[i][j][gp * 8 + 2 * q + 1] * ws[2 * q + 1]));
+              } else {
 #pragma unroll
               for (int q = 0; q < 4; ++q)
                 ov[q] = pack_bf16(alpha * acc[i][j][gp * 8 + 2 * q], alpha * acc[i][j][gp * 8 + 2 * q + 1]);
+              }
               *reinterpret_cast<u32x4*>(smem + ENGRAM_HOFF(tl, (ewf * WF + i * 32 + gp * 16 + hsel) >> 3)) = ov;
             }
           }
@@ -1198,6 +1263,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
     }
   }
   ENGRAM_STAMP(6);
+#undef ENGRAM_WS
 #undef ENGRAM_HOFF
 #undef ENGRAM_QSLOT
 }
