@@ -65,6 +65,9 @@ def parse():
                    help="every branch uses branch 0's W_V (the paper's Eq. 6): W_V e is computed once")
     p.add_argument("--key-norm", choices=("memory", "projected"), default="memory",
                    help="memory: k = W_K RMSNorm(e) (default); projected: k = RMSNorm(W_K e), Eq. 4")
+    p.add_argument("--key-form", choices=("auto", "feature", "memory"), default="auto",
+                   help="the bf16 gate's key tiles: chosen by shape (auto, the library's default), "
+                        "feature-major, or memory-major where that form applies (A/B measurements)")
     p.add_argument("--fp8", action="store_true",
                    help="gate projections on E4M3 codes (engram_gate_forward_fp8; quantization inside the call)")
     p.add_argument("--no-fp8", action="store_true", help="skip the extra fp8-gate step measurement")
@@ -105,6 +108,8 @@ def workload_desc(cfg, args=None):
     if args is not None and (args.shared_wv or args.key_norm != "memory" or args.fp8):
         extra = {"key_norm": args.key_norm, "shared_wv": bool(args.shared_wv),
                  "gate_projections": "fp8 e4m3, per-row scales" if args.fp8 else "bf16"}
+    if args is not None and getattr(args, "key_form", "auto") != "auto":
+        extra["gate_key_tiles"] = args.key_form
     return {**extra,
         "workload": cfg.name,
         "tokens": cfg.tokens, "batch": cfg.batch, "seq_len": cfg.seq,
@@ -303,6 +308,7 @@ def timeline(args):
     from hashed_gram_embedding_hash_amd import build as hb
     eg.LIB_PATH = hb.TIMELINE_LIB  # before anything loads the library
     L = eg.lib()
+    eg.engram_debug_gate_key_form(args.key_form)
     L.engram_gate_timeline_read.argtypes = [ctypes.c_void_p, ctypes.c_int64]
     L.engram_gate_timeline_read.restype = ctypes.c_int
     L.engram_gate_timeline_clear.argtypes = []
@@ -339,7 +345,7 @@ def timeline(args):
     starts = np.where(done, t[:, :, 0], np.iinfo(np.int64).max).min(axis=1)[used]
     ends = np.where(done, t[:, :, 7], 0).max(axis=1)[used]
     span = (ends.max() - t0) * us
-    out = {"timeline": cfg.name, "gate": "fp8" if args.fp8 else "bf16",
+    out = {"timeline": cfg.name, "gate": "fp8" if args.fp8 else "bf16", "key_tiles": args.key_form,
            "gate_call_ms_events": round(a.elapsed_time(b), 4),
            "workgroups": int(used.sum()), "tiles": int(done.sum()),
            "span_us": round(span, 1), "start_skew_us_max": round(float((starts - t0).max()) * us, 2),
@@ -1003,7 +1009,9 @@ def run_workload(args, name, secondary=False):
     ms_step, ms_eager, per, t_wall = time_steps(make_step(args.fp8), args.steps, args.warmup, not args.no_graph)
 
     # The same step as one call, engram_lookup_gate: the gate's kernel hashes each token and
-    # loads the table rows itself (the memory vectors are never stored); bit-identical results.
+    # loads the table rows itself (the memory vectors are never stored).  Its key tiles are
+    # feature-major: bit-identical to the two calls with feature-major key tiles, and within
+    # the fp32 rounding of the logit's sum of them with memory-major ones.
     fused_step = None
     if cfg.dtype == "bf16" and not args.fp8 and not args.no_fused:
         def fused(ev=None):
@@ -1083,7 +1091,8 @@ def run_workload(args, name, secondary=False):
         separate_calls["gate_prepared_weights"] = {
             "ms": round(prepared, 5), "TFLOP/s": round(work["gate"]["flops"] / (prepared * 1e-3) / 1e12, 2),
             "note": "engram_gate_forward_prepared on key weights folded once by engram_gate_prepare "
-                    "(bit-identical results; no per-call folding kernel), timed eagerly after the cache flush"}
+                    "(feature-major key tiles: bit-identical to engram_gate_forward's of that form; no "
+                    "per-call folding kernel), timed eagerly after the cache flush"}
     gate_s = per["gate"] * 1e-3
     if cfg.dtype == "bf16" and args.fp8:
         peak, dtype = PEAK_FP8_TFLOPS, "fp8e4m3 projections, bf16 storage"
@@ -1096,8 +1105,9 @@ def run_workload(args, name, secondary=False):
     traffic = measured_traffic(cfg) if cfg.dtype == "bf16" and default_gate else None
     kernel = ("engram_gate_forward_fp8: gate_prep_projected_kernel + quant_rows_kernel (W_K, W_V, mem) + "
               "gate_persistent_kernel (events bracket all)" if args.fp8 else
-              "engram_gate_forward: gate_prep_kernel + gate_persistent_kernel "
-              "(events bracket both; the prep kernel is about 3 % of the call)")
+              "engram_gate_forward: the key-weight fold (gate_prep_kernel, or gate_prep_t_kernel for "
+              "memory-major key tiles) + gate_persistent_kernel (events bracket both; the fold is about "
+              "3 % of the call)")
     roofline = {"kernel": kernel,
                 "bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic,
@@ -1198,6 +1208,10 @@ def main():
     if args.timeline:
         timeline(args)
         return
+
+    if args.key_form != "auto":
+        import hashed_gram_embedding_hash_amd as eg
+        eg.engram_debug_gate_key_form(args.key_form)
 
     if args.config == "offload":
         run_offload(args)

@@ -60,6 +60,7 @@ EXPORTS = (
     "engram_compress_hash", "engram_quantize_fp8", "engram_gate_forward_fp8", "engram_lookup",
     "engram_lookup_fp8", "engram_gate_prepare_fp8", "engram_gate_forward_fp8q", "engram_gate_prepare",
     "engram_gate_forward_prepared", "engram_gate_wait_timeouts", "engram_debug_force_gate_timeout",
+    "engram_debug_gate_key_form",
     "engram_gate_forward_noalloc", "engram_lookup_gate",
 )
 
@@ -116,6 +117,7 @@ def lib() -> ctypes.CDLL:
         L.engram_prefetch_host_cached.argtypes = [P, i64, i32, P, P, i32, i32, P, i32, P, P, P, P, P]
         L.engram_gate_wait_timeouts.argtypes = [ctypes.POINTER(i32), i32]
         L.engram_debug_force_gate_timeout.argtypes = [i32]
+        L.engram_debug_gate_key_form.argtypes = [i32]
         L.engram_lookup_gate.argtypes = [P, i32, i64, i64, i64, P, i32, P, i32, i32, P, P, i32, P, i32, i32, i32,
                                          P, P, P, P, P, ctypes.c_float, i32, P, P, P, P, P, P]
         for f in ("engram_compress", "engram_hash", "engram_gather", "engram_gate_forward",
@@ -124,7 +126,8 @@ def lib() -> ctypes.CDLL:
                   "engram_compress_hash", "engram_quantize_fp8", "engram_gate_forward_fp8", "engram_lookup",
                   "engram_lookup_fp8", "engram_gate_prepare_fp8", "engram_gate_forward_fp8q",
                   "engram_gate_prepare", "engram_gate_forward_prepared", "engram_gate_wait_timeouts",
-                  "engram_debug_force_gate_timeout", "engram_gate_forward_noalloc", "engram_lookup_gate"):
+                  "engram_debug_force_gate_timeout", "engram_debug_gate_key_form", "engram_gate_forward_noalloc",
+                  "engram_lookup_gate"):
             getattr(L, f).restype = st
         _lib = L
     return _lib
@@ -729,6 +732,15 @@ def engram_gate_wait_timeouts(reset: bool = False) -> int:
 def engram_debug_force_gate_timeout(on: bool):
     """Test hook: make every later gate launch's value-tile wait give up (see engram.h)."""
     _check(lib().engram_debug_force_gate_timeout(1 if on else 0))
+
+
+GATE_KEY_FORMS = {"auto": 0, "feature": 1, "memory": 2}
+
+
+def engram_debug_gate_key_form(form: str):
+    """Test hook: the gate's key-tile form, "auto" (by shape, the default), "feature"
+    (feature-major) or "memory" (memory-major where it applies); see engram.h."""
+    _check(lib().engram_debug_gate_key_form(GATE_KEY_FORMS[form]))
 
 
 def host_alloc(nbytes: int) -> int:

@@ -582,6 +582,12 @@ engram_status engram_debug_force_gate_timeout(int32_t on) {
   return ENGRAM_OK;
 }
 
+engram_status engram_debug_gate_key_form(int32_t form) {
+  if (form < 0 || form > 2) return fail(ENGRAM_ERR_INVALID_ARG, "engram_debug_gate_key_form: form %d not 0, 1 or 2", form);
+  set_gate_key_form(form);
+  return ENGRAM_OK;
+}
+
 engram_status engram_gate_forward_fp8(const void* mem, int64_t n_tok, int32_t d_mem, int32_t d_model,
                                       int32_t n_branch, const void* const* h, const void* const* wk,
                                       const void* const* wv, const void* const* gq,

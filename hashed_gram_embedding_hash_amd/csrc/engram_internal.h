@@ -103,9 +103,9 @@ struct GateArgs {
   void* out[ENGRAM_MAX_BRANCHES];
   void* vout[ENGRAM_MAX_BRANCHES];  // gated values alpha * v, or null per branch
   float* gate_out;   // [n_branch][n_tok] or null
-  float* part_dot;   // scratch: [n_branch][n_ftiles][n_tok]
-  float* part_hh;    // scratch: [n_branch][n_ftiles][n_tok]
-  float* ee;         // scratch: [n_branch][n_ftiles][n_tok] partial sums of e^2
+  float* part_dot;   // scratch: [n_branch][n_ftiles][n_tok] (the first n_ktiles of each branch used)
+  float* part_hh;    // scratch: [n_branch][n_ftiles][n_tok] partial sums of h^2 (memory-major: e^2)
+  float* ee;         // scratch: [n_branch][n_ftiles][n_tok] partial sums of e^2 (memory-major: h^2)
   float* alpha;      // scratch: [n_branch][n_tok] gates, published by the last K tile of a token tile
   int32_t* counters; // scratch: per-queue tile heads, then per-(branch, token tile) done counts
   float* kgain;      // scratch, projected key norm: [n_branch][d_model] gq * gk
@@ -120,10 +120,13 @@ struct GateArgs {
   const float* e_ssq;
   const float* sk[ENGRAM_MAX_BRANCHES];
   const float* sv[ENGRAM_MAX_BRANCHES];
-  // the V tiles' bounded wait: the done count it needs is n_ftiles + 1 + wait_extra
+  // the V tiles' bounded wait: the done count it needs is n_ktiles + 1 + wait_extra
   // (wait_extra is 0 except under the forced-timeout test hook), polled at most
   // spin_limit times (set by launch_gate_bf16)
   int32_t wait_extra, spin_limit;
+  // K tiles per (branch, token tile), set by launch_gate_bf16: n_ftiles, or with the key
+  // phase contracted over d_model (memory-major K tiles) ceil(d_mem / 256) <= n_ftiles
+  int32_t n_ktiles;
 };
 // engram_lookup_gate: the bf16 gate reads its memory rows straight from the tables.
 // Position p's row in table b starts at tab[b] + z * cpr * 16 bytes, with
@@ -167,6 +170,9 @@ void launch_gate_f32(const GateArgs& a, hipStream_t s);
 hipError_t gate_wait_timeouts(int32_t* count, bool reset);
 // Test hook behind engram_debug_force_gate_timeout.
 void set_gate_forced_wait_timeout(bool on);
+// Test hook behind engram_debug_gate_key_form: 0 chooses the K tiles' form by shape,
+// 1 always feature-major, 2 memory-major wherever that form applies.
+void set_gate_key_form(int form);
 // engram_gate_forward_noalloc's bf16 launch on the library's fixed device array (a is
 // checked and filled by the caller; the scratch pointer is set here).
 engram_status gate_forward_noalloc(const char* fn, GateArgs& a, hipStream_t stream);

@@ -25,6 +25,10 @@
 //           is published (usually long before) and writes out = h + alpha acc.
 // Since q . k = (sum_f h_f gq_f k~_f) / (rms(h) rms(e)) with k~ = W_K diag(gk) e,
 // the RMSNorm scales are applied to the reduced scalar, never to a tensor.
+// The same sum is also sum_c e_c u_c with u = W_K'^T h: with d_mem < d_model and
+// enough tokens the K tiles take that memory-major form (TK below: tiles of 256 memory
+// dimensions contracting over d_model, h streamed, the memory rows in the epilogue),
+// fewer and longer tiles for the same FLOPs.
 //
 // Scheduling.  One persistent launch of one workgroup per CU.  Workgroup b
 // serves work queue b % 8 (the XCD it is dispatched to), which holds the token
@@ -255,9 +259,43 @@ __device__ __forceinline__ void blocked(int r, int n_tt, int per, int& tt, int& 
   combo = cb * CBN + rb % cbs;
 }
 
-template <bool SHAREDV, bool GATHER>
+// The same order with run-time block sizes (memory-major K tiles).
+__device__ __forceinline__ void blocked_rt(int r, int n_tt, int per, int ttg, int cbn, int& tt, int& combo) {
+  const int g = r / (ttg * per);
+  const int ntt = min(ttg, n_tt - g * ttg);
+  const int rg = r - g * ttg * per;
+  const int cb = rg / (ntt * cbn);
+  const int cbs = min(cbn, per - cb * cbn);
+  const int rb = rg - cb * ntt * cbn;
+  tt = g * ttg + rb / cbs;
+  combo = cb * cbn + rb % cbs;
+}
+
+template <bool SHAREDV, bool GATHER, bool TK>
 __device__ __forceinline__ bool decode_tile(const GateArgs& a, int x, int q, Tile& t) {
   const int n_tt = a.n_ttiles > x ? (a.n_ttiles - x + NQ - 1) / NQ : 0;  // token tiles of queue x
+  if constexpr (TK) {
+    // n_ktiles K tiles per (branch, token tile), n_ftiles V tiles
+    const int per_k_tt = a.n_branch * a.n_ktiles;
+    const int per_v_tt = SHAREDV ? a.n_ftiles : a.n_branch * a.n_ftiles;
+    const int per_k = n_tt * per_k_tt;
+    const int per_v = n_tt * per_v_tt;
+    if (q >= per_k + per_v) return false;
+    t.phase = q >= per_k ? PHASE_V : PHASE_K;
+    const int r = q - (t.phase == PHASE_V ? per_k : 0);
+    const int per = t.phase == PHASE_V ? per_v_tt : per_k_tt;
+    int tl, combo;
+    // K tiles stream h, which is per branch: a block is one branch's n_ktiles tiles of
+    // about 32 / n_ktiles token tiles, so an XCD's 32 CUs share each h tile n_ktiles ways
+    // and each weight panel that many token tiles' ways
+    if (t.phase == PHASE_K) blocked_rt(r, n_tt, per, max(1, 32 / a.n_ktiles), a.n_ktiles, tl, combo);
+    else blocked<TT_GROUP, CB>(r, n_tt, per, tl, combo);
+    const int nt = t.phase == PHASE_V ? a.n_ftiles : a.n_ktiles;  // output tiles per branch
+    t.m = combo / nt;
+    t.ftile = combo - t.m * nt;
+    t.ttile = tl * NQ + x;
+    return true;
+  }
   const int per_tt = a.n_branch * a.n_ftiles;
   const int per_k = n_tt * per_tt;
   const int per_v = SHAREDV ? n_tt * a.n_ftiles : per_k;
@@ -292,15 +330,26 @@ __device__ __forceinline__ bool decode_tile(const GateArgs& a, int x, int q, Til
 //           weight the epilogues from LDS, the token scale joins the reduced scalars;
 //   GATHER  (bf16) the memory rows are not read from a memory-vector array: each lane
 //           hashes its token's n-grams and its direct loads read the table rows in
-//           place (gs, a GatherSrc; NoGather otherwise).
+//           place (gs, a GatherSrc; NoGather otherwise);
+//   TK      (bf16, memory-side key norm) memory-major K tiles.  The logit's dot product
+//           is also sum_c u_c e_c with u = W_K'^T h: a K tile computes u for 256 memory
+//           dimensions c x 256 tokens, contracting over d_model (a.wk[m] then holds
+//           W_K'^T, [d_mem][d_model]), with h as the streamed token operand and the
+//           memory rows as the epilogue tile.  Its epilogue reduces sum_c e_c u_c and
+//           sum_c e_c^2, its main loop sums h^2 over one slice of d_model.  Same FLOPs,
+//           but ceil(d_mem / 256) K tiles per (branch, token tile) instead of
+//           ceil(d_model / 256), each d_model / 64 k-steps long: the fixed cost of a
+//           tile's edges (first operands, epilogue, publishing) is paid fewer times.
+//           The V tiles are the feature-major ones of the other instantiations.
 struct NoGather {};
 
-template <bool VALUES, bool KEYP, bool SHAREDV, bool F8, bool GATHER, class GS>
+template <bool VALUES, bool KEYP, bool SHAREDV, bool F8, bool GATHER, bool TK, class GS>
 __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const Tile& tile, char* smem, int x,
                                           int& next_claim, int tl_n) {
   ENGRAM_STAMP(1);
   ENGRAM_STAMP_TILE(tile);
   static_assert(!(GATHER && F8), "the gathering gate is bf16");
+  static_assert(!TK || (!KEYP && !F8 && !GATHER), "memory-major K tiles: bf16, memory-side key norm, no gather");
   const int PHASE = tile.phase;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -317,9 +366,16 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
   const uint16_t* W = (const uint16_t*)(PHASE == PHASE_K ? a.wk[m] : a.wv[m]);
   const uint16_t* E = (const uint16_t*)a.mem;
   const uint16_t* H = (const uint16_t*)a.h[m];
+  // TK K tiles swap the roles of the memory rows and h: Lrow is the length of the
+  // streamed rows (the contraction depth), Dout the extent of the tile's output rows and
+  // the row length of its epilogue tile
+  const bool tk = TK && PHASE == PHASE_K;
+  const int Lrow = tk ? d_model : d_mem;
+  const int Dout = tk ? d_mem : d_model;
+  const int nkt = tk ? a.n_ktiles : a.n_ftiles;  // tiles sharing this tile's token rows and phase
 
   // ---- V tiles need the gates of their (branch, token tile), published by its last K
-  // tile (done count n_ftiles + 1), only in the epilogue.  Each wave looks at the count
+  // tile (done count n_ktiles + 1), only in the epilogue.  Each wave looks at the count
   // once here: if the gates are out, it fetches its tokens' gates now and the loads
   // complete behind the main loop; if not, it runs the main loop anyway and waits after
   // it (with few tiles in flight, as in a decode step, V tiles then overlap K tiles).
@@ -330,7 +386,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
     if (lane == 0) {
       for (int mb = SHAREDV ? 0 : m; mb < (SHAREDV ? a.n_branch : m + 1); ++mb)
         seen &= __hip_atomic_load(a.counters + NQ + mb * a.n_ttiles + tile.ttile, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT) >= a.n_ftiles + 1 + a.wait_extra;
+                                  __HIP_MEMORY_SCOPE_AGENT) >= (TK ? a.n_ktiles : a.n_ftiles) + 1 + a.wait_extra;
     }
     gates_ready = __builtin_amdgcn_readfirstlane(seen) != 0;
     // issued only after lane 0's count came back (the branch depends on it)
@@ -359,9 +415,11 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
   //
   // Instruction i of wave w fills rows 64 w + 8 i .. + 7 of a chunk: lane l reads
   // row 64 w + 8 i + l / 8 at physical chunk l % 8 (logical (l % 8) ^ row_key).
-  const int nk = d_mem / (F8 ? 2 * BK : BK);  // k-steps of 128 bytes per row
-  const uint16_t* Et0 = E + t0 * d_mem;   // memory rows of this token tile
-  const uint16_t* Ht0 = H + t0 * d_model;
+  const int nk = Lrow / (F8 ? 2 * BK : BK);  // k-steps of 128 bytes per row
+  // the streamed token rows of this token tile (memory rows; TK K tiles: h rows) and the
+  // rows of its epilogue tile (h; TK K tiles: memory rows)
+  const uint16_t* Et0 = tk ? H + t0 * d_model : E + t0 * d_mem;
+  const uint16_t* Ht0 = tk ? E + t0 * d_mem : H + t0 * d_model;
   const int b_lim = (int)(n_tok - 1 - t0);  // last valid row of the token tile
   uint32_t off_a[G_INSTR], off_b[G_INSTR];
 #pragma unroll
@@ -370,8 +428,8 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
     const int cl = (lane & 7) ^ row_key(r);
     // weight rows are permuted (tile_row_feature); rows past the end are clamped to
     // the last valid one (their results are unused)
-    off_a[i] = (uint32_t)min(f0 + tile_row_feature(r), d_model - 1) * (uint32_t)d_mem + cl * (F8 ? 16 : 8);
-    off_b[i] = (uint32_t)min(r, b_lim) * (uint32_t)d_mem + cl * (F8 ? 16 : 8);
+    off_a[i] = (uint32_t)min(f0 + tile_row_feature(r), Dout - 1) * (uint32_t)Lrow + cl * (F8 ? 16 : 8);
+    off_b[i] = (uint32_t)min(r, b_lim) * (uint32_t)Lrow + cl * (F8 ? 16 : 8);
   }
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr)smem;
   const uint32_t wave_dst = lds0 + (uint32_t)(wave * G_INSTR * 1024);
@@ -517,8 +575,8 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
       const int c = (hl & 31) ^ (tl & 31);
       const int tr = tl < b_lim ? tl : b_lim;
       int f = f0 + c * 8;
-      f = f < d_model ? f : 0;
-      dma16(Ht0 + (uint32_t)tr * (uint32_t)d_model + f, dst + (uint32_t)(blk * 1024));
+      f = f < Dout ? f : 0;
+      dma16(Ht0 + (uint32_t)tr * (uint32_t)Dout + f, dst + (uint32_t)(blk * 1024));
     }
   };
   // FP8: the operands are byte arrays (offsets above are in bytes)
@@ -633,8 +691,8 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
       }                                                                                    \
     }                                                                                      \
   } while (0)
-  // Sum of e^2 over the k-steps kt with kt % n_ftiles == ftile, from the memory
-  // fragments: waves with wf == 0 see every token row of the tile (lanes l and l+32
+  // Sum of e^2 (TK K tiles: h^2) over the k-steps kt with kt % nkt == ftile, from the
+  // token-row fragments: waves with wf == 0 see every token row of the tile (lanes l and l+32
   // hold the two halves of a sub-step's 16 columns).
   float ee_acc[MT];
 #pragma unroll
@@ -688,7 +746,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
     __builtin_amdgcn_sched_barrier(0);                                                     \
     ENGRAM_GROUP(1, 0, 0, sa_, sb_, dma_, true, b0_, o0_, k0_, s0_, 0);                    \
     if (ee_now) ENGRAM_EE(1);                                                              \
-    ee_now = ee_wave && ((kt) % a.n_ftiles) == ftile;                                      \
+    ee_now = ee_wave && ((kt) % nkt) == ftile;                                             \
     ENGRAM_GROUP(0, 1, 1, sa_, sb_, dma_, true, b0_, o0_, k0_, s0_, 4);                    \
     if (ee_now) ENGRAM_EE(0);                                                              \
     /* GATHER: the next iteration's row numbers; the wait at the end covers them */      \
@@ -722,7 +780,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
     ENGRAM_MFMAS(1);
     __builtin_amdgcn_sched_barrier(0);
     if (ee_now) ENGRAM_EE(1);
-    ee_now = ee_wave && (kt % a.n_ftiles) == ftile;
+    ee_now = ee_wave && (kt % nkt) == ftile;
     ENGRAM_LOAD_FRAGS(1, sa, sb, 1);
     __builtin_amdgcn_sched_barrier(0);
     ENGRAM_MFMAS(0);
@@ -890,7 +948,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
         int spin = 0;
         for (int mb = SHAREDV ? 0 : m; mb < (SHAREDV ? a.n_branch : m + 1) && !out_of_polls; ++mb) {
           const int32_t* dn = a.counters + NQ + mb * a.n_ttiles + tile.ttile;
-          while (__hip_atomic_load(dn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < a.n_ftiles + 1 + a.wait_extra) {
+          while (__hip_atomic_load(dn, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (TK ? a.n_ktiles : a.n_ftiles) + 1 + a.wait_extra) {
             if (++spin >= a.spin_limit) {
               out_of_polls = 1;
               break;
@@ -955,7 +1013,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
     for (int j = 0; j < MT; ++j) {
       const int tl = ewt * WT + j * 32 + (elane & 31);
       // all eight cells first (no LDS writes in between, so the reads issue back to
-      // back); features past d_model (a ragged last feature tile) count as zero
+      // back); rows past Dout (a ragged last tile) count as zero
       u32x4 hv[MF][2];
 #pragma unroll
       for (int i = 0; i < MF; ++i)
@@ -963,7 +1021,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
         for (int gp = 0; gp < 2; ++gp) {
           const int fl = ewf * WF + i * 32 + gp * 16 + hsel;
           hv[i][gp] = *reinterpret_cast<const u32x4*>(smem + ENGRAM_HOFF(tl, fl >> 3));
-          if (f0 + fl >= d_model) hv[i][gp] = (u32x4){0u, 0u, 0u, 0u};
+          if (f0 + fl >= Dout) hv[i][gp] = (u32x4){0u, 0u, 0u, 0u};
         }
       if constexpr (!KEYP) {
         float dot = 0.f, hh = 0.f, dot2 = 0.f, hh2 = 0.f;  // two chains each
@@ -1073,14 +1131,14 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
     if (etid == 0) *s_flag = __hip_atomic_fetch_add(done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     lds_barrier();
     ENGRAM_STAMP(11);
-    if (*s_flag == a.n_ftiles - 1) {
+    if (*s_flag == nkt - 1) {
       // The last K tile of this (branch, token tile): every other one stored its
       // partials before its increment, so all are in L2.  Turn them into gates
       // (fixed-order sums: bit-reproducible), publish, and count once more.
       const int64_t t = t0 + etid;
       if (t < n_tok) {
-        const int nf = a.n_ftiles;
-        const int64_t base = (int64_t)m * nf * n_tok + t;
+        const int nf = nkt;  // partials of this branch's K tiles (stride n_ftiles per branch)
+        const int64_t base = (int64_t)m * a.n_ftiles * n_tok + t;
         float dot = 0.f, hh = 0.f, ee = 0.f;
         for (int j0 = 0; j0 < nf; j0 += 8) {  // eight of each in flight at once
           float vd[8], vh[8], ve[8];
@@ -1106,9 +1164,11 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
           dot *= se;
           ee = KEYP ? ee * se * se : a.e_ssq[t];
         }
-        const float rms_h = sqrtf(hh / (float)d_model + a.eps);
+        // TK: the epilogues summed e^2 (hh) and the main loops h^2 (ee)
+        const float ssq_h = TK ? ee : hh, ssq_k = TK ? hh : ee;
+        const float rms_h = sqrtf(ssq_h / (float)d_model + a.eps);
         // the key's norm: of the memory vector (d_mem wide), or KEYP of W_K e (d_model)
-        const float rms_e = sqrtf(ee / (float)(KEYP ? d_model : d_mem) + a.eps);
+        const float rms_e = sqrtf(ssq_k / (float)(KEYP ? d_model : d_mem) + a.eps);
         const float logit = dot / (rms_h * rms_e) * a.inv_sqrt_d;
         const float g = 1.f / (1.f + expf(-logit));
         st_coherent(a.alpha + (int64_t)m * n_tok + t, g);
@@ -1271,7 +1331,7 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
 // The persistent workgroup: claims tiles from its queue until the queue is exhausted.
 // smem: the operand ring, then the h tile and the epilogue scratch; between tiles its
 // first word broadcasts the claimed tile number.
-template <bool VALUES, bool KEYP, bool SHAREDV, bool F8, bool GATHER, class GS>
+template <bool VALUES, bool KEYP, bool SHAREDV, bool F8, bool GATHER, bool TK, class GS>
 __device__ __forceinline__ void persistent_loop(const GateArgs& a, const GS& gs, char* smem) {
   int* s_tile = reinterpret_cast<int*>(smem);
   const int x = blockIdx.x % NQ;
@@ -1282,10 +1342,10 @@ __device__ __forceinline__ void persistent_loop(const GateArgs& a, const GS& gs,
     if (threadIdx.x == 0) *s_tile = claim;
     lds_barrier();
     Tile t;
-    const bool have = decode_tile<SHAREDV, GATHER>(a, x, *s_tile, t);
+    const bool have = decode_tile<SHAREDV, GATHER, TK>(a, x, *s_tile, t);
     lds_barrier();  // every thread has read the tile number before the ring is refilled
     if (!have) break;
-    gate_tile<VALUES, KEYP, SHAREDV, F8, GATHER>(a, gs, t, smem, x, claim, tl_n);
+    gate_tile<VALUES, KEYP, SHAREDV, F8, GATHER, TK>(a, gs, t, smem, x, claim, tl_n);
     // LDS free for the next tile.  A full barrier: letting a V tile's 128 KB of output
     // stores drain behind the next tile's operand loads measured 8 % slower than
     // finishing them first.
@@ -1294,11 +1354,11 @@ __device__ __forceinline__ void persistent_loop(const GateArgs& a, const GS& gs,
   }
 }
 
-template <bool VALUES, bool KEYP, bool SHAREDV, bool F8>
+template <bool VALUES, bool KEYP, bool SHAREDV, bool F8, bool TK>
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gate_persistent_kernel(const GateArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[SMEM_BYTES];
-  persistent_loop<VALUES, KEYP, SHAREDV, F8, false>(a, NoGather{}, smem);
+  persistent_loop<VALUES, KEYP, SHAREDV, F8, false, TK>(a, NoGather{}, smem);
 }
 
 // engram_lookup_gate: the same kernel reading its memory rows from the tables.
@@ -1306,7 +1366,7 @@ template <bool VALUES, bool KEYP, bool SHAREDV>
 __global__ __launch_bounds__(NTHR) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gate_gather_kernel(const GateArgs a, const GatherSrc gs) {
   __shared__ __attribute__((aligned(16))) char smem[SMEM_BYTES];
-  persistent_loop<VALUES, KEYP, SHAREDV, false, true>(a, gs, smem);
+  persistent_loop<VALUES, KEYP, SHAREDV, false, true, false>(a, gs, smem);
 }
 
 // KEYP: the per-feature key gain gq[m][f] * gk[m][f] in fp32 (exact: a product of two
@@ -1344,6 +1404,52 @@ __global__ __launch_bounds__(256) void gate_prep_kernel(const GateArgs a, uint16
   for (int q = 0; q < 4; ++q)
     o[q] = pack_bf16(gq * bf16_lo(wv[q]) * bf16_lo(gv[q]), gq * bf16_hi(wv[q]) * bf16_hi(gv[q]));
   reinterpret_cast<u32x4*>(wk_scaled)[i] = o;
+}
+
+// The same fold for memory-major K tiles, written transposed:
+// W'T[m][c][f] = bf16(gq[m][f] * W_K[m][f][c] * gk[m][c]), the same products rounded the same
+// way.  One workgroup per 64 x 64 block (d_model and d_mem multiples of 64): each thread
+// reads 16 consecutive c of one row f, the block turns in LDS, and each thread writes 16
+// consecutive f of one row c.  The counters are cleared grid-stride.
+__global__ __launch_bounds__(256) void gate_prep_t_kernel(const GateArgs a, uint16_t* wkt, int n_counters) {
+  __shared__ uint16_t blk[64][64 + 2];
+  const int tid = threadIdx.x;
+  const int64_t gid = ((int64_t)blockIdx.z * gridDim.y * gridDim.x + (int64_t)blockIdx.y * gridDim.x + blockIdx.x) * 256 + tid;
+  const int64_t nthreads = (int64_t)gridDim.x * gridDim.y * gridDim.z * 256;
+  for (int64_t i = gid; i < n_counters; i += nthreads) a.counters[i] = 0;
+  const int m = blockIdx.z;
+  const int f0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  const int d_mem = a.d_mem, d_model = a.d_model;
+  {
+    const int r = tid >> 2, cs = (tid & 3) * 16;
+    const uint16_t* src = (const uint16_t*)a.wk[m] + (int64_t)(f0 + r) * d_mem + c0 + cs;
+    const uint16_t* gks = (const uint16_t*)a.gk[m] + c0 + cs;
+    const float gq = __uint_as_float((uint32_t)((const uint16_t*)a.gq[m])[f0 + r] << 16);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const u32x4 wv = reinterpret_cast<const u32x4*>(src)[h];
+      const u32x4 gv = reinterpret_cast<const u32x4*>(gks)[h];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t o = pack_bf16(gq * bf16_lo(wv[q]) * bf16_lo(gv[q]), gq * bf16_hi(wv[q]) * bf16_hi(gv[q]));
+        blk[r][cs + h * 8 + 2 * q] = (uint16_t)(o & 0xffffu);
+        blk[r][cs + h * 8 + 2 * q + 1] = (uint16_t)(o >> 16);
+      }
+    }
+  }
+  __syncthreads();
+  {
+    const int c = tid >> 2, fs = (tid & 3) * 16;
+    uint16_t* dst = wkt + (int64_t)m * d_mem * d_model + (int64_t)(c0 + c) * d_model + f0 + fs;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      u32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        o[q] = (uint32_t)blk[fs + h * 8 + 2 * q][c] | ((uint32_t)blk[fs + h * 8 + 2 * q + 1][c] << 16);
+      reinterpret_cast<u32x4*>(dst)[h] = o;
+    }
+  }
 }
 
 // One W_V for every branch (the same pointer): W_V e is computed once per tile.
@@ -1391,6 +1497,8 @@ ScratchLayout layout_for(const GateArgs& a, bool fp8, bool prequant) {
 // Test hook: every later gate launch waits for a done count its K tiles never reach,
 // bounded by FORCED_SPIN_LIMIT polls, so the give-up path runs (and the kernel ends).
 std::atomic<bool> g_force_wait_timeout{false};
+// Test hook: the K tiles' form (0 by shape, 1 feature-major, 2 memory-major where it applies).
+std::atomic<int> g_key_form{0};
 
 int cu_count() {
   static int n[64] = {0};
@@ -1431,6 +1539,21 @@ void launch_gate_bf16(const GateArgs& a_in, bool fp8, hipStream_t s, bool prequa
   a.counters = (int32_t*)(base + L.wk_bytes + 3 * L.part_bytes + L.alpha_bytes);
 
   const bool keyp = a.key_norm == ENGRAM_KEY_NORM_PROJECTED;
+  int grid = cu_count() / NQ * NQ;
+  if (grid < NQ) grid = NQ;
+  // Memory-major K tiles (TK) where they apply (bf16 with the memory-side key norm and the
+  // folded weights made here, d_mem < d_model so their partials fit the feature-major
+  // layout, d_model a whole number of k-steps) and, chosen by shape, where they measured
+  // faster: at most two branches (each branch streams its own h through the K tiles; at
+  // four, the feature-major tiles, whose memory rows all branches share, were faster) and
+  // at least one K tile per CU (a decode step's one token tile would leave most CUs idle
+  // behind the longer tiles).
+  const int n_ctiles = (a.d_mem + BF - 1) / BF;
+  const int form = g_key_form.load(std::memory_order_relaxed);
+  const bool tk_ok = !fp8 && !prequant && gs == nullptr && !keyp && a.d_mem < a.d_model && a.d_model % BK == 0;
+  const bool tk = tk_ok && form != 1 &&
+                  (form == 2 || (a.n_branch <= 2 && (int64_t)a.n_ttiles * a.n_branch * n_ctiles >= (int64_t)grid));
+  a.n_ktiles = tk ? n_ctiles : a.n_ftiles;
   if (fp8) {
     // the key gains and the counters, then the E4M3 codes: W_K with both gains folded
     // in (memory-side key norm) or as is, W_V, and the memory vectors with their sums
@@ -1477,6 +1600,10 @@ void launch_gate_bf16(const GateArgs& a_in, bool fp8, hipStream_t s, bool prequa
   } else if (prequant) {
     hipLaunchKernelGGL(gate_prep_projected_kernel, dim3((unsigned)((L.n_counters + 255) / 256)), dim3(256), 0, s,
                        a, L.n_counters, false);
+  } else if (tk) {
+    hipLaunchKernelGGL(gate_prep_t_kernel, dim3((unsigned)(a.d_mem / 64), (unsigned)(a.d_model / 64),
+                                               (unsigned)a.n_branch), dim3(256), 0, s, a, wk_scaled, L.n_counters);
+    for (int m = 0; m < a.n_branch; ++m) a.wk[m] = wk_scaled + (size_t)m * a.d_model * a.d_mem;
   } else {
     const int64_t n8 = (int64_t)a.d_model * a.d_mem / 8;
     const int64_t work = n8 * a.n_branch > L.n_counters ? n8 * a.n_branch : L.n_counters;
@@ -1488,8 +1615,6 @@ void launch_gate_bf16(const GateArgs& a_in, bool fp8, hipStream_t s, bool prequa
   const bool forced = g_force_wait_timeout.load(std::memory_order_relaxed);
   a.wait_extra = forced ? 1 : 0;
   a.spin_limit = forced ? FORCED_SPIN_LIMIT : SPIN_LIMIT;
-  int grid = cu_count() / NQ * NQ;
-  if (grid < NQ) grid = NQ;
   bool values = false;
   for (int m = 0; m < a.n_branch; ++m) values = values || a.vout[m] != nullptr;
   const dim3 g((unsigned)grid), b(NTHR);
@@ -1508,9 +1633,20 @@ void launch_gate_bf16(const GateArgs& a_in, bool fp8, hipStream_t s, bool prequa
 #undef ENGRAM_GATHER_LAUNCH
     return;
   }
+  if (tk) {
+#define ENGRAM_TK_LAUNCH(V_, S_)                                                           \
+  if (values == V_ && shared_v == S_)                                                      \
+    hipLaunchKernelGGL((gate_persistent_kernel<V_, false, S_, false, true>), g, b, 0, s, a);
+    ENGRAM_TK_LAUNCH(false, false)
+    ENGRAM_TK_LAUNCH(false, true)
+    ENGRAM_TK_LAUNCH(true, false)
+    ENGRAM_TK_LAUNCH(true, true)
+#undef ENGRAM_TK_LAUNCH
+    return;
+  }
 #define ENGRAM_GATE_LAUNCH(V_, K_, S_, F_)                                                 \
   if (values == V_ && keyp == K_ && shared_v == S_ && fp8 == F_)                           \
-    hipLaunchKernelGGL((gate_persistent_kernel<V_, K_, S_, F_>), g, b, 0, s, a);
+    hipLaunchKernelGGL((gate_persistent_kernel<V_, K_, S_, F_, false>), g, b, 0, s, a);
   ENGRAM_GATE_LAUNCH(false, false, false, false)
   ENGRAM_GATE_LAUNCH(false, false, true, false)
   ENGRAM_GATE_LAUNCH(false, true, false, false)
@@ -1540,6 +1676,8 @@ hipError_t gate_wait_timeouts(int32_t* count, bool reset) {
 }
 
 void set_gate_forced_wait_timeout(bool on) { g_force_wait_timeout.store(on, std::memory_order_relaxed); }
+
+void set_gate_key_form(int form) { g_key_form.store(form, std::memory_order_relaxed); }
 
 void launch_gate_fold(const GateArgs& a_in, uint16_t* const* wk_folded, hipStream_t s) {
   const int64_t n8 = (int64_t)a_in.d_model * a_in.d_mem / 8;

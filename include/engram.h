@@ -220,8 +220,10 @@ engram_status engram_lookup_fp8(const int32_t* raw, int32_t batch, int64_t ld, i
  *        the input of the short convolution (engram_conv_forward).
  * Arithmetic: bf16 products with fp32 accumulation on the matrix cores, fp32
  * elsewhere; with ENGRAM_KEY_NORM_MEMORY the bf16 path folds both gains into a
- * copy of W_K rounded once to bf16.  ENGRAM_F32 (fp32 storage) computes every sum,
- * norm and the sigmoid in fp64 and rounds each output to fp32 once.
+ * copy of W_K rounded once to bf16, and sums the logit's dot product in fp32 over
+ * feature-major or memory-major key tiles, chosen by shape (engram_debug_gate_key_form):
+ * the results are reproducible bit for bit for given shapes.  ENGRAM_F32 (fp32 storage)
+ * computes every sum, norm and the sigmoid in fp64 and rounds each output to fp32 once.
  * Shapes: ENGRAM_BF16 needs d_mem % 64 == 0 and d_model % 32 == 0, d_model * d_mem
  * < 2^32 and n_tok < 2^31, and at most 2^29 tiles of 256 tokens x 256 features over
  * all branches; ENGRAM_F32 needs d_mem <= 16384 (d_mem + d_model <= 16384 with
@@ -281,6 +283,23 @@ engram_status engram_gate_wait_timeouts(int32_t* count, int32_t reset);
 engram_status engram_debug_force_gate_timeout(int32_t on);
 
 /*
+ * Test hook: the form of the key tiles of engram_gate_forward and
+ * engram_gate_forward_noalloc (bf16, memory-side key norm).  The logit's dot product
+ * q . k is the same sum in two tilings -- section 2.3, Eq. (4):
+ *   feature-major  sum_f h_f (W_K' e)_f, over d_model/256 tiles of 256 features, each
+ *                  contracting over d_mem;
+ *   memory-major   sum_c e_c (W_K'^T h)_c, over d_mem/256 tiles of 256 memory
+ *                  dimensions, each contracting over d_model (fewer, longer tiles).
+ * The two differ only in the fp32 rounding order of that sum.  form 0 (the default)
+ * chooses by shape: memory-major when d_mem < d_model, d_model % 64 == 0, n_branch <= 2
+ * and there are at least as many memory-major tiles as compute units; feature-major
+ * otherwise.  1 forces feature-major, 2 memory-major wherever it applies.  The setting is process-wide and
+ * read at each launch.  INVALID_ARG for another form; never set it outside tests and
+ * measurements.
+ */
+engram_status engram_debug_gate_key_form(int32_t form);
+
+/*
  * The bf16 gate with the memory-side key norm, its weights prepared once -- section
  * 2.3, Eq. (3)-(4), as engram_gate_forward computes them.  With this key placement
  * q . k = sum_f h_f gq_f (W_K diag(gk) e)_f / (rms(h) rms(e)), so both RMSNorm gains fold
@@ -291,9 +310,12 @@ engram_status engram_debug_force_gate_timeout(int32_t on);
  *   wk, wk_folded: host arrays of n_branch device pointers to [d_model][d_mem] bf16
  *   (wk_folded caller-allocated, 16-byte aligned).  gq[m]: [d_model]; gk[m]: [d_mem] bf16.
  * engram_gate_forward_prepared: engram_gate_forward(dtype ENGRAM_BF16, key_norm
- *   ENGRAM_KEY_NORM_MEMORY) with W_K replaced by wk_folded and no gains.  Its outputs are
- *   bit-identical to that call's with the weights and gains that were folded.  The other
- *   arguments are as for engram_gate_forward.
+ *   ENGRAM_KEY_NORM_MEMORY) with W_K replaced by wk_folded and no gains.  Its key tiles are
+ *   always feature-major (see engram_debug_gate_key_form): its outputs are bit-identical
+ *   to that call's with the weights and gains that were folded and that form (the form
+ *   engram_gate_forward chooses by itself for token counts that give each compute unit
+ *   fewer than two key tiles, as in decode steps).  The other arguments are as for
+ *   engram_gate_forward.
  * Both require d_mem % 64 == 0 and d_model % 32 == 0 (ENGRAM_ERR_UNSUPPORTED otherwise).
  */
 engram_status engram_gate_prepare(int32_t d_mem, int32_t d_model, int32_t n_branch, const void* const* wk,
@@ -309,7 +331,9 @@ engram_status engram_gate_forward_prepared(const void* mem, int64_t n_tok, int32
  * feeding section 2.3, Eq. (3)-(4) (and section 2.4, Eq. (6) for several branches):
  * exactly engram_lookup of raw (bf16 tables) into memory vectors e [batch*t_count][d_mem],
  * d_mem = n_orders*heads*w, followed by engram_gate_forward(e, batch*t_count, d_mem, ...,
- * ENGRAM_BF16, key_norm, ...); the outputs are bit-identical to those two calls'.  The
+ * ENGRAM_BF16, key_norm, ...); the outputs are bit-identical to those two calls' with
+ * feature-major key tiles (see engram_debug_gate_key_form: where engram_gate_forward would
+ * choose memory-major ones, the two differ in the fp32 rounding order of the logit).  The
  * gate's matrix-core kernel hashes each token's n-grams itself and loads the table rows
  * straight into its operand tiles, so e makes no round trip through device memory.
  * raw .. w, ids_out, err_count: as for engram_lookup (dtype ENGRAM_BF16; no index output).

@@ -149,6 +149,15 @@ def test_gate_wait_timeout_query_argument_errors():
     assert L.engram_debug_force_gate_timeout(0) == _st("ok")
 
 
+def test_gate_key_form_hook_argument_errors():
+    L = eg.lib()
+    assert L.engram_debug_gate_key_form(3) == _st("arg")
+    assert L.engram_debug_gate_key_form(-1) == _st("arg")
+    assert b"form" in L.engram_last_error()
+    for form in (1, 2, 0):  # ends on the default
+        assert L.engram_debug_gate_key_form(form) == _st("ok")
+
+
 def test_lookup_argument_errors():
     import numpy as np
     L = eg.lib()

@@ -3,7 +3,8 @@ matrix-core kernel hashing each token's n-grams and loading the table rows into 
 operand tiles itself.
 
 Bar: every output (the updated hidden states, the gates, the gated values, the canonical
-ids and the error count) bit-identical to engram_lookup followed by engram_gate_forward,
+ids and the error count) bit-identical to engram_lookup followed by engram_gate_forward
+with feature-major key tiles (the fused call's form; set for every test here),
 whose parity with the oracle the other GPU tests establish; and, independently, the gate
 against the oracle (gpu_helpers.check_gate's bars) on memory vectors the oracle builds
 from the same raw ids.  The cases span one to 25 k-steps, table rows of 8 to 25 16-byte
@@ -21,6 +22,20 @@ from gpu_helpers import check_gate, host_view, sentinel_like
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(autouse=True)
+def feature_major_key_tiles():
+    """The gathering gate's key tiles are feature-major; engram_gate_forward chooses
+    memory-major ones for some of these shapes (the small and large workloads), whose
+    logits round differently.  The two-call references here take the same form as the
+    fused call, so the comparison is bit for bit; the memory-major form has its own
+    oracle tests (test_gpu_key_form.py)."""
+    eg.engram_debug_gate_key_form("feature")
+    yield
+    eg.engram_debug_gate_key_form("auto")
+
+
 MEM, PROJ = eg.KEY_NORM_MEMORY, eg.KEY_NORM_PROJECTED
 
 
@@ -159,7 +174,8 @@ def test_lookup_gate_small_config_against_oracle_sampled():
 
 def test_lookup_gate_large_workload_bit_identical():
     """The large workload (26 GB of tables, 262,144 tokens, d_model 4096, two branches) in
-    the benchmark's launch configuration: every output bit-identical to the two calls."""
+    the benchmark's launch configuration: every output bit-identical to the two calls
+    (feature-major key tiles, as throughout this module)."""
     from hashed_gram_embedding_hash_amd.pipeline import EngramLayer
     cfg = synth.CONFIGS["large"]
     say(f"lookup_gate on the large workload: {cfg.tokens} tokens, {cfg.n_tables} x {cfg.rows} rows")
@@ -170,7 +186,7 @@ def test_lookup_gate_large_workload_bit_identical():
     ref_a = torch.empty((cfg.n_branch, cfg.tokens), dtype=torch.float32, device=DEV)
     layer(inp["raw"], inp["h"], out=ref, gate_out=ref_a)
     torch.cuda.synchronize()
-    say("  two-call pass done")
+    say("  two-call pass done (feature-major key tiles)")
     got = [sentinel_like(torch.empty_like(x)) for x in inp["h"]]
     got_a = sentinel_like(torch.empty_like(ref_a))
     eg.engram_lookup_gate(inp["raw"], inp["map"], cfg.orders, cfg.heads, inp["mult"], inp["tables"], cfg.vocab_c,
