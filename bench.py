@@ -613,6 +613,26 @@ def run_offload(args):
             comp["prefetch_cached_us"] = serial(lambda s: cached_prefetch(0, ms))
         pcie_bytes = B * cfg.n_tables * row_bytes
         comp["prefetch_host_GBps"] = pcie_bytes / (comp["prefetch_host_us"] * 1e-6) / 1e9
+        # What kernel loads get over PCIe for this access pattern (the probes of
+        # libengram_probe.so, measurement only): the step's B x n_tables row indices read from
+        # one host table (every table has the same rows), nothing written; and a contiguous
+        # read of the same number of bytes from host memory.
+        from hashed_gram_embedding_hash_amd import build as hb
+        PL = ctypes.CDLL(hb.PROBE_LIB)
+        PL.engram_probe_rows_sink_words.restype = ctypes.c_int64
+        PL.engram_probe_rows_sink_words.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
+        PL.engram_probe_row_reads.argtypes = [P, ctypes.c_int32, P, ctypes.c_int64, ctypes.c_int32, P, P]
+        PL.engram_probe_stream_reads.argtypes = [P, ctypes.c_int64, P, P]
+        sink = torch.empty(max(int(PL.engram_probe_rows_sink_words(B, row_bytes, cfg.n_tables)), 8192 * 256),
+                           dtype=torch.int32, device=dev)
+        assert all(r == rows for r in hrows)
+        comp["probe_host_rows_us"] = serial(lambda s: chk(-1 if PL.engram_probe_row_reads(
+            P(haddr[0]), row_bytes, P(idx[0].data_ptr()), B, cfg.n_tables, P(sink.data_ptr()), ms) else 0))
+        comp["probe_host_rows_GBps"] = pcie_bytes / (comp["probe_host_rows_us"] * 1e-6) / 1e9
+        comp["probe_host_stream_us"] = serial(lambda s: chk(-1 if PL.engram_probe_stream_reads(
+            P(haddr[0]), pcie_bytes, P(sink.data_ptr()), ms) else 0))
+        comp["probe_host_stream_GBps"] = pcie_bytes / (comp["probe_host_stream_us"] * 1e-6) / 1e9
+        comp["prefetch_host_frac_of_row_probe"] = comp["probe_host_rows_us"] / comp["prefetch_host_us"]
         # reference: pinned host-to-device copy of one contiguous 256 MiB block
         nb = min(256 << 20, rows * row_bytes)
         dst = torch.empty(nb, dtype=torch.uint8, device=dev)
