@@ -350,14 +350,20 @@ __device__ __forceinline__ void gate_tile(const GateArgs& a, const GS& gs, const
   ENGRAM_STAMP_TILE(tile);
   static_assert(!(GATHER && F8), "the gathering gate is bf16");
   static_assert(!TK || (!KEYP && !F8 && !GATHER), "memory-major K tiles: bf16, memory-side key norm, no gather");
-  const int PHASE = tile.phase;
+  // TK: the tile's fields are made wave-uniform (scalar registers) here.  The tile number
+  // reaches every lane through LDS, so the compiler would otherwise keep the values derived
+  // from it in vector registers; with the phase-dependent row lengths and bases of the TK
+  // main loop that spilled address registers whose reloads the compiler then waited for
+  // inside the k-step loop (s_waitcnt vmcnt(0), which also drains the operand ring).
+  const int PHASE = TK ? __builtin_amdgcn_readfirstlane(tile.phase) : tile.phase;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wf = wave >> 1, wt = wave & 1;
-  const int m = tile.m, ftile = tile.ftile;
+  const int m = TK ? __builtin_amdgcn_readfirstlane(tile.m) : tile.m;
+  const int ftile = TK ? __builtin_amdgcn_readfirstlane(tile.ftile) : tile.ftile;
   const int f0 = ftile * BF;
-  const int64_t t0 = (int64_t)tile.ttile * BT;
+  const int64_t t0 = (int64_t)(TK ? __builtin_amdgcn_readfirstlane(tile.ttile) : tile.ttile) * BT;
   const int64_t n_tok = a.n_tok;
   const int d_mem = a.d_mem, d_model = a.d_model;
   int32_t* done = a.counters + NQ + m * a.n_ttiles + tile.ttile;
@@ -1543,16 +1549,13 @@ void launch_gate_bf16(const GateArgs& a_in, bool fp8, hipStream_t s, bool prequa
   if (grid < NQ) grid = NQ;
   // Memory-major K tiles (TK) where they apply (bf16 with the memory-side key norm and the
   // folded weights made here, d_mem < d_model so their partials fit the feature-major
-  // layout, d_model a whole number of k-steps) and, chosen by shape, where they measured
-  // faster: at most two branches (each branch streams its own h through the K tiles; at
-  // four, the feature-major tiles, whose memory rows all branches share, were faster) and
-  // at least one K tile per CU (a decode step's one token tile would leave most CUs idle
-  // behind the longer tiles).
+  // layout, d_model a whole number of k-steps) and where there is at least one K tile per
+  // CU (a decode step's one token tile would leave most CUs idle behind the longer tiles).
   const int n_ctiles = (a.d_mem + BF - 1) / BF;
   const int form = g_key_form.load(std::memory_order_relaxed);
   const bool tk_ok = !fp8 && !prequant && gs == nullptr && !keyp && a.d_mem < a.d_model && a.d_model % BK == 0;
   const bool tk = tk_ok && form != 1 &&
-                  (form == 2 || (a.n_branch <= 2 && (int64_t)a.n_ttiles * a.n_branch * n_ctiles >= (int64_t)grid));
+                  (form == 2 || (int64_t)a.n_ttiles * a.n_branch * n_ctiles >= (int64_t)grid);
   a.n_ktiles = tk ? n_ctiles : a.n_ftiles;
   if (fp8) {
     // the key gains and the counters, then the E4M3 codes: W_K with both gains folded

@@ -291,9 +291,8 @@ engram_status engram_debug_force_gate_timeout(int32_t on);
  *   memory-major   sum_c e_c (W_K'^T h)_c, over d_mem/256 tiles of 256 memory
  *                  dimensions, each contracting over d_model (fewer, longer tiles).
  * The two differ only in the fp32 rounding order of that sum.  form 0 (the default)
- * chooses by shape: memory-major when d_mem < d_model, d_model % 64 == 0, n_branch <= 2
- * and there are at least as many memory-major tiles as compute units; feature-major
- * otherwise.  1 forces feature-major, 2 memory-major wherever it applies.  The setting is process-wide and
+ * chooses by shape: memory-major when d_mem < d_model, d_model % 64 == 0 and there are at
+ * least as many memory-major tiles as compute units; feature-major otherwise.  1 forces feature-major, 2 memory-major wherever it applies.  The setting is process-wide and
  * read at each launch.  INVALID_ARG for another form; never set it outside tests and
  * measurements.
  */
