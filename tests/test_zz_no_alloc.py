@@ -40,9 +40,12 @@ def _both(e, hs, wks, wvs, gqs, gks, eps=1e-6):
 
 
 def test_noalloc_equals_gate_forward_two_calls_second_smaller():
+    """Calls in a row, each smaller than the one before: 13,312 tokens x 2 branches (520
+    key tiles: memory-major, the array holding the transposed folded weights), then 3,000
+    x 2 and 300 x 1 (feature-major, the same array refilled)."""
     cfg = synth.CONFIGS["small"]
-    print("noalloc gate: 3000 tokens x 2 branches, then 300 tokens x 1 branch", flush=True)
-    for n_tok, nb, seed in ((3000, 2, 1), (300, 1, 2)):
+    print("noalloc gate: 13312 tokens x 2 branches, 3000 x 2, then 300 x 1", flush=True)
+    for n_tok, nb, seed in ((13312, 2, 4), (3000, 2, 1), (300, 1, 2)):
         ref, a_ref, na, a_na = _both(*_case(cfg, n_tok, nb, seed))
         assert torch.equal(a_ref, a_na) and torch.isfinite(a_na).all()
         for m in range(nb):
