@@ -50,6 +50,8 @@ def _run(form, e, hs, wks, wvs, gqs, gks, inplace=False, values=False):
     (320, 1024, 333, 3, False, False, True),     # ragged last key tile (64 wide); branches past the first
     (1216, 2624, 300, 3, True, True, True),      # shared W_V in place with values; ragged tiles of both kinds
     (1280, 4096, 520, 2, False, True, False),    # the large workload's widths, 64 k-steps
+    (640, 1024, 300, 8, False, True, False),     # the most branches (partials of branch 7), in place
+    (64, 1024, 200, 2, False, False, True),      # one key tile, 64 wide (d_mem one k-step deep)
 ])
 def test_gate_memory_major_against_oracle(d_mem, d_model, n_tok, M, shared, inplace, values):
     """Unit-scale memory and gains != 1 (so |alpha v| ~ |h| and the update bar applies);
