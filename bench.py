@@ -152,6 +152,22 @@ def gate_source_sha():
         return code_sha(f.read())
 
 
+def gate_key_tiles(cfg, args, n_cu=256):
+    """The key-tile form engram_gate_forward takes for this workload, by the rule engram.h
+    documents for engram_debug_gate_key_form (bf16, memory-side key norm, the weights folded
+    by the call: memory-major when d_mem < d_model, d_model % 64 == 0 and there are at least as
+    many memory-major key tiles as compute units; feature-major otherwise)."""
+    if cfg.dtype != "bf16" or args.fp8 or args.key_norm != "memory":
+        return "feature-major"
+    if args.key_form != "auto":
+        forced = args.key_form == "memory" and cfg.d_mem < cfg.d_model and cfg.d_model % 64 == 0
+        return ("memory-major" if forced else "feature-major") + " (forced)"
+    n_ttiles = -(-cfg.tokens // 256)
+    n_ktiles = -(-cfg.d_mem // 256)
+    mm = cfg.d_mem < cfg.d_model and cfg.d_model % 64 == 0 and n_ttiles * cfg.n_branch * n_ktiles >= n_cu
+    return "memory-major" if mm else "feature-major"
+
+
 def measured_traffic(cfg):
     """HBM bytes per launch of the gate's persistent kernel, from the committed counter
     summary (FETCH_SIZE + WRITE_SIZE scaled by a plain copy of known size).  None when
@@ -1128,7 +1144,7 @@ def run_workload(args, name, secondary=False):
               "engram_gate_forward: the key-weight fold (gate_prep_kernel, or gate_prep_t_kernel for "
               "memory-major key tiles) + gate_persistent_kernel (events bracket both; the fold is about "
               "3 % of the call)")
-    roofline = {"kernel": kernel,
+    roofline = {"kernel": kernel, "key_tiles": gate_key_tiles(cfg, args),
                 "bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic,
                 "traffic_algorithmic": work["gate"]["bytes"],

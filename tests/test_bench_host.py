@@ -62,3 +62,19 @@ def test_code_hash_ignores_comments_and_whitespace_only():
     b = "int f(int x){\n\treturn x+1;}"
     c = "int f(int x) { return x + 2; }"
     assert bench.code_sha(a) == bench.code_sha(b) != bench.code_sha(c)
+
+
+def test_key_tile_form_reported_for_each_workload():
+    """The form the JSON line names follows engram.h's rule: memory-major key tiles when
+    d_mem < d_model, d_model % 64 == 0 and at least one key tile per compute unit."""
+    import argparse
+    a = argparse.Namespace(fp8=False, key_norm="memory", key_form="auto")
+    got = {n: bench.gate_key_tiles(synth.CONFIGS[n], a) for n in ("tiny", "small", "multi", "large")}
+    assert got == {"tiny": "feature-major", "small": "memory-major", "multi": "memory-major",
+                   "large": "memory-major"}
+    # a decode step: 256 tokens, 5 key tiles
+    assert bench.gate_key_tiles(synth.CONFIGS["large"].replace(batch=1, seq=256), a) == "feature-major"
+    assert bench.gate_key_tiles(synth.CONFIGS["large"], argparse.Namespace(
+        fp8=False, key_norm="memory", key_form="feature")) == "feature-major (forced)"
+    assert bench.gate_key_tiles(synth.CONFIGS["large"], argparse.Namespace(
+        fp8=True, key_norm="memory", key_form="auto")) == "feature-major"
