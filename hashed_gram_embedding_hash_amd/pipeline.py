@@ -9,7 +9,10 @@ the intermediate device buffers and issues the calls on one stream
 arithmetic is in the HIP kernels.  Passing one W_V tensor for every branch
 (section 2.4, Eq. (6)) lets the gate compute W_V e once for all of them.
 With fused=True the whole pass is one call, engram_lookup_gate, whose gate kernel
-loads the table rows itself (same results bit for bit; no memory-vector buffer).
+loads the table rows itself (no memory-vector buffer).  Its key tiles are feature-major,
+so its results equal the two calls' bit for bit where those take feature-major key tiles
+too (decode-sized batches; engram_debug_gate_key_form); for larger batches the two calls
+take memory-major key tiles and the logits differ in fp32 rounding order only.
 """
 from __future__ import annotations
 
