@@ -243,6 +243,11 @@ constexpr int CB = 8;         // (branch, feature tile) combinations per block
 // the gathering gate (its memory tiles are random table rows): the same, its own sizes
 constexpr int TT_GROUP_G = 4;
 constexpr int CB_G = 8;
+// the V phase behind memory-major key tiles: 8 token tiles x 4 pairs (measured 0.5-1.4 % faster
+// than 4 x 8 there on the large and multi workloads; 4 x 8 stays the faster one behind
+// feature-major key tiles)
+constexpr int TT_GROUP_TKV = 8;
+constexpr int CB_TKV = 4;
 
 // Tile r of a phase whose tiles are the n_tt token tiles of a queue x `per` combinations
 // (branch, feature tile), ordered so that 32 consecutive tiles cover TTG token tiles x CBN
@@ -291,7 +296,7 @@ __device__ __forceinline__ bool decode_tile(const GateArgs& a, int x, int q, Til
     // weight panel that many token tiles' ways) and stay on one branch's weight panels for
     // 32 token tiles (measured 0.5 % faster than switching branch every 32 / n_ktiles)
     if (t.phase == PHASE_K) blocked_rt(r, n_tt, per, 32, a.n_ktiles, tl, combo);
-    else blocked<TT_GROUP, CB>(r, n_tt, per, tl, combo);
+    else blocked<TT_GROUP_TKV, CB_TKV>(r, n_tt, per, tl, combo);
     const int nt = t.phase == PHASE_V ? a.n_ftiles : a.n_ktiles;  // output tiles per branch
     t.m = combo / nt;
     t.ftile = combo - t.m * nt;
